@@ -1,0 +1,172 @@
+"""Python binding of libsparse_ffn.so (include/sparse_ffn.h).
+
+Argument marshalling only: each function takes torch tensors that already
+live on the GPU, passes their device pointers, sizes and torch's current
+HIP stream to the C entry point of the same name, and raises
+:class:`SffnError` on a non-OK status.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback of any kind, and a
+missing library is an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first so the library binds to torch's HIP runtime
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_ffn.so")
+
+SFFN_OK, SFFN_EINVAL, SFFN_EUNSUPPORTED, SFFN_EWORKSPACE, SFFN_EHIP = range(5)
+KEY_ABS_F32, KEY_U32, KEY_F32 = 0, 1, 2
+SCORE_SUM_ABS, SCORE_CLUSTER_MAX, SCORE_SOFTMAX_PICKED = 0, 1, 2
+OP_GLU_SILU, OP_DOT_RELU, OP_GATED, OP_AXPY = 0, 1, 2, 3
+
+_STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
+
+
+class SffnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsparse_ffn.so (built in-tree by ``build.py``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m activation_sparse_decode_amd.build`"
+                " (there is no fallback path)")
+        L = ctypes.CDLL(_LIB_PATH)
+        L.sffn_last_error.restype = ctypes.c_char_p
+        L.sffn_abi_version.restype = _i
+        L.sparse_ffn_workspace_size.restype = _sz
+        L.sparse_ffn_workspace_size.argtypes = [_i, _i, _i]
+        L.sparse_ffn_tier_record_bytes.restype = _sz
+        L.sparse_ffn_tier_record_bytes.argtypes = [_i, _i]
+        L.sparse_ffn_score.restype = _i
+        L.sparse_ffn_score.argtypes = [_i, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp]
+        L.sparse_ffn_select.restype = _i
+        L.sparse_ffn_select.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i,
+                                        _vp, _vp, _vp]
+        L.sparse_ffn_gemv.restype = _i
+        L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
+                                      _vp, _i, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
+        L.sparse_ffn_encode_tiers.restype = _i
+        L.sparse_ffn_encode_tiers.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]
+        L.sparse_ffn_tiered_gemv.restype = _i
+        L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
+                                             _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
+        if L.sffn_abi_version() != 1:
+            raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != SFFN_OK:
+        raise SffnError(status, lib().sffn_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ld(t, default: int) -> int:
+    return t.stride(0) if (t is not None and t.dim() == 2) else default
+
+
+# ------------------------------------------------------------------ sizes
+
+def workspace_size(batch: int, n_rows: int, d_out: int) -> int:
+    return int(lib().sparse_ffn_workspace_size(batch, n_rows, d_out))
+
+
+def tier_record_bytes(d_out: int, n_seg: int) -> int:
+    return int(lib().sparse_ffn_tier_record_bytes(d_out, n_seg))
+
+
+def new_workspace(batch: int, n_rows: int, d_out: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of the size the gathered products need."""
+    return torch.zeros(workspace_size(batch, n_rows, d_out), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def sparse_ffn_score(mode: int, inp: torch.Tensor, out: torch.Tensor, *, cluster: int = 1,
+                     accumulate: bool = False, picked: torch.Tensor | None = None,
+                     stream=None) -> None:
+    T, n = (inp.shape[0], inp.shape[1]) if inp.dim() == 2 else (1, inp.shape[0])
+    k = picked.shape[-1] if picked is not None else 0
+    _check(lib().sparse_ffn_score(mode, _p(inp), T, n, _ld(inp, n), cluster, int(accumulate),
+                                  _p(picked), k, _p(out), _stream(stream)))
+
+
+def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *,
+                      nonzero_only: bool = False, include_mask: torch.Tensor | None = None,
+                      mask_out: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
+                      count_out: torch.Tensor | None = None, freq: torch.Tensor | None = None,
+                      stream=None) -> None:
+    rows, n = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
+    _check(lib().sparse_ffn_select(
+        _p(keys), key_type, rows, n, _ld(keys, n), r_lo, r_hi, int(nonzero_only),
+        _p(include_mask), _p(mask_out), _ld(mask_out, n), _p(idx_out),
+        _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out), _p(freq),
+        _stream(stream)))
+
+
+def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
+                    inp: torch.Tensor, out: torch.Tensor, *, idx: torch.Tensor | None = None,
+                    count: torch.Tensor | None = None, k_max: int = 0, group: int = 1,
+                    row_mask: torch.Tensor | None = None, tau_scale: float = 0.0,
+                    aux: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+                    key_out: torch.Tensor | None = None, accumulate: bool = False,
+                    workspace: torch.Tensor | None = None, stream=None) -> None:
+    W = W0 if W0 is not None else W1
+    n_rows, d = W.shape[0], W.shape[1]
+    ld_w = W.stride(0)
+    batch = inp.shape[0] if inp.dim() == 2 else 1
+    ld_in = _ld(inp, inp.shape[-1])
+    ld_out = _ld(out, out.shape[-1])
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().sparse_ffn_gemv(
+        op, _p(W0), _p(W1), n_rows, d, ld_w, _p(inp), batch, ld_in, _p(idx), _p(count),
+        k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), _p(aux),
+        _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
+        _p(workspace), ws_bytes, _stream(stream)))
+
+
+def _seg_array(seg_rows):
+    arr = (ctypes.c_int32 * len(seg_rows))(*[int(v) for v in seg_rows])
+    return arr, len(seg_rows) - 1
+
+
+def sparse_ffn_encode_tiers(Wt: torch.Tensor, seg_rows, mid_rec: torch.Tensor,
+                            stream=None) -> None:
+    arr, n_seg = _seg_array(seg_rows)
+    _check(lib().sparse_ffn_encode_tiers(
+        _p(Wt), Wt.stride(0), Wt.shape[0], Wt.shape[1], arr, n_seg, _p(mid_rec),
+        mid_rec.stride(0), _stream(stream)))
+
+
+def sparse_ffn_tiered_gemv(Wt: torch.Tensor, mid_rec: torch.Tensor, seg_rows, x: torch.Tensor,
+                           idx_top, cnt_top, k_top_max: int, idx_mid, cnt_mid, k_mid_max: int,
+                           y: torch.Tensor, *, accumulate: bool = False,
+                           workspace: torch.Tensor | None = None, stream=None) -> None:
+    arr, n_seg = _seg_array(seg_rows)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().sparse_ffn_tiered_gemv(
+        _p(Wt), Wt.stride(0), _p(mid_rec), mid_rec.stride(0), arr, n_seg, Wt.shape[0],
+        Wt.shape[1], _p(x), _p(idx_top), _p(cnt_top), k_top_max, _p(idx_mid), _p(cnt_mid),
+        k_mid_max, _p(y), int(accumulate), _p(workspace), ws_bytes, _stream(stream)))

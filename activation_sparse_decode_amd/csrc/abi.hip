@@ -1,0 +1,268 @@
+// C ABI of libsparse_ffn.so: argument validation, error reporting and
+// dispatch to the kernels.  Every check runs before anything is launched;
+// a rejected call launches nothing.  See include/sparse_ffn.h for the
+// contract of each entry point.
+#include <cmath>
+#include <cstdarg>
+#include <algorithm>
+#include <cstdio>
+#include <string>
+
+#include "../../include/sparse_ffn.h"
+#include "sffn_device.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sffn_status fail(sffn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sffn_status ok() {
+  g_last_error.clear();
+  return SFFN_OK;
+}
+
+sffn_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SFFN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+namespace sffn {
+
+size_t workspace_bytes(int batch, int n_rows, int d_out) {
+  if (batch < 1) batch = 1;
+  if (n_rows < 0) n_rows = 0;
+  if (d_out < 0) d_out = 0;
+  if (batch == 1) return kCounterBytes + align256((size_t)kMaxSplit * d_out * sizeof(float));
+  const int Mt = (batch + 15) / 16;
+  const size_t Mpad = (size_t)Mt * 16;
+  const size_t Kpad = ((size_t)n_rows + 63) / 64 * 64;
+  return kCounterBytes + align256((size_t)max_split_mfma(Mt) * Mpad * d_out * sizeof(float)) +
+         2 * align256(Mpad * Kpad * 2);
+}
+}  // namespace sffn
+
+extern "C" {
+
+const char* sffn_last_error(void) { return g_last_error.c_str(); }
+
+int sffn_abi_version(void) { return SFFN_ABI_VERSION; }
+
+size_t sparse_ffn_workspace_size(int batch, int n_rows, int d_out) {
+  return sffn::workspace_bytes(batch, n_rows, d_out);
+}
+
+size_t sparse_ffn_tier_record_bytes(int d_out, int n_seg) {
+  if (d_out <= 0 || n_seg < 1 || n_seg > 4) return 0;
+  const size_t b = 16 + (size_t)(d_out + 1) / 2;
+  return (b + 15) / 16 * 16;
+}
+
+sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld, int cluster,
+                             int accumulate, const int32_t* picked, int k, void* out,
+                             void* stream) {
+  REQUIRE(mode >= 0 && mode <= 2, SFFN_EINVAL, "score: unknown mode %d", mode);
+  REQUIRE(in && out, SFFN_EINVAL, "score: in and out must be non-null");
+  REQUIRE(T >= 0 && n >= 0, SFFN_EINVAL, "score: T=%d and n=%d must be >= 0", T, n);
+  REQUIRE(ld >= n, SFFN_EINVAL, "score: ld=%d < n=%d", ld, n);
+  REQUIRE(aligned(in, 4) && aligned(out, 4), SFFN_EINVAL, "score: in/out must be 4-byte aligned");
+  if (mode == SFFN_SCORE_CLUSTER_MAX) {
+    REQUIRE(cluster >= 1, SFFN_EINVAL, "score: cluster=%d must be >= 1", cluster);
+    REQUIRE(n % cluster == 0, SFFN_EINVAL, "score: n=%d not a multiple of cluster=%d", n, cluster);
+  }
+  if (mode == SFFN_SCORE_SOFTMAX_PICKED) {
+    REQUIRE(picked != nullptr, SFFN_EINVAL, "score: softmax needs the picked indices");
+    REQUIRE(k >= 1 && k <= n, SFFN_EINVAL, "score: k=%d outside [1, n=%d]", k, n);
+  }
+  if (n == 0 || (T == 0 && mode != SFFN_SCORE_SUM_ABS)) return ok();
+  return from_hip(sffn::launch_score(mode, in, T, n, ld, cluster, accumulate, picked, k, out,
+                                     (hipStream_t)stream),
+                  "score launch");
+}
+
+sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld, int r_lo,
+                              int r_hi, int nonzero_only, const uint8_t* include_mask,
+                              uint8_t* mask_out, int ld_mask, int32_t* idx_out, int ld_idx,
+                              int32_t* count_out, uint32_t* freq_inout, void* stream) {
+  REQUIRE(keys != nullptr, SFFN_EINVAL, "select: keys must be non-null");
+  REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "select: unknown key type %d", key_type);
+  REQUIRE(rows >= 0, SFFN_EINVAL, "select: rows=%d must be >= 0", rows);
+  REQUIRE(n >= 1 && n <= 32768, SFFN_EUNSUPPORTED, "select: n=%d outside [1, 32768]", n);
+  REQUIRE(ld >= n, SFFN_EINVAL, "select: ld=%d < n=%d", ld, n);
+  REQUIRE(r_lo >= 0 && r_lo <= r_hi, SFFN_EINVAL, "select: need 0 <= r_lo=%d <= r_hi=%d", r_lo,
+          r_hi);
+  REQUIRE(!(nonzero_only && key_type == SFFN_KEY_F32), SFFN_EINVAL,
+          "select: nonzero_only is not defined for signed keys");
+  REQUIRE(aligned(keys, 4), SFFN_EINVAL, "select: keys must be 4-byte aligned");
+  if (mask_out) REQUIRE(ld_mask >= n, SFFN_EINVAL, "select: ld_mask=%d < n=%d", ld_mask, n);
+  if (idx_out) {
+    const long need = include_mask ? (long)n : std::min((long)r_hi - r_lo, (long)n);
+    REQUIRE(ld_idx >= need, SFFN_EINVAL, "select: ld_idx=%d < %ld", ld_idx, need);
+    REQUIRE(aligned(idx_out, 4), SFFN_EINVAL, "select: idx_out must be 4-byte aligned");
+  }
+  if (count_out) REQUIRE(aligned(count_out, 4), SFFN_EINVAL, "select: count_out misaligned");
+  if (freq_inout) REQUIRE(aligned(freq_inout, 4), SFFN_EINVAL, "select: freq misaligned");
+  if (rows == 0) return ok();
+  sffn::SelectArgs a{keys, key_type, rows, n, ld, r_lo, r_hi, nonzero_only ? 1 : 0, include_mask,
+                     mask_out, ld_mask, idx_out, ld_idx, count_out, freq_inout};
+  return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
+}
+
+sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int n_rows, int d,
+                            int ld_w, const float* in, int batch, int ld_in, const int32_t* idx,
+                            const int32_t* count, int k_max, int group, const uint8_t* row_mask,
+                            int ld_mask, float tau_scale, const float* aux, int ld_aux,
+                            const float* alpha, float* out, uint32_t* key_out, int ld_out,
+                            int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  REQUIRE(op >= 0 && op <= 3, SFFN_EINVAL, "gemv: unknown op %d", op);
+  REQUIRE(in && out, SFFN_EINVAL, "gemv: in and out must be non-null");
+  REQUIRE(n_rows >= 0, SFFN_EINVAL, "gemv: n_rows=%d must be >= 0", n_rows);
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "gemv: d=%d must be a positive multiple of 8", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL, "gemv: ld_w=%d must be >= d and a multiple of 8",
+          ld_w);
+  REQUIRE(batch >= 1, SFFN_EINVAL, "gemv: batch=%d must be >= 1", batch);
+  REQUIRE(batch == 1 || d % 32 == 0, SFFN_EUNSUPPORTED, "gemv: batch > 1 needs d %% 32 == 0 (d=%d)",
+          d);
+  REQUIRE(aligned(in, 16) && aligned(out, 16), SFFN_EINVAL, "gemv: in/out must be 16-byte aligned");
+  if (batch > 1) REQUIRE(ld_in % 4 == 0, SFFN_EINVAL, "gemv: ld_in=%d must be a multiple of 4", ld_in);
+  if (idx) {
+    REQUIRE(count != nullptr, SFFN_EINVAL, "gemv: idx needs a device count");
+    REQUIRE(group >= 1, SFFN_EINVAL, "gemv: group=%d must be >= 1", group);
+    REQUIRE(k_max >= 0 && (long)k_max * group <= n_rows, SFFN_EINVAL,
+            "gemv: k_max=%d * group=%d exceeds n_rows=%d", k_max, group, n_rows);
+    REQUIRE(aligned(idx, 4) && aligned(count, 4), SFFN_EINVAL, "gemv: idx/count misaligned");
+  }
+  const long items = idx ? (long)k_max * group : (long)n_rows;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (op != SFFN_OP_AXPY) {
+    if (op != SFFN_OP_GATED)
+      REQUIRE(W0 && aligned(W0, 16), SFFN_EINVAL, "gemv: W0 must be non-null and 16-byte aligned");
+    if (op != SFFN_OP_DOT_RELU)
+      REQUIRE(W1 && aligned(W1, 16), SFFN_EINVAL, "gemv: W1 must be non-null and 16-byte aligned");
+    REQUIRE(ld_in >= d, SFFN_EINVAL, "gemv: ld_in=%d < d=%d", ld_in, d);
+    REQUIRE(ld_out >= n_rows, SFFN_EINVAL, "gemv: ld_out=%d < n_rows=%d", ld_out, n_rows);
+    REQUIRE(batch > 1 || d <= 8192, SFFN_EUNSUPPORTED, "gemv: d=%d > 8192 at batch 1", d);
+    if (op == SFFN_OP_DOT_RELU)
+      REQUIRE(tau_scale >= 0.f && std::isfinite(tau_scale), SFFN_EINVAL,
+              "gemv: tau_scale must be finite and >= 0");
+    if (op == SFFN_OP_GATED) {
+      REQUIRE(aux != nullptr, SFFN_EINVAL, "gemv: GATED needs aux");
+      REQUIRE(ld_aux >= n_rows, SFFN_EINVAL, "gemv: ld_aux=%d < n_rows=%d", ld_aux, n_rows);
+    }
+    if (key_out) REQUIRE(aligned(key_out, 4), SFFN_EINVAL, "gemv: key_out misaligned");
+    if (items == 0) return ok();
+    sffn::RowOpArgs a{op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max,
+                      idx ? group : 1, tau_scale, aux, ld_aux, out, key_out, ld_out};
+    return from_hip(batch == 1 ? sffn::launch_rowop_b1(a, s) : sffn::launch_rowop_mfma(a, s),
+                    "gemv launch");
+  }
+
+  REQUIRE(W0 && aligned(W0, 16), SFFN_EINVAL, "gemv: W0 must be non-null and 16-byte aligned");
+  REQUIRE(ld_in >= n_rows, SFFN_EINVAL, "gemv: ld_in=%d < n_rows=%d", ld_in, n_rows);
+  REQUIRE(ld_out >= d, SFFN_EINVAL, "gemv: ld_out=%d < d=%d", ld_out, d);
+  if (row_mask) REQUIRE(ld_mask >= n_rows, SFFN_EINVAL, "gemv: ld_mask=%d < n_rows=%d", ld_mask,
+                        n_rows);
+  if (alpha) REQUIRE(aligned(alpha, 4), SFFN_EINVAL, "gemv: alpha misaligned");
+  const size_t need = sffn::workspace_bytes(batch, (int)items, d);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
+          "gemv: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
+  const long tiles = batch == 1 ? (d + 511) / 512 : (long)((d + 255) / 256) * ((batch + 15) / 16);
+  REQUIRE(tiles <= sffn::kMaxCounters, SFFN_EUNSUPPORTED, "gemv: %ld output tiles exceed %d", tiles,
+          sffn::kMaxCounters);
+  sffn::AxpyArgs a{W0, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max, idx ? group : 1,
+                   row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes};
+  return from_hip(batch == 1 ? sffn::launch_axpy_b1(a, s) : sffn::launch_axpy_mfma(a, s),
+                  "gemv launch");
+}
+
+static sffn_status check_segments(const char* who, const int32_t* seg_rows, int n_seg, int d_out) {
+  REQUIRE(seg_rows != nullptr, SFFN_EINVAL, "%s: seg_rows (host) must be non-null", who);
+  REQUIRE(n_seg >= 1 && n_seg <= 4, SFFN_EUNSUPPORTED, "%s: n_seg=%d outside [1, 4]", who, n_seg);
+  REQUIRE(seg_rows[0] == 0 && seg_rows[n_seg] == d_out, SFFN_EINVAL,
+          "%s: segments must start at 0 and end at d_out=%d", who, d_out);
+  for (int i = 0; i < n_seg; ++i) {
+    REQUIRE(seg_rows[i + 1] > seg_rows[i], SFFN_EINVAL, "%s: segments must increase", who);
+    REQUIRE(seg_rows[i + 1] % 64 == 0, SFFN_EINVAL, "%s: segment bound %d not a multiple of 64", who,
+            seg_rows[i + 1]);
+  }
+  return ok();
+}
+
+sffn_status sparse_ffn_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out,
+                                    const int32_t* seg_rows, int n_seg, uint8_t* mid_rec,
+                                    int rec_bytes, void* stream) {
+  REQUIRE(Wt && mid_rec, SFFN_EINVAL, "encode: Wt and mid_rec must be non-null");
+  REQUIRE(n_in >= 0 && d_out >= 64 && d_out % 64 == 0, SFFN_EINVAL,
+          "encode: need n_in >= 0 and d_out a positive multiple of 64 (d_out=%d)", d_out);
+  REQUIRE(ld_w >= d_out && ld_w % 8 == 0, SFFN_EINVAL, "encode: ld_w=%d must be >= d_out, %% 8",
+          ld_w);
+  sffn_status st = check_segments("encode", seg_rows, n_seg, d_out);
+  if (st != SFFN_OK) return st;
+  REQUIRE(rec_bytes % 16 == 0 && (size_t)rec_bytes >= sparse_ffn_tier_record_bytes(d_out, n_seg),
+          SFFN_EINVAL, "encode: rec_bytes=%d must be a multiple of 16 and >= %zu", rec_bytes,
+          sparse_ffn_tier_record_bytes(d_out, n_seg));
+  REQUIRE(aligned(Wt, 16) && aligned(mid_rec, 16), SFFN_EINVAL, "encode: pointers must be 16-byte aligned");
+  if (n_in == 0) return ok();
+  int b[5] = {0, 0, 0, 0, 0};
+  for (int i = 0; i <= n_seg; ++i) b[i] = seg_rows[i];
+  return from_hip(sffn::launch_encode_tiers(Wt, ld_w, n_in, d_out, b, n_seg, mid_rec, rec_bytes,
+                                            (hipStream_t)stream),
+                  "encode launch");
+}
+
+sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w, const uint8_t* mid_rec,
+                                   int rec_bytes, const int32_t* seg_rows, int n_seg, int n_in,
+                                   int d_out, const float* x, const int32_t* idx_top,
+                                   const int32_t* cnt_top, int k_top_max, const int32_t* idx_mid,
+                                   const int32_t* cnt_mid, int k_mid_max, float* y, int accumulate,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  REQUIRE(Wt && mid_rec && x && y, SFFN_EINVAL, "tiered: Wt, mid_rec, x and y must be non-null");
+  REQUIRE(n_in >= 1 && d_out >= 64 && d_out % 64 == 0, SFFN_EINVAL,
+          "tiered: need n_in >= 1 and d_out a positive multiple of 64 (d_out=%d)", d_out);
+  REQUIRE(ld_w >= d_out && ld_w % 8 == 0, SFFN_EINVAL, "tiered: ld_w=%d must be >= d_out, %% 8",
+          ld_w);
+  sffn_status st = check_segments("tiered", seg_rows, n_seg, d_out);
+  if (st != SFFN_OK) return st;
+  REQUIRE(rec_bytes % 16 == 0 && (size_t)rec_bytes >= sparse_ffn_tier_record_bytes(d_out, n_seg),
+          SFFN_EINVAL, "tiered: rec_bytes=%d must be a multiple of 16 and >= %zu", rec_bytes,
+          sparse_ffn_tier_record_bytes(d_out, n_seg));
+  REQUIRE(k_top_max >= 0 && k_top_max <= n_in && k_mid_max >= 0 && k_mid_max <= n_in, SFFN_EINVAL,
+          "tiered: k_top_max=%d / k_mid_max=%d outside [0, n_in=%d]", k_top_max, k_mid_max, n_in);
+  if (k_top_max > 0) REQUIRE(idx_top && cnt_top, SFFN_EINVAL, "tiered: top list needs idx and count");
+  if (k_mid_max > 0) REQUIRE(idx_mid && cnt_mid, SFFN_EINVAL, "tiered: mid list needs idx and count");
+  REQUIRE(aligned(Wt, 16) && aligned(mid_rec, 16) && aligned(y, 16) && aligned(x, 4), SFFN_EINVAL,
+          "tiered: Wt/mid_rec/y must be 16-byte aligned, x 4-byte aligned");
+  const size_t need = sffn::workspace_bytes(1, k_top_max + k_mid_max, d_out);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
+          "tiered: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "tiered: workspace must be 256-byte aligned");
+  sffn::TierArgs a{};
+  a.Wt = Wt; a.ld_w = ld_w; a.rec = mid_rec; a.rec_bytes = rec_bytes;
+  for (int i = 0; i <= n_seg; ++i) a.seg_bounds[i] = seg_rows[i];
+  a.n_seg = n_seg; a.n_in = n_in; a.d_out = d_out; a.x = x;
+  a.idx_top = idx_top; a.cnt_top = cnt_top; a.k_top_max = k_top_max;
+  a.idx_mid = idx_mid; a.cnt_mid = cnt_mid; a.k_mid_max = k_mid_max;
+  a.y = y; a.accumulate = accumulate ? 1 : 0; a.ws = workspace; a.ws_bytes = ws_bytes;
+  return from_hip(sffn::launch_tiered(a, (hipStream_t)stream), "tiered launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Device helpers and launcher declarations shared by the HIP kernels of
+// libsparse_ffn.so.  Internal to the library; the public surface is
+// include/sparse_ffn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sffn {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- bf16 / keys
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Eight bf16 values packed in a uint4 -> fp32, in memory order.
+__device__ __forceinline__ void unpack8(const uint4& w, float (&f)[8]) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// Magnitude key: fp32 bits with the sign cleared (orders |v|).
+__device__ __forceinline__ uint32_t key_abs(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Order-preserving key of a signed fp32 value.
+__device__ __forceinline__ uint32_t key_signed(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Round fp32 to bf16 (nearest-even) and return the bits; finite inputs.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ----------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// ----------------------------------------------------------------- workspace layout
+// [counters: kCounterBytes][partials: fp32][packed activations: bf16 hi/lo]
+constexpr size_t kCounterBytes = 16384;     // 4096 uint32 tile counters
+constexpr int kMaxCounters = 4096;
+constexpr int kMaxSplit = 256;               // largest split-K factor
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already validated.
+
+struct RowOpArgs {
+  int op;
+  const uint16_t* W0; const uint16_t* W1;
+  int n_rows, d, ld_w;
+  const float* x; int batch, ld_in;
+  const int32_t* idx; const int32_t* count; int k_max, group;
+  float tau_scale;
+  const float* aux; int ld_aux;
+  float* out; uint32_t* key_out; int ld_out;
+};
+hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s);
+hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s);
+
+struct AxpyArgs {
+  const uint16_t* W; int n_rows, d, ld_w;
+  const float* in; int batch, ld_in;
+  const int32_t* idx; const int32_t* count; int k_max, group;
+  const uint8_t* row_mask; int ld_mask;
+  const float* alpha;
+  float* out; int ld_out; int accumulate;
+  void* ws; size_t ws_bytes;
+};
+hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s);
+hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s);
+
+struct SelectArgs {
+  const void* keys; int key_type; int rows, n, ld;
+  int r_lo, r_hi, nonzero_only;
+  const uint8_t* include_mask;
+  uint8_t* mask_out; int ld_mask;
+  int32_t* idx_out; int ld_idx;
+  int32_t* count_out;
+  uint32_t* freq;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+hipError_t launch_score(int mode, const float* in, int T, int n, int ld, int cluster,
+                        int accumulate, const int32_t* picked, int k, void* out,
+                        hipStream_t s);
+
+struct TierArgs {
+  const uint16_t* Wt; int ld_w;
+  const uint8_t* rec; int rec_bytes;
+  int seg_bounds[5]; int n_seg;
+  int n_in, d_out;
+  const float* x;
+  const int32_t* idx_top; const int32_t* cnt_top; int k_top_max;
+  const int32_t* idx_mid; const int32_t* cnt_mid; int k_mid_max;
+  float* y; int accumulate;
+  void* ws; size_t ws_bytes;
+};
+hipError_t launch_tiered(const TierArgs& a, hipStream_t s);
+hipError_t launch_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out,
+                               const int* seg_bounds, int n_seg, uint8_t* rec,
+                               int rec_bytes, hipStream_t s);
+
+size_t workspace_bytes(int batch, int n_rows, int d_out);
+int pick_split_b1(long items, int col_tiles);
+int max_split_mfma(int mtiles);
+
+}  // namespace sffn

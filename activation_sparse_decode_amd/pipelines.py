@@ -1,0 +1,257 @@
+"""Decode paths built from the library's entry points.
+
+Each class owns its device buffers (allocated once, at construction) and
+chains ``sparse_ffn_*`` calls on torch's current stream; selections and
+counts stay on the device between calls.  The intermediate buffers are
+attributes so tests can compare every stage.
+
+* :class:`SwigluSparseLayer`   per-token top-k SwiGLU FFN at batch 1
+* :class:`SelectInferStack`    SelectInfer (§3-§5): Eq (1) base set from
+  calibration, per-token top-alpha / frequency top-beta from the prompt,
+  union, then decode over the union in every layer
+* :class:`TieredProjection`    SpAx three-tier read (abstract, Fig 2-4)
+* :class:`ReluMoEStack`        ReLU-sparse MoE with 32-row clusters
+  (PowerInfer-2 guide, neuron clusters) and top-2 routing
+* :class:`BatchedUnionLayer`   batched decode: per-token top-k, union
+  gathered once and contracted on MFMA
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+F32, I32, U8 = torch.float32, torch.int32, torch.uint8
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """bf16 bit patterns (numpy uint16) -> int16 device tensor (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def pct_count(pct: int, n: int) -> int:
+    """Items kept for a ratio of pct percent of n: floor(pct * n / 100)."""
+    return (pct * n) // 100
+
+
+class SwigluSparseLayer:
+    """x -> a = silu(W_g x) * (W_u x) (+ keys) -> top-``keep`` by |a| ->
+    y = sum over the kept neurons of a_n W_down^T[n]."""
+
+    def __init__(self, Wg, Wu, WdT, keep: int):
+        self.Wg, self.Wu, self.WdT, self.keep = Wg, Wu, WdT, keep
+        N, d = Wg.shape
+        dev = Wg.device
+        self.a = torch.zeros(N, dtype=F32, device=dev)
+        self.key = torch.zeros(N, dtype=I32, device=dev)
+        self.idx = torch.zeros(max(keep, 1), dtype=I32, device=dev)
+        self.count = torch.zeros(1, dtype=I32, device=dev)
+        self.ws = B.new_workspace(1, keep, WdT.shape[1], device=dev)
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor, accumulate: bool = False) -> None:
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, x, self.a, key_out=self.key)
+        B.sparse_ffn_select(self.key, B.KEY_U32, 0, self.keep, idx_out=self.idx,
+                            count_out=self.count)
+        B.sparse_ffn_gemv(B.OP_AXPY, self.WdT, None, self.a, y, idx=self.idx, count=self.count,
+                          k_max=self.keep, accumulate=accumulate, workspace=self.ws)
+
+
+class SelectInferStack:
+    """A residual stack of SwiGLU FFN layers, h <- h + FFN_l(h), run the
+    SelectInfer way: dense calibration and prefill, sparse decode over
+    U_l = base_l (top delta by Eq (1)) union dynamic_l (top beta by how often
+    a neuron is in a prompt token's top alpha)."""
+
+    def __init__(self, layers, base_k: int, alpha_k: int, beta_k: int, max_tokens: int = 512):
+        self.layers = layers
+        self.L = len(layers)
+        N, d = layers[0][0].shape
+        self.N, self.d = N, d
+        dev = layers[0][0].device
+        self.base_k, self.alpha_k, self.beta_k = base_k, alpha_k, beta_k
+        self.k_max = min(N, base_k + beta_k)
+        self.scores = torch.zeros(self.L, N, dtype=F32, device=dev)
+        self.base_mask = torch.zeros(self.L, N, dtype=U8, device=dev)
+        self.freq = torch.zeros(self.L, N, dtype=I32, device=dev)
+        self.U_idx = torch.zeros(self.L, N, dtype=I32, device=dev)
+        self.U_cnt = torch.zeros(self.L, dtype=I32, device=dev)
+        self.a = torch.zeros(self.L, N, dtype=F32, device=dev)
+        self.A = torch.zeros(max_tokens, N, dtype=F32, device=dev)
+        self.K = torch.zeros(max_tokens, N, dtype=I32, device=dev)
+        self.ws_dense = B.new_workspace(max_tokens, N, d, device=dev)
+        self.ws = B.new_workspace(1, self.k_max, d, device=dev)
+
+    def _dense_layer(self, l: int, H: torch.Tensor, keys: bool) -> None:
+        Wg, Wu, WdT = self.layers[l]
+        T = H.shape[0]
+        A, K = self.A[:T], self.K[:T]
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, H, A, key_out=K if keys else None)
+
+    def _dense_residual(self, l: int, H: torch.Tensor) -> None:
+        T = H.shape[0]
+        B.sparse_ffn_gemv(B.OP_AXPY, self.layers[l][2], None, self.A[:T], H, accumulate=True,
+                          workspace=self.ws_dense)
+
+    def calibrate(self, X: torch.Tensor, record=None) -> torch.Tensor:
+        """Dense pass of calibration tokens; Eq (1) scores; base sets."""
+        H = X.clone()
+        self.scores.zero_()
+        for l in range(self.L):
+            self._dense_layer(l, H, keys=False)
+            if record is not None:
+                record(l, H, self.A[:H.shape[0]])
+            B.sparse_ffn_score(B.SCORE_SUM_ABS, self.A[:H.shape[0]], self.scores[l])
+            B.sparse_ffn_select(self.scores[l], B.KEY_ABS_F32, 0, self.base_k,
+                                mask_out=self.base_mask[l])
+            self._dense_residual(l, H)
+        return H
+
+    def prefill(self, X: torch.Tensor, record=None) -> torch.Tensor:
+        """Dense pass of the prompt; per-token top-alpha, frequency top-beta,
+        union with the base set, compacted into U_idx / U_cnt."""
+        H = X.clone()
+        self.freq.zero_()
+        T = H.shape[0]
+        for l in range(self.L):
+            self._dense_layer(l, H, keys=True)
+            if record is not None:
+                record(l, H, self.A[:T])
+            B.sparse_ffn_select(self.K[:T], B.KEY_U32, 0, self.alpha_k, freq=self.freq[l])
+            B.sparse_ffn_select(self.freq[l], B.KEY_U32, 0, self.beta_k,
+                                include_mask=self.base_mask[l], idx_out=self.U_idx[l],
+                                count_out=self.U_cnt[l:l + 1])
+            self._dense_residual(l, H)
+        return H
+
+    def decode_layer(self, l: int, h: torch.Tensor, timer=None) -> None:
+        Wg, Wu, WdT = self.layers[l]
+        idx, cnt = self.U_idx[l], self.U_cnt[l:l + 1]
+        if timer is not None:
+            timer.begin()
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, h, self.a[l], idx=idx, count=cnt,
+                          k_max=self.k_max)
+        if timer is not None:
+            timer.end()
+        B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[l], h, idx=idx, count=cnt,
+                          k_max=self.k_max, accumulate=True, workspace=self.ws)
+
+    def decode(self, h: torch.Tensor, timer=None) -> None:
+        """One decode token through every layer (h is updated in place)."""
+        for l in range(self.L):
+            self.decode_layer(l, h, timer)
+
+
+class TieredProjection:
+    """y = W x with the SpAx three tiers: the k_top largest |x_j| columns from
+    bf16, the next k_mid from 4-bit codes, the rest skipped."""
+
+    def __init__(self, Wt: torch.Tensor, seg_rows, k_top: int, k_mid: int):
+        self.Wt, self.seg_rows, self.k_top, self.k_mid = Wt, list(seg_rows), k_top, k_mid
+        n_in, n_out = Wt.shape
+        dev = Wt.device
+        rb = B.tier_record_bytes(n_out, len(seg_rows) - 1)
+        self.rec = torch.zeros(n_in, rb, dtype=U8, device=dev)
+        B.sparse_ffn_encode_tiers(Wt, self.seg_rows, self.rec)
+        self.idx_top = torch.zeros(max(k_top, 1), dtype=I32, device=dev)
+        self.idx_mid = torch.zeros(max(k_mid, 1), dtype=I32, device=dev)
+        self.cnt = torch.zeros(2, dtype=I32, device=dev)
+        self.ws = B.new_workspace(1, k_top + k_mid, n_out, device=dev)
+
+    def __call__(self, x: torch.Tensor, y: torch.Tensor) -> None:
+        B.sparse_ffn_select(x, B.KEY_ABS_F32, 0, self.k_top, idx_out=self.idx_top,
+                            count_out=self.cnt[0:1])
+        B.sparse_ffn_select(x, B.KEY_ABS_F32, self.k_top, self.k_top + self.k_mid,
+                            idx_out=self.idx_mid, count_out=self.cnt[1:2])
+        B.sparse_ffn_tiered_gemv(self.Wt, self.rec, self.seg_rows, x, self.idx_top, self.cnt[0:1],
+                                 self.k_top, self.idx_mid, self.cnt[1:2], self.k_mid, y,
+                                 workspace=self.ws)
+
+
+class ReluMoEStack:
+    """Residual stack of ReLU-sparse MoE FFN layers at batch 1.
+
+    Per layer and token: top-2 experts by router logit (softmax mixing
+    weights); per routed expert r = max(W_g h - tau, 0) densely, the clusters
+    of 32 rows holding a nonzero r, then up and down over those clusters
+    only; h <- h + sum_e w_e y_e."""
+
+    def __init__(self, experts, cluster: int, tau_scale: float, top_k: int = 2):
+        self.experts = experts           # [L][E] of (Wg, Wu, WdT)
+        self.L, self.E = len(experts), len(experts[0])
+        N, d = experts[0][0][0].shape
+        self.N, self.d, self.cluster, self.tau_scale, self.top_k = N, d, cluster, tau_scale, top_k
+        self.nc = N // cluster
+        dev = experts[0][0][0].device
+        self.r = torch.zeros(top_k, N, dtype=F32, device=dev)
+        self.a = torch.zeros(top_k, N, dtype=F32, device=dev)
+        self.kappa = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
+        self.cidx = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
+        self.ccnt = torch.zeros(top_k, dtype=I32, device=dev)
+        self.ws = [B.new_workspace(1, N, d, device=dev) for _ in range(top_k)]
+
+    def route(self, logits: torch.Tensor):
+        """logits [L][T][E] -> (experts [L*T][k] device, weights [L*T][k]
+        device, experts on the host)."""
+        L, T, E = logits.shape
+        flat = logits.reshape(L * T, E)
+        ex = torch.zeros(L * T, self.top_k, dtype=I32, device=logits.device)
+        B.sparse_ffn_select(flat, B.KEY_F32, 0, self.top_k, idx_out=ex)
+        w = torch.zeros(L * T, self.top_k, dtype=F32, device=logits.device)
+        B.sparse_ffn_score(B.SCORE_SOFTMAX_PICKED, flat, w, picked=ex)
+        self.route_idx, self.route_w, self.T = ex, w, T
+        self.route_host = ex.cpu().numpy()     # expert weight pointers are chosen on the host
+        return ex, w
+
+    def layer(self, l: int, t: int, h: torch.Tensor, record=None) -> None:
+        row = l * self.T + t
+        chosen = self.route_host[row]
+        for j, e in enumerate(chosen):
+            Wg, Wu, _ = self.experts[l][e]
+            B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j], tau_scale=self.tau_scale)
+            B.sparse_ffn_score(B.SCORE_CLUSTER_MAX, self.r[j], self.kappa[j], cluster=self.cluster)
+            B.sparse_ffn_select(self.kappa[j], B.KEY_U32, 0, self.nc, nonzero_only=True,
+                                idx_out=self.cidx[j], count_out=self.ccnt[j:j + 1])
+            B.sparse_ffn_gemv(B.OP_GATED, None, Wu, h, self.a[j], idx=self.cidx[j],
+                              count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
+                              aux=self.r[j])
+        if record is not None:
+            record(l, t, h, chosen)
+        for j, e in enumerate(chosen):
+            WdT = self.experts[l][e][2]
+            B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[j], h, idx=self.cidx[j],
+                              count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
+                              alpha=self.route_w[row, j:j + 1], accumulate=True,
+                              workspace=self.ws[j])
+
+    def decode(self, h: torch.Tensor, t: int, record=None) -> None:
+        for l in range(self.L):
+            self.layer(l, t, h, record)
+
+
+class BatchedUnionLayer:
+    """A batch of tokens: per-token top-``keep`` by |a|, the union of the
+    selections gathered once, each token's skipped neurons masked to zero."""
+
+    def __init__(self, Wg, Wu, WdT, keep: int, batch: int):
+        self.Wg, self.Wu, self.WdT, self.keep, self.batch = Wg, Wu, WdT, keep, batch
+        N, d = Wg.shape
+        dev = Wg.device
+        self.A = torch.zeros(batch, N, dtype=F32, device=dev)
+        self.K = torch.zeros(batch, N, dtype=I32, device=dev)
+        self.M = torch.zeros(batch, N, dtype=U8, device=dev)
+        self.F = torch.zeros(N, dtype=I32, device=dev)
+        self.U = torch.zeros(N, dtype=I32, device=dev)
+        self.cnt = torch.zeros(1, dtype=I32, device=dev)
+        self.ws = B.new_workspace(batch, N, d, device=dev)
+
+    def __call__(self, X: torch.Tensor, Y: torch.Tensor) -> None:
+        N = self.Wg.shape[0]
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, X, self.A, key_out=self.K)
+        self.F.zero_()
+        B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M, freq=self.F)
+        B.sparse_ffn_select(self.F, B.KEY_U32, 0, N, nonzero_only=True, idx_out=self.U,
+                            count_out=self.cnt)
+        B.sparse_ffn_gemv(B.OP_AXPY, self.WdT, None, self.A, Y, idx=self.U, count=self.cnt,
+                          k_max=N, row_mask=self.M, workspace=self.ws)

@@ -1,0 +1,241 @@
+/*
+ * sparse_ffn.h -- C ABI of the MI355X (gfx950) activation-sparse FFN /
+ * projection decode library (libsparse_ffn.so).
+ *
+ * The library implements the decode hot path shared by these pages:
+ *   [SelectInfer] "SelectInfer: Selective Neuron Loading and Computation for
+ *                 On-Device LLMs"
+ *   [PowerInfer-2] "PowerInfer-2: Fast 47B LLM Inference on Smartphones" (guide)
+ *   [SpAx]        "Activation Sparsity with Weight Approximation for Faster
+ *                 LLM Decoding on Offloaded Weights"
+ *   [LeanStream]  "LeanStream: A Speculate-and-Refine Streaming Framework for
+ *                 Efficient on-Device LLM Inference"
+ * namely: compute activations, score / rank them by magnitude, select rank
+ * ranges, compact the selection into ascending index lists, and read only
+ * the selected weight rows in a gathered matrix-vector product (plus the
+ * SpAx three-tier read).
+ *
+ * Conventions shared by every call
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  Nothing
+ *    here allocates, frees or synchronises; nothing reads device memory on
+ *    the host.  All work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    null stream).  Counts produced by one call are read on the device by
+ *    the next, so select -> gemv chains never round-trip through the host.
+ *  - Weights are bf16 bit patterns (uint16_t), stored neuron-major: row n of
+ *    W_gate / W_up holds neuron n's input weights, row n of W_down^T holds
+ *    its output weights; [SelectInfer] §3 identifies a neuron with a column
+ *    of gate/up and a row of down.  Row pitch `ld_w` is in elements.
+ *  - Activations and outputs are fp32; keys are uint32; indices and counts
+ *    are int32.  2-D arrays are row-major with the stated leading dimension
+ *    (elements).
+ *  - Arguments are checked before anything is launched.  On a bad argument a
+ *    call returns SFFN_EINVAL / SFFN_EUNSUPPORTED / SFFN_EWORKSPACE, launches
+ *    nothing, and sffn_last_error() describes the problem.  A failed launch
+ *    returns SFFN_EHIP with the HIP error text.  No C++ exception crosses the
+ *    ABI.
+ *  - Device-side preconditions that cannot be checked on the host:
+ *    0 <= idx[i] < n_rows / group, indices in a list are distinct, and
+ *    counts are >= 0; kernels process min(*count, k_max) entries.
+ *  - Calls that take a workspace need it zero-filled once after allocation;
+ *    every call leaves its counters at zero again.  One workspace must not
+ *    be used by two calls that may run at the same time.
+ */
+#ifndef SPARSE_FFN_H
+#define SPARSE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SFFN_OK = 0,
+    SFFN_EINVAL = 1,        /* bad argument (null, misaligned, out of range) */
+    SFFN_EUNSUPPORTED = 2,  /* valid but outside what the kernels handle      */
+    SFFN_EWORKSPACE = 3,    /* workspace missing or too small                 */
+    SFFN_EHIP = 4           /* the HIP runtime reported an error              */
+} sffn_status;
+
+/* How select turns its input into an ordering key (uint32, larger = earlier). */
+typedef enum {
+    SFFN_KEY_ABS_F32 = 0,   /* fp32 input, key = bits & 0x7FFFFFFF: orders |v|;
+                               -0 == +0; NaN above +Inf ([SelectInfer] §2.2 ranks
+                               "by absolute activation value")                  */
+    SFFN_KEY_U32 = 1,       /* uint32 input used as the key (frequency counts)  */
+    SFFN_KEY_F32 = 2        /* fp32 input ordered by signed value (router logits) */
+} sffn_key_type;
+
+typedef enum {
+    SFFN_SCORE_SUM_ABS = 0,        /* [SelectInfer] §3 Eq (1): s_n (+)= sum_t |a_n(t)|,
+                                      fp32, one rounding per add, t ascending      */
+    SFFN_SCORE_CLUSTER_MAX = 1,    /* kappa_c = max over the `cluster` rows of
+                                      cluster c of the magnitude key (exact)       */
+    SFFN_SCORE_SOFTMAX_PICKED = 2  /* w_j = softmax over the k picked entries      */
+} sffn_score_mode;
+
+typedef enum {
+    SFFN_OP_GLU_SILU = 0,   /* out_n = silu(W0[n].x) * (W1[n].x)        (SwiGLU)  */
+    SFFN_OP_DOT_RELU = 1,   /* out_n = max(W0[n].x - tau_scale*||x||_2, 0) (ReGLU gate) */
+    SFFN_OP_GATED = 2,      /* out_n = aux_n * (W1[n].x)                 (ReGLU up) */
+    SFFN_OP_AXPY = 3        /* y (+)= alpha * sum_n m_n in_n W0[n][:]    (down)     */
+} sffn_gemv_op;
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* sffn_last_error(void);
+
+/* ABI revision of this header (bumped on any signature change). */
+int sffn_abi_version(void);
+#define SFFN_ABI_VERSION 1
+
+/* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
+ * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
+ * expansion) and `d_out` outputs per token.  Zero-fill it once. */
+size_t sparse_ffn_workspace_size(int batch, int n_rows, int d_out);
+
+/*
+ * sparse_ffn_score -- per-neuron or per-cluster scores.
+ *  in   : fp32 [T][ld] (ld >= n).
+ *  SUM_ABS:  out = fp32 [n]; s_n = (accumulate ? s_n : 0) + |in[0][n]| + ... +
+ *            |in[T-1][n]|, added left to right in fp32 ([SelectInfer] §3,
+ *            Eq (1); the offline profiler's neuron score).
+ *  CLUSTER_MAX: out = uint32 [T][n / cluster]; out[t][c] = max over rows
+ *            c*cluster .. c*cluster+cluster-1 of (bits(in[t][row]) & 0x7FFFFFFF)
+ *            ([PowerInfer-2], "Neuron Cluster Decomposition": a cluster is a
+ *            block of S_c contiguous neurons); n % cluster == 0.
+ *  SOFTMAX_PICKED: picked = int32 [T][k] column indices (< n), out = fp32
+ *            [T][k]; out[t][j] = exp(in[t][p_j] - m) / sum_j' exp(in[t][p_j'] - m),
+ *            m = max_j in[t][p_j] (mixing weights of the routed experts).
+ *  `picked`/`k` are ignored by the other modes; `cluster`/`accumulate` are
+ *  ignored where they do not apply.
+ */
+sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
+                             int cluster, int accumulate,
+                             const int32_t* picked, int k,
+                             void* out, void* stream);
+
+/*
+ * sparse_ffn_select -- rank-range selection and compaction, one row at a time.
+ * For each row r < rows, the n entries of keys + r*ld are ordered by (key
+ * descending, index ascending) and the entries at ranks [r_lo, r_hi) are
+ * selected.  Top-k ([SelectInfer] §5 per-token top alpha and top beta by
+ * frequency, §4 top delta) is the range [0, k); the SpAx middle tier (Fig 2)
+ * is [k_top, k_top + k_mid).
+ *  nonzero_only : only entries with a nonzero key take part (ranks count
+ *                 among them); not allowed with SFFN_KEY_F32.
+ *  include_mask : nullable uint8 [n]; nonzero entries are OR-ed into every
+ *                 row's selection (union with a static set, [SelectInfer] §5).
+ *  mask_out     : nullable uint8 [rows][ld_mask], 1 = selected, 0 otherwise.
+ *  idx_out      : nullable int32 [rows][ld_idx]: selected indices, ascending.
+ *                 ld_idx >= n if include_mask is set, else >= r_hi - r_lo.
+ *  count_out    : nullable int32 [rows]: number selected.
+ *  freq_inout   : nullable uint32 [n]: += 1 for each row that selects the
+ *                 entry (the frequency count of [SelectInfer] §5).
+ * Limits: 1 <= n <= 32768, 0 <= r_lo <= r_hi, r_hi may exceed the number of
+ * eligible entries (then it is clipped).  The result is unique: bit-exact.
+ */
+sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld,
+                              int r_lo, int r_hi, int nonzero_only,
+                              const uint8_t* include_mask,
+                              uint8_t* mask_out, int ld_mask,
+                              int32_t* idx_out, int ld_idx,
+                              int32_t* count_out,
+                              uint32_t* freq_inout,
+                              void* stream);
+
+/*
+ * sparse_ffn_gemv -- activations and gathered products over weight rows.
+ * Rows processed: all n_rows rows when idx is NULL; otherwise, for
+ * i < min(*count, k_max) and g < group, row idx[i]*group + g (a cluster of
+ * `group` contiguous rows per index, [PowerInfer-2] "Neuron Cluster
+ * Decomposition"; group = 1 for single neurons).  Skipped rows are never
+ * read ([SelectInfer] §5 computes only the selected neurons).
+ *
+ * Row ops (GLU_SILU, DOT_RELU, GATED): W0, W1 are bf16 [n_rows][ld_w] with
+ *  rows of length d; in = x fp32 [batch][ld_in] (length d).  For each token
+ *  b and processed row n: out[b][n] = op value (see sffn_gemv_op) and, if
+ *  key_out is set, key_out[b][n] = bits(out) & 0x7FFFFFFF.  Entries of rows
+ *  not processed are left untouched.  ld_out >= n_rows.  silu(z) = z / (1 +
+ *  e^-z) as in the engine listing of [PowerInfer-2].  DOT_RELU uses W0 only
+ *  (tau = tau_scale * ||x_b||_2, tau_scale >= 0); GATED uses W1 and aux fp32
+ *  [batch][ld_aux] (aux_n read at processed rows only).
+ *
+ * AXPY: W0 is W_down^T, bf16 [n_rows][ld_w] with rows of length d (the
+ *  output width); in = activations fp32 [batch][ld_in] (length n_rows);
+ *  out[b][o] = (accumulate ? out[b][o] : 0) + alpha_b * sum over processed
+ *  rows n of m_bn * in[b][n] * W0[n][o], with m_bn = row_mask[b][n] != 0 if
+ *  row_mask (uint8 [batch][ld_mask]) is given, else 1, and alpha_b =
+ *  alpha[b] (device fp32) if given, else 1.  ld_out >= d.  The sum is
+ *  reduced in a fixed order: results are bitwise reproducible run to run.
+ *  Batch > 1 runs on MFMA (the gathered union as one dense block); the
+ *  masked-out products contribute exactly zero.
+ *
+ * Limits: d % 8 == 0 (d % 32 == 0 when batch > 1), ld_w % 8 == 0, W0/W1/in/
+ *  out 16-byte aligned, d <= 8192 for row ops at batch 1, 1 <= batch.
+ *  workspace: AXPY needs sparse_ffn_workspace_size(batch, rows, d) bytes
+ *  (rows = k_max*group or n_rows); row ops take none (may be NULL).
+ */
+sffn_status sparse_ffn_gemv(int op,
+                            const uint16_t* W0, const uint16_t* W1,
+                            int n_rows, int d, int ld_w,
+                            const float* in, int batch, int ld_in,
+                            const int32_t* idx, const int32_t* count, int k_max, int group,
+                            const uint8_t* row_mask, int ld_mask,
+                            float tau_scale,
+                            const float* aux, int ld_aux,
+                            const float* alpha,
+                            float* out, uint32_t* key_out, int ld_out, int accumulate,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Bytes of one middle-tier column record for d_out outputs in n_seg output
+ * segments: a 16-byte header holding n_seg pairs (fp16 scale, fp16 zero),
+ * then d_out/2 bytes of 4-bit codes (output 2i in the low nibble of byte i,
+ * output 2i+1 in the high nibble), rounded up to 16 bytes.  n_seg <= 4.
+ */
+size_t sparse_ffn_tier_record_bytes(int d_out, int n_seg);
+
+/*
+ * sparse_ffn_encode_tiers -- the offline SpAx encoding (Fig 2, Fig 3): each
+ * input column j (row j of W^T, bf16 [n_in][ld_w], length d_out) gets its
+ * own 4-bit uniform codes, one (scale, zero) per output segment
+ * [seg_rows[s], seg_rows[s+1]) (Q, K and V of Fig 4 are separate segments).
+ *   zero  = fp16(min w);  scale = fp16(fp32(max w - zero) / 15);
+ *   q     = clip(rint((w - zero) / scale), 0, 15) in fp32 (0 if scale == 0).
+ * seg_rows is a HOST array [n_seg+1], 0 = seg_rows[0] < ... < seg_rows[n_seg]
+ * = d_out, every boundary a multiple of 64.  mid_rec: uint8 [n_in][rec_bytes],
+ * rec_bytes >= sparse_ffn_tier_record_bytes(d_out, n_seg), multiple of 16.
+ */
+sffn_status sparse_ffn_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out,
+                                    const int32_t* seg_rows, int n_seg,
+                                    uint8_t* mid_rec, int rec_bytes, void* stream);
+
+/*
+ * sparse_ffn_tiered_gemv -- the SpAx three-tier read (abstract, Fig 2, Fig 3):
+ *   y = (accumulate ? y : 0) + sum_{j in top} W^T[j][:] x_j
+ *                             + sum_{j in mid} What^T[j][:] x_j,
+ *   What^T[j][o] = zero_j,s + scale_j,s * q_j,o  (s = segment of output o);
+ * columns in neither list are skipped and never read.  Wt bf16 [n_in][ld_w]
+ * (rows of length d_out), mid_rec as written by sparse_ffn_encode_tiers,
+ * x fp32 [n_in], y fp32 [d_out].  idx_top / idx_mid are the compacted
+ * column lists of the two tiers (e.g. select ranges [0, k_top) and
+ * [k_top, k_top + k_mid) of |x|), with device counts cnt_top / cnt_mid
+ * (min(*cnt, k_max) entries used).  seg_rows is a HOST array as for the
+ * encoder.  workspace: sparse_ffn_workspace_size(1, k_top_max + k_mid_max,
+ * d_out) bytes.
+ */
+sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w,
+                                   const uint8_t* mid_rec, int rec_bytes,
+                                   const int32_t* seg_rows, int n_seg,
+                                   int n_in, int d_out, const float* x,
+                                   const int32_t* idx_top, const int32_t* cnt_top, int k_top_max,
+                                   const int32_t* idx_mid, const int32_t* cnt_mid, int k_mid_max,
+                                   float* y, int accumulate,
+                                   void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_FFN_H */

@@ -1,0 +1,150 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry
+point the header declares, sizes buffers, and rejects bad arguments with
+the documented status before anything is launched (no GPU needed: every
+call below fails validation, so no kernel is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_ffn.h")
+LIB = os.path.join(ROOT, "activation_sparse_decode_amd", "libsparse_ffn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsparse_ffn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:sffn|sparse_ffn)_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from activation_sparse_decode_amd import binding
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
+
+
+def test_sizes(L):
+    from activation_sparse_decode_amd import binding as B
+    # record = 16-byte header + d_out/2 bytes of codes, rounded to 16 bytes
+    assert B.tier_record_bytes(6144, 3) == 16 + 3072
+    assert B.tier_record_bytes(4096, 1) == 16 + 2048
+    assert B.tier_record_bytes(100, 1) == 80
+    assert B.tier_record_bytes(4096, 5) == 0
+    assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
+    assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
+    assert L.sffn_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+NULL = None
+
+
+def status_and_msg(L, rc):
+    return rc, L.sffn_last_error().decode()
+
+
+def test_select_validation(L):
+    sel = L.sparse_ffn_select
+    rc, msg = status_and_msg(L, sel(NULL, 0, 1, 8, 8, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    assert rc == 1 and "keys" in msg
+    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 40000, 40000, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    assert rc == 2 and "32768" in msg
+    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 4, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    assert rc == 1 and "ld" in msg
+    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 8, 5, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    assert rc == 1 and "r_lo" in msg
+    rc, msg = status_and_msg(L, sel(FAKE, 2, 1, 8, 8, 0, 4, 1, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    assert rc == 1 and "signed" in msg
+    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 8, 0, 4, 0, NULL, NULL, 0, FAKE, 3, NULL, NULL, NULL))
+    assert rc == 1 and "ld_idx" in msg
+    # with a union mask the index list may hold up to n entries
+    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 8, 0, 4, 0, FAKE, NULL, 0, FAKE, 4, NULL, NULL, NULL))
+    assert rc == 1 and "ld_idx" in msg
+    rc, msg = status_and_msg(L, sel(FAKE, 7, 1, 8, 8, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    assert rc == 1 and "key type" in msg
+
+
+def gemv(L, op=3, W0=FAKE, W1=FAKE, n_rows=64, d=64, ld_w=64, inp=FAKE, batch=1, ld_in=64,
+         idx=NULL, count=NULL, k_max=0, group=1, mask=NULL, ld_mask=0, tau=0.0, aux=NULL,
+         ld_aux=0, alpha=NULL, out=FAKE, key=NULL, ld_out=64, acc=0, ws=NULL, ws_bytes=0):
+    rc = L.sparse_ffn_gemv(op, W0, W1, n_rows, d, ld_w, inp, batch, ld_in, idx, count, k_max,
+                           group, mask, ld_mask, ctypes.c_float(tau), aux, ld_aux, alpha, out, key,
+                           ld_out, acc, ws, ws_bytes, NULL)
+    return status_and_msg(L, rc)
+
+
+def test_gemv_validation(L):
+    assert gemv(L, op=9)[0] == 1
+    rc, msg = gemv(L, d=12)
+    assert rc == 1 and "multiple of 8" in msg
+    rc, msg = gemv(L, ld_w=60)
+    assert rc == 1 and "ld_w" in msg
+    rc, msg = gemv(L, batch=2, d=40, ld_w=40, ld_out=40)
+    assert rc == 2 and "d % 32" in msg
+    rc, msg = gemv(L, inp=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "aligned" in msg
+    rc, msg = gemv(L, idx=FAKE, count=NULL, k_max=4)
+    assert rc == 1 and "count" in msg
+    rc, msg = gemv(L, idx=FAKE, count=FAKE, k_max=3, group=32)
+    assert rc == 1 and "exceeds" in msg
+    rc, msg = gemv(L)                       # AXPY without a workspace
+    assert rc == 3 and "workspace" in msg
+    rc, msg = gemv(L, ws=FAKE, ws_bytes=100)
+    assert rc == 3
+    rc, msg = gemv(L, op=0, W1=NULL, ld_out=64)
+    assert rc == 1 and "W1" in msg
+    rc, msg = gemv(L, op=1, tau=-1.0, ld_out=64)
+    assert rc == 1 and "tau" in msg
+    rc, msg = gemv(L, op=2, W0=NULL, aux=NULL, ld_out=64)
+    assert rc == 1 and "aux" in msg
+    rc, msg = gemv(L, op=0, d=8200, ld_w=8200, ld_in=8200)
+    assert rc == 2 and "8192" in msg
+
+
+def test_score_validation(L):
+    sc = L.sparse_ffn_score
+    assert status_and_msg(L, sc(5, FAKE, 1, 8, 8, 1, 0, NULL, 0, FAKE, NULL))[0] == 1
+    rc, msg = status_and_msg(L, sc(1, FAKE, 1, 100, 100, 32, 0, NULL, 0, FAKE, NULL))
+    assert rc == 1 and "multiple" in msg
+    rc, msg = status_and_msg(L, sc(2, FAKE, 1, 8, 8, 1, 0, NULL, 2, FAKE, NULL))
+    assert rc == 1 and "picked" in msg
+    rc, msg = status_and_msg(L, sc(0, FAKE, 1, 8, 4, 1, 0, NULL, 0, FAKE, NULL))
+    assert rc == 1 and "ld" in msg
+
+
+def test_tier_validation(L):
+    seg = (ctypes.c_int32 * 4)(0, 4096, 5120, 6144)
+    bad = (ctypes.c_int32 * 4)(0, 4000, 5120, 6144)
+    enc = L.sparse_ffn_encode_tiers
+    rc, msg = status_and_msg(L, enc(FAKE, 6144, 16, 6144, bad, 3, FAKE, 3088, NULL))
+    assert rc == 1 and "multiple of 64" in msg
+    rc, msg = status_and_msg(L, enc(FAKE, 6144, 16, 6144, seg, 3, FAKE, 3072, NULL))
+    assert rc == 1 and "rec_bytes" in msg
+    rc, msg = status_and_msg(L, enc(FAKE, 6144, 16, 6144, seg, 5, FAKE, 3088, NULL))
+    assert rc == 2
+    tg = L.sparse_ffn_tiered_gemv
+    rc, msg = status_and_msg(L, tg(FAKE, 6144, FAKE, 3088, seg, 3, 4096, 6144, FAKE, FAKE, FAKE, 614,
+                                   NULL, NULL, 1433, FAKE, 0, FAKE, 1 << 30, NULL))
+    assert rc == 1 and "mid list" in msg
+    rc, msg = status_and_msg(L, tg(FAKE, 6144, FAKE, 3088, seg, 3, 4096, 6144, FAKE, FAKE, FAKE, 614,
+                                   FAKE, FAKE, 1433, FAKE, 0, FAKE, 64, NULL))
+    assert rc == 3 and "workspace" in msg
+
+
+def test_no_fallback_when_library_missing(monkeypatch):
+    from activation_sparse_decode_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", "/nonexistent/libsparse_ffn.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.lib()

@@ -1,0 +1,117 @@
+"""SpAx three-tier read (Llama3.1-8B QKV and down at full size): the 4-bit
+encoder is bit-exact with the oracle's, the tiers are bit-exact rank
+ranges of |x|, and the product is within tolerance of the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_decode_amd import binding as B
+from activation_sparse_decode_amd import synth
+from activation_sparse_decode_amd.pipelines import TieredProjection, pct_count
+from gpu_common import assert_close, banner, dev, gpu, host, needs_gpu
+
+pytestmark = [gpu, needs_gpu]
+
+CASES = {
+    "small": (512, 384, [0, 256, 320, 384]),
+    "qkv": (4096, 6144, [0, 4096, 5120, 6144]),
+    "down": (14336, 4096, [0, 4096]),
+}
+
+
+def make(name, seed=0):
+    n_in, n_out, seg = CASES[name]
+    t = synth.T_QKV if name != "down" else synth.T_DOWN
+    Wt = synth.weight_bf16(seed, synth.W_C2, 0, 0, t, n_in, n_out)
+    x = synth.tokens(seed, synth.W_C2, 1 + len(name), 1, n_in)[0]
+    return Wt, x, seg
+
+
+def unpack_records(rec: np.ndarray, n_out: int, n_seg: int):
+    hdr = rec[:, :16].copy().view(np.uint16)            # [n_in][8]
+    scale = hdr[:, 0:2 * n_seg:2].view(np.float16)
+    zero = hdr[:, 1:2 * n_seg:2].view(np.float16)
+    codes = rec[:, 16:16 + n_out // 2]
+    q = np.empty((rec.shape[0], n_out), dtype=np.uint8)
+    q[:, 0::2] = codes & 0x0F
+    q[:, 1::2] = codes >> 4
+    return scale, zero, q
+
+
+@pytest.mark.parametrize("name", ["small", "qkv", "down"])
+def test_tiered_stagewise(name):
+    banner(f"c2 {name}")
+    Wt, x, seg = make(name)
+    n_in, n_out = Wt.shape
+    k_top, k_mid = pct_count(15, n_in), pct_count(35, n_in)
+    proj = TieredProjection(dev(Wt), seg, k_top, k_mid)
+    y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+    proj(dev(x), y)
+    torch.cuda.synchronize()
+    scale, zero, q = unpack_records(host(proj.rec), n_out, len(seg) - 1)
+    o_scale, o_zero, o_q = oracle.encode_4bit(Wt, seg)
+    assert np.array_equal(scale.view(np.uint16), o_scale.view(np.uint16))
+    assert np.array_equal(zero.view(np.uint16), o_zero.view(np.uint16))
+    assert np.array_equal(q, o_q)
+    cnt = host(proj.cnt)
+    top, mid = host(proj.idx_top)[:cnt[0]], host(proj.idx_mid)[:cnt[1]]
+    o_top, o_mid = oracle.tier_sets(x, k_top, k_mid)
+    assert np.array_equal(top, o_top) and np.array_equal(mid, o_mid)
+    y_ref = oracle.tiered_gemv(Wt, o_scale, o_zero, o_q, seg, x, top, mid)
+    e = assert_close(host(y), y_ref, what="tiered product")
+    dense = oracle.widen_bf16(Wt).T @ x.astype(np.float64)
+    print(f"  err {e:.2e}; vs dense product {np.max(np.abs(host(y) - dense)) / np.sqrt(np.mean(dense**2)):.3f} (approximation, reported)")
+
+    # skipped columns are never read: poison their weights and records
+    skipped = np.setdiff1d(np.arange(n_in), np.concatenate([top, mid]))
+    Wp = Wt.copy()
+    Wp[skipped] = 0x7FC0
+    Wp[mid] = 0x7FC0                       # middle tier reads codes only
+    rec = host(proj.rec).copy()
+    rec[skipped] = 0xFF
+    rec[skipped, :16] = np.frombuffer(np.array([0x7E00] * 8, np.uint16).tobytes(), np.uint8)
+    rec[top] = 0xFF
+    y2 = torch.zeros_like(y)
+    B.sparse_ffn_tiered_gemv(dev(Wp), dev(rec), seg, dev(x), proj.idx_top, proj.cnt[0:1], k_top,
+                             proj.idx_mid, proj.cnt[1:2], k_mid, y2, workspace=proj.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+def test_tier_special_cases():
+    banner("c2 special cases")
+    Wt, x, seg = make("small", seed=3)
+    n_in, n_out = Wt.shape
+    xd = dev(x)
+    # all columns in the top tier: the dense product
+    proj = TieredProjection(dev(Wt), seg, n_in, 0)
+    y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+    proj(xd, y)
+    torch.cuda.synchronize()
+    assert_close(host(y), oracle.widen_bf16(Wt).T @ x.astype(np.float64), what="all top")
+    # k_mid = 0: the gathered product of the top columns
+    proj = TieredProjection(dev(Wt), seg, 100, 0)
+    proj(xd, y)
+    torch.cuda.synchronize()
+    top = oracle.tier_sets(x, 100, 0)[0]
+    assert_close(host(y), oracle.down_gather(Wt, top, x[top]), what="top only")
+    # weights on a 4-bit grid: the middle tier reproduces them exactly
+    rng = np.random.default_rng(4)
+    grid = np.zeros((n_in, n_out), np.float32)
+    for s in range(len(seg) - 1):
+        lo, hi = seg[s], seg[s + 1]
+        qq = rng.integers(0, 16, size=(n_in, hi - lo))
+        qq[:, 0], qq[:, 1] = 0, 15
+        grid[:, lo:hi] = -0.5 + 0.0625 * qq
+    Wg = synth.f32_to_bf16_bits(grid)
+    proj = TieredProjection(dev(Wg), seg, 0, n_in)
+    proj(xd, y)
+    torch.cuda.synchronize()
+    assert_close(host(y), grid.T.astype(np.float64) @ x.astype(np.float64), tol=1e-5, what="grid")
+    # empty tiers: y = 0
+    proj = TieredProjection(dev(Wt), seg, 0, 0)
+    y.fill_(5.0)
+    proj(xd, y)
+    torch.cuda.synchronize()
+    assert np.all(host(y) == 0.0)

@@ -1,0 +1,102 @@
+"""ReLU-sparse MoE stack (TurboSparse-Mixtral-like: 8 experts, 4096/14336,
+32 layers at full size, top-2 routing, 32-row clusters): routing, dense
+ReLU gate, cluster keys, active-cluster lists, gated up and the weighted
+down accumulation, against the oracle stage by stage."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_decode_amd import synth
+from activation_sparse_decode_amd.pipelines import ReluMoEStack, to_device_bf16
+from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
+
+pytestmark = [gpu, needs_gpu]
+
+QUANTILE = 1.2815515655446004      # Phi^-1(0.9): ~10% of gate pre-activations above tau
+CLUSTER = 32
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_moe(L, E, N, d, n_tokens, check_layers, on_device_weights, seed=0):
+    banner(f"c3 L={L} E={E} N={N} d={d} tokens={n_tokens}")
+    experts = []
+    for l in range(L):
+        row = []
+        for e in range(E):
+            if on_device_weights:
+                Wg = synth.torch_weight_bf16(seed, synth.W_C3, l, e, synth.T_GATE, N, d, "cuda",
+                                             cluster=CLUSTER)
+                Wu = synth.torch_weight_bf16(seed, synth.W_C3, l, e, synth.T_UP, N, d, "cuda")
+                WdT = synth.torch_weight_bf16(seed, synth.W_C3, l, e, synth.T_DOWN, N, d, "cuda")
+            else:
+                Wg = to_device_bf16(synth.clustered_gate_bf16(seed, synth.W_C3, l, e, N, d, CLUSTER))
+                Wu = to_device_bf16(synth.weight_bf16(seed, synth.W_C3, l, e, synth.T_UP, N, d))
+                WdT = to_device_bf16(synth.weight_bf16(seed, synth.W_C3, l, e, synth.T_DOWN, N, d))
+            row.append((Wg, Wu, WdT))
+        experts.append(row)
+    logits = synth.router_logits(seed, synth.W_C3, L, n_tokens, E)
+    X = synth.tokens(seed, synth.W_C3, 1, n_tokens, d)
+    moe = ReluMoEStack(experts, CLUSTER, tau_scale=QUANTILE * synth.WEIGHT_STD)
+    ex, w = moe.route(dev(logits))
+    torch.cuda.synchronize()
+    ex_h, w_h = host(ex), host(w)
+    for l in range(L):
+        for t in range(n_tokens):
+            o_ex, o_w = oracle.route_top2(logits[l, t])
+            assert np.array_equal(ex_h[l * n_tokens + t], o_ex)
+            assert np.max(np.abs(w_h[l * n_tokens + t] - o_w)) < 1e-6
+
+    stats = []
+    for t in range(n_tokens):
+        h = dev(X[t])
+        for l in range(L):
+            check = l in check_layers
+            h_in = host(h).copy() if check else None
+            got = {}
+
+            def record(ll, tt, hh, chosen):
+                if check:
+                    torch.cuda.synchronize()
+                    got["r"] = host(moe.r).copy()
+                    got["kappa"] = host_u32(moe.kappa).copy()
+                    got["cidx"] = host(moe.cidx).copy()
+                    got["ccnt"] = host(moe.ccnt).copy()
+                    got["a"] = host(moe.a).copy()
+                    got["chosen"] = list(chosen)
+
+            moe.layer(l, t, h, record=record)
+            if not check:
+                continue
+            torch.cuda.synchronize()
+            tau = oracle.relu_threshold(h_in, QUANTILE, synth.WEIGHT_STD)
+            y_ref = np.zeros(d)
+            for j, e in enumerate(got["chosen"]):
+                Wg, Wu, WdT = (host_bits(m) for m in experts[l][e])
+                r = got["r"][j]
+                assert_close(r, oracle.relu_gate(Wg, h_in, tau), what=f"r l={l} t={t} e={e}")
+                assert np.array_equal(got["kappa"][j], oracle.cluster_max_key(oracle.key_abs(r), CLUSTER))
+                clusters = oracle.active_clusters(r, CLUSTER)
+                n_c = int(got["ccnt"][j])
+                assert n_c == clusters.size and np.array_equal(got["cidx"][j][:n_c], clusters)
+                rows = oracle.expand_clusters(clusters, CLUSTER)
+                a = got["a"][j][rows]
+                a_ref = r[rows].astype(np.float64) * oracle.row_dots(Wu, h_in, rows)
+                assert_close(a, a_ref, what=f"a l={l} t={t} e={e}")
+                y_ref += float(w_h[l * n_tokens + t, j]) * oracle.down_gather(WdT, rows, a)
+                stats.append((np.mean(r > 0), n_c / (N // CLUSTER)))
+            assert_close(host(h) - h_in, y_ref, what=f"h update l={l} t={t}")
+    nz, act = np.mean([s[0] for s in stats]), np.mean([s[1] for s in stats])
+    print(f"  nonzero neurons {nz:.3f}, active clusters {act:.3f}")
+    assert 0.05 < nz < 0.15
+
+
+def test_small_moe():
+    run_moe(L=2, E=4, N=1024, d=256, n_tokens=3, check_layers={0, 1}, on_device_weights=False)
+
+
+def test_full_size_moe():
+    run_moe(L=32, E=8, N=14336, d=4096, n_tokens=2, check_layers={0, 31}, on_device_weights=True)

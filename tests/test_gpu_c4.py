@@ -1,0 +1,88 @@
+"""Batched decode (Qwen-27B-like layer at full size, batch 1/4/8/16):
+per-token top-k, union gathered once, MFMA contraction with per-token
+masks, against the oracle stage by stage."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_decode_amd import binding as B
+from activation_sparse_decode_amd import synth
+from activation_sparse_decode_amd.pipelines import BatchedUnionLayer, pct_count
+from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
+
+pytestmark = [gpu, needs_gpu]
+
+
+def make(N, d, batch, seed=0):
+    Wg = synth.weight_bf16(seed, synth.W_C4, 0, 0, synth.T_GATE, N, d)
+    Wu = synth.weight_bf16(seed, synth.W_C4, 0, 0, synth.T_UP, N, d)
+    WdT = synth.weight_bf16(seed, synth.W_C4, 0, 0, synth.T_DOWN, N, d)
+    X = synth.tokens(seed, synth.W_C4, batch, batch, d)
+    return Wg, Wu, WdT, X
+
+
+def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None):
+    Wg, Wu, WdT, X = make(N, d, batch, seed)
+    keep = pct_count(pct, N)
+    layer = BatchedUnionLayer(dev(Wg), dev(Wu), dev(WdT), keep, batch)
+    Y = torch.zeros(batch, d, dtype=torch.float32, device="cuda")
+    layer(dev(X), Y)
+    torch.cuda.synchronize()
+    A = host(layer.A)
+    K = host_u32(layer.K)
+    M = host(layer.M)
+    F = host_u32(layer.F)
+    cnt = int(host(layer.cnt)[0])
+    U = host(layer.U)[:cnt]
+    toks = range(batch) if sample_tokens is None else sample_tokens
+    for b in toks:
+        assert_close(A[b], oracle.swiglu_acts(Wg, Wu, X[b]), what=f"activations b={b}")
+    S = []
+    for b in range(batch):
+        assert np.array_equal(K[b], oracle.key_abs(A[b]))
+        s = oracle.rank_range(oracle.key_abs(A[b]), 0, keep)
+        m = np.zeros(N, np.uint8)
+        m[s] = 1
+        assert np.array_equal(M[b], m), b
+        S.append(s)
+    U_ref = oracle.union(*S)
+    assert np.array_equal(U, U_ref)
+    assert np.array_equal(F, np.bincount(np.concatenate(S), minlength=N).astype(np.uint32))
+    for b in toks:
+        y_ref = oracle.down_gather(WdT, S[b], A[b][S[b]])
+        assert_close(host(Y[b]), y_ref, what=f"output b={b}")
+    print(f"  union {cnt} of {N} ({cnt / N:.3f})")
+    return layer, Y
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8, 16, 19])
+def test_small_shapes(batch):
+    banner(f"c4 small batch={batch}")
+    run_and_check(1000, 256, batch, 40, seed=batch)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 8, 16])
+def test_full_size(batch):
+    banner(f"c4 full batch={batch}")
+    run_and_check(17408, 5120, batch, 40, sample_tokens=[0, batch - 1])
+
+
+def test_mfma_dense_prefill_shape():
+    """The dense batched path used by prefill / calibration (M = 256 tokens,
+    no index list), against a plain fp64 product."""
+    banner("c4 dense M=256")
+    N, d, T = 1024, 512, 256
+    Wg, Wu, WdT, _ = make(N, d, 1, seed=9)
+    X = synth.tokens(9, synth.W_C4, 77, T, d)
+    A = torch.zeros(T, N, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_gemv(B.OP_GLU_SILU, dev(Wg), dev(Wu), dev(X), A)
+    H = dev(X).clone()
+    ws = B.new_workspace(T, N, d)
+    B.sparse_ffn_gemv(B.OP_AXPY, dev(WdT), None, A, H, accumulate=True, workspace=ws)
+    torch.cuda.synchronize()
+    A_ref, Y_ref = oracle.dense_ffn(Wg, Wu, WdT, X)
+    for t in (0, 100, 255):
+        assert_close(host(A[t]), oracle.swiglu_acts(Wg, Wu, X[t]), what=f"A[{t}]")
+        y_ref = oracle.widen_bf16(WdT).T @ host(A[t]).astype(np.float64)
+        assert_close(host(H[t]) - X[t], y_ref, what=f"H[{t}]")
