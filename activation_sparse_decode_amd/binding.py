@@ -57,13 +57,13 @@ def lib() -> ctypes.CDLL:
                                         _vp, _vp, _vp]
         L.sparse_ffn_gemv.restype = _i
         L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
-                                      _vp, _i, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
+                                      _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
         L.sparse_ffn_encode_tiers.restype = _i
         L.sparse_ffn_encode_tiers.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 1:
+        if L.sffn_abi_version() != 2:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -130,6 +130,7 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
                     inp: torch.Tensor, out: torch.Tensor, *, idx: torch.Tensor | None = None,
                     count: torch.Tensor | None = None, k_max: int = 0, group: int = 1,
                     row_mask: torch.Tensor | None = None, tau_scale: float = 0.0,
+                    rms_eps: float = 0.0,
                     aux: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
                     key_out: torch.Tensor | None = None, accumulate: bool = False,
                     workspace: torch.Tensor | None = None, stream=None) -> None:
@@ -142,7 +143,7 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib().sparse_ffn_gemv(
         op, _p(W0), _p(W1), n_rows, d, ld_w, _p(inp), batch, ld_in, _p(idx), _p(count),
-        k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), _p(aux),
+        k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), float(rms_eps), _p(aux),
         _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
 

@@ -128,7 +128,7 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
 sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int n_rows, int d,
                             int ld_w, const float* in, int batch, int ld_in, const int32_t* idx,
                             const int32_t* count, int k_max, int group, const uint8_t* row_mask,
-                            int ld_mask, float tau_scale, const float* aux, int ld_aux,
+                            int ld_mask, float tau_scale, float rms_eps, const float* aux, int ld_aux,
                             const float* alpha, float* out, uint32_t* key_out, int ld_out,
                             int accumulate, void* workspace, size_t ws_bytes, void* stream) {
   REQUIRE(op >= 0 && op <= 3, SFFN_EINVAL, "gemv: unknown op %d", op);
@@ -160,6 +160,8 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     REQUIRE(ld_in >= d, SFFN_EINVAL, "gemv: ld_in=%d < d=%d", ld_in, d);
     REQUIRE(ld_out >= n_rows, SFFN_EINVAL, "gemv: ld_out=%d < n_rows=%d", ld_out, n_rows);
     REQUIRE(batch > 1 || d <= 8192, SFFN_EUNSUPPORTED, "gemv: d=%d > 8192 at batch 1", d);
+    REQUIRE(rms_eps >= 0.f && std::isfinite(rms_eps), SFFN_EINVAL,
+            "gemv: rms_eps must be finite and >= 0");
     if (op == SFFN_OP_DOT_RELU)
       REQUIRE(tau_scale >= 0.f && std::isfinite(tau_scale), SFFN_EINVAL,
               "gemv: tau_scale must be finite and >= 0");
@@ -170,12 +172,14 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     if (key_out) REQUIRE(aligned(key_out, 4), SFFN_EINVAL, "gemv: key_out misaligned");
     if (items == 0) return ok();
     sffn::RowOpArgs a{op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max,
-                      idx ? group : 1, tau_scale, aux, ld_aux, out, key_out, ld_out};
+                      idx ? group : 1, tau_scale, rms_eps, aux, ld_aux, out, key_out,
+                      ld_out};
     return from_hip(batch == 1 ? sffn::launch_rowop_b1(a, s) : sffn::launch_rowop_mfma(a, s),
                     "gemv launch");
   }
 
   REQUIRE(W0 && aligned(W0, 16), SFFN_EINVAL, "gemv: W0 must be non-null and 16-byte aligned");
+  REQUIRE(rms_eps == 0.f, SFFN_EINVAL, "gemv: AXPY takes no input normalisation (rms_eps must be 0)");
   REQUIRE(ld_in >= n_rows, SFFN_EINVAL, "gemv: ld_in=%d < n_rows=%d", ld_in, n_rows);
   REQUIRE(ld_out >= d, SFFN_EINVAL, "gemv: ld_out=%d < d=%d", ld_out, d);
   if (row_mask) REQUIRE(ld_mask >= n_rows, SFFN_EINVAL, "gemv: ld_mask=%d < n_rows=%d", ld_mask,

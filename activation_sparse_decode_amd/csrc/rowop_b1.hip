@@ -47,14 +47,18 @@ __global__ __launch_bounds__(256) void rowop_b1_kernel(RowOpArgs a) {
     }
   }
 
-  float tau = 0.f;
-  if (OP == kOpDotRelu) {
+  // Optional unit-gain RMSNorm of the input, applied to the dot products
+  // (W.(x s) = s (W.x)); tau is taken on the normalised input.
+  float tau = 0.f, inv = 1.f;
+  if (OP == kOpDotRelu || a.rms_eps > 0.f) {
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) s = fmaf(xr[j][e], xr[j][e], s);
-    tau = a.tau_scale * sqrtf(wave_sum(s));
+    s = wave_sum(s);
+    if (a.rms_eps > 0.f) inv = 1.f / sqrtf(s / (float)a.d + a.rms_eps);
+    tau = a.tau_scale * sqrtf(s) * inv;
   }
 
   for (int base = wave * NPI; base < n_items; base += nwaves * NPI) {
@@ -106,8 +110,8 @@ __global__ __launch_bounds__(256) void rowop_b1_kernel(RowOpArgs a) {
           for (int e = 0; e < 8; ++e) s1 = fmaf(f[e], xr[j][e], s1);
         }
       }
-      acc0[i] = (OP != kOpGated) ? wave_sum(s0) : 0.f;
-      acc1[i] = (OP != kOpDotRelu) ? wave_sum(s1) : 0.f;
+      acc0[i] = (OP != kOpGated) ? wave_sum(s0) * inv : 0.f;
+      acc1[i] = (OP != kOpDotRelu) ? wave_sum(s1) * inv : 0.f;
     }
 
 #pragma unroll

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
       p = *reinterpret_cast<const float4*>(xp + k);
       q = *reinterpret_cast<const float4*>(xp + k + 4);
     }
-    if (OP == kOpDotRelu) {
+    {
       sq = fmaf(p.x, p.x, sq); sq = fmaf(p.y, p.y, sq); sq = fmaf(p.z, p.z, sq); sq = fmaf(p.w, p.w, sq);
       sq = fmaf(q.x, q.x, sq); sq = fmaf(q.y, q.y, sq); sq = fmaf(q.z, q.z, sq); sq = fmaf(q.w, q.w, sq);
     }
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
 
   red[0][w][lane] = acc0;
   red[1][w][lane] = acc1;
-  if (OP == kOpDotRelu) {
+  {
     // lanes nl, nl+16, nl+32, nl+48 hold token nl's squares over this wave's K range
     sq += __shfl_xor(sq, 16, kWave);
     sq += __shfl_xor(sq, 32, kWave);
@@ -139,15 +139,17 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
     const int m = 4 * g + i;
     const int b = m0 + m;
     if (b >= a.batch) continue;
+    // optional unit-gain RMSNorm of token b's input, applied to the dot products
+    const float ss = sq_red[0][m] + sq_red[1][m] + sq_red[2][m] + sq_red[3][m];
+    const float inv = a.rms_eps > 0.f ? 1.f / sqrtf(ss / (float)a.d + a.rms_eps) : 1.f;
     float v;
     if (OP == kOpGlu) {
-      const float gg = s0[i];
-      v = (gg / (1.f + expf(-gg))) * s1[i];
+      const float gg = s0[i] * inv;
+      v = (gg / (1.f + expf(-gg))) * (s1[i] * inv);
     } else if (OP == kOpDotRelu) {
-      const float nrm = sqrtf(sq_red[0][m] + sq_red[1][m] + sq_red[2][m] + sq_red[3][m]);
-      v = fmaxf(s0[i] - a.tau_scale * nrm, 0.f);
+      v = fmaxf(s0[i] * inv - a.tau_scale * sqrtf(ss) * inv, 0.f);
     } else {
-      v = a.aux[(size_t)b * a.ld_aux + row] * s1[i];
+      v = a.aux[(size_t)b * a.ld_aux + row] * (s1[i] * inv);
     }
     a.out[(size_t)b * a.ld_out + row] = v;
     if (a.key_out) a.key_out[(size_t)b * a.ld_out + row] = key_abs(v);

@@ -73,7 +73,7 @@ struct RowOpArgs {
   int n_rows, d, ld_w;
   const float* x; int batch, ld_in;
   const int32_t* idx; const int32_t* count; int k_max, group;
-  float tau_scale;
+  float tau_scale, rms_eps;
   const float* aux; int ld_aux;
   float* out; uint32_t* key_out; int ld_out;
 };

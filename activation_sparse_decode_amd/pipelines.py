@@ -25,6 +25,11 @@ from . import binding as B
 
 F32, I32, U8 = torch.float32, torch.int32, torch.uint8
 
+# The stacked workloads normalise the residual stream before each FFN, as the
+# Llama3 / Mixtral blocks they are shaped like do (unit gain, eps of those
+# models); the single-layer workloads feed the token to the FFN directly.
+RMS_EPS = 1e-5
+
 
 def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     """bf16 bit patterns (numpy uint16) -> int16 device tensor (same bits)."""
@@ -59,13 +64,15 @@ class SwigluSparseLayer:
 
 
 class SelectInferStack:
-    """A residual stack of SwiGLU FFN layers, h <- h + FFN_l(h), run the
+    """A residual stack of SwiGLU FFN layers, h <- h + FFN_l(norm(h)), run the
     SelectInfer way: dense calibration and prefill, sparse decode over
     U_l = base_l (top delta by Eq (1)) union dynamic_l (top beta by how often
     a neuron is in a prompt token's top alpha)."""
 
-    def __init__(self, layers, base_k: int, alpha_k: int, beta_k: int, max_tokens: int = 512):
+    def __init__(self, layers, base_k: int, alpha_k: int, beta_k: int, max_tokens: int = 512,
+                 rms_eps: float = RMS_EPS):
         self.layers = layers
+        self.rms_eps = rms_eps
         self.L = len(layers)
         N, d = layers[0][0].shape
         self.N, self.d = N, d
@@ -87,7 +94,8 @@ class SelectInferStack:
         Wg, Wu, WdT = self.layers[l]
         T = H.shape[0]
         A, K = self.A[:T], self.K[:T]
-        B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, H, A, key_out=K if keys else None)
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, H, A, key_out=K if keys else None,
+                          rms_eps=self.rms_eps)
 
     def _dense_residual(self, l: int, H: torch.Tensor) -> None:
         T = H.shape[0]
@@ -131,7 +139,7 @@ class SelectInferStack:
         if timer is not None:
             timer.begin()
         B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, h, self.a[l], idx=idx, count=cnt,
-                          k_max=self.k_max)
+                          k_max=self.k_max, rms_eps=self.rms_eps)
         if timer is not None:
             timer.end()
         B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[l], h, idx=idx, count=cnt,
@@ -175,10 +183,12 @@ class ReluMoEStack:
     Per layer and token: top-2 experts by router logit (softmax mixing
     weights); per routed expert r = max(W_g h - tau, 0) densely, the clusters
     of 32 rows holding a nonzero r, then up and down over those clusters
-    only; h <- h + sum_e w_e y_e."""
+    only; h <- h + sum_e w_e y_e (the expert input is norm(h))."""
 
-    def __init__(self, experts, cluster: int, tau_scale: float, top_k: int = 2):
+    def __init__(self, experts, cluster: int, tau_scale: float, top_k: int = 2,
+                 rms_eps: float = RMS_EPS):
         self.experts = experts           # [L][E] of (Wg, Wu, WdT)
+        self.rms_eps = rms_eps
         self.L, self.E = len(experts), len(experts[0])
         N, d = experts[0][0][0].shape
         self.N, self.d, self.cluster, self.tau_scale, self.top_k = N, d, cluster, tau_scale, top_k
@@ -209,13 +219,14 @@ class ReluMoEStack:
         chosen = self.route_host[row]
         for j, e in enumerate(chosen):
             Wg, Wu, _ = self.experts[l][e]
-            B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j], tau_scale=self.tau_scale)
+            B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j], tau_scale=self.tau_scale,
+                              rms_eps=self.rms_eps)
             B.sparse_ffn_score(B.SCORE_CLUSTER_MAX, self.r[j], self.kappa[j], cluster=self.cluster)
             B.sparse_ffn_select(self.kappa[j], B.KEY_U32, 0, self.nc, nonzero_only=True,
                                 idx_out=self.cidx[j], count_out=self.ccnt[j:j + 1])
             B.sparse_ffn_gemv(B.OP_GATED, None, Wu, h, self.a[j], idx=self.cidx[j],
                               count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
-                              aux=self.r[j])
+                              aux=self.r[j], rms_eps=self.rms_eps)
         if record is not None:
             record(l, t, h, chosen)
         for j, e in enumerate(chosen):

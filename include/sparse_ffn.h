@@ -87,7 +87,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 1
+#define SFFN_ABI_VERSION 2
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -159,7 +159,11 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
  *  not processed are left untouched.  ld_out >= n_rows.  silu(z) = z / (1 +
  *  e^-z) as in the engine listing of [PowerInfer-2].  DOT_RELU uses W0 only
  *  (tau = tau_scale * ||x_b||_2, tau_scale >= 0); GATED uses W1 and aux fp32
- *  [batch][ld_aux] (aux_n read at processed rows only).
+ *  [batch][ld_aux] (aux_n read at processed rows only).  If rms_eps > 0 the
+ *  row ops read each token through a unit-gain RMSNorm, x_b <- x_b /
+ *  sqrt(mean(x_b^2) + rms_eps) (the pre-FFN normalisation of the Llama3 and
+ *  Mixtral blocks the workloads are shaped like; fused, x is not modified);
+ *  rms_eps = 0 uses x as given.  AXPY requires rms_eps = 0.
  *
  * AXPY: W0 is W_down^T, bf16 [n_rows][ld_w] with rows of length d (the
  *  output width); in = activations fp32 [batch][ld_in] (length n_rows);
@@ -182,7 +186,7 @@ sffn_status sparse_ffn_gemv(int op,
                             const float* in, int batch, int ld_in,
                             const int32_t* idx, const int32_t* count, int k_max, int group,
                             const uint8_t* row_mask, int ld_mask,
-                            float tau_scale,
+                            float tau_scale, float rms_eps,
                             const float* aux, int ld_aux,
                             const float* alpha,
                             float* out, uint32_t* key_out, int ld_out, int accumulate,

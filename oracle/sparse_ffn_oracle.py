@@ -153,6 +153,18 @@ def swiglu_acts(Wg_bits, Wu_bits, x, rows=None) -> np.ndarray:
     return silu(row_dots(Wg_bits, x, rows)) * row_dots(Wu_bits, x, rows)
 
 
+def rms_normalize(h: np.ndarray, eps: float) -> np.ndarray:
+    """Unit-gain RMSNorm of an FFN input: h / sqrt(mean(h^2) + eps), fp64.
+
+    The pages describe the FFN alone; the stacked workloads are shaped like
+    Llama3 / Mixtral blocks, which normalise the residual stream before the
+    FFN.  Without it a residual stack of FFNs (each quadratic in its input)
+    overflows within a few layers, so the stacks read their FFN input
+    through this normalisation (the reading taken; gain 1)."""
+    h = np.asarray(h, dtype=np.float64)
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+
+
 def down_gather(WdT_bits: np.ndarray, rows: np.ndarray, a_rows: np.ndarray) -> np.ndarray:
     """y = sum over selected neurons n of a_n * W_down^T[n]  (fp64).
 

@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 1
+    assert L.sffn_abi_version() == 2
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -76,10 +76,10 @@ def test_select_validation(L):
 
 
 def gemv(L, op=3, W0=FAKE, W1=FAKE, n_rows=64, d=64, ld_w=64, inp=FAKE, batch=1, ld_in=64,
-         idx=NULL, count=NULL, k_max=0, group=1, mask=NULL, ld_mask=0, tau=0.0, aux=NULL,
+         idx=NULL, count=NULL, k_max=0, group=1, mask=NULL, ld_mask=0, tau=0.0, eps=0.0, aux=NULL,
          ld_aux=0, alpha=NULL, out=FAKE, key=NULL, ld_out=64, acc=0, ws=NULL, ws_bytes=0):
     rc = L.sparse_ffn_gemv(op, W0, W1, n_rows, d, ld_w, inp, batch, ld_in, idx, count, k_max,
-                           group, mask, ld_mask, ctypes.c_float(tau), aux, ld_aux, alpha, out, key,
+                           group, mask, ld_mask, ctypes.c_float(tau), ctypes.c_float(eps), aux, ld_aux, alpha, out, key,
                            ld_out, acc, ws, ws_bytes, NULL)
     return status_and_msg(L, rc)
 
@@ -110,6 +110,10 @@ def test_gemv_validation(L):
     assert rc == 1 and "aux" in msg
     rc, msg = gemv(L, op=0, d=8200, ld_w=8200, ld_in=8200)
     assert rc == 2 and "8192" in msg
+    rc, msg = gemv(L, op=0, eps=-1.0)
+    assert rc == 1 and "rms_eps" in msg
+    rc, msg = gemv(L, op=3, eps=1e-5, ws=FAKE, ws_bytes=1 << 30)
+    assert rc == 1 and "rms_eps" in msg
 
 
 def test_score_validation(L):

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from activation_sparse_decode_amd import synth
-from activation_sparse_decode_amd.pipelines import SelectInferStack, pct_count, to_device_bf16
+from activation_sparse_decode_amd.pipelines import RMS_EPS, SelectInferStack, pct_count, to_device_bf16
 from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
 
 pytestmark = [gpu, needs_gpu]
@@ -39,7 +39,8 @@ def run_stack(L, N, d, n_calib, n_prompt, n_decode, check_layers, check_tokens, 
         Wg, Wu, WdT = layers[l]
         H, A = seen[("c", l)]
         for t in (0, n_calib // 2, n_calib - 1):
-            assert_close(A[t], oracle.swiglu_acts(Wg, Wu, H[t]), what=f"calib A l={l} t={t}")
+            x = oracle.rms_normalize(H[t], RMS_EPS)
+            assert_close(A[t], oracle.swiglu_acts(Wg, Wu, x), what=f"calib A l={l} t={t}")
         s_ref, base_ref = oracle.base_set(A, base_k)
         assert np.array_equal(scores[l].view(np.uint32), s_ref.view(np.uint32)), l
         assert np.array_equal(np.flatnonzero(base_mask[l]), base_ref), l
@@ -56,8 +57,8 @@ def run_stack(L, N, d, n_calib, n_prompt, n_decode, check_layers, check_tokens, 
     for l in check_layers:
         Wg, Wu, WdT = layers[l]
         H, A = seen[("p", l)]
-        assert_close(A[n_prompt - 1], oracle.swiglu_acts(Wg, Wu, H[n_prompt - 1]),
-                     what=f"prompt A l={l}")
+        x = oracle.rms_normalize(H[n_prompt - 1], RMS_EPS)
+        assert_close(A[n_prompt - 1], oracle.swiglu_acts(Wg, Wu, x), what=f"prompt A l={l}")
         counts, dyn = oracle.dynamic_set(A, alpha_k, beta_k)
         assert np.array_equal(freq[l], counts.astype(np.uint32)), l
         U_ref = oracle.union(np.flatnonzero(base_mask[l]), dyn)
@@ -75,7 +76,8 @@ def run_stack(L, N, d, n_calib, n_prompt, n_decode, check_layers, check_tokens, 
                 Wg, Wu, WdT = layers[l]
                 U = U_idx[l, :U_cnt[l]]
                 a = host(stack.a[l])[U]
-                assert_close(a, oracle.swiglu_acts(Wg, Wu, h_in, U), what=f"decode a t={t} l={l}")
+                x = oracle.rms_normalize(h_in, RMS_EPS)
+                assert_close(a, oracle.swiglu_acts(Wg, Wu, x, U), what=f"decode a t={t} l={l}")
                 y_ref = oracle.down_gather(WdT, U, a)
                 assert_close(host(h) - h_in, y_ref, what=f"decode y t={t} l={l}")
     torch.cuda.synchronize()
@@ -90,3 +92,35 @@ def test_small_stack():
 def test_full_size_stack():
     run_stack(L=28, N=8192, d=3072, n_calib=512, n_prompt=256, n_decode=128,
               check_layers={0, 13, 27}, check_tokens={0, 127})
+
+
+def test_decode_graph_replays_match_eager():
+    """The decode step captured as a HIP graph gives, on every replay, the
+    bits the eager calls give (all reductions run in a fixed order)."""
+    banner("c1 graph replay")
+    L, N, d = 4, 1024, 512
+    layers = synth.ffn_stack(5, synth.W_C1, L, N, d)
+    dev_layers = [tuple(to_device_bf16(m) for m in lay) for lay in layers]
+    stack = SelectInferStack(dev_layers, pct_count(20, N), pct_count(30, N), pct_count(20, N),
+                             max_tokens=64)
+    stack.calibrate(dev(synth.tokens(5, synth.W_C1, 1, 64, d)))
+    stack.prefill(dev(synth.tokens(5, synth.W_C1, 2, 32, d)))
+    X = dev(synth.tokens(5, synth.W_C1, 3, 6, d))
+    eager = []
+    for t in range(6):
+        h = X[t].clone()
+        stack.decode(h)
+        eager.append(host(h))
+    h = torch.zeros(d, dtype=torch.float32, device="cuda")
+    xcur = torch.zeros(d, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.copy_(xcur)
+        stack.decode(h)
+    for rep in range(3):
+        for t in range(6):
+            xcur.copy_(X[t])
+            g.replay()
+            got = host(h)          # synchronizes between replays
+            assert np.array_equal(got.view(np.uint32), eager[t].view(np.uint32)), (rep, t)

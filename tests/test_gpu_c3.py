@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from activation_sparse_decode_amd import synth
-from activation_sparse_decode_amd.pipelines import ReluMoEStack, to_device_bf16
+from activation_sparse_decode_amd.pipelines import RMS_EPS, ReluMoEStack, to_device_bf16
 from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
 
 pytestmark = [gpu, needs_gpu]
@@ -72,19 +72,20 @@ def run_moe(L, E, N, d, n_tokens, check_layers, on_device_weights, seed=0):
             if not check:
                 continue
             torch.cuda.synchronize()
-            tau = oracle.relu_threshold(h_in, QUANTILE, synth.WEIGHT_STD)
+            x = oracle.rms_normalize(h_in, RMS_EPS)
+            tau = oracle.relu_threshold(x, QUANTILE, synth.WEIGHT_STD)
             y_ref = np.zeros(d)
             for j, e in enumerate(got["chosen"]):
                 Wg, Wu, WdT = (host_bits(m) for m in experts[l][e])
                 r = got["r"][j]
-                assert_close(r, oracle.relu_gate(Wg, h_in, tau), what=f"r l={l} t={t} e={e}")
+                assert_close(r, oracle.relu_gate(Wg, x, tau), what=f"r l={l} t={t} e={e}")
                 assert np.array_equal(got["kappa"][j], oracle.cluster_max_key(oracle.key_abs(r), CLUSTER))
                 clusters = oracle.active_clusters(r, CLUSTER)
                 n_c = int(got["ccnt"][j])
                 assert n_c == clusters.size and np.array_equal(got["cidx"][j][:n_c], clusters)
                 rows = oracle.expand_clusters(clusters, CLUSTER)
                 a = got["a"][j][rows]
-                a_ref = r[rows].astype(np.float64) * oracle.row_dots(Wu, h_in, rows)
+                a_ref = r[rows].astype(np.float64) * oracle.row_dots(Wu, x, rows)
                 assert_close(a, a_ref, what=f"a l={l} t={t} e={e}")
                 y_ref += float(w_h[l * n_tokens + t, j]) * oracle.down_gather(WdT, rows, a)
                 stats.append((np.mean(r > 0), n_c / (N // CLUSTER)))

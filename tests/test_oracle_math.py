@@ -171,3 +171,19 @@ def test_eq2_example():
 def test_cluster_storage_example():
     # PowerInfer-2 guide: 64 INT4 neurons x 4096 x 0.5 bytes = 131,072 bytes = 128 KB
     assert oracle.packed_bytes(64, 4096, 4) == 131072
+
+
+# ------------------------------------------------------------------ FFN input normalisation
+
+def test_rms_normalize_closed_forms():
+    # [3, 4]: mean square 12.5, so the result is [3, 4] / sqrt(12.5)
+    got = oracle.rms_normalize(np.array([3.0, 4.0]), 0.0)
+    assert got.tolist() == pytest.approx([3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rel=1e-15)
+    rng = np.random.default_rng(16)
+    h = rng.standard_normal((3, 257)) * 40.0
+    n = oracle.rms_normalize(h, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(n ** 2, axis=-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.rms_normalize(7.0 * h, 0.0), n, rtol=1e-14)   # scale-free
+    # eps only matters for small inputs: h = 0 stays 0, tiny h is damped
+    assert np.all(oracle.rms_normalize(np.zeros(5), 1e-5) == 0.0)
+    assert oracle.rms_normalize(np.full(4, 1e-3), 1e-5)[0] == pytest.approx(1e-3 / math.sqrt(1e-6 + 1e-5))
