@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_
 SFFN_OK, SFFN_EINVAL, SFFN_EUNSUPPORTED, SFFN_EWORKSPACE, SFFN_EHIP = range(5)
 KEY_ABS_F32, KEY_U32, KEY_F32 = 0, 1, 2
 SCORE_SUM_ABS, SCORE_CLUSTER_MAX, SCORE_SOFTMAX_PICKED = 0, 1, 2
-OP_GLU_SILU, OP_DOT_RELU, OP_GATED, OP_AXPY = 0, 1, 2, 3
+OP_GLU_SILU, OP_DOT_RELU, OP_GATED, OP_AXPY, OP_DOT = 0, 1, 2, 3, 4
 
 _STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
 
@@ -58,12 +58,14 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_gemv.restype = _i
         L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
                                       _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
+        L.sparse_ffn_compact.restype = _i
+        L.sparse_ffn_compact.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp]
         L.sparse_ffn_encode_tiers.restype = _i
         L.sparse_ffn_encode_tiers.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 2:
+        if L.sffn_abi_version() != 3:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -146,6 +148,12 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
         k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), float(rms_eps), _p(aux),
         _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_ffn_compact(W: torch.Tensor, idx: torch.Tensor | None, k: int, transpose: bool,
+                       out: torch.Tensor, stream=None) -> None:
+    _check(lib().sparse_ffn_compact(_p(W), W.shape[0], W.shape[1], W.stride(0), _p(idx), k,
+                                    int(transpose), _p(out), out.stride(0), _stream(stream)))
 
 
 def _seg_array(seg_rows):

@@ -131,7 +131,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                             int ld_mask, float tau_scale, float rms_eps, const float* aux, int ld_aux,
                             const float* alpha, float* out, uint32_t* key_out, int ld_out,
                             int accumulate, void* workspace, size_t ws_bytes, void* stream) {
-  REQUIRE(op >= 0 && op <= 3, SFFN_EINVAL, "gemv: unknown op %d", op);
+  REQUIRE(op >= 0 && op <= 4, SFFN_EINVAL, "gemv: unknown op %d", op);
   REQUIRE(in && out, SFFN_EINVAL, "gemv: in and out must be non-null");
   REQUIRE(n_rows >= 0, SFFN_EINVAL, "gemv: n_rows=%d must be >= 0", n_rows);
   REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "gemv: d=%d must be a positive multiple of 8", d);
@@ -155,7 +155,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
   if (op != SFFN_OP_AXPY) {
     if (op != SFFN_OP_GATED)
       REQUIRE(W0 && aligned(W0, 16), SFFN_EINVAL, "gemv: W0 must be non-null and 16-byte aligned");
-    if (op != SFFN_OP_DOT_RELU)
+    if (op == SFFN_OP_GLU_SILU || op == SFFN_OP_GATED)
       REQUIRE(W1 && aligned(W1, 16), SFFN_EINVAL, "gemv: W1 must be non-null and 16-byte aligned");
     REQUIRE(ld_in >= d, SFFN_EINVAL, "gemv: ld_in=%d < d=%d", ld_in, d);
     REQUIRE(ld_out >= n_rows, SFFN_EINVAL, "gemv: ld_out=%d < n_rows=%d", ld_out, n_rows);
@@ -173,7 +173,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     if (items == 0) return ok();
     sffn::RowOpArgs a{op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max,
                       idx ? group : 1, tau_scale, rms_eps, aux, ld_aux, out, key_out,
-                      ld_out};
+                      ld_out, accumulate ? 1 : 0};
     return from_hip(batch == 1 ? sffn::launch_rowop_b1(a, s) : sffn::launch_rowop_mfma(a, s),
                     "gemv launch");
   }
@@ -196,6 +196,25 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                    row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes};
   return from_hip(batch == 1 ? sffn::launch_axpy_b1(a, s) : sffn::launch_axpy_mfma(a, s),
                   "gemv launch");
+}
+
+sffn_status sparse_ffn_compact(const uint16_t* W, int n_rows, int d, int ld_w,
+                               const int32_t* idx, int k, int transpose, uint16_t* out,
+                               int ld_out, void* stream) {
+  REQUIRE(W && out, SFFN_EINVAL, "compact: W and out must be non-null");
+  REQUIRE(n_rows >= 0 && k >= 0 && k <= n_rows, SFFN_EINVAL,
+          "compact: need 0 <= k=%d <= n_rows=%d", k, n_rows);
+  REQUIRE(k == 0 || idx != nullptr, SFFN_EINVAL, "compact: idx must be non-null");
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "compact: d=%d must be a positive multiple of 8", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL, "compact: ld_w=%d must be >= d, %% 8", ld_w);
+  REQUIRE(ld_out % 8 == 0 && ld_out >= (transpose ? k : d), SFFN_EINVAL,
+          "compact: ld_out=%d must be a multiple of 8 and >= %d", ld_out, transpose ? k : d);
+  REQUIRE(aligned(W, 16) && aligned(out, 16), SFFN_EINVAL, "compact: W/out must be 16-byte aligned");
+  if (idx) REQUIRE(aligned(idx, 4), SFFN_EINVAL, "compact: idx misaligned");
+  if (transpose && ld_out == 0) return ok();
+  return from_hip(sffn::launch_compact(W, ld_w, d, idx, k, transpose ? 1 : 0, out, ld_out,
+                                       (hipStream_t)stream),
+                  "compact launch");
 }
 
 static sffn_status check_segments(const char* who, const int32_t* seg_rows, int n_seg, int d_out) {

@@ -131,16 +131,16 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
     }
   }
 
-  __threadfence();
   __syncthreads();
   uint32_t* counter = counters + mt * col_tiles + ct;
   if (t == 0) {
+    __threadfence();
     const unsigned prev = atomicAdd(counter, 1u);
     last_flag = (prev == (unsigned)(KS - 1));
+    if (last_flag) __threadfence();
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
 
   const int o = col0 + t;
   if (o < a.d) {

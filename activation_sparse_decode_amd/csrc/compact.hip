@@ -1,0 +1,83 @@
+// One-time physical compaction of a selected neuron set.
+//
+// LeanStream ("Permutation-Invariant Execution") treats a subset of FFN
+// neurons as one contiguous dense matrix, since the FFN output is a sum over
+// neurons in any order; SelectInfer (§5) fixes the computed set U for the
+// whole decode of a prompt.  Gathering U's weights once per prompt turns
+// every decode step into dense, index-free streaming:
+//  - rows:       out[i][:] = W[idx_i][:]     (gate / up rows of U)
+//  - transposed: out[o][i] = W[idx_i][o]     (down rows of U laid out output-
+//                major, so the down projection becomes one dot product per
+//                output over the compacted activations); columns i >= k up
+//                to ld_out are zero.
+#include "sffn_device.h"
+
+namespace sffn {
+
+__global__ __launch_bounds__(256) void compact_rows_kernel(const uint16_t* __restrict__ W, int ld_w,
+                                                           int d, const int32_t* __restrict__ idx,
+                                                           int k, uint16_t* __restrict__ out,
+                                                           int ld_out) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= k) return;
+  const uint16_t* src = W + (size_t)idx[i] * ld_w;
+  uint16_t* dst = out + (size_t)i * ld_out;
+  for (int c = lane; c < (d >> 3); c += 64)
+    *reinterpret_cast<uint4*>(dst + 8 * c) = *reinterpret_cast<const uint4*>(src + 8 * c);
+}
+
+// 64 (neurons) x 64 (outputs) tile through LDS.
+__global__ __launch_bounds__(256) void compact_cols_kernel(const uint16_t* __restrict__ W, int ld_w,
+                                                           int d, const int32_t* __restrict__ idx,
+                                                           int k, uint16_t* __restrict__ out,
+                                                           int ld_out) {
+  __shared__ uint16_t T[64][66];
+  const int t = threadIdx.x;
+  const int i0 = blockIdx.x * 64, o0 = blockIdx.y * 64;
+  {
+    const int r = t >> 2, q = t & 3;          // neuron i0+r, outputs o0+16q .. +16
+    const int i = i0 + r, o = o0 + 16 * q;
+    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+    if (i < k) {
+      const uint16_t* src = W + (size_t)idx[i] * ld_w + o;
+      if (o < d) v0 = *reinterpret_cast<const uint4*>(src);
+      if (o + 8 < d) v1 = *reinterpret_cast<const uint4*>(src + 8);
+    }
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      T[r][16 * q + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      T[r][16 * q + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    const int r = t >> 2, q = t & 3;          // output o0+r, neurons i0+16q .. +16
+    const int o = o0 + r, i = i0 + 16 * q;
+    if (o >= d) return;
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      w[e] = (uint32_t)T[16 * q + 2 * e][r] | ((uint32_t)T[16 * q + 2 * e + 1][r] << 16);
+    uint16_t* dst = out + (size_t)o * ld_out + i;
+    if (i + 8 <= ld_out) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    if (i + 16 <= ld_out) *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+hipError_t launch_compact(const uint16_t* W, int ld_w, int d, const int32_t* idx, int k,
+                          int transpose, uint16_t* out, int ld_out, hipStream_t s) {
+  if (!transpose) {
+    if (k == 0) return hipSuccess;
+    hipLaunchKernelGGL(compact_rows_kernel, dim3((k + 3) / 4), dim3(256), 0, s, W, ld_w, d, idx, k,
+                       out, ld_out);
+  } else {
+    dim3 grid((ld_out + 63) / 64, (d + 63) / 64);
+    hipLaunchKernelGGL(compact_cols_kernel, grid, dim3(256), 0, s, W, ld_w, d, idx, k, out,
+                       ld_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sffn

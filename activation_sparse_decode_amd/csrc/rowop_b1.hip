@@ -1,26 +1,48 @@
-// Activations at batch 1: one row dot product per neuron, streamed from HBM.
+// Row dot products at batch 1, streamed from HBM.
 //
 // out_n = f(W0[n].x, W1[n].x) for the processed rows n, with the magnitude
 // key bits(|out_n|) written alongside (the ranking input of the selection
-// step; SelectInfer §3 records |a| at the input of down_proj).
+// step; SelectInfer §3 records |a| at the input of down_proj).  The same
+// kernel runs the down projection of a compacted neuron set (plain dot of
+// each output row with the compacted activations, added to the residual).
 //
-// Layout: W rows are neuron-major bf16 (row n = neuron n's d input weights).
-// A wave owns NPI neurons per iteration; lane l reads the 16-byte chunks
-// l, l+64, l+128, ... of each row, so one wave instruction covers 1 KiB of a
-// row, fully coalesced.  x is held in registers for the wave's lifetime
-// (fp32, CPL chunks of 8 per lane) and every row is reduced across the wave
-// with shuffles.  Skipped neurons are never read.
+// Layout and mapping: W rows are contiguous bf16.  A workgroup spans one
+// row: thread t owns the 16-byte chunks t, t+TPB, ... (CPT of them) of every
+// row, so one wave instruction reads 1 KiB of a row, fully coalesced, and
+// the thread keeps the matching 8*CPT entries of x in registers for its
+// whole life.  Each iteration streams NPI rows (both matrices for the GLU),
+// i.e. NPI*CPT (x2) independent 16-byte nontemporal loads per thread, which
+// is the shape a plain streaming read needs on this GPU to approach the HBM
+// rate: many workgroups with a few loads in flight each; the next group's
+// loads are issued before the current group is reduced.  Per-row
+// partial sums are reduced across the wave with shuffles and across the
+// workgroup's waves in LDS.  Skipped neurons are never read.  The optional
+// RMSNorm of x scales the reduced dot products (W.(x s) = s (W.x)).
 #include "sffn_device.h"
 
 namespace sffn {
 
-enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2 };
+enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4 };
 
-template <int OP, int CPL, int NPI>
-__global__ __launch_bounds__(256) void rowop_b1_kernel(RowOpArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int OP, int CPT, int NPI>
+__global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
+  constexpr bool kUse0 = OP != kOpGated;
+  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated;
+  constexpr int kVals = (kUse0 && kUse1) ? 2 : 1;   // dot products per row
+  __shared__ float red[2][16][NPI * kVals];            // [parity][wave][row*vals]
+  __shared__ float sq_red[16];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int nw = blockDim.x >> 6;
+  const int tpb = blockDim.x;
   const int nchunk = a.d >> 3;
 
   int n_items;
@@ -32,10 +54,10 @@ __global__ __launch_bounds__(256) void rowop_b1_kernel(RowOpArgs a) {
     n_items = a.n_rows;
   }
 
-  float xr[CPL][8];
+  float xr[CPT][8];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
+  for (int j = 0; j < CPT; ++j) {
+    const int c = t + tpb * j;
     if (c < nchunk) {
       const float4 p = *reinterpret_cast<const float4*>(a.x + 8 * c);
       const float4 q = *reinterpret_cast<const float4*>(a.x + 8 * c + 4);
@@ -47,122 +69,171 @@ __global__ __launch_bounds__(256) void rowop_b1_kernel(RowOpArgs a) {
     }
   }
 
-  // Optional unit-gain RMSNorm of the input, applied to the dot products
-  // (W.(x s) = s (W.x)); tau is taken on the normalised input.
+  const bool need_norm = OP == kOpDotRelu || a.rms_eps > 0.f;
+  bool have_norm = false;
   float tau = 0.f, inv = 1.f;
-  if (OP == kOpDotRelu || a.rms_eps > 0.f) {
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(xr[j][e], xr[j][e], s);
-    s = wave_sum(s);
-    if (a.rms_eps > 0.f) inv = 1.f / sqrtf(s / (float)a.d + a.rms_eps);
-    tau = a.tau_scale * sqrtf(s) * inv;
-  }
+  int parity = 0;
 
-  for (int base = wave * NPI; base < n_items; base += nwaves * NPI) {
-    int row[NPI];
-    bool live[NPI];
+  // Software pipeline: the weights of the next group of rows are requested
+  // before the current group is reduced, so loads stay in flight across the
+  // reductions and barriers and x is reused for the workgroup's whole life.
+  const int stride = gridDim.x * NPI;
+  int row[NPI];
+  bool live[NPI];
+  uint4 w0[NPI][CPT], w1[NPI][CPT];
+  auto fetch = [&](int base, int (&rw)[NPI], bool (&lv)[NPI], uint4 (&v0)[NPI][CPT],
+                   uint4 (&v1)[NPI][CPT]) {
 #pragma unroll
     for (int i = 0; i < NPI; ++i) {
       const int it = base + i;
-      live[i] = it < n_items;
-      if (!live[i]) {
-        row[i] = 0;
+      lv[i] = it < n_items;
+      if (!lv[i]) {
+        rw[i] = 0;
       } else if (a.idx) {
         const int q = it / a.group;
-        row[i] = a.idx[q] * a.group + (it - q * a.group);
+        rw[i] = a.idx[q] * a.group + (it - q * a.group);
       } else {
-        row[i] = it;
+        rw[i] = it;
       }
     }
-
-    uint4 w0[NPI][CPL], w1[NPI][CPL];
 #pragma unroll
     for (int i = 0; i < NPI; ++i)
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
-        const bool ok = live[i] && c < nchunk;
-        const size_t off = (size_t)row[i] * a.ld_w + 8 * c;
-        if (OP != kOpGated)
-          w0[i][j] = ok ? *reinterpret_cast<const uint4*>(a.W0 + off) : make_uint4(0, 0, 0, 0);
-        if (OP != kOpDotRelu)
-          w1[i][j] = ok ? *reinterpret_cast<const uint4*>(a.W1 + off) : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < CPT; ++j) {
+        const int c = t + tpb * j;
+        const bool ok = lv[i] && c < nchunk;
+        const size_t off = (size_t)rw[i] * a.ld_w + 8 * c;
+        if (kUse0) v0[i][j] = ok ? load_stream(a.W0 + off) : make_uint4(0, 0, 0, 0);
+        if (kUse1) v1[i][j] = ok ? load_stream(a.W1 + off) : make_uint4(0, 0, 0, 0);
       }
+  };
+  int base = blockIdx.x * NPI;
+  if (base < n_items) fetch(base, row, live, w0, w1);
 
-    float acc0[NPI], acc1[NPI];
+  for (; base < n_items; base += stride) {
+    int nrow[NPI];
+    bool nlive[NPI];
+    uint4 n0[NPI][CPT], n1[NPI][CPT];
+    const bool more = base + stride < n_items;
+    if (more) fetch(base + stride, nrow, nlive, n0, n1);
+
+    if (need_norm && !have_norm) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(xr[j][e], xr[j][e], s);
+      s = wave_sum(s);
+      if (lane == 0) sq_red[w] = s;
+    }
+
 #pragma unroll
     for (int i = 0; i < NPI; ++i) {
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
+      for (int j = 0; j < CPT; ++j) {
         float f[8];
-        if (OP != kOpGated) {
+        if (kUse0) {
           unpack8(w0[i][j], f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) s0 = fmaf(f[e], xr[j][e], s0);
         }
-        if (OP != kOpDotRelu) {
+        if (kUse1) {
           unpack8(w1[i][j], f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) s1 = fmaf(f[e], xr[j][e], s1);
         }
       }
-      acc0[i] = (OP != kOpGated) ? wave_sum(s0) * inv : 0.f;
-      acc1[i] = (OP != kOpDotRelu) ? wave_sum(s1) * inv : 0.f;
+      if (kUse0) s0 = wave_sum(s0);
+      if (kUse1) s1 = wave_sum(s1);
+      if (lane == 0) {
+        if (kUse0) red[parity][w][i * kVals] = s0;
+        if (kUse1) red[parity][w][i * kVals + kVals - 1] = s1;
+      }
+    }
+    __syncthreads();
+
+    if (need_norm && !have_norm) {
+      float s = 0.f;
+      for (int ww = 0; ww < nw; ++ww) s += sq_red[ww];
+      if (a.rms_eps > 0.f) inv = 1.f / sqrtf(s / (float)a.d + a.rms_eps);
+      tau = a.tau_scale * sqrtf(s) * inv;   // ||x s|| for the ReLU threshold
+      have_norm = true;
     }
 
+    if (t < NPI && live[t < NPI ? t : 0]) {
+      const int i = t;
+      float g = 0.f, u = 0.f;
+      for (int ww = 0; ww < nw; ++ww) {
+        if (kUse0) g += red[parity][ww][i * kVals];
+        if (kUse1) u += red[parity][ww][i * kVals + kVals - 1];
+      }
+      g *= inv;
+      u *= inv;
+      int r = 0;
 #pragma unroll
-    for (int i = 0; i < NPI; ++i) {
-      if (lane == i && live[i]) {
-        float v;
-        if (OP == kOpGlu) {
-          const float g = acc0[i];
-          v = (g / (1.f + expf(-g))) * acc1[i];
-        } else if (OP == kOpDotRelu) {
-          v = fmaxf(acc0[i] - tau, 0.f);
-        } else {
-          v = a.aux[row[i]] * acc1[i];
+      for (int ii = 0; ii < NPI; ++ii) r = (ii == i) ? row[ii] : r;
+      float v;
+      if (OP == kOpGlu) {
+        v = (g / (1.f + expf(-g))) * u;
+      } else if (OP == kOpDotRelu) {
+        v = fmaxf(g - tau, 0.f);
+      } else if (OP == kOpGated) {
+        v = a.aux[r] * u;
+      } else {
+        v = g;
+      }
+      if (a.accumulate) v += a.out[r];
+      a.out[r] = v;
+      if (a.key_out) a.key_out[r] = key_abs(v);
+    }
+    parity ^= 1;   // the next iteration writes the other LDS half
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NPI; ++i) {
+        row[i] = nrow[i];
+        live[i] = nlive[i];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          if (kUse0) w0[i][j] = n0[i][j];
+          if (kUse1) w1[i][j] = n1[i][j];
         }
-        a.out[row[i]] = v;
-        if (a.key_out) a.key_out[row[i]] = key_abs(v);
       }
     }
   }
 }
 
-template <int OP, int CPL>
-static hipError_t launch_cpl(const RowOpArgs& a, hipStream_t s) {
-  // Neurons per wave iteration: enough 16-byte loads in flight per lane
-  // without spilling (two matrices for GLU).
-  constexpr int NPI = (OP == kOpGlu) ? (CPL <= 6 ? 2 : 1) : (CPL <= 6 ? 4 : 2);
+template <int OP, int CPT, int NPI>
+static hipError_t launch_cfg(const RowOpArgs& a, hipStream_t s) {
+  const int nchunk = a.d >> 3;
+  int tpb = (nchunk + CPT - 1) / CPT;
+  tpb = (tpb + 63) / 64 * 64;
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
-  long waves = (items + NPI - 1) / NPI;
-  if (waves > 4096) waves = 4096;
-  if (waves < 1) waves = 1;
-  const int blocks = (int)((waves + 3) / 4);
-  hipLaunchKernelGGL((rowop_b1_kernel<OP, CPL, NPI>), dim3(blocks), dim3(256), 0, s, a);
+  long blocks = (items + NPI - 1) / NPI;
+  const long cap = 1024;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((rowop_b1_kernel<OP, CPT, NPI>), dim3((unsigned)blocks), dim3(tpb), 0, s, a);
   return hipGetLastError();
 }
 
 template <int OP>
 static hipError_t launch_op(const RowOpArgs& a, hipStream_t s) {
-  const int need = ((a.d >> 3) + 63) / 64;
-  if (need <= 4) return launch_cpl<OP, 4>(a, s);
-  if (need <= 6) return launch_cpl<OP, 6>(a, s);
-  if (need <= 8) return launch_cpl<OP, 8>(a, s);
-  if (need <= 10) return launch_cpl<OP, 10>(a, s);
-  if (need <= 12) return launch_cpl<OP, 12>(a, s);
-  return launch_cpl<OP, 16>(a, s);
+  // Rows per iteration (measured on MI355X at the 28-layer stack shapes): one
+  // neuron (two rows) for the GLU, two rows for single-matrix ops; about four
+  // workgroups per CU, each looping over a few iterations.
+  constexpr int NPI = (OP == kOpGlu) ? 1 : 2;
+  const int nchunk = a.d >> 3;
+  if (nchunk <= 1024) return launch_cfg<OP, 1, NPI>(a, s);
+  return launch_cfg<OP, 2, NPI>(a, s);   // d <= 16384
 }
 
 hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s) {
   switch (a.op) {
     case kOpGlu: return launch_op<kOpGlu>(a, s);
     case kOpDotRelu: return launch_op<kOpDotRelu>(a, s);
-    default: return launch_op<kOpGated>(a, s);
+    case kOpGated: return launch_op<kOpGated>(a, s);
+    default: return launch_op<kOpDot>(a, s);
   }
 }
 

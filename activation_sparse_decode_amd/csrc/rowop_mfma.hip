@@ -17,7 +17,7 @@ namespace sffn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2 };
+enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8, u);
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
     const int k = ks * 32;
     uint4 wa = zero4, wb = zero4;
     if (OP != kOpGated) wa = live ? *reinterpret_cast<const uint4*>(w0p + k) : zero4;
-    if (OP != kOpDotRelu) wb = live ? *reinterpret_cast<const uint4*>(w1p + k) : zero4;
+    if (OP == kOpGlu || OP == kOpGated) wb = live ? *reinterpret_cast<const uint4*>(w1p + k) : zero4;
     float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
     if (tok_ok) {
       p = *reinterpret_cast<const float4*>(xp + k);
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(wa), acc0, 0, 0, 0);
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(wa), acc0, 0, 0, 0);
     }
-    if (OP != kOpDotRelu) {
+    if (OP == kOpGlu || OP == kOpGated) {
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(wb), acc1, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(wb), acc1, 0, 0, 0);
     }
@@ -148,9 +148,12 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
       v = (gg / (1.f + expf(-gg))) * (s1[i] * inv);
     } else if (OP == kOpDotRelu) {
       v = fmaxf(s0[i] * inv - a.tau_scale * sqrtf(ss) * inv, 0.f);
-    } else {
+    } else if (OP == kOpGated) {
       v = a.aux[(size_t)b * a.ld_aux + row] * (s1[i] * inv);
+    } else {
+      v = s0[i] * inv;
     }
+    if (a.accumulate) v += a.out[(size_t)b * a.ld_out + row];
     a.out[(size_t)b * a.ld_out + row] = v;
     if (a.key_out) a.key_out[(size_t)b * a.ld_out + row] = key_abs(v);
   }
@@ -165,7 +168,8 @@ hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s) {
   switch (a.op) {
     case kOpGlu: hipLaunchKernelGGL(rowop_mfma_kernel<kOpGlu>, grid, dim3(256), 0, s, a); break;
     case kOpDotRelu: hipLaunchKernelGGL(rowop_mfma_kernel<kOpDotRelu>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(rowop_mfma_kernel<kOpGated>, grid, dim3(256), 0, s, a); break;
+    case kOpGated: hipLaunchKernelGGL(rowop_mfma_kernel<kOpGated>, grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(rowop_mfma_kernel<kOpDot>, grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -75,7 +75,7 @@ struct RowOpArgs {
   const int32_t* idx; const int32_t* count; int k_max, group;
   float tau_scale, rms_eps;
   const float* aux; int ld_aux;
-  float* out; uint32_t* key_out; int ld_out;
+  float* out; uint32_t* key_out; int ld_out; int accumulate;
 };
 hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s);
 hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s);
@@ -122,6 +122,9 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s);
 hipError_t launch_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out,
                                const int* seg_bounds, int n_seg, uint8_t* rec,
                                int rec_bytes, hipStream_t s);
+
+hipError_t launch_compact(const uint16_t* W, int ld_w, int d, const int32_t* idx, int k,
+                          int transpose, uint16_t* out, int ld_out, hipStream_t s);
 
 size_t workspace_bytes(int batch, int n_rows, int d_out);
 int pick_split_b1(long items, int col_tiles);

@@ -48,15 +48,17 @@ __device__ inline void splitk_finish(float4 (*red)[kTileCols / 4], int* last_fla
                               int d, const float* alpha, float* out, int accumulate) {
   const int c = tile * kTileCols + (int)threadIdx.x;
   if (threadIdx.x < kTileCols && c < d) partials[(size_t)ks * d + c] = part;
-  __threadfence();
+  // One agent-scope fence per workgroup (release of the whole group's
+  // partial, made cumulative by the barrier), then the arrival counter.
   __syncthreads();
   if (threadIdx.x == 0) {
+    __threadfence();
     const unsigned prev = atomicAdd(counter, 1u);
     *last_flag = (prev == (unsigned)(KS - 1));
+    if (*last_flag) __threadfence();   // acquire: the other chunks' partials
   }
   __syncthreads();
   if (!*last_flag) return;
-  __threadfence();
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = tile * kTileCols + 8 * lane;

@@ -118,7 +118,8 @@ class SelectInferStack:
 
     def prefill(self, X: torch.Tensor, record=None) -> torch.Tensor:
         """Dense pass of the prompt; per-token top-alpha, frequency top-beta,
-        union with the base set, compacted into U_idx / U_cnt."""
+        union with the base set, compacted into U_idx / U_cnt; then the
+        weights of every U_l are gathered for decode (compact())."""
         H = X.clone()
         self.freq.zero_()
         T = H.shape[0]
@@ -131,19 +132,51 @@ class SelectInferStack:
                                 include_mask=self.base_mask[l], idx_out=self.U_idx[l],
                                 count_out=self.U_cnt[l:l + 1])
             self._dense_residual(l, H)
+        self.compact()
         return H
 
-    def decode_layer(self, l: int, h: torch.Tensor, timer=None) -> None:
+    def compact(self) -> None:
+        """Gather each layer's U_l weights once per prompt: gate and up rows
+        side by side [|U|][2d], down rows output-major [d][|U| rounded to 8]
+        (zero padded).  Reads the |U_l| counts to the host once to size the
+        buffers (a per-prompt step, outside the decode loop)."""
+        cnt = self.U_cnt.cpu().tolist()
+        d, dev = self.d, self.U_idx.device
+        self.comp = []
+        for l, k in enumerate(cnt):
+            Wg, Wu, WdT = self.layers[l]
+            ldk = max(8, (k + 7) // 8 * 8)
+            gu = torch.zeros(max(k, 1), 2 * d, dtype=torch.int16, device=dev)
+            dT = torch.zeros(d, ldk, dtype=torch.int16, device=dev)
+            ac = torch.zeros(ldk, dtype=F32, device=dev)
+            idx = self.U_idx[l]
+            B.sparse_ffn_compact(Wg, idx, k, False, gu[:, :d])
+            B.sparse_ffn_compact(Wu, idx, k, False, gu[:, d:])
+            B.sparse_ffn_compact(WdT, idx, k, True, dT)
+            self.comp.append((gu[:k], dT, ac, k))
+
+    def decode_layer_gathered(self, l: int, h: torch.Tensor) -> None:
+        """Decode one layer straight from the full weights through U_l."""
         Wg, Wu, WdT = self.layers[l]
         idx, cnt = self.U_idx[l], self.U_cnt[l:l + 1]
-        if timer is not None:
-            timer.begin()
         B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, h, self.a[l], idx=idx, count=cnt,
                           k_max=self.k_max, rms_eps=self.rms_eps)
-        if timer is not None:
-            timer.end()
         B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[l], h, idx=idx, count=cnt,
                           k_max=self.k_max, accumulate=True, workspace=self.ws)
+
+    def decode_layer(self, l: int, h: torch.Tensor, timer=None) -> None:
+        """Decode one layer from the compacted weights: dense gate/up over
+        U_l (activations in U_l order), then one dot per output of the
+        output-major down rows, added to the residual."""
+        gu, dT, ac, k = self.comp[l]
+        d = self.d
+        if timer is not None:
+            timer.begin()
+        if k > 0:
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, gu[:, :d], gu[:, d:], h, ac, rms_eps=self.rms_eps)
+        if timer is not None:
+            timer.end()
+        B.sparse_ffn_gemv(B.OP_DOT, dT, None, ac, h, accumulate=True)
 
     def decode(self, h: torch.Tensor, timer=None) -> None:
         """One decode token through every layer (h is updated in place)."""

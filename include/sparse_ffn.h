@@ -79,7 +79,9 @@ typedef enum {
     SFFN_OP_GLU_SILU = 0,   /* out_n = silu(W0[n].x) * (W1[n].x)        (SwiGLU)  */
     SFFN_OP_DOT_RELU = 1,   /* out_n = max(W0[n].x - tau_scale*||x||_2, 0) (ReGLU gate) */
     SFFN_OP_GATED = 2,      /* out_n = aux_n * (W1[n].x)                 (ReGLU up) */
-    SFFN_OP_AXPY = 3        /* y (+)= alpha * sum_n m_n in_n W0[n][:]    (down)     */
+    SFFN_OP_AXPY = 3,       /* y (+)= alpha * sum_n m_n in_n W0[n][:]    (down)     */
+    SFFN_OP_DOT = 4         /* out_n = W0[n].x   (down over compacted, output-major
+                               weights: one dot per output)                      */
 } sffn_gemv_op;
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
@@ -87,7 +89,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 2
+#define SFFN_ABI_VERSION 3
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -152,10 +154,11 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
  * Decomposition"; group = 1 for single neurons).  Skipped rows are never
  * read ([SelectInfer] §5 computes only the selected neurons).
  *
- * Row ops (GLU_SILU, DOT_RELU, GATED): W0, W1 are bf16 [n_rows][ld_w] with
- *  rows of length d; in = x fp32 [batch][ld_in] (length d).  For each token
- *  b and processed row n: out[b][n] = op value (see sffn_gemv_op) and, if
- *  key_out is set, key_out[b][n] = bits(out) & 0x7FFFFFFF.  Entries of rows
+ * Row ops (GLU_SILU, DOT_RELU, GATED, DOT): W0, W1 are bf16 [n_rows][ld_w]
+ *  with rows of length d; in = x fp32 [batch][ld_in] (length d).  For each
+ *  token b and processed row n: out[b][n] = (accumulate ? out[b][n] : 0) +
+ *  op value (see sffn_gemv_op) and, if key_out is set, key_out[b][n] =
+ *  bits(out[b][n]) & 0x7FFFFFFF.  Entries of rows
  *  not processed are left untouched.  ld_out >= n_rows.  silu(z) = z / (1 +
  *  e^-z) as in the engine listing of [PowerInfer-2].  DOT_RELU uses W0 only
  *  (tau = tau_scale * ||x_b||_2, tau_scale >= 0); GATED uses W1 and aux fp32
@@ -191,6 +194,25 @@ sffn_status sparse_ffn_gemv(int op,
                             const float* alpha,
                             float* out, uint32_t* key_out, int ld_out, int accumulate,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_compact -- gather the weight rows of a selected neuron set into
+ * a dense buffer, once per selection ([SelectInfer] §5 keeps the computed
+ * set U fixed for a prompt's decode; [LeanStream] "Permutation-Invariant
+ * Execution": a neuron subset is an ordinary dense matrix, in any order).
+ *  W     : bf16 [n_rows][ld_w], rows of length d (d % 8 == 0, ld_w % 8 == 0).
+ *  idx   : device int32 [k], rows to gather (0 <= idx[i] < n_rows), k from
+ *          the host (k >= 0).
+ *  transpose = 0: out bf16 [k][ld_out], out[i][0..d) = W[idx[i]][0..d)
+ *          (ld_out >= d, % 8 == 0).
+ *  transpose = 1: out bf16 [d][ld_out], out[o][i] = W[idx[i]][o] for i < k
+ *          and 0 for k <= i < ld_out (ld_out >= k, % 8 == 0): the down
+ *          weights of U output-major, for SFFN_OP_DOT.
+ * W and out 16-byte aligned.
+ */
+sffn_status sparse_ffn_compact(const uint16_t* W, int n_rows, int d, int ld_w,
+                               const int32_t* idx, int k, int transpose,
+                               uint16_t* out, int ld_out, void* stream);
 
 /*
  * Bytes of one middle-tier column record for d_out outputs in n_seg output

@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 2
+    assert L.sffn_abi_version() == 3
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -86,6 +86,8 @@ def gemv(L, op=3, W0=FAKE, W1=FAKE, n_rows=64, d=64, ld_w=64, inp=FAKE, batch=1,
 
 def test_gemv_validation(L):
     assert gemv(L, op=9)[0] == 1
+    rc, msg = gemv(L, op=4, W0=NULL)
+    assert rc == 1 and "W0" in msg
     rc, msg = gemv(L, d=12)
     assert rc == 1 and "multiple of 8" in msg
     rc, msg = gemv(L, ld_w=60)
@@ -144,6 +146,18 @@ def test_tier_validation(L):
     rc, msg = status_and_msg(L, tg(FAKE, 6144, FAKE, 3088, seg, 3, 4096, 6144, FAKE, FAKE, FAKE, 614,
                                    FAKE, FAKE, 1433, FAKE, 0, FAKE, 64, NULL))
     assert rc == 3 and "workspace" in msg
+
+
+def test_compact_validation(L):
+    cp = L.sparse_ffn_compact
+    rc, msg = status_and_msg(L, cp(FAKE, 100, 64, 64, FAKE, 101, 0, FAKE, 64, NULL))
+    assert rc == 1 and "k=" in msg
+    rc, msg = status_and_msg(L, cp(FAKE, 100, 64, 64, FAKE, 10, 0, FAKE, 60, NULL))
+    assert rc == 1 and "ld_out" in msg
+    rc, msg = status_and_msg(L, cp(FAKE, 100, 64, 64, FAKE, 10, 1, FAKE, 4, NULL))
+    assert rc == 1 and "ld_out" in msg
+    rc, msg = status_and_msg(L, cp(FAKE, 100, 64, 64, NULL, 10, 1, FAKE, 16, NULL))
+    assert rc == 1 and "idx" in msg
 
 
 def test_no_fallback_when_library_missing(monkeypatch):

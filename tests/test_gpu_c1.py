@@ -64,18 +64,31 @@ def run_stack(L, N, d, n_calib, n_prompt, n_decode, check_layers, check_tokens, 
         U_ref = oracle.union(np.flatnonzero(base_mask[l]), dyn)
         assert U_cnt[l] == U_ref.size and np.array_equal(U_idx[l, :U_cnt[l]], U_ref), l
     print(f"  |U| per layer: min {U_cnt.min()} mean {U_cnt.mean():.1f} max {U_cnt.max()}")
+    for l in check_layers:                        # per-prompt compaction, bit-exact
+        Wg, Wu, WdT = layers[l]
+        U = U_idx[l, :U_cnt[l]]
+        gu, dT, _, k = stack.comp[l]
+        gu_h = host(gu).view(np.uint16)
+        dT_h = host(dT).view(np.uint16)
+        assert k == U.size
+        assert np.array_equal(gu_h[:, :d], Wg[U]) and np.array_equal(gu_h[:, d:], Wu[U])
+        assert np.array_equal(dT_h[:, :k], WdT[U].T) and not dT_h[:, k:].any()
 
     for t in range(n_decode):
         h = dev(Xd[t])
         for l in range(L):
             check = t in check_tokens and l in check_layers
             h_in = host(h).copy() if check else None
-            stack.decode_layer(l, h)
+            gathered = t == n_decode - 1          # last token: the uncompacted path
+            if gathered:
+                stack.decode_layer_gathered(l, h)
+            else:
+                stack.decode_layer(l, h)
             if check:
                 torch.cuda.synchronize()
                 Wg, Wu, WdT = layers[l]
                 U = U_idx[l, :U_cnt[l]]
-                a = host(stack.a[l])[U]
+                a = host(stack.a[l])[U] if gathered else host(stack.comp[l][2])[:U.size]
                 x = oracle.rms_normalize(h_in, RMS_EPS)
                 assert_close(a, oracle.swiglu_acts(Wg, Wu, x, U), what=f"decode a t={t} l={l}")
                 y_ref = oracle.down_gather(WdT, U, a)
