@@ -164,24 +164,25 @@ class SelectInferStack:
         B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[l], h, idx=idx, count=cnt,
                           k_max=self.k_max, accumulate=True, workspace=self.ws)
 
-    def decode_layer(self, l: int, h: torch.Tensor, timer=None) -> None:
-        """Decode one layer from the compacted weights: dense gate/up over
-        U_l (activations in U_l order), then one dot per output of the
-        output-major down rows, added to the residual."""
-        gu, dT, ac, k = self.comp[l]
-        d = self.d
-        if timer is not None:
-            timer.begin()
+    def decode_gate_up(self, l: int, h: torch.Tensor) -> None:
+        """Activations of layer l over the compacted U_l (in U_l order)."""
+        gu, _, ac, k = self.comp[l]
         if k > 0:
-            B.sparse_ffn_gemv(B.OP_GLU_SILU, gu[:, :d], gu[:, d:], h, ac, rms_eps=self.rms_eps)
-        if timer is not None:
-            timer.end()
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, gu[:, :self.d], gu[:, self.d:], h, ac,
+                              rms_eps=self.rms_eps)
+
+    def decode_layer(self, l: int, h: torch.Tensor) -> None:
+        """Decode one layer from the compacted weights: dense gate/up over
+        U_l, then one dot per output of the output-major down rows, added
+        to the residual."""
+        self.decode_gate_up(l, h)
+        _, dT, ac, _ = self.comp[l]
         B.sparse_ffn_gemv(B.OP_DOT, dT, None, ac, h, accumulate=True)
 
-    def decode(self, h: torch.Tensor, timer=None) -> None:
+    def decode(self, h: torch.Tensor) -> None:
         """One decode token through every layer (h is updated in place)."""
         for l in range(self.L):
-            self.decode_layer(l, h, timer)
+            self.decode_layer(l, h)
 
 
 class TieredProjection:

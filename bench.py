@@ -32,6 +32,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+COPY_CALIB_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rowop_glu_c1.json")
+
+
+def measured_traffic(kernel_sources):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current source of that kernel."""
+    import hashlib
+    import json as _json
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = _json.load(fh)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for path in kernel_sources:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def log(msg: str) -> None:
@@ -50,16 +71,16 @@ def parse():
 
 
 def glu_bytes(u: int, d: int) -> int:
-    """Algorithmic bytes of one gathered gate/up launch over u neurons:
-    2 bf16 rows of d per neuron, the index list, the input h, the fp32
-    activations written."""
-    return 2 * u * d * 2 + 4 * u + 4 * d + 4 * u
+    """Algorithmic bytes of one gate/up launch over the u compacted neurons:
+    2 bf16 rows of d per neuron, the input h read, the fp32 activations
+    written."""
+    return 2 * u * d * 2 + 4 * d + 4 * u
 
 
 def down_bytes(u: int, d: int) -> int:
-    """Gathered down product: u bf16 rows of d, index list and activations
-    read, the residual read and written."""
-    return u * d * 2 + 4 * u + 4 * u + 2 * 4 * d
+    """Down product over the compacted neurons: d output rows of u bf16
+    weights, the activations read, the residual read and written."""
+    return u * d * 2 + 4 * u + 2 * 4 * d
 
 
 def cpu_baseline(layers, U_sets, X, seconds: float, rms_eps: float):
@@ -176,41 +197,34 @@ def main():
     us_per_token = total_ms * 1e3 / args.steps
     log(f"decode: {us_per_token:.1f} us/token over {args.steps} steps")
 
-    # ---- dominant kernel: per-launch events around every gathered gate/up
-    # launch of K eager steps, all enqueued behind a spin kernel so the GPU
-    # runs them back to back (the events then bracket GPU time only).
-    class Timer:
-        def __init__(self):
-            self.pairs = []
-
-        def begin(self):
-            s = ev()
-            s.record()
-            self.pairs.append([s, None])
-
-        def end(self):
-            e = ev()
-            e.record()
-            self.pairs[-1][1] = e
-
-    timer = Timer()
-    # spin-kernel rate, so the spin covers the host's enqueueing (~1 s)
-    a_, b_ = ev(), ev()
+    # ---- dominant kernel (gate/up over the compacted union): its 28
+    # launches of one decode step captured alone in a graph and replayed K
+    # times on the same stream, bracketed by HIP events (per-launch events
+    # in eager mode would add their own overhead to every short launch).
+    glu_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(glu_graph):
+        for l in range(L):
+            stack.decode_gate_up(l, h)
     torch.cuda.synchronize()
-    a_.record()
-    torch.cuda._sleep(int(1e7))
-    b_.record()
+    for _ in range(2):
+        glu_graph.replay()
+    g0, g1 = ev(), ev()
     torch.cuda.synchronize()
-    cycles_per_ms = 1e7 / max(a_.elapsed_time(b_), 1e-3)
-    torch.cuda._sleep(int(min(cycles_per_ms * 1000.0, 5e10)))
-    for t in range(args.warmup, n_tok):
-        h.copy_(Xd[t])
-        stack.decode(h, timer)
+    g0.record()
+    for _ in range(args.steps):
+        glu_graph.replay()
+    g1.record()
     torch.cuda.synchronize()
-    durs = np.array([s.elapsed_time(e) for s, e in timer.pairs]) * 1e3   # us
-    glu_us = float(durs.mean())
+    glu_us = g0.elapsed_time(g1) * 1e3 / (args.steps * L)
     achieved = glu_total_bytes / L / (glu_us * 1e-6) / 1e9
-    log(f"gathered gate/up: {glu_us:.2f} us/launch avg, {achieved:.0f} GB/s")
+    log(f"gate/up over U: {glu_us:.2f} us/launch avg, {achieved:.0f} GB/s")
+
+    # A plain device copy of known size: the reference that scales the HBM
+    # counters (FETCH_SIZE / WRITE_SIZE) of the profiled kernels to bytes.
+    calib = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib)
+    calib_dst.copy_(calib)
+    torch.cuda.synchronize()
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -245,13 +259,15 @@ def main():
         "step_frac_of_peak": round(step_bytes / (us_per_token * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "setup": {"calibrate_ms": round(calib_ms, 2), "prefill_ms": round(prefill_ms, 2)},
         "roofline": {
-            "kernel": "rowop_b1_kernel (gathered gate/up, SwiGLU epilogue)",
+            "kernel": "rowop_b1_kernel<GLU> (gate/up over the compacted union, SwiGLU epilogue)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic([
+                os.path.join(ROOT, "activation_sparse_decode_amd", "csrc", "rowop_b1.hip"),
+                os.path.join(ROOT, "activation_sparse_decode_amd", "csrc", "sffn_device.h")]),
             "launch_us": round(glu_us, 3),
             "bytes_per_launch": int(glu_total_bytes / L),
         },
