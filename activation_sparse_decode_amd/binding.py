@@ -100,7 +100,7 @@ def tier_record_bytes(d_out: int, n_seg: int) -> int:
 
 
 def new_workspace(batch: int, n_rows: int, d_out: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace of the size the gathered products need."""
+    """A workspace of the size the gathered products need."""
     return torch.zeros(workspace_size(batch, n_rows, d_out), dtype=torch.uint8, device=device)
 
 

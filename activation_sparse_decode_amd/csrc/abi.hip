@@ -50,11 +50,11 @@ size_t workspace_bytes(int batch, int n_rows, int d_out) {
   if (batch < 1) batch = 1;
   if (n_rows < 0) n_rows = 0;
   if (d_out < 0) d_out = 0;
-  if (batch == 1) return kCounterBytes + align256((size_t)kMaxSplit * d_out * sizeof(float));
+  if (batch == 1) return kWsHeaderBytes + align256((size_t)kMaxSplit * d_out * sizeof(float));
   const int Mt = (batch + 15) / 16;
   const size_t Mpad = (size_t)Mt * 16;
   const size_t Kpad = ((size_t)n_rows + 63) / 64 * 64;
-  return kCounterBytes + align256((size_t)max_split_mfma(Mt) * Mpad * d_out * sizeof(float)) +
+  return kWsHeaderBytes + align256((size_t)max_split_mfma(Mt) * Mpad * d_out * sizeof(float)) +
          2 * align256(Mpad * Kpad * 2);
 }
 }  // namespace sffn
@@ -189,9 +189,6 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
   REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
           "gemv: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
-  const long tiles = batch == 1 ? (d + 511) / 512 : (long)((d + 255) / 256) * ((batch + 15) / 16);
-  REQUIRE(tiles <= sffn::kMaxCounters, SFFN_EUNSUPPORTED, "gemv: %ld output tiles exceed %d", tiles,
-          sffn::kMaxCounters);
   sffn::AxpyArgs a{W0, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max, idx ? group : 1,
                    row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes};
   return from_hip(batch == 1 ? sffn::launch_axpy_b1(a, s) : sffn::launch_axpy_mfma(a, s),

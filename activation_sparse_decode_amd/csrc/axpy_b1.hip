@@ -5,20 +5,19 @@
 // output is a sum over hidden neurons, so any row order gives the same y up
 // to fp32 rounding).
 //
-// Grid = (512-column tiles) x (KS row chunks).  A 1024-thread workgroup owns
-// one column tile and one contiguous chunk of the compacted row list; wave w
-// takes rows w, w+16, ...; lane l owns columns 8l..8l+7 of the tile and
-// reads them with one 16-byte load per row (1 KiB per wave instruction).
-// Waves are summed in LDS, the chunk's partial goes to the workspace, and
-// the last workgroup to finish a column tile sums all chunks in chunk order
-// (fixed order: the result is bitwise reproducible) and writes y.
+// Kernel 1, grid = (512-column tiles) x (KS row chunks): a 1024-thread
+// workgroup owns one column tile and one contiguous chunk of the compacted
+// row list; wave w takes rows w, w+16, ...; lane l owns columns 8l..8l+7 of
+// the tile and streams them with one 16-byte nontemporal load per row
+// (1 KiB per wave instruction).  Waves are summed in LDS and the chunk's
+// partial row goes to the workspace.  Kernel 2 sums the KS partials in chunk
+// order and applies alpha / accumulate.
 #include "sffn_splitk.h"
 
 namespace sffn {
 
-__global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS) {
+__global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
-  __shared__ int last_flag;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int col = tile * kTileCols + 8 * lane;
@@ -46,7 +45,7 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS) {
         if (a.row_mask && !a.row_mask[row[u]]) v = 0.f;
       }
       av[u] = v;
-      wv[u] = (ok && col_ok) ? *reinterpret_cast<const uint4*>(a.W + (size_t)row[u] * a.ld_w + col)
+      wv[u] = (ok && col_ok) ? load_stream16(a.W + (size_t)row[u] * a.ld_w + col)
                              : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -59,10 +58,51 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS) {
   }
 
   const float part = wg_reduce_cols(red, acc);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws);
-  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterBytes);
-  splitk_finish(red, &last_flag, part, partials, counters + tile, KS, ks, tile, a.d, a.alpha,
-                a.out, a.accumulate);
+  const int c = tile * kTileCols + (int)threadIdx.x;
+  if (threadIdx.x < kTileCols && c < a.d) partials[(size_t)ks * a.d + c] = part;
+}
+
+// Ordered reduction of [KS][Mp][d] partials: a 256-thread workgroup covers
+// 256 columns of one token row; wave w sums chunks w, w+4, ... (float4 per
+// lane), then the four wave sums are added in wave order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partials,
+                                                            int KS, int Mp, int d,
+                                                            const float* __restrict__ alpha,
+                                                            float* __restrict__ out, int ld_out,
+                                                            int accumulate) {
+  __shared__ float4 red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = blockIdx.y;
+  const int c = blockIdx.x * 256 + 4 * lane;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < d) {
+    for (int k = w; k < KS; k += 4) {
+      const float4 p = *reinterpret_cast<const float4*>(partials + ((size_t)k * Mp + m) * d + c);
+      s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    }
+  }
+  red[w][lane] = s;
+  __syncthreads();
+  if (w != 0 || c >= d) return;
+  float4 t = red[0][lane];
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww) {
+    const float4 q = red[ww][lane];
+    t.x += q.x; t.y += q.y; t.z += q.z; t.w += q.w;
+  }
+  const float al = alpha ? alpha[m] : 1.f;
+  float* o = out + (size_t)m * ld_out + c;
+  const float v[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (accumulate ? o[e] : 0.f) + al * v[e];
+}
+
+hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, int d,
+                                const float* alpha, float* out, int ld_out, int accumulate,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((d + 255) / 256, M), dim3(256), 0, s, partials, KS,
+                     Mp, d, alpha, out, ld_out, accumulate);
+  return hipGetLastError();
 }
 
 int pick_split_b1(long items, int col_tiles) {
@@ -79,8 +119,11 @@ hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s) {
   const int col_tiles = (a.d + kTileCols - 1) / kTileCols;
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
   const int KS = pick_split_b1(items, col_tiles);
-  hipLaunchKernelGGL(axpy_b1_kernel, dim3(col_tiles, KS), dim3(1024), 0, s, a, KS);
-  return hipGetLastError();
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
+  hipLaunchKernelGGL(axpy_b1_kernel, dim3(col_tiles, KS), dim3(1024), 0, s, a, KS, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(partials, KS, 1, 1, a.d, a.alpha, a.out, a.d, a.accumulate, s);
 }
 
 }  // namespace sffn

@@ -13,8 +13,8 @@
 //   along N, so a workgroup stages a 64-row x 256-column tile in LDS with
 //   16-byte coalesced loads, and each lane gathers its B operand (8 rows of
 //   one column) from LDS.  The LDS row pitch (129 dwords) puts the four
-//   K-groups of a wave on disjoint banks.  Split-K over row chunks; the last
-//   workgroup of each (column tile, token tile) sums the chunks in order.
+//   K-groups of a wave on disjoint banks.  Split-K over row chunks; a second
+//   kernel sums the chunks' partials in chunk order.
 #include "sffn_splitk.h"
 
 namespace sffn {
@@ -47,10 +47,8 @@ __global__ __launch_bounds__(256) void pack_acts_kernel(AxpyArgs a, int Kpad, ui
 __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int Mpad, int Kpad,
                                                         const uint16_t* __restrict__ Ahi,
                                                         const uint16_t* __restrict__ Alo,
-                                                        float* partials, uint32_t* counters,
-                                                        int col_tiles) {
+                                                        float* partials) {
   __shared__ uint32_t T[kKT * kPitch / 2];
-  __shared__ int last_flag;
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -88,7 +86,7 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
       const int it = kb + lr + 8 * j;
       const bool ok = it < k1 && lcol_ok;
       const int row = ok ? item_row(a.idx, a.group, it) : 0;
-      v[j] = ok ? *reinterpret_cast<const uint4*>(a.W + (size_t)row * a.ld_w + lcol)
+      v[j] = ok ? load_stream16(a.W + (size_t)row * a.ld_w + lcol)
                 : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
@@ -130,31 +128,6 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
         partials[((size_t)ks * Mpad + m0 + 4 * g + i) * a.d + o] = acc[nt][i];
     }
   }
-
-  __syncthreads();
-  uint32_t* counter = counters + mt * col_tiles + ct;
-  if (t == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(counter, 1u);
-    last_flag = (prev == (unsigned)(KS - 1));
-    if (last_flag) __threadfence();
-  }
-  __syncthreads();
-  if (!last_flag) return;
-
-  const int o = col0 + t;
-  if (o < a.d) {
-    for (int m = 0; m < 16; ++m) {
-      const int b = m0 + m;
-      if (b >= a.batch) break;
-      float s = 0.f;
-      for (int kk = 0; kk < KS; ++kk) s += partials[((size_t)kk * Mpad + b) * a.d + o];
-      const float al = a.alpha ? a.alpha[b] : 1.f;
-      float* dst = a.out + (size_t)b * a.ld_out + o;
-      *dst = (a.accumulate ? *dst : 0.f) + al * s;
-    }
-  }
-  if (t == 0) *counter = 0u;
 }
 
 int max_split_mfma(int mtiles) {
@@ -175,10 +148,9 @@ hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s) {
   if (KS < 1) KS = 1;
 
   char* ws = reinterpret_cast<char*>(a.ws);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
-  float* partials = reinterpret_cast<float*>(ws + kCounterBytes);
+  float* partials = reinterpret_cast<float*>(ws + kWsHeaderBytes);
   const size_t part_bytes = align256((size_t)max_split_mfma(Mt) * Mpad * a.d * sizeof(float));
-  uint16_t* hi = reinterpret_cast<uint16_t*>(ws + kCounterBytes + part_bytes);
+  uint16_t* hi = reinterpret_cast<uint16_t*>(ws + kWsHeaderBytes + part_bytes);
   uint16_t* lo = hi + align256((size_t)Mpad * Kpad * 2) / 2;
 
   if (Kpad > 0) {
@@ -188,8 +160,11 @@ hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(axpy_mfma_kernel, dim3(col_tiles, (int)KS, Mt), dim3(256), 0, s, a, (int)KS,
-                     Mpad, Kpad, hi, lo, partials, counters, col_tiles);
-  return hipGetLastError();
+                     Mpad, Kpad, hi, lo, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(partials, (int)KS, a.batch, Mpad, a.d, a.alpha, a.out, a.ld_out,
+                              a.accumulate, s);
 }
 
 }  // namespace sffn

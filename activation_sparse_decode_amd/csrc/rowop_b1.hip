@@ -204,13 +204,12 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
 }
 
 template <int OP, int CPT, int NPI>
-static hipError_t launch_cfg(const RowOpArgs& a, hipStream_t s) {
+static hipError_t launch_cfg(const RowOpArgs& a, hipStream_t s, long cap) {
   const int nchunk = a.d >> 3;
   int tpb = (nchunk + CPT - 1) / CPT;
   tpb = (tpb + 63) / 64 * 64;
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
   long blocks = (items + NPI - 1) / NPI;
-  const long cap = 1024;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((rowop_b1_kernel<OP, CPT, NPI>), dim3((unsigned)blocks), dim3(tpb), 0, s, a);
@@ -219,13 +218,13 @@ static hipError_t launch_cfg(const RowOpArgs& a, hipStream_t s) {
 
 template <int OP>
 static hipError_t launch_op(const RowOpArgs& a, hipStream_t s) {
-  // Rows per iteration (measured on MI355X at the 28-layer stack shapes): one
-  // neuron (two rows) for the GLU, two rows for single-matrix ops; about four
-  // workgroups per CU, each looping over a few iterations.
-  constexpr int NPI = (OP == kOpGlu) ? 1 : 2;
+  // Measured on MI355X at the 28-layer stack shapes: two 16-byte chunks per
+  // thread per row (128-320-thread workgroups), one row (GLU: one neuron)
+  // per iteration, at most 1024 (GLU) / 2048 (single matrix) workgroups.
+  const long cap = OP == kOpGlu ? 1024 : 2048;
   const int nchunk = a.d >> 3;
-  if (nchunk <= 1024) return launch_cfg<OP, 1, NPI>(a, s);
-  return launch_cfg<OP, 2, NPI>(a, s);   // d <= 16384
+  if (nchunk < 128) return launch_cfg<OP, 1, 1>(a, s, cap);
+  return launch_cfg<OP, 2, 1>(a, s, cap);    // nchunk <= 1024 (d <= 8192)
 }
 
 hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s) {

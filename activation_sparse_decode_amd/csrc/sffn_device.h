@@ -57,9 +57,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // ----------------------------------------------------------------- workspace layout
-// [counters: kCounterBytes][partials: fp32][packed activations: bf16 hi/lo]
-constexpr size_t kCounterBytes = 16384;     // 4096 uint32 tile counters
-constexpr int kMaxCounters = 4096;
+// [header: kWsHeaderBytes][partials: fp32][packed activations: bf16 hi/lo]
+constexpr size_t kWsHeaderBytes = 256;
 constexpr int kMaxSplit = 256;               // largest split-K factor
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -1,6 +1,11 @@
-// Split-K pieces shared by the batch-1 gathered products (plain and tiered):
-// row-list expansion, the in-workgroup column reduction, and the
-// last-workgroup-reduces epilogue.  Internal to libsparse_ffn.so.
+// Split-K pieces shared by the gathered products (plain, tiered, batched):
+// row-list expansion, the in-workgroup column reduction, streaming loads and
+// the ordered reduction of per-chunk partials.  Internal to libsparse_ffn.so.
+//
+// A gathered product splits its row list into KS chunks; each chunk's
+// workgroups write fp32 partials [KS][M][d] to the workspace and a second
+// kernel sums them in chunk order (fixed order: bitwise reproducible; no
+// float atomics, no cross-workgroup fences inside a kernel).
 #pragma once
 
 #include "sffn_device.h"
@@ -9,6 +14,18 @@ namespace sffn {
 
 constexpr int kTileCols = 512;
 constexpr int kWaves = 16;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte nontemporal (streaming) load of weights that are read once.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 
 __device__ __forceinline__ int item_count(const int32_t* idx, const int32_t* count, int k_max,
                                           int group, int n_rows) {
@@ -37,47 +54,13 @@ __device__ __forceinline__ float wg_reduce_cols(float4 (*red)[kTileCols / 4], co
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) s += r[ww * kTileCols + threadIdx.x];
   }
-  __syncthreads();
   return s;
 }
 
-// Split-K epilogue shared by the batch-1 kernels: publish this chunk's
-// partial; the last chunk of the tile reduces all chunks in order.
-__device__ inline void splitk_finish(float4 (*red)[kTileCols / 4], int* last_flag, float part,
-                              float* partials, uint32_t* counter, int KS, int ks, int tile,
-                              int d, const float* alpha, float* out, int accumulate) {
-  const int c = tile * kTileCols + (int)threadIdx.x;
-  if (threadIdx.x < kTileCols && c < d) partials[(size_t)ks * d + c] = part;
-  // One agent-scope fence per workgroup (release of the whole group's
-  // partial, made cumulative by the barrier), then the arrival counter.
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(counter, 1u);
-    *last_flag = (prev == (unsigned)(KS - 1));
-    if (*last_flag) __threadfence();   // acquire: the other chunks' partials
-  }
-  __syncthreads();
-  if (!*last_flag) return;
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = tile * kTileCols + 8 * lane;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (col < d) {
-    for (int kk = w; kk < KS; kk += kWaves) {
-      const float4 p = *reinterpret_cast<const float4*>(partials + (size_t)kk * d + col);
-      const float4 q = *reinterpret_cast<const float4*>(partials + (size_t)kk * d + col + 4);
-      acc[0] += p.x; acc[1] += p.y; acc[2] += p.z; acc[3] += p.w;
-      acc[4] += q.x; acc[5] += q.y; acc[6] += q.z; acc[7] += q.w;
-    }
-  }
-  const float total = wg_reduce_cols(red, acc);
-  if (threadIdx.x < kTileCols && c < d) {
-    const float al = alpha ? *alpha : 1.f;
-    const float base = accumulate ? out[c] : 0.f;
-    out[c] = base + al * total;
-  }
-  if (threadIdx.x == 0) *counter = 0u;
-}
+// Launch the ordered reduction: out[m][c] = (accumulate ? out[m][c] : 0) +
+// alpha[m] * sum_{k < KS} partials[k][m][c]   (partials [KS][Mp][d]).
+hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, int d,
+                                const float* alpha, float* out, int ld_out, int accumulate,
+                                hipStream_t s);
 
 }  // namespace sffn

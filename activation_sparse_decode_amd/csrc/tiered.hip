@@ -14,7 +14,7 @@
 // the lane -> output mapping).  The middle tier is decoded in registers:
 // x_j * What[j][o] = (x_j scale_js) q_jo + x_j zero_js, where the second term
 // is the same for all outputs of the segment and is summed once per lane.
-// Partials are combined by the shared split-K epilogue.
+// Partials are summed in chunk order by the shared split-K reduction.
 #include <hip/hip_fp16.h>
 
 #include "sffn_splitk.h"
@@ -27,9 +27,9 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 
 struct SegBounds { int b[5]; };
 
-__global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid) {
+__global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid,
+                                                      float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
-  __shared__ int last_flag;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int col = tile * kTileCols + 8 * lane;
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
         const bool ok = it < k1;
         const int row = ok ? a.idx_top[it] : 0;
         xv[u] = ok ? a.x[row] : 0.f;
-        wv[u] = (ok && col_ok) ? *reinterpret_cast<const uint4*>(a.Wt + (size_t)row * a.ld_w + col)
+        wv[u] = (ok && col_ok) ? load_stream16(a.Wt + (size_t)row * a.ld_w + col)
                                : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
         const uint8_t* rec = a.rec + (size_t)row * a.rec_bytes;
         xv[u] = ok ? a.x[row] : 0.f;
         hdr[u] = ok ? *reinterpret_cast<const uint32_t*>(rec + hdr_off) : 0u;
-        codes[u] = (ok && col_ok) ? *reinterpret_cast<const uint32_t*>(rec + code_off) : 0u;
+        codes[u] = (ok && col_ok) ? load_stream4(rec + code_off) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -111,10 +111,8 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
   }
 
   const float part = wg_reduce_cols(red, acc);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws);
-  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kCounterBytes);
-  splitk_finish(red, &last_flag, part, partials, counters + tile, KS_top + KS_mid, ks, tile,
-                a.d_out, nullptr, a.y, a.accumulate);
+  const int c = tile * kTileCols + (int)threadIdx.x;
+  if (threadIdx.x < kTileCols && c < a.d_out) partials[(size_t)ks * a.d_out + c] = part;
 }
 
 hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
@@ -131,9 +129,13 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   if (a.k_mid_max == 0) ks_mid = 0;
   else if (ks_mid < 1) ks_mid = 1;
   if (ks_top + ks_mid == 0) ks_mid = 1;   // nothing to read: one chunk writes y
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
   hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, ks_top + ks_mid), dim3(1024), 0, s, a, ks_top,
-                     ks_mid);
-  return hipGetLastError();
+                     ks_mid, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(partials, ks_top + ks_mid, 1, 1, a.d_out, nullptr, a.y, a.d_out,
+                              a.accumulate, s);
 }
 
 // ------------------------------------------------------------------ encoder

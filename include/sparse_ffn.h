@@ -36,9 +36,9 @@
  *  - Device-side preconditions that cannot be checked on the host:
  *    0 <= idx[i] < n_rows / group, indices in a list are distinct, and
  *    counts are >= 0; kernels process min(*count, k_max) entries.
- *  - Calls that take a workspace need it zero-filled once after allocation;
- *    every call leaves its counters at zero again.  One workspace must not
- *    be used by two calls that may run at the same time.
+ *  - Calls that take a workspace use it as scratch for split-K partials and
+ *    packed operands; it needs no initialisation.  One workspace must not be
+ *    used by two calls that may run at the same time.
  */
 #ifndef SPARSE_FFN_H
 #define SPARSE_FFN_H
@@ -93,7 +93,7 @@ int sffn_abi_version(void);
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
- * expansion) and `d_out` outputs per token.  Zero-fill it once. */
+ * expansion) and `d_out` outputs per token. */
 size_t sparse_ffn_workspace_size(int batch, int n_rows, int d_out);
 
 /*
@@ -173,8 +173,9 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
  *  out[b][o] = (accumulate ? out[b][o] : 0) + alpha_b * sum over processed
  *  rows n of m_bn * in[b][n] * W0[n][o], with m_bn = row_mask[b][n] != 0 if
  *  row_mask (uint8 [batch][ld_mask]) is given, else 1, and alpha_b =
- *  alpha[b] (device fp32) if given, else 1.  ld_out >= d.  The sum is
- *  reduced in a fixed order: results are bitwise reproducible run to run.
+ *  alpha[b] (device fp32) if given, else 1.  ld_out >= d.  The row list is
+ *  split over workgroups and the partial sums are added in a fixed order
+ *  (a second kernel): results are bitwise reproducible run to run.
  *  Batch > 1 runs on MFMA (the gathered union as one dense block); the
  *  masked-out products contribute exactly zero.
  *
