@@ -53,8 +53,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_score.restype = _i
         L.sparse_ffn_score.argtypes = [_i, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp]
         L.sparse_ffn_select.restype = _i
-        L.sparse_ffn_select.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _i,
-                                        _vp, _vp, _vp]
+        L.sparse_ffn_select.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
+                                        _i, _vp, _vp, _i, _vp, _vp, _vp]
         L.sparse_ffn_gemv.restype = _i
         L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
                                       _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
@@ -65,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 3:
+        if L.sffn_abi_version() != 4:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -116,16 +116,21 @@ def sparse_ffn_score(mode: int, inp: torch.Tensor, out: torch.Tensor, *, cluster
 
 
 def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *,
-                      nonzero_only: bool = False, include_mask: torch.Tensor | None = None,
+                      cluster: int = 1, nonzero_only: bool = False,
+                      include_mask: torch.Tensor | None = None,
                       mask_out: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
-                      count_out: torch.Tensor | None = None, freq: torch.Tensor | None = None,
-                      stream=None) -> None:
-    rows, n = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
+                      count_out: torch.Tensor | None = None,
+                      idx_top_out: torch.Tensor | None = None,
+                      count_top_out: torch.Tensor | None = None,
+                      freq: torch.Tensor | None = None, stream=None) -> None:
+    rows, width = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
+    n = width // cluster
     _check(lib().sparse_ffn_select(
-        _p(keys), key_type, rows, n, _ld(keys, n), r_lo, r_hi, int(nonzero_only),
+        _p(keys), key_type, rows, n, _ld(keys, width), cluster, r_lo, r_hi, int(nonzero_only),
         _p(include_mask), _p(mask_out), _ld(mask_out, n), _p(idx_out),
-        _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out), _p(freq),
-        _stream(stream)))
+        _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out),
+        _p(idx_top_out), _ld(idx_top_out, idx_top_out.shape[-1] if idx_top_out is not None else 0),
+        _p(count_top_out), _p(freq), _stream(stream)))
 
 
 def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,

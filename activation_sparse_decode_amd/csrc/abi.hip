@@ -97,15 +97,19 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld, in
                   "score launch");
 }
 
-sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld, int r_lo,
-                              int r_hi, int nonzero_only, const uint8_t* include_mask,
-                              uint8_t* mask_out, int ld_mask, int32_t* idx_out, int ld_idx,
-                              int32_t* count_out, uint32_t* freq_inout, void* stream) {
+sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld,
+                              int cluster, int r_lo, int r_hi, int nonzero_only,
+                              const uint8_t* include_mask, uint8_t* mask_out, int ld_mask,
+                              int32_t* idx_out, int ld_idx, int32_t* count_out,
+                              int32_t* idx_top_out, int ld_idx_top, int32_t* count_top_out,
+                              uint32_t* freq_inout, void* stream) {
   REQUIRE(keys != nullptr, SFFN_EINVAL, "select: keys must be non-null");
   REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "select: unknown key type %d", key_type);
   REQUIRE(rows >= 0, SFFN_EINVAL, "select: rows=%d must be >= 0", rows);
   REQUIRE(n >= 1 && n <= 32768, SFFN_EUNSUPPORTED, "select: n=%d outside [1, 32768]", n);
-  REQUIRE(ld >= n, SFFN_EINVAL, "select: ld=%d < n=%d", ld, n);
+  REQUIRE(cluster >= 1, SFFN_EINVAL, "select: cluster=%d must be >= 1", cluster);
+  REQUIRE((long)ld >= (long)n * cluster, SFFN_EINVAL, "select: ld=%d < n*cluster=%ld", ld,
+          (long)n * cluster);
   REQUIRE(r_lo >= 0 && r_lo <= r_hi, SFFN_EINVAL, "select: need 0 <= r_lo=%d <= r_hi=%d", r_lo,
           r_hi);
   REQUIRE(!(nonzero_only && key_type == SFFN_KEY_F32), SFFN_EINVAL,
@@ -117,11 +121,18 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
     REQUIRE(ld_idx >= need, SFFN_EINVAL, "select: ld_idx=%d < %ld", ld_idx, need);
     REQUIRE(aligned(idx_out, 4), SFFN_EINVAL, "select: idx_out must be 4-byte aligned");
   }
+  if (idx_top_out) {
+    const long need = std::min((long)r_lo, (long)n);
+    REQUIRE(ld_idx_top >= need, SFFN_EINVAL, "select: ld_idx_top=%d < %ld", ld_idx_top, need);
+    REQUIRE(aligned(idx_top_out, 4), SFFN_EINVAL, "select: idx_top_out must be 4-byte aligned");
+  }
   if (count_out) REQUIRE(aligned(count_out, 4), SFFN_EINVAL, "select: count_out misaligned");
+  if (count_top_out) REQUIRE(aligned(count_top_out, 4), SFFN_EINVAL, "select: count_top_out misaligned");
   if (freq_inout) REQUIRE(aligned(freq_inout, 4), SFFN_EINVAL, "select: freq misaligned");
   if (rows == 0) return ok();
-  sffn::SelectArgs a{keys, key_type, rows, n, ld, r_lo, r_hi, nonzero_only ? 1 : 0, include_mask,
-                     mask_out, ld_mask, idx_out, ld_idx, count_out, freq_inout};
+  sffn::SelectArgs a{keys, key_type, rows, n, ld, cluster, r_lo, r_hi, nonzero_only ? 1 : 0,
+                     include_mask, mask_out, ld_mask, idx_out, ld_idx, count_out, idx_top_out,
+                     ld_idx_top, count_top_out, freq_inout};
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
 }
 

@@ -92,12 +92,14 @@ hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s);
 hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s);
 
 struct SelectArgs {
-  const void* keys; int key_type; int rows, n, ld;
+  const void* keys; int key_type; int rows, n, ld, cluster;
   int r_lo, r_hi, nonzero_only;
   const uint8_t* include_mask;
   uint8_t* mask_out; int ld_mask;
   int32_t* idx_out; int ld_idx;
   int32_t* count_out;
+  int32_t* idx_top_out; int ld_idx_top;
+  int32_t* count_top_out;
   uint32_t* freq;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);

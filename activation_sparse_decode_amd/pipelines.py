@@ -202,10 +202,10 @@ class TieredProjection:
         self.ws = B.new_workspace(1, k_top + k_mid, n_out, device=dev)
 
     def __call__(self, x: torch.Tensor, y: torch.Tensor) -> None:
-        B.sparse_ffn_select(x, B.KEY_ABS_F32, 0, self.k_top, idx_out=self.idx_top,
-                            count_out=self.cnt[0:1])
+        # one selection yields both tiers: ranks [0, k_top) and [k_top, k_top + k_mid)
         B.sparse_ffn_select(x, B.KEY_ABS_F32, self.k_top, self.k_top + self.k_mid,
-                            idx_out=self.idx_mid, count_out=self.cnt[1:2])
+                            idx_out=self.idx_mid, count_out=self.cnt[1:2],
+                            idx_top_out=self.idx_top, count_top_out=self.cnt[0:1])
         B.sparse_ffn_tiered_gemv(self.Wt, self.rec, self.seg_rows, x, self.idx_top, self.cnt[0:1],
                                  self.k_top, self.idx_mid, self.cnt[1:2], self.k_mid, y,
                                  workspace=self.ws)
@@ -230,7 +230,6 @@ class ReluMoEStack:
         dev = experts[0][0][0].device
         self.r = torch.zeros(top_k, N, dtype=F32, device=dev)
         self.a = torch.zeros(top_k, N, dtype=F32, device=dev)
-        self.kappa = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
         self.cidx = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
         self.ccnt = torch.zeros(top_k, dtype=I32, device=dev)
         self.ws = [B.new_workspace(1, N, d, device=dev) for _ in range(top_k)]
@@ -255,9 +254,10 @@ class ReluMoEStack:
             Wg, Wu, _ = self.experts[l][e]
             B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j], tau_scale=self.tau_scale,
                               rms_eps=self.rms_eps)
-            B.sparse_ffn_score(B.SCORE_CLUSTER_MAX, self.r[j], self.kappa[j], cluster=self.cluster)
-            B.sparse_ffn_select(self.kappa[j], B.KEY_U32, 0, self.nc, nonzero_only=True,
-                                idx_out=self.cidx[j], count_out=self.ccnt[j:j + 1])
+            # clusters holding a nonzero r, keyed by their largest |r| (one call)
+            B.sparse_ffn_select(self.r[j], B.KEY_ABS_F32, 0, self.nc, cluster=self.cluster,
+                                nonzero_only=True, idx_out=self.cidx[j],
+                                count_out=self.ccnt[j:j + 1])
             B.sparse_ffn_gemv(B.OP_GATED, None, Wu, h, self.a[j], idx=self.cidx[j],
                               count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
                               aux=self.r[j], rms_eps=self.rms_eps)

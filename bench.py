@@ -1,26 +1,34 @@
 #!/usr/bin/env python3
 """Decode benchmark of the activation-sparse FFN path on one MI355X.
 
-Workload: the Llama3.2-3B-shaped 28-layer SwiGLU FFN stack (d_model 3072,
-d_ff 8192, bf16 N(0, 0.02^2) weights, seed 0) run the SelectInfer way:
-static base set = top 20% of neurons by Eq (1) over 512 calibration
-tokens, dynamic set = top 20% by frequency of per-token top-30% over a
-256-token prompt, unioned; then decode at batch 1 over the union.
+Default workload (the one the headline metric is quoted on): the
+Llama3.2-3B-shaped 28-layer SwiGLU FFN stack (d_model 3072, d_ff 8192, bf16
+N(0, 0.02^2) weights, seed 0) run the SelectInfer way: static base set =
+top 20% of neurons by Eq (1) over 512 calibration tokens, dynamic set = top
+20% by frequency of per-token top-30% over a 256-token prompt, unioned; then
+decode at batch 1 over the union.  A step is one decode token through all 28
+layers (per layer: gate/up over U_l, then the down product over U_l added to
+the residual).  Calibration, prefill and the per-prompt compaction run once
+before timing (reported under "setup").
 
-A step is one decode token through all 28 layers (per layer: the gathered
-gate/up activations over U_l, then the gathered down product accumulated
-into the residual).  Calibration and prefill run once before timing (their
-times are reported under "setup").  The timed steps replay a HIP graph of
-one step; inputs (weights, index sets, tokens) are resident in HBM.
+Other workloads (--workload): c0 single layer with per-token top-50% (every
+step runs activations, keys, select, compaction and the gathered down
+product), c2 SpAx three-tier QKV + down read, c3 ReLU-sparse MoE stack (32
+layers x 8 experts, top-2, 32-row clusters), c4 batched decode with a
+per-token top-40% union contracted on MFMA (--batch 1/4/8/16).
 
-Reported: "value" = decode us/token (lower is better); "roofline" for the
-dominant kernel (gathered gate/up) from per-launch HIP events; and
-"cpu_baseline" = the CPU oracle on a bounded sample of the same decode.
+Every timed step is replayed from a HIP graph with its inputs resident in
+HBM; the weights cycle through enough copies to exceed the 256 MB Infinity
+Cache.  "roofline" is the workload's dominant kernel: algorithmic bytes per
+launch over its average launch time, the launches replayed alone from a
+graph between HIP events on the stream they run on.  "cpu_baseline" is the
+CPU oracle on a bounded sample of the same work.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,26 +41,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 COPY_CALIB_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rowop_glu_c1.json")
-
-
-def measured_traffic(kernel_sources):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, if it was taken on the current source of that kernel."""
-    import hashlib
-    import json as _json
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            rec = _json.load(fh)
-    except (OSError, ValueError):
-        return None
-    h = hashlib.sha256()
-    for path in kernel_sources:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
-    if rec.get("source_sha256") != h.hexdigest():
-        return None
-    return rec.get("bytes_per_launch")
+CSRC = os.path.join(ROOT, "activation_sparse_decode_amd", "csrc")
+METRIC = "sparse-FFN decode us/token and achieved HBM GB/s (% of peak) at batch 1"
 
 
 def log(msg: str) -> None:
@@ -64,83 +54,134 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=128)
     p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bounded CPU work for the oracle baseline (0 disables it)")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        return os.cpu_count()
+
+
+def measured_traffic(tag: str, sources):
+    """HBM bytes per launch of a dominant kernel from the committed counter
+    summary profiles/traffic_<tag>.json, if it was taken on the current
+    source of that kernel; else None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.json")) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for name in sources:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """Graph capture and HIP-event timing on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def capture(self, body):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            body()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(self, g, reps, before=None):
+        """Total ms of `reps` replays (each optionally preceded by before(i))."""
+        torch = self.torch
+        for i in range(2):
+            if before:
+                before(i)
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            if before:
+                before(i)
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+
+def roofline(kernel, bytes_per_launch, launch_us, traffic=None):
+    achieved = bytes_per_launch / (launch_us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "launch_us": round(launch_us, 3), "bytes_per_launch": int(bytes_per_launch)}
+
+
+def result(value, unit, steps, warmup, ms_per_step, config, **extra):
+    out = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "weight_dtype": "bf16",
+           "data": "synthetic (seeded N(0,0.02^2) bf16 weights, heavy-tailed tokens; "
+                   "no trained weights)",
+           "config": config}
+    out.update(extra)
+    return out
+
+
+def timed_cpu(fn, seconds, per_unit=1):
+    """Run fn(i) until `seconds` of CPU work are done (at least once);
+    returns (seconds per unit, count)."""
+    t0, n = time.perf_counter(), 0
+    while True:
+        fn(n)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return (time.perf_counter() - t0) / (n * per_unit), n
+
+
+# ============================================================ c1: SelectInfer stack
+
 def glu_bytes(u: int, d: int) -> int:
-    """Algorithmic bytes of one gate/up launch over the u compacted neurons:
-    2 bf16 rows of d per neuron, the input h read, the fp32 activations
-    written."""
+    """One gate/up launch over u compacted neurons: 2 bf16 rows of d per
+    neuron, the input h read, the fp32 activations written."""
     return 2 * u * d * 2 + 4 * d + 4 * u
 
 
 def down_bytes(u: int, d: int) -> int:
-    """Down product over the compacted neurons: d output rows of u bf16
+    """Down product over u compacted neurons: d output rows of u bf16
     weights, the activations read, the residual read and written."""
     return u * d * 2 + 4 * u + 2 * 4 * d
 
 
-def cpu_baseline(layers, U_sets, X, seconds: float, rms_eps: float):
-    """Time the CPU oracle's decode of whole tokens through the stack until
-    ``seconds`` of work are done (at least one token)."""
-    import oracle
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        pass
-    t0 = time.perf_counter()
-    tokens = 0
-    while True:
-        h = X[tokens % X.shape[0]].astype(np.float64)
-        for l, (Wg, Wu, WdT) in enumerate(layers):
-            _, y = oracle.decode_over_set(Wg, Wu, WdT, oracle.rms_normalize(h, rms_eps), U_sets[l])
-            h = h + y
-        tokens += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return dict(value=dt / tokens * 1e6, unit="us/token", cores=threads or os.cpu_count(),
-                kind="oracle",
-                sample=f"{tokens} decode token(s) x 28 layers over the same union sets, "
-                       f"numpy fp64, {dt:.1f} s")
-
-
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
-              "multi-GPU mode", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    from activation_sparse_decode_amd import binding as B
-    from activation_sparse_decode_amd import synth
-    from activation_sparse_decode_amd.pipelines import (RMS_EPS, SelectInferStack, pct_count,
-                                                        to_device_bf16)
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    B.lib()
-
+def run_c1(args, torch, B, synth, P, T):
     cfg = synth.SHAPES["c1"]
     L, N, d = cfg["layers"], cfg["n"], cfg["d"]
+    dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    threads = min(16, os.cpu_count() or 1)
-    layers = synth.ffn_stack(args.seed, synth.W_C1, L, N, d, threads=threads)
-    dev_layers = [tuple(to_device_bf16(m, dev) for m in lay) for lay in layers]
+    layers = synth.ffn_stack(args.seed, synth.W_C1, L, N, d, threads=min(16, os.cpu_count() or 1))
+    dev_layers = [tuple(P.to_device_bf16(m, dev) for m in lay) for lay in layers]
     log(f"weights: {L} layers x 3 x [{N} x {d}] bf16 in {time.perf_counter() - t0:.1f} s")
-
-    base_k = pct_count(cfg["base_pct"], N)
-    alpha_k = pct_count(cfg["alpha_pct"], N)
-    beta_k = pct_count(cfg["beta_pct"], N)
-    stack = SelectInferStack(dev_layers, base_k, alpha_k, beta_k,
-                             max_tokens=max(cfg["calib_tokens"], cfg["prompt_tokens"]))
+    stack = P.SelectInferStack(dev_layers, P.pct_count(cfg["base_pct"], N),
+                               P.pct_count(cfg["alpha_pct"], N), P.pct_count(cfg["beta_pct"], N),
+                               max_tokens=max(cfg["calib_tokens"], cfg["prompt_tokens"]))
     Xc = torch.from_numpy(synth.tokens(args.seed, synth.W_C1, 1, cfg["calib_tokens"], d)).to(dev)
     Xp = torch.from_numpy(synth.tokens(args.seed, synth.W_C1, 2, cfg["prompt_tokens"], d)).to(dev)
     n_tok = args.warmup + args.steps
@@ -153,126 +194,404 @@ def main():
     e0.record()
     stack.calibrate(Xc)
     e1.record()
-    stack.prefill(Xp)
+    stack.prefill(Xp)          # includes the per-prompt compaction
     e2.record()
     torch.cuda.synchronize()
     calib_ms, prefill_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
     U_cnt = stack.U_cnt.cpu().numpy().astype(np.int64)
-    log(f"calibration {calib_ms:.1f} ms, prefill {prefill_ms:.1f} ms; |U| mean {U_cnt.mean():.0f}")
-
+    log(f"calibration {calib_ms:.1f} ms, prefill + compaction {prefill_ms:.1f} ms; "
+        f"|U| mean {U_cnt.mean():.0f}")
     step_bytes = int(sum(glu_bytes(u, d) + down_bytes(u, d) for u in U_cnt))
-    glu_total_bytes = int(sum(glu_bytes(u, d) for u in U_cnt))
+    glu_total = int(sum(glu_bytes(u, d) for u in U_cnt))
 
-    # ---- one decode step captured as a HIP graph
     h = torch.zeros(d, dtype=torch.float32, device=dev)
     xcur = torch.zeros(d, dtype=torch.float32, device=dev)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        h.copy_(xcur)
-        stack.decode(h)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        h.copy_(xcur)
-        stack.decode(h)
-    torch.cuda.synchronize()
 
+    def step():
+        h.copy_(xcur)
+        stack.decode(h)
+
+    g = T.capture(step)
     for t in range(args.warmup):
         xcur.copy_(Xd[t])
-        graph.replay()
+        g.replay()
     torch.cuda.synchronize()
+    total_ms = T.replay_ms(g, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
+    us_tok = total_ms * 1e3 / args.steps
+    log(f"decode: {us_tok:.1f} us/token over {args.steps} steps")
 
-    # ---- timed region: K graph-replayed decode steps
-    start, end = ev(), ev()
-    torch.cuda.synchronize()
-    start.record()
-    for t in range(args.warmup, n_tok):
-        xcur.copy_(Xd[t])
-        graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    us_per_token = total_ms * 1e3 / args.steps
-    log(f"decode: {us_per_token:.1f} us/token over {args.steps} steps")
-
-    # ---- dominant kernel (gate/up over the compacted union): its 28
-    # launches of one decode step captured alone in a graph and replayed K
-    # times on the same stream, bracketed by HIP events (per-launch events
-    # in eager mode would add their own overhead to every short launch).
-    glu_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(glu_graph):
-        for l in range(L):
-            stack.decode_gate_up(l, h)
-    torch.cuda.synchronize()
-    for _ in range(2):
-        glu_graph.replay()
-    g0, g1 = ev(), ev()
-    torch.cuda.synchronize()
-    g0.record()
-    for _ in range(args.steps):
-        glu_graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    glu_us = g0.elapsed_time(g1) * 1e3 / (args.steps * L)
-    achieved = glu_total_bytes / L / (glu_us * 1e-6) / 1e9
-    log(f"gate/up over U: {glu_us:.2f} us/launch avg, {achieved:.0f} GB/s")
-
-    # A plain device copy of known size: the reference that scales the HBM
-    # counters (FETCH_SIZE / WRITE_SIZE) of the profiled kernels to bytes.
-    calib = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device=dev)
-    calib_dst = torch.empty_like(calib)
-    calib_dst.copy_(calib)
-    torch.cuda.synchronize()
+    gg = T.capture(lambda: [stack.decode_gate_up(l, h) for l in range(L)])
+    glu_us = T.replay_ms(gg, args.steps) * 1e3 / (args.steps * L)
+    log(f"gate/up over U: {glu_us:.2f} us/launch")
 
     cpu = None
     if args.cpu_seconds > 0:
+        import oracle
         U_sets = [stack.U_idx[l, :U_cnt[l]].cpu().numpy() for l in range(L)]
-        cpu = cpu_baseline(layers, U_sets, Xd_host, args.cpu_seconds, RMS_EPS)
-        log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads")
 
-    out = {
-        "metric": "sparse-FFN decode us/token and achieved HBM GB/s (% of peak) at batch 1",
-        "value": round(us_per_token, 3),
-        "unit": "us/token",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(total_ms / args.steps, 5),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "weight_dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02^2) bf16 weights, heavy-tailed tokens; no trained weights)",
-        "config": {
-            "workload": "SelectInfer 28-layer FFN stack, Llama3.2-3B shape (d_model 3072, d_ff 8192), "
-                        "base 20% by Eq (1) over 512 calibration tokens, per-token top-30% / "
-                        "frequency top-20% over a 256-token prompt, union; decode at batch 1",
-            "layers": L, "d_model": d, "d_ff": N, "batch": 1,
-            "union_mean": round(float(U_cnt.mean()), 1), "union_min": int(U_cnt.min()),
-            "union_max": int(U_cnt.max()),
-        },
-        "step_bytes": step_bytes,
-        "step_GBps": round(step_bytes / (us_per_token * 1e-6) / 1e9, 1),
-        "step_frac_of_peak": round(step_bytes / (us_per_token * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-        "setup": {"calibrate_ms": round(calib_ms, 2), "prefill_ms": round(prefill_ms, 2)},
-        "roofline": {
-            "kernel": "rowop_b1_kernel<GLU> (gate/up over the compacted union, SwiGLU epilogue)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic([
-                os.path.join(ROOT, "activation_sparse_decode_amd", "csrc", "rowop_b1.hip"),
-                os.path.join(ROOT, "activation_sparse_decode_amd", "csrc", "sffn_device.h")]),
-            "launch_us": round(glu_us, 3),
-            "bytes_per_launch": int(glu_total_bytes / L),
-        },
-        "cpu_baseline": cpu,
-    }
+        def one(i):
+            hh = Xd_host[i % Xd_host.shape[0]].astype(np.float64)
+            for l, (Wg, Wu, WdT) in enumerate(layers):
+                _, y = oracle.decode_over_set(Wg, Wu, WdT, oracle.rms_normalize(hh, P.RMS_EPS),
+                                              U_sets[l])
+                hh = hh + y
+
+        s, n = timed_cpu(one, args.cpu_seconds)
+        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
+                   sample=f"{n} decode token(s) x 28 layers over the same union sets, numpy fp64")
+
+    config = {"workload": "SelectInfer 28-layer FFN stack, Llama3.2-3B shape (d_model 3072, "
+                          "d_ff 8192), base 20% by Eq (1) over 512 calibration tokens, per-token "
+                          "top-30% / frequency top-20% over a 256-token prompt, union; decode at "
+                          "batch 1 over the per-prompt compacted union",
+              "layers": L, "d_model": d, "d_ff": N, "batch": 1,
+              "union_mean": round(float(U_cnt.mean()), 1), "union_min": int(U_cnt.min()),
+              "union_max": int(U_cnt.max())}
+    return result(us_tok, "us/token", args.steps, args.warmup, total_ms / args.steps, config,
+                  step_bytes=step_bytes,
+                  step_GBps=round(step_bytes / (us_tok * 1e-6) / 1e9, 1),
+                  step_frac_of_peak=round(step_bytes / (us_tok * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  setup={"calibrate_ms": round(calib_ms, 2), "prefill_ms": round(prefill_ms, 2)},
+                  roofline=roofline("rowop_b1_kernel<GLU> (gate/up over the compacted union)",
+                                    glu_total / L, glu_us,
+                                    measured_traffic("rowop_glu_c1",
+                                                     ["rowop_b1.hip", "sffn_device.h"])),
+                  cpu_baseline=cpu)
+
+
+# ============================================================ c0: per-token top-k layer
+
+def run_c0(args, torch, B, synth, P, T):
+    cfg = synth.SHAPES["c0"]
+    N, d = cfg["n"], cfg["d"]
+    keep = P.pct_count(cfg["keep_pct"], N)
+    copies = 16      # 16 x 96 MiB of weights: far beyond the 256 MB Infinity Cache
+    dev = torch.device("cuda:0")
+    lay, host_w = [], None
+    for c in range(copies):
+        mats = [synth.weight_bf16(args.seed, synth.W_C0, c, 0, t, N, d)
+                for t in (synth.T_GATE, synth.T_UP, synth.T_DOWN)]
+        host_w = host_w or mats
+        lay.append(P.SwigluSparseLayer(*[P.to_device_bf16(m, dev) for m in mats], keep))
+    n_tok = (args.steps + 2) * copies
+    X_host = synth.tokens(args.seed, synth.W_C0, 0, n_tok, d)
+    X = torch.from_numpy(X_host).to(dev)
+    xbuf = torch.zeros(copies, d, dtype=torch.float32, device=dev)
+    y = torch.zeros(copies, d, dtype=torch.float32, device=dev)
+
+    def step():
+        for c in range(copies):
+            lay[c](xbuf[c], y[c])
+
+    total_ms = T.replay_ms(T.capture(step), args.steps,
+                           before=lambda i: xbuf.copy_(X[i * copies:(i + 1) * copies]))
+    us_tok = total_ms * 1e3 / (args.steps * copies)
+
+    def glu_only():
+        for c in range(copies):
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, lay[c].Wg, lay[c].Wu, xbuf[c], lay[c].a,
+                              key_out=lay[c].key)
+
+    def sel_only():
+        for c in range(copies):
+            B.sparse_ffn_select(lay[c].key, B.KEY_U32, 0, keep, idx_out=lay[c].idx,
+                                count_out=lay[c].count)
+
+    def down_only():
+        for c in range(copies):
+            B.sparse_ffn_gemv(B.OP_AXPY, lay[c].WdT, None, lay[c].a, y[c], idx=lay[c].idx,
+                              count=lay[c].count, k_max=keep, workspace=lay[c].ws)
+
+    per = lambda body: T.replay_ms(T.capture(body), args.steps) * 1e3 / (args.steps * copies)  # noqa: E731
+    glu_us, sel_us, down_us = per(glu_only), per(sel_only), per(down_only)
+    glu_b = 2 * N * d * 2 + 4 * d + 8 * N
+    sel_b = 4 * N + 4 * keep
+    down_b = keep * d * 2 + 8 * keep + 4 * d
+    step_b = glu_b + sel_b + down_b
+    log(f"c0: {us_tok:.2f} us/token; gate/up {glu_us:.2f} us, select {sel_us:.2f} us, "
+        f"gathered down {down_us:.2f} us")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        s, n = timed_cpu(lambda i: oracle.sparse_swiglu_layer(*host_w, X_host[i], keep),
+                         args.cpu_seconds)
+        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
+                   sample=f"{n} tokens through the layer, numpy fp64")
+    config = {"workload": "single SwiGLU FFN layer, Llama3.2-1B shape (d_model 2048, d_ff 8192), "
+                          "per-token top 50% by |silu(gate)*up|, batch 1 (16 rotating weight copies)",
+              "d_model": d, "d_ff": N, "keep": keep, "batch": 1}
+    return result(us_tok, "us/token", args.steps * copies, 2, total_ms / args.steps, config,
+                  step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
+                  kernels_us={"gate_up_dense": round(glu_us, 3), "select": round(sel_us, 3),
+                              "gathered_down": round(down_us, 3)},
+                  gathered_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
+                  roofline=roofline("rowop_b1_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us),
+                  cpu_baseline=cpu)
+
+
+# ============================================================ c2: SpAx three-tier read
+
+def run_c2(args, torch, B, synth, P, T):
+    cfg = synth.SHAPES["c2"]
+    d, dff = cfg["d"], cfg["d_ff"]
+    n_qkv = sum(cfg["qkv_out"])
+    seg_qkv = [0, cfg["qkv_out"][0], cfg["qkv_out"][0] + cfg["qkv_out"][1], n_qkv]
+    copies = 8       # 8 x ~210 MB (bf16 + codes)
+    dev = torch.device("cuda:0")
+    kq_t, kq_m = P.pct_count(cfg["top_pct"], d), P.pct_count(cfg["mid_pct"], d)
+    kd_t, kd_m = P.pct_count(cfg["top_pct"], dff), P.pct_count(cfg["mid_pct"], dff)
+    projs = []
+    for c in range(copies):
+        Wq = synth.torch_weight_bf16(args.seed, synth.W_C2, c, 0, synth.T_QKV, d, n_qkv, dev)
+        Wd = synth.torch_weight_bf16(args.seed, synth.W_C2, c, 0, synth.T_DOWN, dff, d, dev)
+        projs.append((P.TieredProjection(Wq, seg_qkv, kq_t, kq_m),
+                      P.TieredProjection(Wd, [0, d], kd_t, kd_m)))
+    n_tok = copies * (args.steps + 2)
+    Xq_host = synth.tokens(args.seed, synth.W_C2, 1, n_tok, d)
+    Xd_host = synth.tokens(args.seed, synth.W_C2, 2, n_tok, dff)
+    Xq, Xd = torch.from_numpy(Xq_host).to(dev), torch.from_numpy(Xd_host).to(dev)
+    xq = torch.zeros(copies, d, dtype=torch.float32, device=dev)
+    xd = torch.zeros(copies, dff, dtype=torch.float32, device=dev)
+    yq = torch.zeros(copies, n_qkv, dtype=torch.float32, device=dev)
+    yd = torch.zeros(copies, d, dtype=torch.float32, device=dev)
+
+    def step():
+        for c in range(copies):
+            projs[c][0](xq[c], yq[c])
+            projs[c][1](xd[c], yd[c])
+
+    def before(i):
+        xq.copy_(Xq[i * copies:(i + 1) * copies])
+        xd.copy_(Xd[i * copies:(i + 1) * copies])
+
+    total_ms = T.replay_ms(T.capture(step), args.steps, before=before)
+    us_tok = total_ms * 1e3 / (args.steps * copies)
+
+    def down_only():
+        for c in range(copies):
+            p = projs[c][1]
+            B.sparse_ffn_tiered_gemv(p.Wt, p.rec, p.seg_rows, xd[c], p.idx_top, p.cnt[0:1],
+                                     p.k_top, p.idx_mid, p.cnt[1:2], p.k_mid, yd[c],
+                                     workspace=p.ws)
+
+    down_us = T.replay_ms(T.capture(down_only), args.steps) * 1e3 / (args.steps * copies)
+    rec_q, rec_d = projs[0][0].rec.shape[1], projs[0][1].rec.shape[1]
+    qkv_b = kq_t * n_qkv * 2 + kq_m * rec_q + 8 * (kq_t + kq_m) + 4 * n_qkv
+    down_b = kd_t * d * 2 + kd_m * rec_d + 8 * (kd_t + kd_m) + 4 * d
+    step_b = qkv_b + down_b + 2 * (4 * d + 4 * dff)
+    log(f"c2: {us_tok:.2f} us/token; tiered down {down_us:.2f} us")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        Wq0 = projs[0][0].Wt.cpu().numpy().view(np.uint16)
+        Wd0 = projs[0][1].Wt.cpu().numpy().view(np.uint16)
+        encq, encd = oracle.encode_4bit(Wq0, seg_qkv), oracle.encode_4bit(Wd0, [0, d])
+
+        def one(i):
+            tq, mq = oracle.tier_sets(Xq_host[i], kq_t, kq_m)
+            oracle.tiered_gemv(Wq0, *encq, seg_qkv, Xq_host[i], tq, mq)
+            td, md = oracle.tier_sets(Xd_host[i], kd_t, kd_m)
+            oracle.tiered_gemv(Wd0, *encd, [0, d], Xd_host[i], td, md)
+
+        s, n = timed_cpu(one, args.cpu_seconds)
+        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
+                   sample=f"{n} tokens (QKV + down tiers and products; encoding excluded), "
+                          f"numpy fp64")
+    config = {"workload": "SpAx three-tier read, Llama3.1-8B shape: QKV 4096->4096/1024/1024 and "
+                          "down 14336->4096; 15% bf16 / 35% 4-bit / 50% skipped by |x|; batch 1 "
+                          "(8 rotating weight copies)",
+              "batch": 1, "tiers_qkv": [kq_t, kq_m], "tiers_down": [kd_t, kd_m]}
+    return result(us_tok, "us/token", args.steps * copies, 2, total_ms / args.steps, config,
+                  step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
+                  dense_equivalent_bytes=(d * n_qkv + dff * d) * 2,
+                  roofline=roofline("tiered_kernel (down 14336->4096, 15% bf16 + 35% 4-bit)",
+                                    down_b, down_us),
+                  cpu_baseline=cpu)
+
+
+# ============================================================ c3: ReLU-sparse MoE stack
+
+def run_c3(args, torch, B, synth, P, T):
+    cfg = synth.SHAPES["c3"]
+    L, E, N, d, S = cfg["layers"], cfg["experts"], cfg["n"], cfg["d"], cfg["cluster"]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    experts = [[(synth.torch_weight_bf16(args.seed, synth.W_C3, l, e, synth.T_GATE, N, d, dev,
+                                         cluster=S),
+                 synth.torch_weight_bf16(args.seed, synth.W_C3, l, e, synth.T_UP, N, d, dev),
+                 synth.torch_weight_bf16(args.seed, synth.W_C3, l, e, synth.T_DOWN, N, d, dev))
+                for e in range(E)] for l in range(L)]
+    torch.cuda.synchronize()
+    log(f"c3 weights: {L} x {E} x 3 x [{N} x {d}] bf16 on the device in "
+        f"{time.perf_counter() - t0:.1f} s")
+    steps = min(args.steps, cfg["decode_tokens"])
+    logits = torch.from_numpy(synth.router_logits(args.seed, synth.W_C3, L, steps, E)).to(dev)
+    X_host = synth.tokens(args.seed, synth.W_C3, 1, steps, d)
+    X = torch.from_numpy(X_host).to(dev)
+    moe = P.ReluMoEStack(experts, S, tau_scale=cfg["zero_frac_quantile"] * synth.WEIGHT_STD)
+    moe.route(logits)
+    h = torch.zeros(d, dtype=torch.float32, device=dev)
+
+    # An untimed eager pass records the active-cluster counts (exact bytes
+    # read); then one graph per token (the routed experts differ per token).
+    counts = np.zeros((steps, L, 2), dtype=np.int64)
+    for t in range(steps):
+        h.copy_(X[t])
+
+        def rec(l, tt, hh, chosen, t=t):
+            counts[t, l] = moe.ccnt.cpu().numpy()
+        moe.decode(h, t, record=rec)
+    graphs = [T.capture(lambda t=t: (h.copy_(X[t]), moe.decode(h, t))) for t in range(steps)]
+    for g in graphs[:2]:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for g in graphs:
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    us_tok = total_ms * 1e3 / steps
+    gate_b = N * d * 2 + 4 * d + 4 * N
+    clus_b = 2 * S * d * 2 + 3 * 4 * S          # up + down rows, r read, a written and read
+    step_b = int(L * 2 * (gate_b + 4 * (N // S)) + counts.sum(axis=(1, 2)).mean() * clus_b)
+    log(f"c3: {us_tok:.1f} us/token, {step_b / 1e9:.2f} GB/token, "
+        f"active clusters {counts.mean() / (N // S):.3f}")
+
+    def gates_only():
+        for l in range(L):
+            for j, e in enumerate(moe.route_host[l * moe.T]):
+                B.sparse_ffn_gemv(B.OP_DOT_RELU, experts[l][e][0], None, h, moe.r[j],
+                                  tau_scale=moe.tau_scale, rms_eps=moe.rms_eps)
+
+    gate_us = T.replay_ms(T.capture(gates_only), 4) * 1e3 / (4 * L * 2)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        l_s = [0, L // 2, L - 1]
+        host = {(l, e): tuple(m.cpu().numpy().view(np.uint16) for m in experts[l][e])
+                for l in l_s for e in moe.route_host[l * moe.T]}
+
+        def one(i):
+            l = l_s[i % len(l_s)]
+            x = oracle.rms_normalize(X_host[0], P.RMS_EPS)
+            tau = oracle.relu_threshold(x, cfg["zero_frac_quantile"], synth.WEIGHT_STD)
+            for e in moe.route_host[l * moe.T]:
+                oracle.relu_expert(*host[(l, e)], x, tau, S)
+
+        s, n = timed_cpu(one, args.cpu_seconds)
+        cpu = dict(value=s * L * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
+                   sample=f"{n} layer(s) of 2 routed experts (gate, clusters, up, down) at "
+                          f"token 0, numpy fp64, scaled to {L} layers")
+    config = {"workload": "ReLU-sparse MoE FFN stack, TurboSparse-Mixtral-like: 32 layers x 8 "
+                          "experts (d_model 4096, d_ff 14336), top-2 router, ~90% exact zeros, "
+                          "32-row clusters, batch 1",
+              "layers": L, "experts": E, "batch": 1,
+              "active_cluster_frac": round(float(counts.mean() / (N // S)), 4)}
+    return result(us_tok, "us/token", steps, 2, total_ms / steps, config, step_bytes=step_b,
+                  step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
+                  roofline=roofline("rowop_b1_kernel<DOT_RELU> (dense expert gate)", gate_b,
+                                    gate_us),
+                  cpu_baseline=cpu)
+
+
+# ============================================================ c4: batched union on MFMA
+
+def run_c4(args, torch, B, synth, P, T):
+    cfg = synth.SHAPES["c4"]
+    N, d, batch = cfg["n"], cfg["d"], args.batch
+    keep = P.pct_count(cfg["keep_pct"], N)
+    copies = 4       # 4 x ~535 MB
+    dev = torch.device("cuda:0")
+    lays = []
+    for c in range(copies):
+        w = [synth.torch_weight_bf16(args.seed, synth.W_C4, c, 0, t, N, d, dev)
+             for t in (synth.T_GATE, synth.T_UP, synth.T_DOWN)]
+        lays.append(P.BatchedUnionLayer(*w, keep, batch))
+    n_b = args.steps + 2
+    X_host = synth.tokens(args.seed, synth.W_C4, batch, n_b * copies * batch, d)
+    X = torch.from_numpy(X_host).to(dev).view(n_b * copies, batch, d)
+    xb = torch.zeros(copies, batch, d, dtype=torch.float32, device=dev)
+    Y = torch.zeros(copies, batch, d, dtype=torch.float32, device=dev)
+
+    def step():
+        for c in range(copies):
+            lays[c](xb[c], Y[c])
+
+    total_ms = T.replay_ms(T.capture(step), args.steps,
+                           before=lambda i: xb.copy_(X[i * copies:(i + 1) * copies]))
+    us_batch = total_ms * 1e3 / (args.steps * copies)
+    u = float(np.mean([int(l.cnt.cpu()[0]) for l in lays]))
+
+    def glu_only():
+        for c in range(copies):
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, lays[c].Wg, lays[c].Wu, xb[c], lays[c].A,
+                              key_out=lays[c].K)
+
+    def down_only():
+        for c in range(copies):
+            l = lays[c]
+            B.sparse_ffn_gemv(B.OP_AXPY, l.WdT, None, l.A, Y[c], idx=l.U, count=l.cnt, k_max=N,
+                              row_mask=l.M, workspace=l.ws)
+
+    per = lambda body: T.replay_ms(T.capture(body), args.steps) * 1e3 / (args.steps * copies)  # noqa: E731
+    glu_us, down_us = per(glu_only), per(down_only)
+    glu_b = 2 * N * d * 2 + batch * (4 * d + 8 * N)
+    down_b = int(u * d * 2 + 4 * u + batch * (5 * u + 4 * d))
+    step_b = int(glu_b + down_b + batch * 5 * N)
+    log(f"c4 batch {batch}: {us_batch:.2f} us/batch, union {u:.0f}; MFMA gate/up {glu_us:.2f} us, "
+        f"MFMA union down {down_us:.2f} us")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        w0 = [m.cpu().numpy().view(np.uint16) for m in (lays[0].Wg, lays[0].Wu, lays[0].WdT)]
+        s, n = timed_cpu(lambda i: oracle.batched_union_decode(
+            *w0, X_host[i * batch:(i + 1) * batch], keep), args.cpu_seconds, per_unit=batch)
+        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
+                   sample=f"{n} batch(es) of {batch} tokens, numpy fp64")
+    config = {"workload": f"batched decode, Qwen-27B-like layer (d_model 5120, d_ff 17408), "
+                          f"per-token top 40%, union gathered once and contracted on MFMA, "
+                          f"batch {batch} (4 rotating weight copies)",
+              "d_model": d, "d_ff": N, "batch": batch, "union_mean": u}
+    return result(us_batch / batch, "us/token", args.steps * copies, 2, total_ms / args.steps,
+                  config, us_per_batch=round(us_batch, 3), step_bytes=step_b,
+                  step_GBps=round(step_b / (us_batch * 1e-6) / 1e9, 1),
+                  kernels_us={"gate_up_mfma": round(glu_us, 3),
+                              "union_down_mfma": round(down_us, 3)},
+                  union_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
+                  roofline=roofline("rowop_mfma_kernel<GLU> (batched gate/up)", glu_b, glu_us),
+                  cpu_baseline=cpu)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from activation_sparse_decode_amd import binding as B
+    from activation_sparse_decode_amd import pipelines as P
+    from activation_sparse_decode_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    B.lib()
+    T = Timer(torch)
+    run = {"c0": run_c0, "c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4}[args.workload]
+    out = run(args, torch, B, synth, P, T)
+
+    # A plain device copy of known size: the reference that scales the HBM
+    # counters (FETCH_SIZE / WRITE_SIZE) of profiled kernels to bytes.
+    calib = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    torch.empty_like(calib).copy_(calib)
+    torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 

@@ -89,7 +89,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 3
+#define SFFN_ABI_VERSION 4
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -123,7 +123,13 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  * descending, index ascending) and the entries at ranks [r_lo, r_hi) are
  * selected.  Top-k ([SelectInfer] §5 per-token top alpha and top beta by
  * frequency, §4 top delta) is the range [0, k); the SpAx middle tier (Fig 2)
- * is [k_top, k_top + k_mid).
+ * is [k_top, k_top + k_mid), and the same call can return the top tier
+ * [0, k_top) as a second list.
+ *  cluster      : entry c is the block of `cluster` contiguous values
+ *                 keys[c*cluster .. c*cluster+cluster-1] and its key is the
+ *                 largest key of the block ([PowerInfer-2] "Neuron Cluster
+ *                 Decomposition": a cluster is selected as a unit); 1 for
+ *                 single values.  ld >= n * cluster.
  *  nonzero_only : only entries with a nonzero key take part (ranks count
  *                 among them); not allowed with SFFN_KEY_F32.
  *  include_mask : nullable uint8 [n]; nonzero entries are OR-ed into every
@@ -132,17 +138,23 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  *  idx_out      : nullable int32 [rows][ld_idx]: selected indices, ascending.
  *                 ld_idx >= n if include_mask is set, else >= r_hi - r_lo.
  *  count_out    : nullable int32 [rows]: number selected.
+ *  idx_top_out  : nullable int32 [rows][ld_idx_top]: the entries at ranks
+ *                 [0, r_lo), ascending (ld_idx_top >= r_lo); count_top_out
+ *                 nullable int32 [rows] their number.  Not affected by
+ *                 include_mask.
  *  freq_inout   : nullable uint32 [n]: += 1 for each row that selects the
  *                 entry (the frequency count of [SelectInfer] §5).
  * Limits: 1 <= n <= 32768, 0 <= r_lo <= r_hi, r_hi may exceed the number of
  * eligible entries (then it is clipped).  The result is unique: bit-exact.
  */
 sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld,
-                              int r_lo, int r_hi, int nonzero_only,
+                              int cluster, int r_lo, int r_hi, int nonzero_only,
                               const uint8_t* include_mask,
                               uint8_t* mask_out, int ld_mask,
                               int32_t* idx_out, int ld_idx,
                               int32_t* count_out,
+                              int32_t* idx_top_out, int ld_idx_top,
+                              int32_t* count_top_out,
                               uint32_t* freq_inout,
                               void* stream);
 

@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 3
+    assert L.sffn_abi_version() == 4
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -54,25 +54,40 @@ def status_and_msg(L, rc):
     return rc, L.sffn_last_error().decode()
 
 
+def select(L, keys=FAKE, key_type=0, rows=1, n=8, ld=8, cluster=1, r_lo=0, r_hi=4, nz=0,
+           include=NULL, mask=NULL, ld_mask=0, idx=NULL, ld_idx=0, count=NULL, idx_top=NULL,
+           ld_idx_top=0, count_top=NULL, freq=NULL):
+    return status_and_msg(L, L.sparse_ffn_select(keys, key_type, rows, n, ld, cluster, r_lo, r_hi,
+                                                 nz, include, mask, ld_mask, idx, ld_idx, count,
+                                                 idx_top, ld_idx_top, count_top, freq, NULL))
+
+
 def test_select_validation(L):
-    sel = L.sparse_ffn_select
-    rc, msg = status_and_msg(L, sel(NULL, 0, 1, 8, 8, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    rc, msg = select(L, keys=NULL)
     assert rc == 1 and "keys" in msg
-    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 40000, 40000, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    rc, msg = select(L, n=40000, ld=40000)
     assert rc == 2 and "32768" in msg
-    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 4, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    rc, msg = select(L, ld=4)
     assert rc == 1 and "ld" in msg
-    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 8, 5, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    rc, msg = select(L, r_lo=5)
     assert rc == 1 and "r_lo" in msg
-    rc, msg = status_and_msg(L, sel(FAKE, 2, 1, 8, 8, 0, 4, 1, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    rc, msg = select(L, key_type=2, nz=1)
     assert rc == 1 and "signed" in msg
-    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 8, 0, 4, 0, NULL, NULL, 0, FAKE, 3, NULL, NULL, NULL))
+    rc, msg = select(L, idx=FAKE, ld_idx=3)
     assert rc == 1 and "ld_idx" in msg
     # with a union mask the index list may hold up to n entries
-    rc, msg = status_and_msg(L, sel(FAKE, 0, 1, 8, 8, 0, 4, 0, FAKE, NULL, 0, FAKE, 4, NULL, NULL, NULL))
+    rc, msg = select(L, include=FAKE, idx=FAKE, ld_idx=4)
     assert rc == 1 and "ld_idx" in msg
-    rc, msg = status_and_msg(L, sel(FAKE, 7, 1, 8, 8, 0, 4, 0, NULL, NULL, 0, NULL, 0, NULL, NULL, NULL))
+    rc, msg = select(L, key_type=7)
     assert rc == 1 and "key type" in msg
+    # clusters: ld must hold n * cluster values
+    rc, msg = select(L, cluster=0)
+    assert rc == 1 and "cluster" in msg
+    rc, msg = select(L, n=8, ld=16, cluster=4)
+    assert rc == 1 and "n*cluster" in msg
+    # the top list holds the ranks [0, r_lo)
+    rc, msg = select(L, r_lo=3, r_hi=6, idx_top=FAKE, ld_idx_top=2)
+    assert rc == 1 and "ld_idx_top" in msg
 
 
 def gemv(L, op=3, W0=FAKE, W1=FAKE, n_rows=64, d=64, ld_w=64, inp=FAKE, batch=1, ld_in=64,

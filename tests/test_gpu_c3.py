@@ -9,7 +9,7 @@ import torch
 import oracle
 from activation_sparse_decode_amd import synth
 from activation_sparse_decode_amd.pipelines import RMS_EPS, ReluMoEStack, to_device_bf16
-from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
+from gpu_common import assert_close, banner, dev, gpu, host, needs_gpu
 
 pytestmark = [gpu, needs_gpu]
 
@@ -62,7 +62,6 @@ def run_moe(L, E, N, d, n_tokens, check_layers, on_device_weights, seed=0):
                 if check:
                     torch.cuda.synchronize()
                     got["r"] = host(moe.r).copy()
-                    got["kappa"] = host_u32(moe.kappa).copy()
                     got["cidx"] = host(moe.cidx).copy()
                     got["ccnt"] = host(moe.ccnt).copy()
                     got["a"] = host(moe.a).copy()
@@ -79,7 +78,6 @@ def run_moe(L, E, N, d, n_tokens, check_layers, on_device_weights, seed=0):
                 Wg, Wu, WdT = (host_bits(m) for m in experts[l][e])
                 r = got["r"][j]
                 assert_close(r, oracle.relu_gate(Wg, x, tau), what=f"r l={l} t={t} e={e}")
-                assert np.array_equal(got["kappa"][j], oracle.cluster_max_key(oracle.key_abs(r), CLUSTER))
                 clusters = oracle.active_clusters(r, CLUSTER)
                 n_c = int(got["ccnt"][j])
                 assert n_c == clusters.size and np.array_equal(got["cidx"][j][:n_c], clusters)

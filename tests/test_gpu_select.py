@@ -107,3 +107,59 @@ def test_nonzero_only_clusters():
     kappa = np.where(rng.random((1, 448)) < 0.2, rng.integers(1, 1 << 30, size=(1, 448)), 0)
     check(kappa.astype(np.uint32), B.KEY_U32, 0, 448, nonzero_only=True)
     check(np.zeros((1, 448), np.uint32), B.KEY_U32, 0, 448, nonzero_only=True)
+
+
+def test_cluster_keys():
+    """cluster > 1: an entry is a block of contiguous values keyed by its
+    largest |value| (the oracle forms the cluster keys, then ranks them)."""
+    banner("select cluster keys")
+    rng = np.random.default_rng(8)
+    for n_c, c in [(448, 32), (1000, 3), (4096, 4), (9000, 2)]:
+        r = np.where(rng.random((2, n_c * c)) < 0.1, rng.standard_normal((2, n_c * c)), 0.0)
+        r = r.astype(np.float32)
+        r[1, : c * 5] = r[1, c * 5: c * 10]             # tied clusters
+        keys = dev(r)
+        idx = torch.full((2, n_c), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+        mask = torch.zeros(2, n_c, dtype=torch.uint8, device="cuda")
+        for nz, lo, hi in [(True, 0, n_c), (False, 0, n_c // 3), (True, 2, n_c // 5 + 2)]:
+            B.sparse_ffn_select(keys, B.KEY_ABS_F32, lo, hi, cluster=c, nonzero_only=nz,
+                                idx_out=idx, count_out=cnt, mask_out=mask)
+            torch.cuda.synchronize()
+            gi, gc, gm = host(idx), host(cnt), host(mask)
+            for row in range(2):
+                ck = oracle.cluster_max_key(oracle.key_abs(r[row]), c)
+                exp = oracle.rank_range(ck, lo, hi, nz, None)
+                assert gc[row] == exp.size, (n_c, c, row)
+                assert np.array_equal(gi[row, :gc[row]], exp), (n_c, c, row)
+                m = np.zeros(n_c, np.uint8)
+                m[exp] = 1
+                assert np.array_equal(gm[row], m)
+                if nz and lo == 0:
+                    assert np.array_equal(exp, oracle.active_clusters(r[row], c))
+
+
+@pytest.mark.parametrize("n,k_top,k_mid", [(6144, 1536, 3072), (17408, 4352, 8704),
+                                           (100, 0, 30), (100, 30, 0), (5000, 5000, 10)])
+def test_two_lists(n, k_top, k_mid):
+    """One call yields the ranks [0, k_top) and [k_top, k_top + k_mid) as two
+    ascending lists (the two SpAx tiers)."""
+    banner(f"select two lists n={n}")
+    rng = np.random.default_rng(n + k_top)
+    x = (rng.standard_normal((3, n)) * np.exp(rng.standard_normal((3, n)))).astype(np.float32)
+    x[2, : n // 2] = np.round(x[2, : n // 2])              # heavy ties
+    keys = dev(x)
+    mid = torch.full((3, max(1, k_mid)), -1, dtype=torch.int32, device="cuda")
+    top = torch.full((3, max(1, k_top)), -1, dtype=torch.int32, device="cuda")
+    cm = torch.zeros(3, dtype=torch.int32, device="cuda")
+    ct = torch.zeros(3, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select(keys, B.KEY_ABS_F32, k_top, k_top + k_mid, idx_out=mid, count_out=cm,
+                        idx_top_out=top, count_top_out=ct)
+    torch.cuda.synchronize()
+    gm, gt, gcm, gct = host(mid), host(top), host(cm), host(ct)
+    for row in range(3):
+        k = oracle.key_abs(x[row])
+        exp_top = oracle.rank_range(k, 0, k_top, False, None)
+        exp_mid = oracle.rank_range(k, k_top, k_top + k_mid, False, None)
+        assert gct[row] == exp_top.size and np.array_equal(gt[row, :gct[row]], exp_top), row
+        assert gcm[row] == exp_mid.size and np.array_equal(gm[row, :gcm[row]], exp_mid), row
