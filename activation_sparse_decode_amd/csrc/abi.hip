@@ -108,6 +108,8 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
   REQUIRE(rows >= 0, SFFN_EINVAL, "select: rows=%d must be >= 0", rows);
   REQUIRE(n >= 1 && n <= 32768, SFFN_EUNSUPPORTED, "select: n=%d outside [1, 32768]", n);
   REQUIRE(cluster >= 1, SFFN_EINVAL, "select: cluster=%d must be >= 1", cluster);
+  REQUIRE(cluster == 1 || n <= 4096, SFFN_EUNSUPPORTED,
+          "select: n=%d clusters exceed 4096 (the cluster-mode limit)", n);
   REQUIRE((long)ld >= (long)n * cluster, SFFN_EINVAL, "select: ld=%d < n*cluster=%ld", ld,
           (long)n * cluster);
   REQUIRE(r_lo >= 0 && r_lo <= r_hi, SFFN_EINVAL, "select: need 0 <= r_lo=%d <= r_hi=%d", r_lo,

@@ -62,45 +62,56 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
   if (threadIdx.x < kTileCols && c < a.d) partials[(size_t)ks * a.d + c] = part;
 }
 
-// Ordered reduction of [KS][Mp][d] partials: a 256-thread workgroup covers
-// 256 columns of one token row; wave w sums chunks w, w+4, ... (float4 per
-// lane), then the four wave sums are added in wave order.
+// Ordered reduction of [KS][Mp][d] partials.  A 256-thread workgroup covers
+// 64 columns of one token row: lane group g (16 lanes, one float4 each) sums
+// the chunks g, g+16, ... with all of its loads issued before the first add
+// (the reduction is latency-bound, not bandwidth-bound), then the 16 group
+// sums are added in group order.  The order is fixed, so results are
+// reproducible run to run.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partials,
                                                             int KS, int Mp, int d,
                                                             const float* __restrict__ alpha,
                                                             float* __restrict__ out, int ld_out,
                                                             int accumulate) {
-  __shared__ float4 red[4][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kGroups = 16;
+  constexpr int kPerGroup = kMaxSplit / kGroups;
+  __shared__ float4 red[kGroups][16];
+  const int q = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int m = blockIdx.y;
-  const int c = blockIdx.x * 256 + 4 * lane;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < d) {
-    for (int k = w; k < KS; k += 4) {
-      const float4 p = *reinterpret_cast<const float4*>(partials + ((size_t)k * Mp + m) * d + c);
-      s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
-    }
-  }
-  red[w][lane] = s;
-  __syncthreads();
-  if (w != 0 || c >= d) return;
-  float4 t = red[0][lane];
+  const int c = blockIdx.x * 64 + 4 * q;
+  float4 v[kPerGroup];
 #pragma unroll
-  for (int ww = 1; ww < 4; ++ww) {
-    const float4 q = red[ww][lane];
-    t.x += q.x; t.y += q.y; t.z += q.z; t.w += q.w;
+  for (int i = 0; i < kPerGroup; ++i) {
+    const int k = g + kGroups * i;
+    v[i] = (k < KS && c < d)
+               ? *reinterpret_cast<const float4*>(partials + ((size_t)k * Mp + m) * d + c)
+               : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 s = v[0];
+#pragma unroll
+  for (int i = 1; i < kPerGroup; ++i) {
+    s.x += v[i].x; s.y += v[i].y; s.z += v[i].z; s.w += v[i].w;
+  }
+  red[g][q] = s;
+  __syncthreads();
+  if (g != 0 || c >= d) return;
+  float4 t = red[0][q];
+#pragma unroll
+  for (int gg = 1; gg < kGroups; ++gg) {
+    const float4 r = red[gg][q];
+    t.x += r.x; t.y += r.y; t.z += r.z; t.w += r.w;
   }
   const float al = alpha ? alpha[m] : 1.f;
   float* o = out + (size_t)m * ld_out + c;
-  const float v[4] = {t.x, t.y, t.z, t.w};
+  const float tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = (accumulate ? o[e] : 0.f) + al * v[e];
+  for (int e = 0; e < 4; ++e) o[e] = (accumulate ? o[e] : 0.f) + al * tv[e];
 }
 
 hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, int d,
                                 const float* alpha, float* out, int ld_out, int accumulate,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((d + 255) / 256, M), dim3(256), 0, s, partials, KS,
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((d + 63) / 64, M), dim3(256), 0, s, partials, KS,
                      Mp, d, alpha, out, ld_out, accumulate);
   return hipGetLastError();
 }

@@ -9,45 +9,59 @@
 // values whose key is the largest key of the block (PowerInfer-2 guide,
 // "Neuron Cluster Decomposition": the cluster is the unit that is selected).
 //
-// Method: NT threads; thread t owns the KPT consecutive entries
-// [t*KPT, (t+1)*KPT) in registers, so thread order is index order.
-//  1. MSB-first radix search (digits of 11, 11 and 10 bits, LDS histograms)
-//     finds, for each bound r in {r_hi, r_lo}, the key T_r of the r-th
-//     largest entry and how many entries equal to T_r fall inside the top r.
-//     Both searches share one histogram (16-bit halves of one counter).  A
-//     bound that covers every eligible entry needs no search (pure
-//     compaction, e.g. the nonzero clusters of a ReLU layer).
-//  2. An exclusive scan of per-thread "key == T_r" counts gives every entry
-//     its rank among equal keys in index order, which decides the ties
-//     exactly as the (key desc, index asc) order does.
-//  3. Exclusive scans of the selected counts give output positions: the
-//     compacted index lists come out ascending.
+// Method: NT threads; thread t owns the entries j*NT + t (j < KPT), so every
+// load and every mask store of a wave is contiguous.  One workgroup handles
+// a row (at most 32768 entries), so the cost is the instructions each wave
+// issues and the chain of barriers; the kernel keeps both short.
+//  1. The largest eligible key (an OR over the row) fixes the most
+//     significant bit that varies, so the digits start there: keys that fit
+//     in 11 bits (e.g. frequency counts) take one pass, float magnitudes 3.
+//  2. MSB-first radix search finds, for each bound r in {r_hi, r_lo}, the key
+//     T_r of the r-th largest entry, how many entries equal to T_r fall
+//     inside the top r, and how many equal T_r in all.  Both bounds share
+//     one LDS histogram (16-bit halves of one counter); wave 0 scans it with
+//     DPP lane moves.  After the first pass only the keys in the bins that
+//     hold a bound can matter; they are appended to an LDS list, and the
+//     later passes count only that list.  A bound that covers every eligible
+//     entry needs no search (pure compaction, e.g. the nonzero clusters of a
+//     ReLU layer).
+//  3. Index-order positions come from wave ballots: an entry's position
+//     among the entries with some property is the count in the (j, wave)
+//     blocks before its own plus the count of lower lanes in its ballot.
+//     This places the selected indices (ascending lists, contiguous stores)
+//     and, when T_r is tied across the bound, ranks the tied entries in
+//     index order, which decides them as the (key desc, index asc) order
+//     does.
 // Everything is integer: the result is unique and bit-exact.
 #include "sffn_device.h"
 
 namespace sffn {
 
-template <int NW>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, off, kWave);
-    if (lane >= off) x += y;
+constexpr int kMaxClusters = 4096;   // entries of a row in cluster mode
+
+// Inclusive scan over the 64 lanes of a wave with DPP moves: shifts of 1, 2,
+// 4, 8 within each row of 16 lanes, then rows 1 and 3 take lane 15 of the
+// row below and rows 2 and 3 take lane 31.  Lanes a move leaves out get 0.
+template <bool kOr>
+__device__ __forceinline__ uint32_t wave_incl(uint32_t x) {
+#define SFFN_DPP_STEP(ctrl, rows, bc)                                                      \
+  {                                                                                        \
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, rows, 0xf, bc); \
+    x = kOr ? (x | y) : (x + y);                                                           \
   }
-  if (lane == 63) tmp[w] = x;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t s = tmp[i];
-    before += (i < w) ? s : 0u;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return before + x - v;
+  SFFN_DPP_STEP(0x111, 0xf, true)
+  SFFN_DPP_STEP(0x112, 0xf, true)
+  SFFN_DPP_STEP(0x114, 0xf, true)
+  SFFN_DPP_STEP(0x118, 0xf, true)
+  SFFN_DPP_STEP(0x142, 0xa, false)
+  SFFN_DPP_STEP(0x143, 0xc, false)
+#undef SFFN_DPP_STEP
+  return x;
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 __device__ __forceinline__ uint32_t key_of_bits(int key_type, uint32_t b) {
@@ -56,194 +70,335 @@ __device__ __forceinline__ uint32_t key_of_bits(int key_type, uint32_t b) {
   return key_signed(__uint_as_float(b));
 }
 
-__device__ __forceinline__ uint32_t make_key(const SelectArgs& a, size_t off) {
-  return key_of_bits(a.key_type, reinterpret_cast<const uint32_t*>(a.keys)[off]);
+// Index-order positions of two per-entry predicates, given as bit masks
+// (bit j: entry j*NT + t).  ordered_counts stores the packed (hi half, lo
+// half) count of every (j, wave) block; after a barrier, ordered_offsets
+// gives lane j the packed count of all blocks before (j, this wave) and the
+// totals; an entry's position is then that offset (read from lane j) plus
+// the number of lower lanes in its ballot.
+template <int NT, int KPT>
+__device__ __forceinline__ void ordered_counts(uint32_t bits_h, uint32_t bits_l,
+                                               uint32_t (*cnt)[NT / 64]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t bh = __ballot((bits_h >> j) & 1u);
+    const uint64_t bl = __ballot((bits_l >> j) & 1u);
+    if (lane == 0) cnt[j][w] = ((uint32_t)__popcll(bh) << 16) | (uint32_t)__popcll(bl);
+  }
+}
+
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t ordered_offsets(uint32_t (*cnt)[NT / 64], uint32_t& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t row_total = 0, row_below = 0;
+  if (lane < KPT) {
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const uint32_t c = cnt[lane][ww];
+      row_total += c;
+      row_below += ww < w ? c : 0u;
+    }
+  }
+  const uint32_t incl = wave_incl<false>(row_total);
+  total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  return incl - row_total + row_below;
+}
+
+__device__ __forceinline__ uint32_t ordered_pos(uint32_t off_j, uint32_t bits_h, uint32_t bits_l,
+                                                int j) {
+  const uint64_t bh = __ballot((bits_h >> j) & 1u);
+  const uint64_t bl = __ballot((bits_l >> j) & 1u);
+  return off_j + ((lanes_below(bh) << 16) | lanes_below(bl));
+}
+
+// Wave 0's scan of one radix pass over nb bins (nb <= 2048, H 16-byte
+// aligned): for each bound it writes the digit holding rank `rem` (in the
+// packed counters' hi or lo half), the rank left inside that digit and the
+// digit's count.  Lane l holds q = nb/64 consecutive bins (lane 0 the
+// largest digits), read as 16-byte vectors; a DPP scan gives the counts
+// above each lane, and the lane that holds the rank walks its bins from the
+// top.
+__device__ __forceinline__ void scan_pass(const uint32_t* H, int nb, bool want_hi, uint32_t rem_hi,
+                                          bool want_lo, uint32_t rem_lo, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t h[32];
+  int q, base;
+  if (nb >= 256) {   // 4..32 bins per lane
+    q = nb >> 6;
+    base = nb - q * (lane + 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = 4 * c < q ? *reinterpret_cast<const uint4*>(H + base + 4 * c)
+                                : make_uint4(0u, 0u, 0u, 0u);
+      h[4 * c] = v.x; h[4 * c + 1] = v.y; h[4 * c + 2] = v.z; h[4 * c + 3] = v.w;
+    }
+  } else {           // at most 4 bins per lane: one bin per lane
+    q = 1;
+    base = nb - 1 - lane;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) h[i] = 0u;
+    h[0] = base >= 0 ? H[base] : 0u;
+    if (nb > 64) {   // 128 bins: two per lane
+      q = 2;
+      base = nb - 2 * (lane + 1);
+      h[0] = H[base];
+      h[1] = H[base + 1];
+    }
+  }
+  // group sums of 4 bins, then the lane total
+  uint32_t g4[8];
+  uint32_t own = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    g4[c] = h[4 * c] + h[4 * c + 1] + h[4 * c + 2] + h[4 * c + 3];
+    own += g4[c];
+  }
+  const uint32_t above = wave_incl<false>(own) - own;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const bool want = b == 0 ? want_hi : want_lo;
+    if (!want) continue;
+    const int half = b == 0 ? 16 : 0;
+    const uint32_t rem = b == 0 ? rem_hi : rem_lo;
+    const uint32_t acc0 = (above >> half) & 0xFFFFu;
+    if (!(acc0 < rem && rem <= acc0 + ((own >> half) & 0xFFFFu))) continue;   // one lane
+    // the group of 4 bins holding the rank, then the bin (descending digits);
+    // once the rank is passed, acc >= rem and no later group can match
+    uint32_t acc = acc0, acc_at = acc0;
+    int gsel = 0;
+#pragma unroll
+    for (int c = 7; c >= 0; --c) {
+      const uint32_t n = (g4[c] >> half) & 0xFFFFu;
+      if (acc < rem && rem <= acc + n) { gsel = c; acc_at = acc; }
+      acc += n;
+    }
+    acc = acc_at;
+    uint32_t hb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v = c == gsel ? h[4 * c + e] : v;
+      hb[e] = (v >> half) & 0xFFFFu;
+    }
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      if (acc < rem && rem <= acc + hb[e]) {
+        out[3 * b] = (uint32_t)(base + 4 * gsel + e); out[3 * b + 1] = rem - acc; out[3 * b + 2] = hb[e];
+      }
+      acc += hb[e];
+    }
+  }
 }
 
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr int NW = NT / 64;
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t tmp[NW];
-  __shared__ uint32_t found[4];   // digit_hi, rem_hi, digit_lo, rem_lo
+  constexpr int kBins = 2048;
+  constexpr int kCap = NT * KPT < 8192 ? NT * KPT : 8192;   // candidate list
+  __shared__ __align__(16) uint32_t hist[3][kBins + 4];   // one per pass; bin kBins: not counted
+  __shared__ uint32_t cand[kCap];
+  __shared__ uint32_t cnt[2][KPT][NW];      // ballot counts of the two ordered scans
+  __shared__ uint32_t wsum[2][NW];          // per wave: OR of eligible keys, eligible count
+  __shared__ uint32_t found[8];             // hi: digit, rem, count; lo: digit, rem, count
+  __shared__ uint32_t ncand;
+  __shared__ uint32_t ckey[kMaxClusters];   // cluster keys (cluster > 1)
 
   const int row = blockIdx.x;
   const int t = threadIdx.x;
-  const int base = t * KPT;
+  const int lane = t & 63, w = t >> 6;
   const size_t roff = (size_t)row * a.ld;
 
+  // ---- keys; every load is issued before the first use
   uint32_t key[KPT];
-  uint32_t elig = 0;   // bit j: entry base+j takes part
-  // 16-byte loads when a thread's four consecutive keys are aligned and in range
-  const bool vec = KPT % 4 == 0 && a.cluster == 1 && (a.ld & 3) == 0 &&
-                   (reinterpret_cast<uintptr_t>(a.keys) & 15) == 0;
+  const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.keys) + roff;
+  if (a.cluster == 1) {
 #pragma unroll
-  for (int j4 = 0; j4 < KPT; j4 += 4) {
-    if (vec && base + j4 + 3 < a.n) {
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          reinterpret_cast<const uint32_t*>(a.keys) + roff + base + j4);
-      const uint32_t b[4] = {v.x, v.y, v.z, v.w};
+    for (int j = 0; j < KPT; ++j) key[j] = j * NT + t < a.n ? kp[j * NT + t] : 0u;
 #pragma unroll
-      for (int e = 0; e < 4 && j4 + e < KPT; ++e) key[j4 + e] = key_of_bits(a.key_type, b[e]);
+    for (int j = 0; j < KPT; ++j) key[j] = key_of_bits(a.key_type, key[j]);
+  } else {
+    // cluster keys: coalesced reads of the n*cluster values, max per cluster
+    // in LDS (the value index i belongs to cluster floor((i + 0.5) / cluster),
+    // exact in fp32 for these sizes)
+    for (int c = t; c < a.n; c += NT) ckey[c] = 0u;
+    __syncthreads();
+    const int total = a.n * a.cluster;
+    const float inv = 1.0f / (float)a.cluster;
+    if ((a.cluster & 3) == 0 && (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.keys) & 15) == 0) {
+      for (int i = 4 * t; i < total; i += 4 * NT) {   // 4 values of one cluster
+        const uint4 v = *reinterpret_cast<const uint4*>(kp + i);
+        const uint32_t m = max(max(key_of_bits(a.key_type, v.x), key_of_bits(a.key_type, v.y)),
+                               max(key_of_bits(a.key_type, v.z), key_of_bits(a.key_type, v.w)));
+        if (m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+      }
     } else {
-#pragma unroll
-      for (int e = 0; e < 4 && j4 + e < KPT; ++e) {
-        const int n = base + j4 + e;
-        uint32_t k = 0;
-        if (n < a.n) {
-          if (a.cluster == 1) {
-            k = make_key(a, roff + n);
-          } else {
-            const size_t c0 = roff + (size_t)n * a.cluster;
-            for (int g = 0; g < a.cluster; ++g) {
-              const uint32_t v = make_key(a, c0 + g);
-              k = v > k ? v : k;
-            }
-          }
-        }
-        key[j4 + e] = k;
+      for (int i = t; i < total; i += NT) {
+        const uint32_t m = key_of_bits(a.key_type, kp[i]);
+        if (m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
       }
     }
-  }
+    __syncthreads();
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (base + j < a.n && (!a.nonzero_only || key[j] != 0u)) elig |= 1u << j;
+    for (int j = 0; j < KPT; ++j) key[j] = j * NT + t < a.n ? ckey[j * NT + t] : 0u;
+  }
+  uint32_t elig = 0, kor = 0, ecount = 0;   // bit j: entry j*NT+t takes part
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool e = (j * NT + t < a.n) & (!a.nonzero_only | (key[j] != 0u));
+    elig |= (e ? 1u : 0u) << j;
+    kor |= e ? key[j] : 0u;
+    ecount += (uint32_t)__popcll(__ballot(e));
+  }
+  kor = wave_incl<true>(kor);
+  if (lane == 63) { wsum[0][w] = kor; wsum[1][w] = ecount; }
+  for (int i = t; i < 3 * (kBins + 4); i += NT) (&hist[0][0])[i] = 0u;
+  if (t == 0) ncand = 0u;
+  __syncthreads();
 
-  uint32_t E;
-  block_excl_scan<NW>((uint32_t)__popc(elig), tmp, E);
-  const int rhi = min(a.r_hi, (int)E);
-  const int rlo = min(a.r_lo, rhi);
+  uint32_t all_or = 0, E = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { all_or |= wsum[0][i]; E += wsum[1][i]; }
+  const uint32_t rhi = min((uint32_t)a.r_hi, E);
+  const uint32_t rlo = min((uint32_t)a.r_lo, rhi);
   // all_hi / all_lo: the bound covers every eligible entry (no search)
-  const bool all_hi = rhi == (int)E;
-  const bool all_lo = rlo == (int)E && rlo > 0;
+  const bool all_hi = rhi == E;
+  const bool all_lo = rlo == E && rlo > 0;
   const bool need_hi = rhi > 0 && !all_hi;
   const bool need_lo = rlo > 0 && !all_lo;
 
-  uint32_t pre_hi = 0, pre_lo = 0;
-  uint32_t rem_hi = (uint32_t)rhi, rem_lo = (uint32_t)rlo;
-
+  // T_r (pre_*), rank left among the keys equal to T_r (rem_*), their count (tie_*)
+  uint32_t pre_hi = 0, pre_lo = 0, rem_hi = rhi, rem_lo = rlo, tie_hi = E, tie_lo = E;
   if (need_hi || need_lo) {
+    const int msb = all_or ? 31 - __builtin_clz(all_or) : -1;
+    int lo_bit = msb + 1;                      // lowest bit decided so far
+    bool use_cand = false;
+    uint32_t nc = 0;
 #pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int bits = pass == 2 ? 10 : 11;
-      const int nb = 1 << bits;
-      const int top = shift + bits;   // bits above this digit are decided
-      for (int i = t; i < nb; i += NT) hist[i] = 0u;
-      __syncthreads();
+    for (int pass = 0; lo_bit > 0; ++pass) {
+      const int width = lo_bit < 11 ? lo_bit : 11;
+      const int shift = lo_bit - width;
+      const uint32_t mask = (1u << width) - 1u;
+      uint32_t* H = hist[pass];
+      if (pass == 0) {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        if (elig & (1u << j)) {
-          const uint32_t k = key[j];
-          const bool mh = need_hi && (pass == 0 || (k >> top) == (pre_hi >> top));
-          const bool ml = need_lo && (pass == 0 || (k >> top) == (pre_lo >> top));
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t bin = ((elig >> j) & 1u) ? (key[j] >> shift) & mask : (uint32_t)kBins;
+          atomicAdd(&H[bin], 0x10001u);
+        }
+      } else if (use_cand) {
+        for (uint32_t c = t; c < nc; c += NT) {
+          const uint32_t k = cand[c];
+          const bool mh = need_hi && (k >> lo_bit) == (pre_hi >> lo_bit);
+          const bool ml = need_lo && (k >> lo_bit) == (pre_lo >> lo_bit);
           const uint32_t inc = (mh ? 0x10000u : 0u) + (ml ? 1u : 0u);
-          if (inc) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], inc);
+          if (inc) atomicAdd(&H[(k >> shift) & mask], inc);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t k = key[j];
+          const bool e = (elig >> j) & 1u;
+          const bool mh = e && need_hi && (k >> lo_bit) == (pre_hi >> lo_bit);
+          const bool ml = e && need_lo && (k >> lo_bit) == (pre_lo >> lo_bit);
+          const uint32_t inc = (mh ? 0x10000u : 0u) + (ml ? 1u : 0u);
+          if (inc) atomicAdd(&H[(k >> shift) & mask], inc);
         }
       }
       __syncthreads();
-      // thread t covers the digits nb-1-q*t .. nb-q*(t+1) (descending), q = nb/NT
-      constexpr int Q = 2048 / NT;
-      const int q = nb / NT > 0 ? nb / NT : 1;
-      uint32_t h[Q];
-      uint32_t own = 0;
-#pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        const int dgt = nb - 1 - (q * t + i);
-        h[i] = (i < q && dgt >= 0 && q * t + i < nb) ? hist[dgt] : 0u;
-        own += h[i];
-      }
-      uint32_t tot;
-      const uint32_t above = block_excl_scan<NW>(own, tmp, tot);
-      if (need_hi) {
-        uint32_t acc = above >> 16;
-#pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          const uint32_t c = h[i] >> 16;
-          if (acc < rem_hi && rem_hi <= acc + c) {
-            found[0] = (uint32_t)(nb - 1 - (q * t + i)); found[1] = rem_hi - acc;
-          }
-          acc += c;
-        }
-      }
-      if (need_lo) {
-        uint32_t acc = above & 0xFFFFu;
-#pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          const uint32_t c = h[i] & 0xFFFFu;
-          if (acc < rem_lo && rem_lo <= acc + c) {
-            found[2] = (uint32_t)(nb - 1 - (q * t + i)); found[3] = rem_lo - acc;
-          }
-          acc += c;
-        }
-      }
+      if (w == 0) scan_pass(H, 1 << width, need_hi, rem_hi, need_lo, rem_lo, found);
       __syncthreads();
-      if (need_hi) { pre_hi |= found[0] << shift; rem_hi = found[1]; }
-      if (need_lo) { pre_lo |= found[2] << shift; rem_lo = found[3]; }
-      __syncthreads();
+      // found[] is written again only after the next pass's histogram
+      // barrier, which every thread reaches after these reads
+      if (need_hi) { pre_hi |= found[0] << shift; rem_hi = found[1]; tie_hi = found[2]; }
+      if (need_lo) { pre_lo |= found[3] << shift; rem_lo = found[4]; tie_lo = found[5]; }
+      lo_bit = shift;
+      if (pass == 0 && lo_bit > 0) {
+        // keys in the bins that hold a bound go to the candidate list
+        uint32_t m = 0, wave_n = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t k = key[j];
+          const bool e = (elig >> j) & 1u;
+          const bool c = e && ((need_hi && (k >> lo_bit) == (pre_hi >> lo_bit)) ||
+                               (need_lo && (k >> lo_bit) == (pre_lo >> lo_bit)));
+          m |= (c ? 1u : 0u) << j;
+          wave_n += (uint32_t)__popcll(__ballot(c));
+        }
+        uint32_t wbase = 0;
+        if (lane == 0) wbase = atomicAdd(&ncand, wave_n);
+        wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const bool c = (m >> j) & 1u;
+          const uint64_t b = __ballot(c);
+          const uint32_t p = wbase + lanes_below(b);
+          if (c && p < (uint32_t)kCap) cand[p] = key[j];
+          wbase += (uint32_t)__popcll(b);
+        }
+        __syncthreads();
+        nc = ncand;
+        use_cand = nc <= (uint32_t)kCap;
+      }
     }
   }
 
-  // rank of each entry among the eligible entries equal to T_hi / T_lo
-  uint32_t run_h = 0, run_l = 0;
-  if (need_hi || need_lo) {
-    uint32_t eq = 0;
+  // ---- ties: rank the entries equal to T_r only when the bound splits them
+  const bool split_hi = need_hi && tie_hi > rem_hi;
+  const bool split_lo = need_lo && tie_lo > rem_lo;
+  uint32_t eq_h = 0, eq_l = 0, eq_off = 0;
+  if (split_hi || split_lo) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      if (elig & (1u << j)) {
-        eq += (need_hi && key[j] == pre_hi) ? 0x10000u : 0u;
-        eq += (need_lo && key[j] == pre_lo) ? 1u : 0u;
-      }
+      const bool e = (elig >> j) & 1u;
+      eq_h |= ((e && split_hi && key[j] == pre_hi) ? 1u : 0u) << j;
+      eq_l |= ((e && split_lo && key[j] == pre_lo) ? 1u : 0u) << j;
     }
+    ordered_counts<NT, KPT>(eq_h, eq_l, cnt[0]);
+    __syncthreads();
     uint32_t dummy;
-    const uint32_t eq_before = block_excl_scan<NW>(eq, tmp, dummy);
-    run_h = eq_before >> 16;
-    run_l = eq_before & 0xFFFFu;
+    eq_off = ordered_offsets<NT, KPT>(cnt[0], dummy);
   }
 
-  uint32_t sel = 0, sel_top = 0;
+  uint32_t sel = 0, top = 0;   // bit j: entry j*NT+t is selected / in the top list
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int n = base + j;
-    bool in_hi = false, in_lo = false;
-    if (elig & (1u << j)) {
-      const uint32_t k = key[j];
-      if (all_hi) in_hi = true;
-      else if (need_hi) {
-        if (k > pre_hi) in_hi = true;
-        else if (k == pre_hi) { in_hi = run_h < rem_hi; ++run_h; }
-      }
-      if (all_lo) in_lo = true;
-      else if (need_lo) {
-        if (k > pre_lo) in_lo = true;
-        else if (k == pre_lo) { in_lo = run_l < rem_lo; ++run_l; }
-      }
-    }
-    bool s = in_hi && !in_lo;
-    if (a.include_mask && n < a.n && a.include_mask[n]) s = true;
-    if (s) sel |= 1u << j;
-    if (in_lo) sel_top |= 1u << j;
+    const int n = j * NT + t;
+    const uint32_t k = key[j];
+    const bool e = (elig >> j) & 1u;
+    uint32_t eqpos = 0;
+    if (split_hi || split_lo)
+      eqpos = ordered_pos((uint32_t)__builtin_amdgcn_readlane((int)eq_off, j), eq_h, eq_l, j);
+    const bool gt_hi = (k > pre_hi) | ((k == pre_hi) & ((eqpos >> 16) < rem_hi));
+    const bool gt_lo = (k > pre_lo) | ((k == pre_lo) & ((eqpos & 0xFFFFu) < rem_lo));
+    const bool in_hi = e & (all_hi | (need_hi & gt_hi));
+    const bool in_lo = e & (all_lo | (need_lo & gt_lo));
+    bool s = in_hi & !in_lo;
+    if (a.include_mask && n < a.n) s |= a.include_mask[n] != 0;
+    sel |= (s ? 1u : 0u) << j;
+    top |= (in_lo ? 1u : 0u) << j;
   }
 
-  // one scan for both lists: selected count in the high half, top-list count in the low
+  // one ordered scan for both lists: selected in the high half, top list in the low
+  ordered_counts<NT, KPT>(sel, top, cnt[1]);
+  __syncthreads();
   uint32_t total;
-  const uint32_t pos2 = block_excl_scan<NW>(((uint32_t)__popc(sel) << 16) | (uint32_t)__popc(sel_top),
-                                            tmp, total);
-  uint32_t pos = pos2 >> 16, pos_top = pos2 & 0xFFFFu;
+  const uint32_t off = ordered_offsets<NT, KPT>(cnt[1], total);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int n = base + j;
-    if (n >= a.n) break;
+    const int n = j * NT + t;
+    const uint32_t pos = ordered_pos((uint32_t)__builtin_amdgcn_readlane((int)off, j), sel, top, j);
     const bool s = (sel >> j) & 1u;
-    if (a.mask_out) a.mask_out[(size_t)row * a.ld_mask + n] = s ? 1 : 0;
-    if (s) {
-      if (a.idx_out) a.idx_out[(size_t)row * a.ld_idx + pos] = n;
-      ++pos;
-      if (a.freq) atomicAdd(&a.freq[n], 1u);
-    }
-    if ((sel_top >> j) & 1u) {
-      if (a.idx_top_out) a.idx_top_out[(size_t)row * a.ld_idx_top + pos_top] = n;
-      ++pos_top;
+    if (n < a.n) {
+      if (a.mask_out) a.mask_out[(size_t)row * a.ld_mask + n] = s ? 1 : 0;
+      if (s) {
+        if (a.idx_out) a.idx_out[(size_t)row * a.ld_idx + (pos >> 16)] = n;
+        if (a.freq) atomicAdd(&a.freq[n], 1u);
+      }
+      if (((top >> j) & 1u) && a.idx_top_out)
+        a.idx_top_out[(size_t)row * a.ld_idx_top + (pos & 0xFFFFu)] = n;
     }
   }
   if (t == 0 && a.count_out) a.count_out[row] = (int32_t)(total >> 16);
@@ -264,9 +419,9 @@ static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  // Fewer waves make every barrier and scan cheaper; 256 threads hold up
-  // to 8192 entries (32 per thread), 1024 threads up to 32768.
-  if (a.n <= 8192) return launch_nt<256>(a, s);
+  // Small rows take 256 threads (cheaper barriers); from 1024 entries on,
+  // 1024 threads (up to 32 entries each) spread the histogram atomics.
+  if (a.n <= 1024) return launch_nt<256>(a, s);
   return launch_nt<1024>(a, s);
 }
 

@@ -129,7 +129,8 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  *                 keys[c*cluster .. c*cluster+cluster-1] and its key is the
  *                 largest key of the block ([PowerInfer-2] "Neuron Cluster
  *                 Decomposition": a cluster is selected as a unit); 1 for
- *                 single values.  ld >= n * cluster.
+ *                 single values.  ld >= n * cluster; with cluster > 1,
+ *                 n <= 4096.
  *  nonzero_only : only entries with a nonzero key take part (ranks count
  *                 among them); not allowed with SFFN_KEY_F32.
  *  include_mask : nullable uint8 [n]; nonzero entries are OR-ed into every

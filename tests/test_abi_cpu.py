@@ -85,6 +85,8 @@ def test_select_validation(L):
     assert rc == 1 and "cluster" in msg
     rc, msg = select(L, n=8, ld=16, cluster=4)
     assert rc == 1 and "n*cluster" in msg
+    rc, msg = select(L, n=5000, ld=10000, cluster=2)
+    assert rc == 2 and "4096" in msg
     # the top list holds the ranks [0, r_lo)
     rc, msg = select(L, r_lo=3, r_hi=6, idx_top=FAKE, ld_idx_top=2)
     assert rc == 1 and "ld_idx_top" in msg

@@ -114,10 +114,11 @@ def test_cluster_keys():
     largest |value| (the oracle forms the cluster keys, then ranks them)."""
     banner("select cluster keys")
     rng = np.random.default_rng(8)
-    for n_c, c in [(448, 32), (1000, 3), (4096, 4), (9000, 2)]:
+    for n_c, c in [(448, 32), (1000, 3), (4096, 4), (4000, 2), (7, 5), (1, 64)]:
         r = np.where(rng.random((2, n_c * c)) < 0.1, rng.standard_normal((2, n_c * c)), 0.0)
         r = r.astype(np.float32)
-        r[1, : c * 5] = r[1, c * 5: c * 10]             # tied clusters
+        if n_c >= 10:
+            r[1, : c * 5] = r[1, c * 5: c * 10]         # tied clusters
         keys = dev(r)
         idx = torch.full((2, n_c), -1, dtype=torch.int32, device="cuda")
         cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
