@@ -228,16 +228,34 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const int total = a.n * a.cluster;
     const float inv = 1.0f / (float)a.cluster;
     if ((a.cluster & 3) == 0 && (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.keys) & 15) == 0) {
-      for (int i = 4 * t; i < total; i += 4 * NT) {   // 4 values of one cluster
-        const uint4 v = *reinterpret_cast<const uint4*>(kp + i);
-        const uint32_t m = max(max(key_of_bits(a.key_type, v.x), key_of_bits(a.key_type, v.y)),
-                               max(key_of_bits(a.key_type, v.z), key_of_bits(a.key_type, v.w)));
-        if (m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+      // 4 values of one cluster per load; 8 loads in flight per thread
+      for (int i0 = 4 * t; i0 < total; i0 += 32 * NT) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + 4 * NT * u;
+          v[u] = i < total ? *reinterpret_cast<const uint4*>(kp + i) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + 4 * NT * u;
+          const uint32_t m =
+              max(max(key_of_bits(a.key_type, v[u].x), key_of_bits(a.key_type, v[u].y)),
+                  max(key_of_bits(a.key_type, v[u].z), key_of_bits(a.key_type, v[u].w)));
+          if (i < total && m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+        }
       }
     } else {
-      for (int i = t; i < total; i += NT) {
-        const uint32_t m = key_of_bits(a.key_type, kp[i]);
-        if (m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+      for (int i0 = t; i0 < total; i0 += 8 * NT) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + NT * u < total ? kp[i0 + NT * u] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + NT * u;
+          const uint32_t m = key_of_bits(a.key_type, v[u]);
+          if (i < total && m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+        }
       }
     }
     __syncthreads();
@@ -421,7 +439,8 @@ static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   // Small rows take 256 threads (cheaper barriers); from 1024 entries on,
   // 1024 threads (up to 32 entries each) spread the histogram atomics.
-  if (a.n <= 1024) return launch_nt<256>(a, s);
+  // Cluster mode reads n*cluster values: 1024 threads keep more loads in flight.
+  if (a.n <= 1024 && (long)a.n * a.cluster <= 1024) return launch_nt<256>(a, s);
   return launch_nt<1024>(a, s);
 }
 

@@ -254,7 +254,7 @@ def run_c1(args, torch, B, synth, P, T):
                   setup={"calibrate_ms": round(calib_ms, 2), "prefill_ms": round(prefill_ms, 2)},
                   roofline=roofline("rowop_b1_kernel<GLU> (gate/up over the compacted union)",
                                     glu_total / L, glu_us,
-                                    measured_traffic("rowop_glu_c1",
+                                    measured_traffic("rowop_glu_selectinfer_decode",
                                                      ["rowop_b1.hip", "sffn_device.h"])),
                   cpu_baseline=cpu)
 
