@@ -18,7 +18,7 @@ namespace sffn {
 
 __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int col = tile * kTileCols + 8 * lane;
   const bool col_ok = col < a.d;

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
   __shared__ uint32_t T[kKT * kPitch / 2];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  const int lane = t & 63, w = wave_id();
   const int nl = lane & 15, g = lane >> 4;
   const int ct = blockIdx.x, ks = blockIdx.y, mt = blockIdx.z;
   const int col0 = ct * kOT;

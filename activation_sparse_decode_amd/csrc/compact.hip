@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void compact_rows_kernel(const uint16_t* __res
                                                            int k, uint16_t* __restrict__ out,
                                                            int ld_out) {
   const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int i = blockIdx.x * 4 + wave_id();
   if (i >= k) return;
   const uint16_t* src = W + (size_t)idx[i] * ld_w;
   uint16_t* dst = out + (size_t)i * ld_out;

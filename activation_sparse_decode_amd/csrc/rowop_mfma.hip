@@ -2,20 +2,26 @@
 // dense prefill / calibration passes that feed the selection).
 //
 // C[m][n] = sum_k X[m][k] W[n][k]: tokens are the M dimension, neurons the
-// N dimension.  Neuron-major weights are already K-contiguous, so each lane
-// feeds its MFMA B operand with one 16-byte load of a weight row.  The fp32
-// activations are split into bf16 hi + lo parts (x = hi + lo to ~2^-17
-// relative) and contracted with two MFMAs into one fp32 accumulator, so the
-// result keeps fp32-grade accuracy with bf16 weights.
+// N dimension.  The fp32 activations are split into bf16 hi + lo parts
+// (x = hi + lo to ~2^-17 relative) and contracted with two MFMAs into one
+// fp32 accumulator, so the result keeps fp32-grade accuracy with bf16
+// weights.
 //
-// Work split: a workgroup owns a 16-neuron x 16-token tile; its four waves
-// take disjoint quarters of K and are summed in LDS in a fixed order.
+// Work split: each wave owns a 16-neuron x 16-token tile over all of K, so
+// no cross-wave reduction is needed.  K is walked in chunks of 128: a wave
+// loads its 16 rows (per weight matrix) with row-contiguous 16-byte loads
+// (four rows of 256 bytes per instruction, not 16 rows of 64 bytes as the
+// MFMA operand layout would read them), stores them in its own LDS area, and
+// reads them back in the B-operand layout (lane (n, g) takes 8 consecutive k
+// of row n).  The next chunk's weights and activations are loaded while the
+// current chunk is contracted.
 #include "sffn_device.h"
 
 namespace sffn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // register / LDS vector
 
 enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4 };
 
@@ -24,30 +30,41 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 }
 
 // Split 8 fp32 values into bf16 hi and lo parts (packed pairs, memory order).
-__device__ __forceinline__ void split8(const float4& p, const float4& q, uint4& hi, uint4& lo) {
-  const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16_rne(v[e]);
-    const float r = v[e] - __uint_as_float(h[e] << 16);
-    l[e] = f32_to_bf16_rne(r);
-  }
-  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+__device__ __forceinline__ uint32_t split_pair(float v0, float v1, uint32_t& lo) {
+  const uint32_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
+  const uint32_t l0 = f32_to_bf16_rne(v0 - __uint_as_float(h0 << 16));
+  const uint32_t l1 = f32_to_bf16_rne(v1 - __uint_as_float(h1 << 16));
+  lo = l0 | (l1 << 16);
+  return h0 | (h1 << 16);
 }
+
+__device__ __forceinline__ void split8(const float4& p, const float4& q, uint4& hi, uint4& lo) {
+  hi.x = split_pair(p.x, p.y, lo.x);
+  hi.y = split_pair(p.z, p.w, lo.y);
+  hi.z = split_pair(q.x, q.y, lo.z);
+  hi.w = split_pair(q.z, q.w, lo.w);
+}
+
+constexpr int kKC = 128;                    // k per chunk
+constexpr int kRowU4 = kKC / 8;             // 16-byte groups of bf16 per chunk row
+constexpr int kPitch = kRowU4 + 1;          // LDS row pitch: rows start 4 banks apart
 
 template <int OP>
 __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
-  __shared__ f32x4 red[2][4][64];
-  __shared__ float sq_red[4][16];
+  constexpr bool kW0 = OP != kOpGated;
+  constexpr bool kW1 = OP == kOpGlu || OP == kOpGated;
+  constexpr int kMat = (kW0 && kW1) ? 2 : 1;
+  __shared__ u32x4 stage[4][kMat][16][kPitch];   // each wave's 16 weight rows of the chunk
+  __shared__ u32x4 xs[2][16][kPitch];          // the chunk's activations, bf16 hi / lo
+  __shared__ float sq_tok[16];
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = wave_id();
   const int nl = lane & 15;
   const int g = lane >> 4;
   const int m0 = blockIdx.y * 16;
-  const int t0 = blockIdx.x * 16;
+  const int t0 = (blockIdx.x * 4 + w) * 16;   // this wave's first item
 
   int n_items;
   if (a.idx) {
@@ -57,114 +74,158 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
   } else {
     n_items = a.n_rows;
   }
-  if (t0 >= n_items) return;  // uniform over the workgroup
+  // Every wave runs the same chunk loop (block barriers); rows past the end
+  // read row 0 and tokens past the batch read token 0 (valid, finite data):
+  // an MFMA output (m, n) depends only on A row m and B column n, so those
+  // lanes only produce outputs that are never stored.
+  auto item_to_row = [&](int it) -> int {
+    if (it >= n_items) return 0;
+    if (!a.idx) return it;
+    const int q = it / a.group;
+    return a.idx[q] * a.group + (it - q * a.group);
+  };
+  // weight loader: lane l loads rows 4i + (l >> 4), 16 bytes at k-offset 8*(l & 15)
+  size_t woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = item_to_row(t0 + 4 * i + (lane >> 4));
+    woff[i] = (size_t)r * a.ld_w + 8 * (lane & 15);
+  }
+  const int my_row = item_to_row(t0 + nl);          // output column of this lane
+  const bool my_live = t0 + nl < n_items;
+  // activation loader: thread t loads token t >> 4, k-offset 8*(t & 15) of each chunk
+  const int xt = t >> 4, xg = t & 15;
+  const int xtok = m0 + xt < a.batch ? m0 + xt : 0;
+  const float* xsrc = a.x + (size_t)xtok * a.ld_in + 8 * xg;
 
-  const int it = t0 + nl;
-  const bool live = it < n_items;
-  int row = 0;
-  if (live) {
-    if (a.idx) {
-      const int q = it / a.group;
-      row = a.idx[q] * a.group + (it - q * a.group);
-    } else {
-      row = it;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float sq = 0.f;        // this thread's share of token xt's sum of squares (chunks)
+  float sq_tail = 0.f;   // token nl's squares in k-group g of the tail
+
+  const int nch = a.d / kKC;
+  u32x4 wr0[4], wr1[4];   // in-flight weights (this lane's share of the next chunk)
+  float4 xr0, xr1;        // in-flight activations (this thread's 8 values)
+  auto load_chunk = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kW0) wr0[i] = *reinterpret_cast<const u32x4*>(a.W0 + woff[i] + k);
+      if (kW1) wr1[i] = *reinterpret_cast<const u32x4*>(a.W1 + woff[i] + k);
+    }
+    xr0 = *reinterpret_cast<const float4*>(xsrc + k);
+    xr1 = *reinterpret_cast<const float4*>(xsrc + k + 4);
+  };
+  if (nch > 0) load_chunk(0);
+  for (int c = 0; c < nch; ++c) {
+    __syncthreads();              // the previous chunk's LDS reads are done
+    {
+      const int rr = lane >> 4, cc = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kW0) stage[w][0][4 * i + rr][cc] = wr0[i];
+        if (kW1) stage[w][kMat - 1][4 * i + rr][cc] = wr1[i];
+      }
+      sq = fmaf(xr0.x, xr0.x, sq); sq = fmaf(xr0.y, xr0.y, sq);
+      sq = fmaf(xr0.z, xr0.z, sq); sq = fmaf(xr0.w, xr0.w, sq);
+      sq = fmaf(xr1.x, xr1.x, sq); sq = fmaf(xr1.y, xr1.y, sq);
+      sq = fmaf(xr1.z, xr1.z, sq); sq = fmaf(xr1.w, xr1.w, sq);
+      uint4 h, l;
+      split8(xr0, xr1, h, l);
+      xs[0][xt][xg] = (u32x4){h.x, h.y, h.z, h.w};
+      xs[1][xt][xg] = (u32x4){l.x, l.y, l.z, l.w};
+    }
+    __syncthreads();
+    if (c + 1 < nch) load_chunk((c + 1) * kKC);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // A operand: token nl, k = 32 s + 8 g; B operand: row nl, same k
+      const u32x4 ah = xs[0][nl][4 * s + g], al = xs[1][nl][4 * s + g];
+      if (kW0) {
+        const u32x4 b = stage[w][0][nl][4 * s + g];
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
+      }
+      if (kW1) {
+        const u32x4 b = stage[w][kMat - 1][nl][4 * s + g];
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, b), acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, b), acc1, 0, 0, 0);
+      }
     }
   }
-  const int tok = m0 + nl;
-  const bool tok_ok = tok < a.batch;
-
-  const uint16_t* w0p = a.W0 + (size_t)row * a.ld_w + g * 8;
-  const uint16_t* w1p = a.W1 + (size_t)row * a.ld_w + g * 8;
-  const float* xp = a.x + (size_t)(tok_ok ? tok : 0) * a.ld_in + g * 8;
-
-  const int ksteps = a.d >> 5;
-  const int ks0 = (ksteps * w) >> 2;
-  const int ks1 = (ksteps * (w + 1)) >> 2;
-
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
-  float sq = 0.f;
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int k = ks * 32;
-    uint4 wa = zero4, wb = zero4;
-    if (OP != kOpGated) wa = live ? *reinterpret_cast<const uint4*>(w0p + k) : zero4;
-    if (OP == kOpGlu || OP == kOpGated) wb = live ? *reinterpret_cast<const uint4*>(w1p + k) : zero4;
-    float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
-    if (tok_ok) {
-      p = *reinterpret_cast<const float4*>(xp + k);
-      q = *reinterpret_cast<const float4*>(xp + k + 4);
-    }
-    {
-      sq = fmaf(p.x, p.x, sq); sq = fmaf(p.y, p.y, sq); sq = fmaf(p.z, p.z, sq); sq = fmaf(p.w, p.w, sq);
-      sq = fmaf(q.x, q.x, sq); sq = fmaf(q.y, q.y, sq); sq = fmaf(q.z, q.z, sq); sq = fmaf(q.w, q.w, sq);
-    }
+  // tail (d not a multiple of 128): one 32-k step at a time, straight from memory
+  for (int k = nch * kKC; k < a.d; k += 32) {
+    const float* xp = a.x + (size_t)(m0 + nl < a.batch ? m0 + nl : 0) * a.ld_in + k + 8 * g;
+    const float4 p = *reinterpret_cast<const float4*>(xp);
+    const float4 q = *reinterpret_cast<const float4*>(xp + 4);
+    // lane (nl, g) holds token nl's k-group g (the same in every wave; wave 0's count is used)
+    sq_tail = fmaf(p.x, p.x, sq_tail); sq_tail = fmaf(p.y, p.y, sq_tail);
+    sq_tail = fmaf(p.z, p.z, sq_tail); sq_tail = fmaf(p.w, p.w, sq_tail);
+    sq_tail = fmaf(q.x, q.x, sq_tail); sq_tail = fmaf(q.y, q.y, sq_tail);
+    sq_tail = fmaf(q.z, q.z, sq_tail); sq_tail = fmaf(q.w, q.w, sq_tail);
     uint4 xh, xl;
     split8(p, q, xh, xl);
-    if (OP != kOpGated) {
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(wa), acc0, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(wa), acc0, 0, 0, 0);
+    const size_t off = (size_t)my_row * a.ld_w + k + 8 * g;
+    if (kW0) {
+      const uint4 b = *reinterpret_cast<const uint4*>(a.W0 + off);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(b), acc0, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(b), acc0, 0, 0, 0);
     }
-    if (OP == kOpGlu || OP == kOpGated) {
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(wb), acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(wb), acc1, 0, 0, 0);
+    if (kW1) {
+      const uint4 b = *reinterpret_cast<const uint4*>(a.W1 + off);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(b), acc1, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(b), acc1, 0, 0, 0);
     }
   }
 
-  red[0][w][lane] = acc0;
-  red[1][w][lane] = acc1;
+  // token sums of squares: the chunk part is spread over the 16 loader threads
+  // of each token (lanes 16j..16j+15 of a wave); the tail part over the four
+  // k-groups of wave 0's lanes nl + 16 g.  Both are combined through LDS in a
+  // fixed order.
   {
-    // lanes nl, nl+16, nl+32, nl+48 hold token nl's squares over this wave's K range
-    sq += __shfl_xor(sq, 16, kWave);
-    sq += __shfl_xor(sq, 32, kWave);
-    if (g == 0) sq_red[w][nl] = sq;
-  }
-  __syncthreads();
-  if (w != 0) return;
-
-  f32x4 s0 = red[0][0][lane], s1 = red[1][0][lane];
-#pragma unroll
-  for (int ww = 1; ww < 4; ++ww) {
-    const f32x4 t0v = red[0][ww][lane], t1v = red[1][ww][lane];
-    s0 += t0v;
-    s1 += t1v;
+    float v = sq;
+    v += __shfl_xor(v, 1, kWave); v += __shfl_xor(v, 2, kWave);
+    v += __shfl_xor(v, 4, kWave); v += __shfl_xor(v, 8, kWave);
+    float tv = sq_tail;
+    tv += __shfl_xor(tv, 16, kWave); tv += __shfl_xor(tv, 32, kWave);
+    __syncthreads();
+    if (xg == 0) sq_tok[xt] = v;
+    __syncthreads();
+    if (t < 16 && nch * kKC < a.d) sq_tok[t] += tv;
+    __syncthreads();
   }
 
+  if (!my_live) return;
   // C layout of the 16x16 MFMA: lane l, register i holds row m = 4*(l/16)+i
   // (token) and column n = l%16 (neuron).
-  if (!live) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = 4 * g + i;
     const int b = m0 + m;
     if (b >= a.batch) continue;
+    const float ss = sq_tok[m];
     // optional unit-gain RMSNorm of token b's input, applied to the dot products
-    const float ss = sq_red[0][m] + sq_red[1][m] + sq_red[2][m] + sq_red[3][m];
     const float inv = a.rms_eps > 0.f ? 1.f / sqrtf(ss / (float)a.d + a.rms_eps) : 1.f;
     float v;
     if (OP == kOpGlu) {
-      const float gg = s0[i] * inv;
-      v = (gg / (1.f + expf(-gg))) * (s1[i] * inv);
+      const float gg = acc0[i] * inv;
+      v = (gg / (1.f + expf(-gg))) * (acc1[i] * inv);
     } else if (OP == kOpDotRelu) {
-      v = fmaxf(s0[i] * inv - a.tau_scale * sqrtf(ss) * inv, 0.f);
+      v = fmaxf(acc0[i] * inv - a.tau_scale * sqrtf(ss) * inv, 0.f);
     } else if (OP == kOpGated) {
-      v = a.aux[(size_t)b * a.ld_aux + row] * (s1[i] * inv);
+      v = a.aux[(size_t)b * a.ld_aux + my_row] * (acc1[i] * inv);
     } else {
-      v = s0[i] * inv;
+      v = acc0[i] * inv;
     }
-    if (a.accumulate) v += a.out[(size_t)b * a.ld_out + row];
-    a.out[(size_t)b * a.ld_out + row] = v;
-    if (a.key_out) a.key_out[(size_t)b * a.ld_out + row] = key_abs(v);
+    if (a.accumulate) v += a.out[(size_t)b * a.ld_out + my_row];
+    a.out[(size_t)b * a.ld_out + my_row] = v;
+    if (a.key_out) a.key_out[(size_t)b * a.ld_out + my_row] = key_abs(v);
   }
 }
 
 hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s) {
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
-  const int nt = (int)((items + 15) / 16);
   const int mt = (a.batch + 15) / 16;
-  if (nt == 0) return hipSuccess;
-  dim3 grid(nt, mt);
+  if (items == 0) return hipSuccess;
+  dim3 grid((int)((items + 63) / 64), mt);   // 4 waves x 16 neurons per workgroup
   switch (a.op) {
     case kOpGlu: hipLaunchKernelGGL(rowop_mfma_kernel<kOpGlu>, grid, dim3(256), 0, s, a); break;
     case kOpDotRelu: hipLaunchKernelGGL(rowop_mfma_kernel<kOpDotRelu>, grid, dim3(256), 0, s, a); break;

@@ -79,7 +79,7 @@ __device__ __forceinline__ uint32_t key_of_bits(int key_type, uint32_t b) {
 template <int NT, int KPT>
 __device__ __forceinline__ void ordered_counts(uint32_t bits_h, uint32_t bits_l,
                                                uint32_t (*cnt)[NT / 64]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint64_t bh = __ballot((bits_h >> j) & 1u);
@@ -91,7 +91,7 @@ __device__ __forceinline__ void ordered_counts(uint32_t bits_h, uint32_t bits_l,
 template <int NT, int KPT>
 __device__ __forceinline__ uint32_t ordered_offsets(uint32_t (*cnt)[NT / 64], uint32_t& total) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   uint32_t row_total = 0, row_below = 0;
   if (lane < KPT) {
 #pragma unroll

@@ -39,6 +39,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Wave index within the workgroup as a wave-uniform (scalar) value, so loops
+// bounded by it stay scalar loops rather than exec-masked ones.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // ----------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -44,7 +44,7 @@ __device__ __forceinline__ int item_row(const int32_t* idx, int group, int it) {
 // Sum the 16 waves' 8-column partials held in `acc` (lane owns columns
 // 8*lane..8*lane+7) in wave order; threads 0..511 return their column's sum.
 __device__ __forceinline__ float wg_reduce_cols(float4 (*red)[kTileCols / 4], const float (&acc)[8]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   red[w][2 * lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   red[w][2 * lane + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   __syncthreads();

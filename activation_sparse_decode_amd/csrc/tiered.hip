@@ -30,7 +30,7 @@ struct SegBounds { int b[5]; };
 __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid,
                                                       float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int col = tile * kTileCols + 8 * lane;
   const bool col_ok = col < a.d_out;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const uint16_t* __restrict_
                                                      int n_in, SegBounds sb, int n_seg,
                                                      uint8_t* __restrict__ rec, int rec_bytes) {
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wave_id();
   const int j = gw / n_seg, s = gw - (gw / n_seg) * n_seg;
   if (j >= n_in) return;
   const int lo = sb.b[s], hi = sb.b[s + 1];

@@ -86,3 +86,30 @@ def test_mfma_dense_prefill_shape():
         assert_close(host(A[t]), oracle.swiglu_acts(Wg, Wu, X[t]), what=f"A[{t}]")
         y_ref = oracle.widen_bf16(WdT).T @ host(A[t]).astype(np.float64)
         assert_close(host(H[t]) - X[t], y_ref, what=f"H[{t}]")
+
+
+@pytest.mark.parametrize("d", [96, 288, 416])
+def test_mfma_rowop_ragged_k(d):
+    """The batched row op walks K in 128-wide chunks and finishes the rest
+    32 at a time: d below one chunk (96) and with a 32 / 32+128k tail,
+    with and without the fused RMSNorm of each token's input, over a
+    gathered index list that ends mid-tile."""
+    banner(f"c4 ragged K d={d}")
+    N, T = 200, 21
+    Wg, Wu, _, _ = make(N, d, 1, seed=d)
+    X = synth.tokens(d, synth.W_C4, 5, T, d)
+    rows = np.sort(np.random.default_rng(d).choice(N, 77, replace=False)).astype(np.int32)
+    idx = dev(rows)
+    cnt = torch.tensor([len(rows)], dtype=torch.int32, device="cuda")
+    for eps in (0.0, 1e-5):
+        A = torch.full((T, N), 7.0, dtype=torch.float32, device="cuda")
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, dev(Wg), dev(Wu), dev(X), A, idx=idx, count=cnt,
+                          k_max=len(rows), rms_eps=eps)
+        torch.cuda.synchronize()
+        A_h = host(A)
+        skipped = np.setdiff1d(np.arange(N), rows)
+        assert np.all(A_h[:, skipped] == 7.0), "rows outside the index list were written"
+        for t in range(T):
+            x = oracle.rms_normalize(X[t], eps) if eps > 0 else X[t]
+            assert_close(A_h[t, rows], oracle.swiglu_acts(Wg, Wu, x, rows),
+                         what=f"d={d} eps={eps} token {t}")
