@@ -9,7 +9,7 @@
 // workgroup owns one column tile and one contiguous chunk of the compacted
 // row list; wave w takes rows w, w+16, ...; lane l owns columns 8l..8l+7 of
 // the tile and streams them with one 16-byte nontemporal load per row
-// (1 KiB per wave instruction).  Waves are summed in LDS and the chunk's
+// (1 KiB per wave instruction), four rows in flight per lane.  Waves are summed in LDS and the chunk's
 // partial row goes to the workspace.  Kernel 2 sums the KS partials in chunk
 // order and applies alpha / accumulate.
 #include "sffn_splitk.h"
@@ -21,39 +21,54 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
   const int lane = threadIdx.x & 63, w = wave_id();
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int col = tile * kTileCols + 8 * lane;
-  const bool col_ok = col < a.d;
+  const int colc = col < a.d ? col : 0;   // lanes past the last column re-read column 0 (discarded)
 
   const int n_items = item_count(a.idx, a.count, a.k_max, a.group, a.n_rows);
   const int chunk = (n_items + KS - 1) / KS;
   const int k0 = ks * chunk;
   const int k1 = min(n_items, k0 + chunk);
+  // This wave's items are k0 + w + kWaves * u, u < nu.  Their rows,
+  // activations and masks are fetched with one vector load per lane (lane l:
+  // item u = ub + l), then broadcast with readlane, so the weight loads of all
+  // of the wave's rows are issued back to back without waiting on indices.
+  const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   constexpr int U = 4;
-  for (int kb = k0 + w; kb < k1; kb += kWaves * U) {
-    int row[U];
-    float av[U];
+  for (int ub = 0; ub < nu; ub += 64) {
+    const bool ok = ub + lane < nu;
+    const int it = k0 + w + kWaves * (ok ? ub + lane : 0);
+    const int r = item_row(a.idx, a.group, it);
+    const int nb = min(64, nu - ub);
+    // Every load of a batch is issued (a padding slot past the wave's last
+    // row re-reads its first row with weight 0): no branch around a load, so
+    // nothing waits between them.  The first batch's weights are requested
+    // before the activations, whose gather then overlaps them.
     uint4 wv[U];
+    auto issue = [&](int u) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int it = kb + kWaves * u;
-      const bool ok = it < k1;
-      row[u] = ok ? item_row(a.idx, a.group, it) : 0;
-      float v = 0.f;
-      if (ok) {
-        v = a.in[row[u]];
-        if (a.row_mask && !a.row_mask[row[u]]) v = 0.f;
+      for (int uu = 0; uu < U; ++uu) {
+        const int rr = __builtin_amdgcn_readlane(r, u + uu < nb ? u + uu : 0);
+        wv[uu] = load_stream16(a.W + (size_t)rr * a.ld_w + colc);
       }
-      av[u] = v;
-      wv[u] = (ok && col_ok) ? load_stream16(a.W + (size_t)row[u] * a.ld_w + col)
-                             : make_uint4(0, 0, 0, 0);
-    }
+    };
+    issue(0);
+    float v = a.in[r];
+    if (a.row_mask && !a.row_mask[r]) v = 0.f;
+    const float av = ok ? v : 0.f;
+    for (int u = 0;;) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float f[8];
-      unpack8(wv[u], f);
+      for (int uu = 0; uu < U; ++uu) {
+        const int src = u + uu < nb ? u + uu : 0;
+        const float au = u + uu < nb ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), src)) : 0.f;
+        float f[8];
+        unpack8(wv[uu], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(av[u], f[e], acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(au, f[e], acc[e]);
+      }
+      u += U;
+      if (u >= nb) break;
+      issue(u);
     }
   }
 
@@ -117,8 +132,11 @@ hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, in
 }
 
 int pick_split_b1(long items, int col_tiles) {
-  // about two 16-wave workgroups per CU, at least one row per wave
-  long ks = (512 + col_tiles - 1) / col_tiles;
+  // about four rows per wave (the loads a lane keeps in flight), but at
+  // least ~256 workgroups so every CU streams
+  long ks = (items + 4 * kWaves - 1) / (4 * kWaves);
+  const long min_ks = (256 + col_tiles - 1) / col_tiles;
+  if (ks < min_ks) ks = min_ks;
   const long max_by_rows = (items + kWaves - 1) / kWaves;
   if (ks > max_by_rows) ks = max_by_rows;
   if (ks > kMaxSplit) ks = kMaxSplit;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
   __shared__ float sq_red[16];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  const int lane = t & 63, w = wave_id();
   const int nw = blockDim.x >> 6;
   const int tpb = blockDim.x;
   const int nchunk = a.d >> 3;
@@ -54,10 +54,16 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
     n_items = a.n_rows;
   }
 
+  // This thread's chunks of every row.  Chunks past the row end re-read the
+  // row's first chunk (always valid) against x = 0, so every weight load is
+  // unconditional: no branch around a load, nothing for the compiler to
+  // wait on before the next one is issued.
+  int coff[CPT];
   float xr[CPT][8];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int c = t + tpb * j;
+    coff[j] = c < nchunk ? 8 * c : 0;
     if (c < nchunk) {
       const float4 p = *reinterpret_cast<const float4*>(a.x + 8 * c);
       const float4 q = *reinterpret_cast<const float4*>(a.x + 8 * c + 4);
@@ -69,6 +75,29 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
     }
   }
 
+  // Rows of this workgroup: items base0 + i + stride * it.  With an index
+  // list, one vector load per lane fetches the rows of the first 64 items
+  // up front (lane l: iteration l / NPI, row l % NPI); later items, if any,
+  // read their index when they are reached.
+  const int stride = gridDim.x * NPI;
+  const int base0 = blockIdx.x * NPI;
+  int lane_row = 0;
+  if (a.idx) {
+    const int it = base0 + (lane / NPI) * stride + (lane % NPI);
+    if (it < n_items) {
+      const int q = it / a.group;
+      lane_row = a.idx[q] * a.group + (it - q * a.group);
+    }
+  }
+  auto row_of = [&](int k, int i) -> int {   // row of item base0 + i + stride * k (a live item)
+    const int it = base0 + i + stride * k;
+    if (!a.idx) return it;
+    const int l = k * NPI + i;
+    if (l < 64) return __builtin_amdgcn_readlane(lane_row, l);
+    const int q = it / a.group;
+    return a.idx[q] * a.group + (it - q * a.group);
+  };
+
   const bool need_norm = OP == kOpDotRelu || a.rms_eps > 0.f;
   bool have_norm = false;
   float tau = 0.f, inv = 1.f;
@@ -77,45 +106,34 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
   // Software pipeline: the weights of the next group of rows are requested
   // before the current group is reduced, so loads stay in flight across the
   // reductions and barriers and x is reused for the workgroup's whole life.
-  const int stride = gridDim.x * NPI;
   int row[NPI];
   bool live[NPI];
   uint4 w0[NPI][CPT], w1[NPI][CPT];
-  auto fetch = [&](int base, int (&rw)[NPI], bool (&lv)[NPI], uint4 (&v0)[NPI][CPT],
+  auto fetch = [&](int k, int (&rw)[NPI], bool (&lv)[NPI], uint4 (&v0)[NPI][CPT],
                    uint4 (&v1)[NPI][CPT]) {
 #pragma unroll
     for (int i = 0; i < NPI; ++i) {
-      const int it = base + i;
-      lv[i] = it < n_items;
-      if (!lv[i]) {
-        rw[i] = 0;
-      } else if (a.idx) {
-        const int q = it / a.group;
-        rw[i] = a.idx[q] * a.group + (it - q * a.group);
-      } else {
-        rw[i] = it;
-      }
+      lv[i] = base0 + i + stride * k < n_items;
+      rw[i] = lv[i] ? row_of(k, i) : rw[0];   // a dead row re-reads the group's first row
     }
 #pragma unroll
     for (int i = 0; i < NPI; ++i)
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        const int c = t + tpb * j;
-        const bool ok = lv[i] && c < nchunk;
-        const size_t off = (size_t)rw[i] * a.ld_w + 8 * c;
-        if (kUse0) v0[i][j] = ok ? load_stream(a.W0 + off) : make_uint4(0, 0, 0, 0);
-        if (kUse1) v1[i][j] = ok ? load_stream(a.W1 + off) : make_uint4(0, 0, 0, 0);
+        const size_t off = (size_t)rw[i] * a.ld_w + coff[j];
+        if (kUse0) v0[i][j] = load_stream(a.W0 + off);
+        if (kUse1) v1[i][j] = load_stream(a.W1 + off);
       }
   };
-  int base = blockIdx.x * NPI;
-  if (base < n_items) fetch(base, row, live, w0, w1);
+  int k = 0;
+  if (base0 < n_items) fetch(0, row, live, w0, w1);
 
-  for (; base < n_items; base += stride) {
+  for (; base0 + stride * k < n_items; ++k) {
     int nrow[NPI];
     bool nlive[NPI];
     uint4 n0[NPI][CPT], n1[NPI][CPT];
-    const bool more = base + stride < n_items;
-    if (more) fetch(base + stride, nrow, nlive, n0, n1);
+    const bool more = base0 + stride * (k + 1) < n_items;
+    if (more) fetch(k + 1, nrow, nlive, n0, n1);
 
     if (need_norm && !have_norm) {
       float s = 0.f;

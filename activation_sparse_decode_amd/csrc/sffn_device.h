@@ -47,11 +47,25 @@ __device__ __forceinline__ int wave_id() {
 
 // ----------------------------------------------------------------- wave reductions
 
+// Sum over the 64 lanes with DPP lane moves (no LDS round trips): pairs and
+// quads, then the 8- and 16-lane mirrors, then the row broadcasts of lanes
+// 15 and 31 fold the four 16-lane rows into lane 63, which is read back as a
+// wave-uniform value.  Call with every lane of the wave active.
+#define SFFN_DPP_ADD(v, ctrl)                                                              \
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, false))
+#define SFFN_DPP_ADD_ROWS(v, ctrl, rows)                                                   \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rows, 0xf, false))
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  SFFN_DPP_ADD(v, 0xB1);              // quad_perm [1,0,3,2]
+  SFFN_DPP_ADD(v, 0x4E);              // quad_perm [2,3,0,1]
+  SFFN_DPP_ADD(v, 0x141);             // row_half_mirror
+  SFFN_DPP_ADD(v, 0x140);             // row_mirror: every lane holds its 16-lane row sum
+  SFFN_DPP_ADD_ROWS(v, 0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+  SFFN_DPP_ADD_ROWS(v, 0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+#undef SFFN_DPP_ADD
+#undef SFFN_DPP_ADD_ROWS
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
