@@ -42,21 +42,19 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
     const int nb = min(64, nu - ub);
     // Every load of a batch is issued (a padding slot past the wave's last
     // row re-reads its first row with weight 0): no branch around a load, so
-    // nothing waits between them.  The first batch's weights are requested
-    // before the activations, whose gather then overlaps them.
-    uint4 wv[U];
-    auto issue = [&](int u) {
+    // nothing waits between them.  The activations are gathered after the
+    // batch's weights were requested (r is a valid row for every lane), so
+    // their wait is the batch's wait.
+    for (int u = 0; u < nb; u += U) {
+      uint4 wv[U];
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
         const int rr = __builtin_amdgcn_readlane(r, u + uu < nb ? u + uu : 0);
         wv[uu] = load_stream16(a.W + (size_t)rr * a.ld_w + colc);
       }
-    };
-    issue(0);
-    float v = a.in[r];
-    if (a.row_mask && !a.row_mask[r]) v = 0.f;
-    const float av = ok ? v : 0.f;
-    for (int u = 0;;) {
+      float v = a.in[r];
+      if (a.row_mask && !a.row_mask[r]) v = 0.f;
+      const float av = ok ? v : 0.f;
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
         const int src = u + uu < nb ? u + uu : 0;
@@ -66,9 +64,6 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(au, f[e], acc[e]);
       }
-      u += U;
-      if (u >= nb) break;
-      issue(u);
     }
   }
 
@@ -132,11 +127,14 @@ hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, in
 }
 
 int pick_split_b1(long items, int col_tiles) {
-  // about four rows per wave (the loads a lane keeps in flight), but at
-  // least ~256 workgroups so every CU streams
+  // about four rows per wave (the loads a lane keeps in flight), within
+  // 256..512 workgroups: every CU streams, and a device-side count far
+  // below the launch bound `items` still leaves a few rows per wave
   long ks = (items + 4 * kWaves - 1) / (4 * kWaves);
   const long min_ks = (256 + col_tiles - 1) / col_tiles;
+  const long max_ks = (512 + col_tiles - 1) / col_tiles;
   if (ks < min_ks) ks = min_ks;
+  if (ks > max_ks) ks = max_ks;
   const long max_by_rows = (items + kWaves - 1) / kWaves;
   if (ks > max_by_rows) ks = max_by_rows;
   if (ks > kMaxSplit) ks = kMaxSplit;

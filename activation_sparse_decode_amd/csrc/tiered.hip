@@ -9,9 +9,9 @@
 // (Fig 4), so a selected column is one contiguous read in either tier.
 //
 // The grid is (512-column tiles) x (KS_top + KS_mid chunks): a workgroup
-// streams either top rows (16-byte bf16 loads, 8 outputs per lane) or
-// middle rows (4-byte code loads, 8 outputs per lane, so both tiers share
-// the lane -> output mapping).  The middle tier is decoded in registers:
+// streams either top rows (16-byte bf16 loads, 8 outputs per lane, four rows
+// in flight) or middle rows (4-byte code loads, 8 outputs per lane, so both
+// tiers share the lane -> output mapping; eight rows in flight).  The middle tier is decoded in registers:
 // x_j * What[j][o] = (x_j scale_js) q_jo + x_j zero_js, where the second term
 // is the same for all outputs of the segment and is summed once per lane.
 // Partials are summed in chunk order by the shared split-K reduction.
@@ -27,16 +27,47 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 
 struct SegBounds { int b[5]; };
 
+// Rows of one tier for this wave (items k0 + w + kWaves * u, u < nu): one
+// vector load per lane fetches a row index (lane l: item u = ub + l), and
+// the weight loads of a batch are then issued back to back from
+// readlane-broadcast rows, with no branch around a load (padding slots of a
+// batch re-read the wave's first row with x = 0).
+template <int U, typename Issue, typename Accum>
+__device__ __forceinline__ void tier_rows(const int32_t* idx, const float* x, int k0, int nu,
+                                          Issue issue, Accum accum) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  for (int ub = 0; ub < nu; ub += 64) {
+    const bool ok = ub + lane < nu;
+    const int r = idx[k0 + w + kWaves * (ok ? ub + lane : 0)];
+    const int nb = min(64, nu - ub);
+    auto row_at = [&](int u) { return __builtin_amdgcn_readlane(r, u < nb ? u : 0); };
+    for (int u = 0; u < nb; u += U) {
+      issue(u, row_at);
+      // gathered after the batch's weights were requested (r is a valid row
+      // for every lane), so its wait is the batch's wait; the compiler
+      // barrier keeps it here rather than hoisted ahead of the weights
+      asm volatile("" ::: "memory");
+      const float xr = x[r];
+      const float xv = ok ? xr : 0.f;
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const float xu = u + uu < nb
+            ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), u + uu)) : 0.f;
+        accum(uu, xu);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid,
                                                       float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
   const int lane = threadIdx.x & 63, w = wave_id();
   const int tile = blockIdx.x, ks = blockIdx.y;
   const int col = tile * kTileCols + 8 * lane;
-  const bool col_ok = col < a.d_out;
+  const int colc = col < a.d_out ? col : 0;   // lanes past the last output re-read output 0
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
 
   if (ks < KS_top) {
     int n = a.cnt_top ? *a.cnt_top : 0;
@@ -44,26 +75,22 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
     n = n > 0 ? n : 0;
     const int chunk = (n + KS_top - 1) / KS_top;
     const int k0 = ks * chunk, k1 = min(n, k0 + chunk);
-    for (int kb = k0 + w; kb < k1; kb += kWaves * U) {
-      float xv[U];
-      uint4 wv[U];
+    const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
+    constexpr int U = 4;
+    uint4 wv[U];
+    tier_rows<U>(
+        a.idx_top, a.x, k0, nu,
+        [&](int u, auto row_at) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int it = kb + kWaves * u;
-        const bool ok = it < k1;
-        const int row = ok ? a.idx_top[it] : 0;
-        xv[u] = ok ? a.x[row] : 0.f;
-        wv[u] = (ok && col_ok) ? load_stream16(a.Wt + (size_t)row * a.ld_w + col)
-                               : make_uint4(0, 0, 0, 0);
-      }
+          for (int uu = 0; uu < U; ++uu)
+            wv[uu] = load_stream16(a.Wt + (size_t)row_at(u + uu) * a.ld_w + colc);
+        },
+        [&](int uu, float xu) {
+          float f[8];
+          unpack8(wv[uu], f);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float f[8];
-        unpack8(wv[u], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(xv[u], f[e], acc[e]);
-      }
-    }
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(xu, f[e], acc[e]);
+        });
   } else {
     const int m = ks - KS_top;
     int n = a.cnt_mid ? *a.cnt_mid : 0;
@@ -71,41 +98,39 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
     n = n > 0 ? n : 0;
     const int chunk = (n + KS_mid - 1) / KS_mid;
     const int k0 = m * chunk, k1 = min(n, k0 + chunk);
+    const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
     int seg = 0;
 #pragma unroll
     for (int s = 1; s < 4; ++s)
-      if (s < a.n_seg && col >= a.seg_bounds[s]) seg = s;
+      if (s < a.n_seg && colc >= a.seg_bounds[s]) seg = s;
     const int hdr_off = 4 * seg;
-    const int code_off = 16 + (col >> 1);
+    const int code_off = 16 + (colc >> 1);
     float zacc = 0.f;
-    for (int kb = k0 + w; kb < k1; kb += kWaves * U) {
-      float xv[U];
-      uint32_t hdr[U], codes[U];
+    constexpr int U = 8;
+    uint32_t hdr[U], codes[U];
+    tier_rows<U>(
+        a.idx_mid, a.x, k0, nu,
+        [&](int u, auto row_at) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int it = kb + kWaves * u;
-        const bool ok = it < k1;
-        const int row = ok ? a.idx_mid[it] : 0;
-        const uint8_t* rec = a.rec + (size_t)row * a.rec_bytes;
-        xv[u] = ok ? a.x[row] : 0.f;
-        hdr[u] = ok ? *reinterpret_cast<const uint32_t*>(rec + hdr_off) : 0u;
-        codes[u] = (ok && col_ok) ? load_stream4(rec + code_off) : 0u;
-      }
+          for (int uu = 0; uu < U; ++uu) {
+            const uint8_t* rec = a.rec + (size_t)row_at(u + uu) * a.rec_bytes;
+            hdr[uu] = *reinterpret_cast<const uint32_t*>(rec + hdr_off);
+            codes[uu] = load_stream4(rec + code_off);
+          }
+        },
+        [&](int uu, float xu) {
+          const float sc = half_bits_to_float(hdr[uu] & 0xFFFFu);
+          const float z = half_bits_to_float(hdr[uu] >> 16);
+          const float sx = xu * sc;
+          zacc = fmaf(xu, z, zacc);
+          const uint32_t lo = codes[uu] & 0x0F0F0F0Fu;
+          const uint32_t hi = (codes[uu] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float sc = half_bits_to_float(hdr[u] & 0xFFFFu);
-        const float z = half_bits_to_float(hdr[u] >> 16);
-        const float sx = xv[u] * sc;
-        zacc = fmaf(xv[u], z, zacc);
-        const uint32_t lo = codes[u] & 0x0F0F0F0Fu;
-        const uint32_t hi = (codes[u] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          acc[2 * b] = fmaf(sx, (float)((lo >> (8 * b)) & 0xFFu), acc[2 * b]);
-          acc[2 * b + 1] = fmaf(sx, (float)((hi >> (8 * b)) & 0xFFu), acc[2 * b + 1]);
-        }
-      }
-    }
+          for (int b = 0; b < 4; ++b) {
+            acc[2 * b] = fmaf(sx, (float)((lo >> (8 * b)) & 0xFFu), acc[2 * b]);
+            acc[2 * b + 1] = fmaf(sx, (float)((hi >> (8 * b)) & 0xFFu), acc[2 * b + 1]);
+          }
+        });
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += zacc;
   }
@@ -117,25 +142,26 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
 
 hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   const int col_tiles = (a.d_out + kTileCols - 1) / kTileCols;
-  // split the chunks between the tiers in proportion to the bytes each reads
-  const double top_bytes = (double)a.k_top_max * a.d_out * 2.0;
-  const double mid_bytes = (double)a.k_mid_max * (a.d_out / 2.0 + 4.0);
-  int total = pick_split_b1((long)a.k_top_max + a.k_mid_max, col_tiles);
-  if (total < 2) total = 2;
-  int ks_top = (int)(total * top_bytes / (top_bytes + mid_bytes + 1e-30) + 0.5);
-  if (a.k_top_max == 0) ks_top = 0;
-  else if (ks_top < 1) ks_top = 1;
-  int ks_mid = total - ks_top;
-  if (a.k_mid_max == 0) ks_mid = 0;
-  else if (ks_mid < 1) ks_mid = 1;
+  // about four top rows / eight middle rows per wave (equal bytes in flight
+  // per lane), scaled up together until ~256 workgroups stream
+  long ks_top = a.k_top_max > 0 ? (a.k_top_max + 4 * kWaves - 1) / (4 * kWaves) : 0;
+  long ks_mid = a.k_mid_max > 0 ? (a.k_mid_max + 8 * kWaves - 1) / (8 * kWaves) : 0;
+  for (int grow = 0; grow < 8 && (ks_top + ks_mid) * col_tiles < 256; ++grow) {
+    if (ks_top > 0) ks_top = min(2 * ks_top, ((long)a.k_top_max + kWaves - 1) / kWaves);
+    if (ks_mid > 0) ks_mid = min(2 * ks_mid, ((long)a.k_mid_max + kWaves - 1) / kWaves);
+  }
+  while (ks_top + ks_mid > kMaxSplit) {
+    if (ks_top > 1) ks_top = (ks_top + 1) / 2;
+    if (ks_mid > 1) ks_mid = (ks_mid + 1) / 2;
+  }
   if (ks_top + ks_mid == 0) ks_mid = 1;   // nothing to read: one chunk writes y
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
-  hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, ks_top + ks_mid), dim3(1024), 0, s, a, ks_top,
-                     ks_mid, partials);
+  hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0, s,
+                     a, (int)ks_top, (int)ks_mid, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_splitk_reduce(partials, ks_top + ks_mid, 1, 1, a.d_out, nullptr, a.y, a.d_out,
-                              a.accumulate, s);
+  return launch_splitk_reduce(partials, (int)(ks_top + ks_mid), 1, 1, a.d_out, nullptr, a.y,
+                              a.d_out, a.accumulate, s);
 }
 
 // ------------------------------------------------------------------ encoder
