@@ -6,15 +6,22 @@
 // that token (LeanStream "Permutation-Invariant Execution": a compacted
 // neuron subset is an ordinary dense matrix).
 //
-// Step 1 (pack): A[m][k] = m_{m,row_k} a_{m,row_k}, split into bf16 hi + lo,
-//   [Mpad][Kpad] each, zero beyond the batch and the row count.
-// Step 2 (contract): tokens are the MFMA M dimension, output columns the N
-//   dimension and gathered rows the K dimension.  W^T rows are contiguous
-//   along N, so a workgroup stages a 64-row x 256-column tile in LDS with
-//   16-byte coalesced loads, and each lane gathers its B operand (8 rows of
-//   one column) from LDS.  The LDS row pitch (129 dwords) puts the four
-//   K-groups of a wave on disjoint banks.  Split-K over row chunks; a second
-//   kernel sums the chunks' partials in chunk order.
+// Tokens are the MFMA M dimension, output columns the N dimension and
+// gathered rows the K dimension.  W^T rows are contiguous along N, so a
+// workgroup stages a 64-row x 256-column tile in LDS with 16-byte coalesced
+// loads and each lane gathers its B operand (8 rows of one column) from
+// LDS; the LDS row pitch (129 dwords) puts the four K-groups of a wave on
+// disjoint banks.  The A operand is built per stage in the same kernel: the
+// 16 tokens' activations of the stage's 64 rows are gathered (masked per
+// token), split into bf16 hi + lo (x = hi + lo to ~2^-17 relative) and
+// staged in LDS; two MFMAs (hi, lo) into one fp32 accumulator keep fp32-grade
+// accuracy with bf16 weights.
+//
+// Pipeline: the chunk's row indices are read once into LDS; each stage's
+// weights and activations are requested right after the previous stage was
+// copied to LDS, so they are in flight while that stage is contracted.
+// Split-K over row chunks; a second kernel sums the chunks' partials in
+// chunk order.
 #include "sffn_splitk.h"
 
 namespace sffn {
@@ -25,30 +32,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kOT = 256;          // output columns per workgroup
 constexpr int kKT = 64;           // gathered rows per LDS stage
 constexpr int kPitch = 258;       // LDS row pitch in bf16 elements (129 dwords)
+constexpr int kSeg = 2048;        // row indices held in LDS at a time
+constexpr int kAPitch = kKT / 8 + 1;   // activation tile pitch in 16-byte units
 
-__global__ __launch_bounds__(256) void pack_acts_kernel(AxpyArgs a, int Kpad, uint16_t* hi,
-                                                        uint16_t* lo) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  const int m = blockIdx.y;
-  if (k >= Kpad) return;
-  const int n_items = item_count(a.idx, a.count, a.k_max, a.group, a.n_rows);
-  float v = 0.f;
-  if (m < a.batch && k < n_items) {
-    const int row = item_row(a.idx, a.group, k);
-    v = a.in[(size_t)m * a.ld_in + row];
-    if (a.row_mask && !a.row_mask[(size_t)m * a.ld_mask + row]) v = 0.f;
-  }
-  const uint32_t h = f32_to_bf16_rne(v);
-  const uint32_t l = f32_to_bf16_rne(v - __uint_as_float(h << 16));
-  hi[(size_t)m * Kpad + k] = (uint16_t)h;
-  lo[(size_t)m * Kpad + k] = (uint16_t)l;
-}
-
-__global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int Mpad, int Kpad,
-                                                        const uint16_t* __restrict__ Ahi,
-                                                        const uint16_t* __restrict__ Alo,
+__global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int Mpad,
                                                         float* partials) {
   __shared__ uint32_t T[kKT * kPitch / 2];
+  __shared__ uint4 As[2][16][kAPitch];      // activations of the stage, bf16 hi / lo
+  __shared__ int rows_s[kSeg];
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = wave_id();
@@ -62,58 +53,98 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
   chunk = (chunk + kKT - 1) / kKT * kKT;
   const int k0 = ks * chunk;
   const int k1 = min(n_items, k0 + chunk);
-  const int nst = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
 
-  // loader mapping: column chunk c (8 columns), rows r0 + 8j
-  const int lc = t & 31;
-  const int lr = t >> 5;
+  // weight loader: column chunk lc (8 columns), rows lr + 8j
+  const int lc = t & 31, lr = t >> 5;
   const int lcol = col0 + 8 * lc;
-  const bool lcol_ok = lcol < a.d;
+  const int lcolc = lcol < a.d ? lcol : 0;   // lanes past the last column re-read column 0
+  // activation loader: token am, rows 4 ar .. 4 ar + 3 of the stage
+  const int am = t >> 4, ar = t & 15;
+  const int tok = m0 + am;
+  const bool tok_ok = tok < a.batch;
+  const int tokc = tok_ok ? tok : 0;
 
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const uint16_t* Ahi_row = Ahi + (size_t)(m0 + nl) * Kpad + 8 * g;
-  const uint16_t* Alo_row = Alo + (size_t)(m0 + nl) * Kpad + 8 * g;
   const uint16_t* Ts = reinterpret_cast<const uint16_t*>(T);
 
-  for (int st = 0; st < nst; ++st) {
-    const int kb = k0 + st * kKT;
+  for (int s0 = k0; s0 < k1; s0 += kSeg) {
+    const int s1 = min(k1, s0 + kSeg);
+    const int nst = (s1 - s0 + kKT - 1) / kKT;
+    __syncthreads();   // the previous segment's readers of rows_s are done
+    // rows past the segment end repeat its last row (a valid row; weight 0)
+    for (int i = t; i < nst * kKT; i += 256)
+      rows_s[i] = item_row(a.idx, a.group, min(s0 + i, s1 - 1));
+    __syncthreads();
+
+    // raw loads only (no branch on a loaded value), so a stage's requests
+    // stay in flight until the stage is copied to LDS
+    const bool has_mask = a.row_mask != nullptr;
+    const uint8_t* mrow = has_mask ? a.row_mask + (size_t)tokc * a.ld_mask
+                                   : reinterpret_cast<const uint8_t*>(a.in);   // unused bytes
     uint4 v[8];
+    float xr[4];
+    uint32_t mb[4];
+    auto issue = [&](int st) {
+      const int base = st * kKT;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int it = kb + lr + 8 * j;
-      const bool ok = it < k1 && lcol_ok;
-      const int row = ok ? item_row(a.idx, a.group, it) : 0;
-      v[j] = ok ? load_stream16(a.W + (size_t)row * a.ld_w + lcol)
-                : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
+      for (int j = 0; j < 8; ++j)
+        v[j] = load_stream16(a.W + (size_t)rows_s[base + lr + 8 * j] * a.ld_w + lcolc);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t* dst = T + ((lr + 8 * j) * kPitch + 8 * lc) / 2;
-      dst[0] = v[j].x; dst[1] = v[j].y; dst[2] = v[j].z; dst[3] = v[j].w;
-    }
-    __syncthreads();
+      for (int e = 0; e < 4; ++e) {
+        const int r = rows_s[base + 4 * ar + e];
+        xr[e] = a.in[(size_t)tokc * a.ld_in + r];
+        mb[e] = mrow[r];
+      }
+    };
+    issue(0);
+    for (int st = 0; st < nst; ++st) {
+      __syncthreads();   // the previous stage's LDS readers are done
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kk = kb + 32 * s;
-      const uint4 ah = *reinterpret_cast<const uint4*>(Ahi_row + kk);
-      const uint4 al = *reinterpret_cast<const uint4*>(Alo_row + kk);
-      const bf16x8 Ah = __builtin_bit_cast(bf16x8, ah);
-      const bf16x8 Al = __builtin_bit_cast(bf16x8, al);
+      for (int j = 0; j < 8; ++j) {
+        uint32_t* dst = T + ((lr + 8 * j) * kPitch + 8 * lc) / 2;
+        dst[0] = v[j].x; dst[1] = v[j].y; dst[2] = v[j].z; dst[3] = v[j].w;
+      }
+      {
+        float av[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int o = 64 * w + 16 * nt + nl;
-        const uint16_t* src = Ts + (32 * s + 8 * g) * kPitch + o;
-        uint32_t b[4];
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = tok_ok && s0 + st * kKT + 4 * ar + e < s1 && (!has_mask || mb[e] != 0u);
+          av[e] = keep ? xr[e] : 0.f;
+        }
+        uint32_t hi[2], lo[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = (uint32_t)src[(2 * j) * kPitch] | ((uint32_t)src[(2 * j + 1) * kPitch] << 16);
-        const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(b[0], b[1], b[2], b[3]));
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, B, acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, B, acc[nt], 0, 0, 0);
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t h0 = f32_to_bf16_rne(av[2 * e]), h1 = f32_to_bf16_rne(av[2 * e + 1]);
+          const uint32_t l0 = f32_to_bf16_rne(av[2 * e] - __uint_as_float(h0 << 16));
+          const uint32_t l1 = f32_to_bf16_rne(av[2 * e + 1] - __uint_as_float(h1 << 16));
+          hi[e] = h0 | (h1 << 16);
+          lo[e] = l0 | (l1 << 16);
+        }
+        uint2* ah = reinterpret_cast<uint2*>(&As[0][am][0]) + ar;
+        uint2* al = reinterpret_cast<uint2*>(&As[1][am][0]) + ar;
+        *ah = make_uint2(hi[0], hi[1]);
+        *al = make_uint2(lo[0], lo[1]);
+      }
+      if (st + 1 < nst) issue(st + 1);   // in flight while this stage is contracted
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 Ah = __builtin_bit_cast(bf16x8, As[0][nl][4 * s + g]);
+        const bf16x8 Al = __builtin_bit_cast(bf16x8, As[1][nl][4 * s + g]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int o = 64 * w + 16 * nt + nl;
+          const uint16_t* src = Ts + (32 * s + 8 * g) * kPitch + o;
+          uint32_t b[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            b[jj] = (uint32_t)src[(2 * jj) * kPitch] | ((uint32_t)src[(2 * jj + 1) * kPitch] << 16);
+          const bf16x8 Bv = __builtin_bit_cast(bf16x8, make_uint4(b[0], b[1], b[2], b[3]));
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, Bv, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, Bv, acc[nt], 0, 0, 0);
+        }
       }
     }
   }
@@ -139,28 +170,16 @@ hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s) {
   const int Mt = (a.batch + 15) / 16;
   const int Mpad = Mt * 16;
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
-  const int Kpad = (int)((items + 63) / 64 * 64);
   const int col_tiles = (a.d + kOT - 1) / kOT;
-  long KS = (768 + (long)col_tiles * Mt - 1) / ((long)col_tiles * Mt);
+  // one round of workgroups: three per CU (LDS and registers) on 256 CUs
+  long KS = 768 / ((long)col_tiles * Mt);
   const long by_rows = (items + kKT - 1) / kKT;
   if (KS > by_rows) KS = by_rows;
   if (KS > max_split_mfma(Mt)) KS = max_split_mfma(Mt);
   if (KS < 1) KS = 1;
-
-  char* ws = reinterpret_cast<char*>(a.ws);
-  float* partials = reinterpret_cast<float*>(ws + kWsHeaderBytes);
-  const size_t part_bytes = align256((size_t)max_split_mfma(Mt) * Mpad * a.d * sizeof(float));
-  uint16_t* hi = reinterpret_cast<uint16_t*>(ws + kWsHeaderBytes + part_bytes);
-  uint16_t* lo = hi + align256((size_t)Mpad * Kpad * 2) / 2;
-
-  if (Kpad > 0) {
-    hipLaunchKernelGGL(pack_acts_kernel, dim3((Kpad + 255) / 256, Mpad), dim3(256), 0, s, a,
-                       Kpad, hi, lo);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
   hipLaunchKernelGGL(axpy_mfma_kernel, dim3(col_tiles, (int)KS, Mt), dim3(256), 0, s, a, (int)KS,
-                     Mpad, Kpad, hi, lo, partials);
+                     Mpad, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(partials, (int)KS, a.batch, Mpad, a.d, a.alpha, a.out, a.ld_out,

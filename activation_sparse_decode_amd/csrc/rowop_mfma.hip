@@ -7,14 +7,16 @@
 // fp32 accumulator, so the result keeps fp32-grade accuracy with bf16
 // weights.
 //
-// Work split: each wave owns a 16-neuron x 16-token tile over all of K, so
-// no cross-wave reduction is needed.  K is walked in chunks of 128: a wave
-// loads its 16 rows (per weight matrix) with row-contiguous 16-byte loads
-// (four rows of 256 bytes per instruction, not 16 rows of 64 bytes as the
-// MFMA operand layout would read them), stores them in its own LDS area, and
-// reads them back in the B-operand layout (lane (n, g) takes 8 consecutive k
-// of row n).  The next chunk's weights and activations are loaded while the
-// current chunk is contracted.
+// Work split: a workgroup owns two 16-neuron x 16-token tiles; two waves
+// share a tile, one per half of K, and their accumulators are added in LDS
+// at the end (so a CU keeps twice the loads in flight that one wave per tile
+// would).  K is walked in chunks of 128: a wave loads its 16 rows (per
+// weight matrix) with row-contiguous 16-byte loads (four rows of 256 bytes
+// per instruction, not 16 rows of 64 bytes as the MFMA operand layout would
+// read them), stores them in its own LDS area, and reads them back in the
+// B-operand layout (lane (n, g) takes 8 consecutive k of row n).  The next
+// chunk's weights and activations are in flight while the current chunk is
+// contracted.
 #include "sffn_device.h"
 
 namespace sffn {
@@ -54,17 +56,18 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
   constexpr bool kW0 = OP != kOpGated;
   constexpr bool kW1 = OP == kOpGlu || OP == kOpGated;
   constexpr int kMat = (kW0 && kW1) ? 2 : 1;
-  __shared__ u32x4 stage[4][kMat][16][kPitch];   // each wave's 16 weight rows of the chunk
-  __shared__ u32x4 xs[2][16][kPitch];          // the chunk's activations, bf16 hi / lo
+  __shared__ u32x4 stage[4][kMat][16][kPitch];   // each wave's 16 weight rows of its chunk
+  __shared__ u32x4 xs[2][2][16][kPitch];         // [half][hi / lo][token][k group]
   __shared__ float sq_tok[16];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = wave_id();
+  const int tile = w >> 1, half = w & 1;       // two 16-neuron tiles x two halves of K
   const int nl = lane & 15;
   const int g = lane >> 4;
   const int m0 = blockIdx.y * 16;
-  const int t0 = (blockIdx.x * 4 + w) * 16;   // this wave's first item
+  const int t0 = (blockIdx.x * 2 + tile) * 16;   // this wave's first item
 
   int n_items;
   if (a.idx) {
@@ -74,10 +77,9 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
   } else {
     n_items = a.n_rows;
   }
-  // Every wave runs the same chunk loop (block barriers); rows past the end
-  // read row 0 and tokens past the batch read token 0 (valid, finite data):
-  // an MFMA output (m, n) depends only on A row m and B column n, so those
-  // lanes only produce outputs that are never stored.
+  // Rows past the end read row 0 and tokens past the batch read token 0
+  // (valid, finite data): an MFMA output (m, n) depends only on A row m and
+  // B column n, so those lanes only produce outputs that are never stored.
   auto item_to_row = [&](int it) -> int {
     if (it >= n_items) return 0;
     if (!a.idx) return it;
@@ -93,7 +95,8 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
   }
   const int my_row = item_to_row(t0 + nl);          // output column of this lane
   const bool my_live = t0 + nl < n_items;
-  // activation loader: thread t loads token t >> 4, k-offset 8*(t & 15) of each chunk
+  // activation loader: thread t loads token t >> 4, k-offset 8*(t & 15) of
+  // both halves' chunks
   const int xt = t >> 4, xg = t & 15;
   const int xtok = m0 + xt < a.batch ? m0 + xt : 0;
   const float* xsrc = a.x + (size_t)xtok * a.ld_in + 8 * xg;
@@ -102,98 +105,136 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
   float sq = 0.f;        // this thread's share of token xt's sum of squares (chunks)
   float sq_tail = 0.f;   // token nl's squares in k-group g of the tail
 
+  // chunks of 128 k: the first half of K takes [0, nA), the second [nA, nch)
   const int nch = a.d / kKC;
-  u32x4 wr0[4], wr1[4];   // in-flight weights (this lane's share of the next chunk)
-  float4 xr0, xr1;        // in-flight activations (this thread's 8 values)
-  auto load_chunk = [&](int k) {
+  const int nA = (nch + 1) / 2, nB = nch - nA;
+  const int my_n = half ? nB : nA;
+  const int my_c0 = half ? nA : 0;
+  u32x4 wr0[4], wr1[4];   // in-flight weights (this lane's share of its next chunk)
+  float4 xr[2][2];        // in-flight activations: [half][8 values]
+  auto load_chunk = [&](int c) {
+    if (c < my_n) {
+      const int k = (my_c0 + c) * kKC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kW0) wr0[i] = *reinterpret_cast<const u32x4*>(a.W0 + woff[i] + k);
-      if (kW1) wr1[i] = *reinterpret_cast<const u32x4*>(a.W1 + woff[i] + k);
+      for (int i = 0; i < 4; ++i) {
+        if (kW0) wr0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.W0 + woff[i] + k));
+        if (kW1) wr1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.W1 + woff[i] + k));
+      }
     }
-    xr0 = *reinterpret_cast<const float4*>(xsrc + k);
-    xr1 = *reinterpret_cast<const float4*>(xsrc + k + 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (c < (h ? nB : nA)) {
+        const int k = ((h ? nA : 0) + c) * kKC;
+        xr[h][0] = *reinterpret_cast<const float4*>(xsrc + k);
+        xr[h][1] = *reinterpret_cast<const float4*>(xsrc + k + 4);
+      }
+    }
   };
-  if (nch > 0) load_chunk(0);
-  for (int c = 0; c < nch; ++c) {
+  if (nA > 0) load_chunk(0);
+  for (int c = 0; c < nA; ++c) {
     __syncthreads();              // the previous chunk's LDS reads are done
     {
       const int rr = lane >> 4, cc = lane & 15;
+      if (c < my_n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kW0) stage[w][0][4 * i + rr][cc] = wr0[i];
-        if (kW1) stage[w][kMat - 1][4 * i + rr][cc] = wr1[i];
+        for (int i = 0; i < 4; ++i) {
+          if (kW0) stage[w][0][4 * i + rr][cc] = wr0[i];
+          if (kW1) stage[w][kMat - 1][4 * i + rr][cc] = wr1[i];
+        }
       }
-      sq = fmaf(xr0.x, xr0.x, sq); sq = fmaf(xr0.y, xr0.y, sq);
-      sq = fmaf(xr0.z, xr0.z, sq); sq = fmaf(xr0.w, xr0.w, sq);
-      sq = fmaf(xr1.x, xr1.x, sq); sq = fmaf(xr1.y, xr1.y, sq);
-      sq = fmaf(xr1.z, xr1.z, sq); sq = fmaf(xr1.w, xr1.w, sq);
-      uint4 h, l;
-      split8(xr0, xr1, h, l);
-      xs[0][xt][xg] = (u32x4){h.x, h.y, h.z, h.w};
-      xs[1][xt][xg] = (u32x4){l.x, l.y, l.z, l.w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (c < (h ? nB : nA)) {
+          const float4 p = xr[h][0], q = xr[h][1];
+          sq = fmaf(p.x, p.x, sq); sq = fmaf(p.y, p.y, sq);
+          sq = fmaf(p.z, p.z, sq); sq = fmaf(p.w, p.w, sq);
+          sq = fmaf(q.x, q.x, sq); sq = fmaf(q.y, q.y, sq);
+          sq = fmaf(q.z, q.z, sq); sq = fmaf(q.w, q.w, sq);
+          uint4 hh, ll;
+          split8(p, q, hh, ll);
+          xs[h][0][xt][xg] = (u32x4){hh.x, hh.y, hh.z, hh.w};
+          xs[h][1][xt][xg] = (u32x4){ll.x, ll.y, ll.z, ll.w};
+        }
+      }
     }
     __syncthreads();
-    if (c + 1 < nch) load_chunk((c + 1) * kKC);
+    if (c + 1 < nA) load_chunk(c + 1);
+    if (c < my_n) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // A operand: token nl, k = 32 s + 8 g; B operand: row nl, same k
-      const u32x4 ah = xs[0][nl][4 * s + g], al = xs[1][nl][4 * s + g];
-      if (kW0) {
-        const u32x4 b = stage[w][0][nl][4 * s + g];
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
-      }
-      if (kW1) {
-        const u32x4 b = stage[w][kMat - 1][nl][4 * s + g];
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, b), acc1, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, b), acc1, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        // A operand: token nl, k = 32 s + 8 g; B operand: row nl, same k
+        const u32x4 ah = xs[half][0][nl][4 * s + g], al = xs[half][1][nl][4 * s + g];
+        if (kW0) {
+          const u32x4 b = stage[w][0][nl][4 * s + g];
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, b), acc0, 0, 0, 0);
+        }
+        if (kW1) {
+          const u32x4 b = stage[w][kMat - 1][nl][4 * s + g];
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, b), acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, b), acc1, 0, 0, 0);
+        }
       }
     }
   }
-  // tail (d not a multiple of 128): one 32-k step at a time, straight from memory
-  for (int k = nch * kKC; k < a.d; k += 32) {
-    const float* xp = a.x + (size_t)(m0 + nl < a.batch ? m0 + nl : 0) * a.ld_in + k + 8 * g;
-    const float4 p = *reinterpret_cast<const float4*>(xp);
-    const float4 q = *reinterpret_cast<const float4*>(xp + 4);
-    // lane (nl, g) holds token nl's k-group g (the same in every wave; wave 0's count is used)
-    sq_tail = fmaf(p.x, p.x, sq_tail); sq_tail = fmaf(p.y, p.y, sq_tail);
-    sq_tail = fmaf(p.z, p.z, sq_tail); sq_tail = fmaf(p.w, p.w, sq_tail);
-    sq_tail = fmaf(q.x, q.x, sq_tail); sq_tail = fmaf(q.y, q.y, sq_tail);
-    sq_tail = fmaf(q.z, q.z, sq_tail); sq_tail = fmaf(q.w, q.w, sq_tail);
-    uint4 xh, xl;
-    split8(p, q, xh, xl);
-    const size_t off = (size_t)my_row * a.ld_w + k + 8 * g;
-    if (kW0) {
-      const uint4 b = *reinterpret_cast<const uint4*>(a.W0 + off);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(b), acc0, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(b), acc0, 0, 0, 0);
-    }
-    if (kW1) {
-      const uint4 b = *reinterpret_cast<const uint4*>(a.W1 + off);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(b), acc1, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(b), acc1, 0, 0, 0);
+  // tail (d not a multiple of 128), taken by the second-half waves: one
+  // 32-k step at a time, straight from memory
+  if (half == 1) {
+    for (int k = nch * kKC; k < a.d; k += 32) {
+      const float* xp = a.x + (size_t)(m0 + nl < a.batch ? m0 + nl : 0) * a.ld_in + k + 8 * g;
+      const float4 p = *reinterpret_cast<const float4*>(xp);
+      const float4 q = *reinterpret_cast<const float4*>(xp + 4);
+      // lane (nl, g) holds token nl's k-group g (the same in both such waves; wave 1's count is used)
+      sq_tail = fmaf(p.x, p.x, sq_tail); sq_tail = fmaf(p.y, p.y, sq_tail);
+      sq_tail = fmaf(p.z, p.z, sq_tail); sq_tail = fmaf(p.w, p.w, sq_tail);
+      sq_tail = fmaf(q.x, q.x, sq_tail); sq_tail = fmaf(q.y, q.y, sq_tail);
+      sq_tail = fmaf(q.z, q.z, sq_tail); sq_tail = fmaf(q.w, q.w, sq_tail);
+      uint4 xh, xl;
+      split8(p, q, xh, xl);
+      const size_t off = (size_t)my_row * a.ld_w + k + 8 * g;
+      if (kW0) {
+        const uint4 b = *reinterpret_cast<const uint4*>(a.W0 + off);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(b), acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(b), acc0, 0, 0, 0);
+      }
+      if (kW1) {
+        const uint4 b = *reinterpret_cast<const uint4*>(a.W1 + off);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xh), as_bf16x8(b), acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xl), as_bf16x8(b), acc1, 0, 0, 0);
+      }
     }
   }
 
   // token sums of squares: the chunk part is spread over the 16 loader threads
   // of each token (lanes 16j..16j+15 of a wave); the tail part over the four
-  // k-groups of wave 0's lanes nl + 16 g.  Both are combined through LDS in a
-  // fixed order.
+  // k-groups of wave 1's lanes nl + 16 g.  Both are combined through LDS in a
+  // fixed order, and the second halves' accumulators are handed to the first
+  // halves.
   {
     float v = sq;
     v += __shfl_xor(v, 1, kWave); v += __shfl_xor(v, 2, kWave);
     v += __shfl_xor(v, 4, kWave); v += __shfl_xor(v, 8, kWave);
     float tv = sq_tail;
     tv += __shfl_xor(tv, 16, kWave); tv += __shfl_xor(tv, 32, kWave);
-    __syncthreads();
+    __syncthreads();   // every wave is past its last chunk: the staging area is free
+    // the second halves' accumulators, [tile][matrix][lane], in the staging area
+    f32x4(*comb)[kMat][64] = reinterpret_cast<f32x4(*)[kMat][64]>(&stage[0][0][0][0]);
     if (xg == 0) sq_tok[xt] = v;
+    if (half == 1) {
+      if (kW0) comb[tile][0][lane] = acc0;
+      if (kW1) comb[tile][kMat - 1][lane] = acc1;
+    }
     __syncthreads();
-    if (t < 16 && nch * kKC < a.d) sq_tok[t] += tv;
+    if (t >= 64 && t < 80 && nch * kKC < a.d) sq_tok[t - 64] += tv;
     __syncthreads();
   }
+  if (half == 1 || !my_live) return;
+  {
+    const f32x4(*comb)[kMat][64] = reinterpret_cast<const f32x4(*)[kMat][64]>(&stage[0][0][0][0]);
+    if (kW0) acc0 += comb[tile][0][lane];
+    if (kW1) acc1 += comb[tile][kMat - 1][lane];
+  }
 
-  if (!my_live) return;
   // C layout of the 16x16 MFMA: lane l, register i holds row m = 4*(l/16)+i
   // (token) and column n = l%16 (neuron).
 #pragma unroll
@@ -225,7 +266,7 @@ hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s) {
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
   const int mt = (a.batch + 15) / 16;
   if (items == 0) return hipSuccess;
-  dim3 grid((int)((items + 63) / 64), mt);   // 4 waves x 16 neurons per workgroup
+  dim3 grid((int)((items + 31) / 32), mt);   // 2 tiles of 16 neurons x 2 halves of K per workgroup
   switch (a.op) {
     case kOpGlu: hipLaunchKernelGGL(rowop_mfma_kernel<kOpGlu>, grid, dim3(256), 0, s, a); break;
     case kOpDotRelu: hipLaunchKernelGGL(rowop_mfma_kernel<kOpDotRelu>, grid, dim3(256), 0, s, a); break;

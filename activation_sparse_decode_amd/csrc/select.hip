@@ -432,6 +432,8 @@ static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
   else if (need <= 4) hipLaunchKernelGGL((select_kernel<NT, 4>), grid, block, 0, s, a);
   else if (need <= 8) hipLaunchKernelGGL((select_kernel<NT, 8>), grid, block, 0, s, a);
   else if (need <= 16) hipLaunchKernelGGL((select_kernel<NT, 16>), grid, block, 0, s, a);
+  else if (need <= 20) hipLaunchKernelGGL((select_kernel<NT, 20>), grid, block, 0, s, a);
+  else if (need <= 24) hipLaunchKernelGGL((select_kernel<NT, 24>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((select_kernel<NT, 32>), grid, block, 0, s, a);
   return hipGetLastError();
 }

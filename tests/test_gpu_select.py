@@ -50,7 +50,7 @@ def check(keys_np, key_type, r_lo, r_hi, nonzero_only=False, include=None, want_
         assert np.array_equal(freq, expect_freq)
 
 
-@pytest.mark.parametrize("n", [1, 7, 64, 1000, 1024, 4097, 8192, 14336, 17408, 32768])
+@pytest.mark.parametrize("n", [1, 7, 64, 1000, 1024, 4097, 8192, 14336, 17408, 20480, 23001, 32768])
 def test_topk_float_magnitude(n):
     banner(f"select float n={n}")
     rng = np.random.default_rng(n)
