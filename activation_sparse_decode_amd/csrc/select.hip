@@ -76,14 +76,14 @@ __device__ __forceinline__ uint32_t key_of_bits(int key_type, uint32_t b) {
 // gives lane j the packed count of all blocks before (j, this wave) and the
 // totals; an entry's position is then that offset (read from lane j) plus
 // the number of lower lanes in its ballot.
-template <int NT, int KPT>
+template <int NT, int KPT, bool TWO>
 __device__ __forceinline__ void ordered_counts(uint32_t bits_h, uint32_t bits_l,
                                                uint32_t (*cnt)[NT / 64]) {
   const int lane = threadIdx.x & 63, w = wave_id();
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint64_t bh = __ballot((bits_h >> j) & 1u);
-    const uint64_t bl = __ballot((bits_l >> j) & 1u);
+    const uint64_t bl = TWO ? __ballot((bits_l >> j) & 1u) : 0ull;
     if (lane == 0) cnt[j][w] = ((uint32_t)__popcll(bh) << 16) | (uint32_t)__popcll(bl);
   }
 }
@@ -106,9 +106,11 @@ __device__ __forceinline__ uint32_t ordered_offsets(uint32_t (*cnt)[NT / 64], ui
   return incl - row_total + row_below;
 }
 
+template <bool TWO>
 __device__ __forceinline__ uint32_t ordered_pos(uint32_t off_j, uint32_t bits_h, uint32_t bits_l,
                                                 int j) {
   const uint64_t bh = __ballot((bits_h >> j) & 1u);
+  if (!TWO) return off_j + (lanes_below(bh) << 16);
   const uint64_t bl = __ballot((bits_l >> j) & 1u);
   return off_j + ((lanes_below(bh) << 16) | lanes_below(bl));
 }
@@ -193,7 +195,7 @@ __device__ __forceinline__ void scan_pass(const uint32_t* H, int nb, bool want_h
   }
 }
 
-template <int NT, int KPT>
+template <int NT, int KPT, bool LO>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr int NW = NT / 64;
   constexpr int kBins = 2048;
@@ -268,19 +270,21 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const bool e = (j * NT + t < a.n) & (!a.nonzero_only | (key[j] != 0u));
     elig |= (e ? 1u : 0u) << j;
     kor |= e ? key[j] : 0u;
-    ecount += (uint32_t)__popcll(__ballot(e));
+    if (a.nonzero_only) ecount += (uint32_t)__popcll(__ballot(e));   // else every entry counts
   }
   kor = wave_incl<true>(kor);
   if (lane == 63) { wsum[0][w] = kor; wsum[1][w] = ecount; }
-  for (int i = t; i < 3 * (kBins + 4); i += NT) (&hist[0][0])[i] = 0u;
+  // the first pass's histogram now; the later passes' ones while wave 0 scans the first
+  for (int i = t; i < kBins + 4; i += NT) hist[0][i] = 0u;
   if (t == 0) ncand = 0u;
   __syncthreads();
 
   uint32_t all_or = 0, E = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) { all_or |= wsum[0][i]; E += wsum[1][i]; }
+  if (!a.nonzero_only) E = (uint32_t)a.n;
   const uint32_t rhi = min((uint32_t)a.r_hi, E);
-  const uint32_t rlo = min((uint32_t)a.r_lo, rhi);
+  const uint32_t rlo = LO ? min((uint32_t)a.r_lo, rhi) : 0u;
   // all_hi / all_lo: the bound covers every eligible entry (no search)
   const bool all_hi = rhi == E;
   const bool all_lo = rlo == E && rlo > 0;
@@ -326,7 +330,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         }
       }
       __syncthreads();
-      if (w == 0) scan_pass(H, 1 << width, need_hi, rem_hi, need_lo, rem_lo, found);
+      if (w == 0) {
+        scan_pass(H, 1 << width, need_hi, rem_hi, need_lo, rem_lo, found);
+      } else if (pass == 0) {
+        for (int i = t - 64; i < 2 * (kBins + 4); i += NT - 64) (&hist[1][0])[i] = 0u;
+      }
       __syncthreads();
       // found[] is written again only after the next pass's histogram
       // barrier, which every thread reaches after these reads
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       eq_h |= ((e && split_hi && key[j] == pre_hi) ? 1u : 0u) << j;
       eq_l |= ((e && split_lo && key[j] == pre_lo) ? 1u : 0u) << j;
     }
-    ordered_counts<NT, KPT>(eq_h, eq_l, cnt[0]);
+    ordered_counts<NT, KPT, LO>(eq_h, eq_l, cnt[0]);
     __syncthreads();
     uint32_t dummy;
     eq_off = ordered_offsets<NT, KPT>(cnt[0], dummy);
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const bool e = (elig >> j) & 1u;
     uint32_t eqpos = 0;
     if (split_hi || split_lo)
-      eqpos = ordered_pos((uint32_t)__builtin_amdgcn_readlane((int)eq_off, j), eq_h, eq_l, j);
+      eqpos = ordered_pos<LO>((uint32_t)__builtin_amdgcn_readlane((int)eq_off, j), eq_h, eq_l, j);
     const bool gt_hi = (k > pre_hi) | ((k == pre_hi) & ((eqpos >> 16) < rem_hi));
     const bool gt_lo = (k > pre_lo) | ((k == pre_lo) & ((eqpos & 0xFFFFu) < rem_lo));
     const bool in_hi = e & (all_hi | (need_hi & gt_hi));
@@ -400,14 +408,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 
   // one ordered scan for both lists: selected in the high half, top list in the low
-  ordered_counts<NT, KPT>(sel, top, cnt[1]);
+  ordered_counts<NT, KPT, LO>(sel, top, cnt[1]);
   __syncthreads();
   uint32_t total;
   const uint32_t off = ordered_offsets<NT, KPT>(cnt[1], total);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int n = j * NT + t;
-    const uint32_t pos = ordered_pos((uint32_t)__builtin_amdgcn_readlane((int)off, j), sel, top, j);
+    const uint32_t pos = ordered_pos<LO>((uint32_t)__builtin_amdgcn_readlane((int)off, j), sel, top, j);
     const bool s = (sel >> j) & 1u;
     if (n < a.n) {
       if (a.mask_out) a.mask_out[(size_t)row * a.ld_mask + n] = s ? 1 : 0;
@@ -423,19 +431,26 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if (t == 0 && a.count_top_out) a.count_top_out[row] = (int32_t)(total & 0xFFFFu);
 }
 
-template <int NT>
+template <int NT, bool LO>
 static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
   const int need = (a.n + NT - 1) / NT;
   dim3 grid(a.rows), block(NT);
-  if (need <= 1) hipLaunchKernelGGL((select_kernel<NT, 1>), grid, block, 0, s, a);
-  else if (need <= 2) hipLaunchKernelGGL((select_kernel<NT, 2>), grid, block, 0, s, a);
-  else if (need <= 4) hipLaunchKernelGGL((select_kernel<NT, 4>), grid, block, 0, s, a);
-  else if (need <= 8) hipLaunchKernelGGL((select_kernel<NT, 8>), grid, block, 0, s, a);
-  else if (need <= 16) hipLaunchKernelGGL((select_kernel<NT, 16>), grid, block, 0, s, a);
-  else if (need <= 20) hipLaunchKernelGGL((select_kernel<NT, 20>), grid, block, 0, s, a);
-  else if (need <= 24) hipLaunchKernelGGL((select_kernel<NT, 24>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((select_kernel<NT, 32>), grid, block, 0, s, a);
+  if (need <= 1) hipLaunchKernelGGL((select_kernel<NT, 1, LO>), grid, block, 0, s, a);
+  else if (need <= 2) hipLaunchKernelGGL((select_kernel<NT, 2, LO>), grid, block, 0, s, a);
+  else if (need <= 4) hipLaunchKernelGGL((select_kernel<NT, 4, LO>), grid, block, 0, s, a);
+  else if (need <= 8) hipLaunchKernelGGL((select_kernel<NT, 8, LO>), grid, block, 0, s, a);
+  else if (need <= 16) hipLaunchKernelGGL((select_kernel<NT, 16, LO>), grid, block, 0, s, a);
+  else if (need <= 20) hipLaunchKernelGGL((select_kernel<NT, 20, LO>), grid, block, 0, s, a);
+  else if (need <= 24) hipLaunchKernelGGL((select_kernel<NT, 24, LO>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((select_kernel<NT, 32, LO>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+// Ranges that start at rank 0 (no lower bound, no second list) take the
+// variant that carries one ballot per entry instead of two.
+template <int NT>
+static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
+  return a.r_lo > 0 ? launch_nt<NT, true>(a, s) : launch_nt<NT, false>(a, s);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
