@@ -20,11 +20,11 @@
 //     T_r of the r-th largest entry, how many entries equal to T_r fall
 //     inside the top r, and how many equal T_r in all.  Both bounds share
 //     one LDS histogram (16-bit halves of one counter); wave 0 scans it with
-//     DPP lane moves.  After the first pass only the keys in the bins that
-//     hold a bound can matter; they are appended to an LDS list, and the
-//     later passes count only that list.  A bound that covers every eligible
-//     entry needs no search (pure compaction, e.g. the nonzero clusters of a
-//     ReLU layer).
+//     DPP lane moves.  After the first pass only the keys whose higher
+//     digits match a bound can matter: each thread tests its own keys and
+//     only those are counted in the later passes.  A bound that covers every
+//     eligible entry needs no search (pure compaction, e.g. the nonzero
+//     clusters of a ReLU layer).
 //  3. Index-order positions come from wave ballots: an entry's position
 //     among the entries with some property is the count in the (j, wave)
 //     blocks before its own plus the count of lower lanes in its ballot.
@@ -199,13 +199,10 @@ template <int NT, int KPT, bool LO>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr int NW = NT / 64;
   constexpr int kBins = 2048;
-  constexpr int kCap = NT * KPT < 8192 ? NT * KPT : 8192;   // candidate list
   __shared__ __align__(16) uint32_t hist[3][kBins + 4];   // one per pass; bin kBins: not counted
-  __shared__ uint32_t cand[kCap];
   __shared__ uint32_t cnt[2][KPT][NW];      // ballot counts of the two ordered scans
   __shared__ uint32_t wsum[2][NW];          // per wave: OR of eligible keys, eligible count
   __shared__ uint32_t found[8];             // hi: digit, rem, count; lo: digit, rem, count
-  __shared__ uint32_t ncand;
   __shared__ uint32_t ckey[kMaxClusters];   // cluster keys (cluster > 1)
 
   const int row = blockIdx.x;
@@ -276,7 +273,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if (lane == 63) { wsum[0][w] = kor; wsum[1][w] = ecount; }
   // the first pass's histogram now; the later passes' ones while wave 0 scans the first
   for (int i = t; i < kBins + 4; i += NT) hist[0][i] = 0u;
-  if (t == 0) ncand = 0u;
   __syncthreads();
 
   uint32_t all_or = 0, E = 0;
@@ -296,8 +292,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if (need_hi || need_lo) {
     const int msb = all_or ? 31 - __builtin_clz(all_or) : -1;
     int lo_bit = msb + 1;                      // lowest bit decided so far
-    bool use_cand = false;
-    uint32_t nc = 0;
 #pragma unroll 1
     for (int pass = 0; lo_bit > 0; ++pass) {
       const int width = lo_bit < 11 ? lo_bit : 11;
@@ -309,14 +303,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int j = 0; j < KPT; ++j) {
           const uint32_t bin = ((elig >> j) & 1u) ? (key[j] >> shift) & mask : (uint32_t)kBins;
           atomicAdd(&H[bin], 0x10001u);
-        }
-      } else if (use_cand) {
-        for (uint32_t c = t; c < nc; c += NT) {
-          const uint32_t k = cand[c];
-          const bool mh = need_hi && (k >> lo_bit) == (pre_hi >> lo_bit);
-          const bool ml = need_lo && (k >> lo_bit) == (pre_lo >> lo_bit);
-          const uint32_t inc = (mh ? 0x10000u : 0u) + (ml ? 1u : 0u);
-          if (inc) atomicAdd(&H[(k >> shift) & mask], inc);
         }
       } else {
 #pragma unroll
@@ -341,33 +327,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       if (need_hi) { pre_hi |= found[0] << shift; rem_hi = found[1]; tie_hi = found[2]; }
       if (need_lo) { pre_lo |= found[3] << shift; rem_lo = found[4]; tie_lo = found[5]; }
       lo_bit = shift;
-      if (pass == 0 && lo_bit > 0) {
-        // keys in the bins that hold a bound go to the candidate list
-        uint32_t m = 0, wave_n = 0;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-          const uint32_t k = key[j];
-          const bool e = (elig >> j) & 1u;
-          const bool c = e && ((need_hi && (k >> lo_bit) == (pre_hi >> lo_bit)) ||
-                               (need_lo && (k >> lo_bit) == (pre_lo >> lo_bit)));
-          m |= (c ? 1u : 0u) << j;
-          wave_n += (uint32_t)__popcll(__ballot(c));
-        }
-        uint32_t wbase = 0;
-        if (lane == 0) wbase = atomicAdd(&ncand, wave_n);
-        wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-          const bool c = (m >> j) & 1u;
-          const uint64_t b = __ballot(c);
-          const uint32_t p = wbase + lanes_below(b);
-          if (c && p < (uint32_t)kCap) cand[p] = key[j];
-          wbase += (uint32_t)__popcll(b);
-        }
-        __syncthreads();
-        nc = ncand;
-        use_cand = nc <= (uint32_t)kCap;
-      }
     }
   }
 
