@@ -248,27 +248,49 @@ class ReluMoEStack:
         return ex, w
 
     def layer(self, l: int, t: int, h: torch.Tensor, record=None) -> None:
+        """One layer for token t.  The routed experts are independent until
+        their down products are added to h, so each runs on its own stream
+        (forked from and joined back to the caller's stream); only the
+        residual updates are ordered, expert by expert."""
         row = l * self.T + t
         chosen = self.route_host[row]
+        main = torch.cuda.current_stream()
+        streams = self._streams(len(chosen))
+        for s in streams:
+            s.wait_stream(main)
         for j, e in enumerate(chosen):
             Wg, Wu, _ = self.experts[l][e]
-            B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j], tau_scale=self.tau_scale,
-                              rms_eps=self.rms_eps)
-            # clusters holding a nonzero r, keyed by their largest |r| (one call)
-            B.sparse_ffn_select(self.r[j], B.KEY_ABS_F32, 0, self.nc, cluster=self.cluster,
-                                nonzero_only=True, idx_out=self.cidx[j],
-                                count_out=self.ccnt[j:j + 1])
-            B.sparse_ffn_gemv(B.OP_GATED, None, Wu, h, self.a[j], idx=self.cidx[j],
-                              count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
-                              aux=self.r[j], rms_eps=self.rms_eps)
+            with torch.cuda.stream(streams[j]):
+                B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j],
+                                  tau_scale=self.tau_scale, rms_eps=self.rms_eps)
+                # clusters holding a nonzero r, keyed by their largest |r| (one call)
+                B.sparse_ffn_select(self.r[j], B.KEY_ABS_F32, 0, self.nc, cluster=self.cluster,
+                                    nonzero_only=True, idx_out=self.cidx[j],
+                                    count_out=self.ccnt[j:j + 1])
+                B.sparse_ffn_gemv(B.OP_GATED, None, Wu, h, self.a[j], idx=self.cidx[j],
+                                  count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
+                                  aux=self.r[j], rms_eps=self.rms_eps)
         if record is not None:
+            torch.cuda.synchronize()
             record(l, t, h, chosen)
+        prev = None
         for j, e in enumerate(chosen):
             WdT = self.experts[l][e][2]
-            B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[j], h, idx=self.cidx[j],
-                              count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
-                              alpha=self.route_w[row, j:j + 1], accumulate=True,
-                              workspace=self.ws[j])
+            with torch.cuda.stream(streams[j]):
+                if prev is not None:
+                    streams[j].wait_stream(prev)   # h is updated by one expert at a time
+                B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[j], h, idx=self.cidx[j],
+                                  count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
+                                  alpha=self.route_w[row, j:j + 1], accumulate=True,
+                                  workspace=self.ws[j])
+            prev = streams[j]
+        for s in streams:
+            main.wait_stream(s)
+
+    def _streams(self, k: int):
+        if not hasattr(self, "_expert_streams") or len(self._expert_streams) < k:
+            self._expert_streams = [torch.cuda.Stream() for _ in range(k)]
+        return self._expert_streams[:k]
 
     def decode(self, h: torch.Tensor, t: int, record=None) -> None:
         for l in range(self.L):
