@@ -108,13 +108,17 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
   // reductions and barriers and x is reused for the workgroup's whole life.
   int row[NPI];
   bool live[NPI];
+  float prev[NPI];
   uint4 w0[NPI][CPT], w1[NPI][CPT];
+  // With accumulate, the output value each row adds to is requested with the
+  // row's weights, so the epilogue does not wait for it.
   auto fetch = [&](int k, int (&rw)[NPI], bool (&lv)[NPI], uint4 (&v0)[NPI][CPT],
-                   uint4 (&v1)[NPI][CPT]) {
+                   uint4 (&v1)[NPI][CPT], float (&pv)[NPI]) {
 #pragma unroll
     for (int i = 0; i < NPI; ++i) {
       lv[i] = base0 + i + stride * k < n_items;
       rw[i] = lv[i] ? row_of(k, i) : rw[0];   // a dead row re-reads the group's first row
+      pv[i] = a.accumulate ? a.out[rw[i]] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < NPI; ++i)
@@ -126,14 +130,15 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
       }
   };
   int k = 0;
-  if (base0 < n_items) fetch(0, row, live, w0, w1);
+  if (base0 < n_items) fetch(0, row, live, w0, w1, prev);
 
   for (; base0 + stride * k < n_items; ++k) {
     int nrow[NPI];
     bool nlive[NPI];
+    float nprev[NPI];
     uint4 n0[NPI][CPT], n1[NPI][CPT];
     const bool more = base0 + stride * (k + 1) < n_items;
-    if (more) fetch(k + 1, nrow, nlive, n0, n1);
+    if (more) fetch(k + 1, nrow, nlive, n0, n1, nprev);
 
     if (need_norm && !have_norm) {
       float s = 0.f;
@@ -189,8 +194,12 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
       g *= inv;
       u *= inv;
       int r = 0;
+      float pv = 0.f;
 #pragma unroll
-      for (int ii = 0; ii < NPI; ++ii) r = (ii == i) ? row[ii] : r;
+      for (int ii = 0; ii < NPI; ++ii) {
+        r = (ii == i) ? row[ii] : r;
+        pv = (ii == i) ? prev[ii] : pv;
+      }
       float v;
       if (OP == kOpGlu) {
         v = (g / (1.f + expf(-g))) * u;
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
       } else {
         v = g;
       }
-      if (a.accumulate) v += a.out[r];
+      if (a.accumulate) v += pv;
       a.out[r] = v;
       if (a.key_out) a.key_out[r] = key_abs(v);
     }
@@ -211,6 +220,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
       for (int i = 0; i < NPI; ++i) {
         row[i] = nrow[i];
         live[i] = nlive[i];
+        prev[i] = nprev[i];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
           if (kUse0) w0[i][j] = n0[i][j];
