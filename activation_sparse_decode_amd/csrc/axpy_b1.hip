@@ -89,14 +89,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int q = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int m = blockIdx.y;
   const int c = blockIdx.x * 64 + 4 * q;
+  const int cc = c < d ? c : 0;   // lanes past the last column re-read column 0 (discarded)
+  // The values added to (with accumulate) and the scale are requested right
+  // after the partials, so the epilogue does not wait for them (and the
+  // scale's scalar load does not hold back the partials' requests).
+  float* o = out + (size_t)m * ld_out + cc;   // 4-byte aligned (ld_out may be any stride)
   float4 v[kPerGroup];
 #pragma unroll
   for (int i = 0; i < kPerGroup; ++i) {
     const int k = g + kGroups * i;
-    v[i] = (k < KS && c < d)
-               ? *reinterpret_cast<const float4*>(partials + ((size_t)k * Mp + m) * d + c)
-               : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = k < KS ? *reinterpret_cast<const float4*>(partials + ((size_t)k * Mp + m) * d + cc)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  float prev[4] = {0.f, 0.f, 0.f, 0.f};
+  if (accumulate) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) prev[e] = o[e];
+  }
+  asm volatile("" ::: "memory");
+  const float al = alpha ? alpha[m] : 1.f;
   float4 s = v[0];
 #pragma unroll
   for (int i = 1; i < kPerGroup; ++i) {
@@ -111,11 +122,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const float4 r = red[gg][q];
     t.x += r.x; t.y += r.y; t.z += r.z; t.w += r.w;
   }
-  const float al = alpha ? alpha[m] : 1.f;
-  float* o = out + (size_t)m * ld_out + c;
   const float tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = (accumulate ? o[e] : 0.f) + al * tv[e];
+  for (int e = 0; e < 4; ++e) o[e] = prev[e] + al * tv[e];
 }
 
 hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, int d,

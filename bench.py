@@ -467,7 +467,7 @@ def run_c3(args, torch, B, synth, P, T):
                 B.sparse_ffn_gemv(B.OP_DOT_RELU, experts[l][e][0], None, h, moe.r[j],
                                   tau_scale=moe.tau_scale, rms_eps=moe.rms_eps)
 
-    gate_us = T.replay_ms(T.capture(gates_only), 4) * 1e3 / (4 * L * 2)
+    gate_us = T.replay_ms(T.capture(gates_only), 16) * 1e3 / (16 * L * 2)
 
     cpu = None
     if args.cpu_seconds > 0:
