@@ -9,9 +9,11 @@
 // workgroup owns one column tile and one contiguous chunk of the compacted
 // row list; wave w takes rows w, w+16, ...; lane l owns columns 8l..8l+7 of
 // the tile and streams them with one 16-byte nontemporal load per row
-// (1 KiB per wave instruction), four rows in flight per lane.  Waves are summed in LDS and the chunk's
+// (1 KiB per wave instruction), four or eight rows in flight per lane.  Waves are summed in LDS and the chunk's
 // partial row goes to the workspace.  Kernel 2 sums the KS partials in chunk
 // order and applies alpha / accumulate.
+#include <type_traits>
+
 #include "sffn_splitk.h"
 
 namespace sffn {
@@ -34,7 +36,6 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
   const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
   for (int ub = 0; ub < nu; ub += 64) {
     const bool ok = ub + lane < nu;
     const int it = k0 + w + kWaves * (ok ? ub + lane : 0);
@@ -45,7 +46,8 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
     // nothing waits between them.  The activations are gathered after the
     // batch's weights were requested (r is a valid row for every lane), so
     // their wait is the batch's wait.
-    for (int u = 0; u < nb; u += U) {
+    auto batch = [&](int u, auto width) {
+      constexpr int U = decltype(width)::value;
       uint4 wv[U];
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
@@ -64,7 +66,11 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(au, f[e], acc[e]);
       }
-    }
+    };
+    // eight rows in flight per lane while at least eight remain, then four
+    int u = 0;
+    for (; u + 8 <= nb; u += 8) batch(u, std::integral_constant<int, 8>());
+    for (; u < nb; u += 4) batch(u, std::integral_constant<int, 4>());
   }
 
   const float part = wg_reduce_cols(red, acc);
