@@ -9,29 +9,35 @@
 // values whose key is the largest key of the block (PowerInfer-2 guide,
 // "Neuron Cluster Decomposition": the cluster is the unit that is selected).
 //
-// Method: NT threads; thread t owns the entries j*NT + t (j < KPT), so every
-// load and every mask store of a wave is contiguous.  One workgroup handles
-// a row (at most 32768 entries), so the cost is the instructions each wave
-// issues and the chain of barriers; the kernel keeps both short.
+// Method: NT threads; wave w owns the KPT*64 consecutive entries starting at
+// w*KPT*64, lane l the entries w*KPT*64 + j*64 + l (j < KPT), so every load
+// and every mask store of a wave is contiguous.  One workgroup handles a row
+// (at most 32768 entries): the cost is the instructions each wave issues
+// and the chain of barriers, and the kernel keeps both short.
 //  1. The largest eligible key (an OR over the row) fixes the most
 //     significant bit that varies, so the digits start there: keys that fit
 //     in 11 bits (e.g. frequency counts) take one pass, float magnitudes 3.
 //  2. MSB-first radix search finds, for each bound r in {r_hi, r_lo}, the key
 //     T_r of the r-th largest entry, how many entries equal to T_r fall
 //     inside the top r, and how many equal T_r in all.  Both bounds share
-//     one LDS histogram (16-bit halves of one counter); wave 0 scans it with
-//     DPP lane moves.  After the first pass only the keys whose higher
-//     digits match a bound can matter: each thread tests its own keys and
-//     only those are counted in the later passes.  A bound that covers every
-//     eligible entry needs no search (pure compaction, e.g. the nonzero
-//     clusters of a ReLU layer).
-//  3. Index-order positions come from wave ballots: an entry's position
-//     among the entries with some property is the count in the (j, wave)
-//     blocks before its own plus the count of lower lanes in its ballot.
-//     This places the selected indices (ascending lists, contiguous stores)
-//     and, when T_r is tied across the bound, ranks the tied entries in
-//     index order, which decides them as the (key desc, index asc) order
-//     does.
+//     one LDS histogram (16-bit halves of one counter).  Entries that take no
+//     part count into per-lane sink bins that are never read: LDS atomics of
+//     one wave on one address serialise, so a shared sink would cost ~2
+//     cycles per lane.  Every thread scans its share of the bins (counts
+//     above it from a DPP scan within the wave plus the totals of the waves
+//     before), and the one thread whose bins hold the rank walks them.
+//     After the first pass only the keys whose higher digits match a bound
+//     can matter: each thread tests its own keys and only those are
+//     counted.  A bound that covers every eligible entry needs no search
+//     (pure compaction, e.g. the nonzero clusters of a ReLU layer).
+//  3. Index-order positions: a wave's entries are consecutive, so the
+//     position of an entry among those with some property is the count in
+//     the waves before (one exchange through LDS), plus the wave's running
+//     count over its earlier slots (scalar bit counts of ballots), plus the
+//     lower lanes of its own ballot.  This places the selected indices
+//     (ascending lists, contiguous stores) and, when T_r is tied across the
+//     bound, ranks the tied entries in index order, which decides them as the
+//     (key desc, index asc) order does.
 // Everything is integer: the result is unique and bit-exact.
 #include "sffn_device.h"
 
@@ -70,161 +76,109 @@ __device__ __forceinline__ uint32_t key_of_bits(int key_type, uint32_t b) {
   return key_signed(__uint_as_float(b));
 }
 
-// Index-order positions of two per-entry predicates, given as bit masks
-// (bit j: entry j*NT + t).  ordered_counts stores the packed (hi half, lo
-// half) count of every (j, wave) block; after a barrier, ordered_offsets
-// gives lane j the packed count of all blocks before (j, this wave) and the
-// totals; an entry's position is then that offset (read from lane j) plus
-// the number of lower lanes in its ballot.
-template <int NT, int KPT, bool TWO>
-__device__ __forceinline__ void ordered_counts(uint32_t bits_h, uint32_t bits_l,
-                                               uint32_t (*cnt)[NT / 64]) {
-  const int lane = threadIdx.x & 63, w = wave_id();
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint64_t bh = __ballot((bits_h >> j) & 1u);
-    const uint64_t bl = TWO ? __ballot((bits_l >> j) & 1u) : 0ull;
-    if (lane == 0) cnt[j][w] = ((uint32_t)__popcll(bh) << 16) | (uint32_t)__popcll(bl);
-  }
-}
-
-template <int NT, int KPT>
-__device__ __forceinline__ uint32_t ordered_offsets(uint32_t (*cnt)[NT / 64], uint32_t& total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, w = wave_id();
-  uint32_t row_total = 0, row_below = 0;
-  if (lane < KPT) {
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const uint32_t c = cnt[lane][ww];
-      row_total += c;
-      row_below += ww < w ? c : 0u;
-    }
-  }
-  const uint32_t incl = wave_incl<false>(row_total);
-  total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  return incl - row_total + row_below;
-}
-
-template <bool TWO>
-__device__ __forceinline__ uint32_t ordered_pos(uint32_t off_j, uint32_t bits_h, uint32_t bits_l,
-                                                int j) {
-  const uint64_t bh = __ballot((bits_h >> j) & 1u);
-  if (!TWO) return off_j + (lanes_below(bh) << 16);
-  const uint64_t bl = __ballot((bits_l >> j) & 1u);
-  return off_j + ((lanes_below(bh) << 16) | lanes_below(bl));
-}
-
-// Wave 0's scan of one radix pass over nb bins (nb <= 2048, H 16-byte
-// aligned): for each bound it writes the digit holding rank `rem` (in the
-// packed counters' hi or lo half), the rank left inside that digit and the
-// digit's count.  Lane l holds q = nb/64 consecutive bins (lane 0 the
-// largest digits), read as 16-byte vectors; a DPP scan gives the counts
-// above each lane, and the lane that holds the rank walks its bins from the
-// top.
+// One radix pass's scan over nb bins (nb a power of two <= kBins), done by
+// all NT threads: thread t holds the c = max(1, nb/NT) bins [nb-(t+1)c,
+// nb-tc) (thread 0 the largest digits).  For each bound it writes the digit
+// holding rank `rem` (in the packed counters' hi or lo half), the rank left
+// inside that digit and the digit's count to out[3b..3b+2].  WT: NT/64
+// words of LDS.  Starts after the barrier that completes H; ends with a
+// barrier after which out[] is valid.
+template <int NT>
 __device__ __forceinline__ void scan_pass(const uint32_t* H, int nb, bool want_hi, uint32_t rem_hi,
-                                          bool want_lo, uint32_t rem_lo, uint32_t* out) {
-  const int lane = threadIdx.x & 63;
-  uint32_t h[32];
-  int q, base;
-  if (nb >= 256) {   // 4..32 bins per lane
-    q = nb >> 6;
-    base = nb - q * (lane + 1);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v = 4 * c < q ? *reinterpret_cast<const uint4*>(H + base + 4 * c)
-                                : make_uint4(0u, 0u, 0u, 0u);
-      h[4 * c] = v.x; h[4 * c + 1] = v.y; h[4 * c + 2] = v.z; h[4 * c + 3] = v.w;
-    }
-  } else {           // at most 4 bins per lane: one bin per lane
-    q = 1;
-    base = nb - 1 - lane;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) h[i] = 0u;
-    h[0] = base >= 0 ? H[base] : 0u;
-    if (nb > 64) {   // 128 bins: two per lane
-      q = 2;
-      base = nb - 2 * (lane + 1);
-      h[0] = H[base];
-      h[1] = H[base + 1];
-    }
-  }
-  // group sums of 4 bins, then the lane total
-  uint32_t g4[8];
+                                          bool want_lo, uint32_t rem_lo, uint32_t* WT,
+                                          uint32_t* out) {
+  constexpr int NW = NT / 64;
+  constexpr int CB = 2048 / NT;   // most bins a thread holds
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int c = nb >= NT ? nb / NT : 1;
+  const int base = nb - (t + 1) * c;
+  uint32_t h[CB];
   uint32_t own = 0;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    g4[c] = h[4 * c] + h[4 * c + 1] + h[4 * c + 2] + h[4 * c + 3];
-    own += g4[c];
+  for (int i = 0; i < CB; ++i) {
+    h[i] = (i < c && base >= 0) ? H[base + i] : 0u;
+    own += h[i];
   }
-  const uint32_t above = wave_incl<false>(own) - own;
+  const uint32_t incl = wave_incl<false>(own);
+  if (lane == 63) WT[w] = incl;
+  __syncthreads();
+  uint32_t above = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) above += ww < w ? WT[ww] : 0u;
+  above += incl - own;   // packed count of the bins above this thread's
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const bool want = b == 0 ? want_hi : want_lo;
-    if (!want) continue;
     const int half = b == 0 ? 16 : 0;
     const uint32_t rem = b == 0 ? rem_hi : rem_lo;
-    const uint32_t acc0 = (above >> half) & 0xFFFFu;
-    if (!(acc0 < rem && rem <= acc0 + ((own >> half) & 0xFFFFu))) continue;   // one lane
-    // the group of 4 bins holding the rank, then the bin (descending digits);
-    // once the rank is passed, acc >= rem and no later group can match
-    uint32_t acc = acc0, acc_at = acc0;
-    int gsel = 0;
+    const uint32_t a0 = (above >> half) & 0xFFFFu;
+    if (!(want && a0 < rem && rem <= a0 + ((own >> half) & 0xFFFFu))) continue;   // one thread
+    uint32_t acc = a0;
 #pragma unroll
-    for (int c = 7; c >= 0; --c) {
-      const uint32_t n = (g4[c] >> half) & 0xFFFFu;
-      if (acc < rem && rem <= acc + n) { gsel = c; acc_at = acc; }
-      acc += n;
-    }
-    acc = acc_at;
-    uint32_t hb[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) v = c == gsel ? h[4 * c + e] : v;
-      hb[e] = (v >> half) & 0xFFFFu;
-    }
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (acc < rem && rem <= acc + hb[e]) {
-        out[3 * b] = (uint32_t)(base + 4 * gsel + e); out[3 * b + 1] = rem - acc; out[3 * b + 2] = hb[e];
+    for (int i = CB - 1; i >= 0; --i) {
+      if (i >= c) continue;
+      const uint32_t hb = (h[i] >> half) & 0xFFFFu;
+      if (acc < rem && rem <= acc + hb) {
+        out[3 * b] = (uint32_t)(base + i); out[3 * b + 1] = rem - acc; out[3 * b + 2] = hb;
       }
-      acc += hb[e];
+      acc += hb;
     }
   }
+  __syncthreads();
+}
+
+// Sum over the waves before this one (and over all waves) of a packed
+// per-wave count that lane 0 of each wave stored in WT.  Call after the
+// barrier that follows the stores.
+template <int NW>
+__device__ __forceinline__ uint32_t waves_before(const uint32_t* WT, uint32_t& total) {
+  const int w = wave_id();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const uint32_t v = WT[ww];
+    before += ww < w ? v : 0u;
+    all += v;
+  }
+  total = all;
+  return before;
 }
 
 template <int NT, int KPT, bool LO>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr int NW = NT / 64;
   constexpr int kBins = 2048;
-  __shared__ __align__(16) uint32_t hist[3][kBins + 4];   // one per pass; bin kBins: not counted
-  __shared__ uint32_t cnt[2][KPT][NW];      // ballot counts of the two ordered scans
+  constexpr int kHist = kBins + 64;   // bins kBins + lane: sinks of pass 0, never read
+  __shared__ __align__(16) uint32_t hist[3][kHist];   // one per pass
+  __shared__ uint32_t WT[4][NW];            // per-wave words: scans, ties, list counts
   __shared__ uint32_t wsum[2][NW];          // per wave: OR of eligible keys, eligible count
   __shared__ uint32_t found[8];             // hi: digit, rem, count; lo: digit, rem, count
   __shared__ uint32_t ckey[kMaxClusters];   // cluster keys (cluster > 1)
 
   const int row = blockIdx.x;
   const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
+  const int lane = t & 63, w = wave_id();
   const size_t roff = (size_t)row * a.ld;
+  const int ebase = w * KPT * 64 + lane;   // entry of slot j: ebase + 64 j
+  const int n = a.n;
 
-  // ---- keys; every load is issued before the first use
+  // ---- keys; every load is issued before the first use (clamped addresses,
+  // no branch around a load)
   uint32_t key[KPT];
   const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.keys) + roff;
   if (a.cluster == 1) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = j * NT + t < a.n ? kp[j * NT + t] : 0u;
+    for (int j = 0; j < KPT; ++j) key[j] = kp[min(ebase + 64 * j, n - 1)];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = key_of_bits(a.key_type, key[j]);
+    for (int j = 0; j < KPT; ++j)
+      key[j] = ebase + 64 * j < n ? key_of_bits(a.key_type, key[j]) : 0u;
   } else {
     // cluster keys: coalesced reads of the n*cluster values, max per cluster
     // in LDS (the value index i belongs to cluster floor((i + 0.5) / cluster),
     // exact in fp32 for these sizes)
-    for (int c = t; c < a.n; c += NT) ckey[c] = 0u;
+    for (int c = t; c < n; c += NT) ckey[c] = 0u;
     __syncthreads();
-    const int total = a.n * a.cluster;
+    const int total = n * a.cluster;
     const float inv = 1.0f / (float)a.cluster;
     if ((a.cluster & 3) == 0 && (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.keys) & 15) == 0) {
       // 4 values of one cluster per load; 8 loads in flight per thread
@@ -259,26 +213,38 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = j * NT + t < a.n ? ckey[j * NT + t] : 0u;
+    for (int j = 0; j < KPT; ++j) key[j] = ebase + 64 * j < n ? ckey[ebase + 64 * j] : 0u;
   }
-  uint32_t elig = 0, kor = 0, ecount = 0;   // bit j: entry j*NT+t takes part
+  uint32_t incl = 0;   // bit j: entry of slot j is in include_mask (clamped reads)
+  if (a.include_mask) {
+    uint8_t incm[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) incm[j] = a.include_mask[min(ebase + 64 * j, n - 1)];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) incl |= ((ebase + 64 * j < n) & (incm[j] != 0) ? 1u : 0u) << j;
+  }
+
+  uint32_t elig = 0, kor = 0;   // bit j: entry of slot j takes part
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool e = (j * NT + t < a.n) & (!a.nonzero_only | (key[j] != 0u));
+    const bool e = (ebase + 64 * j < n) & (!a.nonzero_only | (key[j] != 0u));
     elig |= (e ? 1u : 0u) << j;
     kor |= e ? key[j] : 0u;
-    if (a.nonzero_only) ecount += (uint32_t)__popcll(__ballot(e));   // else every entry counts
   }
   kor = wave_incl<true>(kor);
+  const uint32_t ecount = wave_incl<false>((uint32_t)__popc(elig));   // lane 63: the wave's count
   if (lane == 63) { wsum[0][w] = kor; wsum[1][w] = ecount; }
-  // the first pass's histogram now; the later passes' ones while wave 0 scans the first
-  for (int i = t; i < kBins + 4; i += NT) hist[0][i] = 0u;
+  // all three histograms (the sinks are never read)
+  {
+    uint4* hz = reinterpret_cast<uint4*>(&hist[0][0]);
+    for (int i = t; i < 3 * kHist / 4; i += NT) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   __syncthreads();
 
   uint32_t all_or = 0, E = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) { all_or |= wsum[0][i]; E += wsum[1][i]; }
-  if (!a.nonzero_only) E = (uint32_t)a.n;
+  if (!a.nonzero_only) E = (uint32_t)n;
   const uint32_t rhi = min((uint32_t)a.r_hi, E);
   const uint32_t rlo = LO ? min((uint32_t)a.r_lo, rhi) : 0u;
   // all_hi / all_lo: the bound covers every eligible entry (no search)
@@ -301,123 +267,167 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       if (pass == 0) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-          const uint32_t bin = ((elig >> j) & 1u) ? (key[j] >> shift) & mask : (uint32_t)kBins;
+          const uint32_t bin = ((elig >> j) & 1u) ? (key[j] >> shift) & mask : (uint32_t)(kBins + lane);
           atomicAdd(&H[bin], 0x10001u);
         }
       } else {
+        // only keys whose decided digits match a bound's count; a bound that
+        // is not searched compares against a value no shifted key reaches
+        const uint32_t ph = need_hi ? pre_hi >> lo_bit : 0xFFFFFFFFu;
+        const uint32_t pl = need_lo ? pre_lo >> lo_bit : 0xFFFFFFFFu;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
           const uint32_t k = key[j];
-          const bool e = (elig >> j) & 1u;
-          const bool mh = e && need_hi && (k >> lo_bit) == (pre_hi >> lo_bit);
-          const bool ml = e && need_lo && (k >> lo_bit) == (pre_lo >> lo_bit);
-          const uint32_t inc = (mh ? 0x10000u : 0u) + (ml ? 1u : 0u);
+          const uint32_t inc = ((k >> lo_bit) == ph ? 0x10000u : 0u) + ((k >> lo_bit) == pl ? 1u : 0u);
           if (inc) atomicAdd(&H[(k >> shift) & mask], inc);
         }
       }
       __syncthreads();
-      if (w == 0) {
-        scan_pass(H, 1 << width, need_hi, rem_hi, need_lo, rem_lo, found);
-      } else if (pass == 0) {
-        for (int i = t - 64; i < 2 * (kBins + 4); i += NT - 64) (&hist[1][0])[i] = 0u;
-      }
-      __syncthreads();
-      // found[] is written again only after the next pass's histogram
-      // barrier, which every thread reaches after these reads
+      scan_pass<NT>(H, 1 << width, need_hi, rem_hi, need_lo, rem_lo, WT[0], found);
+      // found[] is written again only after the next pass's first barrier
+      // inside scan_pass, which every thread reaches after these reads
       if (need_hi) { pre_hi |= found[0] << shift; rem_hi = found[1]; tie_hi = found[2]; }
       if (need_lo) { pre_lo |= found[3] << shift; rem_lo = found[4]; tie_lo = found[5]; }
+      if (pass == 0 && shift > 0) {
+        // Entries that take no part get a key whose first digit is neither
+        // bound's (the first digit has 11 bits when more passes follow), so
+        // the later passes need no eligibility test.
+        const uint32_t dh = need_hi ? pre_hi >> shift : 0xFFFFFFFFu;
+        const uint32_t dl = need_lo ? pre_lo >> shift : 0xFFFFFFFFu;
+        const uint32_t d = (dh != 0u && dl != 0u) ? 0u : (dh != 1u && dl != 1u) ? 1u : 2u;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = ((elig >> j) & 1u) ? key[j] : d << shift;
+      }
       lo_bit = shift;
     }
   }
 
-  // ---- ties: rank the entries equal to T_r only when the bound splits them
+  // ---- membership of the two rank ranges (before eligibility): bit j of
+  // hib / lob: the entry of slot j is among the top r_hi / top r_lo.  When a
+  // bound splits the entries equal to T_r, those are ranked in index order.
   const bool split_hi = need_hi && tie_hi > rem_hi;
   const bool split_lo = need_lo && tie_lo > rem_lo;
-  uint32_t eq_h = 0, eq_l = 0, eq_off = 0;
-  if (split_hi || split_lo) {
+  const uint32_t th_hi = all_hi ? 0u : pre_hi;   // no split: every tied entry is inside
+  const uint32_t th_lo = all_lo ? 0u : pre_lo;
+  uint32_t hib = 0, lob = 0;
+  if (!(split_hi || split_lo)) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool e = (elig >> j) & 1u;
-      eq_h |= ((e && split_hi && key[j] == pre_hi) ? 1u : 0u) << j;
-      eq_l |= ((e && split_lo && key[j] == pre_lo) ? 1u : 0u) << j;
+      hib |= (key[j] >= th_hi ? 1u : 0u) << j;
+      if (LO) lob |= (key[j] >= th_lo ? 1u : 0u) << j;
     }
-    ordered_counts<NT, KPT, LO>(eq_h, eq_l, cnt[0]);
+  } else {
+    uint32_t eq_h = 0, eq_l = 0;   // bit j: eligible and equal to a split T_r
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      eq_h |= (split_hi && key[j] == pre_hi ? 1u : 0u) << j;
+      eq_l |= (split_lo && key[j] == pre_lo ? 1u : 0u) << j;
+    }
+    eq_h &= elig;
+    eq_l &= elig;
+    const uint32_t wc = wave_incl<false>(((uint32_t)__popc(eq_h) << 16) + (uint32_t)__popc(eq_l));
+    if (lane == 63) WT[1][w] = wc;
     __syncthreads();
     uint32_t dummy;
-    eq_off = ordered_offsets<NT, KPT>(cnt[0], dummy);
-  }
-
-  uint32_t sel = 0, top = 0;   // bit j: entry j*NT+t is selected / in the top list
+    uint32_t eq_run = waves_before<NW>(WT[1], dummy);   // equal entries in earlier waves
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int n = j * NT + t;
-    const uint32_t k = key[j];
-    const bool e = (elig >> j) & 1u;
-    uint32_t eqpos = 0;
-    if (split_hi || split_lo)
-      eqpos = ordered_pos<LO>((uint32_t)__builtin_amdgcn_readlane((int)eq_off, j), eq_h, eq_l, j);
-    const bool gt_hi = (k > pre_hi) | ((k == pre_hi) & ((eqpos >> 16) < rem_hi));
-    const bool gt_lo = (k > pre_lo) | ((k == pre_lo) & ((eqpos & 0xFFFFu) < rem_lo));
-    const bool in_hi = e & (all_hi | (need_hi & gt_hi));
-    const bool in_lo = e & (all_lo | (need_lo & gt_lo));
-    bool s = in_hi & !in_lo;
-    if (a.include_mask && n < a.n) s |= a.include_mask[n] != 0;
-    sel |= (s ? 1u : 0u) << j;
-    top |= (in_lo ? 1u : 0u) << j;
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t k = key[j];
+      const uint64_t bh = __ballot((eq_h >> j) & 1u);
+      const uint64_t bl = __ballot((eq_l >> j) & 1u);
+      const uint32_t pos = eq_run + ((lanes_below(bh) << 16) | lanes_below(bl));
+      eq_run += ((uint32_t)__popcll(bh) << 16) + (uint32_t)__popcll(bl);
+      const bool gh = split_hi ? (k > pre_hi) | ((k == pre_hi) & ((pos >> 16) < rem_hi)) : k >= th_hi;
+      const bool gl = split_lo ? (k > pre_lo) | ((k == pre_lo) & ((pos & 0xFFFFu) < rem_lo)) : k >= th_lo;
+      hib |= (gh ? 1u : 0u) << j;
+      if (LO) lob |= (gl ? 1u : 0u) << j;
+    }
   }
+  hib = rhi > 0 ? hib & elig : 0u;
+  lob = LO && rlo > 0 ? lob & elig : 0u;
+  const uint32_t sel = (hib & ~lob) | incl;   // bit j: selected
+  const uint32_t top = lob;                   // bit j: in the top list
 
-  // one ordered scan for both lists: selected in the high half, top list in the low
-  ordered_counts<NT, KPT, LO>(sel, top, cnt[1]);
+  // ---- per-wave counts (selected: hi half, top list: lo half), then the
+  // counts of the waves before
+  {
+    const uint32_t wc = wave_incl<false>(((uint32_t)__popc(sel) << 16) + (uint32_t)__popc(top));
+    if (lane == 63) WT[2][w] = wc;
+  }
   __syncthreads();
   uint32_t total;
-  const uint32_t off = ordered_offsets<NT, KPT>(cnt[1], total);
+  uint32_t run = waves_before<NW>(WT[2], total);
+
+  // ---- stores; index lists: positions in index order, contiguous within
+  // each ballot
+  int eb = ebase;
+  asm volatile("" : "+v"(eb));   // bounds tests made again here, not kept live since the loads
+  int32_t* irow = a.idx_out ? a.idx_out + (size_t)row * a.ld_idx : nullptr;
+  int32_t* trow = (LO && a.idx_top_out) ? a.idx_top_out + (size_t)row * a.ld_idx_top : nullptr;
+  if (irow || trow) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int n = j * NT + t;
-    const uint32_t pos = ordered_pos<LO>((uint32_t)__builtin_amdgcn_readlane((int)off, j), sel, top, j);
-    const bool s = (sel >> j) & 1u;
-    if (n < a.n) {
-      if (a.mask_out) a.mask_out[(size_t)row * a.ld_mask + n] = s ? 1 : 0;
-      if (s) {
-        if (a.idx_out) a.idx_out[(size_t)row * a.ld_idx + (pos >> 16)] = n;
-        if (a.freq) atomicAdd(&a.freq[n], 1u);
-      }
-      if (((top >> j) & 1u) && a.idx_top_out)
-        a.idx_top_out[(size_t)row * a.ld_idx_top + (pos & 0xFFFFu)] = n;
+    for (int j = 0; j < KPT; ++j) {
+      const int e = eb + 64 * j;
+      const bool sj = (sel >> j) & 1u;
+      const bool tj = LO && ((top >> j) & 1u);
+      const uint64_t bs = __ballot(sj);
+      const uint64_t bt = LO ? __ballot(tj) : 0ull;
+      const uint32_t ps = (run >> 16) + lanes_below(bs);
+      const uint32_t pt = (run & 0xFFFFu) + lanes_below(bt);
+      run += ((uint32_t)__popcll(bs) << 16) + (uint32_t)__popcll(bt);
+      if (irow && sj) irow[ps] = e;
+      if (trow && tj) trow[pt] = e;
     }
+  }
+  if (a.mask_out) {
+    uint8_t* mrow = a.mask_out + (size_t)row * a.ld_mask;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int e = eb + 64 * j;
+      if (e < n) mrow[e] = (uint8_t)((sel >> j) & 1u);
+    }
+  }
+  if (a.freq) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if ((sel >> j) & 1u) atomicAdd(&a.freq[eb + 64 * j], 1u);
   }
   if (t == 0 && a.count_out) a.count_out[row] = (int32_t)(total >> 16);
   if (t == 0 && a.count_top_out) a.count_top_out[row] = (int32_t)(total & 0xFFFFu);
 }
 
-template <int NT, bool LO>
-static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
-  const int need = (a.n + NT - 1) / NT;
-  dim3 grid(a.rows), block(NT);
-  if (need <= 1) hipLaunchKernelGGL((select_kernel<NT, 1, LO>), grid, block, 0, s, a);
-  else if (need <= 2) hipLaunchKernelGGL((select_kernel<NT, 2, LO>), grid, block, 0, s, a);
-  else if (need <= 4) hipLaunchKernelGGL((select_kernel<NT, 4, LO>), grid, block, 0, s, a);
-  else if (need <= 8) hipLaunchKernelGGL((select_kernel<NT, 8, LO>), grid, block, 0, s, a);
-  else if (need <= 16) hipLaunchKernelGGL((select_kernel<NT, 16, LO>), grid, block, 0, s, a);
-  else if (need <= 20) hipLaunchKernelGGL((select_kernel<NT, 20, LO>), grid, block, 0, s, a);
-  else if (need <= 24) hipLaunchKernelGGL((select_kernel<NT, 24, LO>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((select_kernel<NT, 32, LO>), grid, block, 0, s, a);
-  return hipGetLastError();
-}
+template <int NT, bool LO, int... K>
+struct SelectLaunch;
 
-// Ranges that start at rank 0 (no lower bound, no second list) take the
-// variant that carries one ballot per entry instead of two.
-template <int NT>
-static hipError_t launch_nt(const SelectArgs& a, hipStream_t s) {
-  return a.r_lo > 0 ? launch_nt<NT, true>(a, s) : launch_nt<NT, false>(a, s);
+template <int NT, bool LO, int K0, int... K>
+struct SelectLaunch<NT, LO, K0, K...> {
+  static hipError_t go(const SelectArgs& a, hipStream_t s) {
+    if (sizeof...(K) == 0 || a.n <= NT * K0) {
+      hipLaunchKernelGGL((select_kernel<NT, K0, LO>), dim3(a.rows), dim3(NT), 0, s, a);
+      return hipGetLastError();
+    }
+    return SelectLaunch<NT, LO, K...>::go(a, s);
+  }
+};
+template <int NT, bool LO>
+struct SelectLaunch<NT, LO> {
+  static hipError_t go(const SelectArgs&, hipStream_t) { return hipErrorInvalidValue; }
+};
+
+// Entries per lane: the smallest listed count that covers the row, so few
+// slots are dead.  Ranges that start at rank 0 (no lower bound, no second
+// list) take the variant with one list.
+template <bool LO>
+static hipError_t launch_lo(const SelectArgs& a, hipStream_t s) {
+  // Small rows take 256 threads (cheaper barriers); from 1024 entries on,
+  // 1024 threads (up to 32 entries each) spread the work over 16 waves.
+  // Cluster mode reads n*cluster values: 1024 threads keep more loads in flight.
+  if (a.n <= 1024 && (long)a.n * a.cluster <= 1024) return SelectLaunch<256, LO, 1, 2, 4>::go(a, s);
+  return SelectLaunch<1024, LO, 1, 2, 4, 6, 8, 10, 12, 14, 16, 18, 20, 24, 28, 32>::go(a, s);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  // Small rows take 256 threads (cheaper barriers); from 1024 entries on,
-  // 1024 threads (up to 32 entries each) spread the histogram atomics.
-  // Cluster mode reads n*cluster values: 1024 threads keep more loads in flight.
-  if (a.n <= 1024 && (long)a.n * a.cluster <= 1024) return launch_nt<256>(a, s);
-  return launch_nt<1024>(a, s);
+  return a.r_lo > 0 ? launch_lo<true>(a, s) : launch_lo<false>(a, s);
 }
 
 }  // namespace sffn
