@@ -15,6 +15,8 @@
 // x_j * What[j][o] = (x_j scale_js) q_jo + x_j zero_js, where the second term
 // is the same for all outputs of the segment and is summed once per lane.
 // Partials are summed in chunk order by the shared split-K reduction.
+#include <algorithm>
+
 #include <hip/hip_fp16.h>
 
 #include "sffn_splitk.h"
@@ -142,18 +144,25 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
 
 hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   const int col_tiles = (a.d_out + kTileCols - 1) / kTileCols;
-  // about four top rows / eight middle rows per wave (equal bytes in flight
-  // per lane), scaled up together until ~256 workgroups stream
-  long ks_top = a.k_top_max > 0 ? (a.k_top_max + 4 * kWaves - 1) / (4 * kWaves) : 0;
-  long ks_mid = a.k_mid_max > 0 ? (a.k_mid_max + 8 * kWaves - 1) / (8 * kWaves) : 0;
-  for (int grow = 0; grow < 8 && (ks_top + ks_mid) * col_tiles < 256; ++grow) {
-    if (ks_top > 0) ks_top = min(2 * ks_top, ((long)a.k_top_max + kWaves - 1) / kWaves);
-    if (ks_mid > 0) ks_mid = min(2 * ks_mid, ((long)a.k_mid_max + kWaves - 1) / kWaves);
+  // One round of workgroups, one per CU (a second partial round costs more
+  // than it adds).  The chunk slots are split between the tiers by row
+  // count, top rows weighted 1.3: measured on MI355X, a middle-tier row
+  // (4-bit codes decoded in registers) takes about as long as a top-tier row
+  // although it is a quarter of the bytes.  A chunk keeps at least one row
+  // per wave.
+  const long slots = std::max(1, 256 / col_tiles);
+  const long kt = std::max(0, a.k_top_max), km = std::max(0, a.k_mid_max);
+  long ks_top = 0, ks_mid = 0;
+  if (kt + km > 0) {
+    const double wt = 1.3 * (double)kt, wm = (double)km;
+    ks_top = kt > 0 ? std::max(1L, (long)(slots * wt / (wt + wm) + 0.5)) : 0;
+    if (km > 0 && ks_top >= slots) ks_top = std::max(1L, slots - 1);
+    ks_mid = km > 0 ? std::max(1L, slots - ks_top) : 0;
+    ks_top = std::min(ks_top, (kt + kWaves - 1) / kWaves);
+    ks_mid = std::min(ks_mid, (km + kWaves - 1) / kWaves);
   }
-  while (ks_top + ks_mid > kMaxSplit) {
-    if (ks_top > 1) ks_top = (ks_top + 1) / 2;
-    if (ks_mid > 1) ks_mid = (ks_mid + 1) / 2;
-  }
+  ks_top = std::min<long>(ks_top, kMaxSplit / 2);
+  ks_mid = std::min<long>(ks_mid, kMaxSplit / 2);
   if (ks_top + ks_mid == 0) ks_mid = 1;   // nothing to read: one chunk writes y
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
   hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0, s,
