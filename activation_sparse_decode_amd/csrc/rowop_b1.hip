@@ -3,21 +3,23 @@
 // out_n = f(W0[n].x, W1[n].x) for the processed rows n, with the magnitude
 // key bits(|out_n|) written alongside (the ranking input of the selection
 // step; SelectInfer §3 records |a| at the input of down_proj).  The same
-// kernel runs the down projection of a compacted neuron set (plain dot of
+// kernels run the down projection of a compacted neuron set (plain dot of
 // each output row with the compacted activations, added to the residual).
+// Skipped neurons are never read.  The optional RMSNorm of x scales the
+// reduced dot products (W.(x s) = s (W.x)).
 //
-// Layout and mapping: W rows are contiguous bf16.  A workgroup spans one
-// row: thread t owns the 16-byte chunks t, t+TPB, ... (CPT of them) of every
-// row, so one wave instruction reads 1 KiB of a row, fully coalesced, and
-// the thread keeps the matching 8*CPT entries of x in registers for its
-// whole life.  Each iteration streams NPI rows (both matrices for the GLU),
-// i.e. NPI*CPT (x2) independent 16-byte nontemporal loads per thread, which
-// is the shape a plain streaming read needs on this GPU to approach the HBM
-// rate: many workgroups with a few loads in flight each; the next group's
-// loads are issued before the current group is reduced.  Per-row
-// partial sums are reduced across the wave with shuffles and across the
-// workgroup's waves in LDS.  Skipped neurons are never read.  The optional
-// RMSNorm of x scales the reduced dot products (W.(x s) = s (W.x)).
+// Rows up to 5120 wide (every shape of the workloads here) take the
+// wave-per-row kernel: a wave owns whole rows, lane l the 16-byte chunks l,
+// l+64, ... (NCH of them) of each, so one wave instruction reads 1 KiB of a
+// row and the lane keeps the matching 8*NCH entries of x in registers.  A
+// row's loads (both matrices for the GLU) are issued together, the dot
+// product is reduced across the wave with DPP moves only, and lane 0 writes
+// the result: no LDS, no barrier.  Measured on MI355X against the
+// workgroup-per-row kernel below: 5-12% faster on every workload shape
+// (e.g. 12.2 vs 13.9 us for 8192 SwiGLU neurons of 2048, 54 vs 60 us for
+// 17408 of 5120).  Wider rows take the workgroup-per-row kernel: a
+// workgroup spans one row, thread t owns chunks t, t+TPB, ... and the waves'
+// partial sums meet in LDS.
 #include "sffn_device.h"
 
 namespace sffn {
@@ -30,6 +32,168 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// ------------------------------------------------------------ wave per row
+
+constexpr int kWaveMaxChunks = 10;   // 16-byte chunks per lane: rows up to 5120 wide
+
+// Wave gw of W handles the items gw + W*k, k < its (<= 64, guaranteed by the
+// launch).  Lane k fetches the row of item k (and, when used, the value it
+// adds to and its gate) once; the item loop reads them back with readlane.
+// Every load is unconditional: chunks past the row end re-read chunk 0
+// against x = 0.
+template <int OP, int NCH>
+__global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
+  constexpr bool kUse0 = OP != kOpGated;
+  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * (int)(blockDim.x >> 6) + wave_id();
+  const int W = gridDim.x * (int)(blockDim.x >> 6);
+  const int nchunk = a.d >> 3;
+
+  int n_items;
+  if (a.idx) {
+    int c = *a.count;
+    c = c < a.k_max ? c : a.k_max;
+    n_items = (c > 0 ? c : 0) * a.group;
+  } else {
+    n_items = a.n_rows;
+  }
+  if (gw >= n_items) return;
+  const int its = (n_items - gw + W - 1) / W;
+
+  int lane_row;
+  {
+    const int it = gw + W * (lane < its ? lane : 0);
+    if (a.idx) {
+      const int q = it / a.group;
+      lane_row = a.idx[q] * a.group + (it - q * a.group);
+    } else {
+      lane_row = it;
+    }
+  }
+  float lane_pv, lane_av = 0.f;
+  {
+    const float* pp = a.accumulate ? a.out + lane_row : a.x;
+    lane_pv = *pp;
+    if (OP == kOpGated) lane_av = a.aux[lane_row];
+  }
+
+  // x is requested first but consumed only after the first row's weights
+  // are requested: x is usually the previous kernel's output, so waiting
+  // for it before the weight loads would add a round trip to every wave.
+  int coff[NCH];
+  float xm[NCH];
+  float4 xp[NCH], xq[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    coff[j] = c < nchunk ? 8 * c : 0;
+    xm[j] = c < nchunk ? 1.f : 0.f;
+    xp[j] = *reinterpret_cast<const float4*>(a.x + coff[j]);
+    xq[j] = *reinterpret_cast<const float4*>(a.x + coff[j] + 4);
+  }
+  float xr[NCH][8];
+  float inv = 1.f, tau = 0.f;
+
+  for (int k = 0; k < its; ++k) {
+    const int r = __builtin_amdgcn_readlane(lane_row, k);
+    const size_t base = (size_t)r * a.ld_w;
+    uint4 v0[NCH], v1[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (kUse0) v0[j] = load_stream(a.W0 + base + coff[j]);
+      if (kUse1) v1[j] = load_stream(a.W1 + base + coff[j]);
+    }
+    if (k == 0) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        xr[j][0] = xp[j].x * xm[j]; xr[j][1] = xp[j].y * xm[j];
+        xr[j][2] = xp[j].z * xm[j]; xr[j][3] = xp[j].w * xm[j];
+        xr[j][4] = xq[j].x * xm[j]; xr[j][5] = xq[j].y * xm[j];
+        xr[j][6] = xq[j].z * xm[j]; xr[j][7] = xq[j].w * xm[j];
+      }
+      if (OP == kOpDotRelu || a.rms_eps > 0.f) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf(xr[j][e], xr[j][e], ss);
+        ss = wave_sum(ss);
+        if (a.rms_eps > 0.f) inv = 1.f / sqrtf(ss / (float)a.d + a.rms_eps);
+        tau = a.tau_scale * sqrtf(ss) * inv;   // ||x s|| for the ReLU threshold
+      }
+    }
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      float f[8];
+      if (kUse0) {
+        unpack8(v0[j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s0 = fmaf(f[e], xr[j][e], s0);
+      }
+      if (kUse1) {
+        unpack8(v1[j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s1 = fmaf(f[e], xr[j][e], s1);
+      }
+    }
+    if (kUse0) s0 = wave_sum(s0);
+    if (kUse1) s1 = wave_sum(s1);
+    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_pv), k));
+    const float av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_av), k));
+    if (lane == 0) {
+      const float g = s0 * inv, u = s1 * inv;
+      float v;
+      if (OP == kOpGlu) {
+        v = (g / (1.f + expf(-g))) * u;
+      } else if (OP == kOpDotRelu) {
+        v = fmaxf(g - tau, 0.f);
+      } else if (OP == kOpGated) {
+        v = av * u;
+      } else {
+        v = g;
+      }
+      if (a.accumulate) v += pv;
+      a.out[r] = v;
+      if (a.key_out) a.key_out[r] = key_abs(v);
+    }
+  }
+}
+
+template <int OP, int NCH>
+static hipError_t launch_wave(const RowOpArgs& a, hipStream_t s) {
+  // Workgroups of four waves, a multiple of 256 of them (the same number on
+  // every CU): 256 up to ~3000 rows, doubling per doubling of the rows up to
+  // 2048; at most 64 rows per wave.
+  const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
+  long blocks = 256;
+  while (blocks < 2048 && items >= 6 * blocks * 2) blocks *= 2;
+  if (blocks * 4 > items) blocks = (items + 3) / 4;
+  if (blocks * 4 * 64 < items) blocks = (items + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((rowop_wave_kernel<OP, NCH>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int OP>
+static hipError_t launch_wave_op(const RowOpArgs& a, hipStream_t s) {
+  switch ((a.d / 8 + 63) / 64) {
+    case 0:
+    case 1: return launch_wave<OP, 1>(a, s);
+    case 2: return launch_wave<OP, 2>(a, s);
+    case 3: return launch_wave<OP, 3>(a, s);
+    case 4: return launch_wave<OP, 4>(a, s);
+    case 5: return launch_wave<OP, 5>(a, s);
+    case 6: return launch_wave<OP, 6>(a, s);
+    case 7:
+    case 8: return launch_wave<OP, 8>(a, s);
+    default: return launch_wave<OP, kWaveMaxChunks>(a, s);
+  }
+}
+
+// ------------------------------------------------------------ workgroup per row
 
 template <int OP, int CPT, int NPI>
 __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
@@ -246,12 +410,12 @@ static hipError_t launch_cfg(const RowOpArgs& a, hipStream_t s, long cap) {
 
 template <int OP>
 static hipError_t launch_op(const RowOpArgs& a, hipStream_t s) {
+  const int nchunk = a.d >> 3;
+  if (nchunk <= 64 * kWaveMaxChunks) return launch_wave_op<OP>(a, s);
   // Measured on MI355X at the 28-layer stack shapes: two 16-byte chunks per
   // thread per row (128-320-thread workgroups), one row (GLU: one neuron)
   // per iteration, at most 1024 (GLU) / 2048 (single matrix) workgroups.
   const long cap = OP == kOpGlu ? 1024 : 2048;
-  const int nchunk = a.d >> 3;
-  if (nchunk < 128) return launch_cfg<OP, 1, 1>(a, s, cap);
   return launch_cfg<OP, 2, 1>(a, s, cap);    // nchunk <= 1024 (d <= 8192)
 }
 
