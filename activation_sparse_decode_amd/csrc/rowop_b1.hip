@@ -80,8 +80,12 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
   }
 
   // x is requested first but consumed only after the first row's weights
-  // are requested: x is usually the previous kernel's output, so waiting
-  // for it before the weight loads would add a round trip to every wave.
+  // are requested (x is usually the previous kernel's output, so waiting for
+  // it first would add a round trip to every wave); the empty asm (a
+  // compiler barrier that also redefines `zero`) keeps the conversion of x
+  // and the norm from moving ahead of those loads.  The loop is rotated:
+  // reduce and store row k, then request row k+1, so each row's FMAs start
+  // a block and consume its loads in arrival order.
   int coff[NCH];
   float xm[NCH];
   float4 xp[NCH], xq[NCH];
@@ -93,37 +97,44 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     xp[j] = *reinterpret_cast<const float4*>(a.x + coff[j]);
     xq[j] = *reinterpret_cast<const float4*>(a.x + coff[j] + 4);
   }
-  float xr[NCH][8];
-  float inv = 1.f, tau = 0.f;
-
-  for (int k = 0; k < its; ++k) {
-    const int r = __builtin_amdgcn_readlane(lane_row, k);
+  uint4 v0[NCH], v1[NCH];
+  auto fetch = [&](int r) {
     const size_t base = (size_t)r * a.ld_w;
-    uint4 v0[NCH], v1[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       if (kUse0) v0[j] = load_stream(a.W0 + base + coff[j]);
       if (kUse1) v1[j] = load_stream(a.W1 + base + coff[j]);
     }
-    if (k == 0) {
+  };
+  auto row_of = [&](int k) { return a.idx ? __builtin_amdgcn_readlane(lane_row, k) : gw + W * k; };
+  int r = row_of(0);
+  fetch(r);
+
+  int zero = 0;
+  asm volatile("" : "+v"(zero) : : "memory");
+  const float zf = (float)zero;
+  float xr[NCH][8];
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        xr[j][0] = xp[j].x * xm[j]; xr[j][1] = xp[j].y * xm[j];
-        xr[j][2] = xp[j].z * xm[j]; xr[j][3] = xp[j].w * xm[j];
-        xr[j][4] = xq[j].x * xm[j]; xr[j][5] = xq[j].y * xm[j];
-        xr[j][6] = xq[j].z * xm[j]; xr[j][7] = xq[j].w * xm[j];
-      }
-      if (OP == kOpDotRelu || a.rms_eps > 0.f) {
-        float ss = 0.f;
+  for (int j = 0; j < NCH; ++j) {
+    const float m = xm[j] + zf;
+    xr[j][0] = xp[j].x * m; xr[j][1] = xp[j].y * m;
+    xr[j][2] = xp[j].z * m; xr[j][3] = xp[j].w * m;
+    xr[j][4] = xq[j].x * m; xr[j][5] = xq[j].y * m;
+    xr[j][6] = xq[j].z * m; xr[j][7] = xq[j].w * m;
+  }
+  float inv = 1.f, tau = 0.f;
+  if (OP == kOpDotRelu || a.rms_eps > 0.f) {
+    float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j)
+    for (int j = 0; j < NCH; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(xr[j][e], xr[j][e], ss);
-        ss = wave_sum(ss);
-        if (a.rms_eps > 0.f) inv = 1.f / sqrtf(ss / (float)a.d + a.rms_eps);
-        tau = a.tau_scale * sqrtf(ss) * inv;   // ||x s|| for the ReLU threshold
-      }
-    }
+      for (int e = 0; e < 8; ++e) ss = fmaf(xr[j][e], xr[j][e], ss);
+    ss = wave_sum(ss);
+    if (a.rms_eps > 0.f) inv = 1.f / sqrtf(ss / (float)a.d + a.rms_eps);
+    tau = a.tau_scale * sqrtf(ss) * inv;   // ||x s|| for the ReLU threshold
+  }
+
+  for (int k = 0;;) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -159,6 +170,9 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
       a.out[r] = v;
       if (a.key_out) a.key_out[r] = key_abs(v);
     }
+    if (++k >= its) break;
+    r = row_of(k);
+    fetch(r);
   }
 }
 
