@@ -252,7 +252,7 @@ def run_c1(args, torch, B, synth, P, T):
                   step_GBps=round(step_bytes / (us_tok * 1e-6) / 1e9, 1),
                   step_frac_of_peak=round(step_bytes / (us_tok * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                   setup={"calibrate_ms": round(calib_ms, 2), "prefill_ms": round(prefill_ms, 2)},
-                  roofline=roofline("rowop_b1_kernel<GLU> (gate/up over the compacted union)",
+                  roofline=roofline("rowop_wave_kernel<GLU> (gate/up over the compacted union)",
                                     glu_total / L, glu_us,
                                     measured_traffic("rowop_glu_selectinfer_decode",
                                                      ["rowop_b1.hip", "sffn_device.h"])),
@@ -326,7 +326,7 @@ def run_c0(args, torch, B, synth, P, T):
                   kernels_us={"gate_up_dense": round(glu_us, 3), "select": round(sel_us, 3),
                               "gathered_down": round(down_us, 3)},
                   gathered_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_b1_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us),
+                  roofline=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us),
                   cpu_baseline=cpu)
 
 
@@ -494,7 +494,7 @@ def run_c3(args, torch, B, synth, P, T):
               "active_cluster_frac": round(float(counts.mean() / (N // S)), 4)}
     return result(us_tok, "us/token", steps, 2, total_ms / steps, config, step_bytes=step_b,
                   step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_b1_kernel<DOT_RELU> (dense expert gate)", gate_b,
+                  roofline=roofline("rowop_wave_kernel<DOT_RELU> (dense expert gate)", gate_b,
                                     gate_us),
                   cpu_baseline=cpu)
 
