@@ -543,8 +543,10 @@ def run_c4(args, torch, B, synth, P, T):
     glu_b = 2 * N * d * 2 + batch * (4 * d + 8 * N)
     down_b = int(u * d * 2 + 4 * u + batch * (5 * u + 4 * d))
     step_b = int(glu_b + down_b + batch * 5 * N)
-    log(f"c4 batch {batch}: {us_batch:.2f} us/batch, union {u:.0f}; MFMA gate/up {glu_us:.2f} us, "
-        f"MFMA union down {down_us:.2f} us")
+    # at batch 1 the same calls run the wave-per-row kernel and the split-K gathered product
+    k_glu, k_down = ("gate_up_mfma", "union_down_mfma") if batch > 1 else ("gate_up_rows", "union_down_splitk")
+    log(f"c4 batch {batch}: {us_batch:.2f} us/batch, union {u:.0f}; {k_glu} {glu_us:.2f} us, "
+        f"{k_down} {down_us:.2f} us")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -561,10 +563,10 @@ def run_c4(args, torch, B, synth, P, T):
     return result(us_batch / batch, "us/token", args.steps * copies, 2, total_ms / args.steps,
                   config, us_per_batch=round(us_batch, 3), step_bytes=step_b,
                   step_GBps=round(step_b / (us_batch * 1e-6) / 1e9, 1),
-                  kernels_us={"gate_up_mfma": round(glu_us, 3),
-                              "union_down_mfma": round(down_us, 3)},
+                  kernels_us={k_glu: round(glu_us, 3), k_down: round(down_us, 3)},
                   union_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_mfma_kernel<GLU> (batched gate/up)", glu_b, glu_us),
+                  roofline=roofline("rowop_mfma_kernel<GLU> (batched gate/up)" if batch > 1 else
+                                    "rowop_wave_kernel<GLU> (gate/up, batch 1)", glu_b, glu_us),
                   cpu_baseline=cpu)
 
 
