@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_gemv.restype = _i
         L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
                                       _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
+        L.sparse_ffn_gemv_lists.restype = _i
+        L.sparse_ffn_gemv_lists.argtypes = [_i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp,
+                                            _vp, _i, _vp, _sz, _vp]
         L.sparse_ffn_compact.restype = _i
         L.sparse_ffn_compact.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp]
         L.sparse_ffn_encode_tiers.restype = _i
@@ -65,7 +68,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 4:
+        if L.sffn_abi_version() != 5:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -152,6 +155,23 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
         op, _p(W0), _p(W1), n_rows, d, ld_w, _p(inp), batch, ld_in, _p(idx), _p(count),
         k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), float(rms_eps), _p(aux),
         _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
+        _p(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_ffn_gemv_lists(Ws, ins, idxs, counts, k_maxs, out: torch.Tensor, *, group: int = 1,
+                          alphas=None, accumulate: bool = False,
+                          workspace: torch.Tensor | None = None, stream=None) -> None:
+    """One gathered product over several row lists into ``out`` (batch 1):
+    list l reads rows of ``Ws[l]`` picked by ``idxs[l]`` / ``counts[l]``,
+    weighted by ``ins[l]`` and the device scalar ``alphas[l]`` (or 1)."""
+    n = len(Ws)
+    ptrs = lambda ts: (_vp * n)(*[None if t is None else t.data_ptr() for t in ts])  # noqa: E731
+    ints = lambda vs: (_i * n)(*[int(v) for v in vs])  # noqa: E731
+    d, ld_w = Ws[0].shape[1], Ws[0].stride(0)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().sparse_ffn_gemv_lists(
+        n, ptrs(Ws), ints([w.shape[0] for w in Ws]), d, ld_w, ptrs(ins), ptrs(idxs), ptrs(counts),
+        ints(k_maxs), group, None if alphas is None else ptrs(alphas), _p(out), int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
 
 

@@ -208,6 +208,53 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                   "gemv launch");
 }
 
+sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const int* n_rows,
+                                  int d, int ld_w, const float* const* in,
+                                  const int32_t* const* idx, const int32_t* const* count,
+                                  const int* k_max, int group, const float* const* alpha,
+                                  float* out, int accumulate, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  REQUIRE(n_lists >= 1 && n_lists <= sffn::kMaxLists, SFFN_EINVAL,
+          "gemv_lists: n_lists=%d must be in [1, %d]", n_lists, sffn::kMaxLists);
+  REQUIRE(W && n_rows && in && idx && count && k_max, SFFN_EINVAL,
+          "gemv_lists: W, n_rows, in, idx, count and k_max (host arrays) must be non-null");
+  REQUIRE(out && aligned(out, 16), SFFN_EINVAL, "gemv_lists: out must be non-null, 16-byte aligned");
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "gemv_lists: d=%d must be a positive multiple of 8", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL,
+          "gemv_lists: ld_w=%d must be >= d and a multiple of 8", ld_w);
+  REQUIRE(group >= 1, SFFN_EINVAL, "gemv_lists: group=%d must be >= 1", group);
+  sffn::AxpyListsArgs a{};
+  long items = 0;
+  for (int l = 0; l < n_lists; ++l) {
+    REQUIRE(W[l] && aligned(W[l], 16), SFFN_EINVAL,
+            "gemv_lists: W[%d] must be non-null and 16-byte aligned", l);
+    REQUIRE(in[l] && aligned(in[l], 4), SFFN_EINVAL, "gemv_lists: in[%d] must be non-null", l);
+    REQUIRE(idx[l] && count[l] && aligned(idx[l], 4) && aligned(count[l], 4), SFFN_EINVAL,
+            "gemv_lists: idx[%d] and count[%d] must be non-null and 4-byte aligned", l, l);
+    REQUIRE(n_rows[l] >= 0 && k_max[l] >= 0 && (long)k_max[l] * group <= n_rows[l], SFFN_EINVAL,
+            "gemv_lists: list %d: k_max=%d * group=%d exceeds n_rows=%d", l, k_max[l], group,
+            n_rows[l]);
+    const float* al = alpha ? alpha[l] : nullptr;
+    if (al) REQUIRE(aligned(al, 4), SFFN_EINVAL, "gemv_lists: alpha[%d] misaligned", l);
+    a.l[l] = sffn::AxpyList{W[l], in[l], idx[l], count[l], al, k_max[l]};
+    items += (long)k_max[l] * group;
+  }
+  REQUIRE(items <= INT32_MAX, SFFN_EINVAL, "gemv_lists: too many rows");
+  const size_t need = sffn::workspace_bytes(1, (int)items, d);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
+          "gemv_lists: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv_lists: workspace must be 256-byte aligned");
+  a.n = n_lists;
+  a.d = d;
+  a.ld_w = ld_w;
+  a.group = group;
+  a.out = out;
+  a.accumulate = accumulate ? 1 : 0;
+  a.ws = workspace;
+  a.ws_bytes = ws_bytes;
+  return from_hip(sffn::launch_axpy_lists(a, (hipStream_t)stream), "gemv_lists launch");
+}
+
 sffn_status sparse_ffn_compact(const uint16_t* W, int n_rows, int d, int ld_w,
                                const int32_t* idx, int k, int transpose, uint16_t* out,
                                int ld_out, void* stream) {

@@ -12,34 +12,27 @@
 // (1 KiB per wave instruction), four or eight rows in flight per lane.  Waves are summed in LDS and the chunk's
 // partial row goes to the workspace.  Kernel 2 sums the KS partials in chunk
 // order and applies alpha / accumulate.
+#include <algorithm>
 #include <type_traits>
 
 #include "sffn_splitk.h"
 
 namespace sffn {
 
-__global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float* partials) {
-  __shared__ float4 red[kWaves][kTileCols / 4];
+// Adds this wave's rows of the chunk [k0, k1) of a row list to acc: wave w
+// takes items k0 + w + kWaves * u.  Their rows, activations and masks are
+// fetched with one vector load per lane (lane l: item u = ub + l), then
+// broadcast with readlane, so the weight loads of all of the wave's rows are
+// issued back to back without waiting on indices.
+__device__ __forceinline__ void axpy_chunk(const uint16_t* W, int ld_w, const float* in,
+                                           const int32_t* idx, int group, const uint8_t* row_mask,
+                                           int k0, int k1, int colc, float (&acc)[8]) {
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int tile = blockIdx.x, ks = blockIdx.y;
-  const int col = tile * kTileCols + 8 * lane;
-  const int colc = col < a.d ? col : 0;   // lanes past the last column re-read column 0 (discarded)
-
-  const int n_items = item_count(a.idx, a.count, a.k_max, a.group, a.n_rows);
-  const int chunk = (n_items + KS - 1) / KS;
-  const int k0 = ks * chunk;
-  const int k1 = min(n_items, k0 + chunk);
-  // This wave's items are k0 + w + kWaves * u, u < nu.  Their rows,
-  // activations and masks are fetched with one vector load per lane (lane l:
-  // item u = ub + l), then broadcast with readlane, so the weight loads of all
-  // of the wave's rows are issued back to back without waiting on indices.
   const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int ub = 0; ub < nu; ub += 64) {
     const bool ok = ub + lane < nu;
     const int it = k0 + w + kWaves * (ok ? ub + lane : 0);
-    const int r = item_row(a.idx, a.group, it);
+    const int r = item_row(idx, group, it);
     const int nb = min(64, nu - ub);
     // Every load of a batch is issued (a padding slot past the wave's last
     // row re-reads its first row with weight 0): no branch around a load, so
@@ -52,10 +45,10 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
         const int rr = __builtin_amdgcn_readlane(r, u + uu < nb ? u + uu : 0);
-        wv[uu] = load_stream16(a.W + (size_t)rr * a.ld_w + colc);
+        wv[uu] = load_stream16(W + (size_t)rr * ld_w + colc);
       }
-      float v = a.in[r];
-      if (a.row_mask && !a.row_mask[r]) v = 0.f;
+      float v = in[r];
+      if (row_mask && !row_mask[r]) v = 0.f;
       const float av = ok ? v : 0.f;
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
@@ -72,10 +65,55 @@ __global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float
     for (; u + 8 <= nb; u += 8) batch(u, std::integral_constant<int, 8>());
     for (; u < nb; u += 4) batch(u, std::integral_constant<int, 4>());
   }
+}
+
+__global__ __launch_bounds__(1024) void axpy_b1_kernel(AxpyArgs a, int KS, float* partials) {
+  __shared__ float4 red[kWaves][kTileCols / 4];
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x, ks = blockIdx.y;
+  const int col = tile * kTileCols + 8 * lane;
+  const int colc = col < a.d ? col : 0;   // lanes past the last column re-read column 0 (discarded)
+
+  const int n_items = item_count(a.idx, a.count, a.k_max, a.group, a.n_rows);
+  const int chunk = (n_items + KS - 1) / KS;
+  const int k0 = ks * chunk;
+  const int k1 = min(n_items, k0 + chunk);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  axpy_chunk(a.W, a.ld_w, a.in, a.idx, a.group, a.row_mask, k0, k1, colc, acc);
 
   const float part = wg_reduce_cols(red, acc);
   const int c = tile * kTileCols + (int)threadIdx.x;
   if (threadIdx.x < kTileCols && c < a.d) partials[(size_t)ks * a.d + c] = part;
+}
+
+// Several row lists into one output: chunk ks belongs to the list l with
+// ks_begin[l] <= ks < ks_begin[l+1]; its partial is scaled by alpha_l here,
+// so the ordered reduction adds plain partials.
+struct ListChunks { int ks_begin[kMaxLists + 1]; };
+
+__global__ __launch_bounds__(1024) void axpy_lists_kernel(AxpyListsArgs a, ListChunks lc,
+                                                          float* partials) {
+  __shared__ float4 red[kWaves][kTileCols / 4];
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x, ks = blockIdx.y;
+  const int col = tile * kTileCols + 8 * lane;
+  const int colc = col < a.d ? col : 0;   // lanes past the last column re-read column 0 (discarded)
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxLists; ++i) l += (i < a.n && ks >= lc.ks_begin[i]) ? 1 : 0;
+  const AxpyList L = a.l[l];
+  const int KS = lc.ks_begin[l + 1] - lc.ks_begin[l];
+  const int n_items = item_count(L.idx, L.count, L.k_max, a.group, 0);
+  const int chunk = (n_items + KS - 1) / KS;
+  const int k0 = (ks - lc.ks_begin[l]) * chunk;
+  const int k1 = min(n_items, k0 + chunk);
+  const float al = L.alpha ? *L.alpha : 1.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  axpy_chunk(L.W, a.ld_w, L.in, L.idx, a.group, nullptr, k0, k1, colc, acc);
+
+  const float part = wg_reduce_cols(red, acc);
+  const int c = tile * kTileCols + (int)threadIdx.x;
+  if (threadIdx.x < kTileCols && c < a.d) partials[(size_t)ks * a.d + c] = al * part;
 }
 
 // Ordered reduction of [KS][Mp][d] partials.  A 256-thread workgroup covers
@@ -166,6 +204,35 @@ hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(partials, KS, 1, 1, a.d, a.alpha, a.out, a.d, a.accumulate, s);
+}
+
+hipError_t launch_axpy_lists(const AxpyListsArgs& a, hipStream_t s) {
+  const int col_tiles = (a.d + kTileCols - 1) / kTileCols;
+  long items = 0;
+  for (int l = 0; l < a.n; ++l) items += (long)a.l[l].k_max * a.group;
+  // the split one product of all the rows would take, shared out by the
+  // lists' row bounds (every list with rows keeps at least one chunk)
+  // (every list's rounding may add one chunk: keep the total within kMaxSplit)
+  const int KS = std::min(pick_split_b1(items, col_tiles), kMaxSplit - a.n);
+  ListChunks lc{};
+  int ks = 0;
+  for (int l = 0; l < a.n; ++l) {
+    lc.ks_begin[l] = ks;
+    const long li = (long)a.l[l].k_max * a.group;
+    long k = items > 0 ? (long)((double)KS * (double)li / (double)items + 0.5) : 0;
+    if (li > 0 && k < 1) k = 1;
+    if (k > (li + kWaves - 1) / kWaves) k = (li + kWaves - 1) / kWaves;
+    ks += (int)k;
+  }
+  for (int l = a.n; l <= kMaxLists; ++l) lc.ks_begin[l] = ks;
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
+  if (ks > 0) {
+    hipLaunchKernelGGL(axpy_lists_kernel, dim3(col_tiles, ks), dim3(1024), 0, s, a, lc, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // no rows at all: zero chunks, the reduction writes out (+)= 0
+  return launch_splitk_reduce(partials, ks, 1, 1, a.d, nullptr, a.out, a.d, a.accumulate, s);
 }
 
 }  // namespace sffn

@@ -111,6 +111,20 @@ struct AxpyArgs {
 hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s);
 hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s);
 
+// Gathered products over several row lists into one output at batch 1.
+constexpr int kMaxLists = 8;
+struct AxpyList {
+  const uint16_t* W; const float* in; const int32_t* idx; const int32_t* count;
+  const float* alpha; int k_max;
+};
+struct AxpyListsArgs {
+  AxpyList l[kMaxLists];
+  int n, d, ld_w, group;
+  float* out; int accumulate;
+  void* ws; size_t ws_bytes;
+};
+hipError_t launch_axpy_lists(const AxpyListsArgs& a, hipStream_t s);
+
 struct SelectArgs {
   const void* keys; int key_type; int rows, n, ld, cluster;
   int r_lo, r_hi, nonzero_only;

@@ -232,7 +232,7 @@ class ReluMoEStack:
         self.a = torch.zeros(top_k, N, dtype=F32, device=dev)
         self.cidx = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
         self.ccnt = torch.zeros(top_k, dtype=I32, device=dev)
-        self.ws = [B.new_workspace(1, N, d, device=dev) for _ in range(top_k)]
+        self.ws = B.new_workspace(1, top_k * N, d, device=dev)
 
     def route(self, logits: torch.Tensor):
         """logits [L][T][E] -> (experts [L*T][k] device, weights [L*T][k]
@@ -249,9 +249,11 @@ class ReluMoEStack:
 
     def layer(self, l: int, t: int, h: torch.Tensor, record=None) -> None:
         """One layer for token t.  The routed experts are independent until
-        their down products are added to h, so each runs on its own stream
-        (forked from and joined back to the caller's stream); only the
-        residual updates are ordered, expert by expert."""
+        their down products are added to h, so each expert's gate, cluster
+        selection and up run on its own stream (forked from and joined back
+        to the caller's stream); then both experts' down products, weighted
+        by the router, are one gathered product over two row lists added to
+        h (one split-K launch and one reduction)."""
         row = l * self.T + t
         chosen = self.route_host[row]
         main = torch.cuda.current_stream()
@@ -273,19 +275,15 @@ class ReluMoEStack:
         if record is not None:
             torch.cuda.synchronize()
             record(l, t, h, chosen)
-        prev = None
-        for j, e in enumerate(chosen):
-            WdT = self.experts[l][e][2]
-            with torch.cuda.stream(streams[j]):
-                if prev is not None:
-                    streams[j].wait_stream(prev)   # h is updated by one expert at a time
-                B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.a[j], h, idx=self.cidx[j],
-                                  count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
-                                  alpha=self.route_w[row, j:j + 1], accumulate=True,
-                                  workspace=self.ws[j])
-            prev = streams[j]
         for s in streams:
             main.wait_stream(s)
+        k = len(chosen)
+        B.sparse_ffn_gemv_lists([self.experts[l][e][2] for e in chosen],
+                                [self.a[j] for j in range(k)], [self.cidx[j] for j in range(k)],
+                                [self.ccnt[j:j + 1] for j in range(k)], [self.nc] * k, h,
+                                group=self.cluster,
+                                alphas=[self.route_w[row, j:j + 1] for j in range(k)],
+                                accumulate=True, workspace=self.ws)
 
     def _streams(self, k: int):
         if not hasattr(self, "_expert_streams") or len(self._expert_streams) < k:

@@ -89,7 +89,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 4
+#define SFFN_ABI_VERSION 5
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -208,6 +208,37 @@ sffn_status sparse_ffn_gemv(int op,
                             const float* alpha,
                             float* out, uint32_t* key_out, int ld_out, int accumulate,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_gemv_lists -- one gathered product over several row lists into
+ * one output, at batch 1.  The routed experts of a MoE layer add their FFN
+ * outputs with the router's mixing weights ([PowerInfer-2] guide, the MoE
+ * engine listing sums the selected experts' outputs); with every expert's
+ * active rows as one list, their down products become one product:
+ *   out[o] = (accumulate ? out[o] : 0)
+ *            + sum_{l < n_lists} alpha_l * sum over processed rows n of list l
+ *              of in_l[n] * W_l[n][o]
+ * List l processes, for i < min(*count[l], k_max[l]) and g < group, row
+ * idx[l][i]*group + g of W[l] (bf16 [n_rows[l]][ld_w], rows of length d,
+ * 16-byte aligned); in[l] is fp32 [n_rows[l]]; alpha[l] is a device fp32
+ * scalar, or NULL for 1.  W, n_rows, in, idx, count, k_max and alpha are
+ * HOST arrays of n_lists entries (the pointers they hold are device
+ * pointers; alpha itself may be NULL).  The lists share d, ld_w and group.
+ * Rows of every list are split into chunks whose partial sums (scaled by
+ * alpha_l) are added in a fixed order by a second kernel: bitwise
+ * reproducible run to run.  Skipped rows are never read.
+ * Limits: 1 <= n_lists <= 8; d % 8 == 0; ld_w >= d, ld_w % 8 == 0;
+ * 0 <= k_max[l], k_max[l]*group <= n_rows[l]; out 16-byte aligned.
+ * workspace: sparse_ffn_workspace_size(1, sum_l k_max[l]*group, d) bytes,
+ * 256-byte aligned.  Errors as for sparse_ffn_gemv (nothing is launched on
+ * a rejected call).
+ */
+sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const int* n_rows,
+                                  int d, int ld_w, const float* const* in,
+                                  const int32_t* const* idx, const int32_t* const* count,
+                                  const int* k_max, int group, const float* const* alpha,
+                                  float* out, int accumulate,
+                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * sparse_ffn_compact -- gather the weight rows of a selected neuron set into

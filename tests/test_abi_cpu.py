@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 4
+    assert L.sffn_abi_version() == 5
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -133,6 +133,44 @@ def test_gemv_validation(L):
     assert rc == 1 and "rms_eps" in msg
     rc, msg = gemv(L, op=3, eps=1e-5, ws=FAKE, ws_bytes=1 << 30)
     assert rc == 1 and "rms_eps" in msg
+
+
+def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),
+               idx=(FAKE, FAKE), count=(FAKE, FAKE), k_max=(2, 2), group=32, alpha=None, out=FAKE,
+               ws=FAKE, ws_bytes=1 << 30, null_arrays=False):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    arr = lambda T, vs: (T * len(vs))(*vs)  # noqa: E731
+    rc = L.sparse_ffn_gemv_lists(
+        n, None if null_arrays else arr(P, W), arr(I, n_rows), d, ld_w, arr(P, inp), arr(P, idx),
+        arr(P, count), arr(I, k_max), group, None if alpha is None else arr(P, alpha), out, 1, ws,
+        ws_bytes, NULL)
+    return status_and_msg(L, rc)
+
+
+def test_gemv_lists_validation(L):
+    rc, msg = gemv_lists(L, n=0)
+    assert rc == 1 and "n_lists" in msg
+    rc, msg = gemv_lists(L, n=9)
+    assert rc == 1 and "n_lists" in msg
+    rc, msg = gemv_lists(L, null_arrays=True)
+    assert rc == 1 and "host arrays" in msg
+    rc, msg = gemv_lists(L, W=(FAKE, NULL))
+    assert rc == 1 and "W[1]" in msg
+    rc, msg = gemv_lists(L, idx=(FAKE, NULL))
+    assert rc == 1 and "idx[1]" in msg
+    rc, msg = gemv_lists(L, k_max=(2, 3))       # 3 clusters of 32 rows > 64 rows
+    assert rc == 1 and "exceeds" in msg
+    rc, msg = gemv_lists(L, d=60, ld_w=64)
+    assert rc == 1 and "multiple of 8" in msg
+    rc, msg = gemv_lists(L, group=0)
+    assert rc == 1 and "group" in msg
+    rc, msg = gemv_lists(L, alpha=(FAKE, ctypes.c_void_p(0x1002)))
+    assert rc == 1 and "alpha[1]" in msg
+    rc, msg = gemv_lists(L, ws=NULL, ws_bytes=0)
+    assert rc == 3 and "workspace" in msg
+    rc, msg = gemv_lists(L, ws_bytes=64)
+    assert rc == 3
 
 
 def test_score_validation(L):

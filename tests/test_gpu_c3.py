@@ -99,3 +99,55 @@ def test_small_moe():
 
 def test_full_size_moe():
     run_moe(L=32, E=8, N=14336, d=4096, n_tokens=2, check_layers={0, 31}, on_device_weights=True)
+
+
+def test_gemv_lists_against_oracle():
+    """The routed experts' down products as one gathered product over
+    several row lists: sum_l alpha_l * sum over list l's rows of a_n W_l[n],
+    added to the output; rows outside the lists are poisoned with NaN and
+    must never be read; repeated calls are bitwise equal."""
+    from activation_sparse_decode_amd import binding as B
+    banner("c3 gemv_lists")
+    rng = np.random.default_rng(21)
+    N, d = 2048, 1024
+    W = [synth.weight_bf16(5, synth.W_C3, 9, e, synth.T_DOWN, N, d) for e in range(3)]
+
+    def case(group, counts, k_maxs, with_alpha):
+        n_l = len(counts)
+        sel = [np.sort(rng.choice(N // group, size=c, replace=False)).astype(np.int32)
+               for c in counts]
+        acts = [rng.standard_normal(N).astype(np.float32) for _ in range(n_l)]
+        alphas = rng.uniform(0.1, 0.9, n_l).astype(np.float32) if with_alpha else np.ones(n_l, np.float32)
+        Wp, y_ref = [], rng.standard_normal(d).astype(np.float64)
+        y0 = y_ref.astype(np.float32)
+        y_ref = y0.astype(np.float64)
+        for l in range(n_l):
+            used = sel[l][:min(counts[l], k_maxs[l])]
+            rows = oracle.expand_clusters(used, group) if group > 1 else used
+            poisoned = W[l].copy()
+            keep = np.zeros(N, bool)
+            keep[rows] = True
+            poisoned[~keep] = 0x7FC0            # bf16 NaN in every row no list reads
+            Wp.append(poisoned)
+            y_ref = y_ref + float(alphas[l]) * oracle.down_gather(W[l], rows, acts[l][rows])
+        out = dev(y0)
+        ws = B.new_workspace(1, sum(k * group for k in k_maxs), d)
+        al = [torch.tensor([a], dtype=torch.float32, device="cuda") for a in alphas]
+        args = ([dev(w) for w in Wp], [dev(a) for a in acts],
+                [dev(np.pad(s, (0, 1))) for s in sel],
+                [torch.tensor([c], dtype=torch.int32, device="cuda") for c in counts], list(k_maxs))
+        B.sparse_ffn_gemv_lists(*args, out, group=group, alphas=al if with_alpha else None,
+                                accumulate=True, workspace=ws)
+        torch.cuda.synchronize()
+        got = host(out)
+        assert np.all(np.isfinite(got)), "a row outside the lists was read"
+        assert_close(got - y0, y_ref - y0, what=f"lists group={group} counts={counts}")
+        out2 = dev(y0)
+        B.sparse_ffn_gemv_lists(*args, out2, group=group, alphas=al if with_alpha else None,
+                                accumulate=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out2), got), "repeated calls differ"
+
+    case(32, [13, 20], [N // 32, N // 32], True)          # two experts' active clusters
+    case(32, [0, 17], [N // 32, N // 32], True)           # one expert with no active cluster
+    case(1, [700, 31, 1200], [700, 31, 1000], False)      # single rows; k_max caps the third list
