@@ -53,8 +53,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_score.restype = _i
         L.sparse_ffn_score.argtypes = [_i, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp]
         L.sparse_ffn_select.restype = _i
-        L.sparse_ffn_select.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
-                                        _i, _vp, _vp, _i, _vp, _vp, _vp]
+        L.sparse_ffn_select.argtypes = [_vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i,
+                                        _vp, _i, _vp, _vp, _i, _vp, _vp, _vp]
+        L.sparse_ffn_row_norms.restype = _i
+        L.sparse_ffn_row_norms.argtypes = [_vp, _i, _i, _i, _vp, _vp]
         L.sparse_ffn_gemv.restype = _i
         L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
                                       _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 5:
+        if L.sffn_abi_version() != 6:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -125,11 +127,13 @@ def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *
                       count_out: torch.Tensor | None = None,
                       idx_top_out: torch.Tensor | None = None,
                       count_top_out: torch.Tensor | None = None,
-                      freq: torch.Tensor | None = None, stream=None) -> None:
+                      freq: torch.Tensor | None = None, key_scale: torch.Tensor | None = None,
+                      stream=None) -> None:
     rows, width = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
     n = width // cluster
     _check(lib().sparse_ffn_select(
-        _p(keys), key_type, rows, n, _ld(keys, width), cluster, r_lo, r_hi, int(nonzero_only),
+        _p(keys), key_type, _p(key_scale), rows, n, _ld(keys, width), cluster, r_lo, r_hi,
+        int(nonzero_only),
         _p(include_mask), _p(mask_out), _ld(mask_out, n), _p(idx_out),
         _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out),
         _p(idx_top_out), _ld(idx_top_out, idx_top_out.shape[-1] if idx_top_out is not None else 0),
@@ -156,6 +160,11 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
         k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), float(rms_eps), _p(aux),
         _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_ffn_row_norms(W: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _check(lib().sparse_ffn_row_norms(_p(W), W.shape[0], W.shape[1], W.stride(0), _p(out),
+                                      _stream(stream)))
 
 
 def sparse_ffn_gemv_lists(Ws, ins, idxs, counts, k_maxs, out: torch.Tensor, *, group: int = 1,

@@ -97,7 +97,8 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld, in
                   "score launch");
 }
 
-sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld,
+sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_scale, int rows,
+                              int n, int ld,
                               int cluster, int r_lo, int r_hi, int nonzero_only,
                               const uint8_t* include_mask, uint8_t* mask_out, int ld_mask,
                               int32_t* idx_out, int ld_idx, int32_t* count_out,
@@ -117,6 +118,11 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
   REQUIRE(!(nonzero_only && key_type == SFFN_KEY_F32), SFFN_EINVAL,
           "select: nonzero_only is not defined for signed keys");
   REQUIRE(aligned(keys, 4), SFFN_EINVAL, "select: keys must be 4-byte aligned");
+  if (key_scale) {
+    REQUIRE(key_type == SFFN_KEY_ABS_F32 && cluster == 1, SFFN_EINVAL,
+            "select: key_scale needs SFFN_KEY_ABS_F32 keys and cluster == 1");
+    REQUIRE(aligned(key_scale, 4), SFFN_EINVAL, "select: key_scale must be 4-byte aligned");
+  }
   if (mask_out) REQUIRE(ld_mask >= n, SFFN_EINVAL, "select: ld_mask=%d < n=%d", ld_mask, n);
   if (idx_out) {
     const long need = include_mask ? (long)n : std::min((long)r_hi - r_lo, (long)n);
@@ -132,7 +138,7 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, i
   if (count_top_out) REQUIRE(aligned(count_top_out, 4), SFFN_EINVAL, "select: count_top_out misaligned");
   if (freq_inout) REQUIRE(aligned(freq_inout, 4), SFFN_EINVAL, "select: freq misaligned");
   if (rows == 0) return ok();
-  sffn::SelectArgs a{keys, key_type, rows, n, ld, cluster, r_lo, r_hi, nonzero_only ? 1 : 0,
+  sffn::SelectArgs a{keys, key_type, key_scale, rows, n, ld, cluster, r_lo, r_hi, nonzero_only ? 1 : 0,
                      include_mask, mask_out, ld_mask, idx_out, ld_idx, count_out, idx_top_out,
                      ld_idx_top, count_top_out, freq_inout};
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
@@ -206,6 +212,19 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                    row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes};
   return from_hip(batch == 1 ? sffn::launch_axpy_b1(a, s) : sffn::launch_axpy_mfma(a, s),
                   "gemv launch");
+}
+
+sffn_status sparse_ffn_row_norms(const uint16_t* W, int n_rows, int d, int ld_w, float* out,
+                                 void* stream) {
+  REQUIRE(W && out, SFFN_EINVAL, "row_norms: W and out must be non-null");
+  REQUIRE(n_rows >= 0, SFFN_EINVAL, "row_norms: n_rows=%d must be >= 0", n_rows);
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "row_norms: d=%d must be a positive multiple of 8", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL,
+          "row_norms: ld_w=%d must be >= d and a multiple of 8", ld_w);
+  REQUIRE(aligned(W, 16) && aligned(out, 4), SFFN_EINVAL, "row_norms: W/out misaligned");
+  if (n_rows == 0) return ok();
+  return from_hip(sffn::launch_row_norms(W, n_rows, d, ld_w, out, (hipStream_t)stream),
+                  "row_norms launch");
 }
 
 sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const int* n_rows,

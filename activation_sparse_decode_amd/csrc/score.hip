@@ -8,6 +8,10 @@
 //               is order-free, so the result is exact.
 //  SOFTMAX_PICKED  mixing weights of the picked entries of a row (the two
 //               routed experts of the MoE layer).
+// Row norms of a bf16 matrix (offline): ||W[r]||_2 of each row of W^T, the
+// weight norm of input channel r that WiSparse's weight-aware saliency
+// multiplies with the activation magnitude.  A wave per row; lane l adds
+// the squares of chunks l, l+64, ... in order, then the wave sum.
 #include "sffn_device.h"
 
 namespace sffn {
@@ -51,6 +55,30 @@ __global__ __launch_bounds__(256) void score_softmax_picked_kernel(const float* 
   float z = 0.f;
   for (int j = 0; j < k; ++j) z += expf(v[p[j]] - m);
   for (int j = 0; j < k; ++j) out[(size_t)t * k + j] = expf(v[p[j]] - m) / z;
+}
+
+__global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restrict__ W, int n_rows,
+                                                        int d, int ld_w, float* __restrict__ out) {
+  const int r = blockIdx.x * 4 + wave_id();
+  if (r >= n_rows) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* w = W + (size_t)r * ld_w;
+  float s = 0.f;
+  for (int c = lane; c < (d >> 3); c += 64) {
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(w + 8 * c), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(f[e], f[e], s);
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[r] = sqrtf(s);
+}
+
+hipError_t launch_row_norms(const uint16_t* W, int n_rows, int d, int ld_w, float* out,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(row_norms_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, s, W, n_rows, d, ld_w,
+                     out);
+  return hipGetLastError();
 }
 
 hipError_t launch_score(int mode, const float* in, int T, int n, int ld, int cluster,

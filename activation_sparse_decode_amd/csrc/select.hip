@@ -8,6 +8,10 @@
 // second list.  With cluster > 1 an entry is a block of `cluster` contiguous
 // values whose key is the largest key of the block (PowerInfer-2 guide,
 // "Neuron Cluster Decomposition": the cluster is the unit that is selected).
+// With a key scale vector, the key of entry j is the magnitude key of the
+// fp32 product v_j * scale_j, formed as the keys are loaded (WiSparse's
+// weight-aware saliency: activation magnitude times a precomputed weight
+// norm of the channel).
 //
 // Method: NT threads; wave w owns the KPT*64 consecutive entries starting at
 // w*KPT*64, lane l the entries w*KPT*64 + j*64 + l (j < KPT), so every load
@@ -169,9 +173,19 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if (a.cluster == 1) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = kp[min(ebase + 64 * j, n - 1)];
+    if (a.key_scale) {
+      // weight-aware magnitude: the key of the fp32 product v_j * scale_j
+      float sc[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      key[j] = ebase + 64 * j < n ? key_of_bits(a.key_type, key[j]) : 0u;
+      for (int j = 0; j < KPT; ++j) sc[j] = a.key_scale[min(ebase + 64 * j, n - 1)];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        key[j] = ebase + 64 * j < n ? key_abs(__uint_as_float(key[j]) * sc[j]) : 0u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        key[j] = ebase + 64 * j < n ? key_of_bits(a.key_type, key[j]) : 0u;
+    }
   } else {
     // cluster keys: coalesced reads of the n*cluster values, max per cluster
     // in LDS (the value index i belongs to cluster floor((i + 0.5) / cluster),

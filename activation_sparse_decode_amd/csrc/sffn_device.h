@@ -126,7 +126,7 @@ struct AxpyListsArgs {
 hipError_t launch_axpy_lists(const AxpyListsArgs& a, hipStream_t s);
 
 struct SelectArgs {
-  const void* keys; int key_type; int rows, n, ld, cluster;
+  const void* keys; int key_type; const float* key_scale; int rows, n, ld, cluster;
   int r_lo, r_hi, nonzero_only;
   const uint8_t* include_mask;
   uint8_t* mask_out; int ld_mask;
@@ -141,6 +141,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_score(int mode, const float* in, int T, int n, int ld, int cluster,
                         int accumulate, const int32_t* picked, int k, void* out,
                         hipStream_t s);
+hipError_t launch_row_norms(const uint16_t* W, int n_rows, int d, int ld_w, float* out,
+                            hipStream_t s);
 
 struct TierArgs {
   const uint16_t* Wt; int ld_w;

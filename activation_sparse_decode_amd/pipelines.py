@@ -187,12 +187,20 @@ class SelectInferStack:
 
 class TieredProjection:
     """y = W x with the SpAx three tiers: the k_top largest |x_j| columns from
-    bf16, the next k_mid from 4-bit codes, the rest skipped."""
+    bf16, the next k_mid from 4-bit codes, the rest skipped.
 
-    def __init__(self, Wt: torch.Tensor, seg_rows, k_top: int, k_mid: int):
+    With ``weight_aware`` the columns are ranked by the WiSparse saliency
+    |x_j| * ||W[:, j]||_2 instead, the norms computed once here."""
+
+    def __init__(self, Wt: torch.Tensor, seg_rows, k_top: int, k_mid: int,
+                 weight_aware: bool = False):
         self.Wt, self.seg_rows, self.k_top, self.k_mid = Wt, list(seg_rows), k_top, k_mid
         n_in, n_out = Wt.shape
         dev = Wt.device
+        self.norms = None
+        if weight_aware:
+            self.norms = torch.zeros(n_in, dtype=F32, device=dev)
+            B.sparse_ffn_row_norms(Wt, self.norms)
         rb = B.tier_record_bytes(n_out, len(seg_rows) - 1)
         self.rec = torch.zeros(n_in, rb, dtype=U8, device=dev)
         B.sparse_ffn_encode_tiers(Wt, self.seg_rows, self.rec)
@@ -205,7 +213,8 @@ class TieredProjection:
         # one selection yields both tiers: ranks [0, k_top) and [k_top, k_top + k_mid)
         B.sparse_ffn_select(x, B.KEY_ABS_F32, self.k_top, self.k_top + self.k_mid,
                             idx_out=self.idx_mid, count_out=self.cnt[1:2],
-                            idx_top_out=self.idx_top, count_top_out=self.cnt[0:1])
+                            idx_top_out=self.idx_top, count_top_out=self.cnt[0:1],
+                            key_scale=self.norms)
         B.sparse_ffn_tiered_gemv(self.Wt, self.rec, self.seg_rows, x, self.idx_top, self.cnt[0:1],
                                  self.k_top, self.idx_mid, self.cnt[1:2], self.k_mid, y,
                                  workspace=self.ws)

@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
     p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
+    p.add_argument("--weight-aware", action="store_true",
+                   help="workload c2: rank columns by |x_j| * ||W[:, j]||_2 (WiSparse)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="bounded CPU work for the oracle baseline (0 disables it)")
     p.add_argument("--seed", type=int, default=0)
@@ -345,8 +347,9 @@ def run_c2(args, torch, B, synth, P, T):
     for c in range(copies):
         Wq = synth.torch_weight_bf16(args.seed, synth.W_C2, c, 0, synth.T_QKV, d, n_qkv, dev)
         Wd = synth.torch_weight_bf16(args.seed, synth.W_C2, c, 0, synth.T_DOWN, dff, d, dev)
-        projs.append((P.TieredProjection(Wq, seg_qkv, kq_t, kq_m),
-                      P.TieredProjection(Wd, [0, d], kd_t, kd_m)))
+        wa = args.weight_aware
+        projs.append((P.TieredProjection(Wq, seg_qkv, kq_t, kq_m, weight_aware=wa),
+                      P.TieredProjection(Wd, [0, d], kd_t, kd_m, weight_aware=wa)))
     n_tok = copies * (args.steps + 2)
     Xq_host = synth.tokens(args.seed, synth.W_C2, 1, n_tok, d)
     Xd_host = synth.tokens(args.seed, synth.W_C2, 2, n_tok, dff)
@@ -379,7 +382,8 @@ def run_c2(args, torch, B, synth, P, T):
     rec_q, rec_d = projs[0][0].rec.shape[1], projs[0][1].rec.shape[1]
     qkv_b = kq_t * n_qkv * 2 + kq_m * rec_q + 8 * (kq_t + kq_m) + 4 * n_qkv
     down_b = kd_t * d * 2 + kd_m * rec_d + 8 * (kd_t + kd_m) + 4 * d
-    step_b = qkv_b + down_b + 2 * (4 * d + 4 * dff)
+    # selection reads x (and the column norms when weight-aware), the product x again
+    step_b = qkv_b + down_b + (3 if args.weight_aware else 2) * (4 * d + 4 * dff)
     log(f"c2: {us_tok:.2f} us/token; tiered down {down_us:.2f} us")
 
     cpu = None
@@ -388,11 +392,18 @@ def run_c2(args, torch, B, synth, P, T):
         Wq0 = projs[0][0].Wt.cpu().numpy().view(np.uint16)
         Wd0 = projs[0][1].Wt.cpu().numpy().view(np.uint16)
         encq, encd = oracle.encode_4bit(Wq0, seg_qkv), oracle.encode_4bit(Wd0, [0, d])
+        if args.weight_aware:
+            nq = oracle.row_norms(Wq0).astype(np.float32)
+            nd = oracle.row_norms(Wd0).astype(np.float32)
+            sets = lambda x, kt, km, nrm: oracle.weighted_tier_sets(x, nrm, kt, km)  # noqa: E731
+        else:
+            nq = nd = None
+            sets = lambda x, kt, km, nrm: oracle.tier_sets(x, kt, km)  # noqa: E731
 
         def one(i):
-            tq, mq = oracle.tier_sets(Xq_host[i], kq_t, kq_m)
+            tq, mq = sets(Xq_host[i], kq_t, kq_m, nq)
             oracle.tiered_gemv(Wq0, *encq, seg_qkv, Xq_host[i], tq, mq)
-            td, md = oracle.tier_sets(Xd_host[i], kd_t, kd_m)
+            td, md = sets(Xd_host[i], kd_t, kd_m, nd)
             oracle.tiered_gemv(Wd0, *encd, [0, d], Xd_host[i], td, md)
 
         s, n = timed_cpu(one, args.cpu_seconds)
@@ -400,8 +411,10 @@ def run_c2(args, torch, B, synth, P, T):
                    sample=f"{n} tokens (QKV + down tiers and products; encoding excluded), "
                           f"numpy fp64")
     config = {"workload": "SpAx three-tier read, Llama3.1-8B shape: QKV 4096->4096/1024/1024 and "
-                          "down 14336->4096; 15% bf16 / 35% 4-bit / 50% skipped by |x|; batch 1 "
-                          "(8 rotating weight copies)",
+                          "down 14336->4096; 15% bf16 / 35% 4-bit / 50% skipped by "
+                          + ("|x_j| * ||W[:, j]||_2 (WiSparse weight-aware)" if args.weight_aware
+                             else "|x|")
+                          + "; batch 1 (8 rotating weight copies)",
               "batch": 1, "tiers_qkv": [kq_t, kq_m], "tiers_down": [kd_t, kd_m]}
     return result(us_tok, "us/token", args.steps * copies, 2, total_ms / args.steps, config,
                   step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),

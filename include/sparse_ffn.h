@@ -10,6 +10,8 @@
  *                 LLM Decoding on Offloaded Weights"
  *   [LeanStream]  "LeanStream: A Speculate-and-Refine Streaming Framework for
  *                 Efficient on-Device LLM Inference"
+ *   [WiSparse]    "WiSparse: Boosting LLM Inference Efficiency with
+ *                 Weight-Aware Mixed Activation Sparsity" (abstract)
  * namely: compute activations, score / rank them by magnitude, select rank
  * ranges, compact the selection into ascending index lists, and read only
  * the selected weight rows in a gathered matrix-vector product (plus the
@@ -89,7 +91,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 5
+#define SFFN_ABI_VERSION 6
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -131,6 +133,12 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  *                 Decomposition": a cluster is selected as a unit); 1 for
  *                 single values.  ld >= n * cluster; with cluster > 1,
  *                 n <= 4096.
+ *  key_scale    : nullable fp32 [n]; with SFFN_KEY_ABS_F32 keys and
+ *                 cluster == 1 only.  The key of entry j becomes the magnitude
+ *                 key of the fp32 product keys[r][j] * key_scale[j]: the
+ *                 weight-aware channel saliency of [WiSparse] (activation
+ *                 magnitude times a precomputed weight norm, e.g. from
+ *                 sparse_ffn_row_norms of the projection's W^T).
  *  nonzero_only : only entries with a nonzero key take part (ranks count
  *                 among them); not allowed with SFFN_KEY_F32.
  *  include_mask : nullable uint8 [n]; nonzero entries are OR-ed into every
@@ -148,7 +156,8 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  * Limits: 1 <= n <= 32768, 0 <= r_lo <= r_hi, r_hi may exceed the number of
  * eligible entries (then it is clipped).  The result is unique: bit-exact.
  */
-sffn_status sparse_ffn_select(const void* keys, int key_type, int rows, int n, int ld,
+sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_scale,
+                              int rows, int n, int ld,
                               int cluster, int r_lo, int r_hi, int nonzero_only,
                               const uint8_t* include_mask,
                               uint8_t* mask_out, int ld_mask,
@@ -208,6 +217,17 @@ sffn_status sparse_ffn_gemv(int op,
                             const float* alpha,
                             float* out, uint32_t* key_out, int ld_out, int accumulate,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_row_norms -- out[r] = sqrt(sum_{o < d} W[r][o]^2) for each row r
+ * of a bf16 matrix W [n_rows][ld_w] (rows of length d), accumulated in fp32
+ * (offline).  For W^T of a projection (row j = input channel j) this is the
+ * channel's weight norm ||W[:, j]||_2 that [WiSparse] multiplies with the
+ * activation magnitude to rank channels (see key_scale of sparse_ffn_select).
+ * Limits: d % 8 == 0, ld_w >= d, ld_w % 8 == 0, W 16-byte aligned.
+ */
+sffn_status sparse_ffn_row_norms(const uint16_t* W, int n_rows, int d, int ld_w, float* out,
+                                 void* stream);
 
 /*
  * sparse_ffn_gemv_lists -- one gathered product over several row lists into

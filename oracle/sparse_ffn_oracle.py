@@ -19,12 +19,17 @@ Pages cited (by title and section / equation / figure):
   Decoding on Offloaded Weights" -- abstract, Fig 2, Fig 3, Fig 4.
 * [LeanStream] "LeanStream: A Speculate-and-Refine Streaming Framework for
   Efficient on-Device LLM Inference" -- "Permutation-Invariant Execution".
+* [WiSparse] "WiSparse: Boosting LLM Inference Efficiency with Weight-Aware
+  Mixed Activation Sparsity" -- abstract (weight-aware channel saliency:
+  activation magnitude combined with precomputed weight norms).
 
 Readings taken where the pages are silent (each is listed in the design doc):
 magnitude ranking |v| everywhere; ties go to the lower index; a percentage p
 of N items is floor(p*N/100); NaN ranks above +Inf and -0 equals +0; Eq (1)
 is a sequential fp32 sum in token order; the dynamic set is unioned with the
-static set; the 4-bit codec is min/max affine with fp16 scale/zero.
+static set; the 4-bit codec is min/max affine with fp16 scale/zero; the
+weight-aware saliency of channel j is the fp32 product |x_j| * ||W[:, j]||_2
+with the weight norm precomputed in fp32.
 
 Parity status: every function below is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, special cases, invariants); none is unpinned.
@@ -245,6 +250,29 @@ def tier_sets(x: np.ndarray, k_top: int, k_mid: int) -> tuple:
     """SpAx abstract / Fig 2: the k_top columns of largest |x_j| are read
     in the original format, the next k_mid from codes, the rest skipped."""
     keys = key_abs(x)
+    return rank_range(keys, 0, k_top), rank_range(keys, k_top, k_top + k_mid)
+
+
+def row_norms(WT_bits: np.ndarray) -> np.ndarray:
+    """[WiSparse] abstract, precomputed weight norms: for W^T (row j = the
+    weights of input channel j), ||W[:, j]||_2 = sqrt(sum_o W^T[j][o]^2),
+    fp64."""
+    w = widen_bf16(WT_bits)
+    return np.sqrt(np.sum(w * w, axis=1))
+
+
+def weighted_key(x: np.ndarray, norms_f32: np.ndarray) -> np.ndarray:
+    """[WiSparse] abstract, weight-aware channel saliency: the activation
+    magnitude times the channel's weight norm, as the fp32 product of the
+    fp32 activation and the fp32 norm, keyed by magnitude."""
+    prod = np.asarray(x, dtype=np.float32) * np.asarray(norms_f32, dtype=np.float32)
+    return key_abs(prod.astype(np.float32))
+
+
+def weighted_tier_sets(x: np.ndarray, norms_f32: np.ndarray, k_top: int, k_mid: int) -> tuple:
+    """SpAx tiers (abstract, Fig 2) ranked by the [WiSparse] weight-aware
+    saliency instead of |x_j| alone."""
+    keys = weighted_key(x, norms_f32)
     return rank_range(keys, 0, k_top), rank_range(keys, k_top, k_top + k_mid)
 
 

@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 5
+    assert L.sffn_abi_version() == 6
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -56,10 +56,10 @@ def status_and_msg(L, rc):
 
 def select(L, keys=FAKE, key_type=0, rows=1, n=8, ld=8, cluster=1, r_lo=0, r_hi=4, nz=0,
            include=NULL, mask=NULL, ld_mask=0, idx=NULL, ld_idx=0, count=NULL, idx_top=NULL,
-           ld_idx_top=0, count_top=NULL, freq=NULL):
-    return status_and_msg(L, L.sparse_ffn_select(keys, key_type, rows, n, ld, cluster, r_lo, r_hi,
-                                                 nz, include, mask, ld_mask, idx, ld_idx, count,
-                                                 idx_top, ld_idx_top, count_top, freq, NULL))
+           ld_idx_top=0, count_top=NULL, freq=NULL, scale=NULL):
+    return status_and_msg(L, L.sparse_ffn_select(keys, key_type, scale, rows, n, ld, cluster, r_lo,
+                                                 r_hi, nz, include, mask, ld_mask, idx, ld_idx,
+                                                 count, idx_top, ld_idx_top, count_top, freq, NULL))
 
 
 def test_select_validation(L):
@@ -90,6 +90,24 @@ def test_select_validation(L):
     # the top list holds the ranks [0, r_lo)
     rc, msg = select(L, r_lo=3, r_hi=6, idx_top=FAKE, ld_idx_top=2)
     assert rc == 1 and "ld_idx_top" in msg
+    # weight-aware keys: fp32 magnitudes of single entries only
+    rc, msg = select(L, key_type=1, scale=FAKE)
+    assert rc == 1 and "key_scale" in msg
+    rc, msg = select(L, n=4, ld=16, cluster=4, scale=FAKE)
+    assert rc == 1 and "key_scale" in msg
+    rc, msg = select(L, scale=ctypes.c_void_p(0x1002))
+    assert rc == 1 and "key_scale" in msg
+
+
+def test_row_norms_validation(L):
+    rn = L.sparse_ffn_row_norms
+    rc, msg = status_and_msg(L, rn(NULL, 8, 64, 64, FAKE, NULL))
+    assert rc == 1 and "non-null" in msg
+    rc, msg = status_and_msg(L, rn(FAKE, 8, 60, 64, FAKE, NULL))
+    assert rc == 1 and "multiple of 8" in msg
+    rc, msg = status_and_msg(L, rn(FAKE, 8, 64, 56, FAKE, NULL))
+    assert rc == 1 and "ld_w" in msg
+    assert status_and_msg(L, rn(FAKE, 0, 64, 64, FAKE, NULL))[0] == 0   # nothing to do
 
 
 def gemv(L, op=3, W0=FAKE, W1=FAKE, n_rows=64, d=64, ld_w=64, inp=FAKE, batch=1, ld_in=64,

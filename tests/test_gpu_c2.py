@@ -115,3 +115,87 @@ def test_tier_special_cases():
     proj(xd, y)
     torch.cuda.synchronize()
     assert np.all(host(y) == 0.0)
+
+
+# ------------------------------------------------------------------ WiSparse weight-aware tiers
+@pytest.mark.parametrize("n_rows,d", [(1, 8), (7, 520), (4096, 6144), (14336, 4096)])
+def test_row_norms(n_rows, d):
+    """||W^T[j]||_2 per row: fp32 accumulation within 1e-5 relative of the
+    oracle's fp64 (about sqrt(d/8) rounding steps per lane plus the 64-lane
+    tree, far below the bound), and bit-exact where the sum of squares is an
+    integer below 2^24 (exact in any order; the fp32 square root is correctly
+    rounded, as is the fp64 one rounded to fp32)."""
+    banner(f"row norms {n_rows}x{d}")
+    Wt = synth.weight_bf16(5, synth.W_C2, 0, 0, synth.T_DOWN, n_rows, d)
+    out = torch.full((n_rows,), -1.0, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_row_norms(dev(Wt), out)
+    torch.cuda.synchronize()
+    ref = oracle.row_norms(Wt)
+    np.testing.assert_allclose(host(out), ref, rtol=1e-5, atol=0)
+    rng = np.random.default_rng(n_rows + d)
+    Wi = rng.integers(-8, 9, size=(n_rows, d)).astype(np.float32)
+    Wi[0] = 0.0                                            # a zero row
+    B.sparse_ffn_row_norms(dev(synth.f32_to_bf16_bits(Wi)), out)
+    torch.cuda.synchronize()
+    exp = oracle.row_norms(synth.f32_to_bf16_bits(Wi)).astype(np.float32)
+    assert np.array_equal(host(out).view(np.uint32), exp.view(np.uint32))
+    # a row stride wider than the row
+    Wp = np.zeros((n_rows, d + 64), np.uint16)
+    Wp[:, :d] = Wt
+    Wp[:, d:] = 0x7FC0                                     # never read
+    B.sparse_ffn_row_norms(dev(Wp)[:, :d], out)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(out), ref, rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("name", ["small", "qkv", "down"])
+def test_weight_aware_tiers(name):
+    """Tiers ranked by |x_j| * ||W[:, j]||_2.  With integer weights the GPU
+    norms equal the oracle's, so the tiers are bit-exact; with the workload's
+    weights the norms agree to rounding, so the tiers may differ only at
+    near-ties of the saliency, which is checked, and the product is compared
+    with the oracle's on the tiers taken."""
+    banner(f"c2 weight-aware {name}")
+    Wt, x, seg = make(name, seed=7)
+    n_in, n_out = Wt.shape
+    k_top, k_mid = pct_count(15, n_in), pct_count(35, n_in)
+    rng = np.random.default_rng(n_in)
+    # integer weights with per-channel spread, so the norm reorders channels
+    Wi = np.round(rng.standard_normal((n_in, n_out)) * rng.uniform(0.3, 3.0, (n_in, 1)))
+    Wi = synth.f32_to_bf16_bits(np.clip(Wi, -16, 16).astype(np.float32))
+    y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+    proj = TieredProjection(dev(Wi), seg, k_top, k_mid, weight_aware=True)
+    proj(dev(x), y)
+    torch.cuda.synchronize()
+    nrm = oracle.row_norms(Wi).astype(np.float32)
+    assert np.array_equal(host(proj.norms).view(np.uint32), nrm.view(np.uint32))
+    cnt = host(proj.cnt)
+    top, mid = host(proj.idx_top)[:cnt[0]], host(proj.idx_mid)[:cnt[1]]
+    o_top, o_mid = oracle.weighted_tier_sets(x, nrm, k_top, k_mid)
+    assert np.array_equal(top, o_top) and np.array_equal(mid, o_mid)
+    assert not np.array_equal(o_top, oracle.tier_sets(x, k_top, k_mid)[0])
+    enc = oracle.encode_4bit(Wi, seg)
+    assert_close(host(y), oracle.tiered_gemv(Wi, *enc, seg, x, o_top, o_mid), what="integer W")
+
+    # the workload's weights
+    proj = TieredProjection(dev(Wt), seg, k_top, k_mid, weight_aware=True)
+    proj(dev(x), y)
+    torch.cuda.synchronize()
+    ref_n = oracle.row_norms(Wt)
+    np.testing.assert_allclose(host(proj.norms), ref_n, rtol=1e-5, atol=0)
+    cnt = host(proj.cnt)
+    top, mid = host(proj.idx_top)[:cnt[0]], host(proj.idx_mid)[:cnt[1]]
+    assert top.size == k_top and mid.size == k_mid and np.intersect1d(top, mid).size == 0
+    assert np.all(np.diff(top) > 0) and np.all(np.diff(mid) > 0)
+    o_top, o_mid = oracle.weighted_tier_sets(x, ref_n.astype(np.float32), k_top, k_mid)
+    sal = np.abs(x.astype(np.float64)) * ref_n
+    rest = np.setdiff1d(np.arange(n_in), np.concatenate([top, mid]))
+    for got, exp, below in [(top, o_top, np.concatenate([mid, rest])), (mid, o_mid, rest)]:
+        diff = np.setxor1d(got, exp)
+        if diff.size and got.size and below.size:
+            edge = sal[got].min()
+            assert np.all(np.abs(sal[diff] - edge) <= 1e-5 * edge), (name, diff)
+        if got.size and below.size:
+            assert sal[got].min() >= sal[below].max() * (1 - 1e-5)
+    enc = oracle.encode_4bit(Wt, seg)
+    assert_close(host(y), oracle.tiered_gemv(Wt, *enc, seg, x, top, mid), what="weight-aware")

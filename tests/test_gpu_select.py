@@ -164,3 +164,45 @@ def test_two_lists(n, k_top, k_mid):
         exp_mid = oracle.rank_range(k, k_top, k_top + k_mid, False, None)
         assert gct[row] == exp_top.size and np.array_equal(gt[row, :gct[row]], exp_top), row
         assert gcm[row] == exp_mid.size and np.array_equal(gm[row, :gcm[row]], exp_mid), row
+
+
+@pytest.mark.parametrize("n", [1, 7, 1000, 4096, 14336, 20480])
+def test_weight_aware_scale(n):
+    """key_scale: entries ranked by the magnitude of the fp32 product x_j *
+    s_j (WiSparse saliency), as two tier lists; bit-exact with the oracle."""
+    banner(f"select weight-aware n={n}")
+    rng = np.random.default_rng(1000 + n)
+    x = (rng.standard_normal((3, n)) * np.exp(rng.standard_normal((3, n)))).astype(np.float32)
+    s = np.exp(rng.standard_normal(n) * 0.5).astype(np.float32)
+    x[1, : n // 2] = np.round(x[1, : n // 2])               # ties in x ...
+    s[: n // 4] = 1.0                                      # ... and in the products
+    s[n // 4: n // 4 + n // 10] = 0.0                      # zero-norm channels
+    x[2, ::3] = -x[2, ::3]
+    x[2, 1::7] *= np.float32(1e-30)                        # products down to subnormals
+    k_top, k_mid = (15 * n) // 100, (35 * n) // 100
+    mid = torch.full((3, max(1, k_mid)), -1, dtype=torch.int32, device="cuda")
+    top = torch.full((3, max(1, k_top)), -1, dtype=torch.int32, device="cuda")
+    cm = torch.zeros(3, dtype=torch.int32, device="cuda")
+    ct = torch.zeros(3, dtype=torch.int32, device="cuda")
+    mask = torch.zeros(3, n, dtype=torch.uint8, device="cuda")
+    B.sparse_ffn_select(dev(x), B.KEY_ABS_F32, k_top, k_top + k_mid, idx_out=mid, count_out=cm,
+                        idx_top_out=top, count_top_out=ct, mask_out=mask, key_scale=dev(s))
+    torch.cuda.synchronize()
+    gm, gt, gcm, gct, gmask = host(mid), host(top), host(cm), host(ct), host(mask)
+    for row in range(3):
+        exp_top, exp_mid = oracle.weighted_tier_sets(x[row], s, k_top, k_mid)
+        assert gct[row] == exp_top.size and np.array_equal(gt[row, :gct[row]], exp_top), row
+        assert gcm[row] == exp_mid.size and np.array_equal(gm[row, :gcm[row]], exp_mid), row
+        m = np.zeros(n, np.uint8)
+        m[exp_mid] = 1
+        assert np.array_equal(gmask[row], m), row
+    # unit scales reproduce the plain |x| ranking
+    k = max(1, n // 2)
+    idx = torch.full((3, k), -1, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select(dev(x), B.KEY_ABS_F32, 0, k, idx_out=idx, count_out=cm,
+                        key_scale=dev(np.ones(n, np.float32)))
+    torch.cuda.synchronize()
+    gi, gc = host(idx), host(cm)
+    for row in range(3):
+        exp = oracle.rank_range(oracle.key_abs(x[row]), 0, k)
+        assert gc[row] == exp.size and np.array_equal(gi[row, :gc[row]], exp), row

@@ -122,6 +122,79 @@ def test_tier_sets_partition_and_order():
     assert np.abs(x[mid]).min() >= np.abs(x[skipped]).max()
 
 
+# ------------------------------------------------------------------ WiSparse weight-aware saliency
+def test_row_norms_closed_forms():
+    d = 16
+    const = np.full((3, d), 0.0, np.float32)
+    const[0], const[1], const[2] = 0.5, -3.0, 0.0
+    assert oracle.row_norms(bf16(const)).tolist() == [0.5 * 4, 3.0 * 4, 0.0]
+    # Pythagorean rows, placed in different columns and in a non-square W^T
+    W = np.zeros((4, 7), np.float32)
+    W[0, [0, 6]] = [3, 4]
+    W[1, [1, 2, 5]] = [-2, 3, 6]
+    W[2, 3] = -9
+    W[3, :] = np.arange(1, 8)
+    got = oracle.row_norms(bf16(W))
+    np.testing.assert_array_equal(got[:3], [5.0, 7.0, 9.0])
+    assert got[3] == pytest.approx(np.sqrt(sum(i * i for i in range(1, 8))), rel=1e-15)
+    # one norm per input channel (row of W^T), not per output
+    assert oracle.row_norms(bf16(np.ones((5, 9), np.float32))).shape == (5,)
+
+
+def test_weighted_key_fp32_product_brute_force():
+    rng = np.random.default_rng(27)
+    for trial in range(200):
+        n = int(rng.integers(1, 12))
+        x = rng.integers(-20, 21, n).astype(np.float32)
+        w = rng.integers(0, 16, n).astype(np.float32)
+        keys = oracle.weighted_key(x, w)
+        sal = [abs(int(a)) * int(b) for a, b in zip(x, w)]        # exact in fp32
+        order = sorted(range(n), key=lambda j: (-sal[j], j))
+        k_top = int(rng.integers(0, n + 1))
+        k_mid = int(rng.integers(0, n + 1 - k_top))
+        top, mid = oracle.weighted_tier_sets(x, w, k_top, k_mid)
+        assert top.tolist() == sorted(order[:k_top]), (trial, x, w)
+        assert mid.tolist() == sorted(order[k_top:k_top + k_mid]), (trial, x, w)
+        assert all(int(keys[j]) == np.float32(sal[j]).view(np.uint32) for j in range(n))
+
+
+def test_weighted_key_special_cases():
+    rng = np.random.default_rng(28)
+    x = (rng.standard_normal(300) * np.exp(rng.standard_normal(300))).astype(np.float32)
+    # unit norms, and a power-of-two norm for every channel: the |x| tiers
+    for c in (1.0, 0.25, 8.0):
+        for got, ref in zip(oracle.weighted_tier_sets(x, np.full(300, c, np.float32), 40, 90),
+                            oracle.tier_sets(x, 40, 90)):
+            assert np.array_equal(got, ref)
+    # the sign of x does not matter
+    for got, ref in zip(oracle.weighted_tier_sets(-x, np.ones(300, np.float32), 40, 90),
+                        oracle.tier_sets(x, 40, 90)):
+        assert np.array_equal(got, ref)
+    # a zero-norm channel ranks with the zero activations, after every live one
+    w = np.ones(300, np.float32)
+    big = int(np.argmax(np.abs(x)))
+    w[big] = 0.0
+    top, _ = oracle.weighted_tier_sets(x, w, 299, 0)
+    assert big not in top.tolist() and top.size == 299
+    # the norm reorders: |x| prefers channel 1, |x| * norm channel 0
+    top, mid = oracle.weighted_tier_sets(np.array([1.0, 2.0], np.float32),
+                                         np.array([3.0, 1.0], np.float32), 1, 1)
+    assert top.tolist() == [0] and mid.tolist() == [1]
+    assert oracle.tier_sets(np.array([1.0, 2.0], np.float32), 1, 1)[0].tolist() == [1]
+
+
+def test_weighted_key_is_rounded_to_fp32():
+    # channel 0: (1 + 2^-22) * 1 exactly; channel 1: (1 + 2^-23)^2 = 1 + 2^-22 + 2^-46,
+    # larger in exact arithmetic but the same fp32 value, so the tie goes to index 0
+    e23, e22 = np.float32(2.0 ** -23), np.float32(2.0 ** -22)
+    x = np.array([1 + e22, 1 + e23], np.float32)
+    w = np.array([1.0, 1 + e23], np.float32)
+    assert (1 + 2.0 ** -23) ** 2 > 1 + 2.0 ** -22
+    keys = oracle.weighted_key(x, w)
+    assert keys[0] == keys[1]
+    assert oracle.weighted_tier_sets(x, w, 1, 0)[0].tolist() == [0]
+
+
 def test_tiered_special_cases():
     rng = np.random.default_rng(26)
     n_in, n_out = 64, 48
