@@ -53,8 +53,8 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_score.restype = _i
         L.sparse_ffn_score.argtypes = [_i, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp]
         L.sparse_ffn_select.restype = _i
-        L.sparse_ffn_select.argtypes = [_vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i,
-                                        _vp, _i, _vp, _vp, _i, _vp, _vp, _vp]
+        L.sparse_ffn_select.argtypes = [_vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                                        _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp]
         L.sparse_ffn_row_norms.restype = _i
         L.sparse_ffn_row_norms.argtypes = [_vp, _i, _i, _i, _vp, _vp]
         L.sparse_ffn_gemv.restype = _i
@@ -65,12 +65,14 @@ def lib() -> ctypes.CDLL:
                                             _vp, _i, _vp, _sz, _vp]
         L.sparse_ffn_compact.restype = _i
         L.sparse_ffn_compact.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp]
+        L.sparse_ffn_gather.restype = _i
+        L.sparse_ffn_gather.argtypes = [_vp, _i, _vp, _vp, _i, _vp, _vp]
         L.sparse_ffn_encode_tiers.restype = _i
         L.sparse_ffn_encode_tiers.argtypes = [_vp, _i, _i, _i, _vp, _i, _vp, _i, _vp]
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 6:
+        if L.sffn_abi_version() != 7:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -123,6 +125,7 @@ def sparse_ffn_score(mode: int, inp: torch.Tensor, out: torch.Tensor, *, cluster
 def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *,
                       cluster: int = 1, nonzero_only: bool = False,
                       include_mask: torch.Tensor | None = None,
+                      exclude_mask: torch.Tensor | None = None,
                       mask_out: torch.Tensor | None = None, idx_out: torch.Tensor | None = None,
                       count_out: torch.Tensor | None = None,
                       idx_top_out: torch.Tensor | None = None,
@@ -134,7 +137,7 @@ def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *
     _check(lib().sparse_ffn_select(
         _p(keys), key_type, _p(key_scale), rows, n, _ld(keys, width), cluster, r_lo, r_hi,
         int(nonzero_only),
-        _p(include_mask), _p(mask_out), _ld(mask_out, n), _p(idx_out),
+        _p(include_mask), _p(exclude_mask), _p(mask_out), _ld(mask_out, n), _p(idx_out),
         _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out),
         _p(idx_top_out), _ld(idx_top_out, idx_top_out.shape[-1] if idx_top_out is not None else 0),
         _p(count_top_out), _p(freq), _stream(stream)))
@@ -182,6 +185,15 @@ def sparse_ffn_gemv_lists(Ws, ins, idxs, counts, k_maxs, out: torch.Tensor, *, g
         n, ptrs(Ws), ints([w.shape[0] for w in Ws]), d, ld_w, ptrs(ins), ptrs(idxs), ptrs(counts),
         ints(k_maxs), group, None if alphas is None else ptrs(alphas), _p(out), int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_ffn_gather(src: torch.Tensor, idx: torch.Tensor, dst: torch.Tensor, *,
+                      count: torch.Tensor | None = None, k_max: int | None = None,
+                      stream=None) -> None:
+    """dst[i] = src[idx[i]] (4-byte elements) for i < min(*count, k_max)."""
+    k = idx.shape[0] if k_max is None else k_max
+    _check(lib().sparse_ffn_gather(_p(src), src.numel(), _p(idx), _p(count), k, _p(dst),
+                                   _stream(stream)))
 
 
 def sparse_ffn_compact(W: torch.Tensor, idx: torch.Tensor | None, k: int, transpose: bool,

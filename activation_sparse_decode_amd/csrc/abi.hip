@@ -100,7 +100,8 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld, in
 sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_scale, int rows,
                               int n, int ld,
                               int cluster, int r_lo, int r_hi, int nonzero_only,
-                              const uint8_t* include_mask, uint8_t* mask_out, int ld_mask,
+                              const uint8_t* include_mask, const uint8_t* exclude_mask,
+                              uint8_t* mask_out, int ld_mask,
                               int32_t* idx_out, int ld_idx, int32_t* count_out,
                               int32_t* idx_top_out, int ld_idx_top, int32_t* count_top_out,
                               uint32_t* freq_inout, void* stream) {
@@ -139,7 +140,8 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
   if (freq_inout) REQUIRE(aligned(freq_inout, 4), SFFN_EINVAL, "select: freq misaligned");
   if (rows == 0) return ok();
   sffn::SelectArgs a{keys, key_type, key_scale, rows, n, ld, cluster, r_lo, r_hi, nonzero_only ? 1 : 0,
-                     include_mask, mask_out, ld_mask, idx_out, ld_idx, count_out, idx_top_out,
+                     include_mask, exclude_mask, mask_out, ld_mask, idx_out, ld_idx, count_out,
+                     idx_top_out,
                      ld_idx_top, count_top_out, freq_inout};
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
 }
@@ -272,6 +274,19 @@ sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const i
   a.ws = workspace;
   a.ws_bytes = ws_bytes;
   return from_hip(sffn::launch_axpy_lists(a, (hipStream_t)stream), "gemv_lists launch");
+}
+
+sffn_status sparse_ffn_gather(const void* src, int n_src, const int32_t* idx, const int32_t* count,
+                              int k_max, void* dst, void* stream) {
+  REQUIRE(n_src >= 1, SFFN_EINVAL, "gather: n_src=%d must be >= 1", n_src);
+  REQUIRE(k_max >= 0, SFFN_EINVAL, "gather: k_max=%d must be >= 0", k_max);
+  REQUIRE(src && dst && (k_max == 0 || idx), SFFN_EINVAL, "gather: src, dst and idx must be non-null");
+  REQUIRE(aligned(src, 4) && aligned(dst, 4) && aligned(idx, 4) && aligned(count, 4), SFFN_EINVAL,
+          "gather: src/dst/idx/count must be 4-byte aligned");
+  if (k_max == 0) return ok();
+  return from_hip(sffn::launch_gather32(static_cast<const uint32_t*>(src), n_src, idx, count, k_max,
+                                        static_cast<uint32_t*>(dst), (hipStream_t)stream),
+                  "gather launch");
 }
 
 sffn_status sparse_ffn_compact(const uint16_t* W, int n_rows, int d, int ld_w,

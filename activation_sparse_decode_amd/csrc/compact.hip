@@ -10,6 +10,10 @@
 //                major, so the down projection becomes one dot product per
 //                output over the compacted activations); columns i >= k up
 //                to ld_out are zero.
+// A 4-byte gather, dst[i] = src[idx_i], carries per-neuron values (scores,
+// masks, keys) into the positions of a compacted subset: the index remap of
+// a selectively loaded layer (SelectInfer §4), whose resident weights hold
+// only the loaded neurons, in ascending order.
 #include "sffn_device.h"
 
 namespace sffn {
@@ -64,6 +68,25 @@ __global__ __launch_bounds__(256) void compact_cols_kernel(const uint16_t* __res
     if (i + 8 <= ld_out) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     if (i + 16 <= ld_out) *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
   }
+}
+
+// dst[i] = src[idx[i]] for i < min(*count, k_max) (k_max without a count);
+// an index outside [0, n_src) reads the nearest valid element.
+__global__ __launch_bounds__(256) void gather32_kernel(const uint32_t* __restrict__ src, int n_src,
+                                                       const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ count, int k_max,
+                                                       uint32_t* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int k = count ? min(max(*count, 0), k_max) : k_max;
+  if (i >= k) return;
+  dst[i] = src[min(max(idx[i], 0), n_src - 1)];
+}
+
+hipError_t launch_gather32(const uint32_t* src, int n_src, const int32_t* idx,
+                           const int32_t* count, int k_max, uint32_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(gather32_kernel, dim3((k_max + 255) / 256), dim3(256), 0, s, src, n_src, idx,
+                     count, k_max, dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const uint16_t* W, int ld_w, int d, const int32_t* idx, int k,

@@ -11,7 +11,12 @@
 // With a key scale vector, the key of entry j is the magnitude key of the
 // fp32 product v_j * scale_j, formed as the keys are loaded (WiSparse's
 // weight-aware saliency: activation magnitude times a precomputed weight
-// norm of the channel).
+// norm of the channel).  Entries marked in an exclusion mask take no part
+// in the ranking; with the same mask as the include mask the call yields
+// "the set, then the best-ranked entries outside it until k more": the
+// secondary neurons added to the base set until the loading budget is met
+// (SelectInfer §4, Fig 6) and the dynamic neurons added to the static ones
+// until the computed fraction is reached (§5).
 //
 // Method: NT threads; wave w owns the KPT*64 consecutive entries starting at
 // w*KPT*64, lane l the entries w*KPT*64 + j*64 + l (j < KPT), so every load
@@ -237,11 +242,19 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) incl |= ((ebase + 64 * j < n) & (incm[j] != 0) ? 1u : 0u) << j;
   }
+  uint32_t excl = 0;   // bit j: entry of slot j is in exclude_mask (clamped reads)
+  if (a.exclude_mask) {
+    uint8_t exm[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) exm[j] = a.exclude_mask[min(ebase + 64 * j, n - 1)];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) excl |= (exm[j] != 0 ? 1u : 0u) << j;
+  }
 
   uint32_t elig = 0, kor = 0;   // bit j: entry of slot j takes part
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const bool e = (ebase + 64 * j < n) & (!a.nonzero_only | (key[j] != 0u));
+    const bool e = (ebase + 64 * j < n) & (!a.nonzero_only | (key[j] != 0u)) & !((excl >> j) & 1u);
     elig |= (e ? 1u : 0u) << j;
     kor |= e ? key[j] : 0u;
   }
@@ -258,7 +271,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   uint32_t all_or = 0, E = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) { all_or |= wsum[0][i]; E += wsum[1][i]; }
-  if (!a.nonzero_only) E = (uint32_t)n;
+  if (!a.nonzero_only && !a.exclude_mask) E = (uint32_t)n;
   const uint32_t rhi = min((uint32_t)a.r_hi, E);
   const uint32_t rlo = LO ? min((uint32_t)a.r_lo, rhi) : 0u;
   // all_hi / all_lo: the bound covers every eligible entry (no search)

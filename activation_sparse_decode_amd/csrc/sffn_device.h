@@ -129,6 +129,7 @@ struct SelectArgs {
   const void* keys; int key_type; const float* key_scale; int rows, n, ld, cluster;
   int r_lo, r_hi, nonzero_only;
   const uint8_t* include_mask;
+  const uint8_t* exclude_mask;
   uint8_t* mask_out; int ld_mask;
   int32_t* idx_out; int ld_idx;
   int32_t* count_out;
@@ -162,6 +163,8 @@ hipError_t launch_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out
 
 hipError_t launch_compact(const uint16_t* W, int ld_w, int d, const int32_t* idx, int k,
                           int transpose, uint16_t* out, int ld_out, hipStream_t s);
+hipError_t launch_gather32(const uint32_t* src, int n_src, const int32_t* idx,
+                           const int32_t* count, int k_max, uint32_t* dst, hipStream_t s);
 
 size_t workspace_bytes(int batch, int n_rows, int d_out);
 int pick_split_b1(long items, int col_tiles);

@@ -9,6 +9,8 @@ attributes so tests can compare every stage.
 * :class:`SelectInferStack`    SelectInfer (§3-§5): Eq (1) base set from
   calibration, per-token top-alpha / frequency top-beta from the prompt,
   union, then decode over the union in every layer
+* :class:`SelectInferLoadedStack` SelectInfer with selective loading, the
+  fill-to-phi computed set and the Table 1 layer range (§4, §5, §6.4)
 * :class:`TieredProjection`    SpAx three-tier read (abstract, Fig 2-4)
 * :class:`ReluMoEStack`        ReLU-sparse MoE with 32-row clusters
   (PowerInfer-2 guide, neuron clusters) and top-2 routing
@@ -181,6 +183,179 @@ class SelectInferStack:
 
     def decode(self, h: torch.Tensor) -> None:
         """One decode token through every layer (h is updated in place)."""
+        for l in range(self.L):
+            self.decode_layer(l, h)
+
+
+class SelectInferLoadedStack:
+    """SelectInfer with its loading and computation knobs (§4, §5, Table 1).
+
+    Layers ``first .. L + last - 1`` are modified: only their loaded neurons
+    stay resident (the top ``delta_k`` by task-specific Eq (1) scores, then
+    model-specific neurons in score order until ``gamma_k``), the prompt
+    ranks each token's top ``alpha_k`` among the loaded neurons, and the
+    computed set is the static (base) neurons filled with the most frequent
+    dynamic neurons until ``phi_k``.  The other layers are loaded and
+    computed densely.  Decode streams each layer's computed set from
+    per-prompt compacted buffers (dense layers: all neurons)."""
+
+    def __init__(self, layers, delta_k: int, gamma_k: int, alpha_k: int, phi_k: int,
+                 first: int = 5, last: int = -2, max_tokens: int = 512, rms_eps: float = RMS_EPS):
+        self.layers = list(layers)    # full weights; profile() and load() read them
+        self.rms_eps = rms_eps
+        self.L = len(layers)
+        N, d = layers[0][0].shape
+        self.N, self.d = N, d
+        dev = layers[0][0].device
+        self.delta_k, self.alpha_k, self.phi_k = delta_k, alpha_k, phi_k
+        self.gamma_k = min(gamma_k, N)
+        assert delta_k <= self.gamma_k, "the base set must fit the loading budget"
+        self.modified = set(range(first, self.L + last if last <= 0 else last))
+        self.s_task = torch.zeros(self.L, N, dtype=F32, device=dev)
+        self.s_model = torch.zeros(self.L, N, dtype=F32, device=dev)
+        self.base_mask = torch.zeros(self.L, N, dtype=U8, device=dev)
+        self.load_idx = torch.zeros(self.L, N, dtype=I32, device=dev)
+        self.load_cnt = torch.zeros(self.L, dtype=I32, device=dev)
+        self.s_loaded = torch.zeros(self.L, N, dtype=F32, device=dev)
+        self.static_mask = torch.zeros(self.L, N, dtype=U8, device=dev)
+        self.freq = torch.zeros(self.L, N, dtype=I32, device=dev)
+        self.U_pos = torch.zeros(self.L, N, dtype=I32, device=dev)
+        self.U_cnt = torch.zeros(self.L, dtype=I32, device=dev)
+        self.A = torch.zeros(max_tokens, N, dtype=F32, device=dev)
+        self.K = torch.zeros(max_tokens, N, dtype=I32, device=dev)
+        self.ws_dense = B.new_workspace(max_tokens, N, d, device=dev)
+        # per layer: (W_gate, W_up, W_down^T, gate|up rows side by side or None)
+        self.resident = [None] * self.L
+
+    # ---------------------------------------------------------------- offline
+    def _profile_pass(self, X: torch.Tensor, scores: torch.Tensor, record=None) -> None:
+        H = X.clone()
+        T = H.shape[0]
+        A = self.A[:T]
+        for l in range(self.L):
+            Wg, Wu, WdT = self.layers[l]
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, H, A, rms_eps=self.rms_eps)
+            if record is not None:
+                record(l, H, A)
+            B.sparse_ffn_score(B.SCORE_SUM_ABS, A, scores[l])
+            B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, A, H, accumulate=True,
+                              workspace=self.ws_dense)
+
+    def profile(self, X_task: torch.Tensor, X_model: torch.Tensor, record=None) -> None:
+        """Eq (1) scores of every neuron over task-specific and over
+        model-specific (cross-task) calibration tokens, full model, dense."""
+        self.s_task.zero_()
+        self.s_model.zero_()
+        self._profile_pass(X_task, self.s_task,
+                           None if record is None else lambda l, H, A: record("task", l, H, A))
+        self._profile_pass(X_model, self.s_model,
+                           None if record is None else lambda l, H, A: record("model", l, H, A))
+
+    def load(self) -> None:
+        """Selective loading: per modified layer, base = top delta by task
+        scores, then model-specific neurons until gamma; the loaded rows are
+        copied into resident buffers (gate and up side by side), and the base
+        set is ranked again in loaded positions (the static set of decode).
+        Dense layers keep their full weights and an output-major down copy."""
+        d, dev = self.d, self.s_task.device
+        k = self.gamma_k
+        for l in range(self.L):
+            Wg, Wu, WdT = self.layers[l]
+            if l not in self.modified:
+                self.resident[l] = (Wg, Wu, WdT, None)
+                continue
+            B.sparse_ffn_select(self.s_task[l], B.KEY_ABS_F32, 0, self.delta_k,
+                                mask_out=self.base_mask[l])
+            B.sparse_ffn_select(self.s_model[l], B.KEY_ABS_F32, 0, k - self.delta_k,
+                                include_mask=self.base_mask[l], exclude_mask=self.base_mask[l],
+                                idx_out=self.load_idx[l], count_out=self.load_cnt[l:l + 1])
+            gu = torch.zeros(k, 2 * d, dtype=torch.int16, device=dev)
+            dn = torch.zeros(k, d, dtype=torch.int16, device=dev)
+            idx = self.load_idx[l, :k]
+            B.sparse_ffn_compact(Wg, idx, k, False, gu[:, :d])
+            B.sparse_ffn_compact(Wu, idx, k, False, gu[:, d:])
+            B.sparse_ffn_compact(WdT, idx, k, False, dn)
+            self.resident[l] = (gu[:, :d], gu[:, d:], dn, gu)
+            # index remap: the task scores in loaded positions, ranked again
+            B.sparse_ffn_gather(self.s_task[l], idx, self.s_loaded[l, :k])
+            B.sparse_ffn_select(self.s_loaded[l, :k], B.KEY_ABS_F32, 0, self.delta_k,
+                                mask_out=self.static_mask[l, :k])
+
+    def release_full_weights(self) -> None:
+        """Drop the references to the full weights of the modified layers
+        (only the resident buffers are used after load())."""
+        for l in self.modified:
+            self.layers[l] = None
+
+    # ---------------------------------------------------------------- per prompt
+    def prefill(self, X: torch.Tensor, record=None) -> torch.Tensor:
+        """Prompt pass over the resident weights: modified layers compute all
+        loaded neurons, rank each token's top alpha among them, count, and
+        fill the static set with the most frequent neurons until phi; then
+        each layer's computed set is compacted for decode."""
+        H = X.clone()
+        T = H.shape[0]
+        k = self.gamma_k
+        self.freq.zero_()
+        for l in range(self.L):
+            Wg, Wu, WdT, _ = self.resident[l]
+            n = Wg.shape[0]
+            A, K = self.A[:T, :n], self.K[:T, :n]
+            sparse = l in self.modified
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, H, A, key_out=K if sparse else None,
+                              rms_eps=self.rms_eps)
+            if record is not None:
+                record(l, H, A)
+            if sparse:
+                B.sparse_ffn_select(K, B.KEY_U32, 0, self.alpha_k, freq=self.freq[l, :k])
+                B.sparse_ffn_select(self.freq[l, :k], B.KEY_U32, 0,
+                                    max(0, self.phi_k - self.delta_k),
+                                    include_mask=self.static_mask[l, :k],
+                                    exclude_mask=self.static_mask[l, :k],
+                                    idx_out=self.U_pos[l, :k], count_out=self.U_cnt[l:l + 1])
+            B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, A, H, accumulate=True,
+                              workspace=self.ws_dense)
+        self.compact()
+        return H
+
+    def compact(self) -> None:
+        """Per prompt: the computed set of each modified layer gathered from
+        the resident buffers (gate/up rows [|U|][2d], down output-major
+        [d][|U| rounded to 8]); dense layers use all neurons.  Reads the |U|
+        counts to the host once to size the buffers."""
+        cnt = self.U_cnt.cpu().tolist()
+        d, dev = self.d, self.s_task.device
+        self.comp = []
+        for l in range(self.L):
+            Wg, Wu, WdT, gu_res = self.resident[l]
+            if l in self.modified:
+                k = cnt[l]
+                idx = self.U_pos[l]
+                gu = torch.zeros(max(k, 1), 2 * d, dtype=torch.int16, device=dev)
+                B.sparse_ffn_compact(gu_res, idx, k, False, gu)
+                W0, W1 = gu[:k, :d], gu[:k, d:]
+            else:
+                k = self.N
+                idx = torch.arange(k, dtype=I32, device=dev)
+                W0, W1 = Wg, Wu
+            ldk = max(8, (k + 7) // 8 * 8)
+            dT = torch.zeros(d, ldk, dtype=torch.int16, device=dev)
+            B.sparse_ffn_compact(WdT, idx, k, True, dT)
+            ac = torch.zeros(ldk, dtype=F32, device=dev)
+            self.comp.append((W0, W1, dT, ac, k))
+
+    # ---------------------------------------------------------------- decode
+    def decode_gate_up(self, l: int, h: torch.Tensor) -> None:
+        W0, W1, _, ac, k = self.comp[l]
+        if k > 0:
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, W0, W1, h, ac, rms_eps=self.rms_eps)
+
+    def decode_layer(self, l: int, h: torch.Tensor) -> None:
+        self.decode_gate_up(l, h)
+        _, _, dT, ac, _ = self.comp[l]
+        B.sparse_ffn_gemv(B.OP_DOT, dT, None, ac, h, accumulate=True)
+
+    def decode(self, h: torch.Tensor) -> None:
         for l in range(self.L):
             self.decode_layer(l, h)
 

@@ -16,7 +16,9 @@ no trained weights and no dataset items are used anywhere):
   weights and row ``n`` of ``W_down^T`` is neuron n's output weights;
 * a decode token is ``x = z * s`` with z ~ N(0, I) and one per-channel scale
   vector ``s = exp(N(0, 1))`` per (workload, width), shared by all tokens of
-  that workload (heavy-tailed input columns);
+  that workload (heavy-tailed input columns); a "task" is another such scale
+  vector (tasks 1, 2, ... stand in for other prompt distributions, and a
+  cross-task calibration set is equal blocks of tokens of tasks 0, 1, 2);
 * the cluster-correlated gate of the ReLU-sparse MoE workload draws one
   centre c_k per 32-row cluster and sets row n of cluster k to
   ``0.02 * (sqrt(rho) c_k + sqrt(1 - rho) e_n)``, rho = 0.95, so the
@@ -47,6 +49,10 @@ SHAPES = {
     "c1": dict(d=3072, n=8192, layers=28, base_pct=20, alpha_pct=30,
                beta_pct=20, calib_tokens=512, prompt_tokens=256,
                decode_tokens=128),                                 # Llama3.2-3B FFN
+    "c1_loading": dict(d=3072, n=8192, layers=28, base_pct=30, loaded_pct=70,
+                       alpha_pct=30, computed_pct=40, first=5, last=-2,
+                       task_tokens=512, mixture_tokens_per_task=256,
+                       prompt_tokens=256, decode_tokens=128),      # SelectInfer Table 1
     "c2": dict(d=4096, qkv_out=(4096, 1024, 1024), d_ff=14336,
                top_pct=15, mid_pct=35),                            # Llama3.1-8B
     "c3": dict(d=4096, n=14336, experts=8, top_experts=2, layers=32,
@@ -95,15 +101,24 @@ def clustered_gate_bf16(seed: int, workload: int, layer: int, expert: int,
     return f32_to_bf16_bits(w)
 
 
-def channel_scale(seed: int, workload: int, d: int) -> np.ndarray:
-    """Per-channel lognormal(0, 1) scale, one vector per (workload, width)."""
-    return np.exp(normal_f32(seed, workload, 0, 0, T_SCALE, (d,), draw=d)).astype(np.float32)
+def channel_scale(seed: int, workload: int, d: int, task: int = 0) -> np.ndarray:
+    """Per-channel lognormal(0, 1) scale, one vector per (workload, width,
+    task); task 0 is the workload's own input distribution."""
+    return np.exp(normal_f32(seed, workload, 0, task, T_SCALE, (d,), draw=d)).astype(np.float32)
 
 
-def tokens(seed: int, workload: int, draw: int, count: int, d: int) -> np.ndarray:
-    """``count`` heavy-tailed tokens x = z * s, fp32 [count][d]."""
-    z = normal_f32(seed, workload, 0, 0, T_TOKEN, (count, d), draw=draw)
-    return (z * channel_scale(seed, workload, d)[None, :]).astype(np.float32)
+def tokens(seed: int, workload: int, draw: int, count: int, d: int, task: int = 0) -> np.ndarray:
+    """``count`` heavy-tailed tokens x = z * s, fp32 [count][d]; ``task``
+    selects the scale vector (and an independent z stream for task > 0)."""
+    z = normal_f32(seed, workload, 0, task, T_TOKEN, (count, d), draw=draw)
+    return (z * channel_scale(seed, workload, d, task)[None, :]).astype(np.float32)
+
+
+def mixture_tokens(seed: int, workload: int, draw: int, per_task: int, d: int,
+                   tasks=(0, 1, 2)) -> np.ndarray:
+    """A cross-task calibration set: ``per_task`` tokens of each task, in
+    task blocks, fp32 [per_task * len(tasks)][d]."""
+    return np.concatenate([tokens(seed, workload, draw, per_task, d, t) for t in tasks])
 
 
 def router_logits(seed: int, workload: int, layers: int, count: int,

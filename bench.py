@@ -13,7 +13,8 @@ before timing (reported under "setup").
 
 Other workloads (--workload): c0 single layer with per-token top-50% (every
 step runs activations, keys, select, compaction and the gathered down
-product), c2 SpAx three-tier QKV + down read, c3 ReLU-sparse MoE stack (32
+product), c1-loading the same stack with SelectInfer's Table 1 knobs
+(selective loading to 70%, 40% computed, layers 5..25 modified), c2 SpAx three-tier QKV + down read, c3 ReLU-sparse MoE stack (32
 layers x 8 experts, top-2, 32-row clusters), c4 batched decode with a
 per-token top-40% union contracted on MFMA (--batch 1/4/8/16).
 
@@ -54,7 +55,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=128)
     p.add_argument("--warmup", type=int, default=16)
-    p.add_argument("--workload", default="c1", choices=["c0", "c1", "c2", "c3", "c4"])
+    p.add_argument("--workload", default="c1",
+                   choices=["c0", "c1", "c1-loading", "c2", "c3", "c4"])
     p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
     p.add_argument("--weight-aware", action="store_true",
                    help="workload c2: rank columns by |x_j| * ||W[:, j]||_2 (WiSparse)")
@@ -258,6 +260,109 @@ def run_c1(args, torch, B, synth, P, T):
                                     glu_total / L, glu_us,
                                     measured_traffic("rowop_glu_selectinfer_decode",
                                                      ["rowop_b1.hip", "sffn_device.h"])),
+                  cpu_baseline=cpu)
+
+
+# ============================================================ c1-loading: SelectInfer Table 1 knobs
+
+def run_c1_loading(args, torch, B, synth, P, T):
+    cfg = synth.SHAPES["c1_loading"]
+    L, N, d = cfg["layers"], cfg["n"], cfg["d"]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    layers = synth.ffn_stack(args.seed, synth.W_C1, L, N, d, threads=min(16, os.cpu_count() or 1))
+    dev_layers = [tuple(P.to_device_bf16(m, dev) for m in lay) for lay in layers]
+    log(f"weights: {L} layers x 3 x [{N} x {d}] bf16 in {time.perf_counter() - t0:.1f} s")
+    pc = lambda k: P.pct_count(cfg[k], N)  # noqa: E731
+    stack = P.SelectInferLoadedStack(dev_layers, pc("base_pct"), pc("loaded_pct"), pc("alpha_pct"),
+                                     pc("computed_pct"), first=cfg["first"], last=cfg["last"],
+                                     max_tokens=max(cfg["task_tokens"], cfg["prompt_tokens"],
+                                                    3 * cfg["mixture_tokens_per_task"]))
+    del dev_layers
+    Xt = torch.from_numpy(synth.tokens(args.seed, synth.W_C1, 11, cfg["task_tokens"], d)).to(dev)
+    Xm = torch.from_numpy(synth.mixture_tokens(args.seed, synth.W_C1, 12,
+                                               cfg["mixture_tokens_per_task"], d)).to(dev)
+    Xp = torch.from_numpy(synth.tokens(args.seed, synth.W_C1, 13, cfg["prompt_tokens"], d)).to(dev)
+    n_tok = args.warmup + args.steps
+    Xd_host = synth.tokens(args.seed, synth.W_C1, 14, n_tok, d)
+    Xd = torch.from_numpy(Xd_host).to(dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+    torch.cuda.synchronize()
+    e0.record()
+    stack.profile(Xt, Xm)
+    e1.record()
+    stack.load()
+    e2.record()
+    stack.release_full_weights()
+    stack.prefill(Xp)          # includes the per-prompt compaction
+    e3.record()
+    torch.cuda.synchronize()
+    profile_ms, load_ms, prefill_ms = e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3)
+    ks = [stack.comp[l][4] for l in range(L)]
+    n_mod = len(stack.modified)
+    resident = sum((stack.gamma_k if l in stack.modified else N) * 3 * d * 2 for l in range(L))
+    log(f"profile {profile_ms:.1f} ms, load {load_ms:.1f} ms, prefill + compaction "
+        f"{prefill_ms:.1f} ms; computed per layer {sorted(set(ks))}; resident FFN "
+        f"{resident / 1e9:.2f} GB of {L * N * 3 * d * 2 / 1e9:.2f} GB")
+    step_bytes = int(sum(glu_bytes(k, d) + down_bytes(k, d) for k in ks))
+    glu_total = int(sum(glu_bytes(k, d) for k in ks))
+
+    h = torch.zeros(d, dtype=torch.float32, device=dev)
+    xcur = torch.zeros(d, dtype=torch.float32, device=dev)
+
+    def step():
+        h.copy_(xcur)
+        stack.decode(h)
+
+    g = T.capture(step)
+    for t in range(args.warmup):
+        xcur.copy_(Xd[t])
+        g.replay()
+    torch.cuda.synchronize()
+    total_ms = T.replay_ms(g, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
+    us_tok = total_ms * 1e3 / args.steps
+    log(f"decode: {us_tok:.1f} us/token over {args.steps} steps")
+    gg = T.capture(lambda: [stack.decode_gate_up(l, h) for l in range(L)])
+    glu_us = T.replay_ms(gg, args.steps) * 1e3 / (args.steps * L)
+    log(f"gate/up (28 launches, mixed sizes): {glu_us:.2f} us/launch")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        U_pos, U_cnt = stack.U_pos.cpu().numpy(), stack.U_cnt.cpu().numpy()
+        load_idx = stack.load_idx.cpu().numpy()
+        ids = [load_idx[l][U_pos[l, :U_cnt[l]]] if l in stack.modified else np.arange(N)
+               for l in range(L)]
+
+        def one(i):
+            hh = Xd_host[i % Xd_host.shape[0]].astype(np.float64)
+            for l, (Wg, Wu, WdT) in enumerate(layers):
+                _, y = oracle.decode_over_set(Wg, Wu, WdT, oracle.rms_normalize(hh, P.RMS_EPS),
+                                              ids[l])
+                hh = hh + y
+
+        s, n = timed_cpu(one, args.cpu_seconds)
+        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
+                   sample=f"{n} decode token(s) x 28 layers over the same computed sets, numpy fp64")
+
+    config = {"workload": "SelectInfer 28-layer FFN stack, Llama3.2-3B shape, Table 1 knobs: layers "
+                          "5..25 loaded selectively (base 30% by task-specific Eq (1) scores + "
+                          "secondary by cross-task scores up to 70% resident) and computed over "
+                          "40% (base + the most frequent of each prompt token's top 30% of loaded "
+                          "neurons), layers 0-4 and 26-27 dense; decode at batch 1",
+              "layers": L, "modified_layers": n_mod, "d_model": d, "d_ff": N, "batch": 1,
+              "computed_per_modified_layer": stack.comp[min(stack.modified)][4],
+              "resident_ffn_bytes": resident, "full_ffn_bytes": L * N * 3 * d * 2}
+    return result(us_tok, "us/token", args.steps, args.warmup, total_ms / args.steps, config,
+                  step_bytes=step_bytes,
+                  step_GBps=round(step_bytes / (us_tok * 1e-6) / 1e9, 1),
+                  step_frac_of_peak=round(step_bytes / (us_tok * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  setup={"profile_ms": round(profile_ms, 2), "load_ms": round(load_ms, 2),
+                         "prefill_ms": round(prefill_ms, 2)},
+                  roofline=roofline("rowop_wave_kernel<GLU> (gate/up of every layer, mean launch)",
+                                    glu_total / L, glu_us),
                   cpu_baseline=cpu)
 
 
@@ -599,7 +704,8 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     T = Timer(torch)
-    run = {"c0": run_c0, "c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4}[args.workload]
+    run = {"c0": run_c0, "c1": run_c1, "c1-loading": run_c1_loading, "c2": run_c2, "c3": run_c3,
+           "c4": run_c4}[args.workload]
     out = run(args, torch, B, synth, P, T)
 
     # A plain device copy of known size: the reference that scales the HBM

@@ -91,7 +91,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 6
+#define SFFN_ABI_VERSION 7
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -143,6 +143,15 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  *                 among them); not allowed with SFFN_KEY_F32.
  *  include_mask : nullable uint8 [n]; nonzero entries are OR-ed into every
  *                 row's selection (union with a static set, [SelectInfer] §5).
+ *  exclude_mask : nullable uint8 [n]; nonzero entries take no part in the
+ *                 ranking (ranks count among the others).  With the same
+ *                 mask as include_mask and [0, k) the result is the set plus
+ *                 the k best-ranked entries outside it: the secondary neurons
+ *                 added to the base neurons until the loading budget is met
+ *                 ([SelectInfer] §4, Fig 6), and the dynamic neurons added to
+ *                 the static ones until the computed fraction is reached
+ *                 (§5).  An entry in both masks is selected through the
+ *                 include mask only (not in idx_top_out).
  *  mask_out     : nullable uint8 [rows][ld_mask], 1 = selected, 0 otherwise.
  *  idx_out      : nullable int32 [rows][ld_idx]: selected indices, ascending.
  *                 ld_idx >= n if include_mask is set, else >= r_hi - r_lo.
@@ -160,6 +169,7 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
                               int rows, int n, int ld,
                               int cluster, int r_lo, int r_hi, int nonzero_only,
                               const uint8_t* include_mask,
+                              const uint8_t* exclude_mask,
                               uint8_t* mask_out, int ld_mask,
                               int32_t* idx_out, int ld_idx,
                               int32_t* count_out,
@@ -278,6 +288,23 @@ sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const i
 sffn_status sparse_ffn_compact(const uint16_t* W, int n_rows, int d, int ld_w,
                                const int32_t* idx, int k, int transpose,
                                uint16_t* out, int ld_out, void* stream);
+
+/*
+ * sparse_ffn_gather -- dst[i] = src[idx[i]] for 4-byte elements (fp32,
+ * uint32 or int32), i < min(*count, k_max) (k_max if count is NULL); the
+ * rest of dst is untouched.  It carries per-neuron values into the
+ * positions of a compacted subset: the index remap of a selectively loaded
+ * layer ([SelectInfer] §4), whose resident weights keep only the loaded
+ * neurons in ascending order, so that e.g. the base set can be ranked again
+ * in the loaded positions, or positions mapped back to neuron ids.
+ *  src   : device [n_src], n_src >= 1.
+ *  idx   : device int32 [k_max]; an index outside [0, n_src) reads the
+ *          nearest valid element (a precondition violation, not an error).
+ *  count : nullable device int32 [1].
+ *  dst   : device [k_max].  All 4-byte aligned; k_max >= 0.
+ */
+sffn_status sparse_ffn_gather(const void* src, int n_src, const int32_t* idx,
+                              const int32_t* count, int k_max, void* dst, void* stream);
 
 /*
  * Bytes of one middle-tier column record for d_out outputs in n_seg output

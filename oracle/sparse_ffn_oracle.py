@@ -236,6 +236,50 @@ def union(*sets) -> np.ndarray:
     return np.unique(np.concatenate([np.asarray(s, dtype=np.int64) for s in sets])).astype(np.int32)
 
 
+def selective_loading(s_task: np.ndarray, s_model: np.ndarray, delta: int, gamma: int) -> tuple:
+    """SelectInfer §4 and Fig 6: the base neurons are the top ``delta`` by
+    the task-specific scores; model-specific neurons are then added in the
+    order of their scores, skipping neurons already chosen, until ``gamma``
+    neurons are loaded.  Returns (base, loaded), both ascending int32."""
+    base = rank_range(key_abs(s_task), 0, delta)
+    loaded = set(int(n) for n in base)
+    for n in rank_order(key_abs(s_model)):
+        if len(loaded) >= gamma:
+            break
+        loaded.add(int(n))
+    return base, np.array(sorted(loaded), dtype=np.int32)
+
+
+def loaded_positions(loaded: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Positions of neuron ids within the ascending loaded list (the resident
+    weights of a selectively loaded layer hold only the loaded neurons, in
+    that order).  Every id must be loaded."""
+    loaded = np.asarray(loaded, dtype=np.int64)
+    pos = np.searchsorted(loaded, np.asarray(ids, dtype=np.int64))
+    assert np.all(pos < loaded.size) and np.array_equal(loaded[pos], ids), "id not loaded"
+    return pos.astype(np.int32)
+
+
+def fill_to_phi(static: np.ndarray, counts: np.ndarray, phi: int) -> np.ndarray:
+    """SelectInfer §5: the static neurons are combined with dynamic neurons,
+    taken in the order of their prompt frequency counts (most frequent
+    first, ties to the lower index), until ``phi`` neurons are computed.
+    Returns U ascending int32 (unchanged static set if it already has phi)."""
+    U = set(int(n) for n in static)
+    for n in rank_order(np.asarray(counts).astype(np.uint32)):
+        if len(U) >= phi:
+            break
+        U.add(int(n))
+    return np.array(sorted(U), dtype=np.int32)
+
+
+def modified_layers(n_layers: int, first: int, last: int) -> range:
+    """SelectInfer Table 1 layer range: layers first .. n_layers + last - 1
+    (last <= 0 counts from the end; -2 skips the last two) are loaded and
+    computed selectively, the others densely."""
+    return range(first, n_layers + last if last <= 0 else last)
+
+
 def decode_over_set(Wg, Wu, WdT, h, U):
     """A decode token at one layer computing only neurons in U: returns
     (a32 over U, y) with y = sum_{n in U} a_n W_down^T[n]."""

@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 6
+    assert L.sffn_abi_version() == 7
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -56,9 +56,9 @@ def status_and_msg(L, rc):
 
 def select(L, keys=FAKE, key_type=0, rows=1, n=8, ld=8, cluster=1, r_lo=0, r_hi=4, nz=0,
            include=NULL, mask=NULL, ld_mask=0, idx=NULL, ld_idx=0, count=NULL, idx_top=NULL,
-           ld_idx_top=0, count_top=NULL, freq=NULL, scale=NULL):
+           ld_idx_top=0, count_top=NULL, freq=NULL, scale=NULL, exclude=NULL):
     return status_and_msg(L, L.sparse_ffn_select(keys, key_type, scale, rows, n, ld, cluster, r_lo,
-                                                 r_hi, nz, include, mask, ld_mask, idx, ld_idx,
+                                                 r_hi, nz, include, exclude, mask, ld_mask, idx, ld_idx,
                                                  count, idx_top, ld_idx_top, count_top, freq, NULL))
 
 
@@ -231,6 +231,19 @@ def test_compact_validation(L):
     assert rc == 1 and "ld_out" in msg
     rc, msg = status_and_msg(L, cp(FAKE, 100, 64, 64, NULL, 10, 1, FAKE, 16, NULL))
     assert rc == 1 and "idx" in msg
+
+
+def test_gather_validation(L):
+    g = L.sparse_ffn_gather
+    rc, msg = status_and_msg(L, g(FAKE, 0, FAKE, NULL, 4, FAKE, NULL))
+    assert rc == 1 and "n_src" in msg
+    rc, msg = status_and_msg(L, g(FAKE, 10, FAKE, NULL, -1, FAKE, NULL))
+    assert rc == 1 and "k_max" in msg
+    rc, msg = status_and_msg(L, g(FAKE, 10, NULL, NULL, 4, FAKE, NULL))
+    assert rc == 1 and "non-null" in msg
+    rc, msg = status_and_msg(L, g(FAKE, 10, FAKE, ctypes.c_void_p(0x1002), 4, FAKE, NULL))
+    assert rc == 1 and "aligned" in msg
+    assert g(FAKE, 10, NULL, NULL, 0, FAKE, NULL) == 0     # nothing to gather: no launch
 
 
 def test_no_fallback_when_library_missing(monkeypatch):

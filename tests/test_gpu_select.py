@@ -206,3 +206,70 @@ def test_weight_aware_scale(n):
     for row in range(3):
         exp = oracle.rank_range(oracle.key_abs(x[row]), 0, k)
         assert gc[row] == exp.size and np.array_equal(gi[row, :gc[row]], exp), row
+
+
+@pytest.mark.parametrize("n,k_set,k_add", [(8192, 2457, 3277), (5734, 2457, 819), (7, 2, 3),
+                                           (1000, 0, 400), (1000, 300, 0), (1000, 300, 900),
+                                           (20000, 6000, 5000)])
+def test_exclude_mask_fill(n, k_set, k_add):
+    """include = exclude = a set S and ranks [0, k): S plus the k best-ranked
+    entries outside S (SelectInfer's secondary neurons / fill to phi),
+    bit-exact with the oracle's add-until-reached walk."""
+    banner(f"select exclude n={n} set={k_set} add={k_add}")
+    rng = np.random.default_rng(n + k_set + k_add)
+    for key_type in (B.KEY_ABS_F32, B.KEY_U32):
+        if key_type == B.KEY_ABS_F32:
+            keys = (rng.standard_normal(n) * np.exp(rng.standard_normal(n))).astype(np.float32)
+            keys[: n // 3] = np.round(keys[: n // 3])                  # ties, zeros
+            okeys = oracle.key_abs(keys)
+        else:
+            keys = rng.integers(0, 40, n).astype(np.uint32)            # frequency-like counts
+            okeys = keys
+        S = np.sort(rng.choice(n, size=k_set, replace=False)).astype(np.int32)
+        m = np.zeros(n, np.uint8)
+        m[S] = 1
+        md = dev(m)
+        idx = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+        mask = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        B.sparse_ffn_select(dev(keys), key_type, 0, k_add, include_mask=md, exclude_mask=md,
+                            idx_out=idx, count_out=cnt, mask_out=mask)
+        torch.cuda.synchronize()
+        exp = oracle.fill_to_phi(S, okeys, k_set + k_add)
+        c = int(host(cnt)[0])
+        assert c == exp.size and np.array_equal(host(idx)[:c], exp), key_type
+        mm = np.zeros(n, np.uint8)
+        mm[exp] = 1
+        assert np.array_equal(host(mask), mm)
+        # exclusion alone: ranks among the entries outside S
+        B.sparse_ffn_select(dev(keys), key_type, 0, k_add, exclude_mask=md, idx_out=idx,
+                            count_out=cnt)
+        torch.cuda.synchronize()
+        ok = okeys.copy()
+        elig = np.setdiff1d(np.arange(n), S)
+        order = elig[oracle.rank_order(ok[elig])][:k_add]
+        c = int(host(cnt)[0])
+        assert c == order.size and np.array_equal(host(idx)[:c], np.sort(order))
+
+
+@pytest.mark.parametrize("n_src,k", [(1, 1), (8192, 5734), (5734, 2457), (100, 0), (300, 257)])
+def test_gather(n_src, k):
+    banner(f"gather n_src={n_src} k={k}")
+    rng = np.random.default_rng(n_src + k)
+    src = rng.standard_normal(n_src).astype(np.float32)
+    idx = rng.integers(0, n_src, max(k, 1)).astype(np.int32)
+    dst = torch.full((max(k, 1) + 3,), 7.0, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_gather(dev(src), dev(idx[:k]) if k else dev(idx), dst, k_max=k)
+    torch.cuda.synchronize()
+    got = host(dst)
+    assert np.array_equal(got[:k].view(np.uint32), src[idx[:k]].view(np.uint32))
+    assert np.all(got[k:] == 7.0)
+    # device count below k_max: only the first count entries are written
+    c = k // 2
+    dst.fill_(7.0)
+    B.sparse_ffn_gather(dev(src), dev(idx), dst, count=dev(np.array([c], np.int32)),
+                        k_max=max(k, 1))
+    torch.cuda.synchronize()
+    got = host(dst)
+    assert np.array_equal(got[:c].view(np.uint32), src[idx[:c]].view(np.uint32))
+    assert np.all(got[c:] == 7.0)

@@ -122,6 +122,90 @@ def test_tier_sets_partition_and_order():
     assert np.abs(x[mid]).min() >= np.abs(x[skipped]).max()
 
 
+# ------------------------------------------------------------------ SelectInfer selective loading
+def test_selective_loading_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "selectinfer_loading_tiny.json")))
+    s_task = np.array(g["s_task"], np.float32)
+    s_model = np.array(g["s_model"], np.float32)
+    base, loaded = oracle.selective_loading(s_task, s_model, g["delta"], g["gamma"])
+    assert base.tolist() == g["expected_base"]
+    assert loaded.tolist() == g["expected_loaded"]
+    pos = oracle.loaded_positions(loaded, base)
+    assert pos.tolist() == g["expected_static_positions"]
+    counts = np.array(g["counts_over_loaded"])
+    for phi, exp in g["phi_cases"]:
+        assert oracle.fill_to_phi(pos, counts, phi).tolist() == exp, phi
+    assert loaded[oracle.fill_to_phi(pos, counts, 3)].tolist() == g["expected_ids_phi3"]
+    r = oracle.modified_layers(g["layers"], g["first"], g["last"])
+    assert [r[0], r[-1]] == g["expected_modified"] and len(r) == 21
+
+
+def brute_fill(start, values, total):
+    """Walk the entries by (|value| desc, index asc) with Python floats,
+    adding those not yet present, until ``total`` are present."""
+    chosen = sorted(set(start))
+    order = sorted(range(len(values)), key=lambda n: (-abs(float(values[n])), n))
+    for n in order:
+        if len(chosen) >= total:
+            break
+        if n not in chosen:
+            chosen = sorted(chosen + [n])
+    return chosen
+
+
+def test_selective_loading_brute_force():
+    rng = np.random.default_rng(29)
+    for trial in range(300):
+        N = int(rng.integers(1, 11))
+        s_task = rng.integers(0, 4, N).astype(np.float32) * np.float32(0.5)
+        s_model = rng.integers(0, 4, N).astype(np.float32)        # ties and zeros
+        delta = int(rng.integers(0, N + 1))
+        gamma = int(rng.integers(delta, N + 2))
+        base, loaded = oracle.selective_loading(s_task, s_model, delta, gamma)
+        exp_base = sorted(range(N), key=lambda n: (-float(s_task[n]), n))[:delta]
+        assert base.tolist() == sorted(exp_base), trial
+        assert loaded.tolist() == brute_fill(exp_base, s_model, gamma), trial
+        assert loaded.size == min(gamma, N) and np.isin(base, loaded).all()
+        counts = rng.integers(0, 3, loaded.size)
+        static = oracle.loaded_positions(loaded, base)
+        phi = int(rng.integers(0, loaded.size + 2))
+        U = oracle.fill_to_phi(static, counts, phi)
+        assert U.tolist() == brute_fill(static.tolist(), counts, phi), trial
+        assert U.size == max(static.size, min(phi, loaded.size))
+
+
+def test_selective_loading_special_cases():
+    rng = np.random.default_rng(30)
+    N = 500
+    s = (rng.random(N) * 10).astype(np.float32)
+    s2 = (rng.random(N) * 10).astype(np.float32)
+    # the same scores for both: the loaded set is the top gamma of that ranking
+    base, loaded = oracle.selective_loading(s, s, 150, 350)
+    assert np.array_equal(loaded, oracle.rank_range(oracle.key_abs(s), 0, 350))
+    # gamma = delta: only the base is loaded; gamma = N: everything
+    base, loaded = oracle.selective_loading(s, s2, 150, 150)
+    assert np.array_equal(loaded, base)
+    assert np.array_equal(oracle.selective_loading(s, s2, 150, N)[1], np.arange(N))
+    # base and secondary are disjoint and together fill gamma
+    base, loaded = oracle.selective_loading(s, s2, 150, 350)
+    sec = np.setdiff1d(loaded, base)
+    assert sec.size == 200
+    rest = np.setdiff1d(np.arange(N), loaded)
+    assert s2[sec].min() >= s2[rest].max()
+    # fill to phi: counts ranked like the static set give the plain top phi
+    static = oracle.rank_range(oracle.key_abs(s), 0, 100)
+    cnt = (s * 100).astype(np.int64)
+    assert np.array_equal(oracle.fill_to_phi(static, cnt, 180),
+                          oracle.rank_range(cnt.astype(np.uint32), 0, 180))
+    # phi below the static size leaves the static set; union of static and top-beta
+    # frequency set when no static neuron is among the frequent ones
+    assert np.array_equal(oracle.fill_to_phi(static, cnt, 50), static)
+    cnt2 = cnt.copy()
+    cnt2[static] = 0
+    U = oracle.fill_to_phi(static, cnt2, 180)
+    assert np.array_equal(U, oracle.union(static, oracle.rank_range(cnt2.astype(np.uint32), 0, 80)))
+
+
 # ------------------------------------------------------------------ WiSparse weight-aware saliency
 def test_row_norms_closed_forms():
     d = 16
