@@ -152,7 +152,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                             int ld_mask, float tau_scale, float rms_eps, const float* aux, int ld_aux,
                             const float* alpha, float* out, uint32_t* key_out, int ld_out,
                             int accumulate, void* workspace, size_t ws_bytes, void* stream) {
-  REQUIRE(op >= 0 && op <= 4, SFFN_EINVAL, "gemv: unknown op %d", op);
+  REQUIRE(op >= 0 && op <= 6, SFFN_EINVAL, "gemv: unknown op %d", op);
   REQUIRE(in && out, SFFN_EINVAL, "gemv: in and out must be non-null");
   REQUIRE(n_rows >= 0, SFFN_EINVAL, "gemv: n_rows=%d must be >= 0", n_rows);
   REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "gemv: d=%d must be a positive multiple of 8", d);
@@ -176,16 +176,32 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
   if (op != SFFN_OP_AXPY) {
     if (op != SFFN_OP_GATED)
       REQUIRE(W0 && aligned(W0, 16), SFFN_EINVAL, "gemv: W0 must be non-null and 16-byte aligned");
-    if (op == SFFN_OP_GLU_SILU || op == SFFN_OP_GATED)
+    if (op == SFFN_OP_GLU_SILU || op == SFFN_OP_GATED || op == SFFN_OP_GLU_RELU)
       REQUIRE(W1 && aligned(W1, 16), SFFN_EINVAL, "gemv: W1 must be non-null and 16-byte aligned");
+    if (op == SFFN_OP_GLU_RELU || op == SFFN_OP_PREDICT)
+      REQUIRE(batch == 1, SFFN_EUNSUPPORTED, "gemv: op %d runs at batch 1 only", op);
     REQUIRE(ld_in >= d, SFFN_EINVAL, "gemv: ld_in=%d < d=%d", ld_in, d);
     REQUIRE(ld_out >= n_rows, SFFN_EINVAL, "gemv: ld_out=%d < n_rows=%d", ld_out, n_rows);
     REQUIRE(batch > 1 || d <= 8192, SFFN_EUNSUPPORTED, "gemv: d=%d > 8192 at batch 1", d);
     REQUIRE(rms_eps >= 0.f && std::isfinite(rms_eps), SFFN_EINVAL,
             "gemv: rms_eps must be finite and >= 0");
-    if (op == SFFN_OP_DOT_RELU)
+    if (op == SFFN_OP_DOT_RELU || op == SFFN_OP_GLU_RELU)
       REQUIRE(tau_scale >= 0.f && std::isfinite(tau_scale), SFFN_EINVAL,
               "gemv: tau_scale must be finite and >= 0");
+    if (op == SFFN_OP_PREDICT) {
+      REQUIRE(tau_scale > 0.f && tau_scale < 1.f, SFFN_EINVAL,
+              "gemv: PREDICT takes a probability threshold in (0, 1) as tau_scale");
+      REQUIRE(!accumulate, SFFN_EINVAL, "gemv: PREDICT does not accumulate");
+      if (aux) REQUIRE(ld_aux >= n_rows && aligned(aux, 4), SFFN_EINVAL,
+                       "gemv: PREDICT bias needs ld_aux >= n_rows and 4-byte alignment");
+      // sigmoid(z) > theta  <=>  z > ln(theta / (1 - theta)); with t the
+      // largest fp32 not above that logit, an fp32 z exceeds the exact logit
+      // exactly when z > t.
+      const double exact = std::log((double)tau_scale / (1.0 - (double)tau_scale));
+      float t = (float)exact;
+      if ((double)t > exact) t = std::nextafter(t, -INFINITY);
+      tau_scale = t;
+    }
     if (op == SFFN_OP_GATED) {
       REQUIRE(aux != nullptr, SFFN_EINVAL, "gemv: GATED needs aux");
       REQUIRE(ld_aux >= n_rows, SFFN_EINVAL, "gemv: ld_aux=%d < n_rows=%d", ld_aux, n_rows);

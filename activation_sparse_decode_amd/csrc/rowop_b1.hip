@@ -8,6 +8,14 @@
 // Skipped neurons are never read.  The optional RMSNorm of x scales the
 // reduced dot products (W.(x s) = s (W.x)).
 //
+// Two ops serve the predictor-driven ReLU-sparse FFN (PowerInfer-2 guide,
+// "Online Predictor"): PREDICT computes the cluster logits z = W x + b of
+// the linear predictor and keys the clusters whose activation probability
+// sigmoid(z) exceeds the threshold (the host passes the equivalent fp32
+// logit threshold) so one selection compacts them; GLU_RELU computes the
+// thresholded ReGLU max(W_g x - tau, 0) * (W_u x) of the predicted rows in
+// one pass over both matrices.
+//
 // Rows up to 5120 wide (every shape of the workloads here) take the
 // wave-per-row kernel: a wave owns whole rows, lane l the 16-byte chunks l,
 // l+64, ... (NCH of them) of each, so one wave instruction reads 1 KiB of a
@@ -24,7 +32,15 @@
 
 namespace sffn {
 
-enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4 };
+enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4, kOpGluRelu = 5, kOpPredict = 6 };
+
+// Key of a row-op value: the magnitude key, or for PREDICT the order-
+// preserving key of a logit above the threshold (nonzero) and 0 otherwise.
+template <int OP>
+__device__ __forceinline__ uint32_t out_key(float v, float thr) {
+  if (OP == kOpPredict) return v > thr ? key_signed(v) : 0u;
+  return key_abs(v);
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -45,7 +61,7 @@ constexpr int kWaveMaxChunks = 10;   // 16-byte chunks per lane: rows up to 5120
 template <int OP, int NCH>
 __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
   constexpr bool kUse0 = OP != kOpGated;
-  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated;
+  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated || OP == kOpGluRelu;
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * (int)(blockDim.x >> 6) + wave_id();
   const int W = gridDim.x * (int)(blockDim.x >> 6);
@@ -77,6 +93,10 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     const float* pp = a.accumulate ? a.out + lane_row : a.x;
     lane_pv = *pp;
     if (OP == kOpGated) lane_av = a.aux[lane_row];
+    if (OP == kOpPredict) {   // bias, if any (the load is unconditional)
+      const float b = *(a.aux ? a.aux + lane_row : a.x);
+      lane_av = a.aux ? b : 0.f;
+    }
   }
 
   // x is requested first but consumed only after the first row's weights
@@ -123,7 +143,7 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     xr[j][6] = xq[j].z * m; xr[j][7] = xq[j].w * m;
   }
   float inv = 1.f, tau = 0.f;
-  if (OP == kOpDotRelu || a.rms_eps > 0.f) {
+  if (OP == kOpDotRelu || OP == kOpGluRelu || a.rms_eps > 0.f) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -163,12 +183,16 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
         v = fmaxf(g - tau, 0.f);
       } else if (OP == kOpGated) {
         v = av * u;
+      } else if (OP == kOpGluRelu) {
+        v = fmaxf(g - tau, 0.f) * u;
+      } else if (OP == kOpPredict) {
+        v = g + av;
       } else {
         v = g;
       }
       if (a.accumulate) v += pv;
       a.out[r] = v;
-      if (a.key_out) a.key_out[r] = key_abs(v);
+      if (a.key_out) a.key_out[r] = out_key<OP>(v, a.tau_scale);
     }
     if (++k >= its) break;
     r = row_of(k);
@@ -212,7 +236,7 @@ static hipError_t launch_wave_op(const RowOpArgs& a, hipStream_t s) {
 template <int OP, int CPT, int NPI>
 __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
   constexpr bool kUse0 = OP != kOpGated;
-  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated;
+  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated || OP == kOpGluRelu;
   constexpr int kVals = (kUse0 && kUse1) ? 2 : 1;   // dot products per row
   __shared__ float red[2][16][NPI * kVals];            // [parity][wave][row*vals]
   __shared__ float sq_red[16];
@@ -276,7 +300,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
     return a.idx[q] * a.group + (it - q * a.group);
   };
 
-  const bool need_norm = OP == kOpDotRelu || a.rms_eps > 0.f;
+  const bool need_norm = OP == kOpDotRelu || OP == kOpGluRelu || a.rms_eps > 0.f;
   bool have_norm = false;
   float tau = 0.f, inv = 1.f;
   int parity = 0;
@@ -385,12 +409,16 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
         v = fmaxf(g - tau, 0.f);
       } else if (OP == kOpGated) {
         v = a.aux[r] * u;
+      } else if (OP == kOpGluRelu) {
+        v = fmaxf(g - tau, 0.f) * u;
+      } else if (OP == kOpPredict) {
+        v = g + (a.aux ? a.aux[r] : 0.f);
       } else {
         v = g;
       }
       if (a.accumulate) v += pv;
       a.out[r] = v;
-      if (a.key_out) a.key_out[r] = key_abs(v);
+      if (a.key_out) a.key_out[r] = out_key<OP>(v, a.tau_scale);
     }
     parity ^= 1;   // the next iteration writes the other LDS half
     if (more) {
@@ -429,7 +457,7 @@ static hipError_t launch_op(const RowOpArgs& a, hipStream_t s) {
   // Measured on MI355X at the 28-layer stack shapes: two 16-byte chunks per
   // thread per row (128-320-thread workgroups), one row (GLU: one neuron)
   // per iteration, at most 1024 (GLU) / 2048 (single matrix) workgroups.
-  const long cap = OP == kOpGlu ? 1024 : 2048;
+  const long cap = (OP == kOpGlu || OP == kOpGluRelu) ? 1024 : 2048;
   return launch_cfg<OP, 2, 1>(a, s, cap);    // nchunk <= 1024 (d <= 8192)
 }
 
@@ -438,6 +466,8 @@ hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s) {
     case kOpGlu: return launch_op<kOpGlu>(a, s);
     case kOpDotRelu: return launch_op<kOpDotRelu>(a, s);
     case kOpGated: return launch_op<kOpGated>(a, s);
+    case kOpGluRelu: return launch_op<kOpGluRelu>(a, s);
+    case kOpPredict: return launch_op<kOpPredict>(a, s);
     default: return launch_op<kOpDot>(a, s);
   }
 }

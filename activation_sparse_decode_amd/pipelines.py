@@ -14,6 +14,8 @@ attributes so tests can compare every stage.
 * :class:`TieredProjection`    SpAx three-tier read (abstract, Fig 2-4)
 * :class:`ReluMoEStack`        ReLU-sparse MoE with 32-row clusters
   (PowerInfer-2 guide, neuron clusters) and top-2 routing
+* :class:`PredictedMoEStack`   the same stack with an online cluster predictor
+  per layer and expert (PowerInfer-2 guide, "Online Predictor")
 * :class:`BatchedUnionLayer`   batched decode: per-token top-k, union
   gathered once and contracted on MFMA
 """
@@ -475,6 +477,80 @@ class ReluMoEStack:
         return self._expert_streams[:k]
 
     def decode(self, h: torch.Tensor, t: int, record=None) -> None:
+        for l in range(self.L):
+            self.layer(l, t, h, record)
+
+
+class PredictedMoEStack(ReluMoEStack):
+    """The ReLU-sparse MoE stack with an online cluster predictor per layer
+    and expert (PowerInfer-2 guide, "Online Predictor"): the clusters of
+    layer l's routed experts are those with sigmoid(W_pred x + b) > theta,
+    x the (normalised) FFN input of layer l - 1 (of layer 0 for layer 0).
+    The lookahead runs on a stream of its own while layer l - 1 computes;
+    each layer then reads gate, up and down rows of its predicted clusters
+    only (no dense gate).  The predictors here are random: the stack shows
+    the cost of the structure, not a trained predictor's accuracy."""
+
+    def __init__(self, experts, predictors, cluster: int, tau_scale: float, theta: float,
+                 top_k: int = 2, rms_eps: float = RMS_EPS):
+        super().__init__(experts, cluster, tau_scale, top_k, rms_eps)
+        self.predictors = predictors     # [L][E] of (W_pred bf16 [clusters][d], bias fp32 [clusters])
+        self.theta = theta
+        dev = experts[0][0][0].device
+        nc = self.nc
+        self.z = torch.zeros(2, top_k, nc, dtype=F32, device=dev)      # logits, by layer parity
+        self.zkey = torch.zeros(2, top_k, nc, dtype=I32, device=dev)
+        self.pidx = torch.zeros(2, top_k, nc, dtype=I32, device=dev)   # predicted clusters
+        self.pcnt = torch.zeros(2, top_k, dtype=I32, device=dev)
+
+    def predict(self, l: int, t: int, h: torch.Tensor) -> None:
+        """Predicted clusters of layer l's routed experts from h (on the
+        current stream) into buffer l % 2."""
+        buf = l & 1
+        for j, e in enumerate(self.route_host[l * self.T + t]):
+            Wp, bp = self.predictors[l][e]
+            B.sparse_ffn_gemv(B.OP_PREDICT, Wp, None, h, self.z[buf, j], aux=bp,
+                              tau_scale=self.theta, key_out=self.zkey[buf, j], rms_eps=self.rms_eps)
+            B.sparse_ffn_select(self.zkey[buf, j], B.KEY_U32, 0, self.nc, nonzero_only=True,
+                                idx_out=self.pidx[buf, j], count_out=self.pcnt[buf, j:j + 1])
+
+    def layer(self, l: int, t: int, h: torch.Tensor, record=None) -> None:
+        """One layer for token t: the lookahead prediction for layer l + 1
+        and each routed expert's ReGLU over its predicted clusters run on
+        forked streams; then both down products, weighted by the router, in
+        one gathered product added to h."""
+        row = l * self.T + t
+        chosen = self.route_host[row]
+        cur = l & 1
+        main = torch.cuda.current_stream()
+        streams = self._streams(len(chosen) + 1)
+        for s in streams:
+            s.wait_stream(main)
+        if l + 1 < self.L:
+            with torch.cuda.stream(streams[-1]):
+                self.predict(l + 1, t, h)
+        for j, e in enumerate(chosen):
+            Wg, Wu, _ = self.experts[l][e]
+            with torch.cuda.stream(streams[j]):
+                B.sparse_ffn_gemv(B.OP_GLU_RELU, Wg, Wu, h, self.a[j], idx=self.pidx[cur, j],
+                                  count=self.pcnt[cur, j:j + 1], k_max=self.nc,
+                                  group=self.cluster, tau_scale=self.tau_scale,
+                                  rms_eps=self.rms_eps)
+        if record is not None:
+            torch.cuda.synchronize()
+            record(l, t, h, chosen)
+        for s in streams:
+            main.wait_stream(s)
+        k = len(chosen)
+        B.sparse_ffn_gemv_lists([self.experts[l][e][2] for e in chosen],
+                                [self.a[j] for j in range(k)], [self.pidx[cur, j] for j in range(k)],
+                                [self.pcnt[cur, j:j + 1] for j in range(k)], [self.nc] * k, h,
+                                group=self.cluster,
+                                alphas=[self.route_w[row, j:j + 1] for j in range(k)],
+                                accumulate=True, workspace=self.ws)
+
+    def decode(self, h: torch.Tensor, t: int, record=None) -> None:
+        self.predict(0, t, h)
         for l in range(self.L):
             self.layer(l, t, h, record)
 

@@ -24,7 +24,10 @@ no trained weights and no dataset items are used anywhere):
   ``0.02 * (sqrt(rho) c_k + sqrt(1 - rho) e_n)``, rho = 0.95, so the
   marginal of every entry is still N(0, 0.02^2) while neurons of a cluster
   fire together;
-* router logits are N(0, 1) per (layer, token, expert).
+* router logits are N(0, 1) per (layer, token, expert);
+* an (untrained) cluster predictor is a bf16 N(0, 0.02^2) matrix [clusters][d]
+  with one constant bias, set so that a fraction ``frac`` of the clusters is
+  predicted for an RMS-normalised input (logit ~ N(b, (0.02 sqrt(d))^2)).
 """
 
 from __future__ import annotations
@@ -38,7 +41,7 @@ import numpy as np
 W_C0, W_C1, W_C2, W_C3, W_C4 = 0, 1, 2, 3, 4
 
 # tensor ids
-T_GATE, T_UP, T_DOWN, T_TOKEN, T_SCALE, T_ROUTER, T_QKV, T_CENTRE = range(8)
+T_GATE, T_UP, T_DOWN, T_TOKEN, T_SCALE, T_ROUTER, T_QKV, T_CENTRE, T_PRED = range(9)
 
 WEIGHT_STD = 0.02
 CLUSTER_RHO = 0.95
@@ -57,7 +60,7 @@ SHAPES = {
                top_pct=15, mid_pct=35),                            # Llama3.1-8B
     "c3": dict(d=4096, n=14336, experts=8, top_experts=2, layers=32,
                cluster=32, zero_frac_quantile=1.2815515655446004,
-               decode_tokens=128),                                 # TurboSparse-Mixtral
+               decode_tokens=128, pred_theta=0.45, pred_frac=0.2),  # TurboSparse-Mixtral
     "c4": dict(d=5120, n=17408, keep_pct=40, batches=(1, 4, 8, 16)),  # Qwen-27B-like
 }
 
@@ -119,6 +122,16 @@ def mixture_tokens(seed: int, workload: int, draw: int, per_task: int, d: int,
     """A cross-task calibration set: ``per_task`` tokens of each task, in
     task blocks, fp32 [per_task * len(tasks)][d]."""
     return np.concatenate([tokens(seed, workload, draw, per_task, d, t) for t in tasks])
+
+
+def predictor_bias(n_clusters: int, d: int, theta: float, frac: float) -> np.ndarray:
+    """Constant fp32 bias b of a random predictor: with weights N(0, 0.02^2)
+    and an input of norm sqrt(d), a logit is ~N(b, (0.02 sqrt(d))^2), and
+    P(logit > ln(theta / (1 - theta))) = frac for
+    b = ln(theta / (1 - theta)) - Phi^-1(1 - frac) * 0.02 * sqrt(d)."""
+    from statistics import NormalDist
+    b = math.log(theta / (1.0 - theta)) - NormalDist().inv_cdf(1.0 - frac) * WEIGHT_STD * math.sqrt(d)
+    return np.full(n_clusters, b, dtype=np.float32)
 
 
 def router_logits(seed: int, workload: int, layers: int, count: int,

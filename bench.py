@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--workload", default="c1",
                    choices=["c0", "c1", "c1-loading", "c2", "c3", "c4"])
     p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
+    p.add_argument("--predictor", action="store_true",
+                   help="workload c3: clusters from an online predictor (PowerInfer-2), no dense gate")
     p.add_argument("--weight-aware", action="store_true",
                    help="workload c2: rank columns by |x_j| * ||W[:, j]||_2 (WiSparse)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -548,7 +550,15 @@ def run_c3(args, torch, B, synth, P, T):
     logits = torch.from_numpy(synth.router_logits(args.seed, synth.W_C3, L, steps, E)).to(dev)
     X_host = synth.tokens(args.seed, synth.W_C3, 1, steps, d)
     X = torch.from_numpy(X_host).to(dev)
-    moe = P.ReluMoEStack(experts, S, tau_scale=cfg["zero_frac_quantile"] * synth.WEIGHT_STD)
+    tau_scale = cfg["zero_frac_quantile"] * synth.WEIGHT_STD
+    nc = N // S
+    if args.predictor:
+        bias = torch.from_numpy(synth.predictor_bias(nc, d, cfg["pred_theta"], cfg["pred_frac"])).to(dev)
+        preds = [[(synth.torch_weight_bf16(args.seed, synth.W_C3, l, e, synth.T_PRED, nc, d, dev),
+                   bias) for e in range(E)] for l in range(L)]
+        moe = P.PredictedMoEStack(experts, preds, S, tau_scale=tau_scale, theta=cfg["pred_theta"])
+    else:
+        moe = P.ReluMoEStack(experts, S, tau_scale=tau_scale)
     moe.route(logits)
     h = torch.zeros(d, dtype=torch.float32, device=dev)
 
@@ -559,7 +569,7 @@ def run_c3(args, torch, B, synth, P, T):
         h.copy_(X[t])
 
         def rec(l, tt, hh, chosen, t=t):
-            counts[t, l] = moe.ccnt.cpu().numpy()
+            counts[t, l] = (moe.pcnt[l & 1] if args.predictor else moe.ccnt).cpu().numpy()
         moe.decode(h, t, record=rec)
     graphs = [T.capture(lambda t=t: (h.copy_(X[t]), moe.decode(h, t))) for t in range(steps)]
     for g in graphs[:2]:
@@ -573,19 +583,42 @@ def run_c3(args, torch, B, synth, P, T):
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     us_tok = total_ms * 1e3 / steps
-    gate_b = N * d * 2 + 4 * d + 4 * N
-    clus_b = 2 * S * d * 2 + 3 * 4 * S          # up + down rows, r read, a written and read
-    step_b = int(L * 2 * (gate_b + 4 * (N // S)) + counts.sum(axis=(1, 2)).mean() * clus_b)
+    if args.predictor:
+        # per routed expert: predictor rows, bias, logits and keys; per
+        # predicted cluster: gate, up and down rows, a written and read
+        gate_b = nc * d * 2 + 4 * d + 3 * 4 * nc
+        clus_b = 3 * S * d * 2 + 2 * 4 * S
+    else:
+        gate_b = N * d * 2 + 4 * d + 4 * N
+        clus_b = 2 * S * d * 2 + 3 * 4 * S      # up + down rows, r read, a written and read
+    step_b = int(L * 2 * (gate_b + 4 * nc) + counts.sum(axis=(1, 2)).mean() * clus_b)
     log(f"c3: {us_tok:.1f} us/token, {step_b / 1e9:.2f} GB/token, "
-        f"active clusters {counts.mean() / (N // S):.3f}")
+        f"{'predicted' if args.predictor else 'active'} clusters {counts.mean() / nc:.3f}")
 
-    def gates_only():
-        for l in range(L):
-            for j, e in enumerate(moe.route_host[l * moe.T]):
-                B.sparse_ffn_gemv(B.OP_DOT_RELU, experts[l][e][0], None, h, moe.r[j],
-                                  tau_scale=moe.tau_scale, rms_eps=moe.rms_eps)
+    if args.predictor:
+        # dominant kernel: the ReGLU over each routed expert's predicted clusters
+        def dom():
+            for l in range(L):
+                for j, e in enumerate(moe.route_host[l * moe.T]):
+                    Wg, Wu, _ = experts[l][e]
+                    B.sparse_ffn_gemv(B.OP_GLU_RELU, Wg, Wu, h, moe.a[j], idx=moe.pidx[0, j],
+                                      count=moe.pcnt[0, j:j + 1], k_max=nc, group=S,
+                                      tau_scale=moe.tau_scale, rms_eps=moe.rms_eps)
+        moe.predict(0, 0, h)
+        torch.cuda.synchronize()
+        dom_count = int(moe.pcnt[0].sum().item())
+        dom_b = dom_count * S * (2 * d * 2 + 4) / 2 + 4 * d
+        dom_name = "rowop_wave_kernel<GLU_RELU> (gate + up over predicted clusters)"
+    else:
+        def dom():
+            for l in range(L):
+                for j, e in enumerate(moe.route_host[l * moe.T]):
+                    B.sparse_ffn_gemv(B.OP_DOT_RELU, experts[l][e][0], None, h, moe.r[j],
+                                      tau_scale=moe.tau_scale, rms_eps=moe.rms_eps)
+        dom_b = gate_b
+        dom_name = "rowop_wave_kernel<DOT_RELU> (dense expert gate)"
 
-    gate_us = T.replay_ms(T.capture(gates_only), 16) * 1e3 / (16 * L * 2)
+    gate_us = T.replay_ms(T.capture(dom), 16) * 1e3 / (16 * L * 2)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -593,27 +626,41 @@ def run_c3(args, torch, B, synth, P, T):
         l_s = [0, L // 2, L - 1]
         host = {(l, e): tuple(m.cpu().numpy().view(np.uint16) for m in experts[l][e])
                 for l in l_s for e in moe.route_host[l * moe.T]}
+        if args.predictor:
+            pred_host = {(l, e): preds[l][e][0].cpu().numpy().view(np.uint16)
+                         for l in l_s for e in moe.route_host[l * moe.T]}
+            bias_h = bias.cpu().numpy()
+            theta32 = float(np.float32(cfg["pred_theta"]))
 
         def one(i):
             l = l_s[i % len(l_s)]
             x = oracle.rms_normalize(X_host[0], P.RMS_EPS)
             tau = oracle.relu_threshold(x, cfg["zero_frac_quantile"], synth.WEIGHT_STD)
-            for e in moe.route_host[l * moe.T]:
-                oracle.relu_expert(*host[(l, e)], x, tau, S)
+            for j, e in enumerate(moe.route_host[l * moe.T]):
+                if args.predictor:
+                    Wp = pred_host[(l, e)]
+                    cl = oracle.predicted_clusters(oracle.predictor_logits(Wp, bias_h, x), theta32)
+                    oracle.predicted_expert(*host[(l, e)], x, tau, cl, S)
+                else:
+                    oracle.relu_expert(*host[(l, e)], x, tau, S)
 
         s, n = timed_cpu(one, args.cpu_seconds)
         cpu = dict(value=s * L * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} layer(s) of 2 routed experts (gate, clusters, up, down) at "
+                   sample=f"{n} layer(s) of 2 routed experts "
+                          f"({'predictor, ' if args.predictor else 'gate, '}clusters, up, down) at "
                           f"token 0, numpy fp64, scaled to {L} layers")
     config = {"workload": "ReLU-sparse MoE FFN stack, TurboSparse-Mixtral-like: 32 layers x 8 "
                           "experts (d_model 4096, d_ff 14336), top-2 router, ~90% exact zeros, "
-                          "32-row clusters, batch 1",
+                          "32-row clusters, batch 1"
+                          + ("; clusters from a random online predictor per layer and expert "
+                             "(sigmoid(W_pred h + b) > 0.45 on the previous layer's input, "
+                             "~20% of clusters), no dense gate" if args.predictor else ""),
               "layers": L, "experts": E, "batch": 1,
-              "active_cluster_frac": round(float(counts.mean() / (N // S)), 4)}
+              ("predicted_cluster_frac" if args.predictor else "active_cluster_frac"):
+                  round(float(counts.mean() / nc), 4)}
     return result(us_tok, "us/token", steps, 2, total_ms / steps, config, step_bytes=step_b,
                   step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_wave_kernel<DOT_RELU> (dense expert gate)", gate_b,
-                                    gate_us),
+                  roofline=roofline(dom_name, dom_b, gate_us),
                   cpu_baseline=cpu)
 
 

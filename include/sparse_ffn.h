@@ -82,8 +82,12 @@ typedef enum {
     SFFN_OP_DOT_RELU = 1,   /* out_n = max(W0[n].x - tau_scale*||x||_2, 0) (ReGLU gate) */
     SFFN_OP_GATED = 2,      /* out_n = aux_n * (W1[n].x)                 (ReGLU up) */
     SFFN_OP_AXPY = 3,       /* y (+)= alpha * sum_n m_n in_n W0[n][:]    (down)     */
-    SFFN_OP_DOT = 4         /* out_n = W0[n].x   (down over compacted, output-major
+    SFFN_OP_DOT = 4,        /* out_n = W0[n].x   (down over compacted, output-major
                                weights: one dot per output)                      */
+    SFFN_OP_GLU_RELU = 5,   /* out_n = max(W0[n].x - tau_scale*||x||_2, 0) * (W1[n].x)
+                               (thresholded ReGLU, both matrices in one pass)    */
+    SFFN_OP_PREDICT = 6     /* out_n = W0[n].x + aux_n (cluster logits of the online
+                               predictor); key nonzero iff sigmoid(out_n) > theta */
 } sffn_gemv_op;
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
@@ -91,7 +95,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 7
+#define SFFN_ABI_VERSION 8
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -199,6 +203,15 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
  *  sqrt(mean(x_b^2) + rms_eps) (the pre-FFN normalisation of the Llama3 and
  *  Mixtral blocks the workloads are shaped like; fused, x is not modified);
  *  rms_eps = 0 uses x as given.  AXPY requires rms_eps = 0.
+ *  GLU_RELU and PREDICT run at batch 1 only.  PREDICT ([PowerInfer-2] guide,
+ *  "Online Predictor": a linear classifier over the hidden state gives each
+ *  neuron cluster an activation probability sigmoid(W_pred h + b), and the
+ *  clusters above a threshold theta are the ones computed): W0 = W_pred
+ *  [n_clusters][ld_w], aux = the bias fp32 [n_rows] (nullable: no bias),
+ *  tau_scale = theta in (0, 1), no accumulate; out = the logits, and
+ *  key_out[n] = 0 unless sigmoid(out_n) > theta holds for the fp32 logit in
+ *  exact arithmetic, else the order-preserving key of out_n (nonzero), so a
+ *  nonzero_only selection compacts the predicted clusters.
  *
  * AXPY: W0 is W_down^T, bf16 [n_rows][ld_w] with rows of length d (the
  *  output width); in = activations fp32 [batch][ld_in] (length n_rows);

@@ -428,6 +428,41 @@ def relu_expert(Wg, Wu, WdT, h, tau: float, cluster: int) -> dict:
     return dict(r32=r32, clusters=clusters, rows=rows, a32=a32, y=y)
 
 
+def predictor_logits(Wp_bits, bias, h) -> np.ndarray:
+    """PowerInfer-2 guide, "Online Predictor": the cluster logits of the
+    single linear layer, z = W_pred h + b (fp64; bias may be None)."""
+    z = row_dots(Wp_bits, h)
+    return z if bias is None else z + np.asarray(bias, dtype=np.float64)
+
+
+def predicted_clusters(z: np.ndarray, theta: float) -> np.ndarray:
+    """PowerInfer-2 guide, "Online Predictor": the clusters whose predicted
+    activation probability sigma(z_k) exceeds the threshold theta, ascending
+    (the guide's equation writes >=, its predictor listing >; > is used:
+    the two differ only where sigma(z) equals theta exactly).  sigma is
+    increasing, so the test is taken as z_k > ln(theta / (1 - theta)): an
+    fp64 sigmoid of a tiny z rounds to exactly 1/2 and would decide theta =
+    1/2 wrongly."""
+    t = np.log(theta / (1.0 - theta))
+    return np.flatnonzero(np.asarray(z, dtype=np.float64) > t).astype(np.int32)
+
+
+def relu_glu_rows(Wg_bits, Wu_bits, h, tau: float, rows) -> np.ndarray:
+    """a_n = max(W_g[n].h - tau, 0) * (W_u[n].h) for the given rows, fp64
+    (the thresholded ReGLU of the ReLU-sparse FFN, computed only where the
+    predictor says the cluster is active)."""
+    return np.maximum(row_dots(Wg_bits, h, rows) - tau, 0.0) * row_dots(Wu_bits, h, rows)
+
+
+def predicted_expert(Wg, Wu, WdT, h, tau: float, clusters, cluster: int) -> dict:
+    """One routed expert computed over predicted clusters only: gate, up
+    and down read for the rows of those clusters (none of the dense gate);
+    y = sum over their rows of a_n W_down^T[n]."""
+    rows = expand_clusters(np.asarray(clusters, dtype=np.int64), cluster)
+    a32 = relu_glu_rows(Wg, Wu, h, tau, rows).astype(np.float32)
+    return dict(rows=rows, a32=a32, y=down_gather(WdT, rows, a32))
+
+
 # ---------------------------------------------------------------- batched decode (C4)
 
 

@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 7
+    assert L.sffn_abi_version() == 8
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -151,6 +151,22 @@ def test_gemv_validation(L):
     assert rc == 1 and "rms_eps" in msg
     rc, msg = gemv(L, op=3, eps=1e-5, ws=FAKE, ws_bytes=1 << 30)
     assert rc == 1 and "rms_eps" in msg
+    # thresholded ReGLU and the cluster predictor
+    rc, msg = gemv(L, op=5, W1=NULL, ld_out=64)
+    assert rc == 1 and "W1" in msg
+    rc, msg = gemv(L, op=5, batch=2, ld_out=64)
+    assert rc == 2 and "batch 1" in msg
+    rc, msg = gemv(L, op=5, tau=-0.5, ld_out=64)
+    assert rc == 1 and "tau" in msg
+    for theta in (0.0, 1.0, -0.2, 1.5):
+        rc, msg = gemv(L, op=6, tau=theta, ld_out=64)
+        assert rc == 1 and "probability" in msg, theta
+    rc, msg = gemv(L, op=6, tau=0.45, acc=1, ld_out=64)
+    assert rc == 1 and "accumulate" in msg
+    rc, msg = gemv(L, op=6, tau=0.45, aux=FAKE, ld_aux=10, ld_out=64)
+    assert rc == 1 and "bias" in msg
+    rc, msg = gemv(L, op=6, tau=0.45, batch=2, ld_out=64)
+    assert rc == 2 and "batch 1" in msg
 
 
 def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),

@@ -206,6 +206,78 @@ def test_selective_loading_special_cases():
     assert np.array_equal(U, oracle.union(static, oracle.rank_range(cnt2.astype(np.uint32), 0, 80)))
 
 
+# ------------------------------------------------------------------ PowerInfer-2 online predictor
+def test_predictor_logits_integer_bruteforce():
+    rng = np.random.default_rng(31)
+    W = rng.integers(-4, 5, (7, 16)).astype(np.float32)
+    h = rng.integers(-3, 4, 16).astype(np.float64)
+    b = rng.integers(-5, 6, 7).astype(np.float64)
+    got = oracle.predictor_logits(bf16(W), b, h)
+    for k in range(7):
+        assert got[k] == sum(int(W[k, i]) * int(h[i]) for i in range(16)) + int(b[k])
+    assert np.array_equal(oracle.predictor_logits(bf16(W), None, h), got - b)
+
+
+def exact_above(z: float, theta: float) -> bool:
+    """sigma(z) > theta at 60 significant digits."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        zd, td = decimal.Decimal(float(z)), decimal.Decimal(float(theta))
+        return 1 / (1 + (-zd).exp()) > td
+
+
+def test_predicted_clusters_exact_decision():
+    rng = np.random.default_rng(32)
+    for theta in (float(np.float32(0.45)), 0.5, float(np.float32(0.3)), float(np.float32(0.9))):
+        t = np.log(theta / (1 - theta))
+        near = np.float32(t)
+        z = [near]
+        for _ in range(4):                       # fp32 neighbours on both sides of the logit
+            z = [np.nextafter(z[0], np.float32(-10), dtype=np.float32)] + z + \
+                [np.nextafter(z[-1], np.float32(10), dtype=np.float32)]
+        z = np.concatenate([np.array(z, np.float32),
+                            rng.uniform(-4, 4, 200).astype(np.float32), np.float32([0.0])])
+        got = oracle.predicted_clusters(z.astype(np.float64), theta)
+        exp = [k for k in range(z.size) if exact_above(z[k], theta)]
+        assert got.tolist() == exp, theta
+    # sigma(0) = 1/2: strictly above theta = 1/2 needs z > 0
+    z = np.array([0.0, 1e-30, -1e-30], np.float64)
+    assert oracle.predicted_clusters(z, 0.5).tolist() == [1]
+    # the sets shrink as theta grows
+    z = rng.standard_normal(500)
+    prev = None
+    for theta in (0.1, 0.3, 0.45, 0.5, 0.7, 0.95):
+        cur = set(oracle.predicted_clusters(z, theta).tolist())
+        assert prev is None or cur <= prev
+        prev = cur
+
+
+def test_predicted_expert_special_cases():
+    rng = np.random.default_rng(33)
+    N, d, S = 256, 64, 32
+    Wg = synth.weight_bf16(0, 9, 1, 0, 0, N, d)
+    Wu = synth.weight_bf16(0, 9, 1, 0, 1, N, d)
+    WdT = synth.weight_bf16(0, 9, 1, 0, 2, N, d)
+    h = rng.standard_normal(d)
+    tau = oracle.relu_threshold(h, 1.2815515655446004, 0.02)
+    ref = oracle.relu_expert(Wg, Wu, WdT, h, tau, S)
+    # all clusters, or exactly the active ones: the ReLU expert's output
+    for cl in (np.arange(N // S), ref["clusters"]):
+        got = oracle.predicted_expert(Wg, Wu, WdT, h, tau, cl, S)
+        np.testing.assert_allclose(got["y"], ref["y"], rtol=1e-6, atol=1e-9)
+    # an inactive cluster contributes exactly nothing; a missed active one its own rows
+    inactive = np.setdiff1d(np.arange(N // S), ref["clusters"])
+    if inactive.size and ref["clusters"].size:
+        more = oracle.predicted_expert(Wg, Wu, WdT, h, tau, np.union1d(ref["clusters"], inactive[:1]), S)
+        act = oracle.predicted_expert(Wg, Wu, WdT, h, tau, ref["clusters"], S)
+        assert np.array_equal(more["y"], act["y"]) or np.allclose(more["y"], act["y"], rtol=1e-15)
+        assert not np.any(more["a32"][np.isin(more["rows"], oracle.expand_clusters(inactive[:1], S))])
+    # no cluster predicted: nothing computed
+    none = oracle.predicted_expert(Wg, Wu, WdT, h, tau, np.zeros(0, np.int32), S)
+    assert none["rows"].size == 0 and not np.any(none["y"])
+
+
 # ------------------------------------------------------------------ WiSparse weight-aware saliency
 def test_row_norms_closed_forms():
     d = 16
