@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_gemv_lists.restype = _i
         L.sparse_ffn_gemv_lists.argtypes = [_i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp,
                                             _vp, _i, _vp, _sz, _vp]
+        L.sparse_ffn_rowop_lists.restype = _i
+        L.sparse_ffn_rowop_lists.argtypes = [_i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                             _i, _f, _f, _vp, _vp, _vp, _i, _vp]
         L.sparse_ffn_compact.restype = _i
         L.sparse_ffn_compact.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _vp]
         L.sparse_ffn_gather.restype = _i
@@ -72,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 8:
+        if L.sffn_abi_version() != 9:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -194,6 +197,23 @@ def sparse_ffn_gather(src: torch.Tensor, idx: torch.Tensor, dst: torch.Tensor, *
     k = idx.shape[0] if k_max is None else k_max
     _check(lib().sparse_ffn_gather(_p(src), src.numel(), _p(idx), _p(count), k, _p(dst),
                                    _stream(stream)))
+
+
+def sparse_ffn_rowop_lists(op: int, W0s, W1s, x: torch.Tensor, outs, *, idxs=None, counts=None,
+                           k_maxs=None, group: int = 1, tau_scale: float = 0.0,
+                           rms_eps: float = 0.0, auxs=None, key_outs=None,
+                           accumulate: bool = False, stream=None) -> None:
+    """One row op over several row lists (batch 1): list l reads W0s[l] /
+    W1s[l] and writes outs[l] (and key_outs[l]) as sparse_ffn_gemv would."""
+    n = len(outs)
+    ptrs = lambda ts: None if ts is None else (_vp * n)(  # noqa: E731
+        *[None if t is None else t.data_ptr() for t in ts])
+    ints = lambda vs: None if vs is None else (_i * n)(*[int(v) for v in vs])  # noqa: E731
+    W = next(w for w in (list(W0s or []) + list(W1s or [])) if w is not None)
+    _check(lib().sparse_ffn_rowop_lists(
+        op, n, ptrs(W0s), ptrs(W1s), W.shape[0], W.shape[1], W.stride(0), _p(x), ptrs(idxs),
+        ptrs(counts), ints(k_maxs), group, float(tau_scale), float(rms_eps), ptrs(auxs),
+        ptrs(outs), ptrs(key_outs), int(accumulate), _stream(stream)))
 
 
 def sparse_ffn_compact(W: torch.Tensor, idx: torch.Tensor | None, k: int, transpose: bool,

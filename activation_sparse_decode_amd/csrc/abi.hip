@@ -146,6 +146,16 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
 }
 
+// sigmoid(z) > theta  <=>  z > ln(theta / (1 - theta)); with t the largest
+// fp32 not above that logit, an fp32 z exceeds the exact logit exactly when
+// z > t.
+static float logit_threshold(float theta) {
+  const double exact = std::log((double)theta / (1.0 - (double)theta));
+  float t = (float)exact;
+  if ((double)t > exact) t = std::nextafter(t, -INFINITY);
+  return t;
+}
+
 sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int n_rows, int d,
                             int ld_w, const float* in, int batch, int ld_in, const int32_t* idx,
                             const int32_t* count, int k_max, int group, const uint8_t* row_mask,
@@ -194,13 +204,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
       REQUIRE(!accumulate, SFFN_EINVAL, "gemv: PREDICT does not accumulate");
       if (aux) REQUIRE(ld_aux >= n_rows && aligned(aux, 4), SFFN_EINVAL,
                        "gemv: PREDICT bias needs ld_aux >= n_rows and 4-byte alignment");
-      // sigmoid(z) > theta  <=>  z > ln(theta / (1 - theta)); with t the
-      // largest fp32 not above that logit, an fp32 z exceeds the exact logit
-      // exactly when z > t.
-      const double exact = std::log((double)tau_scale / (1.0 - (double)tau_scale));
-      float t = (float)exact;
-      if ((double)t > exact) t = std::nextafter(t, -INFINITY);
-      tau_scale = t;
+      tau_scale = logit_threshold(tau_scale);
     }
     if (op == SFFN_OP_GATED) {
       REQUIRE(aux != nullptr, SFFN_EINVAL, "gemv: GATED needs aux");
@@ -243,6 +247,83 @@ sffn_status sparse_ffn_row_norms(const uint16_t* W, int n_rows, int d, int ld_w,
   if (n_rows == 0) return ok();
   return from_hip(sffn::launch_row_norms(W, n_rows, d, ld_w, out, (hipStream_t)stream),
                   "row_norms launch");
+}
+
+sffn_status sparse_ffn_rowop_lists(int op, int n_lists, const uint16_t* const* W0,
+                                  const uint16_t* const* W1, int n_rows, int d, int ld_w,
+                                  const float* x, const int32_t* const* idx,
+                                  const int32_t* const* count, const int* k_max, int group,
+                                  float tau_scale, float rms_eps, const float* const* aux,
+                                  float* const* out, uint32_t* const* key_out, int accumulate,
+                                  void* stream) {
+  REQUIRE(op >= 0 && op <= 6 && op != SFFN_OP_AXPY, SFFN_EINVAL,
+          "rowop_lists: op %d is not a row op", op);
+  REQUIRE(n_lists >= 1 && n_lists <= sffn::kMaxRowLists, SFFN_EINVAL,
+          "rowop_lists: n_lists=%d must be in [1, %d]", n_lists, sffn::kMaxRowLists);
+  REQUIRE(out != nullptr, SFFN_EINVAL, "rowop_lists: out (host array) must be non-null");
+  REQUIRE(x && aligned(x, 16), SFFN_EINVAL, "rowop_lists: x must be non-null, 16-byte aligned");
+  REQUIRE(n_rows >= 0, SFFN_EINVAL, "rowop_lists: n_rows=%d must be >= 0", n_rows);
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "rowop_lists: d=%d must be a positive multiple of 8", d);
+  REQUIRE(d <= 5120, SFFN_EUNSUPPORTED, "rowop_lists: d=%d > 5120", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL,
+          "rowop_lists: ld_w=%d must be >= d and a multiple of 8", ld_w);
+  REQUIRE(rms_eps >= 0.f && std::isfinite(rms_eps), SFFN_EINVAL,
+          "rowop_lists: rms_eps must be finite and >= 0");
+  const bool use0 = op != SFFN_OP_GATED;
+  const bool use1 = op == SFFN_OP_GLU_SILU || op == SFFN_OP_GATED || op == SFFN_OP_GLU_RELU;
+  REQUIRE(!use0 || W0, SFFN_EINVAL, "rowop_lists: W0 (host array) must be non-null");
+  REQUIRE(!use1 || W1, SFFN_EINVAL, "rowop_lists: W1 (host array) must be non-null");
+  REQUIRE(op != SFFN_OP_GATED || aux, SFFN_EINVAL, "rowop_lists: GATED needs aux");
+  if (idx) {
+    REQUIRE(count && k_max, SFFN_EINVAL, "rowop_lists: idx needs count and k_max (host arrays)");
+    REQUIRE(group >= 1, SFFN_EINVAL, "rowop_lists: group=%d must be >= 1", group);
+  }
+  if (op == SFFN_OP_DOT_RELU || op == SFFN_OP_GLU_RELU)
+    REQUIRE(tau_scale >= 0.f && std::isfinite(tau_scale), SFFN_EINVAL,
+            "rowop_lists: tau_scale must be finite and >= 0");
+  if (op == SFFN_OP_PREDICT) {
+    REQUIRE(tau_scale > 0.f && tau_scale < 1.f, SFFN_EINVAL,
+            "rowop_lists: PREDICT takes a probability threshold in (0, 1) as tau_scale");
+    REQUIRE(!accumulate, SFFN_EINVAL, "rowop_lists: PREDICT does not accumulate");
+    tau_scale = logit_threshold(tau_scale);
+  }
+  sffn::RowOpListsArgs L{};
+  L.base = sffn::RowOpArgs{op, nullptr, nullptr, n_rows, d, ld_w, x, 1, d, nullptr, nullptr, 0,
+                           idx ? group : 1, tau_scale, rms_eps, nullptr, n_rows, nullptr, nullptr,
+                           n_rows, accumulate ? 1 : 0};
+  L.n = n_lists;
+  long items = 0;
+  for (int l = 0; l < n_lists; ++l) {
+    if (use0) REQUIRE(W0[l] && aligned(W0[l], 16), SFFN_EINVAL,
+                      "rowop_lists: W0[%d] must be non-null and 16-byte aligned", l);
+    if (use1) REQUIRE(W1[l] && aligned(W1[l], 16), SFFN_EINVAL,
+                      "rowop_lists: W1[%d] must be non-null and 16-byte aligned", l);
+    REQUIRE(out[l] && aligned(out[l], 4), SFFN_EINVAL, "rowop_lists: out[%d] must be non-null", l);
+    if (key_out) REQUIRE(aligned(key_out[l], 4), SFFN_EINVAL, "rowop_lists: key_out[%d] misaligned", l);
+    if (aux) REQUIRE(aligned(aux[l], 4), SFFN_EINVAL, "rowop_lists: aux[%d] misaligned", l);
+    if (op == SFFN_OP_GATED) REQUIRE(aux[l] != nullptr, SFFN_EINVAL, "rowop_lists: aux[%d] is null", l);
+    if (idx) {
+      REQUIRE(idx[l] && count[l] && aligned(idx[l], 4) && aligned(count[l], 4), SFFN_EINVAL,
+              "rowop_lists: idx[%d] / count[%d] must be non-null and 4-byte aligned", l, l);
+      REQUIRE(k_max[l] >= 0 && (long)k_max[l] * group <= n_rows, SFFN_EINVAL,
+              "rowop_lists: k_max[%d]=%d * group=%d exceeds n_rows=%d", l, k_max[l], group, n_rows);
+      items += (long)k_max[l] * group;
+    } else {
+      items += n_rows;
+    }
+    L.W0[l] = use0 ? W0[l] : nullptr;
+    L.W1[l] = use1 ? W1[l] : (use0 ? W0[l] : nullptr);
+    L.idx[l] = idx ? idx[l] : nullptr;
+    L.count[l] = idx ? count[l] : nullptr;
+    L.k_max[l] = idx ? k_max[l] : 0;
+    L.aux[l] = aux ? aux[l] : nullptr;
+    L.out[l] = out[l];
+    L.key_out[l] = key_out ? key_out[l] : nullptr;
+  }
+  if (!use0)
+    for (int l = 0; l < n_lists; ++l) L.W0[l] = W1[l];   // GATED reads W1 only
+  if (items == 0) return ok();
+  return from_hip(sffn::launch_rowop_lists(L, (hipStream_t)stream), "rowop_lists launch");
 }
 
 sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const int* n_rows,

@@ -204,10 +204,14 @@ template <int OP, int NCH>
 static hipError_t launch_wave(const RowOpArgs& a, hipStream_t s) {
   // Workgroups of four waves, a multiple of 256 of them (the same number on
   // every CU): 256 up to ~3000 rows, doubling per doubling of the rows up to
-  // 2048; at most 64 rows per wave.
+  // 2048; at most 64 rows per wave.  A gathered launch is sized by its bound
+  // k_max while the device count is often a fraction of it (MoE clusters:
+  // ~20%): it takes at most 512 (measured on 2 x ~90 of 448 clusters of
+  // 14336 x 4096 experts: 10.7 us at 512 vs 13.7 us at 2048 workgroups).
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
   long blocks = 256;
   while (blocks < 2048 && items >= 6 * blocks * 2) blocks *= 2;
+  if (a.idx && blocks > 512) blocks = 512;
   if (blocks * 4 > items) blocks = (items + 3) / 4;
   if (blocks * 4 * 64 < items) blocks = (items + 255) / 256;
   if (blocks < 1) blocks = 1;
@@ -228,6 +232,235 @@ static hipError_t launch_wave_op(const RowOpArgs& a, hipStream_t s) {
     case 7:
     case 8: return launch_wave<OP, 8>(a, s);
     default: return launch_wave<OP, kWaveMaxChunks>(a, s);
+  }
+}
+
+// ------------------------------------------------------------ several row lists
+
+// 64-bit pointer held per lane, read back for lane k as a wave-uniform value.
+template <typename T>
+__device__ __forceinline__ T* lane_ptr(T* p, int k) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, k);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), k);
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// The wave-per-row kernel over the concatenated items of several lists (the
+// routed experts of a MoE layer in one launch): lane k resolves item k's
+// list and row once and keeps the row's weight and output addresses, which
+// the item loop reads back with readlane.  Per row the arithmetic is the
+// single-list kernel's, so each list's results are bitwise those of a
+// separate call.
+template <int OP, int NCH>
+__global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
+  constexpr bool kUse0 = OP != kOpGated;
+  constexpr bool kUse1 = OP == kOpGlu || OP == kOpGated || OP == kOpGluRelu;
+  const RowOpArgs& a = L.base;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * (int)(blockDim.x >> 6) + wave_id();
+  const int W = gridDim.x * (int)(blockDim.x >> 6);
+  const int nchunk = a.d >> 3;
+
+  // list l covers the items [pre[l], pre[l + 1])
+  int pre[kMaxRowLists + 1];
+  int n_items = 0;
+#pragma unroll
+  for (int l = 0; l < kMaxRowLists; ++l) {
+    pre[l] = n_items;
+    int c = 0;
+    if (l < L.n) {
+      if (L.idx[l]) {
+        c = *L.count[l];
+        c = c < L.k_max[l] ? c : L.k_max[l];
+        c = (c > 0 ? c : 0) * a.group;
+      } else {
+        c = a.n_rows;
+      }
+    }
+    n_items += c;
+  }
+  pre[kMaxRowLists] = n_items;
+  if (gw >= n_items) return;
+  const int its = (n_items - gw + W - 1) / W;
+
+  const uint16_t* lp0;
+  const uint16_t* lp1;
+  float* lpo;
+  uint32_t* lpk;
+  float lane_pv, lane_av = 0.f;
+  {
+    const int it = gw + W * (lane < its ? lane : 0);
+    int li = 0;
+#pragma unroll
+    for (int l = 1; l < kMaxRowLists; ++l) li += (l < L.n && it >= pre[l]) ? 1 : 0;
+    const uint16_t* w0 = L.W0[0];
+    const uint16_t* w1 = L.W1[0];
+    const int32_t* ix = L.idx[0];
+    const float* ax = L.aux[0];
+    float* o = L.out[0];
+    uint32_t* ko = L.key_out[0];
+    int p = 0;
+#pragma unroll
+    for (int l = 1; l < kMaxRowLists; ++l) {
+      if (li == l) {
+        w0 = L.W0[l]; w1 = L.W1[l]; ix = L.idx[l]; ax = L.aux[l]; o = L.out[l]; ko = L.key_out[l];
+        p = pre[l];
+      }
+    }
+    const int q0 = it - p;
+    int row;
+    if (ix) {
+      const int q = q0 / a.group;
+      row = ix[q] * a.group + (q0 - q * a.group);
+    } else {
+      row = q0;
+    }
+    lp0 = w0 + (size_t)row * a.ld_w;
+    lp1 = kUse1 ? w1 + (size_t)row * a.ld_w : lp0;
+    lpo = o + row;
+    lpk = ko ? ko + row : nullptr;
+    lane_pv = *(a.accumulate ? lpo : a.x);
+    if (OP == kOpGated) lane_av = ax[row];
+    if (OP == kOpPredict) {
+      const float b = *(ax ? ax + row : a.x);
+      lane_av = ax ? b : 0.f;
+    }
+  }
+
+  int coff[NCH];
+  float xm[NCH];
+  float4 xp[NCH], xq[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    coff[j] = c < nchunk ? 8 * c : 0;
+    xm[j] = c < nchunk ? 1.f : 0.f;
+    xp[j] = *reinterpret_cast<const float4*>(a.x + coff[j]);
+    xq[j] = *reinterpret_cast<const float4*>(a.x + coff[j] + 4);
+  }
+  uint4 v0[NCH], v1[NCH];
+  auto fetch = [&](int k) {
+    const uint16_t* p0 = lane_ptr(lp0, k);
+    const uint16_t* p1 = kUse1 ? lane_ptr(lp1, k) : p0;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (kUse0) v0[j] = load_stream(p0 + coff[j]);
+      if (kUse1) v1[j] = load_stream(p1 + coff[j]);
+    }
+  };
+  fetch(0);
+
+  int zero = 0;
+  asm volatile("" : "+v"(zero) : : "memory");
+  const float zf = (float)zero;
+  float xr[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const float m = xm[j] + zf;
+    xr[j][0] = xp[j].x * m; xr[j][1] = xp[j].y * m;
+    xr[j][2] = xp[j].z * m; xr[j][3] = xp[j].w * m;
+    xr[j][4] = xq[j].x * m; xr[j][5] = xq[j].y * m;
+    xr[j][6] = xq[j].z * m; xr[j][7] = xq[j].w * m;
+  }
+  float inv = 1.f, tau = 0.f;
+  if (OP == kOpDotRelu || OP == kOpGluRelu || a.rms_eps > 0.f) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(xr[j][e], xr[j][e], ss);
+    ss = wave_sum(ss);
+    if (a.rms_eps > 0.f) inv = 1.f / sqrtf(ss / (float)a.d + a.rms_eps);
+    tau = a.tau_scale * sqrtf(ss) * inv;
+  }
+
+  for (int k = 0;;) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      float f[8];
+      if (kUse0) {
+        unpack8(v0[j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s0 = fmaf(f[e], xr[j][e], s0);
+      }
+      if (kUse1) {
+        unpack8(v1[j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s1 = fmaf(f[e], xr[j][e], s1);
+      }
+    }
+    if (kUse0) s0 = wave_sum(s0);
+    if (kUse1) s1 = wave_sum(s1);
+    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_pv), k));
+    const float av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_av), k));
+    float* po = lane_ptr(lpo, k);
+    uint32_t* pk = lane_ptr(lpk, k);
+    if (lane == 0) {
+      const float g = s0 * inv, u = s1 * inv;
+      float v;
+      if (OP == kOpGlu) {
+        v = (g / (1.f + expf(-g))) * u;
+      } else if (OP == kOpDotRelu) {
+        v = fmaxf(g - tau, 0.f);
+      } else if (OP == kOpGated) {
+        v = av * u;
+      } else if (OP == kOpGluRelu) {
+        v = fmaxf(g - tau, 0.f) * u;
+      } else if (OP == kOpPredict) {
+        v = g + av;
+      } else {
+        v = g;
+      }
+      if (a.accumulate) v += pv;
+      *po = v;
+      if (pk) *pk = out_key<OP>(v, a.tau_scale);
+    }
+    if (++k >= its) break;
+    fetch(k);
+  }
+}
+
+template <int OP, int NCH>
+static hipError_t launch_lists_nch(const RowOpListsArgs& L, hipStream_t s) {
+  long items = 0;
+  for (int l = 0; l < L.n; ++l)
+    items += L.idx[l] ? (long)L.k_max[l] * L.base.group : (long)L.base.n_rows;
+  long blocks = 256;   // as launch_wave, gathered lists capped at 512
+  while (blocks < 2048 && items >= 6 * blocks * 2) blocks *= 2;
+  if (L.idx[0] && blocks > 512) blocks = 512;
+  if (blocks * 4 > items) blocks = (items + 3) / 4;
+  if (blocks * 4 * 64 < items) blocks = (items + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((rowop_lists_kernel<OP, NCH>), dim3((unsigned)blocks), dim3(256), 0, s, L);
+  return hipGetLastError();
+}
+
+template <int OP>
+static hipError_t launch_lists_op(const RowOpListsArgs& L, hipStream_t s) {
+  switch ((L.base.d / 8 + 63) / 64) {
+    case 0:
+    case 1: return launch_lists_nch<OP, 1>(L, s);
+    case 2: return launch_lists_nch<OP, 2>(L, s);
+    case 3: return launch_lists_nch<OP, 3>(L, s);
+    case 4: return launch_lists_nch<OP, 4>(L, s);
+    case 5: return launch_lists_nch<OP, 5>(L, s);
+    case 6: return launch_lists_nch<OP, 6>(L, s);
+    case 7:
+    case 8: return launch_lists_nch<OP, 8>(L, s);
+    default: return launch_lists_nch<OP, kWaveMaxChunks>(L, s);
+  }
+}
+
+hipError_t launch_rowop_lists(const RowOpListsArgs& L, hipStream_t s) {
+  switch (L.base.op) {
+    case kOpGlu: return launch_lists_op<kOpGlu>(L, s);
+    case kOpDotRelu: return launch_lists_op<kOpDotRelu>(L, s);
+    case kOpGated: return launch_lists_op<kOpGated>(L, s);
+    case kOpGluRelu: return launch_lists_op<kOpGluRelu>(L, s);
+    case kOpPredict: return launch_lists_op<kOpPredict>(L, s);
+    default: return launch_lists_op<kOpDot>(L, s);
   }
 }
 

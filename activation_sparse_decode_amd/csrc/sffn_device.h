@@ -99,6 +99,25 @@ struct RowOpArgs {
 hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s);
 hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s);
 
+// A row op over several row lists at batch 1 (e.g. the routed experts of a
+// MoE layer): list l reads W0[l] / W1[l] at its rows and writes out[l],
+// key_out[l]; the shared fields (op, shape, x, group, tau_scale, rms_eps)
+// come from `base`, whose per-list fields are unused.
+constexpr int kMaxRowLists = 8;
+struct RowOpListsArgs {
+  RowOpArgs base;
+  int n;
+  const uint16_t* W0[kMaxRowLists];
+  const uint16_t* W1[kMaxRowLists];
+  const int32_t* idx[kMaxRowLists];
+  const int32_t* count[kMaxRowLists];
+  int k_max[kMaxRowLists];
+  const float* aux[kMaxRowLists];
+  float* out[kMaxRowLists];
+  uint32_t* key_out[kMaxRowLists];
+};
+hipError_t launch_rowop_lists(const RowOpListsArgs& a, hipStream_t s);
+
 struct AxpyArgs {
   const uint16_t* W; int n_rows, d, ld_w;
   const float* in; int batch, ld_in;

@@ -434,47 +434,32 @@ class ReluMoEStack:
         return ex, w
 
     def layer(self, l: int, t: int, h: torch.Tensor, record=None) -> None:
-        """One layer for token t.  The routed experts are independent until
-        their down products are added to h, so each expert's gate, cluster
-        selection and up run on its own stream (forked from and joined back
-        to the caller's stream); then both experts' down products, weighted
-        by the router, are one gathered product over two row lists added to
-        h (one split-K launch and one reduction)."""
+        """One layer for token t.  The routed experts read the same input, so
+        each step runs once for all of them: their gates in one launch, their
+        active-cluster lists in one selection (a row per expert), their ups
+        over those clusters in one launch, and their down products, weighted
+        by the router, in one gathered product added to h."""
         row = l * self.T + t
         chosen = self.route_host[row]
-        main = torch.cuda.current_stream()
-        streams = self._streams(len(chosen))
-        for s in streams:
-            s.wait_stream(main)
-        for j, e in enumerate(chosen):
-            Wg, Wu, _ = self.experts[l][e]
-            with torch.cuda.stream(streams[j]):
-                B.sparse_ffn_gemv(B.OP_DOT_RELU, Wg, None, h, self.r[j],
-                                  tau_scale=self.tau_scale, rms_eps=self.rms_eps)
-                # clusters holding a nonzero r, keyed by their largest |r| (one call)
-                B.sparse_ffn_select(self.r[j], B.KEY_ABS_F32, 0, self.nc, cluster=self.cluster,
-                                    nonzero_only=True, idx_out=self.cidx[j],
-                                    count_out=self.ccnt[j:j + 1])
-                B.sparse_ffn_gemv(B.OP_GATED, None, Wu, h, self.a[j], idx=self.cidx[j],
-                                  count=self.ccnt[j:j + 1], k_max=self.nc, group=self.cluster,
-                                  aux=self.r[j], rms_eps=self.rms_eps)
+        k = len(chosen)
+        ex = [self.experts[l][e] for e in chosen]
+        r, a = [self.r[j] for j in range(k)], [self.a[j] for j in range(k)]
+        idx, cnt = [self.cidx[j] for j in range(k)], [self.ccnt[j:j + 1] for j in range(k)]
+        B.sparse_ffn_rowop_lists(B.OP_DOT_RELU, [m[0] for m in ex], None, h, r,
+                                 tau_scale=self.tau_scale, rms_eps=self.rms_eps)
+        # clusters holding a nonzero r, keyed by their largest |r| (one call, a row per expert)
+        B.sparse_ffn_select(self.r[:k], B.KEY_ABS_F32, 0, self.nc, cluster=self.cluster,
+                            nonzero_only=True, idx_out=self.cidx[:k], count_out=self.ccnt[:k])
+        B.sparse_ffn_rowop_lists(B.OP_GATED, None, [m[1] for m in ex], h, a, idxs=idx, counts=cnt,
+                                 k_maxs=[self.nc] * k, group=self.cluster, auxs=r,
+                                 rms_eps=self.rms_eps)
         if record is not None:
             torch.cuda.synchronize()
             record(l, t, h, chosen)
-        for s in streams:
-            main.wait_stream(s)
-        k = len(chosen)
-        B.sparse_ffn_gemv_lists([self.experts[l][e][2] for e in chosen],
-                                [self.a[j] for j in range(k)], [self.cidx[j] for j in range(k)],
-                                [self.ccnt[j:j + 1] for j in range(k)], [self.nc] * k, h,
+        B.sparse_ffn_gemv_lists([m[2] for m in ex], a, idx, cnt, [self.nc] * k, h,
                                 group=self.cluster,
                                 alphas=[self.route_w[row, j:j + 1] for j in range(k)],
                                 accumulate=True, workspace=self.ws)
-
-    def _streams(self, k: int):
-        if not hasattr(self, "_expert_streams") or len(self._expert_streams) < k:
-            self._expert_streams = [torch.cuda.Stream() for _ in range(k)]
-        return self._expert_streams[:k]
 
     def decode(self, h: torch.Tensor, t: int, record=None) -> None:
         for l in range(self.L):
@@ -486,8 +471,7 @@ class PredictedMoEStack(ReluMoEStack):
     and expert (PowerInfer-2 guide, "Online Predictor"): the clusters of
     layer l's routed experts are those with sigmoid(W_pred x + b) > theta,
     x the (normalised) FFN input of layer l - 1 (of layer 0 for layer 0).
-    The lookahead runs on a stream of its own while layer l - 1 computes;
-    each layer then reads gate, up and down rows of its predicted clusters
+    Each layer then reads gate, up and down rows of its predicted clusters
     only (no dense gate).  The predictors here are random: the stack shows
     the cost of the structure, not a trained predictor's accuracy."""
 
@@ -505,46 +489,44 @@ class PredictedMoEStack(ReluMoEStack):
 
     def predict(self, l: int, t: int, h: torch.Tensor) -> None:
         """Predicted clusters of layer l's routed experts from h (on the
-        current stream) into buffer l % 2."""
+        current stream) into buffer l % 2: both predictors in one launch, both
+        cluster lists in one selection."""
         buf = l & 1
-        for j, e in enumerate(self.route_host[l * self.T + t]):
-            Wp, bp = self.predictors[l][e]
-            B.sparse_ffn_gemv(B.OP_PREDICT, Wp, None, h, self.z[buf, j], aux=bp,
-                              tau_scale=self.theta, key_out=self.zkey[buf, j], rms_eps=self.rms_eps)
-            B.sparse_ffn_select(self.zkey[buf, j], B.KEY_U32, 0, self.nc, nonzero_only=True,
-                                idx_out=self.pidx[buf, j], count_out=self.pcnt[buf, j:j + 1])
+        chosen = self.route_host[l * self.T + t]
+        k = len(chosen)
+        P = [self.predictors[l][e] for e in chosen]
+        B.sparse_ffn_rowop_lists(B.OP_PREDICT, [p[0] for p in P], None, h,
+                                 [self.z[buf, j] for j in range(k)], auxs=[p[1] for p in P],
+                                 tau_scale=self.theta,
+                                 key_outs=[self.zkey[buf, j] for j in range(k)],
+                                 rms_eps=self.rms_eps)
+        B.sparse_ffn_select(self.zkey[buf, :k], B.KEY_U32, 0, self.nc, nonzero_only=True,
+                            idx_out=self.pidx[buf, :k], count_out=self.pcnt[buf, :k])
 
     def layer(self, l: int, t: int, h: torch.Tensor, record=None) -> None:
         """One layer for token t: the lookahead prediction for layer l + 1
-        and each routed expert's ReGLU over its predicted clusters run on
-        forked streams; then both down products, weighted by the router, in
-        one gathered product added to h."""
+        (from this layer's input), the routed experts' ReGLU over their
+        predicted clusters (one launch), then both down products, weighted
+        by the router, in one gathered product added to h."""
         row = l * self.T + t
         chosen = self.route_host[row]
+        k = len(chosen)
         cur = l & 1
-        main = torch.cuda.current_stream()
-        streams = self._streams(len(chosen) + 1)
-        for s in streams:
-            s.wait_stream(main)
+        ex = [self.experts[l][e] for e in chosen]
+        a = [self.a[j] for j in range(k)]
+        idx, cnt = [self.pidx[cur, j] for j in range(k)], [self.pcnt[cur, j:j + 1] for j in range(k)]
+        # The lookahead prediction is issued first on the same stream: a
+        # forked stream measured slower (the graph's cross-queue waits cost
+        # more than the small predictor launches).
         if l + 1 < self.L:
-            with torch.cuda.stream(streams[-1]):
-                self.predict(l + 1, t, h)
-        for j, e in enumerate(chosen):
-            Wg, Wu, _ = self.experts[l][e]
-            with torch.cuda.stream(streams[j]):
-                B.sparse_ffn_gemv(B.OP_GLU_RELU, Wg, Wu, h, self.a[j], idx=self.pidx[cur, j],
-                                  count=self.pcnt[cur, j:j + 1], k_max=self.nc,
-                                  group=self.cluster, tau_scale=self.tau_scale,
-                                  rms_eps=self.rms_eps)
+            self.predict(l + 1, t, h)
+        B.sparse_ffn_rowop_lists(B.OP_GLU_RELU, [m[0] for m in ex], [m[1] for m in ex], h, a,
+                                 idxs=idx, counts=cnt, k_maxs=[self.nc] * k, group=self.cluster,
+                                 tau_scale=self.tau_scale, rms_eps=self.rms_eps)
         if record is not None:
             torch.cuda.synchronize()
             record(l, t, h, chosen)
-        for s in streams:
-            main.wait_stream(s)
-        k = len(chosen)
-        B.sparse_ffn_gemv_lists([self.experts[l][e][2] for e in chosen],
-                                [self.a[j] for j in range(k)], [self.pidx[cur, j] for j in range(k)],
-                                [self.pcnt[cur, j:j + 1] for j in range(k)], [self.nc] * k, h,
+        B.sparse_ffn_gemv_lists([m[2] for m in ex], a, idx, cnt, [self.nc] * k, h,
                                 group=self.cluster,
                                 alphas=[self.route_w[row, j:j + 1] for j in range(k)],
                                 accumulate=True, workspace=self.ws)

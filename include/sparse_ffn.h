@@ -95,7 +95,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 8
+#define SFFN_ABI_VERSION 9
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -282,6 +282,36 @@ sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const i
                                   const int* k_max, int group, const float* const* alpha,
                                   float* out, int accumulate,
                                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_rowop_lists -- one row op (GLU_SILU, DOT_RELU, GATED, DOT,
+ * GLU_RELU or PREDICT, as in sparse_ffn_gemv) over several row lists at
+ * batch 1, in one launch: the routed experts of a MoE layer are computed
+ * on the same input ([PowerInfer-2] guide, MoE engine listing), so their
+ * gates, ups or predictors can run as one pass instead of one call per
+ * expert.  List l reads W0[l] / W1[l] (bf16 [n_rows][ld_w], rows of length
+ * d, 16-byte aligned) at its rows -- all n_rows rows when idx is NULL, else
+ * for i < min(*count[l], k_max[l]) and g < group, row idx[l][i]*group + g --
+ * and writes out[l][row] (and key_out[l][row]) exactly as sparse_ffn_gemv
+ * would for that list alone (bitwise the same values); aux[l] is GATED's
+ * gate values or PREDICT's bias (fp32 [n_rows]).  x: fp32 [d], shared, read
+ * through the optional RMSNorm (rms_eps).  W0, W1, idx, count, k_max, aux,
+ * out and key_out are HOST arrays of n_lists entries holding device
+ * pointers; W1 may be NULL unless the op uses it (GLU_SILU, GATED,
+ * GLU_RELU), W0 may be NULL for GATED, idx NULL processes every row of
+ * every list, aux NULL except for GATED, key_out NULL or with NULL entries.
+ * tau_scale and accumulate as in sparse_ffn_gemv.
+ * Limits: 1 <= n_lists <= 8; 8 <= d <= 5120, d % 8 == 0; ld_w >= d,
+ * ld_w % 8 == 0; k_max[l]*group <= n_rows; x 16-byte aligned.  Errors as
+ * for sparse_ffn_gemv (nothing is launched on a rejected call).
+ */
+sffn_status sparse_ffn_rowop_lists(int op, int n_lists, const uint16_t* const* W0,
+                                   const uint16_t* const* W1, int n_rows, int d, int ld_w,
+                                   const float* x, const int32_t* const* idx,
+                                   const int32_t* const* count, const int* k_max, int group,
+                                   float tau_scale, float rms_eps, const float* const* aux,
+                                   float* const* out, uint32_t* const* key_out, int accumulate,
+                                   void* stream);
 
 /*
  * sparse_ffn_compact -- gather the weight rows of a selected neuron set into

@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 8
+    assert L.sffn_abi_version() == 9
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -247,6 +247,49 @@ def test_compact_validation(L):
     assert rc == 1 and "ld_out" in msg
     rc, msg = status_and_msg(L, cp(FAKE, 100, 64, 64, NULL, 10, 1, FAKE, 16, NULL))
     assert rc == 1 and "idx" in msg
+
+
+def rowop_lists(L, op=0, n=2, W0=(FAKE, FAKE), W1=(FAKE, FAKE), n_rows=64, d=64, ld_w=64, x=FAKE,
+                idx=None, count=(FAKE, FAKE), k_max=(2, 2), group=1, tau=0.0, eps=0.0, aux=None,
+                out=(FAKE, FAKE), key=None, acc=0):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    arr = lambda T, vs: None if vs is None else (T * len(vs))(*vs)  # noqa: E731
+    rc = L.sparse_ffn_rowop_lists(op, n, arr(P, W0), arr(P, W1), n_rows, d, ld_w, x, arr(P, idx),
+                                  arr(P, count), arr(I, k_max), group, ctypes.c_float(tau),
+                                  ctypes.c_float(eps), arr(P, aux), arr(P, out), arr(P, key), acc,
+                                  NULL)
+    return status_and_msg(L, rc)
+
+
+def test_rowop_lists_validation(L):
+    rc, msg = rowop_lists(L, op=3)
+    assert rc == 1 and "not a row op" in msg
+    rc, msg = rowop_lists(L, n=0)
+    assert rc == 1 and "n_lists" in msg
+    rc, msg = rowop_lists(L, n=9)
+    assert rc == 1 and "n_lists" in msg
+    rc, msg = rowop_lists(L, out=None)
+    assert rc == 1 and "out" in msg
+    rc, msg = rowop_lists(L, d=5128, ld_w=5128)
+    assert rc == 2 and "5120" in msg
+    rc, msg = rowop_lists(L, W1=None)
+    assert rc == 1 and "W1" in msg
+    rc, msg = rowop_lists(L, op=2, W0=None, aux=None)
+    assert rc == 1 and "aux" in msg
+    rc, msg = rowop_lists(L, idx=(FAKE, FAKE), k_max=None)
+    assert rc == 1 and "k_max" in msg
+    rc, msg = rowop_lists(L, idx=(FAKE, FAKE), k_max=(2, 65))
+    assert rc == 1 and "exceeds" in msg
+    rc, msg = rowop_lists(L, W0=(FAKE, ctypes.c_void_p(0x1008)))
+    assert rc == 1 and "W0[1]" in msg
+    rc, msg = rowop_lists(L, op=6, tau=1.0)
+    assert rc == 1 and "probability" in msg
+    rc, msg = rowop_lists(L, op=6, tau=0.45, acc=1)
+    assert rc == 1 and "accumulate" in msg
+    rc, msg = rowop_lists(L, op=5, tau=-1.0)
+    assert rc == 1 and "tau" in msg
+    rc, msg = rowop_lists(L, x=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "x must" in msg
 
 
 def test_gather_validation(L):

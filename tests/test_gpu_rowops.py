@@ -89,3 +89,51 @@ def test_dot_relu_and_gated(d):
     assert np.all(got[np.setdiff1d(np.arange(N), rows)] == -9.0), "a row outside the clusters was written"
     ref = aux[rows].astype(np.float64) * oracle.row_dots(W1, xn, rows)
     assert_close(got[rows], ref, what=f"gated product d={d}")
+
+
+@pytest.mark.parametrize("op", ["glu", "dot_relu", "gated", "dot", "glu_relu", "predict"])
+def test_rowop_lists_match_separate_calls(op):
+    """One launch over several row lists writes, for each list, bitwise what
+    a separate sparse_ffn_gemv call writes; rows outside a list keep their
+    values; an empty list is allowed."""
+    banner(f"rowop lists {op}")
+    rng = np.random.default_rng(["glu", "dot_relu", "gated", "dot", "glu_relu", "predict"].index(op))
+    N, d, S = 2048, 4096, 32
+    code = {"glu": B.OP_GLU_SILU, "dot_relu": B.OP_DOT_RELU, "gated": B.OP_GATED, "dot": B.OP_DOT,
+            "glu_relu": B.OP_GLU_RELU, "predict": B.OP_PREDICT}[op]
+    tau = {"dot_relu": 0.0256, "glu_relu": 0.0256, "predict": 0.45}.get(op, 0.0)
+    eps = 0.0 if op == "dot" else 1e-5
+    n_l = 3
+    W0 = [dev(synth.weight_bf16(8, synth.W_C3, 0, e, synth.T_GATE, N, d)) for e in range(n_l)]
+    W1 = [dev(synth.weight_bf16(8, synth.W_C3, 0, e, synth.T_UP, N, d)) for e in range(n_l)]
+    aux = [dev(rng.standard_normal(N).astype(np.float32)) for _ in range(n_l)]
+    x = dev(synth.tokens(8, synth.W_C3, 3, 1, d)[0])
+    use0, use1 = op != "gated", op in ("glu", "gated", "glu_relu")
+    for clustered in (False, True):
+        if clustered:
+            counts = [17, 0, 40]
+            sel = [np.sort(rng.choice(N // S, size=max(c, 1), replace=False)).astype(np.int32)
+                   for c in counts]
+            idx = [dev(s) for s in sel]
+            cnt = [dev(np.array([c], np.int32)) for c in counts]
+            kw = dict(k_max=N // S, group=S)
+        outs = [torch.full((N,), 3.0, dtype=torch.float32, device="cuda") for _ in range(n_l)]
+        keys = [torch.zeros(N, dtype=torch.int32, device="cuda") for _ in range(n_l)]
+        ref = [o.clone() for o in outs]
+        rkeys = [k.clone() for k in keys]
+        for l in range(n_l):
+            B.sparse_ffn_gemv(code, W0[l] if use0 else None, W1[l] if use1 else None, x, ref[l],
+                              key_out=rkeys[l], tau_scale=tau, rms_eps=eps,
+                              aux=aux[l] if op in ("gated", "predict") else None,
+                              **(dict(idx=idx[l], count=cnt[l], **kw) if clustered else {}))
+        B.sparse_ffn_rowop_lists(code, W0 if use0 else None, W1 if use1 else None, x, outs,
+                                 key_outs=keys, tau_scale=tau, rms_eps=eps,
+                                 auxs=aux if op in ("gated", "predict") else None,
+                                 **(dict(idxs=idx, counts=cnt, k_maxs=[N // S] * n_l, group=S)
+                                    if clustered else {}))
+        torch.cuda.synchronize()
+        for l in range(n_l):
+            assert np.array_equal(host_u32(outs[l]), host_u32(ref[l])), (op, clustered, l)
+            assert np.array_equal(host_u32(keys[l]), host_u32(rkeys[l])), (op, clustered, l)
+        if clustered:
+            assert np.all(host(outs[1]) == 3.0)
