@@ -38,7 +38,10 @@
 //     After the first pass only the keys whose higher digits match a bound
 //     can matter: each thread tests its own keys and only those are
 //     counted.  A bound that covers every eligible entry needs no search
-//     (pure compaction, e.g. the nonzero clusters of a ReLU layer).
+//     (pure compaction, e.g. the nonzero clusters of a ReLU layer), and a
+//     bound whose boundary digit holds exactly the entries still needed
+//     stops there: every key with that prefix or a larger one is in (for
+//     float magnitudes usually after the second pass, saving the third).
 //  3. Index-order positions: a wave's entries are consecutive, so the
 //     position of an entry among those with some property is the count in
 //     the waves before (one exchange through LDS), plus the wave's running
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   // all_hi / all_lo: the bound covers every eligible entry (no search)
   const bool all_hi = rhi == E;
   const bool all_lo = rlo == E && rlo > 0;
-  const bool need_hi = rhi > 0 && !all_hi;
-  const bool need_lo = rlo > 0 && !all_lo;
+  bool need_hi = rhi > 0 && !all_hi;
+  bool need_lo = rlo > 0 && !all_lo;
 
   // T_r (pre_*), rank left among the keys equal to T_r (rem_*), their count (tie_*)
   uint32_t pre_hi = 0, pre_lo = 0, rem_hi = rhi, rem_lo = rlo, tie_hi = E, tie_lo = E;
@@ -315,6 +318,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       // inside scan_pass, which every thread reaches after these reads
       if (need_hi) { pre_hi |= found[0] << shift; rem_hi = found[1]; tie_hi = found[2]; }
       if (need_lo) { pre_lo |= found[3] << shift; rem_lo = found[4]; tie_lo = found[5]; }
+      // A bound whose boundary digit holds exactly the entries still needed
+      // is decided: every key whose prefix is at least pre_* is in, whatever
+      // its lower bits (pre_* has zeros there), so its search stops.
+      if (need_hi && tie_hi == rem_hi) need_hi = false;
+      if (need_lo && tie_lo == rem_lo) need_lo = false;
       if (pass == 0 && shift > 0) {
         // Entries that take no part get a key whose first digit is neither
         // bound's (the first digit has 11 bits when more passes follow), so
@@ -326,6 +334,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int j = 0; j < KPT; ++j) key[j] = ((elig >> j) & 1u) ? key[j] : d << shift;
       }
       lo_bit = shift;
+      if (!need_hi && !need_lo) break;   // uniform: found[] is shared
     }
   }
 
