@@ -152,3 +152,38 @@ def test_full_size_table1_stack():
                n_decode=cfg["decode_tokens"], first=cfg["first"], last=cfg["last"],
                check_layers={0, 5, 15, 25, 27}, check_tokens={0, 127},
                pcts=(cfg["base_pct"], cfg["loaded_pct"], cfg["alpha_pct"], cfg["computed_pct"]))
+
+
+def test_loaded_decode_graph_replays_match_eager():
+    """The Table 1 stack's decode step captured as a HIP graph gives, on
+    every replay, the bits of the eager calls."""
+    banner("c1-loading graph replay")
+    L, N, d = 5, 1024, 512
+    layers = synth.ffn_stack(7, synth.W_C1, L, N, d)
+    dev_layers = [tuple(to_device_bf16(m) for m in lay) for lay in layers]
+    stack = SelectInferLoadedStack(dev_layers, pct_count(30, N), pct_count(70, N), pct_count(30, N),
+                                   pct_count(40, N), first=1, last=-1, max_tokens=96)
+    stack.profile(dev(synth.tokens(7, synth.W_C1, 11, 64, d)),
+                  dev(synth.mixture_tokens(7, synth.W_C1, 12, 32, d)))
+    stack.load()
+    stack.release_full_weights()
+    stack.prefill(dev(synth.tokens(7, synth.W_C1, 13, 32, d)))
+    X = dev(synth.tokens(7, synth.W_C1, 14, 4, d))
+    eager = []
+    for t in range(4):
+        h = X[t].clone()
+        stack.decode(h)
+        eager.append(host(h))
+    h = torch.zeros(d, dtype=torch.float32, device="cuda")
+    xcur = torch.zeros(d, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.copy_(xcur)
+        stack.decode(h)
+    for rep in range(3):
+        for t in range(4):
+            xcur.copy_(X[t])
+            g.replay()
+            got = host(h)
+            assert np.array_equal(got.view(np.uint32), eager[t].view(np.uint32)), (rep, t)

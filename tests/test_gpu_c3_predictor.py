@@ -197,3 +197,49 @@ def test_small_predicted_moe():
 def test_full_size_predicted_moe():
     run_pred(L=32, E=8, N=14336, d=4096, n_tokens=2, check_layers={0, 1, 31},
              on_device_weights=True)
+
+
+def test_moe_graph_replays_match_eager():
+    """Both MoE stacks (dense gate and predictor) captured per token as HIP
+    graphs give, on every replay, the bits of the eager calls (reductions in
+    a fixed order, no memset nodes)."""
+    from activation_sparse_decode_amd.pipelines import ReluMoEStack
+    banner("c3 graph replay")
+    L, E, N, d = 3, 4, 1024, 256
+    nc = N // CLUSTER
+    cfg = synth.SHAPES["c3"]
+    experts = [[(to_device_bf16(synth.clustered_gate_bf16(6, synth.W_C3, l, e, N, d, CLUSTER)),
+                 to_device_bf16(synth.weight_bf16(6, synth.W_C3, l, e, synth.T_UP, N, d)),
+                 to_device_bf16(synth.weight_bf16(6, synth.W_C3, l, e, synth.T_DOWN, N, d)))
+                for e in range(E)] for l in range(L)]
+    preds = [[(to_device_bf16(synth.weight_bf16(6, synth.W_C3, l, e, synth.T_PRED, nc, d)),
+               dev(synth.predictor_bias(nc, d, cfg["pred_theta"], cfg["pred_frac"])))
+              for e in range(E)] for l in range(L)]
+    T = 3
+    logits = dev(synth.router_logits(6, synth.W_C3, L, T, E))
+    X = dev(synth.tokens(6, synth.W_C3, 1, T, d))
+    tau_scale = QUANTILE * synth.WEIGHT_STD
+    for moe in (ReluMoEStack(experts, CLUSTER, tau_scale=tau_scale),
+                PredictedMoEStack(experts, preds, CLUSTER, tau_scale=tau_scale,
+                                  theta=cfg["pred_theta"])):
+        moe.route(logits)
+        eager = []
+        for t in range(T):
+            h = X[t].clone()
+            moe.decode(h, t)
+            eager.append(host(h))
+        h = torch.zeros(d, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        graphs = []
+        for t in range(T):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                h.copy_(X[t])
+                moe.decode(h, t)
+            graphs.append(g)
+        for rep in range(3):
+            for t in range(T):
+                graphs[t].replay()
+                got = host(h)                  # synchronizes between replays
+                assert np.array_equal(got.view(np.uint32), eager[t].view(np.uint32)), \
+                    (type(moe).__name__, rep, t)
