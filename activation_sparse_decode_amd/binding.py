@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_score.argtypes = [_i, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _vp]
         L.sparse_ffn_select.restype = _i
         L.sparse_ffn_select.argtypes = [_vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
-                                        _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _vp]
+                                        _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _vp]
         L.sparse_ffn_row_norms.restype = _i
         L.sparse_ffn_row_norms.argtypes = [_vp, _i, _i, _i, _vp, _vp]
         L.sparse_ffn_gemv.restype = _i
@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 9:
+        if L.sffn_abi_version() != 10:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -134,7 +134,7 @@ def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *
                       idx_top_out: torch.Tensor | None = None,
                       count_top_out: torch.Tensor | None = None,
                       freq: torch.Tensor | None = None, key_scale: torch.Tensor | None = None,
-                      stream=None) -> None:
+                      clear_keys: bool = False, stream=None) -> None:
     rows, width = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
     n = width // cluster
     _check(lib().sparse_ffn_select(
@@ -143,7 +143,7 @@ def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *
         _p(include_mask), _p(exclude_mask), _p(mask_out), _ld(mask_out, n), _p(idx_out),
         _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out),
         _p(idx_top_out), _ld(idx_top_out, idx_top_out.shape[-1] if idx_top_out is not None else 0),
-        _p(count_top_out), _p(freq), _stream(stream)))
+        _p(count_top_out), _p(freq), int(clear_keys), _stream(stream)))
 
 
 def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,

@@ -104,7 +104,7 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
                               uint8_t* mask_out, int ld_mask,
                               int32_t* idx_out, int ld_idx, int32_t* count_out,
                               int32_t* idx_top_out, int ld_idx_top, int32_t* count_top_out,
-                              uint32_t* freq_inout, void* stream) {
+                              uint32_t* freq_inout, int clear_keys, void* stream) {
   REQUIRE(keys != nullptr, SFFN_EINVAL, "select: keys must be non-null");
   REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "select: unknown key type %d", key_type);
   REQUIRE(rows >= 0, SFFN_EINVAL, "select: rows=%d must be >= 0", rows);
@@ -138,11 +138,14 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
   if (count_out) REQUIRE(aligned(count_out, 4), SFFN_EINVAL, "select: count_out misaligned");
   if (count_top_out) REQUIRE(aligned(count_top_out, 4), SFFN_EINVAL, "select: count_top_out misaligned");
   if (freq_inout) REQUIRE(aligned(freq_inout, 4), SFFN_EINVAL, "select: freq misaligned");
+  if (clear_keys)
+    REQUIRE(cluster == 1 && !key_scale && (void*)freq_inout != keys, SFFN_EINVAL,
+            "select: clear_keys needs cluster == 1, no key_scale and freq distinct from keys");
   if (rows == 0) return ok();
   sffn::SelectArgs a{keys, key_type, key_scale, rows, n, ld, cluster, r_lo, r_hi, nonzero_only ? 1 : 0,
                      include_mask, exclude_mask, mask_out, ld_mask, idx_out, ld_idx, count_out,
                      idx_top_out,
-                     ld_idx_top, count_top_out, freq_inout};
+                     ld_idx_top, count_top_out, freq_inout, clear_keys ? 1 : 0};
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
 }
 

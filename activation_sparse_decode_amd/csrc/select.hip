@@ -11,7 +11,9 @@
 // With a key scale vector, the key of entry j is the magnitude key of the
 // fp32 product v_j * scale_j, formed as the keys are loaded (WiSparse's
 // weight-aware saliency: activation magnitude times a precomputed weight
-// norm of the channel).  Entries marked in an exclusion mask take no part
+// norm of the channel).  With clear_keys the row's keys are set to zero
+// once read (a frequency count consumed and reset in the same pass).
+// Entries marked in an exclusion mask take no part
 // in the ranking; with the same mask as the include mask the call yields
 // "the set, then the best-ranked entries outside it until k more": the
 // secondary neurons added to the base set until the loading budget is met
@@ -260,6 +262,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const bool e = (ebase + 64 * j < n) & (!a.nonzero_only | (key[j] != 0u)) & !((excl >> j) & 1u);
     elig |= (e ? 1u : 0u) << j;
     kor |= e ? key[j] : 0u;
+  }
+  if (a.clear_keys) {
+    // the keys were consumed above (their loads have completed): reset the
+    // row's own entries, so a frequency count can be read and cleared in one pass
+    uint32_t* kw = const_cast<uint32_t*>(kp);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (ebase + 64 * j < n) kw[ebase + 64 * j] = 0u;
   }
   kor = wave_incl<true>(kor);
   const uint32_t ecount = wave_incl<false>((uint32_t)__popc(elig));   // lane 63: the wave's count

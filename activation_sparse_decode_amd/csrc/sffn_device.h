@@ -155,6 +155,7 @@ struct SelectArgs {
   int32_t* idx_top_out; int ld_idx_top;
   int32_t* count_top_out;
   uint32_t* freq;
+  int clear_keys;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 

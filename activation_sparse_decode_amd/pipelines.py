@@ -556,9 +556,10 @@ class BatchedUnionLayer:
     def __call__(self, X: torch.Tensor, Y: torch.Tensor) -> None:
         N = self.Wg.shape[0]
         B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, X, self.A, key_out=self.K)
-        self.F.zero_()
+        # F starts at zero (allocation) and the union select resets it as it
+        # reads it, ready for the next batch's counts
         B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M, freq=self.F)
         B.sparse_ffn_select(self.F, B.KEY_U32, 0, N, nonzero_only=True, idx_out=self.U,
-                            count_out=self.cnt)
+                            count_out=self.cnt, clear_keys=True)
         B.sparse_ffn_gemv(B.OP_AXPY, self.WdT, None, self.A, Y, idx=self.U, count=self.cnt,
                           k_max=N, row_mask=self.M, workspace=self.ws)

@@ -95,7 +95,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 9
+#define SFFN_ABI_VERSION 10
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -166,6 +166,10 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  *                 include_mask.
  *  freq_inout   : nullable uint32 [n]: += 1 for each row that selects the
  *                 entry (the frequency count of [SelectInfer] §5).
+ *  clear_keys   : nonzero: each row's keys[r][0..n) are set to 0 once read
+ *                 (cluster == 1, no key_scale), so a frequency count can be
+ *                 consumed and reset for its next accumulation in one pass
+ *                 (keys is then written: it must not be read-only memory).
  * Limits: 1 <= n <= 32768, 0 <= r_lo <= r_hi, r_hi may exceed the number of
  * eligible entries (then it is clipped).  The result is unique: bit-exact.
  */
@@ -180,6 +184,7 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
                               int32_t* idx_top_out, int ld_idx_top,
                               int32_t* count_top_out,
                               uint32_t* freq_inout,
+                              int clear_keys,
                               void* stream);
 
 /*

@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 9
+    assert L.sffn_abi_version() == 10
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -56,10 +56,11 @@ def status_and_msg(L, rc):
 
 def select(L, keys=FAKE, key_type=0, rows=1, n=8, ld=8, cluster=1, r_lo=0, r_hi=4, nz=0,
            include=NULL, mask=NULL, ld_mask=0, idx=NULL, ld_idx=0, count=NULL, idx_top=NULL,
-           ld_idx_top=0, count_top=NULL, freq=NULL, scale=NULL, exclude=NULL):
+           ld_idx_top=0, count_top=NULL, freq=NULL, scale=NULL, exclude=NULL, clear=0):
     return status_and_msg(L, L.sparse_ffn_select(keys, key_type, scale, rows, n, ld, cluster, r_lo,
                                                  r_hi, nz, include, exclude, mask, ld_mask, idx, ld_idx,
-                                                 count, idx_top, ld_idx_top, count_top, freq, NULL))
+                                                 count, idx_top, ld_idx_top, count_top, freq, clear,
+                                                 NULL))
 
 
 def test_select_validation(L):
@@ -97,6 +98,12 @@ def test_select_validation(L):
     assert rc == 1 and "key_scale" in msg
     rc, msg = select(L, scale=ctypes.c_void_p(0x1002))
     assert rc == 1 and "key_scale" in msg
+    rc, msg = select(L, n=4, ld=16, cluster=4, clear=1)
+    assert rc == 1 and "clear_keys" in msg
+    rc, msg = select(L, scale=FAKE, clear=1)
+    assert rc == 1 and "clear_keys" in msg
+    rc, msg = select(L, freq=FAKE, clear=1)
+    assert rc == 1 and "clear_keys" in msg
 
 
 def test_row_norms_validation(L):

@@ -48,11 +48,20 @@ def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None):
         S.append(s)
     U_ref = oracle.union(*S)
     assert np.array_equal(U, U_ref)
-    assert np.array_equal(F, np.bincount(np.concatenate(S), minlength=N).astype(np.uint32))
+    # the frequency counts were consumed by the union select and reset
+    assert not F.any()
     for b in toks:
         y_ref = oracle.down_gather(WdT, S[b], A[b][S[b]])
         assert_close(host(Y[b]), y_ref, what=f"output b={b}")
     print(f"  union {cnt} of {N} ({cnt / N:.3f})")
+    # a second batch on other tokens: its union starts from the reset counts
+    X2 = synth.tokens(seed, synth.W_C4, batch + 100, batch, d)
+    layer(dev(X2), Y)
+    torch.cuda.synchronize()
+    A2 = host(layer.A)
+    S2 = [oracle.rank_range(oracle.key_abs(A2[b]), 0, keep) for b in range(batch)]
+    cnt2 = int(host(layer.cnt)[0])
+    assert np.array_equal(host(layer.U)[:cnt2], oracle.union(*S2))
     return layer, Y
 
 

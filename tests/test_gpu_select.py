@@ -273,3 +273,25 @@ def test_gather(n_src, k):
     got = host(dst)
     assert np.array_equal(got[:c].view(np.uint32), src[idx[:c]].view(np.uint32))
     assert np.all(got[c:] == 7.0)
+
+
+def test_clear_keys():
+    """clear_keys: the selection is unchanged and the rows' keys read as zero
+    afterwards (a frequency count consumed and reset in one pass); entries
+    past n in a wider row are untouched."""
+    banner("select clear_keys")
+    rng = np.random.default_rng(44)
+    rows, n, ld = 3, 5000, 5008
+    counts = rng.integers(0, 17, size=(rows, ld)).astype(np.uint32)
+    keys = dev(counts)
+    idx = torch.full((rows, n), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select(keys[:, :n], B.KEY_U32, 0, n, nonzero_only=True, idx_out=idx,
+                        count_out=cnt, clear_keys=True)
+    torch.cuda.synchronize()
+    after = host_u32(keys)
+    assert not after[:, :n].any() and np.array_equal(after[:, n:], counts[:, n:])
+    gi, gc = host(idx), host(cnt)
+    for r in range(rows):
+        exp = oracle.rank_range(counts[r, :n], 0, n, True, None)
+        assert gc[r] == exp.size and np.array_equal(gi[r, :gc[r]], exp), r
