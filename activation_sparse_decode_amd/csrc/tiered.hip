@@ -62,10 +62,20 @@ __device__ __forceinline__ void tier_rows(const int32_t* idx, const float* x, in
 }
 
 __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid,
-                                                      float* partials) {
+                                                      int xcd_order, float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int tile = blockIdx.x, ks = blockIdx.y;
+  int tile = blockIdx.x, ks = blockIdx.y;
+  if (xcd_order) {
+    // Workgroups go to the eight XCDs round-robin by linear id; remap so that
+    // every column tile of a row chunk runs on one XCD and the chunk's record
+    // headers and boundary lines are fetched into one L2 (needs the chunk
+    // count to be a multiple of 8).
+    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    const int x = L & 7, sl = L >> 3;
+    tile = sl % (int)gridDim.x;
+    ks = (sl / (int)gridDim.x) * 8 + x;
+  }
   const int col = tile * kTileCols + 8 * lane;
   const int colc = col < a.d_out ? col : 0;   // lanes past the last output re-read output 0
 
@@ -164,9 +174,13 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   ks_top = std::min<long>(ks_top, kMaxSplit / 2);
   ks_mid = std::min<long>(ks_mid, kMaxSplit / 2);
   if (ks_top + ks_mid == 0) ks_mid = 1;   // nothing to read: one chunk writes y
+  // XCD-grouped block order where the chunk count allows it (measured on the
+  // 14336 -> 4096 down projection: 13.0 -> 11.9 us; with 12 column tiles and
+  // 21 chunks the plain order is kept)
+  const int xcd_order = (ks_top + ks_mid) % 8 == 0 ? 1 : 0;
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
   hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0, s,
-                     a, (int)ks_top, (int)ks_mid, partials);
+                     a, (int)ks_top, (int)ks_mid, xcd_order, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(partials, (int)(ks_top + ks_mid), 1, 1, a.d_out, nullptr, a.y,
