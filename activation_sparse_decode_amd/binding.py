@@ -21,6 +21,7 @@ SFFN_OK, SFFN_EINVAL, SFFN_EUNSUPPORTED, SFFN_EWORKSPACE, SFFN_EHIP = range(5)
 KEY_ABS_F32, KEY_U32, KEY_F32 = 0, 1, 2
 SCORE_SUM_ABS, SCORE_CLUSTER_MAX, SCORE_SOFTMAX_PICKED = 0, 1, 2
 OP_GLU_SILU, OP_DOT_RELU, OP_GATED, OP_AXPY, OP_DOT, OP_GLU_RELU, OP_PREDICT = 0, 1, 2, 3, 4, 5, 6
+OP_DOT_RELU_CLUSTER = 7
 
 _STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
 
@@ -75,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 10:
+        if L.sffn_abi_version() != 11:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib

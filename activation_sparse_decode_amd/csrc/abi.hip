@@ -165,7 +165,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                             int ld_mask, float tau_scale, float rms_eps, const float* aux, int ld_aux,
                             const float* alpha, float* out, uint32_t* key_out, int ld_out,
                             int accumulate, void* workspace, size_t ws_bytes, void* stream) {
-  REQUIRE(op >= 0 && op <= 6, SFFN_EINVAL, "gemv: unknown op %d", op);
+  REQUIRE(op >= 0 && op <= 7, SFFN_EINVAL, "gemv: unknown op %d", op);
   REQUIRE(in && out, SFFN_EINVAL, "gemv: in and out must be non-null");
   REQUIRE(n_rows >= 0, SFFN_EINVAL, "gemv: n_rows=%d must be >= 0", n_rows);
   REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "gemv: d=%d must be a positive multiple of 8", d);
@@ -191,14 +191,19 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
       REQUIRE(W0 && aligned(W0, 16), SFFN_EINVAL, "gemv: W0 must be non-null and 16-byte aligned");
     if (op == SFFN_OP_GLU_SILU || op == SFFN_OP_GATED || op == SFFN_OP_GLU_RELU)
       REQUIRE(W1 && aligned(W1, 16), SFFN_EINVAL, "gemv: W1 must be non-null and 16-byte aligned");
-    if (op == SFFN_OP_GLU_RELU || op == SFFN_OP_PREDICT)
+    if (op == SFFN_OP_GLU_RELU || op == SFFN_OP_PREDICT || op == SFFN_OP_DOT_RELU_CLUSTER)
       REQUIRE(batch == 1, SFFN_EUNSUPPORTED, "gemv: op %d runs at batch 1 only", op);
+    if (op == SFFN_OP_DOT_RELU_CLUSTER) {
+      REQUIRE(!idx, SFFN_EUNSUPPORTED, "gemv: DOT_RELU_CLUSTER processes every row (idx must be NULL)");
+      REQUIRE(group >= 1 && n_rows % group == 0, SFFN_EINVAL,
+              "gemv: DOT_RELU_CLUSTER needs group >= 1 dividing n_rows=%d (group=%d)", n_rows, group);
+    }
     REQUIRE(ld_in >= d, SFFN_EINVAL, "gemv: ld_in=%d < d=%d", ld_in, d);
     REQUIRE(ld_out >= n_rows, SFFN_EINVAL, "gemv: ld_out=%d < n_rows=%d", ld_out, n_rows);
     REQUIRE(batch > 1 || d <= 8192, SFFN_EUNSUPPORTED, "gemv: d=%d > 8192 at batch 1", d);
     REQUIRE(rms_eps >= 0.f && std::isfinite(rms_eps), SFFN_EINVAL,
             "gemv: rms_eps must be finite and >= 0");
-    if (op == SFFN_OP_DOT_RELU || op == SFFN_OP_GLU_RELU)
+    if (op == SFFN_OP_DOT_RELU || op == SFFN_OP_GLU_RELU || op == SFFN_OP_DOT_RELU_CLUSTER)
       REQUIRE(tau_scale >= 0.f && std::isfinite(tau_scale), SFFN_EINVAL,
               "gemv: tau_scale must be finite and >= 0");
     if (op == SFFN_OP_PREDICT) {
@@ -216,7 +221,8 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     if (key_out) REQUIRE(aligned(key_out, 4), SFFN_EINVAL, "gemv: key_out misaligned");
     if (items == 0) return ok();
     sffn::RowOpArgs a{op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max,
-                      idx ? group : 1, tau_scale, rms_eps, aux, ld_aux, out, key_out,
+                      (idx || op == SFFN_OP_DOT_RELU_CLUSTER) ? group : 1, tau_scale, rms_eps,
+                      aux, ld_aux, out, key_out,
                       ld_out, accumulate ? 1 : 0};
     return from_hip(batch == 1 ? sffn::launch_rowop_b1(a, s) : sffn::launch_rowop_mfma(a, s),
                     "gemv launch");
@@ -259,8 +265,14 @@ sffn_status sparse_ffn_rowop_lists(int op, int n_lists, const uint16_t* const* W
                                   float tau_scale, float rms_eps, const float* const* aux,
                                   float* const* out, uint32_t* const* key_out, int accumulate,
                                   void* stream) {
-  REQUIRE(op >= 0 && op <= 6 && op != SFFN_OP_AXPY, SFFN_EINVAL,
+  REQUIRE(op >= 0 && op <= 7 && op != SFFN_OP_AXPY, SFFN_EINVAL,
           "rowop_lists: op %d is not a row op", op);
+  if (op == SFFN_OP_DOT_RELU_CLUSTER) {
+    REQUIRE(!idx, SFFN_EUNSUPPORTED, "rowop_lists: DOT_RELU_CLUSTER processes every row (idx NULL)");
+    REQUIRE(group >= 1 && n_rows % group == 0, SFFN_EINVAL,
+            "rowop_lists: DOT_RELU_CLUSTER needs group >= 1 dividing n_rows=%d (group=%d)", n_rows,
+            group);
+  }
   REQUIRE(n_lists >= 1 && n_lists <= sffn::kMaxRowLists, SFFN_EINVAL,
           "rowop_lists: n_lists=%d must be in [1, %d]", n_lists, sffn::kMaxRowLists);
   REQUIRE(out != nullptr, SFFN_EINVAL, "rowop_lists: out (host array) must be non-null");
@@ -281,7 +293,7 @@ sffn_status sparse_ffn_rowop_lists(int op, int n_lists, const uint16_t* const* W
     REQUIRE(count && k_max, SFFN_EINVAL, "rowop_lists: idx needs count and k_max (host arrays)");
     REQUIRE(group >= 1, SFFN_EINVAL, "rowop_lists: group=%d must be >= 1", group);
   }
-  if (op == SFFN_OP_DOT_RELU || op == SFFN_OP_GLU_RELU)
+  if (op == SFFN_OP_DOT_RELU || op == SFFN_OP_GLU_RELU || op == SFFN_OP_DOT_RELU_CLUSTER)
     REQUIRE(tau_scale >= 0.f && std::isfinite(tau_scale), SFFN_EINVAL,
             "rowop_lists: tau_scale must be finite and >= 0");
   if (op == SFFN_OP_PREDICT) {
@@ -292,7 +304,8 @@ sffn_status sparse_ffn_rowop_lists(int op, int n_lists, const uint16_t* const* W
   }
   sffn::RowOpListsArgs L{};
   L.base = sffn::RowOpArgs{op, nullptr, nullptr, n_rows, d, ld_w, x, 1, d, nullptr, nullptr, 0,
-                           idx ? group : 1, tau_scale, rms_eps, nullptr, n_rows, nullptr, nullptr,
+                           (idx || op == SFFN_OP_DOT_RELU_CLUSTER) ? group : 1, tau_scale,
+                           rms_eps, nullptr, n_rows, nullptr, nullptr,
                            n_rows, accumulate ? 1 : 0};
   L.n = n_lists;
   long items = 0;

@@ -32,7 +32,12 @@
 
 namespace sffn {
 
-enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4, kOpGluRelu = 5, kOpPredict = 6 };
+enum { kOpGlu = 0, kOpDotRelu = 1, kOpGated = 2, kOpDot = 4, kOpGluRelu = 5, kOpPredict = 6,
+       kOpDotReluC = 7 };
+
+// Ops with the thresholded ReLU gate max(W x - tau, 0).
+template <int OP>
+constexpr bool relu_gate_op() { return OP == kOpDotRelu || OP == kOpDotReluC; }
 
 // Key of a row-op value: the magnitude key, or for PREDICT the order-
 // preserving key of a logit above the threshold (nonzero) and 0 otherwise.
@@ -40,6 +45,18 @@ template <int OP>
 __device__ __forceinline__ uint32_t out_key(float v, float thr) {
   if (OP == kOpPredict) return v > thr ? key_signed(v) : 0u;
   return key_abs(v);
+}
+
+// Key output of one processed row: per row, or for DOT_RELU_CLUSTER the max
+// of the magnitude keys of a cluster's nonzero rows, raised atomically in
+// key_out[row / group] (a zero row leaves it as it is).
+template <int OP>
+__device__ __forceinline__ void store_key(uint32_t* key_out, int row, int group, float v, float thr) {
+  if (OP == kOpDotReluC) {
+    if (v > 0.f) atomicMax(key_out + row / group, key_abs(v));
+  } else {
+    key_out[row] = out_key<OP>(v, thr);
+  }
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -143,7 +160,7 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     xr[j][6] = xq[j].z * m; xr[j][7] = xq[j].w * m;
   }
   float inv = 1.f, tau = 0.f;
-  if (OP == kOpDotRelu || OP == kOpGluRelu || a.rms_eps > 0.f) {
+  if (relu_gate_op<OP>() || OP == kOpGluRelu || a.rms_eps > 0.f) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -179,7 +196,7 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
       float v;
       if (OP == kOpGlu) {
         v = (g / (1.f + expf(-g))) * u;
-      } else if (OP == kOpDotRelu) {
+      } else if (relu_gate_op<OP>()) {
         v = fmaxf(g - tau, 0.f);
       } else if (OP == kOpGated) {
         v = av * u;
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
       }
       if (a.accumulate) v += pv;
       a.out[r] = v;
-      if (a.key_out) a.key_out[r] = out_key<OP>(v, a.tau_scale);
+      if (a.key_out) store_key<OP>(a.key_out, r, a.group, v, a.tau_scale);
     }
     if (++k >= its) break;
     r = row_of(k);
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
     lp0 = w0 + (size_t)row * a.ld_w;
     lp1 = kUse1 ? w1 + (size_t)row * a.ld_w : lp0;
     lpo = o + row;
-    lpk = ko ? ko + row : nullptr;
+    lpk = ko ? ko + (OP == kOpDotReluC ? row / a.group : row) : nullptr;
     lane_pv = *(a.accumulate ? lpo : a.x);
     if (OP == kOpGated) lane_av = ax[row];
     if (OP == kOpPredict) {
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
     xr[j][6] = xq[j].z * m; xr[j][7] = xq[j].w * m;
   }
   float inv = 1.f, tau = 0.f;
-  if (OP == kOpDotRelu || OP == kOpGluRelu || a.rms_eps > 0.f) {
+  if (relu_gate_op<OP>() || OP == kOpGluRelu || a.rms_eps > 0.f) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -402,7 +419,7 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
       float v;
       if (OP == kOpGlu) {
         v = (g / (1.f + expf(-g))) * u;
-      } else if (OP == kOpDotRelu) {
+      } else if (relu_gate_op<OP>()) {
         v = fmaxf(g - tau, 0.f);
       } else if (OP == kOpGated) {
         v = av * u;
@@ -415,7 +432,13 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
       }
       if (a.accumulate) v += pv;
       *po = v;
-      if (pk) *pk = out_key<OP>(v, a.tau_scale);
+      if (pk) {
+        if (OP == kOpDotReluC) {
+          if (v > 0.f) atomicMax(pk, key_abs(v));
+        } else {
+          *pk = out_key<OP>(v, a.tau_scale);
+        }
+      }
     }
     if (++k >= its) break;
     fetch(k);
@@ -460,6 +483,7 @@ hipError_t launch_rowop_lists(const RowOpListsArgs& L, hipStream_t s) {
     case kOpGated: return launch_lists_op<kOpGated>(L, s);
     case kOpGluRelu: return launch_lists_op<kOpGluRelu>(L, s);
     case kOpPredict: return launch_lists_op<kOpPredict>(L, s);
+    case kOpDotReluC: return launch_lists_op<kOpDotReluC>(L, s);
     default: return launch_lists_op<kOpDot>(L, s);
   }
 }
@@ -533,7 +557,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
     return a.idx[q] * a.group + (it - q * a.group);
   };
 
-  const bool need_norm = OP == kOpDotRelu || OP == kOpGluRelu || a.rms_eps > 0.f;
+  const bool need_norm = relu_gate_op<OP>() || OP == kOpGluRelu || a.rms_eps > 0.f;
   bool have_norm = false;
   float tau = 0.f, inv = 1.f;
   int parity = 0;
@@ -638,7 +662,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
       float v;
       if (OP == kOpGlu) {
         v = (g / (1.f + expf(-g))) * u;
-      } else if (OP == kOpDotRelu) {
+      } else if (relu_gate_op<OP>()) {
         v = fmaxf(g - tau, 0.f);
       } else if (OP == kOpGated) {
         v = a.aux[r] * u;
@@ -651,7 +675,7 @@ __global__ __launch_bounds__(1024) void rowop_b1_kernel(RowOpArgs a) {
       }
       if (a.accumulate) v += pv;
       a.out[r] = v;
-      if (a.key_out) a.key_out[r] = out_key<OP>(v, a.tau_scale);
+      if (a.key_out) store_key<OP>(a.key_out, r, a.group, v, a.tau_scale);
     }
     parity ^= 1;   // the next iteration writes the other LDS half
     if (more) {
@@ -690,7 +714,7 @@ static hipError_t launch_op(const RowOpArgs& a, hipStream_t s) {
   // Measured on MI355X at the 28-layer stack shapes: two 16-byte chunks per
   // thread per row (128-320-thread workgroups), one row (GLU: one neuron)
   // per iteration, at most 1024 (GLU) / 2048 (single matrix) workgroups.
-  const long cap = (OP == kOpGlu || OP == kOpGluRelu) ? 1024 : 2048;
+  const long cap = (OP == kOpGlu || OP == kOpGluRelu) ? 1024 : 2048;   // two matrices or one
   return launch_cfg<OP, 2, 1>(a, s, cap);    // nchunk <= 1024 (d <= 8192)
 }
 
@@ -701,6 +725,7 @@ hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s) {
     case kOpGated: return launch_op<kOpGated>(a, s);
     case kOpGluRelu: return launch_op<kOpGluRelu>(a, s);
     case kOpPredict: return launch_op<kOpPredict>(a, s);
+    case kOpDotReluC: return launch_op<kOpDotReluC>(a, s);
     default: return launch_op<kOpDot>(a, s);
   }
 }

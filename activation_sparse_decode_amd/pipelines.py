@@ -418,6 +418,8 @@ class ReluMoEStack:
         self.a = torch.zeros(top_k, N, dtype=F32, device=dev)
         self.cidx = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
         self.ccnt = torch.zeros(top_k, dtype=I32, device=dev)
+        # cluster keys raised by the gate and reset by the select that reads them
+        self.ckey = torch.zeros(top_k, self.nc, dtype=I32, device=dev)
         self.ws = B.new_workspace(1, top_k * N, d, device=dev)
 
     def route(self, logits: torch.Tensor):
@@ -445,11 +447,14 @@ class ReluMoEStack:
         ex = [self.experts[l][e] for e in chosen]
         r, a = [self.r[j] for j in range(k)], [self.a[j] for j in range(k)]
         idx, cnt = [self.cidx[j] for j in range(k)], [self.ccnt[j:j + 1] for j in range(k)]
-        B.sparse_ffn_rowop_lists(B.OP_DOT_RELU, [m[0] for m in ex], None, h, r,
+        # the gates also leave each cluster's largest |r| as its key (0: inactive)
+        B.sparse_ffn_rowop_lists(B.OP_DOT_RELU_CLUSTER, [m[0] for m in ex], None, h, r,
+                                 key_outs=[self.ckey[j] for j in range(k)], group=self.cluster,
                                  tau_scale=self.tau_scale, rms_eps=self.rms_eps)
-        # clusters holding a nonzero r, keyed by their largest |r| (one call, a row per expert)
-        B.sparse_ffn_select(self.r[:k], B.KEY_ABS_F32, 0, self.nc, cluster=self.cluster,
-                            nonzero_only=True, idx_out=self.cidx[:k], count_out=self.ccnt[:k])
+        # the clusters holding a nonzero r, ascending (one call, a row per expert);
+        # the keys are reset for the next layer as they are read
+        B.sparse_ffn_select(self.ckey[:k], B.KEY_U32, 0, self.nc, nonzero_only=True,
+                            idx_out=self.cidx[:k], count_out=self.ccnt[:k], clear_keys=True)
         B.sparse_ffn_rowop_lists(B.OP_GATED, None, [m[1] for m in ex], h, a, idxs=idx, counts=cnt,
                                  k_maxs=[self.nc] * k, group=self.cluster, auxs=r,
                                  rms_eps=self.rms_eps)

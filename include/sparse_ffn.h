@@ -86,8 +86,11 @@ typedef enum {
                                weights: one dot per output)                      */
     SFFN_OP_GLU_RELU = 5,   /* out_n = max(W0[n].x - tau_scale*||x||_2, 0) * (W1[n].x)
                                (thresholded ReGLU, both matrices in one pass)    */
-    SFFN_OP_PREDICT = 6     /* out_n = W0[n].x + aux_n (cluster logits of the online
+    SFFN_OP_PREDICT = 6,    /* out_n = W0[n].x + aux_n (cluster logits of the online
                                predictor); key nonzero iff sigmoid(out_n) > theta */
+    SFFN_OP_DOT_RELU_CLUSTER = 7 /* out_n as DOT_RELU; key_out holds cluster keys:
+                               key_out[c] = max(key_out[c], bits(out_n) & 0x7FFFFFFF)
+                               over the nonzero rows n of cluster c = n / group   */
 } sffn_gemv_op;
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
@@ -95,7 +98,7 @@ const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any signature change). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 10
+#define SFFN_ABI_VERSION 11
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -208,7 +211,15 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
  *  sqrt(mean(x_b^2) + rms_eps) (the pre-FFN normalisation of the Llama3 and
  *  Mixtral blocks the workloads are shaped like; fused, x is not modified);
  *  rms_eps = 0 uses x as given.  AXPY requires rms_eps = 0.
- *  GLU_RELU and PREDICT run at batch 1 only.  PREDICT ([PowerInfer-2] guide,
+ *  DOT_RELU_CLUSTER ([PowerInfer-2] guide, "Neuron Cluster Decomposition":
+ *  a cluster of `group` contiguous rows is active when any of its ReLU
+ *  outputs is nonzero) processes every row (idx NULL, n_rows % group == 0)
+ *  and raises key_out[n / group] (uint32 [n_rows / group], atomically) to
+ *  the magnitude key of each nonzero out_n, so that with key_out zeroed
+ *  beforehand it ends as the cluster's largest key (0 for an inactive
+ *  cluster): the keys sparse_ffn_select ranks in cluster mode, without
+ *  re-reading out (select's clear_keys re-zeroes them for the next call).
+ *  GLU_RELU, PREDICT and DOT_RELU_CLUSTER run at batch 1 only.  PREDICT ([PowerInfer-2] guide,
  *  "Online Predictor": a linear classifier over the hidden state gives each
  *  neuron cluster an activation probability sigmoid(W_pred h + b), and the
  *  clusters above a threshold theta are the ones computed): W0 = W_pred

@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 10
+    assert L.sffn_abi_version() == 11
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -174,6 +174,14 @@ def test_gemv_validation(L):
     assert rc == 1 and "bias" in msg
     rc, msg = gemv(L, op=6, tau=0.45, batch=2, ld_out=64)
     assert rc == 2 and "batch 1" in msg
+    rc, msg = gemv(L, op=7, idx=FAKE, count=FAKE, k_max=2, group=32, ld_out=64)
+    assert rc == 2 and "idx must be NULL" in msg
+    rc, msg = gemv(L, op=7, group=48, ld_out=64)
+    assert rc == 1 and "dividing" in msg
+    rc, msg = gemv(L, op=7, group=32, batch=2, ld_out=64)
+    assert rc == 2 and "batch 1" in msg
+    rc, msg = gemv(L, op=7, group=32, tau=-1.0, ld_out=64)
+    assert rc == 1 and "tau" in msg
 
 
 def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),
@@ -297,6 +305,10 @@ def test_rowop_lists_validation(L):
     assert rc == 1 and "tau" in msg
     rc, msg = rowop_lists(L, x=ctypes.c_void_p(0x1004))
     assert rc == 1 and "x must" in msg
+    rc, msg = rowop_lists(L, op=7, idx=(FAKE, FAKE), group=32)
+    assert rc == 2 and "idx NULL" in msg
+    rc, msg = rowop_lists(L, op=7, group=48)
+    assert rc == 1 and "dividing" in msg
 
 
 def test_gather_validation(L):

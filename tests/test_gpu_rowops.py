@@ -137,3 +137,37 @@ def test_rowop_lists_match_separate_calls(op):
             assert np.array_equal(host_u32(keys[l]), host_u32(rkeys[l])), (op, clustered, l)
         if clustered:
             assert np.all(host(outs[1]) == 3.0)
+
+
+def test_dot_relu_cluster_keys():
+    """DOT_RELU_CLUSTER: the outputs are DOT_RELU's bit for bit, and the
+    cluster keys are the largest magnitude key of each cluster's nonzero
+    rows, raised over what key_out held (as the oracle's cluster max key),
+    both for one matrix and over several lists."""
+    banner("dot_relu cluster keys")
+    N, d, S = 2048, 4096, 32
+    tau = 1.2815515655446004 * 0.02
+    Ws = [synth.clustered_gate_bf16(10 + e, synth.W_C3, 0, e, N, d, S) for e in range(2)]
+    x = dev(synth.tokens(10, synth.W_C3, 4, 1, d)[0])
+    outs = [torch.zeros(N, dtype=torch.float32, device="cuda") for _ in range(2)]
+    ref = [torch.zeros(N, dtype=torch.float32, device="cuda") for _ in range(2)]
+    prev = np.zeros((2, N // S), np.uint32)
+    prev[1, ::7] = 0x3F000000                         # pre-existing keys are raised, not replaced
+    keys = [dev(prev[j].copy()) for j in range(2)]
+    for j in range(2):
+        B.sparse_ffn_gemv(B.OP_DOT_RELU, dev(Ws[j]), None, x, ref[j], tau_scale=tau, rms_eps=EPS)
+    B.sparse_ffn_rowop_lists(B.OP_DOT_RELU_CLUSTER, [dev(w) for w in Ws], None, x, outs,
+                             key_outs=keys, group=S, tau_scale=tau, rms_eps=EPS)
+    single = torch.zeros(N // S, dtype=torch.int32, device="cuda")
+    out1 = torch.zeros(N, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_gemv(B.OP_DOT_RELU_CLUSTER, dev(Ws[0]), None, x, out1, key_out=single, group=S,
+                      tau_scale=tau, rms_eps=EPS)
+    torch.cuda.synchronize()
+    for j in range(2):
+        r = host(outs[j])
+        assert np.array_equal(r.view(np.uint32), host_u32(ref[j]))
+        exp = np.maximum(oracle.cluster_max_key(oracle.key_abs(r), S), prev[j])
+        assert np.array_equal(host_u32(keys[j]), exp), j
+        assert 0.05 < np.mean(exp != 0) < 0.6
+    assert np.array_equal(host_u32(out1), host_u32(ref[0]))
+    assert np.array_equal(host_u32(single), oracle.cluster_max_key(oracle.key_abs(host(ref[0])), S))
