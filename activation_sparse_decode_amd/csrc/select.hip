@@ -245,7 +245,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) incm[j] = a.include_mask[min(ebase + 64 * j, n - 1)];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) incl |= ((ebase + 64 * j < n) & (incm[j] != 0) ? 1u : 0u) << j;
+    for (int j = 0; j < KPT; ++j) incl |= (((ebase + 64 * j < n) & (incm[j] != 0)) ? 1u : 0u) << j;
   }
   uint32_t excl = 0;   // bit j: entry of slot j is in exclude_mask (clamped reads)
   if (a.exclude_mask) {
@@ -466,10 +466,13 @@ struct SelectLaunch<NT, LO> {
 // list) take the variant with one list.
 template <bool LO>
 static hipError_t launch_lo(const SelectArgs& a, hipStream_t s) {
-  // Small rows take 256 threads (cheaper barriers); from 1024 entries on,
-  // 1024 threads (up to 32 entries each) spread the work over 16 waves.
-  // Cluster mode reads n*cluster values: 1024 threads keep more loads in flight.
+  // Small rows take 256 threads (cheaper barriers), rows up to 4096 entries
+  // 512 threads, longer rows 1024 threads (up to 32 entries each) over 16
+  // waves (measured on MI355X: 4096 keys 7.8 us at 512 threads vs 8.2 at
+  // 1024; 8192 and 14336 keys faster at 1024).  Cluster mode reads
+  // n*cluster values: 1024 threads keep more loads in flight.
   if (a.n <= 1024 && (long)a.n * a.cluster <= 1024) return SelectLaunch<256, LO, 1, 2, 4>::go(a, s);
+  if (a.n <= 4096 && a.cluster == 1) return SelectLaunch<512, LO, 4, 6, 8>::go(a, s);
   return SelectLaunch<1024, LO, 1, 2, 4, 6, 8, 10, 12, 14, 16, 18, 20, 24, 28, 32>::go(a, s);
 }
 
