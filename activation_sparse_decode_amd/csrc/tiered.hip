@@ -68,13 +68,21 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
   int tile = blockIdx.x, ks = blockIdx.y;
   if (xcd_order) {
     // Workgroups go to the eight XCDs round-robin by linear id; remap so that
-    // every column tile of a row chunk runs on one XCD and the chunk's record
-    // headers and boundary lines are fetched into one L2 (needs the chunk
-    // count to be a multiple of 8).
-    const int L = blockIdx.x + gridDim.x * blockIdx.y;
+    // the column tiles of a row chunk run on one XCD (or two), and a chunk's
+    // record headers and boundary lines are fetched into one L2.
+    const int T = (int)gridDim.x, G = T * (int)gridDim.y;
+    const int L = blockIdx.x + T * blockIdx.y;
     const int x = L & 7, sl = L >> 3;
-    tile = sl % (int)gridDim.x;
-    ks = (sl / (int)gridDim.x) * 8 + x;
+    if (xcd_order == 1) {
+      // chunk count a multiple of 8: XCD x takes chunks x, x + 8, ...
+      tile = sl % T;
+      ks = (sl / T) * 8 + x;
+    } else {
+      // otherwise XCD x takes a contiguous run of the (chunk, tile) sequence
+      const int q = x * (G >> 3) + min(x, G & 7) + sl;
+      tile = q % T;
+      ks = q / T;
+    }
   }
   const int col = tile * kTileCols + 8 * lane;
   const int colc = col < a.d_out ? col : 0;   // lanes past the last output re-read output 0
@@ -177,7 +185,7 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   // XCD-grouped block order where the chunk count allows it (measured on the
   // 14336 -> 4096 down projection: 13.0 -> 11.9 us; with 12 column tiles and
   // 21 chunks the plain order is kept)
-  const int xcd_order = (ks_top + ks_mid) % 8 == 0 ? 1 : 0;
+  const int xcd_order = (ks_top + ks_mid) % 8 == 0 ? 1 : 2;
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
   hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0, s,
                      a, (int)ks_top, (int)ks_mid, xcd_order, partials);

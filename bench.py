@@ -486,12 +486,21 @@ def run_c2(args, torch, B, synth, P, T):
                                      workspace=p.ws)
 
     down_us = T.replay_ms(T.capture(down_only), args.steps) * 1e3 / (args.steps * copies)
+
+    def qkv_only():
+        for c in range(copies):
+            p = projs[c][0]
+            B.sparse_ffn_tiered_gemv(p.Wt, p.rec, p.seg_rows, xq[c], p.idx_top, p.cnt[0:1],
+                                     p.k_top, p.idx_mid, p.cnt[1:2], p.k_mid, yq[c],
+                                     workspace=p.ws)
+
+    qkv_us = T.replay_ms(T.capture(qkv_only), args.steps) * 1e3 / (args.steps * copies)
     rec_q, rec_d = projs[0][0].rec.shape[1], projs[0][1].rec.shape[1]
     qkv_b = kq_t * n_qkv * 2 + kq_m * rec_q + 8 * (kq_t + kq_m) + 4 * n_qkv
     down_b = kd_t * d * 2 + kd_m * rec_d + 8 * (kd_t + kd_m) + 4 * d
     # selection reads x (and the column norms when weight-aware), the product x again
     step_b = qkv_b + down_b + (3 if args.weight_aware else 2) * (4 * d + 4 * dff)
-    log(f"c2: {us_tok:.2f} us/token; tiered down {down_us:.2f} us")
+    log(f"c2: {us_tok:.2f} us/token; tiered down {down_us:.2f} us, tiered QKV {qkv_us:.2f} us")
 
     cpu = None
     if args.cpu_seconds > 0:
