@@ -23,13 +23,16 @@ Pages cited (by title and section / equation / figure):
   Mixed Activation Sparsity" -- abstract (weight-aware channel saliency:
   activation magnitude combined with precomputed weight norms).
 
-Readings taken where the pages are silent (each is listed in the design doc):
-magnitude ranking |v| everywhere; ties go to the lower index; a percentage p
-of N items is floor(p*N/100); NaN ranks above +Inf and -0 equals +0; Eq (1)
-is a sequential fp32 sum in token order; the dynamic set is unioned with the
-static set; the 4-bit codec is min/max affine with fp16 scale/zero; the
-weight-aware saliency of channel j is the fp32 product |x_j| * ||W[:, j]||_2
-with the weight norm precomputed in fp32.
+Readings taken where the pages are silent: magnitude ranking |v|
+everywhere; ties go to the lower index; a percentage p of N items is
+floor(p*N/100); NaN ranks above +Inf and -0 equals +0; Eq (1) is a
+sequential fp32 sum in token order; the dynamic set is unioned with the
+static set (or, with the Table 1 knobs, dynamic neurons fill the static set
+up to phi in frequency order); the 4-bit codec is min/max affine with fp16
+scale/zero; the weight-aware saliency of channel j is the fp32 product
+|x_j| * ||W[:, j]||_2 with the weight norm precomputed in fp32; the online
+predictor's clusters are those with sigmoid(z) > theta, decided on the fp32
+logit.
 
 Parity status: every function below is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, special cases, invariants); none is unpinned.
