@@ -64,7 +64,7 @@ typedef enum {
 typedef enum {
     SFFN_KEY_ABS_F32 = 0,   /* fp32 input, key = bits & 0x7FFFFFFF: orders |v|;
                                -0 == +0; NaN above +Inf ([SelectInfer] §2.2 ranks
-                               "by absolute activation value")                  */
+                               neurons by activation magnitude)                 */
     SFFN_KEY_U32 = 1,       /* uint32 input used as the key (frequency counts)  */
     SFFN_KEY_F32 = 2        /* fp32 input ordered by signed value (router logits) */
 } sffn_key_type;

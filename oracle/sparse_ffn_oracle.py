@@ -62,8 +62,8 @@ def count_of(pct: int, n: int) -> int:
 def key_abs(v: np.ndarray) -> np.ndarray:
     """Magnitude key of fp32 values: the fp32 bits with the sign cleared.
 
-    Ordering these uint32 keys orders |v| (SelectInfer §2.2 ranks neurons
-    "by absolute activation value"; Eq (1) scores are sums of |a|).  -0 and
+    Ordering these uint32 keys orders |v| (SelectInfer §2.2 ranks neurons by
+    the magnitude of their activations; Eq (1) scores are sums of |a|).  -0 and
     +0 get the same key; NaN keys sort above +Inf."""
     v = np.ascontiguousarray(v, dtype=np.float32)
     return v.view(np.uint32) & np.uint32(0x7FFFFFFF)
