@@ -171,3 +171,49 @@ def test_dot_relu_cluster_keys():
         assert 0.05 < np.mean(exp != 0) < 0.6
     assert np.array_equal(host_u32(out1), host_u32(ref[0]))
     assert np.array_equal(host_u32(single), oracle.cluster_max_key(oracle.key_abs(host(ref[0])), S))
+
+
+def test_dot_relu_cluster_keys_wide_rows():
+    """DOT_RELU_CLUSTER on rows wider than the wave kernel's limit (the
+    workgroup-per-row kernel): same outputs as DOT_RELU, oracle cluster keys."""
+    banner("dot_relu cluster keys, wide rows")
+    N, d, S = 1024, 6144, 32
+    tau = 1.2815515655446004 * 0.02
+    W = synth.clustered_gate_bf16(12, synth.W_C3, 0, 0, N, d, S)
+    x = dev(synth.tokens(12, synth.W_C3, 5, 1, d)[0])
+    out = torch.zeros(N, dtype=torch.float32, device="cuda")
+    ref = torch.zeros(N, dtype=torch.float32, device="cuda")
+    keys = torch.zeros(N // S, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_gemv(B.OP_DOT_RELU, dev(W), None, x, ref, tau_scale=tau, rms_eps=EPS)
+    B.sparse_ffn_gemv(B.OP_DOT_RELU_CLUSTER, dev(W), None, x, out, key_out=keys, group=S,
+                      tau_scale=tau, rms_eps=EPS)
+    torch.cuda.synchronize()
+    r = host(out)
+    assert np.array_equal(r.view(np.uint32), host_u32(ref))
+    assert np.array_equal(host_u32(keys), oracle.cluster_max_key(oracle.key_abs(r), S))
+    assert np.any(host_u32(keys)) and not np.all(host_u32(keys))
+
+
+def test_rowop_lists_eight_lists():
+    """The maximum of eight lists, with ragged counts (one empty), against
+    one call per list, bitwise."""
+    banner("rowop lists x8")
+    rng = np.random.default_rng(13)
+    N, d, S = 1024, 2048, 32
+    Wg = [dev(synth.weight_bf16(13, synth.W_C3, 1, e, synth.T_GATE, N, d)) for e in range(8)]
+    Wu = [dev(synth.weight_bf16(13, synth.W_C3, 1, e, synth.T_UP, N, d)) for e in range(8)]
+    x = dev(synth.tokens(13, synth.W_C3, 6, 1, d)[0])
+    counts = [5, 0, 32, 17, 1, 9, 23, 2]
+    idx = [dev(np.sort(rng.choice(N // S, size=32, replace=False)).astype(np.int32)) for _ in range(8)]
+    cnt = [dev(np.array([c], np.int32)) for c in counts]
+    outs = [torch.full((N,), -2.0, dtype=torch.float32, device="cuda") for _ in range(8)]
+    refs = [o.clone() for o in outs]
+    for l in range(8):
+        B.sparse_ffn_gemv(B.OP_GLU_RELU, Wg[l], Wu[l], x, refs[l], idx=idx[l], count=cnt[l],
+                          k_max=N // S, group=S, tau_scale=0.02, rms_eps=EPS)
+    B.sparse_ffn_rowop_lists(B.OP_GLU_RELU, Wg, Wu, x, outs, idxs=idx, counts=cnt,
+                             k_maxs=[N // S] * 8, group=S, tau_scale=0.02, rms_eps=EPS)
+    torch.cuda.synchronize()
+    for l in range(8):
+        assert np.array_equal(host_u32(outs[l]), host_u32(refs[l])), l
+    assert np.all(host(outs[1]) == -2.0)
