@@ -114,6 +114,27 @@ class Timer:
         torch.cuda.synchronize()
         return g
 
+    def step_stats(self, graphs, reps, before=None, per_step=1):
+        """Median, p10 and p90 of the per-replay time (us per unit of work), in
+        a pass of its own with HIP events around every replay (the per-step
+        input copies of before(i) fall outside the pairs).  `graphs` is one
+        graph replayed `reps` times, or a list replayed in turn."""
+        torch = self.torch
+        seq = graphs if isinstance(graphs, (list, tuple)) else [graphs] * reps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in seq]
+        for i, g in enumerate(seq):
+            if before:
+                before(i)
+            ev[i][0].record()
+            g.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) * 1e3 / per_step for a, b in ev])
+        return {"median_us": round(float(np.median(t)), 3),
+                "p10_us": round(float(np.percentile(t, 10)), 3),
+                "p90_us": round(float(np.percentile(t, 90)), 3), "replays": len(seq)}
+
     def replay_ms(self, g, reps, before=None):
         """Total ms of `reps` replays (each optionally preceded by before(i))."""
         torch = self.torch
@@ -225,6 +246,7 @@ def run_c1(args, torch, B, synth, P, T):
     total_ms = T.replay_ms(g, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
     us_tok = total_ms * 1e3 / args.steps
     log(f"decode: {us_tok:.1f} us/token over {args.steps} steps")
+    dist = T.step_stats(g, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
 
     gg = T.capture(lambda: [stack.decode_gate_up(l, h) for l in range(L)])
     glu_us = T.replay_ms(gg, args.steps) * 1e3 / (args.steps * L)
@@ -257,6 +279,7 @@ def run_c1(args, torch, B, synth, P, T):
                   step_bytes=step_bytes,
                   step_GBps=round(step_bytes / (us_tok * 1e-6) / 1e9, 1),
                   step_frac_of_peak=round(step_bytes / (us_tok * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  step_stats=dist,
                   setup={"calibrate_ms": round(calib_ms, 2), "prefill_ms": round(prefill_ms, 2)},
                   roofline=roofline("rowop_wave_kernel<GLU> (gate/up over the compacted union)",
                                     glu_total / L, glu_us,
@@ -326,6 +349,7 @@ def run_c1_loading(args, torch, B, synth, P, T):
     total_ms = T.replay_ms(g, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
     us_tok = total_ms * 1e3 / args.steps
     log(f"decode: {us_tok:.1f} us/token over {args.steps} steps")
+    dist = T.step_stats(g, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
     gg = T.capture(lambda: [stack.decode_gate_up(l, h) for l in range(L)])
     glu_us = T.replay_ms(gg, args.steps) * 1e3 / (args.steps * L)
     log(f"gate/up (28 launches, mixed sizes): {glu_us:.2f} us/launch")
@@ -361,6 +385,7 @@ def run_c1_loading(args, torch, B, synth, P, T):
                   step_bytes=step_bytes,
                   step_GBps=round(step_bytes / (us_tok * 1e-6) / 1e9, 1),
                   step_frac_of_peak=round(step_bytes / (us_tok * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  step_stats=dist,
                   setup={"profile_ms": round(profile_ms, 2), "load_ms": round(load_ms, 2),
                          "prefill_ms": round(prefill_ms, 2)},
                   roofline=roofline("rowop_wave_kernel<GLU> (gate/up of every layer, mean launch)",
@@ -392,9 +417,12 @@ def run_c0(args, torch, B, synth, P, T):
         for c in range(copies):
             lay[c](xbuf[c], y[c])
 
-    total_ms = T.replay_ms(T.capture(step), args.steps,
+    gs = T.capture(step)
+    total_ms = T.replay_ms(gs, args.steps,
                            before=lambda i: xbuf.copy_(X[i * copies:(i + 1) * copies]))
     us_tok = total_ms * 1e3 / (args.steps * copies)
+    dist = T.step_stats(gs, args.steps, before=lambda i: xbuf.copy_(X[i * copies:(i + 1) * copies]),
+                        per_step=copies)
 
     def glu_only():
         for c in range(copies):
@@ -436,7 +464,8 @@ def run_c0(args, torch, B, synth, P, T):
                               "gathered_down": round(down_us, 3)},
                   gathered_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
                   roofline=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us),
-                  cpu_baseline=cpu)
+                  cpu_baseline=cpu,
+                  step_stats=dist)
 
 
 # ============================================================ c2: SpAx three-tier read
@@ -475,8 +504,10 @@ def run_c2(args, torch, B, synth, P, T):
         xq.copy_(Xq[i * copies:(i + 1) * copies])
         xd.copy_(Xd[i * copies:(i + 1) * copies])
 
-    total_ms = T.replay_ms(T.capture(step), args.steps, before=before)
+    gs = T.capture(step)
+    total_ms = T.replay_ms(gs, args.steps, before=before)
     us_tok = total_ms * 1e3 / (args.steps * copies)
+    dist = T.step_stats(gs, args.steps, before=before, per_step=copies)
 
     def down_only():
         for c in range(copies):
@@ -537,7 +568,8 @@ def run_c2(args, torch, B, synth, P, T):
                   dense_equivalent_bytes=(d * n_qkv + dff * d) * 2,
                   roofline=roofline("tiered_kernel (down 14336->4096, 15% bf16 + 35% 4-bit)",
                                     down_b, down_us),
-                  cpu_baseline=cpu)
+                  cpu_baseline=cpu,
+                  step_stats=dist)
 
 
 # ============================================================ c3: ReLU-sparse MoE stack
@@ -592,6 +624,7 @@ def run_c3(args, torch, B, synth, P, T):
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
     us_tok = total_ms * 1e3 / steps
+    dist = T.step_stats(graphs, steps)
     if args.predictor:
         # per routed expert: predictor rows, bias, logits and keys; per
         # predicted cluster: gate, up and down rows, a written and read
@@ -670,7 +703,8 @@ def run_c3(args, torch, B, synth, P, T):
     return result(us_tok, "us/token", steps, 2, total_ms / steps, config, step_bytes=step_b,
                   step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
                   roofline=roofline(dom_name, dom_b, gate_us),
-                  cpu_baseline=cpu)
+                  cpu_baseline=cpu,
+                  step_stats=dist)
 
 
 # ============================================================ c4: batched union on MFMA
@@ -696,9 +730,12 @@ def run_c4(args, torch, B, synth, P, T):
         for c in range(copies):
             lays[c](xb[c], Y[c])
 
-    total_ms = T.replay_ms(T.capture(step), args.steps,
+    gs = T.capture(step)
+    total_ms = T.replay_ms(gs, args.steps,
                            before=lambda i: xb.copy_(X[i * copies:(i + 1) * copies]))
     us_batch = total_ms * 1e3 / (args.steps * copies)
+    dist = T.step_stats(gs, args.steps, before=lambda i: xb.copy_(X[i * copies:(i + 1) * copies]),
+                        per_step=copies * batch)
     u = float(np.mean([int(l.cnt.cpu()[0]) for l in lays]))
 
     def glu_only():
@@ -741,7 +778,8 @@ def run_c4(args, torch, B, synth, P, T):
                   union_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
                   roofline=roofline("rowop_mfma_kernel<GLU> (batched gate/up)" if batch > 1 else
                                     "rowop_wave_kernel<GLU> (gate/up, batch 1)", glu_b, glu_us),
-                  cpu_baseline=cpu)
+                  cpu_baseline=cpu,
+                  step_stats=dist)
 
 
 def main():
@@ -763,6 +801,10 @@ def main():
     run = {"c0": run_c0, "c1": run_c1, "c1-loading": run_c1_loading, "c2": run_c2, "c3": run_c3,
            "c4": run_c4}[args.workload]
     out = run(args, torch, B, synth, P, T)
+    props = torch.cuda.get_device_properties(0)
+    out["env"] = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+                  "compute_units": props.multi_processor_count,
+                  "hip": torch.version.hip, "torch": torch.__version__}
 
     # A plain device copy of known size: the reference that scales the HBM
     # counters (FETCH_SIZE / WRITE_SIZE) of profiled kernels to bytes.
