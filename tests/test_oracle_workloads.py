@@ -140,6 +140,15 @@ def test_selective_loading_fixture():
     assert [r[0], r[-1]] == g["expected_modified"] and len(r) == 21
 
 
+def test_modified_layers_range_forms():
+    # last <= 0 counts from the end, last > 0 is an exclusive bound
+    assert list(oracle.modified_layers(28, 0, 0)) == list(range(28))
+    assert list(oracle.modified_layers(28, 5, -2)) == list(range(5, 26))
+    assert list(oracle.modified_layers(6, 1, -1)) == [1, 2, 3, 4]
+    assert list(oracle.modified_layers(28, 4, 27)) == list(range(4, 27))
+    assert list(oracle.modified_layers(3, 3, 0)) == []
+
+
 def brute_fill(start, values, total):
     """Walk the entries by (|value| desc, index asc) with Python floats,
     adding those not yet present, until ``total`` are present."""
