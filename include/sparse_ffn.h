@@ -96,7 +96,8 @@ typedef enum {
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* sffn_last_error(void);
 
-/* ABI revision of this header (bumped on any signature change). */
+/* ABI revision of this header (bumped on any change of a signature or of what
+   a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
 #define SFFN_ABI_VERSION 11
 
