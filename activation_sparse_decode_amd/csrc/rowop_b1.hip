@@ -120,9 +120,13 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
   // are requested (x is usually the previous kernel's output, so waiting for
   // it first would add a round trip to every wave); the empty asm (a
   // compiler barrier that also redefines `zero`) keeps the conversion of x
-  // and the norm from moving ahead of those loads.  The loop is rotated:
-  // reduce and store row k, then request row k+1, so each row's FMAs start
-  // a block and consume its loads in arrival order.
+  // and the norm from moving ahead of those loads.  With one weight matrix
+  // the row loads are double-buffered: row k+1 is requested before row k is
+  // reduced, so the wave's reduction and store overlap the next row's
+  // fetch (measured on 28 layers of 3072 x 2736 down projections: 5.31 ->
+  // 5.11 us per launch).  With two matrices (gate and up) the registers go
+  // to the second matrix instead (measured: no gain from a second buffer),
+  // and the loop is rotated: reduce and store row k, then request row k+1.
   int coff[NCH];
   float xm[NCH];
   float4 xp[NCH], xq[NCH];
@@ -134,18 +138,18 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     xp[j] = *reinterpret_cast<const float4*>(a.x + coff[j]);
     xq[j] = *reinterpret_cast<const float4*>(a.x + coff[j] + 4);
   }
-  uint4 v0[NCH], v1[NCH];
-  auto fetch = [&](int r) {
+  constexpr int NB = (kUse0 && kUse1) ? 1 : 2;   // row buffers
+  uint4 v0[NB][NCH], v1[NB][NCH];
+  auto fetch = [&](int r, int b) {
     const size_t base = (size_t)r * a.ld_w;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      if (kUse0) v0[j] = load_stream(a.W0 + base + coff[j]);
-      if (kUse1) v1[j] = load_stream(a.W1 + base + coff[j]);
+      if (kUse0) v0[b][j] = load_stream(a.W0 + base + coff[j]);
+      if (kUse1) v1[b][j] = load_stream(a.W1 + base + coff[j]);
     }
   };
   auto row_of = [&](int k) { return a.idx ? __builtin_amdgcn_readlane(lane_row, k) : gw + W * k; };
-  int r = row_of(0);
-  fetch(r);
+  fetch(row_of(0), 0);
 
   int zero = 0;
   asm volatile("" : "+v"(zero) : : "memory");
@@ -171,18 +175,19 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     tau = a.tau_scale * sqrtf(ss) * inv;   // ||x s|| for the ReLU threshold
   }
 
-  for (int k = 0;;) {
+  // reduce row k (held in buffer b) and store its result
+  auto finish = [&](int k, int b) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       float f[8];
       if (kUse0) {
-        unpack8(v0[j], f);
+        unpack8(v0[b][j], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s0 = fmaf(f[e], xr[j][e], s0);
       }
       if (kUse1) {
-        unpack8(v1[j], f);
+        unpack8(v1[b][j], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s1 = fmaf(f[e], xr[j][e], s1);
       }
@@ -191,6 +196,7 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
     if (kUse1) s1 = wave_sum(s1);
     const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_pv), k));
     const float av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_av), k));
+    const int r = row_of(k);
     if (lane == 0) {
       const float g = s0 * inv, u = s1 * inv;
       float v;
@@ -211,9 +217,22 @@ __global__ __launch_bounds__(256) void rowop_wave_kernel(RowOpArgs a) {
       a.out[r] = v;
       if (a.key_out) store_key<OP>(a.key_out, r, a.group, v, a.tau_scale);
     }
-    if (++k >= its) break;
-    r = row_of(k);
-    fetch(r);
+  };
+
+  if constexpr (NB == 2) {
+    for (int k = 0; k < its; k += 2) {
+      if (k + 1 < its) fetch(row_of(k + 1), 1);
+      finish(k, 0);
+      if (k + 1 >= its) break;
+      if (k + 2 < its) fetch(row_of(k + 2), 0);
+      finish(k + 1, 1);
+    }
+  } else {
+    for (int k = 0;;) {
+      finish(k, 0);
+      if (++k >= its) break;
+      fetch(row_of(k), 0);
+    }
   }
 }
 
@@ -356,17 +375,18 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
     xp[j] = *reinterpret_cast<const float4*>(a.x + coff[j]);
     xq[j] = *reinterpret_cast<const float4*>(a.x + coff[j] + 4);
   }
-  uint4 v0[NCH], v1[NCH];
-  auto fetch = [&](int k) {
+  constexpr int NB = (kUse0 && kUse1) ? 1 : 2;   // row buffers, as above
+  uint4 v0[NB][NCH], v1[NB][NCH];
+  auto fetch = [&](int k, int b) {
     const uint16_t* p0 = lane_ptr(lp0, k);
     const uint16_t* p1 = kUse1 ? lane_ptr(lp1, k) : p0;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      if (kUse0) v0[j] = load_stream(p0 + coff[j]);
-      if (kUse1) v1[j] = load_stream(p1 + coff[j]);
+      if (kUse0) v0[b][j] = load_stream(p0 + coff[j]);
+      if (kUse1) v1[b][j] = load_stream(p1 + coff[j]);
     }
   };
-  fetch(0);
+  fetch(0, 0);
 
   int zero = 0;
   asm volatile("" : "+v"(zero) : : "memory");
@@ -392,18 +412,18 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
     tau = a.tau_scale * sqrtf(ss) * inv;
   }
 
-  for (int k = 0;;) {
+  auto finish = [&](int k, int b) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       float f[8];
       if (kUse0) {
-        unpack8(v0[j], f);
+        unpack8(v0[b][j], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s0 = fmaf(f[e], xr[j][e], s0);
       }
       if (kUse1) {
-        unpack8(v1[j], f);
+        unpack8(v1[b][j], f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s1 = fmaf(f[e], xr[j][e], s1);
       }
@@ -440,8 +460,22 @@ __global__ __launch_bounds__(256) void rowop_lists_kernel(RowOpListsArgs L) {
         }
       }
     }
-    if (++k >= its) break;
-    fetch(k);
+  };
+
+  if constexpr (NB == 2) {
+    for (int k = 0; k < its; k += 2) {
+      if (k + 1 < its) fetch(k + 1, 1);
+      finish(k, 0);
+      if (k + 1 >= its) break;
+      if (k + 2 < its) fetch(k + 2, 0);
+      finish(k + 1, 1);
+    }
+  } else {
+    for (int k = 0;;) {
+      finish(k, 0);
+      if (++k >= its) break;
+      fetch(k, 0);
+    }
   }
 }
 
