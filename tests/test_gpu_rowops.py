@@ -4,7 +4,8 @@ kernel.  Widths cover ragged chunk counts, the wave kernel's limit and the
 wider path; 2912 rows give several rows per wave.  Cases: SwiGLU with keys
 (dense, with the fused RMSNorm, and over a gathered index list that leaves
 other rows untouched), plain dots added to an output, the thresholded ReLU
-gate and the gated product over 32-row clusters."""
+gate and the gated product over 32-row clusters; tall single-matrix cases
+give up to seven rows per wave."""
 import numpy as np
 import pytest
 import torch
@@ -89,6 +90,58 @@ def test_dot_relu_and_gated(d):
     assert np.all(got[np.setdiff1d(np.arange(N), rows)] == -9.0), "a row outside the clusters was written"
     ref = aux[rows].astype(np.float64) * oracle.row_dots(W1, xn, rows)
     assert_close(got[rows], ref, what=f"gated product d={d}")
+
+
+@pytest.mark.parametrize("n_rows", [40000, 57000])
+def test_single_matrix_many_rows_per_wave(n_rows):
+    """Single-matrix row ops keep two rows in flight per wave.  40000 and
+    57000 rows give 4-5 and 6-7 rows per wave on the plain path (2048
+    workgroups), a quarter of them gathered 4-5 and 6-7 on the gathered path
+    (512 workgroups), so the two-buffer loop ends on either buffer and waves
+    one row short of the others.  Dots, the ReLU gate and two row lists (bitwise
+    what separate calls write) against the oracle."""
+    banner(f"rowops single-matrix rows={n_rows}")
+    d = 256
+    W0 = synth.weight_bf16(13, synth.W_C0, 9, 0, synth.T_GATE, n_rows, d)
+    x = synth.tokens(13, synth.W_C0, 9, 1, d)[0]
+    rng = np.random.default_rng(n_rows)
+    y0 = rng.standard_normal(n_rows).astype(np.float32)
+    y = dev(y0)
+    B.sparse_ffn_gemv(B.OP_DOT, dev(W0), None, dev(x), y, accumulate=True)
+    torch.cuda.synchronize()
+    assert_close(host(y), y0 + oracle.row_dots(W0, x), what=f"dot, {n_rows} rows")
+
+    q = 1.2815515655446004 * synth.WEIGHT_STD
+    r = torch.zeros(n_rows, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_gemv(B.OP_DOT_RELU, dev(W0), None, dev(x), r, tau_scale=q, rms_eps=EPS)
+    torch.cuda.synchronize()
+    xn = oracle.rms_normalize(x, EPS)
+    tau = oracle.relu_threshold(xn, 1.2815515655446004, synth.WEIGHT_STD)
+    assert_close(host(r), oracle.relu_gate(W0, xn, tau), what=f"ReLU gate, {n_rows} rows")
+
+    k = n_rows // 4
+    sel = np.sort(rng.choice(n_rows, size=k, replace=False)).astype(np.int32)
+    cnt = torch.tensor([k], dtype=torch.int32, device="cuda")
+    g = torch.full((n_rows,), 4321.0, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_gemv(B.OP_DOT, dev(W0), None, dev(x), g, idx=dev(sel), count=cnt, k_max=k)
+    torch.cuda.synchronize()
+    gg = host(g)
+    assert np.all(gg[np.setdiff1d(np.arange(n_rows), sel)] == 4321.0), "an unselected row was written"
+    assert_close(gg[sel], oracle.row_dots(W0, x, sel), what=f"gathered dot, {k} of {n_rows} rows")
+
+    h = n_rows // 2
+    Wd = dev(W0)
+    halves = [Wd[:h], Wd[h:]]
+    outs = [torch.zeros(h, dtype=torch.float32, device="cuda") for _ in range(2)]
+    refs = [torch.zeros(h, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for l in range(2):
+        B.sparse_ffn_gemv(B.OP_DOT, halves[l], None, dev(x), refs[l])
+    B.sparse_ffn_rowop_lists(B.OP_DOT, halves, None, dev(x), outs)
+    torch.cuda.synchronize()
+    for l in range(2):
+        assert np.array_equal(host_u32(outs[l]), host_u32(refs[l])), ("lists", l)
+    assert_close(np.concatenate([host(o) for o in outs]), oracle.row_dots(W0, x),
+                 what=f"two row lists, {n_rows} rows")
 
 
 @pytest.mark.parametrize("op", ["glu", "dot_relu", "gated", "dot", "glu_relu", "predict"])
