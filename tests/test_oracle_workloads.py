@@ -287,6 +287,38 @@ def test_predicted_expert_special_cases():
     assert none["rows"].size == 0 and not np.any(none["y"])
 
 
+def test_relu_glu_rows_worked_example():
+    # gate rows (1, 2) and (-1, 0.5), up rows (3, 0) and (0, 4), h = (1, 1),
+    # tau = 1: gate dots 3 and -0.5, up dots 3 and 4, so a = (max(3 - 1, 0) * 3,
+    # max(-0.5 - 1, 0) * 4) = (6, 0).  A dropped threshold gives 9 for row 0,
+    # swapped gate and up rows -1.5 for row 1, a wrong row subset the other value.
+    Wg = bf16([[1.0, 2.0], [-1.0, 0.5]])
+    Wu = bf16([[3.0, 0.0], [0.0, 4.0]])
+    h = np.array([1.0, 1.0])
+    assert oracle.relu_glu_rows(Wg, Wu, h, 1.0, np.array([0, 1])).tolist() == [6.0, 0.0]
+    assert oracle.relu_glu_rows(Wg, Wu, h, 1.0, np.array([1, 0])).tolist() == [0.0, 6.0]
+    assert oracle.relu_glu_rows(Wg, Wu, h, 1.0, np.array([1])).tolist() == [0.0]
+    # tau = -1 lets row 1's gate through: max(-0.5 + 1, 0) * 4 = 2
+    assert oracle.relu_glu_rows(Wg, Wu, h, -1.0, np.array([0, 1])).tolist() == [12.0, 2.0]
+
+
+def test_active_clusters_bruteforce():
+    rng = np.random.default_rng(41)
+    for trial in range(100):
+        c = int(rng.choice([1, 2, 4, 32]))
+        n = c * int(rng.integers(1, 40))
+        r = np.maximum(rng.standard_normal(n), 0.0).astype(np.float32)
+        if trial % 3 == 0:   # whole clusters at zero, some with a single nonzero value
+            dead = rng.random(n // c) < 0.6
+            r.reshape(-1, c)[dead] = 0.0
+            lone = np.flatnonzero(dead)[: max(1, dead.sum() // 3)]
+            r.reshape(-1, c)[lone, rng.integers(0, c)] = np.float32(1e-30)
+        if trial == 7:
+            r[:] = 0.0
+        expected = [q for q in range(n // c) if any(v != 0.0 for v in r[q * c:(q + 1) * c])]
+        assert oracle.active_clusters(r, c).tolist() == expected, (trial, c, n)
+
+
 # ------------------------------------------------------------------ WiSparse weight-aware saliency
 def test_row_norms_closed_forms():
     d = 16
