@@ -463,7 +463,9 @@ def run_c0(args, torch, B, synth, P, T):
                   kernels_us={"gate_up_dense": round(glu_us, 3), "select": round(sel_us, 3),
                               "gathered_down": round(down_us, 3)},
                   gathered_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us),
+                  roofline=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us,
+                                    measured_traffic("rowop_glu_swiglu_top50_layer",
+                                                     ["rowop_b1.hip", "sffn_device.h"])),
                   cpu_baseline=cpu,
                   step_stats=dist)
 
@@ -702,7 +704,10 @@ def run_c3(args, torch, B, synth, P, T):
                   round(float(counts.mean() / nc), 4)}
     return result(us_tok, "us/token", steps, 2, total_ms / steps, config, step_bytes=step_b,
                   step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
-                  roofline=roofline(dom_name, dom_b, gate_us),
+                  roofline=roofline(dom_name, dom_b, gate_us,
+                                    None if args.predictor else
+                                    measured_traffic("rowop_relu_gate_moe",
+                                                     ["rowop_b1.hip", "sffn_device.h"])),
                   cpu_baseline=cpu,
                   step_stats=dist)
 

@@ -41,10 +41,11 @@ def _sha(csrc):
     return h.hexdigest()
 
 
-def test_committed_traffic_follows_its_sources():
-    with open(os.path.join(ROOT, "profiles", f"traffic_{TAG}.json")) as fh:
+@pytest.mark.parametrize("tag", [TAG, "rowop_glu_swiglu_top50_layer", "rowop_relu_gate_moe"])
+def test_committed_traffic_follows_its_sources(tag):
+    with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.json")) as fh:
         rec = json.load(fh)
-    got = bench.measured_traffic(TAG, SOURCES)
+    got = bench.measured_traffic(tag, SOURCES)
     if rec["source_sha256"] == _sha(bench.CSRC):
         assert got == rec["bytes_per_launch"] and got > 0
     else:
