@@ -569,7 +569,10 @@ def run_c2(args, torch, B, synth, P, T):
                   step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
                   dense_equivalent_bytes=(d * n_qkv + dff * d) * 2,
                   roofline=roofline("tiered_kernel (down 14336->4096, 15% bf16 + 35% 4-bit)",
-                                    down_b, down_us),
+                                    down_b, down_us,
+                                    None if args.weight_aware else
+                                    measured_traffic("tiered_down_spax",
+                                                     ["tiered.hip", "axpy_b1.hip", "sffn_device.h"])),
                   cpu_baseline=cpu,
                   step_stats=dist)
 

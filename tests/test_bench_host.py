@@ -33,20 +33,22 @@ def test_roofline_fields():
     assert rf["traffic"] == 8_100_000
 
 
-def _sha(csrc):
+def _sha(csrc, sources=SOURCES):
     h = hashlib.sha256()
-    for name in SOURCES:
+    for name in sources:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-@pytest.mark.parametrize("tag", [TAG, "rowop_glu_swiglu_top50_layer", "rowop_relu_gate_moe"])
+@pytest.mark.parametrize("tag", [TAG, "rowop_glu_swiglu_top50_layer", "rowop_relu_gate_moe",
+                                 "tiered_down_spax"])
 def test_committed_traffic_follows_its_sources(tag):
     with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.json")) as fh:
         rec = json.load(fh)
-    got = bench.measured_traffic(tag, SOURCES)
-    if rec["source_sha256"] == _sha(bench.CSRC):
+    sources = rec.get("sources", SOURCES)
+    got = bench.measured_traffic(tag, sources)
+    if rec["source_sha256"] == _sha(bench.CSRC, sources):
         assert got == rec["bytes_per_launch"] and got > 0
     else:
         assert got is None
