@@ -112,6 +112,8 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
   REQUIRE(cluster >= 1, SFFN_EINVAL, "select: cluster=%d must be >= 1", cluster);
   REQUIRE(cluster == 1 || n <= 4096, SFFN_EUNSUPPORTED,
           "select: n=%d clusters exceed 4096 (the cluster-mode limit)", n);
+  REQUIRE(cluster == 1 || (long)n * cluster <= (1L << 30), SFFN_EUNSUPPORTED,
+          "select: n*cluster=%ld values exceed 2^30 (the cluster-mode limit)", (long)n * cluster);
   REQUIRE((long)ld >= (long)n * cluster, SFFN_EINVAL, "select: ld=%d < n*cluster=%ld", ld,
           (long)n * cluster);
   REQUIRE(r_lo >= 0 && r_lo <= r_hi, SFFN_EINVAL, "select: need 0 <= r_lo=%d <= r_hi=%d", r_lo,

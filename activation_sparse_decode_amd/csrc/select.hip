@@ -198,12 +198,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
   } else {
     // cluster keys: coalesced reads of the n*cluster values, max per cluster
-    // in LDS (the value index i belongs to cluster floor((i + 0.5) / cluster),
-    // exact in fp32 for these sizes)
+    // in LDS (value i belongs to cluster i / cluster, an exact unsigned
+    // integer division for every accepted cluster size)
     for (int c = t; c < n; c += NT) ckey[c] = 0u;
     __syncthreads();
     const int total = n * a.cluster;
-    const float inv = 1.0f / (float)a.cluster;
+    const uint32_t csz = (uint32_t)a.cluster;
     if ((a.cluster & 3) == 0 && (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.keys) & 15) == 0) {
       // 4 values of one cluster per load; 8 loads in flight per thread
       for (int i0 = 4 * t; i0 < total; i0 += 32 * NT) {
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           const uint32_t m =
               max(max(key_of_bits(a.key_type, v[u].x), key_of_bits(a.key_type, v[u].y)),
                   max(key_of_bits(a.key_type, v[u].z), key_of_bits(a.key_type, v[u].w)));
-          if (i < total && m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+          if (i < total && m) atomicMax(&ckey[(uint32_t)i / csz], m);
         }
       }
     } else {
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int u = 0; u < 8; ++u) {
           const int i = i0 + NT * u;
           const uint32_t m = key_of_bits(a.key_type, v[u]);
-          if (i < total && m) atomicMax(&ckey[(int)(((float)i + 0.5f) * inv)], m);
+          if (i < total && m) atomicMax(&ckey[(uint32_t)i / csz], m);
         }
       }
     }

@@ -140,7 +140,9 @@ sffn_status sparse_ffn_score(int mode, const float* in, int T, int n, int ld,
  *                 largest key of the block ([PowerInfer-2] "Neuron Cluster
  *                 Decomposition": a cluster is selected as a unit); 1 for
  *                 single values.  ld >= n * cluster; with cluster > 1,
- *                 n <= 4096.
+ *                 n <= 4096 and n * cluster <= 2^30 (else
+ *                 SFFN_EUNSUPPORTED).  Value i belongs to cluster
+ *                 i / cluster exactly, for any cluster size.
  *  key_scale    : nullable fp32 [n]; with SFFN_KEY_ABS_F32 keys and
  *                 cluster == 1 only.  The key of entry j becomes the magnitude
  *                 key of the fp32 product keys[r][j] * key_scale[j]: the

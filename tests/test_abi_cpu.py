@@ -88,6 +88,8 @@ def test_select_validation(L):
     assert rc == 1 and "n*cluster" in msg
     rc, msg = select(L, n=5000, ld=10000, cluster=2)
     assert rc == 2 and "4096" in msg
+    rc, msg = select(L, n=4096, ld=2**31 - 1, cluster=(1 << 18) + 1)
+    assert rc == 2 and "2^30" in msg
     # the top list holds the ranks [0, r_lo)
     rc, msg = select(L, r_lo=3, r_hi=6, idx_top=FAKE, ld_idx_top=2)
     assert rc == 1 and "ld_idx_top" in msg

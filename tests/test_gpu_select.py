@@ -140,6 +140,34 @@ def test_cluster_keys():
                     assert np.array_equal(exp, oracle.active_clusters(r[row], c))
 
 
+@pytest.mark.parametrize("n_c,c", [(4096, 3), (4096, 7), (1000, 2047), (4096, 2000), (4096, 4095)])
+def test_cluster_keys_large(n_c, c):
+    """Large clusters whose size is not a power of two: every cluster's two
+    largest values sit on its first and last entry (distinct per cluster),
+    so a value credited to a neighbouring cluster changes the keys and the
+    ranking."""
+    banner(f"select cluster keys n={n_c} cluster={c}")
+    rng = np.random.default_rng(n_c + c)
+    r = (rng.random((2, n_c * c), dtype=np.float32) * 0.5).astype(np.float32)
+    first = np.arange(n_c) * c
+    r[0, first] = 1.0 + rng.permutation(n_c).astype(np.float32)
+    r[0, first + c - 1] = -(1.0 + n_c + rng.permutation(n_c).astype(np.float32))
+    r[1, first + c - 1] = 2.0 + rng.permutation(n_c).astype(np.float32)
+    r[1, first[: n_c // 2]] = 1e6                      # tied clusters
+    keys = dev(r)
+    idx = torch.full((2, n_c), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for lo, hi in [(0, n_c // 3), (n_c // 5, n_c // 2 + 1)]:
+        B.sparse_ffn_select(keys, B.KEY_ABS_F32, lo, hi, cluster=c, idx_out=idx, count_out=cnt)
+        torch.cuda.synchronize()
+        gi, gc = host(idx), host(cnt)
+        for row in range(2):
+            ck = oracle.cluster_max_key(oracle.key_abs(r[row]), c)
+            exp = oracle.rank_range(ck, lo, hi)
+            assert gc[row] == exp.size, (n_c, c, row)
+            assert np.array_equal(gi[row, :gc[row]], exp), (n_c, c, row, lo, hi)
+
+
 @pytest.mark.parametrize("n,k_top,k_mid", [(6144, 1536, 3072), (17408, 4352, 8704),
                                            (100, 0, 30), (100, 30, 0), (5000, 5000, 10)])
 def test_two_lists(n, k_top, k_mid):
