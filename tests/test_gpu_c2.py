@@ -151,10 +151,9 @@ def test_row_norms(n_rows, d):
 @pytest.mark.parametrize("name", ["small", "qkv", "down"])
 def test_weight_aware_tiers(name):
     """Tiers ranked by |x_j| * ||W[:, j]||_2.  With integer weights the GPU
-    norms equal the oracle's, so the tiers are bit-exact; with the workload's
-    weights the norms agree to rounding, so the tiers may differ only at
-    near-ties of the saliency, which is checked, and the product is compared
-    with the oracle's on the tiers taken."""
+    norms equal the oracle's, so the tiers are bit-exact end to end; with the
+    workload's weights the norms agree to rounding (checked on their own) and
+    the tiers are bit-exact with the oracle's ranking of the GPU's norms."""
     banner(f"c2 weight-aware {name}")
     Wt, x, seg = make(name, seed=7)
     n_in, n_out = Wt.shape
@@ -177,25 +176,21 @@ def test_weight_aware_tiers(name):
     enc = oracle.encode_4bit(Wi, seg)
     assert_close(host(y), oracle.tiered_gemv(Wi, *enc, seg, x, o_top, o_mid), what="integer W")
 
-    # the workload's weights
+    # the workload's weights: the norms are fp32 sums on the GPU and fp64 in
+    # the oracle, so they are compared within rounding; the tiers are then
+    # checked bit-exact with the oracle's ranking fed the GPU's own norms
+    # (stage by stage: the select stage sees the bytes the GPU ranked)
     proj = TieredProjection(dev(Wt), seg, k_top, k_mid, weight_aware=True)
     proj(dev(x), y)
     torch.cuda.synchronize()
     ref_n = oracle.row_norms(Wt)
-    np.testing.assert_allclose(host(proj.norms), ref_n, rtol=1e-5, atol=0)
+    gpu_n = host(proj.norms)
+    np.testing.assert_allclose(gpu_n, ref_n, rtol=1e-5, atol=0)
     cnt = host(proj.cnt)
     top, mid = host(proj.idx_top)[:cnt[0]], host(proj.idx_mid)[:cnt[1]]
-    assert top.size == k_top and mid.size == k_mid and np.intersect1d(top, mid).size == 0
-    assert np.all(np.diff(top) > 0) and np.all(np.diff(mid) > 0)
-    o_top, o_mid = oracle.weighted_tier_sets(x, ref_n.astype(np.float32), k_top, k_mid)
-    sal = np.abs(x.astype(np.float64)) * ref_n
-    rest = np.setdiff1d(np.arange(n_in), np.concatenate([top, mid]))
-    for got, exp, below in [(top, o_top, np.concatenate([mid, rest])), (mid, o_mid, rest)]:
-        diff = np.setxor1d(got, exp)
-        if diff.size and got.size and below.size:
-            edge = sal[got].min()
-            assert np.all(np.abs(sal[diff] - edge) <= 1e-5 * edge), (name, diff)
-        if got.size and below.size:
-            assert sal[got].min() >= sal[below].max() * (1 - 1e-5)
+    assert top.size == k_top and mid.size == k_mid
+    o_top, o_mid = oracle.weighted_tier_sets(x, gpu_n.astype(np.float32), k_top, k_mid)
+    assert np.array_equal(top, o_top), (name, np.setxor1d(top, o_top))
+    assert np.array_equal(mid, o_mid), (name, np.setxor1d(mid, o_mid))
     enc = oracle.encode_4bit(Wt, seg)
     assert_close(host(y), oracle.tiered_gemv(Wt, *enc, seg, x, top, mid), what="weight-aware")
