@@ -77,11 +77,14 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a) {
   } else {
     n_items = a.n_rows;
   }
-  // Rows past the end read row 0 and tokens past the batch read token 0
-  // (valid, finite data): an MFMA output (m, n) depends only on A row m and
+  // A workgroup with no live item has nothing to do (uniform exit, before
+  // any barrier).  Otherwise items past the end re-read the last live item's
+  // row (a selected row: skipped rows are never read) and tokens past the
+  // batch read token 0: an MFMA output (m, n) depends only on A row m and
   // B column n, so those lanes only produce outputs that are never stored.
+  if ((int)blockIdx.x * 32 >= n_items) return;
   auto item_to_row = [&](int it) -> int {
-    if (it >= n_items) return 0;
+    it = it < n_items ? it : n_items - 1;
     if (!a.idx) return it;
     const int q = it / a.group;
     return a.idx[q] * a.group + (it - q * a.group);
