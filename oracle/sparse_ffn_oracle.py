@@ -398,12 +398,13 @@ def route_top2(logits: np.ndarray) -> tuple:
     return experts, e / e.sum()
 
 
-def relu_threshold(h: np.ndarray, quantile: float, std: float) -> float:
-    """tau = Phi^-1(q) * std * ||h||_2: the threshold that leaves a fraction
-    1-q of the gate pre-activations W_g[n].h (each ~ N(0, (std ||h||)^2))
-    above it, giving the ReLU sparsity the PowerInfer-2 guide describes
-    (10-20% of neurons nonzero)."""
-    return float(quantile * std * np.sqrt(np.sum(np.asarray(h, dtype=np.float64) ** 2)))
+def relu_threshold(h: np.ndarray, phi_inv_q: float, std: float) -> float:
+    """tau = Phi^-1(q) * std * ||h||_2, with ``phi_inv_q`` = Phi^-1(q) (the
+    standard normal quantile of q, e.g. 1.2816 for q = 0.9): the threshold
+    that leaves a fraction 1-q of the gate pre-activations W_g[n].h (each
+    ~ N(0, (std ||h||)^2)) above it, giving the ReLU sparsity the
+    PowerInfer-2 guide describes (10-20% of neurons nonzero)."""
+    return float(phi_inv_q * std * np.sqrt(np.sum(np.asarray(h, dtype=np.float64) ** 2)))
 
 
 def relu_gate(Wg_bits, h, tau: float) -> np.ndarray:
