@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_gemv.restype = _i
         L.sparse_ffn_gemv.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i, _i,
                                       _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _sz, _vp]
+        L.sparse_ffn_gemv_noalloc.restype = _i
+        L.sparse_ffn_gemv_noalloc.argtypes = [_i, _vp, _vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _i,
+                                              _i, _vp, _i, _f, _f, _vp, _i, _vp, _vp, _vp, _i, _i,
+                                              _vp]
         L.sparse_ffn_gemv_lists.restype = _i
         L.sparse_ffn_gemv_lists.argtypes = [_i, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp,
                                             _vp, _i, _vp, _sz, _vp]
@@ -76,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 11:
+        if L.sffn_abi_version() != 12:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -167,6 +171,27 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
         k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), float(rms_eps), _p(aux),
         _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_ffn_gemv_noalloc(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
+                            inp: torch.Tensor, out: torch.Tensor, *,
+                            idx: torch.Tensor | None = None, count: torch.Tensor | None = None,
+                            k_max: int = 0, group: int = 1,
+                            row_mask: torch.Tensor | None = None, tau_scale: float = 0.0,
+                            rms_eps: float = 0.0, aux: torch.Tensor | None = None,
+                            alpha: torch.Tensor | None = None,
+                            key_out: torch.Tensor | None = None, accumulate: bool = False,
+                            stream=None) -> None:
+    """sparse_ffn_gemv without a workspace: AXPY's scratch is the library's
+    static per-GPU array (shared by every call on that GPU)."""
+    W = W0 if W0 is not None else W1
+    n_rows, d = W.shape[0], W.shape[1]
+    batch = inp.shape[0] if inp.dim() == 2 else 1
+    _check(lib().sparse_ffn_gemv_noalloc(
+        op, _p(W0), _p(W1), n_rows, d, W.stride(0), _p(inp), batch, _ld(inp, inp.shape[-1]),
+        _p(idx), _p(count), k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale),
+        float(rms_eps), _p(aux), _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out),
+        _ld(out, out.shape[-1]), int(accumulate), _stream(stream)))
 
 
 def sparse_ffn_row_norms(W: torch.Tensor, out: torch.Tensor, stream=None) -> None:

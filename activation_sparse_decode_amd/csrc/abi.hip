@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/sparse_ffn.h"
@@ -41,6 +42,38 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
   do {                         \
     if (!(cond)) return fail(st, __VA_ARGS__); \
   } while (0)
+
+// Device memory of the allocation-free gemv entry point: a file-scope array
+// that each GPU holds (its own copy) from the library's load until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address on the current GPU comes from hipGetSymbolAddress, looked up once
+// per device and kept in scratch_ptr[].
+constexpr size_t kScratchBytes = SFFN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The scratch array's address on the current device (looked up on the first
+// call per device, with that device current).
+sffn_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SFFN_EHIP, "gemv_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SFFN_EUNSUPPORTED, "gemv_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SFFN_EHIP, "gemv_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return SFFN_OK;
+}
 
 }  // namespace
 
@@ -492,6 +525,38 @@ sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w, const uint8_t* 
   a.idx_mid = idx_mid; a.cnt_mid = cnt_mid; a.k_mid_max = k_mid_max;
   a.y = y; a.accumulate = accumulate ? 1 : 0; a.ws = workspace; a.ws_bytes = ws_bytes;
   return from_hip(sffn::launch_tiered(a, (hipStream_t)stream), "tiered launch");
+}
+
+sffn_status sparse_ffn_gemv_noalloc(int op, const uint16_t* W0, const uint16_t* W1, int n_rows,
+                                    int d, int ld_w, const float* in, int batch, int ld_in,
+                                    const int32_t* idx, const int32_t* count, int k_max, int group,
+                                    const uint8_t* row_mask, int ld_mask, float tau_scale,
+                                    float rms_eps, const float* aux, int ld_aux, const float* alpha,
+                                    float* out, uint32_t* key_out, int ld_out, int accumulate,
+                                    void* stream) {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (op == SFFN_OP_AXPY) {
+    // the size check needs no GPU: sizes beyond the array are rejected first
+    REQUIRE(batch >= 1 && d >= 8 && n_rows >= 0 && k_max >= 0 && group >= 1, SFFN_EINVAL,
+            "gemv_noalloc: bad shape (batch=%d d=%d n_rows=%d k_max=%d group=%d)", batch, d,
+            n_rows, k_max, group);
+    const long items = idx ? (long)k_max * group : (long)n_rows;
+    REQUIRE(items <= n_rows, SFFN_EINVAL, "gemv_noalloc: k_max=%d * group=%d exceeds n_rows=%d",
+            k_max, group, n_rows);
+    const size_t need = sffn::workspace_bytes(batch, (int)items, d);
+    REQUIRE(need <= kScratchBytes, SFFN_EWORKSPACE,
+            "gemv_noalloc: this product needs %zu bytes of scratch, above the %zu-byte static "
+            "array (use sparse_ffn_gemv with a workspace)", need, kScratchBytes);
+    const sffn_status st = current_scratch(&ws);
+    if (st != SFFN_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
+  // row ops use no scratch; everything else (validation, kernels) is
+  // sparse_ffn_gemv's, which allocates nothing
+  return sparse_ffn_gemv(op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max, group,
+                         row_mask, ld_mask, tau_scale, rms_eps, aux, ld_aux, alpha, out, key_out,
+                         ld_out, accumulate, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

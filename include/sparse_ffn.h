@@ -99,7 +99,7 @@ const char* sffn_last_error(void);
 /* ABI revision of this header (bumped on any change of a signature or of what
    a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 11
+#define SFFN_ABI_VERSION 12
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -259,6 +259,42 @@ sffn_status sparse_ffn_gemv(int op,
                             const float* alpha,
                             float* out, uint32_t* key_out, int ld_out, int accumulate,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_gemv_noalloc -- sparse_ffn_gemv without a workspace argument, for
+ * callers that cannot allocate device memory: code recorded under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  Same
+ * arguments, operations, results and errors as sparse_ffn_gemv (it validates
+ * and launches through it, so the results are bitwise those of
+ * sparse_ffn_gemv); AXPY's split-K partials go to a static device array of
+ * SFFN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates and frees nothing.
+ *  - Limit: an AXPY whose sparse_ffn_workspace_size(batch, rows, d) exceeds
+ *    SFFN_NOALLOC_SCRATCH_BYTES is rejected with SFFN_EWORKSPACE before any
+ *    device work (e.g. batch 1 up to d of about 32K outputs; batch 16 at
+ *    d = 5120).  Row ops need no scratch.
+ *  - The array of the current device is used (its address is looked up once
+ *    per device, with that device current); `stream` must belong to the
+ *    current device.  The array needs no initialisation: every call writes
+ *    the partials it reads.
+ *  - All calls on one GPU share its array, which keeps the last call's
+ *    contents: two calls that may run at the same time on one GPU (other
+ *    streams, other host threads) race on it and give wrong results.
+ *    Order such calls on one stream, or give them sparse_ffn_gemv with their
+ *    own workspaces.
+ */
+#define SFFN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+sffn_status sparse_ffn_gemv_noalloc(int op,
+                                    const uint16_t* W0, const uint16_t* W1,
+                                    int n_rows, int d, int ld_w,
+                                    const float* in, int batch, int ld_in,
+                                    const int32_t* idx, const int32_t* count, int k_max, int group,
+                                    const uint8_t* row_mask, int ld_mask,
+                                    float tau_scale, float rms_eps,
+                                    const float* aux, int ld_aux,
+                                    const float* alpha,
+                                    float* out, uint32_t* key_out, int ld_out, int accumulate,
+                                    void* stream);
 
 /*
  * sparse_ffn_row_norms -- out[r] = sqrt(sum_{o < d} W[r][o]^2) for each row r

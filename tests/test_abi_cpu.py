@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 11
+    assert L.sffn_abi_version() == 12
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -184,6 +184,36 @@ def test_gemv_validation(L):
     assert rc == 2 and "batch 1" in msg
     rc, msg = gemv(L, op=7, group=32, tau=-1.0, ld_out=64)
     assert rc == 1 and "tau" in msg
+
+
+def test_gemv_noalloc_limits(L):
+    """The allocation-free gemv rejects a product whose scratch exceeds the
+    static array before any device work (no GPU needed), and shares
+    sparse_ffn_gemv's argument checks."""
+    f = L.sparse_ffn_gemv_noalloc
+    c = ctypes.c_float
+    # batch 1, 64 rows, 16384 outputs: 256 B + 64 KiB per chunk -> within 32 MiB
+    # batch 1, d = 2^16: 256 chunks x 256 KiB = 64 MiB -> above it
+    rc, msg = status_and_msg(L, f(3, FAKE, NULL, 64, 1 << 16, 1 << 16, FAKE, 1, 64, NULL, NULL, 0,
+                                  1, NULL, 0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 1 << 16, 0,
+                                  NULL))
+    assert rc == 3 and "static" in msg
+    assert L.sparse_ffn_workspace_size(1, 64, 1 << 16) > (32 << 20)
+    # batch 256 at d = 5120, 17408 rows: above the array
+    assert L.sparse_ffn_workspace_size(256, 17408, 5120) > (32 << 20)
+    rc, msg = status_and_msg(L, f(3, FAKE, NULL, 17408, 5120, 5120, FAKE, 256, 17408, NULL, NULL,
+                                  0, 1, NULL, 0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 5120, 0,
+                                  NULL))
+    assert rc == 3 and "static" in msg
+    # the workloads' batched union (batch 16, d = 5120) fits
+    assert L.sparse_ffn_workspace_size(16, 17408, 5120) <= (32 << 20)
+    # row ops take no scratch: their argument errors are sparse_ffn_gemv's
+    rc, msg = status_and_msg(L, f(0, FAKE, NULL, 64, 64, 64, FAKE, 1, 64, NULL, NULL, 0, 1, NULL,
+                                  0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 64, 0, NULL))
+    assert rc == 1 and "W1" in msg
+    rc, msg = status_and_msg(L, f(3, FAKE, NULL, 64, 64, 64, FAKE, 1, 64, FAKE, FAKE, 4, 32, NULL,
+                                  0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 64, 0, NULL))
+    assert rc == 1 and "exceeds" in msg
 
 
 def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),
