@@ -11,19 +11,24 @@ layers (per layer: gate/up over U_l, then the down product over U_l added to
 the residual).  Calibration, prefill and the per-prompt compaction run once
 before timing (reported under "setup").
 
-Other workloads (--workload): c0 single layer with per-token top-50% (every
-step runs activations, keys, select, compaction and the gathered down
-product), c1-loading the same stack with SelectInfer's Table 1 knobs
-(selective loading to 70%, 40% computed, layers 5..25 modified), c2 SpAx three-tier QKV + down read, c3 ReLU-sparse MoE stack (32
-layers x 8 experts, top-2, 32-row clusters), c4 batched decode with a
-per-token top-40% union contracted on MFMA (--batch 1/4/8/16).
+The default run (--workload all) reports that stack as the line's value and
+adds every other workload under "configs", each with its own gathered
+kernel as the roofline: c0 single layer with per-token top-50% (every step
+runs activations, keys, select, compaction and the gathered down product),
+c2 SpAx three-tier QKV + down read, c3 ReLU-sparse MoE stack (32 layers x 8
+experts, top-2, 32-row clusters), c4 batched decode with a per-token
+top-40% union contracted on MFMA at batch 1, 4, 8 and 16.  --workload runs
+one of them alone (also c1-loading: the stack with SelectInfer's Table 1
+knobs, and the --predictor / --weight-aware variants).
 
 Every timed step is replayed from a HIP graph with its inputs resident in
 HBM; the weights cycle through enough copies to exceed the 256 MB Infinity
-Cache.  "roofline" is the workload's dominant kernel: algorithmic bytes per
-launch over its average launch time, the launches replayed alone from a
-graph between HIP events on the stream they run on.  "cpu_baseline" is the
-CPU oracle on a bounded sample of the same work.
+Cache.  "roofline" is the workload's gathered (sparse) product: algorithmic
+bytes per launch over its average launch time, the launches replayed alone
+from a graph between HIP events on the stream they run on; the dense
+kernels that feed a selection are reported beside it.  "cpu_baseline" is
+the CPU oracle on a bounded sample of the same work, with all host cores
+and with one.
 """
 
 from __future__ import annotations
@@ -44,6 +49,10 @@ PEAK_HBM_GBS = 8000.0
 COPY_CALIB_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "activation_sparse_decode_amd", "csrc")
 METRIC = "sparse-FFN decode us/token and achieved HBM GB/s (% of peak) at batch 1"
+# sources of the gathered products (a committed traffic figure is reported
+# only while they are unchanged)
+AXPY_B1_SOURCES = ["axpy_b1.hip", "sffn_splitk.h", "sffn_device.h"]
+AXPY_MFMA_SOURCES = ["axpy_mfma.hip", "axpy_b1.hip", "sffn_splitk.h", "sffn_device.h"]
 
 
 def log(msg: str) -> None:
@@ -55,15 +64,18 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=128)
     p.add_argument("--warmup", type=int, default=16)
-    p.add_argument("--workload", default="c1",
-                   choices=["c0", "c1", "c1-loading", "c2", "c3", "c4"])
+    p.add_argument("--workload", default="all",
+                   choices=["all", "c0", "c1", "c1-loading", "c2", "c3", "c4"])
     p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
     p.add_argument("--predictor", action="store_true",
                    help="workload c3: clusters from an online predictor (PowerInfer-2), no dense gate")
     p.add_argument("--weight-aware", action="store_true",
                    help="workload c2: rank columns by |x_j| * ||W[:, j]||_2 (WiSparse)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="bounded CPU work for the oracle baseline (0 disables it)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="bounded CPU work for the oracle baseline, per thread setting "
+                        "(0 disables it)")
+    p.add_argument("--cpu-seconds-sub", type=float, default=2.5,
+                   help="the same for each workload under \"configs\" of the default run")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -184,6 +196,23 @@ def timed_cpu(fn, seconds, per_unit=1):
     return (time.perf_counter() - t0) / (n * per_unit), n
 
 
+def cpu_baseline(fn, seconds, sample, per_unit=1, scale=1e6, unit="us/token"):
+    """The oracle on a bounded sample: timed with the BLAS pool at all host
+    cores, then again limited to one thread.  value = seconds per unit x scale."""
+    s_all, n_all = timed_cpu(fn, seconds, per_unit)
+    cores = blas_threads()
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            s_one, n_one = timed_cpu(fn, seconds, per_unit)
+        one = {"value": s_one * scale, "cores": 1, "sample_units": n_one}
+    except ImportError:
+        pass
+    return {"value": s_all * scale, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{n_all} x {sample}", "one_core": one}
+
+
 # ============================================================ c1: SelectInfer stack
 
 def glu_bytes(u: int, d: int) -> int:
@@ -264,9 +293,8 @@ def run_c1(args, torch, B, synth, P, T):
                                               U_sets[l])
                 hh = hh + y
 
-        s, n = timed_cpu(one, args.cpu_seconds)
-        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} decode token(s) x 28 layers over the same union sets, numpy fp64")
+        cpu = cpu_baseline(one, args.cpu_seconds,
+                           "decode token(s) x 28 layers over the same union sets, numpy fp64")
 
     config = {"workload": "SelectInfer 28-layer FFN stack, Llama3.2-3B shape (d_model 3072, "
                           "d_ff 8192), base 20% by Eq (1) over 512 calibration tokens, per-token "
@@ -369,9 +397,8 @@ def run_c1_loading(args, torch, B, synth, P, T):
                                               ids[l])
                 hh = hh + y
 
-        s, n = timed_cpu(one, args.cpu_seconds)
-        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} decode token(s) x 28 layers over the same computed sets, numpy fp64")
+        cpu = cpu_baseline(one, args.cpu_seconds,
+                           "decode token(s) x 28 layers over the same computed sets, numpy fp64")
 
     config = {"workload": "SelectInfer 28-layer FFN stack, Llama3.2-3B shape, Table 1 knobs: layers "
                           "5..25 loaded selectively (base 30% by task-specific Eq (1) scores + "
@@ -451,10 +478,8 @@ def run_c0(args, torch, B, synth, P, T):
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        s, n = timed_cpu(lambda i: oracle.sparse_swiglu_layer(*host_w, X_host[i], keep),
-                         args.cpu_seconds)
-        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} tokens through the layer, numpy fp64")
+        cpu = cpu_baseline(lambda i: oracle.sparse_swiglu_layer(*host_w, X_host[i], keep),
+                           args.cpu_seconds, "token(s) through the layer, numpy fp64")
     config = {"workload": "single SwiGLU FFN layer, Llama3.2-1B shape (d_model 2048, d_ff 8192), "
                           "per-token top 50% by |silu(gate)*up|, batch 1 (16 rotating weight copies)",
               "d_model": d, "d_ff": N, "keep": keep, "batch": 1}
@@ -462,10 +487,13 @@ def run_c0(args, torch, B, synth, P, T):
                   step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
                   kernels_us={"gate_up_dense": round(glu_us, 3), "select": round(sel_us, 3),
                               "gathered_down": round(down_us, 3)},
-                  gathered_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b, glu_us,
-                                    measured_traffic("rowop_glu_swiglu_top50_layer",
-                                                     ["rowop_b1.hip", "sffn_device.h"])),
+                  roofline=roofline("axpy_b1_kernel + splitk_reduce_kernel (gathered down over "
+                                    "the kept 50%, one call)", down_b, down_us,
+                                    measured_traffic("axpy_b1_swiglu_top50_layer", AXPY_B1_SOURCES)),
+                  dense_gate_up=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b,
+                                         glu_us,
+                                         measured_traffic("rowop_glu_swiglu_top50_layer",
+                                                          ["rowop_b1.hip", "sffn_device.h"])),
                   cpu_baseline=cpu,
                   step_stats=dist)
 
@@ -555,10 +583,9 @@ def run_c2(args, torch, B, synth, P, T):
             td, md = sets(Xd_host[i], kd_t, kd_m, nd)
             oracle.tiered_gemv(Wd0, *encd, [0, d], Xd_host[i], td, md)
 
-        s, n = timed_cpu(one, args.cpu_seconds)
-        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} tokens (QKV + down tiers and products; encoding excluded), "
-                          f"numpy fp64")
+        cpu = cpu_baseline(one, args.cpu_seconds,
+                           "token(s) (QKV + down tiers and products; encoding excluded), "
+                           "numpy fp64")
     config = {"workload": "SpAx three-tier read, Llama3.1-8B shape: QKV 4096->4096/1024/1024 and "
                           "down 14336->4096; 15% bf16 / 35% 4-bit / 50% skipped by "
                           + ("|x_j| * ||W[:, j]||_2 (WiSparse weight-aware)" if args.weight_aware
@@ -611,11 +638,15 @@ def run_c3(args, torch, B, synth, P, T):
     # An untimed eager pass records the active-cluster counts (exact bytes
     # read); then one graph per token (the routed experts differ per token).
     counts = np.zeros((steps, L, 2), dtype=np.int64)
+    saved = []     # token 0, per layer: routed experts and their cluster lists
     for t in range(steps):
         h.copy_(X[t])
 
         def rec(l, tt, hh, chosen, t=t):
-            counts[t, l] = (moe.pcnt[l & 1] if args.predictor else moe.ccnt).cpu().numpy()
+            ci, cc = (moe.pidx[l & 1], moe.pcnt[l & 1]) if args.predictor else (moe.cidx, moe.ccnt)
+            counts[t, l] = cc.cpu().numpy()
+            if t == 0:
+                saved.append((list(chosen), ci.clone(), cc.clone()))
         moe.decode(h, t, record=rec)
     graphs = [T.capture(lambda t=t: (h.copy_(X[t]), moe.decode(h, t))) for t in range(steps)]
     for g in graphs[:2]:
@@ -667,6 +698,34 @@ def run_c3(args, torch, B, synth, P, T):
 
     gate_us = T.replay_ms(T.capture(dom), 16) * 1e3 / (16 * L * 2)
 
+    # The gathered part of each layer, replayed alone over token 0's cluster
+    # lists: the routed experts' ups (or fused ReGLUs) over their clusters in
+    # one launch, then both down products in one gathered product.
+    hs = torch.zeros(d, dtype=torch.float32, device=dev)
+
+    def gathered():
+        for l, (chosen, ci, cc) in enumerate(saved):
+            k = len(chosen)
+            ex = [experts[l][e] for e in chosen]
+            idx, cnt = [ci[j] for j in range(k)], [cc[j:j + 1] for j in range(k)]
+            a = [moe.a[j] for j in range(k)]
+            if args.predictor:
+                B.sparse_ffn_rowop_lists(B.OP_GLU_RELU, [m[0] for m in ex], [m[1] for m in ex], h,
+                                         a, idxs=idx, counts=cnt, k_maxs=[nc] * k, group=S,
+                                         tau_scale=moe.tau_scale, rms_eps=moe.rms_eps)
+            else:
+                B.sparse_ffn_rowop_lists(B.OP_GATED, None, [m[1] for m in ex], h, a, idxs=idx,
+                                         counts=cnt, k_maxs=[nc] * k, group=S,
+                                         auxs=[moe.r[j] for j in range(k)], rms_eps=moe.rms_eps)
+            B.sparse_ffn_gemv_lists([m[2] for m in ex], a, idx, cnt, [nc] * k, hs, group=S,
+                                    alphas=[moe.route_w[l * moe.T, j:j + 1] for j in range(k)],
+                                    accumulate=True, workspace=moe.ws)
+
+    gath_us = T.replay_ms(T.capture(gathered), max(4, steps)) * 1e3 / (max(4, steps) * L)
+    c0 = counts[0].sum(axis=1)      # clusters of both routed experts, per layer, token 0
+    rows_per_cluster_b = S * d * 2 * (3 if args.predictor else 2)   # (gate,) up, down rows
+    gath_b = float(np.mean(c0 * (rows_per_cluster_b + S * 12 + 8) + 12 * d))
+
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
@@ -691,11 +750,10 @@ def run_c3(args, torch, B, synth, P, T):
                 else:
                     oracle.relu_expert(*host[(l, e)], x, tau, S)
 
-        s, n = timed_cpu(one, args.cpu_seconds)
-        cpu = dict(value=s * L * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} layer(s) of 2 routed experts "
-                          f"({'predictor, ' if args.predictor else 'gate, '}clusters, up, down) at "
-                          f"token 0, numpy fp64, scaled to {L} layers")
+        cpu = cpu_baseline(one, args.cpu_seconds,
+                           f"layer(s) of 2 routed experts "
+                           f"({'predictor, ' if args.predictor else 'gate, '}clusters, up, down) "
+                           f"at token 0, numpy fp64, scaled to {L} layers", scale=L * 1e6)
     config = {"workload": "ReLU-sparse MoE FFN stack, TurboSparse-Mixtral-like: 32 layers x 8 "
                           "experts (d_model 4096, d_ff 14336), top-2 router, ~90% exact zeros, "
                           "32-row clusters, batch 1"
@@ -705,12 +763,24 @@ def run_c3(args, torch, B, synth, P, T):
               "layers": L, "experts": E, "batch": 1,
               ("predicted_cluster_frac" if args.predictor else "active_cluster_frac"):
                   round(float(counts.mean() / nc), 4)}
+    gname = ("rowop_lists_kernel<GLU_RELU> + axpy_lists_kernel + splitk_reduce_kernel (gate, up "
+             "and down rows of the predicted clusters of both routed experts, one layer)"
+             if args.predictor else
+             "rowop_lists_kernel<GATED> + axpy_lists_kernel + splitk_reduce_kernel (up and down "
+             "rows of the active clusters of both routed experts, one layer)")
+    log(f"c3 gathered part: {gath_us:.2f} us/layer for {gath_b / 1e6:.1f} MB")
     return result(us_tok, "us/token", steps, 2, total_ms / steps, config, step_bytes=step_b,
                   step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
-                  roofline=roofline(dom_name, dom_b, gate_us,
-                                    None if args.predictor else
-                                    measured_traffic("rowop_relu_gate_moe",
-                                                     ["rowop_b1.hip", "sffn_device.h"])),
+                  kernels_us={"dense_part_per_expert": round(gate_us, 3),
+                              "gathered_part_per_layer": round(gath_us, 3)},
+                  roofline=roofline(gname, gath_b, gath_us,
+                                    measured_traffic("moe_gathered_layer_predictor" if args.predictor
+                                                     else "moe_gathered_layer",
+                                                     ["rowop_b1.hip"] + AXPY_B1_SOURCES)),
+                  dense_part=roofline(dom_name, dom_b, gate_us,
+                                      None if args.predictor else
+                                      measured_traffic("rowop_relu_gate_moe",
+                                                       ["rowop_b1.hip", "sffn_device.h"])),
                   cpu_baseline=cpu,
                   step_stats=dist)
 
@@ -771,10 +841,9 @@ def run_c4(args, torch, B, synth, P, T):
     if args.cpu_seconds > 0:
         import oracle
         w0 = [m.cpu().numpy().view(np.uint16) for m in (lays[0].Wg, lays[0].Wu, lays[0].WdT)]
-        s, n = timed_cpu(lambda i: oracle.batched_union_decode(
-            *w0, X_host[i * batch:(i + 1) * batch], keep), args.cpu_seconds, per_unit=batch)
-        cpu = dict(value=s * 1e6, unit="us/token", cores=blas_threads(), kind="oracle",
-                   sample=f"{n} batch(es) of {batch} tokens, numpy fp64")
+        cpu = cpu_baseline(lambda i: oracle.batched_union_decode(
+            *w0, X_host[i * batch:(i + 1) * batch], keep), args.cpu_seconds,
+            f"batch(es) of {batch} tokens, numpy fp64", per_unit=batch)
     config = {"workload": f"batched decode, Qwen-27B-like layer (d_model 5120, d_ff 17408), "
                           f"per-token top 40%, union gathered once and contracted on MFMA, "
                           f"batch {batch} (4 rotating weight copies)",
@@ -783,11 +852,53 @@ def run_c4(args, torch, B, synth, P, T):
                   config, us_per_batch=round(us_batch, 3), step_bytes=step_b,
                   step_GBps=round(step_b / (us_batch * 1e-6) / 1e9, 1),
                   kernels_us={k_glu: round(glu_us, 3), k_down: round(down_us, 3)},
-                  union_down_GBps=round(down_b / (down_us * 1e-6) / 1e9, 1),
-                  roofline=roofline("rowop_mfma_kernel<GLU> (batched gate/up)" if batch > 1 else
-                                    "rowop_wave_kernel<GLU> (gate/up, batch 1)", glu_b, glu_us),
+                  roofline=roofline(("axpy_mfma_kernel" if batch > 1 else "axpy_b1_kernel")
+                                    + " + splitk_reduce_kernel (the union's down rows read once, "
+                                    "per-token masks, one call)", down_b, down_us,
+                                    measured_traffic(f"union_down_b{batch}",
+                                                     AXPY_MFMA_SOURCES if batch > 1
+                                                     else AXPY_B1_SOURCES)),
+                  dense_gate_up=roofline("rowop_mfma_kernel<GLU> (batched gate/up)" if batch > 1
+                                         else "rowop_wave_kernel<GLU> (gate/up, batch 1)", glu_b,
+                                         glu_us),
                   cpu_baseline=cpu,
                   step_stats=dist)
+
+
+# ============================================================ all: the headline stack and every workload
+
+SUB_KEYS_DROPPED = ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "dtype",
+                    "weight_dtype", "data")
+
+
+def run_all(args, torch, B, synth, P, T):
+    """The SelectInfer stack as the line's value, then every other workload
+    under "configs" (each with its gathered kernel as the roofline and a
+    shorter CPU-oracle sample)."""
+    import gc
+
+    out = run_c1(args, torch, B, synth, P, T)
+    subs = [("c0", dict(workload="c0")), ("c2", dict(workload="c2")), ("c3", dict(workload="c3"))]
+    subs += [(f"c4_b{b}", dict(workload="c4", batch=b)) for b in (1, 4, 8, 16)]
+    fns = {"c0": run_c0, "c2": run_c2, "c3": run_c3, "c4": run_c4}
+    configs = {}
+    for name, over in subs:
+        gc.collect()
+        torch.cuda.empty_cache()
+        a = argparse.Namespace(**vars(args))
+        a.cpu_seconds = args.cpu_seconds_sub
+        a.predictor = a.weight_aware = False
+        for k, v in over.items():
+            setattr(a, k, v)
+        t0 = time.perf_counter()
+        r = fns[a.workload](a, torch, B, synth, P, T)
+        configs[name] = {k: v for k, v in r.items() if k not in SUB_KEYS_DROPPED}
+        rf = r["roofline"]
+        log(f"{name}: {r['value']:.2f} {r['unit']}; gathered kernel {rf['launch_us']:.2f} us "
+            f"= {rf['achieved']:.0f} GB/s ({100 * rf['frac']:.1f}% of peak) "
+            f"[{time.perf_counter() - t0:.0f} s]")
+    out["configs"] = configs
+    return out
 
 
 def main():
@@ -806,8 +917,8 @@ def main():
     torch.cuda.set_device(0)
     B.lib()
     T = Timer(torch)
-    run = {"c0": run_c0, "c1": run_c1, "c1-loading": run_c1_loading, "c2": run_c2, "c3": run_c3,
-           "c4": run_c4}[args.workload]
+    run = {"all": run_all, "c0": run_c0, "c1": run_c1, "c1-loading": run_c1_loading, "c2": run_c2,
+           "c3": run_c3, "c4": run_c4}[args.workload]
     out = run(args, torch, B, synth, P, T)
     props = torch.cuda.get_device_properties(0)
     out["env"] = {"device": props.name, "arch": getattr(props, "gcnArchName", None),

@@ -69,3 +69,24 @@ def test_traffic_dropped_when_a_source_changes(tmp_path, monkeypatch):
         fh.write("\n// edited\n")
     assert bench.measured_traffic(TAG, SOURCES) is None
     assert bench.measured_traffic("no_such_kernel", SOURCES) is None
+
+
+def test_cpu_baseline_reports_all_cores_and_one():
+    calls = []
+    cb = bench.cpu_baseline(lambda i: calls.append(i), 0.01, "item(s) of nothing", per_unit=2)
+    assert cb["kind"] == "oracle" and cb["unit"] == "us/token" and cb["cores"] >= 1
+    assert cb["value"] > 0 and cb["sample"].endswith("item(s) of nothing")
+    assert cb["one_core"]["cores"] == 1 and cb["one_core"]["value"] > 0
+    assert calls[0] == 0
+
+
+def test_default_workload_is_the_full_run():
+    import argparse
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        a = bench.parse()
+    finally:
+        sys.argv = old
+    assert a.workload == "all" and a.gpus == 1
+    assert isinstance(a, argparse.Namespace) and a.cpu_seconds_sub > 0
