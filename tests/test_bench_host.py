@@ -42,7 +42,7 @@ def _sha(csrc, sources=SOURCES):
 
 
 @pytest.mark.parametrize("tag", [TAG, "rowop_glu_swiglu_top50_layer", "rowop_relu_gate_moe",
-                                 "tiered_down_spax"])
+                                 "tiered_down_spax", "axpy_b1_swiglu_top50_layer"])
 def test_committed_traffic_follows_its_sources(tag):
     with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.json")) as fh:
         rec = json.load(fh)
