@@ -255,10 +255,13 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     }
     if (key_out) REQUIRE(aligned(key_out, 4), SFFN_EINVAL, "gemv: key_out misaligned");
     if (items == 0) return ok();
+    if (batch > 1 && workspace)
+      REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
     sffn::RowOpArgs a{op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max,
                       (idx || op == SFFN_OP_DOT_RELU_CLUSTER) ? group : 1, tau_scale, rms_eps,
                       aux, ld_aux, out, key_out,
-                      ld_out, accumulate ? 1 : 0};
+                      ld_out, accumulate ? 1 : 0, batch > 1 ? workspace : nullptr,
+                      batch > 1 && workspace ? ws_bytes : 0};
     return from_hip(batch == 1 ? sffn::launch_rowop_b1(a, s) : sffn::launch_rowop_mfma(a, s),
                     "gemv launch");
   }

@@ -95,6 +95,7 @@ struct RowOpArgs {
   float tau_scale, rms_eps;
   const float* aux; int ld_aux;
   float* out; uint32_t* key_out; int ld_out; int accumulate;
+  void* ws; size_t ws_bytes;   // optional (batched row ops: K split of the last tiles)
 };
 hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s);
 hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s);

@@ -560,7 +560,9 @@ class BatchedUnionLayer:
 
     def __call__(self, X: torch.Tensor, Y: torch.Tensor) -> None:
         N = self.Wg.shape[0]
-        B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, X, self.A, key_out=self.K)
+        # the workspace lets the batched gate/up split its last tiles along K
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, X, self.A, key_out=self.K,
+                          workspace=self.ws)
         # F starts at zero (allocation) and the union select resets it as it
         # reads it, ready for the next batch's counts
         B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M, freq=self.F)

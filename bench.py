@@ -819,7 +819,7 @@ def run_c4(args, torch, B, synth, P, T):
     def glu_only():
         for c in range(copies):
             B.sparse_ffn_gemv(B.OP_GLU_SILU, lays[c].Wg, lays[c].Wu, xb[c], lays[c].A,
-                              key_out=lays[c].K)
+                              key_out=lays[c].K, workspace=lays[c].ws)
 
     def down_only():
         for c in range(copies):

@@ -246,7 +246,13 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
  * Limits: d % 8 == 0 (d % 32 == 0 when batch > 1), ld_w % 8 == 0, W0/W1/in/
  *  out 16-byte aligned, d <= 8192 for row ops at batch 1, 1 <= batch.
  *  workspace: AXPY needs sparse_ffn_workspace_size(batch, rows, d) bytes
- *  (rows = k_max*group or n_rows); row ops take none (may be NULL).
+ *  (rows = k_max*group or n_rows).  Row ops at batch 1 take none (may be
+ *  NULL).  Row ops at batch > 1 without an index list use it when given
+ *  (256-byte aligned; sparse_ffn_workspace_size(batch, n_rows, d) bytes
+ *  suffice): when the 32-row tile pairs do not split evenly over the CUs,
+ *  the last pairs are split along K and a second kernel adds the slices in
+ *  a fixed order (results stay reproducible run to run); without one, or
+ *  if it is too small, the call runs unsplit.  It needs no initialisation.
  */
 sffn_status sparse_ffn_gemv(int op,
                             const uint16_t* W0, const uint16_t* W1,

@@ -122,3 +122,50 @@ def test_mfma_rowop_ragged_k(d):
             x = oracle.rms_normalize(X[t], eps) if eps > 0 else X[t]
             assert_close(A_h[t, rows], oracle.swiglu_acts(Wg, Wu, x, rows),
                          what=f"d={d} eps={eps} token {t}")
+
+
+@pytest.mark.parametrize("d,batch", [(416, 16), (1024, 19)])
+def test_mfma_rowop_k_slices(d, batch):
+    """With a workspace, a batched dense row op whose 32-row tile pairs do
+    not split evenly over the CUs runs the last pairs as K slices plus a
+    fix-up: 8240 rows = 258 pairs (the last with one live tile), d = 416
+    (three 128-chunks and a 32-wide remainder, taken by the last slice) and
+    1024; every op, with the fused RMSNorm where it applies, against the
+    oracle; two sliced runs are bitwise equal."""
+    banner(f"c4 K-sliced row ops d={d} batch={batch}")
+    N = 8240
+    Wg, Wu, _, _ = make(N, d, 1, seed=d + batch)
+    X = synth.tokens(d, synth.W_C4, 7, batch, d)
+    rng = np.random.default_rng(d)
+    aux = rng.standard_normal((batch, N)).astype(np.float32)
+    ws = B.new_workspace(batch, N, d)
+    q = 1.2815515655446004 * synth.WEIGHT_STD
+    cases = [(B.OP_GLU_SILU, dict(rms_eps=1e-5)), (B.OP_GLU_SILU, {}), (B.OP_DOT_RELU,
+             dict(tau_scale=q, rms_eps=1e-5)), (B.OP_GATED, dict(rms_eps=1e-5)), (B.OP_DOT, {})]
+    for op, kw in cases:
+        outs = []
+        for _ in range(2):
+            A = torch.full((batch, N), 3.0, dtype=torch.float32, device="cuda")
+            Kk = torch.zeros((batch, N), dtype=torch.int32, device="cuda")
+            B.sparse_ffn_gemv(op, None if op == B.OP_GATED else dev(Wg),
+                              dev(Wu) if op in (B.OP_GLU_SILU, B.OP_GATED) else None, dev(X), A,
+                              aux=dev(aux) if op == B.OP_GATED else None, key_out=Kk,
+                              workspace=ws, **kw)
+            torch.cuda.synchronize()
+            outs.append((host(A), host_u32(Kk)))
+        assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32)), op
+        A_h, K_h = outs[0]
+        assert np.array_equal(K_h, oracle.key_abs(A_h)), op
+        eps = kw.get("rms_eps", 0.0)
+        for b in (0, batch // 2, batch - 1):
+            x = oracle.rms_normalize(X[b], eps) if eps > 0 else X[b].astype(np.float64)
+            if op == B.OP_GLU_SILU:
+                ref = oracle.swiglu_acts(Wg, Wu, x)
+            elif op == B.OP_DOT_RELU:
+                ref = oracle.relu_gate(Wg, x, oracle.relu_threshold(x, 1.2815515655446004,
+                                                                     synth.WEIGHT_STD))
+            elif op == B.OP_GATED:
+                ref = aux[b].astype(np.float64) * oracle.row_dots(Wu, x)
+            else:
+                ref = oracle.row_dots(Wg, x)
+            assert_close(A_h[b], ref, what=f"op {op} eps {eps} token {b}")
