@@ -171,8 +171,10 @@ hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s) {
   const int Mpad = Mt * 16;
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
   const int col_tiles = (a.d + kOT - 1) / kOT;
-  // one round of workgroups: three per CU (LDS and registers) on 256 CUs
-  long KS = 768 / ((long)col_tiles * Mt);
+  // one round of workgroups, two per CU on 256 CUs (three fit; measured on
+  // the 17408 x 5120 union at batch 16: 512 workgroups 46.0 us, 768 49.4,
+  // 384 53.6, the fewer chunks also halving the partials' round trip)
+  long KS = 512 / ((long)col_tiles * Mt);
   const long by_rows = (items + kKT - 1) / kKT;
   if (KS > by_rows) KS = by_rows;
   if (KS > max_split_mfma(Mt)) KS = max_split_mfma(Mt);
