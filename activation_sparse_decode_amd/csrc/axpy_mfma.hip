@@ -8,7 +8,7 @@
 //
 // Tokens are the MFMA M dimension, output columns the N dimension and
 // gathered rows the K dimension.  W^T rows are contiguous along N, so a
-// workgroup stages a 64-row x 256-column tile in LDS with 16-byte coalesced
+// workgroup stages a 32-row x 256-column tile in LDS with 16-byte coalesced
 // loads and each lane gathers its B operand (8 rows of one column) from
 // LDS; the LDS row pitch (129 dwords) puts the four K-groups of a wave on
 // disjoint banks.  The A operand is built per stage in the same kernel: the
@@ -30,7 +30,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kOT = 256;          // output columns per workgroup
-constexpr int kKT = 64;           // gathered rows per LDS stage
+// Gathered rows per LDS stage.  32 (16 KB of weights per workgroup in
+// flight) measured faster than 64 on the 17408 x 5120 union: batch 16 46.0
+// -> 41.9 us, batch 8 -> 39.6, batch 4 39.1 -> 35.0 us with 512 workgroups
+// (256 or 1024 workgroups slower).
+constexpr int kKT = 32;
+constexpr int kWJ = kKT / 8;         // weight loads per thread per stage
+constexpr int kAR = kKT / 16;        // activations per thread per stage
 constexpr int kPitch = 258;       // LDS row pitch in bf16 elements (129 dwords)
 constexpr int kSeg = 2048;        // row indices held in LDS at a time
 constexpr int kAPitch = kKT / 8 + 1;   // activation tile pitch in 16-byte units
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
   const int lc = t & 31, lr = t >> 5;
   const int lcol = col0 + 8 * lc;
   const int lcolc = lcol < a.d ? lcol : 0;   // lanes past the last column re-read column 0
-  // activation loader: token am, rows 4 ar .. 4 ar + 3 of the stage
+  // activation loader: token am, rows kAR ar .. kAR ar + kAR - 1 of the stage
   const int am = t >> 4, ar = t & 15;
   const int tok = m0 + am;
   const bool tok_ok = tok < a.batch;
@@ -83,17 +89,17 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
     const bool has_mask = a.row_mask != nullptr;
     const uint8_t* mrow = has_mask ? a.row_mask + (size_t)tokc * a.ld_mask
                                    : reinterpret_cast<const uint8_t*>(a.in);   // unused bytes
-    uint4 v[8];
-    float xr[4];
-    uint32_t mb[4];
+    uint4 v[kWJ];
+    float xr[kAR];
+    uint32_t mb[kAR];
     auto issue = [&](int st) {
       const int base = st * kKT;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < kWJ; ++j)
         v[j] = load_stream16(a.W + (size_t)rows_s[base + lr + 8 * j] * a.ld_w + lcolc);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rows_s[base + 4 * ar + e];
+      for (int e = 0; e < kAR; ++e) {
+        const int r = rows_s[base + kAR * ar + e];
         xr[e] = a.in[(size_t)tokc * a.ld_in + r];
         mb[e] = mrow[r];
       }
@@ -102,35 +108,35 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
     for (int st = 0; st < nst; ++st) {
       __syncthreads();   // the previous stage's LDS readers are done
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < kWJ; ++j) {
         uint32_t* dst = T + ((lr + 8 * j) * kPitch + 8 * lc) / 2;
         dst[0] = v[j].x; dst[1] = v[j].y; dst[2] = v[j].z; dst[3] = v[j].w;
       }
       {
-        float av[4];
+        float av[kAR];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool keep = tok_ok && s0 + st * kKT + 4 * ar + e < s1 && (!has_mask || mb[e] != 0u);
+        for (int e = 0; e < kAR; ++e) {
+          const bool keep = tok_ok && s0 + st * kKT + kAR * ar + e < s1 && (!has_mask || mb[e] != 0u);
           av[e] = keep ? xr[e] : 0.f;
         }
-        uint32_t hi[2], lo[2];
+        uint32_t hi[kAR / 2], lo[kAR / 2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < kAR / 2; ++e) {
           const uint32_t h0 = f32_to_bf16_rne(av[2 * e]), h1 = f32_to_bf16_rne(av[2 * e + 1]);
           const uint32_t l0 = f32_to_bf16_rne(av[2 * e] - __uint_as_float(h0 << 16));
           const uint32_t l1 = f32_to_bf16_rne(av[2 * e + 1] - __uint_as_float(h1 << 16));
           hi[e] = h0 | (h1 << 16);
           lo[e] = l0 | (l1 << 16);
         }
-        uint2* ah = reinterpret_cast<uint2*>(&As[0][am][0]) + ar;
-        uint2* al = reinterpret_cast<uint2*>(&As[1][am][0]) + ar;
-        *ah = make_uint2(hi[0], hi[1]);
-        *al = make_uint2(lo[0], lo[1]);
+        uint32_t* ah = reinterpret_cast<uint32_t*>(&As[0][am][0]) + (kAR / 2) * ar;
+        uint32_t* al = reinterpret_cast<uint32_t*>(&As[1][am][0]) + (kAR / 2) * ar;
+#pragma unroll
+        for (int e = 0; e < kAR / 2; ++e) { ah[e] = hi[e]; al[e] = lo[e]; }
       }
       if (st + 1 < nst) issue(st + 1);   // in flight while this stage is contracted
       __syncthreads();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < kKT / 32; ++s) {
         const bf16x8 Ah = __builtin_bit_cast(bf16x8, As[0][nl][4 * s + g]);
         const bf16x8 Al = __builtin_bit_cast(bf16x8, As[1][nl][4 * s + g]);
 #pragma unroll
@@ -171,9 +177,10 @@ hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s) {
   const int Mpad = Mt * 16;
   const long items = a.idx ? (long)a.k_max * a.group : (long)a.n_rows;
   const int col_tiles = (a.d + kOT - 1) / kOT;
-  // one round of workgroups, two per CU on 256 CUs (three fit; measured on
-  // the 17408 x 5120 union at batch 16: 512 workgroups 46.0 us, 768 49.4,
-  // 384 53.6, the fewer chunks also halving the partials' round trip)
+  // one round of workgroups, two per CU on 256 CUs (measured on the 17408 x
+  // 5120 union at batch 16 with 64-row stages: 512 workgroups 46.0 us, 768
+  // 49.4, 384 53.6; with 32-row stages 512: 41.9, 256: 52.3, 1024: 45.3;
+  // fewer chunks also shrink the partials' round trip)
   long KS = 512 / ((long)col_tiles * Mt);
   const long by_rows = (items + kKT - 1) / kKT;
   if (KS > by_rows) KS = by_rows;
