@@ -45,14 +45,30 @@ def pct_count(pct: int, n: int) -> int:
     return (pct * n) // 100
 
 
+def _reuse(layer, other, names) -> bool:
+    """Point `layer`'s intermediate buffers at `other`'s (layers of one model
+    run one after another on one stream, so they can share them)."""
+    if other is None:
+        return False
+    for n in names:
+        setattr(layer, n, getattr(other, n))
+    return True
+
+
 class SwigluSparseLayer:
     """x -> a = silu(W_g x) * (W_u x) (+ keys) -> top-``keep`` by |a| ->
-    y = sum over the kept neurons of a_n W_down^T[n]."""
+    y = sum over the kept neurons of a_n W_down^T[n].
 
-    def __init__(self, Wg, Wu, WdT, keep: int):
+    ``buffers_from``: another layer of the same shape whose intermediate
+    buffers (activations, keys, index list, count, workspace) this one reuses,
+    as the layers of a model decoded on one stream do."""
+
+    def __init__(self, Wg, Wu, WdT, keep: int, buffers_from=None):
         self.Wg, self.Wu, self.WdT, self.keep = Wg, Wu, WdT, keep
         N, d = Wg.shape
         dev = Wg.device
+        if _reuse(self, buffers_from, ("a", "key", "idx", "count", "ws")):
+            return
         self.a = torch.zeros(N, dtype=F32, device=dev)
         self.key = torch.zeros(N, dtype=I32, device=dev)
         self.idx = torch.zeros(max(keep, 1), dtype=I32, device=dev)
@@ -367,10 +383,12 @@ class TieredProjection:
     bf16, the next k_mid from 4-bit codes, the rest skipped.
 
     With ``weight_aware`` the columns are ranked by the WiSparse saliency
-    |x_j| * ||W[:, j]||_2 instead, the norms computed once here."""
+    |x_j| * ||W[:, j]||_2 instead, the norms computed once here.
+    ``buffers_from``: a projection of the same shape whose tier lists, counts
+    and workspace this one reuses (projections run one after another)."""
 
     def __init__(self, Wt: torch.Tensor, seg_rows, k_top: int, k_mid: int,
-                 weight_aware: bool = False):
+                 weight_aware: bool = False, buffers_from=None):
         self.Wt, self.seg_rows, self.k_top, self.k_mid = Wt, list(seg_rows), k_top, k_mid
         n_in, n_out = Wt.shape
         dev = Wt.device
@@ -381,6 +399,8 @@ class TieredProjection:
         rb = B.tier_record_bytes(n_out, len(seg_rows) - 1)
         self.rec = torch.zeros(n_in, rb, dtype=U8, device=dev)
         B.sparse_ffn_encode_tiers(Wt, self.seg_rows, self.rec)
+        if _reuse(self, buffers_from, ("idx_top", "idx_mid", "cnt", "ws")):
+            return
         self.idx_top = torch.zeros(max(k_top, 1), dtype=I32, device=dev)
         self.idx_mid = torch.zeros(max(k_mid, 1), dtype=I32, device=dev)
         self.cnt = torch.zeros(2, dtype=I32, device=dev)
@@ -544,12 +564,17 @@ class PredictedMoEStack(ReluMoEStack):
 
 class BatchedUnionLayer:
     """A batch of tokens: per-token top-``keep`` by |a|, the union of the
-    selections gathered once, each token's skipped neurons masked to zero."""
+    selections gathered once, each token's skipped neurons masked to zero.
+    ``buffers_from``: a layer of the same shape and batch whose intermediate
+    buffers this one reuses (layers run one after another; the frequency
+    counts are left at zero by every call)."""
 
-    def __init__(self, Wg, Wu, WdT, keep: int, batch: int):
+    def __init__(self, Wg, Wu, WdT, keep: int, batch: int, buffers_from=None):
         self.Wg, self.Wu, self.WdT, self.keep, self.batch = Wg, Wu, WdT, keep, batch
         N, d = Wg.shape
         dev = Wg.device
+        if _reuse(self, buffers_from, ("A", "K", "M", "F", "U", "cnt", "ws")):
+            return
         self.A = torch.zeros(batch, N, dtype=F32, device=dev)
         self.K = torch.zeros(batch, N, dtype=I32, device=dev)
         self.M = torch.zeros(batch, N, dtype=U8, device=dev)

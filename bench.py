@@ -433,7 +433,10 @@ def run_c0(args, torch, B, synth, P, T):
         mats = [synth.weight_bf16(args.seed, synth.W_C0, c, 0, t, N, d)
                 for t in (synth.T_GATE, synth.T_UP, synth.T_DOWN)]
         host_w = host_w or mats
-        lay.append(P.SwigluSparseLayer(*[P.to_device_bf16(m, dev) for m in mats], keep))
+        # the copies stand for successive layers: one set of intermediate
+        # buffers (activations, index list, workspace) serves them all
+        lay.append(P.SwigluSparseLayer(*[P.to_device_bf16(m, dev) for m in mats], keep,
+                                       buffers_from=lay[0] if lay else None))
     n_tok = (args.steps + 2) * copies
     X_host = synth.tokens(args.seed, synth.W_C0, 0, n_tok, d)
     X = torch.from_numpy(X_host).to(dev)
@@ -514,8 +517,12 @@ def run_c2(args, torch, B, synth, P, T):
         Wq = synth.torch_weight_bf16(args.seed, synth.W_C2, c, 0, synth.T_QKV, d, n_qkv, dev)
         Wd = synth.torch_weight_bf16(args.seed, synth.W_C2, c, 0, synth.T_DOWN, dff, d, dev)
         wa = args.weight_aware
-        projs.append((P.TieredProjection(Wq, seg_qkv, kq_t, kq_m, weight_aware=wa),
-                      P.TieredProjection(Wd, [0, d], kd_t, kd_m, weight_aware=wa)))
+        # the copies stand for successive layers and share their tier lists
+        # and workspaces
+        projs.append((P.TieredProjection(Wq, seg_qkv, kq_t, kq_m, weight_aware=wa,
+                                         buffers_from=projs[0][0] if projs else None),
+                      P.TieredProjection(Wd, [0, d], kd_t, kd_m, weight_aware=wa,
+                                         buffers_from=projs[0][1] if projs else None)))
     n_tok = copies * (args.steps + 2)
     Xq_host = synth.tokens(args.seed, synth.W_C2, 1, n_tok, d)
     Xd_host = synth.tokens(args.seed, synth.W_C2, 2, n_tok, dff)
@@ -797,7 +804,8 @@ def run_c4(args, torch, B, synth, P, T):
     for c in range(copies):
         w = [synth.torch_weight_bf16(args.seed, synth.W_C4, c, 0, t, N, d, dev)
              for t in (synth.T_GATE, synth.T_UP, synth.T_DOWN)]
-        lays.append(P.BatchedUnionLayer(*w, keep, batch))
+        # the copies stand for successive layers and share their buffers
+        lays.append(P.BatchedUnionLayer(*w, keep, batch, buffers_from=lays[0] if lays else None))
     n_b = args.steps + 2
     X_host = synth.tokens(args.seed, synth.W_C4, batch, n_b * copies * batch, d)
     X = torch.from_numpy(X_host).to(dev).view(n_b * copies, batch, d)
