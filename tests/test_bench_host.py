@@ -42,7 +42,9 @@ def _sha(csrc, sources=SOURCES):
 
 
 @pytest.mark.parametrize("tag", [TAG, "rowop_glu_swiglu_top50_layer", "rowop_relu_gate_moe",
-                                 "tiered_down_spax", "axpy_b1_swiglu_top50_layer"])
+                                 "tiered_down_spax", "tiered_qkv_spax", "axpy_b1_swiglu_top50_layer",
+                                 "moe_gathered_layer", "union_down_b1", "union_down_b4",
+                                 "union_down_b8", "union_down_b16"])
 def test_committed_traffic_follows_its_sources(tag):
     with open(os.path.join(ROOT, "profiles", f"traffic_{tag}.json")) as fh:
         rec = json.load(fh)
