@@ -80,7 +80,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_tiered_gemv.restype = _i
         L.sparse_ffn_tiered_gemv.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _i,
                                              _vp, _vp, _i, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 12:
+        L.sparse_ffn_fused_swiglu.restype = _i
+        L.sparse_ffn_fused_swiglu.argtypes = [_vp, _vp, _vp, _i, _i, _i, _vp, _f, _vp, _vp, _i,
+                                              _vp, _vp, _i, _vp, _sz, _vp]
+        if L.sffn_abi_version() != 13:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -192,6 +195,25 @@ def sparse_ffn_gemv_noalloc(op: int, W0: torch.Tensor | None, W1: torch.Tensor |
         _p(idx), _p(count), k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale),
         float(rms_eps), _p(aux), _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out),
         _ld(out, out.shape[-1]), int(accumulate), _stream(stream)))
+
+
+def sparse_ffn_fused_swiglu(Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
+                            x: torch.Tensor, y: torch.Tensor, *, idx: torch.Tensor | None = None,
+                            count: torch.Tensor | None = None, k_max: int = 0,
+                            rms_eps: float = 0.0, a_out: torch.Tensor | None = None,
+                            accumulate: bool = False, workspace: torch.Tensor | None = None,
+                            stream=None) -> None:
+    """One sparse SwiGLU FFN at batch 1, a pass per neuron (gate, up, silu *
+    mul, down row).  Wg / Wu / Wd are [n_rows][d] views with one row stride
+    (e.g. the three column blocks of a [n][3d] per-neuron record buffer)."""
+    n_rows, d = Wg.shape[0], Wg.shape[1]
+    ld_w = Wg.stride(0)
+    if Wu.stride(0) != ld_w or Wd.stride(0) != ld_w:
+        raise ValueError("Wg, Wu and Wd must share one row stride")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().sparse_ffn_fused_swiglu(
+        _p(Wg), _p(Wu), _p(Wd), n_rows, d, ld_w, _p(x), float(rms_eps), _p(idx), _p(count),
+        k_max, _p(a_out), _p(y), int(accumulate), _p(workspace), ws_bytes, _stream(stream)))
 
 
 def sparse_ffn_row_norms(W: torch.Tensor, out: torch.Tensor, stream=None) -> None:

@@ -283,6 +283,40 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                   "gemv launch");
 }
 
+sffn_status sparse_ffn_fused_swiglu(const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                                    int n_rows, int d, int ld_w, const float* x, float rms_eps,
+                                    const int32_t* idx, const int32_t* count, int k_max,
+                                    float* a_out, float* y, int accumulate, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  REQUIRE(Wg && Wu && Wd, SFFN_EINVAL, "fused_swiglu: Wg, Wu and Wd must be non-null");
+  REQUIRE(aligned(Wg, 16) && aligned(Wu, 16) && aligned(Wd, 16), SFFN_EINVAL,
+          "fused_swiglu: Wg/Wu/Wd must be 16-byte aligned");
+  REQUIRE(x && y, SFFN_EINVAL, "fused_swiglu: x and y must be non-null");
+  REQUIRE(aligned(x, 16) && aligned(y, 16), SFFN_EINVAL, "fused_swiglu: x/y must be 16-byte aligned");
+  REQUIRE(n_rows >= 0, SFFN_EINVAL, "fused_swiglu: n_rows=%d must be >= 0", n_rows);
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "fused_swiglu: d=%d must be a positive multiple of 8", d);
+  REQUIRE(d <= 4096, SFFN_EUNSUPPORTED, "fused_swiglu: d=%d > 4096", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL,
+          "fused_swiglu: ld_w=%d must be >= d and a multiple of 8", ld_w);
+  REQUIRE(rms_eps >= 0.f && std::isfinite(rms_eps), SFFN_EINVAL,
+          "fused_swiglu: rms_eps must be finite and >= 0");
+  if (idx) {
+    REQUIRE(count != nullptr, SFFN_EINVAL, "fused_swiglu: idx needs a device count");
+    REQUIRE(k_max >= 0 && k_max <= n_rows, SFFN_EINVAL, "fused_swiglu: k_max=%d outside [0, n_rows=%d]",
+            k_max, n_rows);
+    REQUIRE(aligned(idx, 4) && aligned(count, 4), SFFN_EINVAL, "fused_swiglu: idx/count misaligned");
+  }
+  if (a_out) REQUIRE(aligned(a_out, 4), SFFN_EINVAL, "fused_swiglu: a_out misaligned");
+  const long items = idx ? (long)k_max : (long)n_rows;
+  const size_t need = sffn::workspace_bytes(1, (int)items, d);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
+          "fused_swiglu: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "fused_swiglu: workspace must be 256-byte aligned");
+  sffn::FusedArgs a{Wg, Wu, Wd, ld_w, n_rows, d, x, rms_eps, idx, count, k_max, a_out, y,
+                    accumulate ? 1 : 0, workspace, ws_bytes};
+  return from_hip(sffn::launch_fused_swiglu(a, (hipStream_t)stream), "fused_swiglu launch");
+}
+
 sffn_status sparse_ffn_row_norms(const uint16_t* W, int n_rows, int d, int ld_w, float* out,
                                  void* stream) {
   REQUIRE(W && out, SFFN_EINVAL, "row_norms: W and out must be non-null");

@@ -182,6 +182,19 @@ hipError_t launch_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out
                                const int* seg_bounds, int n_seg, uint8_t* rec,
                                int rec_bytes, hipStream_t s);
 
+// Fused sparse-SwiGLU decode at batch 1: gate, up, silu * mul and the down
+// row of every processed neuron in one pass; workgroup partials of y in the
+// workspace, added in order by the split-K reduction.
+struct FusedArgs {
+  const uint16_t* Wg; const uint16_t* Wu; const uint16_t* Wd; int ld_w;
+  int n_rows, d;
+  const float* x; float rms_eps;
+  const int32_t* idx; const int32_t* count; int k_max;
+  float* a_out; float* y; int accumulate;
+  void* ws; size_t ws_bytes;
+};
+hipError_t launch_fused_swiglu(const FusedArgs& a, hipStream_t s);
+
 hipError_t launch_compact(const uint16_t* W, int ld_w, int d, const int32_t* idx, int k,
                           int transpose, uint16_t* out, int ld_out, hipStream_t s);
 hipError_t launch_gather32(const uint32_t* src, int n_src, const int32_t* idx,

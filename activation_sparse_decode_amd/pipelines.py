@@ -175,6 +175,47 @@ class SelectInferStack:
             B.sparse_ffn_compact(WdT, idx, k, True, dT)
             self.comp.append((gu[:k], dT, ac, k))
 
+    def compact_records(self) -> None:
+        """Gather each layer's U_l weights into one record per neuron for the
+        fused decode: [gate row | up row | down row (W_down^T)], 3d bf16, so
+        a layer's weights are read as one sequential stream.  A per-prompt
+        step like compact() (reads the |U_l| counts to the host once)."""
+        cnt = self.U_cnt.cpu().tolist()
+        d, dev = self.d, self.U_idx.device
+        self.rec = []
+        for l, k in enumerate(cnt):
+            Wg, Wu, WdT = self.layers[l]
+            R = torch.zeros(max(k, 1), 3 * d, dtype=torch.int16, device=dev)
+            idx = self.U_idx[l]
+            B.sparse_ffn_compact(Wg, idx, k, False, R[:, :d])
+            B.sparse_ffn_compact(Wu, idx, k, False, R[:, d:2 * d])
+            B.sparse_ffn_compact(WdT, idx, k, False, R[:, 2 * d:])
+            self.rec.append(R[:k])
+
+    def decode_layer_fused(self, l: int, h: torch.Tensor, a_out=None) -> None:
+        """Decode one layer in one pass per neuron of U_l over its records
+        (gate, up, silu * mul and the down row; a second launch adds the
+        workgroups' partials to the residual h in a fixed order)."""
+        R, d = self.rec[l], self.d
+        B.sparse_ffn_fused_swiglu(R[:, :d], R[:, d:2 * d], R[:, 2 * d:], h, h,
+                                  rms_eps=self.rms_eps, a_out=a_out, accumulate=True,
+                                  workspace=self.ws)
+
+    def decode_layer_fused_gathered(self, l: int, h: torch.Tensor, a_out=None) -> None:
+        """The fused pass straight from the full weights through U_l's index
+        list (no compaction)."""
+        Wg, Wu, WdT = self.layers[l]
+        B.sparse_ffn_fused_swiglu(Wg, Wu, WdT, h, h, idx=self.U_idx[l],
+                                  count=self.U_cnt[l:l + 1], k_max=self.k_max,
+                                  rms_eps=self.rms_eps, a_out=a_out, accumulate=True,
+                                  workspace=self.ws)
+
+    def decode_fused(self, h: torch.Tensor) -> None:
+        """One decode token through every layer with the fused pass
+        (compact_records() first)."""
+        for l in range(self.L):
+            self.decode_layer_fused(l, h)
+
     def decode_layer_gathered(self, l: int, h: torch.Tensor) -> None:
         """Decode one layer straight from the full weights through U_l."""
         Wg, Wu, WdT = self.layers[l]

@@ -280,6 +280,7 @@ def run_c1(args, torch, B, synth, P, T):
     gg = T.capture(lambda: [stack.decode_gate_up(l, h) for l in range(L)])
     glu_us = T.replay_ms(gg, args.steps) * 1e3 / (args.steps * L)
     log(f"gate/up over U: {glu_us:.2f} us/launch")
+    fused = run_c1_fused(args, torch, stack, Xd, h, xcur, g, L, d, U_cnt, T)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -313,7 +314,50 @@ def run_c1(args, torch, B, synth, P, T):
                                     glu_total / L, glu_us,
                                     measured_traffic("rowop_glu_selectinfer_decode",
                                                      ["rowop_b1.hip", "sffn_device.h"])),
+                  fused_decode=fused,
                   cpu_baseline=cpu)
+
+
+def fused_bytes(u: int, d: int) -> int:
+    """One fused layer over u neurons: the gate, up and down bf16 rows of d
+    per neuron, h read, the workgroups' fp32 partials written and read back
+    by the reduction (G = min(256, ceil(u / 8)) of d each), h read and
+    written by the reduction."""
+    G = min(256, max(1, (u + 7) // 8))
+    return 3 * u * d * 2 + 4 * d + 2 * G * d * 4 + 2 * 4 * d
+
+
+def run_c1_fused(args, torch, stack, Xd, h, xcur, g_two, L, d, U_cnt, T):
+    """The same decode with the fused per-neuron pass (one record of gate, up
+    and down rows per neuron of U; a second launch adds the workgroup
+    partials to the residual), timed the same way; plus the largest
+    difference from the two-launch decode over one token."""
+    stack.compact_records()
+
+    def step():
+        h.copy_(xcur)
+        stack.decode_fused(h)
+
+    gf = T.capture(step)
+    for t in range(args.warmup):
+        xcur.copy_(Xd[t])
+        gf.replay()
+    torch.cuda.synchronize()
+    ms = T.replay_ms(gf, args.steps, before=lambda i: xcur.copy_(Xd[args.warmup + i]))
+    us_tok = ms * 1e3 / args.steps
+    xcur.copy_(Xd[0])
+    g_two.replay()
+    torch.cuda.synchronize()
+    ref = h.clone()
+    gf.replay()
+    torch.cuda.synchronize()
+    diff = float((h - ref).abs().max() / ref.pow(2).mean().sqrt())
+    byts = int(sum(fused_bytes(int(u), d) for u in U_cnt))
+    log(f"fused decode: {us_tok:.1f} us/token; max |fused - two-launch| / rms = {diff:.2e}")
+    return {"kernels": "fused_swiglu_kernel + splitk_reduce_kernel per layer",
+            "us_per_token": round(us_tok, 2), "us_per_layer": round(us_tok / L, 3),
+            "bytes_per_token": byts, "GBps": round(byts / (us_tok * 1e-6) / 1e9, 1),
+            "max_rel_diff_vs_two_launch": diff}
 
 
 # ============================================================ c1-loading: SelectInfer Table 1 knobs

@@ -99,7 +99,7 @@ const char* sffn_last_error(void);
 /* ABI revision of this header (bumped on any change of a signature or of what
    a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 12
+#define SFFN_ABI_VERSION 13
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -301,6 +301,47 @@ sffn_status sparse_ffn_gemv_noalloc(int op,
                                     const float* alpha,
                                     float* out, uint32_t* key_out, int ld_out, int accumulate,
                                     void* stream);
+
+/*
+ * sparse_ffn_fused_swiglu -- one sparse SwiGLU FFN at batch 1 in a single
+ * pass per neuron ([SelectInfer] §5 computes only the neurons of the set U;
+ * [LeanStream] "Permutation-Invariant Execution": the FFN output is a sum
+ * over hidden neurons, so each neuron's contribution can be finished on its
+ * own, in any order).  For every processed neuron n:
+ *   a_n = silu(s * W_g[n].x) * (s * W_u[n].x),  silu(z) = z / (1 + e^-z),
+ *   y   = (accumulate ? y : 0) + sum_n a_n * W_d[n],
+ * with s = 1 / sqrt(mean(x^2) + rms_eps) if rms_eps > 0 (the unit-gain
+ * RMSNorm of sparse_ffn_gemv's row ops), else s = 1.  Processed neurons:
+ * all n < n_rows if idx is NULL (e.g. a set U compacted once per prompt
+ * with sparse_ffn_compact, decoded with no indirection), otherwise idx[i]
+ * for i < min(*count, k_max).  Skipped neurons are never read.
+ *  Wg, Wu : bf16 [n_rows][ld_w], row n = neuron n's gate / up weights
+ *           (length d).
+ *  Wd     : bf16 [n_rows][ld_w], row n = W_down^T[n], the neuron's down
+ *           weights over the d outputs (d_model in and out).  The three
+ *           matrices share ld_w, so one record per neuron [gate | up | down]
+ *           (ld_w = 3d, Wu = Wg + d, Wd = Wg + 2d) streams a layer as one
+ *           sequential read.
+ *  x      : fp32 [d]; y : fp32 [d]; x and y may be the same buffer (a
+ *           residual stream updated in place): y is written by a second
+ *           kernel after every read of x.
+ *  a_out  : nullable fp32 [n_rows]: a_n at each processed neuron n; other
+ *           entries are left untouched.
+ *  workspace: sparse_ffn_workspace_size(1, rows, d) bytes, rows = k_max if
+ *           idx is given, else n_rows; 256-byte aligned; no initialisation.
+ *           The workgroups' partial sums are added in a fixed order (a
+ *           second kernel): results are bitwise reproducible run to run.
+ * Limits: d % 8 == 0, 8 <= d <= 4096 (EUNSUPPORTED above), ld_w >= d,
+ * ld_w % 8 == 0, Wg / Wu / Wd / x / y 16-byte aligned, 0 <= k_max <=
+ * n_rows.  Errors: EINVAL for a bad argument, EWORKSPACE for a missing or
+ * short workspace; nothing is launched then.
+ */
+sffn_status sparse_ffn_fused_swiglu(const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd,
+                                    int n_rows, int d, int ld_w,
+                                    const float* x, float rms_eps,
+                                    const int32_t* idx, const int32_t* count, int k_max,
+                                    float* a_out, float* y, int accumulate,
+                                    void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * sparse_ffn_row_norms -- out[r] = sqrt(sum_{o < d} W[r][o]^2) for each row r

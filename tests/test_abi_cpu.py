@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 12
+    assert L.sffn_abi_version() == 13
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -214,6 +214,47 @@ def test_gemv_noalloc_limits(L):
     rc, msg = status_and_msg(L, f(3, FAKE, NULL, 64, 64, 64, FAKE, 1, 64, FAKE, FAKE, 4, 32, NULL,
                                   0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 64, 0, NULL))
     assert rc == 1 and "exceeds" in msg
+
+
+def fused(L, Wg=FAKE, Wu=FAKE, Wd=FAKE, n_rows=64, d=64, ld_w=192, x=FAKE, eps=0.0, idx=NULL,
+          count=NULL, k_max=0, a_out=NULL, y=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return status_and_msg(L, L.sparse_ffn_fused_swiglu(Wg, Wu, Wd, n_rows, d, ld_w, x,
+                                                       ctypes.c_float(eps), idx, count, k_max,
+                                                       a_out, y, 1, ws, ws_bytes, NULL))
+
+
+def test_fused_swiglu_validation(L):
+    """The fused per-neuron SwiGLU entry rejects bad arguments before any
+    launch, with the documented status."""
+    rc, msg = fused(L, Wd=NULL)
+    assert rc == 1 and "Wd" in msg
+    rc, msg = fused(L, Wu=ctypes.c_void_p(0x1008))
+    assert rc == 1 and "16-byte" in msg
+    rc, msg = fused(L, x=NULL)
+    assert rc == 1 and "x and y" in msg
+    rc, msg = fused(L, d=60, ld_w=192)
+    assert rc == 1 and "multiple of 8" in msg
+    rc, msg = fused(L, d=4104, ld_w=4104 * 3)
+    assert rc == 2 and "4096" in msg
+    rc, msg = fused(L, d=64, ld_w=56)
+    assert rc == 1 and "ld_w" in msg
+    rc, msg = fused(L, eps=-1.0)
+    assert rc == 1 and "rms_eps" in msg
+    rc, msg = fused(L, eps=float("nan"))
+    assert rc == 1 and "rms_eps" in msg
+    rc, msg = fused(L, idx=FAKE, count=NULL, k_max=4)
+    assert rc == 1 and "count" in msg
+    rc, msg = fused(L, idx=FAKE, count=FAKE, k_max=65)
+    assert rc == 1 and "k_max" in msg
+    rc, msg = fused(L, a_out=ctypes.c_void_p(0x1002))
+    assert rc == 1 and "a_out" in msg
+    rc, msg = fused(L, ws=NULL, ws_bytes=0)
+    assert rc == 3 and "workspace" in msg
+    need = L.sparse_ffn_workspace_size(1, 64, 64)
+    rc, msg = fused(L, ws_bytes=need - 1)
+    assert rc == 3 and "workspace" in msg
+    rc, msg = fused(L, ws=ctypes.c_void_p(0x1010))
+    assert rc == 1 and "256-byte" in msg
 
 
 def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),
