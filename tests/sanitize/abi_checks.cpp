@@ -161,6 +161,27 @@ void single_thread_cases() {
          SFFN_EINVAL, "k=");
   expect("norms d", sparse_ffn_row_norms(W(), 8, 60, 64, Fo(), nullptr), SFFN_EINVAL,
          "multiple of 8");
+
+  // fused per-neuron SwiGLU
+  auto fused = [](const uint16_t* Wd, int d, int ld_w, float eps, const int32_t* idx,
+                  const int32_t* cnt, int k_max, void* ws, size_t ws_bytes) {
+    return sparse_ffn_fused_swiglu(W(), W(), Wd, 64, d, ld_w, F(), eps, idx, cnt, k_max, nullptr,
+                                   Fo(), 1, ws, ws_bytes, nullptr);
+  };
+  expect("fused Wd", fused(nullptr, 64, 192, 0.f, nullptr, nullptr, 0, FAKE, 1 << 30), SFFN_EINVAL,
+         "Wd");
+  expect("fused align", fused(W(MIS4), 64, 192, 0.f, nullptr, nullptr, 0, FAKE, 1 << 30),
+         SFFN_EINVAL, "16-byte");
+  expect("fused d", fused(W(), 4104, 12312, 0.f, nullptr, nullptr, 0, FAKE, 1 << 30),
+         SFFN_EUNSUPPORTED, "4096");
+  expect("fused eps", fused(W(), 64, 192, -1.f, nullptr, nullptr, 0, FAKE, 1 << 30), SFFN_EINVAL,
+         "rms_eps");
+  expect("fused count", fused(W(), 64, 192, 0.f, I(), nullptr, 4, FAKE, 1 << 30), SFFN_EINVAL,
+         "count");
+  expect("fused k_max", fused(W(), 64, 192, 0.f, I(), I(), 65, FAKE, 1 << 30), SFFN_EINVAL,
+         "k_max");
+  expect("fused workspace", fused(W(), 64, 192, 0.f, nullptr, nullptr, 0, nullptr, 0),
+         SFFN_EWORKSPACE, "workspace");
 }
 
 // Several threads provoke different errors at once; each must read back the
