@@ -22,6 +22,8 @@ KEY_ABS_F32, KEY_U32, KEY_F32 = 0, 1, 2
 SCORE_SUM_ABS, SCORE_CLUSTER_MAX, SCORE_SOFTMAX_PICKED = 0, 1, 2
 OP_GLU_SILU, OP_DOT_RELU, OP_GATED, OP_AXPY, OP_DOT, OP_GLU_RELU, OP_PREDICT = 0, 1, 2, 3, 4, 5, 6
 OP_DOT_RELU_CLUSTER = 7
+PACKED = 0x100                                  # op flag: W0 / W1 in a packed layout
+LAYOUT_ROW_TILES, LAYOUT_COL_PANELS = 1, 2
 
 _STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
 
@@ -83,7 +85,11 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_fused_swiglu.restype = _i
         L.sparse_ffn_fused_swiglu.argtypes = [_vp, _vp, _vp, _i, _i, _i, _vp, _f, _vp, _vp, _i,
                                               _vp, _vp, _i, _vp, _sz, _vp]
-        if L.sffn_abi_version() != 13:
+        L.sparse_ffn_packed_elems.restype = _sz
+        L.sparse_ffn_packed_elems.argtypes = [_i, _i, _i]
+        L.sparse_ffn_pack_weights.restype = _i
+        L.sparse_ffn_pack_weights.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
+        if L.sffn_abi_version() != 14:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -105,6 +111,27 @@ def _stream(stream=None):
 
 def _ld(t, default: int) -> int:
     return t.stride(0) if (t is not None and t.dim() == 2) else default
+
+
+class PackedWeights:
+    """A weight matrix in a packed layout of the batched kernels: the flat
+    packed data and the logical [n_rows][d] shape (built by pack_weights)."""
+
+    def __init__(self, data: torch.Tensor, n_rows: int, d: int, layout: int):
+        self.data, self.n_rows, self.d, self.layout = data, n_rows, d, layout
+
+    @property
+    def shape(self):
+        return (self.n_rows, self.d)
+
+
+def _weights(op: int, W0, W1):
+    """Pointers, op and shape for row-major tensors or PackedWeights."""
+    W = W0 if W0 is not None else W1
+    if isinstance(W, PackedWeights):
+        ptr = lambda w: None if w is None else ctypes.c_void_p(w.data.data_ptr())  # noqa: E731
+        return op | PACKED, ptr(W0), ptr(W1), W.n_rows, W.d, W.d
+    return op, _p(W0), _p(W1), W.shape[0], W.shape[1], W.stride(0)
 
 
 # ------------------------------------------------------------------ sizes
@@ -162,15 +189,13 @@ def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,
                     aux: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
                     key_out: torch.Tensor | None = None, accumulate: bool = False,
                     workspace: torch.Tensor | None = None, stream=None) -> None:
-    W = W0 if W0 is not None else W1
-    n_rows, d = W.shape[0], W.shape[1]
-    ld_w = W.stride(0)
+    op, p0, p1, n_rows, d, ld_w = _weights(op, W0, W1)
     batch = inp.shape[0] if inp.dim() == 2 else 1
     ld_in = _ld(inp, inp.shape[-1])
     ld_out = _ld(out, out.shape[-1])
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib().sparse_ffn_gemv(
-        op, _p(W0), _p(W1), n_rows, d, ld_w, _p(inp), batch, ld_in, _p(idx), _p(count),
+        op, p0, p1, n_rows, d, ld_w, _p(inp), batch, ld_in, _p(idx), _p(count),
         k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale), float(rms_eps), _p(aux),
         _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out), ld_out, int(accumulate),
         _p(workspace), ws_bytes, _stream(stream)))
@@ -187,11 +212,10 @@ def sparse_ffn_gemv_noalloc(op: int, W0: torch.Tensor | None, W1: torch.Tensor |
                             stream=None) -> None:
     """sparse_ffn_gemv without a workspace: AXPY's scratch is the library's
     static per-GPU array (shared by every call on that GPU)."""
-    W = W0 if W0 is not None else W1
-    n_rows, d = W.shape[0], W.shape[1]
+    op, p0, p1, n_rows, d, ld_w = _weights(op, W0, W1)
     batch = inp.shape[0] if inp.dim() == 2 else 1
     _check(lib().sparse_ffn_gemv_noalloc(
-        op, _p(W0), _p(W1), n_rows, d, W.stride(0), _p(inp), batch, _ld(inp, inp.shape[-1]),
+        op, p0, p1, n_rows, d, ld_w, _p(inp), batch, _ld(inp, inp.shape[-1]),
         _p(idx), _p(count), k_max, group, _p(row_mask), _ld(row_mask, n_rows), float(tau_scale),
         float(rms_eps), _p(aux), _ld(aux, n_rows), _p(alpha), _p(out), _p(key_out),
         _ld(out, out.shape[-1]), int(accumulate), _stream(stream)))
@@ -214,6 +238,23 @@ def sparse_ffn_fused_swiglu(Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor
     _check(lib().sparse_ffn_fused_swiglu(
         _p(Wg), _p(Wu), _p(Wd), n_rows, d, ld_w, _p(x), float(rms_eps), _p(idx), _p(count),
         k_max, _p(a_out), _p(y), int(accumulate), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def packed_elems(n_rows: int, d: int, layout: int) -> int:
+    return int(lib().sparse_ffn_packed_elems(n_rows, d, layout))
+
+
+def pack_weights(W: torch.Tensor, layout: int, out: torch.Tensor | None = None,
+                 stream=None) -> PackedWeights:
+    """W [n_rows][d] (row-major bf16 bits) re-laid in a packed layout of the
+    batched kernels (LAYOUT_ROW_TILES for row ops, LAYOUT_COL_PANELS for AXPY)."""
+    n_rows, d = W.shape[0], W.shape[1]
+    n_out = packed_elems(n_rows, d, layout)
+    if out is None:
+        out = torch.empty(max(n_out, 8), dtype=torch.int16, device=W.device)
+    _check(lib().sparse_ffn_pack_weights(_p(W), n_rows, d, W.stride(0), layout, _p(out),
+                                         _stream(stream)))
+    return PackedWeights(out, n_rows, d, layout)
 
 
 def sparse_ffn_row_norms(W: torch.Tensor, out: torch.Tensor, stream=None) -> None:

@@ -200,6 +200,8 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                             int ld_mask, float tau_scale, float rms_eps, const float* aux, int ld_aux,
                             const float* alpha, float* out, uint32_t* key_out, int ld_out,
                             int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  const int packed = (op & SFFN_PACKED) ? 1 : 0;
+  op &= ~SFFN_PACKED;
   REQUIRE(op >= 0 && op <= 7, SFFN_EINVAL, "gemv: unknown op %d", op);
   REQUIRE(in && out, SFFN_EINVAL, "gemv: in and out must be non-null");
   REQUIRE(n_rows >= 0, SFFN_EINVAL, "gemv: n_rows=%d must be >= 0", n_rows);
@@ -217,6 +219,17 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     REQUIRE(k_max >= 0 && (long)k_max * group <= n_rows, SFFN_EINVAL,
             "gemv: k_max=%d * group=%d exceeds n_rows=%d", k_max, group, n_rows);
     REQUIRE(aligned(idx, 4) && aligned(count, 4), SFFN_EINVAL, "gemv: idx/count misaligned");
+  }
+  if (packed) {
+    REQUIRE(batch > 1, SFFN_EUNSUPPORTED,
+            "gemv: packed weights are read by the batched kernels only (batch > 1)");
+    REQUIRE(ld_w == d, SFFN_EINVAL, "gemv: packed weights take ld_w == d (d=%d, ld_w=%d)", d, ld_w);
+    if (op == SFFN_OP_AXPY)
+      REQUIRE(d % 256 == 0, SFFN_EUNSUPPORTED, "gemv: packed AXPY weights need d %% 256 == 0 (d=%d)",
+              d);
+    else
+      REQUIRE(d % 128 == 0, SFFN_EUNSUPPORTED,
+              "gemv: packed row-op weights need d %% 128 == 0 (d=%d)", d);
   }
   const long items = idx ? (long)k_max * group : (long)n_rows;
   hipStream_t s = (hipStream_t)stream;
@@ -261,7 +274,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                       (idx || op == SFFN_OP_DOT_RELU_CLUSTER) ? group : 1, tau_scale, rms_eps,
                       aux, ld_aux, out, key_out,
                       ld_out, accumulate ? 1 : 0, batch > 1 ? workspace : nullptr,
-                      batch > 1 && workspace ? ws_bytes : 0};
+                      batch > 1 && workspace ? ws_bytes : 0, packed};
     return from_hip(batch == 1 ? sffn::launch_rowop_b1(a, s) : sffn::launch_rowop_mfma(a, s),
                     "gemv launch");
   }
@@ -278,7 +291,8 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
           "gemv: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
   sffn::AxpyArgs a{W0, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max, idx ? group : 1,
-                   row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes};
+                   row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes,
+                   packed};
   return from_hip(batch == 1 ? sffn::launch_axpy_b1(a, s) : sffn::launch_axpy_mfma(a, s),
                   "gemv launch");
 }
@@ -315,6 +329,30 @@ sffn_status sparse_ffn_fused_swiglu(const uint16_t* Wg, const uint16_t* Wu, cons
   sffn::FusedArgs a{Wg, Wu, Wd, ld_w, n_rows, d, x, rms_eps, idx, count, k_max, a_out, y,
                     accumulate ? 1 : 0, workspace, ws_bytes};
   return from_hip(sffn::launch_fused_swiglu(a, (hipStream_t)stream), "fused_swiglu launch");
+}
+
+size_t sparse_ffn_packed_elems(int n_rows, int d, int layout) {
+  return sffn::packed_elems(n_rows, d, layout);
+}
+
+sffn_status sparse_ffn_pack_weights(const uint16_t* W, int n_rows, int d, int ld_w, int layout,
+                                    uint16_t* out, void* stream) {
+  REQUIRE(W && out, SFFN_EINVAL, "pack: W and out must be non-null");
+  REQUIRE(layout == SFFN_LAYOUT_ROW_TILES || layout == SFFN_LAYOUT_COL_PANELS, SFFN_EINVAL,
+          "pack: unknown layout %d", layout);
+  REQUIRE(n_rows >= 0, SFFN_EINVAL, "pack: n_rows=%d must be >= 0", n_rows);
+  REQUIRE(d > 0 && d % (layout == SFFN_LAYOUT_ROW_TILES ? 128 : 256) == 0, SFFN_EINVAL,
+          "pack: d=%d must be a positive multiple of %d for layout %d", d,
+          layout == SFFN_LAYOUT_ROW_TILES ? 128 : 256, layout);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL, "pack: ld_w=%d must be >= d and a multiple of 8",
+          ld_w);
+  REQUIRE(aligned(W, 16) && aligned(out, 16), SFFN_EINVAL, "pack: W/out must be 16-byte aligned");
+  const size_t n_out = sffn::packed_elems(n_rows, d, layout);
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(W), o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t w1 = w0 + 2 * ((n_rows > 0 ? (size_t)(n_rows - 1) * ld_w : 0) + (size_t)d);
+  REQUIRE(o0 + 2 * n_out <= w0 || o0 >= w1, SFFN_EINVAL, "pack: out overlaps W");
+  return from_hip(sffn::launch_pack(W, n_rows, d, ld_w, layout, out, (hipStream_t)stream),
+                  "pack launch");
 }
 
 sffn_status sparse_ffn_row_norms(const uint16_t* W, int n_rows, int d, int ld_w, float* out,
@@ -573,7 +611,7 @@ sffn_status sparse_ffn_gemv_noalloc(int op, const uint16_t* W0, const uint16_t* 
                                     void* stream) {
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  if (op == SFFN_OP_AXPY) {
+  if ((op & ~SFFN_PACKED) == SFFN_OP_AXPY) {
     // the size check needs no GPU: sizes beyond the array are rejected first
     REQUIRE(batch >= 1 && d >= 8 && n_rows >= 0 && k_max >= 0 && group >= 1, SFFN_EINVAL,
             "gemv_noalloc: bad shape (batch=%d d=%d n_rows=%d k_max=%d group=%d)", batch, d,

@@ -60,10 +60,14 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
   const int k0 = ks * chunk;
   const int k1 = min(n_items, k0 + chunk);
 
-  // weight loader: column chunk lc (8 columns), rows lr + 8j
+  // weight loader: column chunk lc (8 columns), rows lr + 8j.  Row-major: row
+  // r at r * ld_w.  Packed column panels: the 256 columns of this workgroup's
+  // tile are one contiguous 512-byte piece per row, rows back to back.
   const int lc = t & 31, lr = t >> 5;
   const int lcol = col0 + 8 * lc;
   const int lcolc = lcol < a.d ? lcol : 0;   // lanes past the last column re-read column 0
+  const uint16_t* wbase = a.packed ? a.W + (size_t)ct * a.n_rows * kOT + 8 * lc : a.W + lcolc;
+  const size_t wstride = a.packed ? (size_t)kOT : (size_t)a.ld_w;
   // activation loader: token am, rows kAR ar .. kAR ar + kAR - 1 of the stage
   const int am = t >> 4, ar = t & 15;
   const int tok = m0 + am;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
       const int base = st * kKT;
 #pragma unroll
       for (int j = 0; j < kWJ; ++j)
-        v[j] = load_stream16(a.W + (size_t)rows_s[base + lr + 8 * j] * a.ld_w + lcolc);
+        v[j] = load_stream16(wbase + (size_t)rows_s[base + lr + 8 * j] * wstride);
 #pragma unroll
       for (int e = 0; e < kAR; ++e) {
         const int r = rows_s[base + kAR * ar + e];

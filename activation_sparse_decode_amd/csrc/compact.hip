@@ -10,10 +10,14 @@
 //                major, so the down projection becomes one dot product per
 //                output over the compacted activations); columns i >= k up
 //                to ld_out are zero.
+// The packed layouts of the batched MFMA kernels are built here too (a
+// one-time re-layout of a weight matrix at load time).
 // A 4-byte gather, dst[i] = src[idx_i], carries per-neuron values (scores,
 // masks, keys) into the positions of a compacted subset: the index remap of
 // a selectively loaded layer (SelectInfer §4), whose resident weights hold
 // only the loaded neurons, in ascending order.
+#include <algorithm>
+
 #include "sffn_device.h"
 
 namespace sffn {
@@ -86,6 +90,66 @@ hipError_t launch_gather32(const uint32_t* src, int n_src, const int32_t* idx,
                            const int32_t* count, int k_max, uint32_t* dst, hipStream_t s) {
   hipLaunchKernelGGL(gather32_kernel, dim3((k_max + 255) / 256), dim3(256), 0, s, src, n_src, idx,
                      count, k_max, dst);
+  return hipGetLastError();
+}
+
+// Packed layouts of the batched kernels (see sffn_device.h), one 16-byte
+// output unit per thread: each thread reads the 8 weights its unit holds
+// from the row-major source (zeros for padding rows) and stores them, so
+// the stores are contiguous.
+__global__ __launch_bounds__(256) void pack_row_tiles_kernel(const uint16_t* __restrict__ W,
+                                                             int n_rows, int d, int ld_w,
+                                                             uint16_t* __restrict__ out,
+                                                             size_t units) {
+  const int cpr = d >> 7;   // 128-wide chunks per row
+  for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < units;
+       u += (size_t)gridDim.x * blockDim.x) {
+    // u = ((tile * cpr + chunk) * 16 + row in tile) * 16 + unit in chunk
+    const int q = (int)(u & 15);
+    const int rr = (int)((u >> 4) & 15);
+    const size_t tc = u >> 8;
+    const int c = (int)(tc % cpr);
+    const size_t r = (tc / cpr) * 16 + rr;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < (size_t)n_rows) v = *reinterpret_cast<const uint4*>(W + r * ld_w + 128 * c + 8 * q);
+    *reinterpret_cast<uint4*>(out + 8 * u) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_col_panels_kernel(const uint16_t* __restrict__ W,
+                                                              int n_rows, int ld_w,
+                                                              uint16_t* __restrict__ out,
+                                                              size_t units) {
+  for (size_t u = blockIdx.x * (size_t)blockDim.x + threadIdx.x; u < units;
+       u += (size_t)gridDim.x * blockDim.x) {
+    // u = (panel * n_rows + row) * 32 + unit in panel row
+    const int q = (int)(u & 31);
+    const size_t pr = u >> 5;
+    const size_t r = pr % (size_t)n_rows;
+    const size_t p = pr / (size_t)n_rows;
+    *reinterpret_cast<uint4*>(out + 8 * u) =
+        *reinterpret_cast<const uint4*>(W + r * ld_w + 256 * p + 8 * q);
+  }
+}
+
+size_t packed_elems(int n_rows, int d, int layout) {
+  if (n_rows < 0 || d <= 0) return 0;
+  if (layout == kLayoutRowTiles && d % 128 == 0) return ((size_t)n_rows + 15) / 16 * 16 * d;
+  if (layout == kLayoutColPanels && d % 256 == 0) return (size_t)n_rows * d;
+  return 0;
+}
+
+hipError_t launch_pack(const uint16_t* W, int n_rows, int d, int ld_w, int layout, uint16_t* out,
+                       hipStream_t s) {
+  const size_t units = packed_elems(n_rows, d, layout) / 8;
+  if (units == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((units + 255) / 256, 8192);
+  if (layout == kLayoutRowTiles)
+    hipLaunchKernelGGL(pack_row_tiles_kernel, dim3(blocks), dim3(256), 0, s, W, n_rows, d, ld_w,
+                       out, units);
+  else
+    hipLaunchKernelGGL(pack_col_panels_kernel, dim3(blocks), dim3(256), 0, s, W, n_rows, ld_w, out,
+                       units);
   return hipGetLastError();
 }
 

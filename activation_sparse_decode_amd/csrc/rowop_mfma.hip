@@ -18,6 +18,10 @@
 // chunk's weights and activations are in flight while the current chunk is
 // contracted.
 //
+// Packed weights (row tiles, see sffn_device.h): the same work split and
+// arithmetic; only the addresses differ, so results are bitwise those of the
+// row-major layout.
+//
 // Balance (dense row ops with a workspace): a layer whose tile pairs do not
 // split evenly over the 256 CUs (17408 neurons = 544 pairs: a third of the
 // CUs would carry a third workgroup) runs the largest multiple of 256 pairs
@@ -143,12 +147,17 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a, int G_main
     const int q = it / a.group;
     return a.idx[q] * a.group + (it - q * a.group);
   };
-  // weight loader: lane l loads rows 4i + (l >> 4), 16 bytes at k-offset 8*(l & 15)
+  // weight loader: lane l loads rows 4i + (l >> 4), 16 bytes at k-offset
+  // 8*(l & 15).  Row-major: row r at r * ld_w, chunk c at 128 c.  Packed row
+  // tiles: the 16 rows of a tile and the 128 k of a chunk are one contiguous
+  // 4 KB block (a wave's chunk is one sequential read), chunk c 16 * 128 c on.
+  const size_t kstep = a.packed ? 16 : 1;
   size_t woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = item_to_row(t0 + 4 * i + (lane >> 4));
-    woff[i] = (size_t)r * a.ld_w + 8 * (lane & 15);
+    woff[i] = a.packed ? (size_t)(r >> 4) * 16 * a.d + (size_t)(r & 15) * kKC + 8 * (lane & 15)
+                       : (size_t)r * a.ld_w + 8 * (lane & 15);
   }
   const int my_row = item_to_row(t0 + nl);          // output column of this lane
   const bool my_live = t0 + nl < n_items;
@@ -170,7 +179,8 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a, int G_main
   const int nA = (ce - cb + 1) / 2, nB = ce - cb - nA;
   const int my_n = half ? nB : nA;
   const int my_c0 = cb + (half ? nA : 0);
-  const bool has_tail = ce == nch && nch * kKC < a.d;   // the k past the last chunk
+  // the k past the last chunk (row-major only: packed rows have d % 128 == 0)
+  const bool has_tail = ce == nch && nch * kKC < a.d && !a.packed;
   u32x4 wr0[4], wr1[4];   // in-flight weights (this lane's share of its next chunk)
   float4 xr[2][2];        // in-flight activations: [half][8 values]
   auto load_chunk = [&](int c) {
@@ -178,8 +188,8 @@ __global__ __launch_bounds__(256) void rowop_mfma_kernel(RowOpArgs a, int G_main
       const int k = (my_c0 + c) * kKC;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (kW0) wr0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.W0 + woff[i] + k));
-        if (kW1) wr1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.W1 + woff[i] + k));
+        if (kW0) wr0[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.W0 + woff[i] + k * kstep));
+        if (kW1) wr1[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.W1 + woff[i] + k * kstep));
       }
     }
 #pragma unroll

@@ -96,6 +96,7 @@ struct RowOpArgs {
   const float* aux; int ld_aux;
   float* out; uint32_t* key_out; int ld_out; int accumulate;
   void* ws; size_t ws_bytes;   // optional (batched row ops: K split of the last tiles)
+  int packed;                  // W0 / W1 in the row-tile layout (batched kernel only)
 };
 hipError_t launch_rowop_b1(const RowOpArgs& a, hipStream_t s);
 hipError_t launch_rowop_mfma(const RowOpArgs& a, hipStream_t s);
@@ -127,6 +128,7 @@ struct AxpyArgs {
   const float* alpha;
   float* out; int ld_out; int accumulate;
   void* ws; size_t ws_bytes;
+  int packed;                  // W in the column-panel layout (batched kernel only)
 };
 hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s);
 hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s);
@@ -194,6 +196,18 @@ struct FusedArgs {
   void* ws; size_t ws_bytes;
 };
 hipError_t launch_fused_swiglu(const FusedArgs& a, hipStream_t s);
+
+// Packed weight layouts of the batched (MFMA) kernels.
+//  row tiles   : element (r, k) at ((r / 16) * (d / 128) + k / 128) * 2048
+//                + (r % 16) * 128 + k % 128; rows padded to a multiple of 16
+//                with zeros (d % 128 == 0).
+//  col panels  : element (r, o) at (o / 256) * n * 256 + r * 256 + o % 256
+//                (d % 256 == 0).
+constexpr int kLayoutRowTiles = 1;
+constexpr int kLayoutColPanels = 2;
+size_t packed_elems(int n_rows, int d, int layout);
+hipError_t launch_pack(const uint16_t* W, int n_rows, int d, int ld_w, int layout, uint16_t* out,
+                       hipStream_t s);
 
 hipError_t launch_compact(const uint16_t* W, int ld_w, int d, const int32_t* idx, int k,
                           int transpose, uint16_t* out, int ld_out, hipStream_t s);

@@ -610,10 +610,19 @@ class BatchedUnionLayer:
     buffers this one reuses (layers run one after another; the frequency
     counts are left at zero by every call)."""
 
-    def __init__(self, Wg, Wu, WdT, keep: int, batch: int, buffers_from=None):
+    def __init__(self, Wg, Wu, WdT, keep: int, batch: int, buffers_from=None,
+                 packed: bool = False):
         self.Wg, self.Wu, self.WdT, self.keep, self.batch = Wg, Wu, WdT, keep, batch
         N, d = Wg.shape
         dev = Wg.device
+        # packed: the batched kernels read the weights re-laid once here (gate
+        # and up in row tiles, down in column panels) -- contiguous blocks
+        # where the row-major layout gives 256- and 512-byte pieces of rows
+        self.packed = packed and batch > 1
+        if self.packed:
+            self.Pg = B.pack_weights(Wg, B.LAYOUT_ROW_TILES)
+            self.Pu = B.pack_weights(Wu, B.LAYOUT_ROW_TILES)
+            self.Pd = B.pack_weights(WdT, B.LAYOUT_COL_PANELS)
         if _reuse(self, buffers_from, ("A", "K", "M", "F", "U", "cnt", "ws")):
             return
         self.A = torch.zeros(batch, N, dtype=F32, device=dev)
@@ -626,13 +635,13 @@ class BatchedUnionLayer:
 
     def __call__(self, X: torch.Tensor, Y: torch.Tensor) -> None:
         N = self.Wg.shape[0]
+        Wg, Wu, WdT = (self.Pg, self.Pu, self.Pd) if self.packed else (self.Wg, self.Wu, self.WdT)
         # the workspace lets the batched gate/up split its last tiles along K
-        B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, X, self.A, key_out=self.K,
-                          workspace=self.ws)
+        B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, X, self.A, key_out=self.K, workspace=self.ws)
         # F starts at zero (allocation) and the union select resets it as it
         # reads it, ready for the next batch's counts
         B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M, freq=self.F)
         B.sparse_ffn_select(self.F, B.KEY_U32, 0, N, nonzero_only=True, idx_out=self.U,
                             count_out=self.cnt, clear_keys=True)
-        B.sparse_ffn_gemv(B.OP_AXPY, self.WdT, None, self.A, Y, idx=self.U, count=self.cnt,
+        B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.A, Y, idx=self.U, count=self.cnt,
                           k_max=N, row_mask=self.M, workspace=self.ws)

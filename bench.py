@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--workload", default="all",
                    choices=["all", "c0", "c1", "c1-loading", "c2", "c3", "c4"])
     p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
+    p.add_argument("--layout", choices=("packed", "rows"), default="packed",
+                   help="c4 at batch > 1: weights packed for the batched kernels, or row-major")
     p.add_argument("--predictor", action="store_true",
                    help="workload c3: clusters from an online predictor (PowerInfer-2), no dense gate")
     p.add_argument("--weight-aware", action="store_true",
@@ -851,7 +853,8 @@ def run_c4(args, torch, B, synth, P, T):
         w = [synth.torch_weight_bf16(args.seed, synth.W_C4, c, 0, t, N, d, dev)
              for t in (synth.T_GATE, synth.T_UP, synth.T_DOWN)]
         # the copies stand for successive layers and share their buffers
-        lays.append(P.BatchedUnionLayer(*w, keep, batch, buffers_from=lays[0] if lays else None))
+        lays.append(P.BatchedUnionLayer(*w, keep, batch, buffers_from=lays[0] if lays else None,
+                                        packed=args.layout == "packed"))
     n_b = args.steps + 2
     X_host = synth.tokens(args.seed, synth.W_C4, batch, n_b * copies * batch, d)
     X = torch.from_numpy(X_host).to(dev).view(n_b * copies, batch, d)
@@ -871,16 +874,20 @@ def run_c4(args, torch, B, synth, P, T):
                         per_step=copies * batch)
     u = float(np.mean([int(l.cnt.cpu()[0]) for l in lays]))
 
+    def weights(l):
+        return (l.Pg, l.Pu, l.Pd) if l.packed else (l.Wg, l.Wu, l.WdT)
+
     def glu_only():
         for c in range(copies):
-            B.sparse_ffn_gemv(B.OP_GLU_SILU, lays[c].Wg, lays[c].Wu, xb[c], lays[c].A,
+            Wg, Wu, _ = weights(lays[c])
+            B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, xb[c], lays[c].A,
                               key_out=lays[c].K, workspace=lays[c].ws)
 
     def down_only():
         for c in range(copies):
             l = lays[c]
-            B.sparse_ffn_gemv(B.OP_AXPY, l.WdT, None, l.A, Y[c], idx=l.U, count=l.cnt, k_max=N,
-                              row_mask=l.M, workspace=l.ws)
+            B.sparse_ffn_gemv(B.OP_AXPY, weights(l)[2], None, l.A, Y[c], idx=l.U, count=l.cnt,
+                              k_max=N, row_mask=l.M, workspace=l.ws)
 
     per = lambda body: T.replay_ms(T.capture(body), args.steps) * 1e3 / (args.steps * copies)  # noqa: E731
     glu_us, down_us = per(glu_only), per(down_only)
@@ -902,7 +909,9 @@ def run_c4(args, torch, B, synth, P, T):
     config = {"workload": f"batched decode, Qwen-27B-like layer (d_model 5120, d_ff 17408), "
                           f"per-token top 40%, union gathered once and contracted on MFMA, "
                           f"batch {batch} (4 rotating weight copies)",
-              "d_model": d, "d_ff": N, "batch": batch, "union_mean": u}
+              "d_model": d, "d_ff": N, "batch": batch, "union_mean": u,
+              "weight_layout": ("packed: gate/up in 16-row x 128 tiles, down in 256-column panels"
+                                if lays[0].packed else "row-major")}
     return result(us_batch / batch, "us/token", args.steps * copies, 2, total_ms / args.steps,
                   config, us_per_batch=round(us_batch, 3), step_bytes=step_b,
                   step_GBps=round(step_b / (us_batch * 1e-6) / 1e9, 1),

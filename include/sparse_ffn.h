@@ -93,13 +93,32 @@ typedef enum {
                                over the nonzero rows n of cluster c = n / group   */
 } sffn_gemv_op;
 
+/* Flag OR-ed into a sparse_ffn_gemv op: W0 / W1 are in the packed layout of
+   the batched (batch > 1) kernels, built by sparse_ffn_pack_weights: the
+   row-tile layout for the row ops (GLU_SILU, DOT_RELU, GATED, DOT), the
+   column-panel layout for AXPY.  Same rows processed, same arithmetic in the
+   same order: results are bitwise those of the row-major weights. */
+#define SFFN_PACKED 0x100
+
+/* Packed weight layouts (sparse_ffn_pack_weights). */
+typedef enum {
+    /* [ceil(n/16)][d/128][16][128]: element (r, k) at ((r/16)*(d/128) + k/128)
+       * 2048 + (r%16)*128 + k%128; rows past n are zero.  A batched row op
+       reads 16 rows x 128 k of one tile as one contiguous 4 KB block. */
+    SFFN_LAYOUT_ROW_TILES = 1,
+    /* [d/256][n][256]: element (r, o) at (o/256)*n*256 + r*256 + o%256.  The
+       batched AXPY reads a row's 256 outputs of one panel as one contiguous
+       512-byte piece, the rows of a panel back to back. */
+    SFFN_LAYOUT_COL_PANELS = 2
+} sffn_layout;
+
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* sffn_last_error(void);
 
 /* ABI revision of this header (bumped on any change of a signature or of what
    a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 13
+#define SFFN_ABI_VERSION 14
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -245,6 +264,9 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
  *
  * Limits: d % 8 == 0 (d % 32 == 0 when batch > 1), ld_w % 8 == 0, W0/W1/in/
  *  out 16-byte aligned, d <= 8192 for row ops at batch 1, 1 <= batch.
+ *  With SFFN_PACKED in op: batch > 1 (EUNSUPPORTED otherwise), ld_w == d,
+ *  d % 128 == 0 for row ops and d % 256 == 0 for AXPY (EUNSUPPORTED), and
+ *  W0 / W1 hold sparse_ffn_packed_elems(n_rows, d, layout) elements.
  *  workspace: AXPY needs sparse_ffn_workspace_size(batch, rows, d) bytes
  *  (rows = k_max*group or n_rows).  Row ops at batch 1 take none (may be
  *  NULL).  Row ops at batch > 1 without an index list use it when given
@@ -342,6 +364,26 @@ sffn_status sparse_ffn_fused_swiglu(const uint16_t* Wg, const uint16_t* Wu, cons
                                     const int32_t* idx, const int32_t* count, int k_max,
                                     float* a_out, float* y, int accumulate,
                                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_packed_elems -- bf16 elements of W [n_rows][d] in a packed
+ * layout (sffn_layout); 0 if d does not fit the layout (ROW_TILES: d % 128
+ * == 0; COL_PANELS: d % 256 == 0) or the layout is unknown.
+ *
+ * sparse_ffn_pack_weights -- out = W [n_rows][ld_w] (rows of length d)
+ * re-laid in a packed layout, once per weight matrix (load time), for the
+ * batched kernels' contiguous reads (sparse_ffn_gemv with SFFN_PACKED).  A
+ * layout only orders the same weights differently: which rows a product
+ * reads and what it computes are unchanged.
+ *  W   : bf16, 16-byte aligned, ld_w >= d, ld_w % 8 == 0.
+ *  out : bf16 [sparse_ffn_packed_elems(n_rows, d, layout)], 16-byte aligned,
+ *        not overlapping W.
+ * Errors: EINVAL for a bad argument or a layout d does not fit; nothing is
+ * launched then.
+ */
+size_t sparse_ffn_packed_elems(int n_rows, int d, int layout);
+sffn_status sparse_ffn_pack_weights(const uint16_t* W, int n_rows, int d, int ld_w, int layout,
+                                    uint16_t* out, void* stream);
 
 /*
  * sparse_ffn_row_norms -- out[r] = sqrt(sum_{o < d} W[r][o]^2) for each row r

@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 13
+    assert L.sffn_abi_version() == 14
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -255,6 +255,41 @@ def test_fused_swiglu_validation(L):
     assert rc == 3 and "workspace" in msg
     rc, msg = fused(L, ws=ctypes.c_void_p(0x1010))
     assert rc == 1 and "256-byte" in msg
+
+
+def test_packed_layouts_validation(L):
+    """Packed sizes, the pack entry's checks and the gemv flag's limits, all
+    rejected before any launch."""
+    from activation_sparse_decode_amd import binding as B
+    assert L.sparse_ffn_packed_elems(1000, 384, 1) == 1008 * 384      # rows padded to 16
+    assert L.sparse_ffn_packed_elems(1000, 512, 2) == 1000 * 512
+    assert L.sparse_ffn_packed_elems(1000, 200, 1) == 0               # d % 128
+    assert L.sparse_ffn_packed_elems(1000, 384, 2) == 0               # d % 256
+    assert L.sparse_ffn_packed_elems(10, 128, 3) == 0
+    pk = L.sparse_ffn_pack_weights
+    rc, msg = status_and_msg(L, pk(FAKE, 64, 384, 384, 3, ctypes.c_void_p(0x100000), NULL))
+    assert rc == 1 and "layout" in msg
+    rc, msg = status_and_msg(L, pk(FAKE, 64, 384, 384, 2, ctypes.c_void_p(0x100000), NULL))
+    assert rc == 1 and "multiple of 256" in msg
+    rc, msg = status_and_msg(L, pk(FAKE, 64, 256, 248, 1, ctypes.c_void_p(0x100000), NULL))
+    assert rc == 1 and "ld_w" in msg
+    rc, msg = status_and_msg(L, pk(FAKE, 64, 256, 256, 1, ctypes.c_void_p(0x1008), NULL))
+    assert rc == 1 and "aligned" in msg
+    rc, msg = status_and_msg(L, pk(FAKE, 64, 256, 256, 1, ctypes.c_void_p(0x1000 + 512), NULL))
+    assert rc == 1 and "overlaps" in msg
+    rc, msg = status_and_msg(L, pk(NULL, 64, 256, 256, 1, FAKE, NULL))
+    assert rc == 1 and "non-null" in msg
+    # the gemv flag: batched kernels only, ld_w == d, the layout's d multiple
+    rc, msg = gemv(L, op=B.OP_GLU_SILU | B.PACKED, ld_out=64)
+    assert rc == 2 and "batch > 1" in msg
+    rc, msg = gemv(L, op=B.OP_GLU_SILU | B.PACKED, d=256, ld_w=264, batch=4, ld_out=64, ld_in=256)
+    assert rc == 1 and "ld_w == d" in msg
+    rc, msg = gemv(L, op=B.OP_GLU_SILU | B.PACKED, d=96, ld_w=96, batch=4, ld_out=64, ld_in=96)
+    assert rc == 2 and "128" in msg
+    rc, msg = gemv(L, op=B.OP_AXPY | B.PACKED, d=384, ld_w=384, batch=4, ld_out=384, ld_in=64)
+    assert rc == 2 and "256" in msg
+    rc, msg = gemv(L, op=B.OP_GLU_RELU | B.PACKED, d=256, ld_w=256, batch=4, ld_out=64, ld_in=256)
+    assert rc == 2 and "batch 1" in msg
 
 
 def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),
