@@ -207,6 +207,11 @@ def test_gemv_noalloc_limits(L):
     assert rc == 3 and "static" in msg
     # the workloads' batched union (batch 16, d = 5120) fits
     assert L.sparse_ffn_workspace_size(16, 17408, 5120) <= (32 << 20)
+    # a packed AXPY (op flag 0x100) takes the same scratch and limit
+    rc, msg = status_and_msg(L, f(3 | 0x100, FAKE, NULL, 17408, 5120, 5120, FAKE, 256, 17408, NULL,
+                                  NULL, 0, 1, NULL, 0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 5120,
+                                  0, NULL))
+    assert rc == 3 and "static" in msg
     # row ops take no scratch: their argument errors are sparse_ffn_gemv's
     rc, msg = status_and_msg(L, f(0, FAKE, NULL, 64, 64, 64, FAKE, 1, 64, NULL, NULL, 0, 1, NULL,
                                   0, c(0), c(0), NULL, 0, NULL, FAKE, NULL, 64, 0, NULL))

@@ -26,9 +26,11 @@ def gathered_case(seed, N, d, k, batch):
     return WdT, A, U, M
 
 
-def run_both(WdT, A, U, M, batch):
+def run_both(WdT, A, U, M, batch, packed=False):
     N, d = WdT.shape
     W, Ad, Ud = dev(WdT), dev(A if batch > 1 else A[0]), dev(U)
+    if packed:
+        W = B.pack_weights(W, B.LAYOUT_COL_PANELS)
     cnt = torch.tensor([U.size], dtype=torch.int32, device="cuda")
     Md = dev(M) if batch > 1 else None
     shape = (batch, d) if batch > 1 else (d,)
@@ -43,8 +45,8 @@ def run_both(WdT, A, U, M, batch):
     return host(y_ws), host(y_na)
 
 
-def check(WdT, A, U, M, batch, what):
-    y_ws, y_na = run_both(WdT, A, U, M, batch)
+def check(WdT, A, U, M, batch, what, packed=False):
+    y_ws, y_na = run_both(WdT, A, U, M, batch, packed)
     assert np.array_equal(y_ws.view(np.uint32), y_na.view(np.uint32)), f"{what}: differs from gemv"
     y_na = y_na.reshape(batch, -1)
     for b in sorted({0, batch - 1}):
@@ -63,6 +65,14 @@ def test_noalloc_batched_two_calls():
     banner("noalloc batch 16: 17408x5120 k=16000, then batch 4 1000x256 k=300")
     check(*gathered_case(3, 17408, 5120, 16000, 16), 16, "batch 16 large")
     check(*gathered_case(4, 1000, 256, 300, 4), 4, "batch 4 small")
+
+
+def test_noalloc_packed_batched_two_calls():
+    """The same with packed column panels (the op flag reaches the static
+    scratch path like a row-major AXPY)."""
+    banner("noalloc packed: batch 16 17408x5120 k=16000, then batch 4 1000x256 k=300")
+    check(*gathered_case(6, 17408, 5120, 16000, 16), 16, "packed batch 16 large", packed=True)
+    check(*gathered_case(7, 1000, 256, 300, 4), 4, "packed batch 4 small", packed=True)
 
 
 def test_noalloc_row_op_and_limit():
