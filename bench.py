@@ -211,8 +211,8 @@ def cpu_baseline(fn, seconds, sample, per_unit=1, scale=1e6, unit="us/token"):
         one = {"value": s_one * scale, "cores": 1, "sample_units": n_one}
     except ImportError:
         pass
-    return {"value": s_all * scale, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{n_all} x {sample}", "one_core": one}
+    return {"value": s_all * scale, "unit": unit, "cores": cores, "host_cpus": os.cpu_count(),
+            "kind": "oracle", "sample": f"{n_all} x {sample}", "one_core": one}
 
 
 # ============================================================ c1: SelectInfer stack
@@ -987,7 +987,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     out["env"] = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
                   "compute_units": props.multi_processor_count,
-                  "hip": torch.version.hip, "torch": torch.__version__}
+                  "hip": torch.version.hip, "torch": torch.__version__, **clock_info()}
 
     # A plain device copy of known size: the reference that scales the HBM
     # counters (FETCH_SIZE / WRITE_SIZE) of profiled kernels to bytes.
@@ -995,6 +995,27 @@ def main():
     torch.empty_like(calib).copy_(calib)
     torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
+
+
+def clock_info() -> dict:
+    """The GPU's current clocks as rocm-smi reports them and the amdgpu driver
+    version, best effort (either is left out when the tool or file is absent)."""
+    import subprocess
+    info = {}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        cards = json.loads(r.stdout)
+        card = cards[sorted(cards)[0]]
+        info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
+    except Exception:   # noqa: BLE001 -- a missing tool or odd output only drops the field
+        pass
+    try:
+        with open("/sys/module/amdgpu/version") as f:
+            info["amdgpu_driver"] = f.read().strip()
+    except OSError:
+        pass
+    return info
 
 
 if __name__ == "__main__":
