@@ -336,7 +336,8 @@ sffn_status sparse_ffn_gemv_noalloc(int op,
  * RMSNorm of sparse_ffn_gemv's row ops), else s = 1.  Processed neurons:
  * all n < n_rows if idx is NULL (e.g. a set U compacted once per prompt
  * with sparse_ffn_compact, decoded with no indirection), otherwise idx[i]
- * for i < min(*count, k_max).  Skipped neurons are never read.
+ * for i < min(*count, k_max) (device int32, 0 <= idx[i] < n_rows, a
+ * precondition the kernels do not check).  Skipped neurons are never read.
  *  Wg, Wu : bf16 [n_rows][ld_w], row n = neuron n's gate / up weights
  *           (length d).
  *  Wd     : bf16 [n_rows][ld_w], row n = W_down^T[n], the neuron's down

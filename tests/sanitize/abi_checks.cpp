@@ -182,6 +182,25 @@ void single_thread_cases() {
          "k_max");
   expect("fused workspace", fused(W(), 64, 192, 0.f, nullptr, nullptr, 0, nullptr, 0),
          SFFN_EWORKSPACE, "workspace");
+
+  // packed layouts and the gemv flag
+  if (sparse_ffn_packed_elems(1000, 384, SFFN_LAYOUT_ROW_TILES) != (size_t)1008 * 384) {
+    std::printf("FAIL packed elems\n"); ++failures;
+  }
+  uint16_t* const OUT = static_cast<uint16_t*>(reinterpret_cast<void*>(0x100000));
+  expect("pack layout", sparse_ffn_pack_weights(W(), 64, 384, 384, 3, OUT, nullptr), SFFN_EINVAL,
+         "layout");
+  expect("pack d", sparse_ffn_pack_weights(W(), 64, 384, 384, SFFN_LAYOUT_COL_PANELS, OUT, nullptr),
+         SFFN_EINVAL, "multiple of 256");
+  expect("pack overlap", sparse_ffn_pack_weights(W(), 64, 256, 256, SFFN_LAYOUT_ROW_TILES,
+                                                 static_cast<uint16_t*>(FAKE), nullptr),
+         SFFN_EINVAL, "overlaps");
+  expect("packed batch 1", gemv(SFFN_OP_GLU_SILU | SFFN_PACKED, 64, 128, 128, 1, nullptr, nullptr,
+                                0, 1, nullptr, 0, F(), W(), 0.f, 0.f, nullptr, 0, 64, 128),
+         SFFN_EUNSUPPORTED, "batch > 1");
+  expect("packed axpy d", gemv(SFFN_OP_AXPY | SFFN_PACKED, 64, 384, 384, 4, nullptr, nullptr, 0, 1,
+                               FAKE, 1 << 30, F(), W(), 0.f, 0.f, nullptr, 0, 384, 64),
+         SFFN_EUNSUPPORTED, "256");
 }
 
 // Several threads provoke different errors at once; each must read back the
