@@ -605,7 +605,8 @@ class PredictedMoEStack(ReluMoEStack):
 
 class BatchedUnionLayer:
     """A batch of tokens: per-token top-``keep`` by |a|, the union of the
-    selections gathered once, each token's skipped neurons masked to zero.
+    selections gathered once, each token's skipped neurons masked to zero
+    (one token: its own selection is the union, listed by one select).
     ``buffers_from``: a layer of the same shape and batch whose intermediate
     buffers this one reuses (layers run one after another; the frequency
     counts are left at zero by every call)."""
@@ -638,6 +639,16 @@ class BatchedUnionLayer:
         Wg, Wu, WdT = (self.Pg, self.Pu, self.Pd) if self.packed else (self.Wg, self.Wu, self.WdT)
         # the workspace lets the batched gate/up split its last tiles along K
         B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, X, self.A, key_out=self.K, workspace=self.ws)
+        if self.batch == 1:
+            # one token: the union is the token's own set, so its ascending
+            # list comes straight from the token's select (the frequency
+            # counts and the union select would return the same list), and
+            # every listed row is the token's (no mask in the product)
+            B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M, idx_out=self.U,
+                                count_out=self.cnt)
+            B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.A, Y, idx=self.U, count=self.cnt,
+                              k_max=N, workspace=self.ws)
+            return
         # F starts at zero (allocation) and the union select resets it as it
         # reads it, ready for the next batch's counts
         B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M, freq=self.F)

@@ -886,13 +886,14 @@ def run_c4(args, torch, B, synth, P, T):
     def down_only():
         for c in range(copies):
             l = lays[c]
+            # at batch 1 the list is the token's own set: no mask (as the layer)
             B.sparse_ffn_gemv(B.OP_AXPY, weights(l)[2], None, l.A, Y[c], idx=l.U, count=l.cnt,
-                              k_max=N, row_mask=l.M, workspace=l.ws)
+                              k_max=N, row_mask=l.M if batch > 1 else None, workspace=l.ws)
 
     per = lambda body: T.replay_ms(T.capture(body), args.steps) * 1e3 / (args.steps * copies)  # noqa: E731
     glu_us, down_us = per(glu_only), per(down_only)
     glu_b = 2 * N * d * 2 + batch * (4 * d + 8 * N)
-    down_b = int(u * d * 2 + 4 * u + batch * (5 * u + 4 * d))
+    down_b = int(u * d * 2 + 4 * u + batch * ((5 if batch > 1 else 4) * u + 4 * d))
     step_b = int(glu_b + down_b + batch * 5 * N)
     # at batch 1 the same calls run the wave-per-row kernel and the split-K gathered product
     k_glu, k_down = ("gate_up_mfma", "union_down_mfma") if batch > 1 else ("gate_up_rows", "union_down_splitk")
