@@ -23,6 +23,7 @@ SCORE_SUM_ABS, SCORE_CLUSTER_MAX, SCORE_SOFTMAX_PICKED = 0, 1, 2
 OP_GLU_SILU, OP_DOT_RELU, OP_GATED, OP_AXPY, OP_DOT, OP_GLU_RELU, OP_PREDICT = 0, 1, 2, 3, 4, 5, 6
 OP_DOT_RELU_CLUSTER = 7
 PACKED = 0x100                                  # op flag: W0 / W1 in a packed layout
+MASKED_ROWS = 0x200                             # op flag: AXPY over the rows some token's mask selects
 LAYOUT_ROW_TILES, LAYOUT_COL_PANELS = 1, 2
 
 _STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
@@ -89,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_packed_elems.argtypes = [_i, _i, _i]
         L.sparse_ffn_pack_weights.restype = _i
         L.sparse_ffn_pack_weights.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
-        if L.sffn_abi_version() != 14:
+        if L.sffn_abi_version() != 15:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib

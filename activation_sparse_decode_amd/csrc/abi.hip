@@ -201,7 +201,8 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
                             const float* alpha, float* out, uint32_t* key_out, int ld_out,
                             int accumulate, void* workspace, size_t ws_bytes, void* stream) {
   const int packed = (op & SFFN_PACKED) ? 1 : 0;
-  op &= ~SFFN_PACKED;
+  const int mask_rows = (op & SFFN_MASKED_ROWS) ? 1 : 0;
+  op &= ~(SFFN_PACKED | SFFN_MASKED_ROWS);
   REQUIRE(op >= 0 && op <= 7, SFFN_EINVAL, "gemv: unknown op %d", op);
   REQUIRE(in && out, SFFN_EINVAL, "gemv: in and out must be non-null");
   REQUIRE(n_rows >= 0, SFFN_EINVAL, "gemv: n_rows=%d must be >= 0", n_rows);
@@ -230,6 +231,15 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     else
       REQUIRE(d % 128 == 0, SFFN_EUNSUPPORTED,
               "gemv: packed row-op weights need d %% 128 == 0 (d=%d)", d);
+  }
+  if (mask_rows) {
+    REQUIRE(op == SFFN_OP_AXPY, SFFN_EINVAL, "gemv: SFFN_MASKED_ROWS applies to AXPY only");
+    REQUIRE(batch > 1, SFFN_EUNSUPPORTED, "gemv: SFFN_MASKED_ROWS needs batch > 1");
+    REQUIRE(!idx, SFFN_EINVAL, "gemv: SFFN_MASKED_ROWS takes no index list (idx must be NULL)");
+    REQUIRE(row_mask != nullptr, SFFN_EINVAL, "gemv: SFFN_MASKED_ROWS needs row_mask");
+    REQUIRE(aligned(row_mask, 16) && ld_mask % 16 == 0, SFFN_EINVAL,
+            "gemv: SFFN_MASKED_ROWS needs row_mask 16-byte aligned and ld_mask %% 16 == 0 "
+            "(ld_mask=%d)", ld_mask);
   }
   const long items = idx ? (long)k_max * group : (long)n_rows;
   hipStream_t s = (hipStream_t)stream;
@@ -292,7 +302,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
   REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
   sffn::AxpyArgs a{W0, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max, idx ? group : 1,
                    row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes,
-                   packed};
+                   packed, mask_rows};
   return from_hip(batch == 1 ? sffn::launch_axpy_b1(a, s) : sffn::launch_axpy_mfma(a, s),
                   "gemv launch");
 }
@@ -611,7 +621,7 @@ sffn_status sparse_ffn_gemv_noalloc(int op, const uint16_t* W0, const uint16_t* 
                                     void* stream) {
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  if ((op & ~SFFN_PACKED) == SFFN_OP_AXPY) {
+  if ((op & ~(SFFN_PACKED | SFFN_MASKED_ROWS)) == SFFN_OP_AXPY) {
     // the size check needs no GPU: sizes beyond the array are rejected first
     REQUIRE(batch >= 1 && d >= 8 && n_rows >= 0 && k_max >= 0 && group >= 1, SFFN_EINVAL,
             "gemv_noalloc: bad shape (batch=%d d=%d n_rows=%d k_max=%d group=%d)", batch, d,

@@ -22,6 +22,12 @@
 // copied to LDS, so they are in flight while that stage is contracted.
 // Split-K over row chunks; a second kernel sums the chunks' partials in
 // chunk order.
+//
+// Without an index list and with mask_rows set, the union is formed here:
+// a chunk is a range of neurons, and of each segment of it only the
+// neurons whose mask is set for some token of the workgroup's token tile
+// are listed (OR of the tokens' 16-byte mask words, then an in-order
+// compaction), so exactly those rows are read, once, in index order.
 #include "sffn_splitk.h"
 
 namespace sffn {
@@ -46,6 +52,8 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
   __shared__ uint32_t T[kKT * kPitch / 2];
   __shared__ uint4 As[2][16][kAPitch];      // activations of the stage, bf16 hi / lo
   __shared__ int rows_s[kSeg];
+  __shared__ uint32_t live_w[kSeg / 4];     // mask_rows: liveness byte per candidate
+  __shared__ uint32_t cnt_w[4];             // mask_rows: live rows per wave
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = wave_id();
@@ -81,11 +89,75 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
 
   for (int s0 = k0; s0 < k1; s0 += kSeg) {
     const int s1 = min(k1, s0 + kSeg);
-    const int nst = (s1 - s0 + kKT - 1) / kKT;
+    int nseg = s1 - s0;   // rows of this segment (mask_rows: its live rows)
     __syncthreads();   // the previous segment's readers of rows_s are done
-    // rows past the segment end repeat its last row (a valid row; weight 0)
-    for (int i = t; i < nst * kKT; i += 256)
-      rows_s[i] = item_row(a.idx, a.group, min(s0 + i, s1 - 1));
+    if (a.mask_rows) {
+      // liveness: thread t ORs the 16-byte mask words of candidates
+      // 16 (t & 127) .. +16 over tokens m0 + 8 (t >> 7) .. +8 of the tile
+      for (int i = t; i < kSeg / 4; i += 256) live_w[i] = 0u;
+      __syncthreads();
+      {
+        const int cb = t & 127, th = t >> 7;
+        if (16 * cb < nseg) {
+          uint4 o = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int b = m0 + 8 * th + e;
+            if (b < a.batch) {
+              const uint4 m = *reinterpret_cast<const uint4*>(a.row_mask + (size_t)b * a.ld_mask +
+                                                             s0 + 16 * cb);
+              o.x |= m.x; o.y |= m.y; o.z |= m.z; o.w |= m.w;
+            }
+          }
+          atomicOr(&live_w[4 * cb], o.x);
+          atomicOr(&live_w[4 * cb + 1], o.y);
+          atomicOr(&live_w[4 * cb + 2], o.z);
+          atomicOr(&live_w[4 * cb + 3], o.w);
+        }
+      }
+      __syncthreads();
+      // in-order compaction: thread t takes candidates 8t .. 8t + 7
+      const uint32_t lw0 = live_w[2 * t], lw1 = live_w[2 * t + 1];
+      uint32_t f = 0;   // bit k: candidate 8t + k is live
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t byte = ((k < 4 ? lw0 : lw1) >> (8 * (k & 3))) & 0xFFu;
+        f |= ((byte != 0u) && (8 * t + k < nseg) ? 1u : 0u) << k;
+      }
+      const uint32_t c = (uint32_t)__popc(f);
+      uint32_t incl = c;   // inclusive scan of the counts over the wave
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      if (lane == 63) cnt_w[w] = incl;
+      __syncthreads();
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        before += ww < w ? cnt_w[ww] : 0u;
+        total += cnt_w[ww];
+      }
+      uint32_t pos = before + incl - c;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if ((f >> k) & 1u) rows_s[pos++] = s0 + 8 * t + k;
+      nseg = (int)total;
+      if (nseg == 0) continue;   // uniform: no live row in this segment
+      __syncthreads();
+      // rows past the last live one repeat it (a live row; weight 0)
+      const int nst = (nseg + kKT - 1) / kKT;
+      const int last = rows_s[nseg - 1];
+      __syncthreads();
+      for (int i = nseg + t; i < nst * kKT; i += 256) rows_s[i] = last;
+    } else {
+      const int nst = (nseg + kKT - 1) / kKT;
+      // rows past the segment end repeat its last row (a valid row; weight 0)
+      for (int i = t; i < nst * kKT; i += 256)
+        rows_s[i] = item_row(a.idx, a.group, min(s0 + i, s1 - 1));
+    }
+    const int nst = (nseg + kKT - 1) / kKT;
     __syncthreads();
 
     // raw loads only (no branch on a loaded value), so a stage's requests
@@ -120,7 +192,7 @@ __global__ __launch_bounds__(256) void axpy_mfma_kernel(AxpyArgs a, int KS, int 
         float av[kAR];
 #pragma unroll
         for (int e = 0; e < kAR; ++e) {
-          const bool keep = tok_ok && s0 + st * kKT + kAR * ar + e < s1 && (!has_mask || mb[e] != 0u);
+          const bool keep = tok_ok && st * kKT + kAR * ar + e < nseg && (!has_mask || mb[e] != 0u);
           av[e] = keep ? xr[e] : 0.f;
         }
         uint32_t hi[kAR / 2], lo[kAR / 2];

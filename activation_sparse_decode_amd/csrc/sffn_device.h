@@ -129,6 +129,7 @@ struct AxpyArgs {
   float* out; int ld_out; int accumulate;
   void* ws; size_t ws_bytes;
   int packed;                  // W in the column-panel layout (batched kernel only)
+  int mask_rows;               // no index list: the rows some token's mask selects (batched)
 };
 hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s);
 hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s);

@@ -606,14 +606,19 @@ class PredictedMoEStack(ReluMoEStack):
 class BatchedUnionLayer:
     """A batch of tokens: per-token top-``keep`` by |a|, the union of the
     selections gathered once, each token's skipped neurons masked to zero
-    (one token: its own selection is the union, listed by one select).
+    (one token: its own selection is the union, listed by one select; more:
+    the product reads the rows some token's mask selects).
     ``buffers_from``: a layer of the same shape and batch whose intermediate
     buffers this one reuses (layers run one after another; the frequency
     counts are left at zero by every call)."""
 
     def __init__(self, Wg, Wu, WdT, keep: int, batch: int, buffers_from=None,
-                 packed: bool = False):
+                 packed: bool = False, union_list: bool = False):
         self.Wg, self.Wu, self.WdT, self.keep, self.batch = Wg, Wu, WdT, keep, batch
+        # batch > 1: the product forms the union from the tokens' masks
+        # (SFFN_MASKED_ROWS), or with union_list the frequency counts and a
+        # union select list it first
+        self.union_list = union_list
         N, d = Wg.shape
         dev = Wg.device
         # packed: the batched kernels read the weights re-laid once here (gate
@@ -628,7 +633,9 @@ class BatchedUnionLayer:
             return
         self.A = torch.zeros(batch, N, dtype=F32, device=dev)
         self.K = torch.zeros(batch, N, dtype=I32, device=dev)
-        self.M = torch.zeros(batch, N, dtype=U8, device=dev)
+        # token masks with a row stride of a multiple of 16 bytes (the masked
+        # product reads them 16 bytes at a time)
+        self.M = torch.zeros(batch, (N + 15) // 16 * 16, dtype=U8, device=dev)[:, :N]
         self.F = torch.zeros(N, dtype=I32, device=dev)
         self.U = torch.zeros(N, dtype=I32, device=dev)
         self.cnt = torch.zeros(1, dtype=I32, device=dev)
@@ -648,6 +655,11 @@ class BatchedUnionLayer:
                                 count_out=self.cnt)
             B.sparse_ffn_gemv(B.OP_AXPY, WdT, None, self.A, Y, idx=self.U, count=self.cnt,
                               k_max=N, workspace=self.ws)
+            return
+        if not self.union_list:
+            B.sparse_ffn_select(self.K, B.KEY_U32, 0, self.keep, mask_out=self.M)
+            B.sparse_ffn_gemv(B.OP_AXPY | B.MASKED_ROWS, WdT, None, self.A, Y, row_mask=self.M,
+                              workspace=self.ws)
             return
         # F starts at zero (allocation) and the union select resets it as it
         # reads it, ready for the next batch's counts

@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--batch", type=int, default=16, help="tokens per step of workload c4")
     p.add_argument("--layout", choices=("packed", "rows"), default="packed",
                    help="c4 at batch > 1: weights packed for the batched kernels, or row-major")
+    p.add_argument("--union", choices=("mask", "list"), default="mask",
+                   help="c4 at batch > 1: union formed in the product from the token masks, "
+                        "or listed first (frequency counts and a union select)")
     p.add_argument("--predictor", action="store_true",
                    help="workload c3: clusters from an online predictor (PowerInfer-2), no dense gate")
     p.add_argument("--weight-aware", action="store_true",
@@ -854,7 +857,8 @@ def run_c4(args, torch, B, synth, P, T):
              for t in (synth.T_GATE, synth.T_UP, synth.T_DOWN)]
         # the copies stand for successive layers and share their buffers
         lays.append(P.BatchedUnionLayer(*w, keep, batch, buffers_from=lays[0] if lays else None,
-                                        packed=args.layout == "packed"))
+                                        packed=args.layout == "packed",
+                                        union_list=args.union == "list"))
     n_b = args.steps + 2
     X_host = synth.tokens(args.seed, synth.W_C4, batch, n_b * copies * batch, d)
     X = torch.from_numpy(X_host).to(dev).view(n_b * copies, batch, d)
@@ -872,7 +876,8 @@ def run_c4(args, torch, B, synth, P, T):
     us_batch = total_ms * 1e3 / (args.steps * copies)
     dist = T.step_stats(gs, args.steps, before=lambda i: xb.copy_(X[i * copies:(i + 1) * copies]),
                         per_step=copies * batch)
-    u = float(np.mean([int(l.cnt.cpu()[0]) for l in lays]))
+    u = float(np.mean([int((l.M != 0).any(dim=0).sum()) for l in lays]))   # union sizes
+    masked = batch > 1 and not lays[0].union_list
 
     def weights(l):
         return (l.Pg, l.Pu, l.Pd) if l.packed else (l.Wg, l.Wu, l.WdT)
@@ -886,6 +891,10 @@ def run_c4(args, torch, B, synth, P, T):
     def down_only():
         for c in range(copies):
             l = lays[c]
+            if masked:   # the union formed in the product from the token masks
+                B.sparse_ffn_gemv(B.OP_AXPY | B.MASKED_ROWS, weights(l)[2], None, l.A, Y[c],
+                                  row_mask=l.M, workspace=l.ws)
+                continue
             # at batch 1 the list is the token's own set: no mask (as the layer)
             B.sparse_ffn_gemv(B.OP_AXPY, weights(l)[2], None, l.A, Y[c], idx=l.U, count=l.cnt,
                               k_max=N, row_mask=l.M if batch > 1 else None, workspace=l.ws)
@@ -893,7 +902,10 @@ def run_c4(args, torch, B, synth, P, T):
     per = lambda body: T.replay_ms(T.capture(body), args.steps) * 1e3 / (args.steps * copies)  # noqa: E731
     glu_us, down_us = per(glu_only), per(down_only)
     glu_b = 2 * N * d * 2 + batch * (4 * d + 8 * N)
-    down_b = int(u * d * 2 + 4 * u + batch * ((5 if batch > 1 else 4) * u + 4 * d))
+    if masked:   # union rows, every token's mask (the union is formed from them), activations
+        down_b = int(u * d * 2 + batch * (N + 4 * u + 4 * d))
+    else:        # union rows and their indices, per token activations (+ masks), outputs
+        down_b = int(u * d * 2 + 4 * u + batch * ((5 if batch > 1 else 4) * u + 4 * d))
     step_b = int(glu_b + down_b + batch * 5 * N)
     # at batch 1 the same calls run the wave-per-row kernel and the split-K gathered product
     k_glu, k_down = ("gate_up_mfma", "union_down_mfma") if batch > 1 else ("gate_up_rows", "union_down_splitk")
@@ -912,7 +924,10 @@ def run_c4(args, torch, B, synth, P, T):
                           f"batch {batch} (4 rotating weight copies)",
               "d_model": d, "d_ff": N, "batch": batch, "union_mean": u,
               "weight_layout": ("packed: gate/up in 16-row x 128 tiles, down in 256-column panels"
-                                if lays[0].packed else "row-major")}
+                                if lays[0].packed else "row-major"),
+              "union": ("formed in the product from the token masks" if masked
+                        else "the token's own list" if batch == 1
+                        else "listed by frequency counts and a union select")}
     return result(us_batch / batch, "us/token", args.steps * copies, 2, total_ms / args.steps,
                   config, us_per_batch=round(us_batch, 3), step_bytes=step_b,
                   step_GBps=round(step_b / (us_batch * 1e-6) / 1e9, 1),

@@ -100,6 +100,16 @@ typedef enum {
    same order: results are bitwise those of the row-major weights. */
 #define SFFN_PACKED 0x100
 
+/* Flag OR-ed into SFFN_OP_AXPY at batch > 1 with idx NULL and a row_mask:
+   only the rows whose mask is nonzero for some token of the batch are read
+   -- the union of the tokens' selections ([SelectInfer] §5; [LeanStream]
+   "Permutation-Invariant Execution": the union read once as one dense
+   block) formed inside the product, in index order, with no index list or
+   count.  The result is that of the union's index list (up to the order
+   of fp32 additions).  Needs row_mask 16-byte aligned and ld_mask % 16 == 0
+   (EINVAL), batch > 1 (EUNSUPPORTED). */
+#define SFFN_MASKED_ROWS 0x200
+
 /* Packed weight layouts (sparse_ffn_pack_weights). */
 typedef enum {
     /* [ceil(n/16)][d/128][16][128]: element (r, k) at ((r/16)*(d/128) + k/128)
@@ -118,7 +128,7 @@ const char* sffn_last_error(void);
 /* ABI revision of this header (bumped on any change of a signature or of what
    a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 14
+#define SFFN_ABI_VERSION 15
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster

@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 14
+    assert L.sffn_abi_version() == 15
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first

@@ -22,10 +22,13 @@ def make(N, d, batch, seed=0):
     return Wg, Wu, WdT, X
 
 
-def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None):
+def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None, union_list=False):
     Wg, Wu, WdT, X = make(N, d, batch, seed)
     keep = pct_count(pct, N)
-    layer = BatchedUnionLayer(dev(Wg), dev(Wu), dev(WdT), keep, batch)
+    layer = BatchedUnionLayer(dev(Wg), dev(Wu), dev(WdT), keep, batch, union_list=union_list)
+    # the union as an index list exists at batch 1 and with union_list; the
+    # masked product forms it from the token masks without listing it
+    listed = batch == 1 or union_list
     Y = torch.zeros(batch, d, dtype=torch.float32, device="cuda")
     layer(dev(X), Y)
     torch.cuda.synchronize()
@@ -33,8 +36,8 @@ def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None):
     K = host_u32(layer.K)
     M = host(layer.M)
     F = host_u32(layer.F)
-    cnt = int(host(layer.cnt)[0])
-    U = host(layer.U)[:cnt]
+    cnt = int(host(layer.cnt)[0]) if listed else int(M.any(axis=0).sum())
+    U = host(layer.U)[:cnt] if listed else np.flatnonzero(M.any(axis=0))
     toks = range(batch) if sample_tokens is None else sample_tokens
     for b in toks:
         assert_close(A[b], oracle.swiglu_acts(Wg, Wu, X[b]), what=f"activations b={b}")
@@ -60,21 +63,30 @@ def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None):
     torch.cuda.synchronize()
     A2 = host(layer.A)
     S2 = [oracle.rank_range(oracle.key_abs(A2[b]), 0, keep) for b in range(batch)]
-    cnt2 = int(host(layer.cnt)[0])
-    assert np.array_equal(host(layer.U)[:cnt2], oracle.union(*S2))
+    if listed:
+        cnt2 = int(host(layer.cnt)[0])
+        assert np.array_equal(host(layer.U)[:cnt2], oracle.union(*S2))
+    else:
+        M2 = host(layer.M)
+        assert np.array_equal(np.flatnonzero(M2.any(axis=0)), oracle.union(*S2))
+    for b in toks:
+        assert_close(host(Y[b]), oracle.down_gather(WdT, S2[b], A2[b][S2[b]]),
+                     what=f"second batch output b={b}")
     return layer, Y
 
 
+@pytest.mark.parametrize("union_list", [False, True])
 @pytest.mark.parametrize("batch", [1, 2, 4, 8, 16, 19])
-def test_small_shapes(batch):
-    banner(f"c4 small batch={batch}")
-    run_and_check(1000, 256, batch, 40, seed=batch)
+def test_small_shapes(batch, union_list):
+    banner(f"c4 small batch={batch} union_list={union_list}")
+    run_and_check(1000, 256, batch, 40, seed=batch, union_list=union_list)
 
 
+@pytest.mark.parametrize("union_list", [False, True])
 @pytest.mark.parametrize("batch", [1, 4, 8, 16])
-def test_full_size(batch):
-    banner(f"c4 full batch={batch}")
-    run_and_check(17408, 5120, batch, 40, sample_tokens=[0, batch - 1])
+def test_full_size(batch, union_list):
+    banner(f"c4 full batch={batch} union_list={union_list}")
+    run_and_check(17408, 5120, batch, 40, sample_tokens=[0, batch - 1], union_list=union_list)
 
 
 def test_mfma_dense_prefill_shape():
