@@ -201,6 +201,18 @@ void single_thread_cases() {
   expect("packed axpy d", gemv(SFFN_OP_AXPY | SFFN_PACKED, 64, 384, 384, 4, nullptr, nullptr, 0, 1,
                                FAKE, 1 << 30, F(), W(), 0.f, 0.f, nullptr, 0, 384, 64),
          SFFN_EUNSUPPORTED, "256");
+
+  // the union formed in the product (masked rows)
+  auto masked = [](int batch, const int32_t* idx, const uint8_t* mask, int ld_mask) {
+    return sparse_ffn_gemv(SFFN_OP_AXPY | SFFN_MASKED_ROWS, W(), nullptr, 64, 256, 256, F(), batch,
+                           64, idx, idx ? I() : nullptr, idx ? 4 : 0, 1, mask, ld_mask, 0.f, 0.f,
+                           nullptr, 0, nullptr, Fo(), nullptr, 256, 0, FAKE, 1 << 30, nullptr);
+  };
+  const uint8_t* MK = static_cast<const uint8_t*>(FAKE);
+  expect("masked batch", masked(1, nullptr, MK, 64), SFFN_EUNSUPPORTED, "batch > 1");
+  expect("masked mask", masked(4, nullptr, nullptr, 0), SFFN_EINVAL, "row_mask");
+  expect("masked idx", masked(4, I(), MK, 64), SFFN_EINVAL, "idx must be NULL");
+  expect("masked ld", masked(4, nullptr, MK, 72), SFFN_EINVAL, "ld_mask");
 }
 
 // Several threads provoke different errors at once; each must read back the

@@ -297,6 +297,28 @@ def test_packed_layouts_validation(L):
     assert rc == 2 and "batch 1" in msg
 
 
+def test_masked_rows_validation(L):
+    """SFFN_MASKED_ROWS: AXPY only, batch > 1, no index list, a 16-byte
+    aligned mask with a row stride of a multiple of 16; rejected before any
+    launch."""
+    from activation_sparse_decode_amd import binding as B
+    op = B.OP_AXPY | B.MASKED_ROWS
+    kw = dict(n_rows=64, d=256, ld_w=256, batch=4, ld_in=64, ld_out=256, ws=FAKE, ws_bytes=1 << 30)
+    rc, msg = gemv(L, op=op, **{**kw, "batch": 1})
+    assert rc == 2 and "batch > 1" in msg
+    rc, msg = gemv(L, op=op, **kw)
+    assert rc == 1 and "row_mask" in msg
+    rc, msg = gemv(L, op=op, idx=FAKE, count=FAKE, k_max=4, mask=FAKE, ld_mask=64, **kw)
+    assert rc == 1 and "idx must be NULL" in msg
+    rc, msg = gemv(L, op=op, mask=FAKE, ld_mask=72, **kw)
+    assert rc == 1 and "ld_mask" in msg
+    rc, msg = gemv(L, op=op, mask=ctypes.c_void_p(0x1004), ld_mask=64, **kw)
+    assert rc == 1 and "aligned" in msg
+    rc, msg = gemv(L, op=B.OP_GLU_SILU | B.MASKED_ROWS, mask=FAKE, ld_mask=64,
+                   **{**kw, "ld_in": 256, "ld_out": 64})
+    assert rc == 1 and "AXPY only" in msg
+
+
 def gemv_lists(L, n=2, W=(FAKE, FAKE), n_rows=(64, 64), d=64, ld_w=64, inp=(FAKE, FAKE),
                idx=(FAKE, FAKE), count=(FAKE, FAKE), k_max=(2, 2), group=32, alpha=None, out=FAKE,
                ws=FAKE, ws_bytes=1 << 30, null_arrays=False):
