@@ -181,3 +181,34 @@ def test_mfma_rowop_k_slices(d, batch):
             else:
                 ref = oracle.row_dots(Wg, x)
             assert_close(A_h[b], ref, what=f"op {op} eps {eps} token {b}")
+
+
+@pytest.mark.parametrize("batch,packed", [(4, False), (16, True)])
+def test_batched_layer_graph_replays_match_eager(batch, packed):
+    """The batched layer (union formed inside the product; row-major or
+    packed weights) captured as a HIP graph gives, on every replay, the bits
+    the eager calls give, with other work and synchronisations between the
+    replays."""
+    banner(f"c4 graph replay batch={batch} packed={packed}")
+    N, d = 3000, 512
+    Wg, Wu, WdT, _ = make(N, d, 1, seed=31)
+    layer = BatchedUnionLayer(dev(Wg), dev(Wu), dev(WdT), pct_count(40, N), batch, packed=packed)
+    X = [dev(synth.tokens(31, synth.W_C4, 200 + t, batch, d)) for t in range(4)]
+    eager = []
+    for t in range(4):
+        Y = torch.zeros(batch, d, dtype=torch.float32, device="cuda")
+        layer(X[t], Y)
+        eager.append(host(Y))
+    xb = torch.zeros(batch, d, dtype=torch.float32, device="cuda")
+    Y = torch.zeros(batch, d, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(xb, Y)
+    for rep in range(3):
+        for t in range(4):
+            xb.copy_(X[t])
+            g.replay()
+            got = host(Y)          # synchronizes between replays
+            assert np.array_equal(got.view(np.uint32), eager[t].view(np.uint32)), (rep, t)
+            layer(X[(t + 1) % 4], torch.empty_like(Y))   # eager work between replays
