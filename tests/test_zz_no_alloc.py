@@ -75,6 +75,38 @@ def test_noalloc_packed_batched_two_calls():
     check(*gathered_case(7, 1000, 256, 300, 4), 4, "packed batch 4 small", packed=True)
 
 
+def masked_check(seed, N, d, batch, what):
+    """The union formed in the product (SFFN_MASKED_ROWS, packed panels)
+    through both entries: bitwise equal, and the oracle per token."""
+    WdT, A, U, M = gathered_case(seed, N, d, max(1, N // 3), batch)
+    ldm = (N + 15) // 16 * 16
+    Md = torch.zeros(batch, ldm, dtype=torch.uint8, device="cuda")
+    Md[:, :N] = dev(M)
+    W = B.pack_weights(dev(WdT), B.LAYOUT_COL_PANELS)
+    outs = []
+    for noalloc in (False, True):
+        y = torch.full((batch, d), 3.0, dtype=torch.float32, device="cuda")
+        if noalloc:
+            B.sparse_ffn_gemv_noalloc(B.OP_AXPY | B.MASKED_ROWS, W, None, dev(A), y,
+                                      row_mask=Md[:, :N], accumulate=True)
+        else:
+            B.sparse_ffn_gemv(B.OP_AXPY | B.MASKED_ROWS, W, None, dev(A), y, row_mask=Md[:, :N],
+                              accumulate=True, workspace=B.new_workspace(batch, N, d))
+        torch.cuda.synchronize()
+        outs.append(host(y))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), what
+    for b in sorted({0, batch - 1}):
+        s = np.flatnonzero(M[b])
+        assert_close(outs[1][b], 3.0 + oracle.down_gather(WdT, s.astype(np.int32), A[b, s]),
+                     what=f"{what} token {b}")
+
+
+def test_noalloc_masked_rows_two_calls():
+    banner("noalloc masked rows: batch 16 17408x5120, then batch 4 1000x256")
+    masked_check(8, 17408, 5120, 16, "masked batch 16 large")
+    masked_check(9, 1000, 256, 4, "masked batch 4 small")
+
+
 def test_noalloc_row_op_and_limit():
     banner("noalloc row op and scratch limit")
     N, d = 2000, 1024
