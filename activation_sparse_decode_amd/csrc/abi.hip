@@ -6,8 +6,10 @@
 #include <cstdarg>
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/sparse_ffn.h"
 #include "sffn_device.h"
@@ -74,6 +76,57 @@ sffn_status current_scratch(void** out) {
   *out = scratch_ptr[dev];
   return SFFN_OK;
 }
+
+// Checked mode (the environment variable SFFN_DEBUG_CHECKS set to anything
+// but "0", read at every call): before a launch, a call that takes a device
+// index list waits for its stream, reads the count and the list on the host
+// and checks the preconditions the kernels rely on.  For debugging only: it
+// synchronises and reads device memory, which the normal contract never does.
+bool debug_checks() {
+  const char* e = std::getenv("SFFN_DEBUG_CHECKS");
+  return e && e[0] && !(e[0] == '0' && e[1] == '\0');
+}
+
+// The entries idx[i], i < min(*count, k_max) (k_max without a count), must be
+// in [0, limit) and, if `distinct`, pairwise different; *count must be >= 0.
+sffn_status check_list(const char* what, int list, const int32_t* idx, const int32_t* count,
+                       int k_max, long limit, bool distinct, hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(SFFN_EHIP, "%s: debug check: %s", what, hipGetErrorString(e));
+  int n = k_max;
+  if (count) {
+    int32_t c = 0;
+    e = hipMemcpy(&c, count, sizeof(c), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(SFFN_EHIP, "%s: debug check: %s", what, hipGetErrorString(e));
+    if (c < 0) return fail(SFFN_EINVAL, "%s: list %d: device count %d < 0 (debug check)", what, list, c);
+    n = std::min(c, k_max);
+  }
+  if (n <= 0) return SFFN_OK;
+  std::vector<int32_t> h((size_t)n);
+  e = hipMemcpy(h.data(), idx, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SFFN_EHIP, "%s: debug check: %s", what, hipGetErrorString(e));
+  std::vector<uint8_t> seen(distinct ? (size_t)std::max(limit, 0L) : 0);
+  for (int i = 0; i < n; ++i) {
+    if (h[i] < 0 || h[i] >= limit)
+      return fail(SFFN_EINVAL, "%s: list %d: idx[%d] = %d outside [0, %ld) (debug check)", what,
+                  list, i, h[i], limit);
+    if (distinct) {
+      if (seen[h[i]])
+        return fail(SFFN_EINVAL, "%s: list %d: idx[%d] = %d repeats an earlier entry (debug check)",
+                    what, list, i, h[i]);
+      seen[h[i]] = 1;
+    }
+  }
+  return SFFN_OK;
+}
+
+#define DEBUG_CHECK_LIST(...)                              \
+  do {                                                     \
+    if (debug_checks()) {                                  \
+      const sffn_status st_ = check_list(__VA_ARGS__);     \
+      if (st_ != SFFN_OK) return st_;                      \
+    }                                                      \
+  } while (0)
 
 }  // namespace
 
@@ -280,6 +333,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
     if (items == 0) return ok();
     if (batch > 1 && workspace)
       REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
+    if (idx) DEBUG_CHECK_LIST("gemv", 0, idx, count, k_max, (long)n_rows / group, true, s);
     sffn::RowOpArgs a{op, W0, W1, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max,
                       (idx || op == SFFN_OP_DOT_RELU_CLUSTER) ? group : 1, tau_scale, rms_eps,
                       aux, ld_aux, out, key_out,
@@ -300,6 +354,7 @@ sffn_status sparse_ffn_gemv(int op, const uint16_t* W0, const uint16_t* W1, int 
   REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
           "gemv: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv: workspace must be 256-byte aligned");
+  if (idx) DEBUG_CHECK_LIST("gemv", 0, idx, count, k_max, (long)n_rows / group, true, s);
   sffn::AxpyArgs a{W0, n_rows, d, ld_w, in, batch, ld_in, idx, count, k_max, idx ? group : 1,
                    row_mask, ld_mask, alpha, out, ld_out, accumulate ? 1 : 0, workspace, ws_bytes,
                    packed, mask_rows};
@@ -336,6 +391,8 @@ sffn_status sparse_ffn_fused_swiglu(const uint16_t* Wg, const uint16_t* Wu, cons
   REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
           "fused_swiglu: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
   REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "fused_swiglu: workspace must be 256-byte aligned");
+  if (idx)
+    DEBUG_CHECK_LIST("fused_swiglu", 0, idx, count, k_max, n_rows, true, (hipStream_t)stream);
   sffn::FusedArgs a{Wg, Wu, Wd, ld_w, n_rows, d, x, rms_eps, idx, count, k_max, a_out, y,
                     accumulate ? 1 : 0, workspace, ws_bytes};
   return from_hip(sffn::launch_fused_swiglu(a, (hipStream_t)stream), "fused_swiglu launch");
@@ -459,6 +516,10 @@ sffn_status sparse_ffn_rowop_lists(int op, int n_lists, const uint16_t* const* W
   if (!use0)
     for (int l = 0; l < n_lists; ++l) L.W0[l] = W1[l];   // GATED reads W1 only
   if (items == 0) return ok();
+  if (idx)
+    for (int l = 0; l < n_lists; ++l)
+      DEBUG_CHECK_LIST("rowop_lists", l, idx[l], count[l], k_max[l], (long)n_rows / group, true,
+                       (hipStream_t)stream);
   return from_hip(sffn::launch_rowop_lists(L, (hipStream_t)stream), "rowop_lists launch");
 }
 
@@ -506,6 +567,9 @@ sffn_status sparse_ffn_gemv_lists(int n_lists, const uint16_t* const* W, const i
   a.accumulate = accumulate ? 1 : 0;
   a.ws = workspace;
   a.ws_bytes = ws_bytes;
+  for (int l = 0; l < n_lists; ++l)
+    DEBUG_CHECK_LIST("gemv_lists", l, idx[l], count[l], k_max[l], (long)n_rows[l] / group, true,
+                     (hipStream_t)stream);
   return from_hip(sffn::launch_axpy_lists(a, (hipStream_t)stream), "gemv_lists launch");
 }
 
@@ -536,6 +600,7 @@ sffn_status sparse_ffn_compact(const uint16_t* W, int n_rows, int d, int ld_w,
   REQUIRE(aligned(W, 16) && aligned(out, 16), SFFN_EINVAL, "compact: W/out must be 16-byte aligned");
   if (idx) REQUIRE(aligned(idx, 4), SFFN_EINVAL, "compact: idx misaligned");
   if (transpose && ld_out == 0) return ok();
+  if (k > 0) DEBUG_CHECK_LIST("compact", 0, idx, nullptr, k, n_rows, false, (hipStream_t)stream);
   return from_hip(sffn::launch_compact(W, ld_w, d, idx, k, transpose ? 1 : 0, out, ld_out,
                                        (hipStream_t)stream),
                   "compact launch");
@@ -609,6 +674,10 @@ sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w, const uint8_t* 
   a.idx_top = idx_top; a.cnt_top = cnt_top; a.k_top_max = k_top_max;
   a.idx_mid = idx_mid; a.cnt_mid = cnt_mid; a.k_mid_max = k_mid_max;
   a.y = y; a.accumulate = accumulate ? 1 : 0; a.ws = workspace; a.ws_bytes = ws_bytes;
+  if (k_top_max > 0)
+    DEBUG_CHECK_LIST("tiered (top)", 0, idx_top, cnt_top, k_top_max, n_in, true, (hipStream_t)stream);
+  if (k_mid_max > 0)
+    DEBUG_CHECK_LIST("tiered (mid)", 1, idx_mid, cnt_mid, k_mid_max, n_in, true, (hipStream_t)stream);
   return from_hip(sffn::launch_tiered(a, (hipStream_t)stream), "tiered launch");
 }
 

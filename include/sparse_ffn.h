@@ -38,6 +38,14 @@
  *  - Device-side preconditions that cannot be checked on the host:
  *    0 <= idx[i] < n_rows / group, indices in a list are distinct, and
  *    counts are >= 0; kernels process min(*count, k_max) entries.
+ *    Checked mode, for debugging: with the environment variable
+ *    SFFN_DEBUG_CHECKS set to anything but "0" (read at every call), a call
+ *    that takes device index lists (gemv, gemv_noalloc, gemv_lists,
+ *    rowop_lists, fused_swiglu, tiered_gemv, compact) waits for its stream,
+ *    reads the counts and lists on the host and checks these preconditions
+ *    before launching; a violation returns SFFN_EINVAL naming the entry and
+ *    launches nothing.  That mode synchronises and reads device memory, so
+ *    it is not for use under graph capture or in timed runs.
  *  - Calls that take a workspace use it as scratch for split-K partials and
  *    packed operands; it needs no initialisation.  One workspace must not be
  *    used by two calls that may run at the same time.
