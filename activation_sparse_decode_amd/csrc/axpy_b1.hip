@@ -182,10 +182,13 @@ hipError_t launch_splitk_reduce(const float* partials, int KS, int M, int Mp, in
 int pick_split_b1(long items, int col_tiles) {
   // about four rows per wave (the loads a lane keeps in flight), within
   // 256..512 workgroups: every CU streams, and a device-side count far
-  // below the launch bound `items` still leaves a few rows per wave
+  // below the launch bound `items` still leaves a few rows per wave.  The
+  // upper bound rounds down: two 1024-thread workgroups fit a CU, so 512 is
+  // one round, and a few workgroups past it would start only when the first
+  // ones end (at 10 column tiles, 520 workgroups took 8% longer than 510)
   long ks = (items + 4 * kWaves - 1) / (4 * kWaves);
   const long min_ks = (256 + col_tiles - 1) / col_tiles;
-  const long max_ks = (512 + col_tiles - 1) / col_tiles;
+  const long max_ks = std::max(1, 512 / col_tiles);
   if (ks < min_ks) ks = min_ks;
   if (ks > max_ks) ks = max_ks;
   const long max_by_rows = (items + kWaves - 1) / kWaves;
