@@ -90,7 +90,12 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_packed_elems.argtypes = [_i, _i, _i]
         L.sparse_ffn_pack_weights.restype = _i
         L.sparse_ffn_pack_weights.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
-        if L.sffn_abi_version() != 15:
+        L.sparse_ffn_select_threshold.restype = _i
+        L.sparse_ffn_select_threshold.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
+        L.sparse_ffn_gemv_keyed.restype = _i
+        L.sparse_ffn_gemv_keyed.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _i,
+                                            _vp, _sz, _vp]
+        if L.sffn_abi_version() != 16:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -180,6 +185,28 @@ def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *
         _ld(idx_out, idx_out.shape[-1] if idx_out is not None else 0), _p(count_out),
         _p(idx_top_out), _ld(idx_top_out, idx_top_out.shape[-1] if idx_top_out is not None else 0),
         _p(count_top_out), _p(freq), int(clear_keys), _stream(stream)))
+
+
+def sparse_ffn_select_threshold(keys: torch.Tensor, key_type: int, k: int, thr_out: torch.Tensor,
+                                stream=None) -> None:
+    """Per row of keys ([n] or [rows][n]): the top-k range [0, k) as a
+    threshold pair (T, I) in thr_out (int32/uint32 [rows][2] or [2])."""
+    rows, n = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
+    _check(lib().sparse_ffn_select_threshold(_p(keys), key_type, rows, n, _ld(keys, n), k,
+                                             _p(thr_out), _stream(stream)))
+
+
+def sparse_ffn_gemv_keyed(W: torch.Tensor, inp: torch.Tensor, keys: torch.Tensor, key_type: int,
+                          thr: torch.Tensor, k_max: int, out: torch.Tensor, *,
+                          alpha: torch.Tensor | None = None, accumulate: bool = False,
+                          workspace: torch.Tensor | None = None, stream=None) -> None:
+    """out (+)= alpha * sum of inp[n] * W[n] over the rows the threshold thr
+    selects among keys (batch 1)."""
+    n_rows, d = W.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sparse_ffn_gemv_keyed(_p(W), n_rows, d, _ld(W, d), _p(inp), _p(keys), key_type,
+                                       _p(thr), k_max, _p(alpha), _p(out), int(accumulate),
+                                       _p(workspace), ws_bytes, _stream(stream)))
 
 
 def sparse_ffn_gemv(op: int, W0: torch.Tensor | None, W1: torch.Tensor | None,

@@ -12,7 +12,7 @@
 #include <vector>
 
 #include "../../include/sparse_ffn.h"
-#include "sffn_device.h"
+#include "sffn_splitk.h"
 
 namespace {
 
@@ -235,6 +235,25 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
                      idx_top_out,
                      ld_idx_top, count_top_out, freq_inout, clear_keys ? 1 : 0};
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select launch");
+}
+
+sffn_status sparse_ffn_select_threshold(const void* keys, int key_type, int rows, int n, int ld,
+                                        int k, uint32_t* thr_out, void* stream) {
+  REQUIRE(keys != nullptr, SFFN_EINVAL, "select_threshold: keys must be non-null");
+  REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "select_threshold: unknown key type %d",
+          key_type);
+  REQUIRE(rows >= 0, SFFN_EINVAL, "select_threshold: rows=%d must be >= 0", rows);
+  REQUIRE(n >= 1 && n <= 32768, SFFN_EUNSUPPORTED, "select_threshold: n=%d outside [1, 32768]", n);
+  REQUIRE(ld >= n, SFFN_EINVAL, "select_threshold: ld=%d < n=%d", ld, n);
+  REQUIRE(k >= 0, SFFN_EINVAL, "select_threshold: k=%d must be >= 0", k);
+  REQUIRE(aligned(keys, 4), SFFN_EINVAL, "select_threshold: keys must be 4-byte aligned");
+  REQUIRE(thr_out != nullptr && aligned(thr_out, 8), SFFN_EINVAL,
+          "select_threshold: thr_out must be non-null and 8-byte aligned");
+  if (rows == 0) return ok();
+  sffn::SelectArgs a{keys, key_type, nullptr, rows, n, ld, 1, 0, k, 0,
+                     nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr,
+                     nullptr, 0, nullptr, nullptr, 0, thr_out};
+  return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select_threshold launch");
 }
 
 // sigmoid(z) > theta  <=>  z > ln(theta / (1 - theta)); with t the largest
@@ -679,6 +698,41 @@ sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w, const uint8_t* 
   if (k_mid_max > 0)
     DEBUG_CHECK_LIST("tiered (mid)", 1, idx_mid, cnt_mid, k_mid_max, n_in, true, (hipStream_t)stream);
   return from_hip(sffn::launch_tiered(a, (hipStream_t)stream), "tiered launch");
+}
+
+sffn_status sparse_ffn_gemv_keyed(const uint16_t* W, int n_rows, int d, int ld_w, const float* in,
+                                  const void* keys, int key_type, const uint32_t* thr, int k_max,
+                                  const float* alpha, float* out, int accumulate, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  REQUIRE(W != nullptr && aligned(W, 16), SFFN_EINVAL,
+          "gemv_keyed: W must be non-null and 16-byte aligned");
+  REQUIRE(in != nullptr && aligned(in, 16), SFFN_EINVAL,
+          "gemv_keyed: in must be non-null and 16-byte aligned");
+  REQUIRE(out != nullptr && aligned(out, 16), SFFN_EINVAL,
+          "gemv_keyed: out must be non-null and 16-byte aligned");
+  REQUIRE(keys != nullptr && aligned(keys, 4), SFFN_EINVAL,
+          "gemv_keyed: keys must be non-null and 4-byte aligned");
+  REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "gemv_keyed: unknown key type %d", key_type);
+  REQUIRE(thr != nullptr && aligned(thr, 8), SFFN_EINVAL,
+          "gemv_keyed: thr must be non-null and 8-byte aligned");
+  REQUIRE(n_rows >= 1, SFFN_EINVAL, "gemv_keyed: n_rows=%d must be >= 1", n_rows);
+  REQUIRE(d >= 8 && d % 8 == 0, SFFN_EINVAL, "gemv_keyed: d=%d must be a multiple of 8, >= 8", d);
+  REQUIRE(ld_w >= d && ld_w % 8 == 0, SFFN_EINVAL, "gemv_keyed: ld_w=%d must be >= d, %% 8 == 0",
+          ld_w);
+  REQUIRE(k_max >= 0 && k_max <= n_rows, SFFN_EINVAL, "gemv_keyed: k_max=%d outside [0, n_rows=%d]",
+          k_max, n_rows);
+  if (alpha) REQUIRE(aligned(alpha, 4), SFFN_EINVAL, "gemv_keyed: alpha misaligned");
+  const int col_tiles = (d + sffn::kTileCols - 1) / sffn::kTileCols;
+  REQUIRE(sffn::keyed_split(n_rows, k_max, col_tiles) <= sffn::kMaxSplit, SFFN_EUNSUPPORTED,
+          "gemv_keyed: n_rows=%d needs more row chunks than the reduction takes", n_rows);
+  const size_t need = sffn::workspace_bytes(1, k_max, d);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
+          "gemv_keyed: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "gemv_keyed: workspace must be 256-byte aligned");
+  sffn::AxpyArgs a{W, n_rows, d, ld_w, in, 1, n_rows, nullptr, nullptr, k_max, 1,
+                   nullptr, 0, alpha, out, d, accumulate ? 1 : 0, workspace, ws_bytes, 0, 0};
+  return from_hip(sffn::launch_axpy_keyed(a, keys, key_type, thr, (hipStream_t)stream),
+                  "gemv_keyed launch");
 }
 
 sffn_status sparse_ffn_gemv_noalloc(int op, const uint16_t* W0, const uint16_t* W1, int n_rows,

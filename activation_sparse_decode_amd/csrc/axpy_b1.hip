@@ -19,6 +19,11 @@
 
 namespace sffn {
 
+__device__ __forceinline__ uint32_t lanes_below_u64(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Adds this wave's rows of the chunk [k0, k1) of a row list to acc: wave w
 // takes items k0 + w + kWaves * u.  Their rows, activations and masks are
 // fetched with one vector load per lane (lane l: item u = ub + l), then
@@ -236,6 +241,102 @@ hipError_t launch_axpy_lists(const AxpyListsArgs& a, hipStream_t s) {
   }
   // no rows at all: zero chunks, the reduction writes out (+)= 0
   return launch_splitk_reduce(partials, ks, 1, 1, a.d, nullptr, a.out, a.d, a.accumulate, s);
+}
+
+
+// ---------------------------------------------------------------- keyed rows
+// The product over the rows a threshold selects, with no index list: chunk ks
+// of the grid covers the neurons [ks c, min(n, (ks + 1) c)), c <= 1024, and
+// wave w of the workgroup the w-th sixteenth of it (at most 64 neurons, one
+// per lane).  Each lane tests its neuron's key against (T, I); the selected
+// neurons of the wave, in index order, are sent to lanes 0, 1, ...
+// (ds_permute to the lane's rank in the ballot), so lane q holds the wave's
+// q-th row; the rows then stream as in the listed product, and the partials
+// go to the same ordered reduction.
+__device__ __forceinline__ uint32_t keyed_key(const void* keys, int key_type, int n) {
+  const uint32_t b = reinterpret_cast<const uint32_t*>(keys)[n];
+  if (key_type == 0) return b & 0x7FFFFFFFu;
+  if (key_type == 1) return b;
+  return key_signed(__uint_as_float(b));
+}
+
+__global__ __launch_bounds__(1024) void axpy_keyed_kernel(AxpyArgs a, const void* keys, int key_type,
+                                                          const uint32_t* thr, int KS,
+                                                          float* partials) {
+  __shared__ float4 red[kWaves][kTileCols / 4];
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int tile = blockIdx.x, ks = blockIdx.y;
+  const int col = tile * kTileCols + 8 * lane;
+  const int colc = col < a.d ? col : 0;   // lanes past the last column re-read column 0 (discarded)
+  const int N = a.n_rows;
+  const int chunk = (N + KS - 1) / KS;
+  const int sub = (chunk + kWaves - 1) / kWaves;   // <= 64
+  const int n0 = ks * chunk, n1 = min(N, n0 + chunk);
+  const int s0 = n0 + w * sub, s1 = min(n1, s0 + sub);
+  const uint32_t T = thr[0];
+  const int I = (int)thr[1];
+
+  const int nn = s0 + lane;
+  const uint32_t kv = keyed_key(keys, key_type, min(nn, N - 1));   // clamped: no branch around a load
+  const bool in = nn < s1 && (kv > T || (kv == T && nn <= I));
+  const uint64_t m = __ballot(in);
+  const int nb = (int)__popcll(m);
+  // lane q receives the q-th selected neuron; the others send to lane 63,
+  // which is a row slot only when all 64 are selected (then nobody else sends)
+  const int got = __builtin_amdgcn_ds_permute((in ? (int)lanes_below_u64(m) : 63) << 2, nn);
+  const int r = lane < nb ? got : min(s0, N - 1);   // a valid row for every lane
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (nb > 0) {
+    const float av = lane < nb ? a.in[r] : 0.f;
+    auto batch = [&](int u, auto width) {
+      constexpr int U = decltype(width)::value;
+      uint4 wv[U];
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const int rr = __builtin_amdgcn_readlane(r, u + uu < nb ? u + uu : 0);
+        wv[uu] = load_stream16(a.W + (size_t)rr * a.ld_w + colc);
+      }
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const float au = u + uu < nb
+            ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av), u + uu)) : 0.f;
+        float f[8];
+        unpack8(wv[uu], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(au, f[e], acc[e]);
+      }
+    };
+    // eight rows in flight per lane while more than four remain, then four
+    int u = 0;
+    for (; nb - u > 4; u += 8) batch(u, std::integral_constant<int, 8>());
+    if (u < nb) batch(u, std::integral_constant<int, 4>());
+  }
+
+  const float part = wg_reduce_cols(red, acc);
+  const int c = tile * kTileCols + (int)threadIdx.x;
+  if (threadIdx.x < kTileCols && c < a.d) partials[(size_t)ks * a.d + c] = part;
+}
+
+// Chunk count: the listed product's split for k_max rows, raised until a
+// chunk fits 16 waves x 64 neurons.
+int keyed_split(int n_rows, long k_max, int col_tiles) {
+  const int KS = pick_split_b1(k_max, col_tiles);
+  const int need = (n_rows + kWaves * 64 - 1) / (kWaves * 64);
+  return std::max(KS, need);
+}
+
+hipError_t launch_axpy_keyed(const AxpyArgs& a, const void* keys, int key_type, const uint32_t* thr,
+                             hipStream_t s) {
+  const int col_tiles = (a.d + kTileCols - 1) / kTileCols;
+  const int KS = keyed_split(a.n_rows, a.k_max, col_tiles);
+  if (KS > kMaxSplit) return hipErrorInvalidValue;
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
+  hipLaunchKernelGGL(axpy_keyed_kernel, dim3(col_tiles, KS), dim3(1024), 0, s, a, keys, key_type,
+                     thr, KS, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(partials, KS, 1, 1, a.d, a.alpha, a.out, a.d, a.accumulate, s);
 }
 
 }  // namespace sffn

@@ -349,6 +349,41 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
   }
 
+  if (a.thr_out) {
+    // Threshold mode (the range [0, r_hi), every entry eligible, no lists):
+    // T and the index I of the last entry equal to T inside; entry j is in
+    // iff key_j > T, or key_j == T and j <= I.  Without a split tie every
+    // entry whose key reaches the decided prefix is in (I = INT_MAX).
+    uint32_t* thr = a.thr_out + 2 * (size_t)row;
+    const bool split = need_hi && tie_hi > rem_hi;
+    if (!split) {
+      if (t == 0) {
+        thr[0] = rhi > 0 ? (all_hi ? 0u : pre_hi) : 0xFFFFFFFFu;
+        thr[1] = rhi > 0 ? 0x7FFFFFFFu : 0xFFFFFFFFu;
+      }
+      return;
+    }
+    // the entries equal to T in index order: the rem_hi-th is the last inside
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) eq |= (key[j] == pre_hi ? 1u : 0u) << j;
+    eq &= elig;
+    const uint32_t wc = wave_incl<false>((uint32_t)__popc(eq));
+    if (lane == 63) WT[1][w] = wc;
+    __syncthreads();
+    uint32_t dummy;
+    uint32_t eq_run = waves_before<NW>(WT[1], dummy);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t b = __ballot((eq >> j) & 1u);
+      const uint32_t pos = eq_run + lanes_below(b);
+      eq_run += (uint32_t)__popcll(b);
+      if (((eq >> j) & 1u) && pos + 1u == rem_hi) thr[1] = (uint32_t)(ebase + 64 * j);
+    }
+    if (t == 0) thr[0] = pre_hi;
+    return;
+  }
+
   // ---- membership of the two rank ranges (before eligibility): bit j of
   // hib / lob: the entry of slot j is among the top r_hi / top r_lo.  When a
   // bound splits the entries equal to T_r, those are ranked in index order.

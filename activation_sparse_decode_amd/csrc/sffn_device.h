@@ -133,6 +133,12 @@ struct AxpyArgs {
 };
 hipError_t launch_axpy_b1(const AxpyArgs& a, hipStream_t s);
 hipError_t launch_axpy_mfma(const AxpyArgs& a, hipStream_t s);
+// The batch-1 gathered product over the rows a threshold (T, I) selects:
+// row n is read iff key_n > T, or key_n == T and n <= I (key_n = keys[n]
+// read as key_type); AxpyArgs.idx / count are unused, k_max bounds the
+// selected count (launch shape only).
+hipError_t launch_axpy_keyed(const AxpyArgs& a, const void* keys, int key_type,
+                             const uint32_t* thr, hipStream_t s);
 
 // Gathered products over several row lists into one output at batch 1.
 constexpr int kMaxLists = 8;
@@ -160,6 +166,7 @@ struct SelectArgs {
   int32_t* count_top_out;
   uint32_t* freq;
   int clear_keys;
+  uint32_t* thr_out;   // threshold mode (one bound from rank 0, no lists): (T, I) per row
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
@@ -217,6 +224,7 @@ hipError_t launch_gather32(const uint32_t* src, int n_src, const int32_t* idx,
 
 size_t workspace_bytes(int batch, int n_rows, int d_out);
 int pick_split_b1(long items, int col_tiles);
+int keyed_split(int n_rows, long k_max, int col_tiles);
 int max_split_mfma(int mtiles);
 
 }  // namespace sffn

@@ -55,32 +55,61 @@ def _reuse(layer, other, names) -> bool:
     return True
 
 
+def threshold_members(keys_u32: np.ndarray, thr) -> np.ndarray:
+    """Ascending indices n with key_n > T, or key_n == T and n <= I: the set a
+    threshold pair (T, I) of sparse_ffn_select_threshold stands for (host
+    side, for tests and reports; the keys as uint32)."""
+    keys = np.asarray(keys_u32).view(np.uint32).ravel()
+    T = np.uint32(int(thr[0]) & 0xFFFFFFFF)
+    I = int(np.int64(thr[1]).astype(np.int32))
+    n = np.arange(keys.size)
+    return np.flatnonzero((keys > T) | ((keys == T) & (n <= I)))
+
+
 class SwigluSparseLayer:
     """x -> a = silu(W_g x) * (W_u x) (+ keys) -> top-``keep`` by |a| ->
     y = sum over the kept neurons of a_n W_down^T[n].
 
+    keyed (default): the selection is a threshold pair (``thr``) and the
+    product forms its rows from the keys (sparse_ffn_select_threshold +
+    sparse_ffn_gemv_keyed); otherwise an ascending index list and count
+    (``idx``, ``count``) feed the listed product.  The selected set is the
+    same either way.
+
     ``buffers_from``: another layer of the same shape whose intermediate
-    buffers (activations, keys, index list, count, workspace) this one reuses,
+    buffers (activations, keys, selection, workspace) this one reuses,
     as the layers of a model decoded on one stream do."""
 
-    def __init__(self, Wg, Wu, WdT, keep: int, buffers_from=None):
-        self.Wg, self.Wu, self.WdT, self.keep = Wg, Wu, WdT, keep
+    def __init__(self, Wg, Wu, WdT, keep: int, buffers_from=None, keyed: bool = True):
+        self.Wg, self.Wu, self.WdT, self.keep, self.keyed = Wg, Wu, WdT, keep, keyed
         N, d = Wg.shape
         dev = Wg.device
-        if _reuse(self, buffers_from, ("a", "key", "idx", "count", "ws")):
+        if _reuse(self, buffers_from, ("a", "key", "idx", "count", "thr", "ws")):
             return
         self.a = torch.zeros(N, dtype=F32, device=dev)
         self.key = torch.zeros(N, dtype=I32, device=dev)
         self.idx = torch.zeros(max(keep, 1), dtype=I32, device=dev)
         self.count = torch.zeros(1, dtype=I32, device=dev)
+        self.thr = torch.zeros(2, dtype=I32, device=dev)
         self.ws = B.new_workspace(1, keep, WdT.shape[1], device=dev)
 
     def __call__(self, x: torch.Tensor, y: torch.Tensor, accumulate: bool = False) -> None:
         B.sparse_ffn_gemv(B.OP_GLU_SILU, self.Wg, self.Wu, x, self.a, key_out=self.key)
+        if self.keyed:
+            B.sparse_ffn_select_threshold(self.key, B.KEY_U32, self.keep, self.thr)
+            B.sparse_ffn_gemv_keyed(self.WdT, self.a, self.key, B.KEY_U32, self.thr, self.keep, y,
+                                    accumulate=accumulate, workspace=self.ws)
+            return
         B.sparse_ffn_select(self.key, B.KEY_U32, 0, self.keep, idx_out=self.idx,
                             count_out=self.count)
         B.sparse_ffn_gemv(B.OP_AXPY, self.WdT, None, self.a, y, idx=self.idx, count=self.count,
                           k_max=self.keep, accumulate=accumulate, workspace=self.ws)
+
+    def selected(self) -> np.ndarray:
+        """The last call's selected neurons, ascending (host)."""
+        if self.keyed:
+            return threshold_members(self.key.cpu().numpy(), self.thr.cpu().numpy())
+        return self.idx.cpu().numpy()[:int(self.count.cpu()[0])]
 
 
 class SelectInferStack:
@@ -606,15 +635,19 @@ class PredictedMoEStack(ReluMoEStack):
 class BatchedUnionLayer:
     """A batch of tokens: per-token top-``keep`` by |a|, the union of the
     selections gathered once, each token's skipped neurons masked to zero
-    (one token: its own selection is the union, listed by one select; more:
-    the product reads the rows some token's mask selects).
+    (one token: its own selection is the union, passed as a threshold to the
+    keyed product, or with keyed=False listed by one select; more: the
+    product reads the rows some token's mask selects).
     ``buffers_from``: a layer of the same shape and batch whose intermediate
     buffers this one reuses (layers run one after another; the frequency
     counts are left at zero by every call)."""
 
     def __init__(self, Wg, Wu, WdT, keep: int, batch: int, buffers_from=None,
-                 packed: bool = False, union_list: bool = False):
+                 packed: bool = False, union_list: bool = False, keyed: bool = True):
         self.Wg, self.Wu, self.WdT, self.keep, self.batch = Wg, Wu, WdT, keep, batch
+        # batch 1: the token's selection as a threshold read by the keyed
+        # product (keyed), or as its listed index set
+        self.keyed = keyed and batch == 1
         # batch > 1: the product forms the union from the tokens' masks
         # (SFFN_MASKED_ROWS), or with union_list the frequency counts and a
         # union select list it first
@@ -629,7 +662,7 @@ class BatchedUnionLayer:
             self.Pg = B.pack_weights(Wg, B.LAYOUT_ROW_TILES)
             self.Pu = B.pack_weights(Wu, B.LAYOUT_ROW_TILES)
             self.Pd = B.pack_weights(WdT, B.LAYOUT_COL_PANELS)
-        if _reuse(self, buffers_from, ("A", "K", "M", "F", "U", "cnt", "ws")):
+        if _reuse(self, buffers_from, ("A", "K", "M", "F", "U", "cnt", "thr", "ws")):
             return
         self.A = torch.zeros(batch, N, dtype=F32, device=dev)
         self.K = torch.zeros(batch, N, dtype=I32, device=dev)
@@ -639,6 +672,7 @@ class BatchedUnionLayer:
         self.F = torch.zeros(N, dtype=I32, device=dev)
         self.U = torch.zeros(N, dtype=I32, device=dev)
         self.cnt = torch.zeros(1, dtype=I32, device=dev)
+        self.thr = torch.zeros(2, dtype=I32, device=dev)
         self.ws = B.new_workspace(batch, N, d, device=dev)
 
     def __call__(self, X: torch.Tensor, Y: torch.Tensor) -> None:
@@ -646,6 +680,13 @@ class BatchedUnionLayer:
         Wg, Wu, WdT = (self.Pg, self.Pu, self.Pd) if self.packed else (self.Wg, self.Wu, self.WdT)
         # the workspace lets the batched gate/up split its last tiles along K
         B.sparse_ffn_gemv(B.OP_GLU_SILU, Wg, Wu, X, self.A, key_out=self.K, workspace=self.ws)
+        if self.keyed:
+            # one token: the union is the token's own set; the product reads
+            # the rows the token's threshold selects, with no list
+            B.sparse_ffn_select_threshold(self.K, B.KEY_U32, self.keep, self.thr)
+            B.sparse_ffn_gemv_keyed(WdT, self.A, self.K, B.KEY_U32, self.thr, self.keep, Y,
+                                    workspace=self.ws)
+            return
         if self.batch == 1:
             # one token: the union is the token's own set, so its ascending
             # list comes straight from the token's select (the frequency

@@ -220,6 +220,13 @@ def cpu_baseline(fn, seconds, sample, per_unit=1, scale=1e6, unit="us/token"):
 
 # ============================================================ c1: SelectInfer stack
 
+def keyed_down_bytes(n: int, k: int, d: int) -> int:
+    """Algorithmic bytes of one keyed batch-1 product: the k selected rows
+    (d bf16 each), every neuron's 4-byte key, the k selected activations, the
+    threshold pair and the d fp32 outputs written."""
+    return k * d * 2 + 4 * n + 4 * k + 8 + 4 * d
+
+
 def glu_bytes(u: int, d: int) -> int:
     """One gate/up launch over u compacted neurons: 2 bf16 rows of d per
     neuron, the input h read, the fp32 activations written."""
@@ -509,21 +516,21 @@ def run_c0(args, torch, B, synth, P, T):
             B.sparse_ffn_gemv(B.OP_GLU_SILU, lay[c].Wg, lay[c].Wu, xbuf[c], lay[c].a,
                               key_out=lay[c].key)
 
+    # the layer's calls: the selection as a threshold, the keyed product
     def sel_only():
         for c in range(copies):
-            B.sparse_ffn_select(lay[c].key, B.KEY_U32, 0, keep, idx_out=lay[c].idx,
-                                count_out=lay[c].count)
+            B.sparse_ffn_select_threshold(lay[c].key, B.KEY_U32, keep, lay[c].thr)
 
     def down_only():
         for c in range(copies):
-            B.sparse_ffn_gemv(B.OP_AXPY, lay[c].WdT, None, lay[c].a, y[c], idx=lay[c].idx,
-                              count=lay[c].count, k_max=keep, workspace=lay[c].ws)
+            B.sparse_ffn_gemv_keyed(lay[c].WdT, lay[c].a, lay[c].key, B.KEY_U32, lay[c].thr, keep,
+                                    y[c], workspace=lay[c].ws)
 
     per = lambda body: T.replay_ms(T.capture(body), args.steps) * 1e3 / (args.steps * copies)  # noqa: E731
     glu_us, sel_us, down_us = per(glu_only), per(sel_only), per(down_only)
     glu_b = 2 * N * d * 2 + 4 * d + 8 * N
-    sel_b = 4 * N + 4 * keep
-    down_b = keep * d * 2 + 8 * keep + 4 * d
+    sel_b = 4 * N + 8
+    down_b = keyed_down_bytes(N, keep, d)
     step_b = glu_b + sel_b + down_b
     log(f"c0: {us_tok:.2f} us/token; gate/up {glu_us:.2f} us, select {sel_us:.2f} us, "
         f"gathered down {down_us:.2f} us")
@@ -540,8 +547,9 @@ def run_c0(args, torch, B, synth, P, T):
                   step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),
                   kernels_us={"gate_up_dense": round(glu_us, 3), "select": round(sel_us, 3),
                               "gathered_down": round(down_us, 3)},
-                  roofline=roofline("axpy_b1_kernel + splitk_reduce_kernel (gathered down over "
-                                    "the kept 50%, one call)", down_b, down_us,
+                  roofline=roofline("axpy_keyed_kernel + splitk_reduce_kernel (gathered down "
+                                    "over the kept 50%, rows formed from the keys, one call)",
+                                    down_b, down_us,
                                     measured_traffic("axpy_b1_swiglu_top50_layer", AXPY_B1_SOURCES)),
                   dense_gate_up=roofline("rowop_wave_kernel<GLU> (dense gate/up, keys)", glu_b,
                                          glu_us,
@@ -876,7 +884,11 @@ def run_c4(args, torch, B, synth, P, T):
     us_batch = total_ms * 1e3 / (args.steps * copies)
     dist = T.step_stats(gs, args.steps, before=lambda i: xb.copy_(X[i * copies:(i + 1) * copies]),
                         per_step=copies * batch)
-    u = float(np.mean([int((l.M != 0).any(dim=0).sum()) for l in lays]))   # union sizes
+    if lays[0].keyed:   # batch 1: the token's set, from its threshold pair
+        u = float(np.mean([P.threshold_members(l.K.cpu().numpy(), l.thr.cpu().numpy()).size
+                           for l in lays]))
+    else:               # union sizes from the token masks
+        u = float(np.mean([int((l.M != 0).any(dim=0).sum()) for l in lays]))
     masked = batch > 1 and not lays[0].union_list
 
     def weights(l):
@@ -895,7 +907,11 @@ def run_c4(args, torch, B, synth, P, T):
                 B.sparse_ffn_gemv(B.OP_AXPY | B.MASKED_ROWS, weights(l)[2], None, l.A, Y[c],
                                   row_mask=l.M, workspace=l.ws)
                 continue
-            # at batch 1 the list is the token's own set: no mask (as the layer)
+            if l.keyed:  # batch 1: the rows the token's threshold selects (as the layer)
+                B.sparse_ffn_gemv_keyed(weights(l)[2], l.A, l.K, B.KEY_U32, l.thr, keep, Y[c],
+                                        workspace=l.ws)
+                continue
+            # the listed union (union_list)
             B.sparse_ffn_gemv(B.OP_AXPY, weights(l)[2], None, l.A, Y[c], idx=l.U, count=l.cnt,
                               k_max=N, row_mask=l.M if batch > 1 else None, workspace=l.ws)
 
@@ -904,11 +920,14 @@ def run_c4(args, torch, B, synth, P, T):
     glu_b = 2 * N * d * 2 + batch * (4 * d + 8 * N)
     if masked:   # union rows, every token's mask (the union is formed from them), activations
         down_b = int(u * d * 2 + batch * (N + 4 * u + 4 * d))
+    elif lays[0].keyed:   # the token's rows, every key, its activations, the threshold, outputs
+        down_b = keyed_down_bytes(N, int(round(u)), d)
     else:        # union rows and their indices, per token activations (+ masks), outputs
         down_b = int(u * d * 2 + 4 * u + batch * ((5 if batch > 1 else 4) * u + 4 * d))
     step_b = int(glu_b + down_b + batch * 5 * N)
     # at batch 1 the same calls run the wave-per-row kernel and the split-K gathered product
-    k_glu, k_down = ("gate_up_mfma", "union_down_mfma") if batch > 1 else ("gate_up_rows", "union_down_splitk")
+    k_glu, k_down = (("gate_up_mfma", "union_down_mfma") if batch > 1
+                     else ("gate_up_rows", "union_down_keyed"))
     log(f"c4 batch {batch}: {us_batch:.2f} us/batch, union {u:.0f}; {k_glu} {glu_us:.2f} us, "
         f"{k_down} {down_us:.2f} us")
 
@@ -926,15 +945,18 @@ def run_c4(args, torch, B, synth, P, T):
               "weight_layout": ("packed: gate/up in 16-row x 128 tiles, down in 256-column panels"
                                 if lays[0].packed else "row-major"),
               "union": ("formed in the product from the token masks" if masked
-                        else "the token's own list" if batch == 1
+                        else "the token's own set, a threshold read by the keyed product"
+                        if lays[0].keyed
                         else "listed by frequency counts and a union select")}
     return result(us_batch / batch, "us/token", args.steps * copies, 2, total_ms / args.steps,
                   config, us_per_batch=round(us_batch, 3), step_bytes=step_b,
                   step_GBps=round(step_b / (us_batch * 1e-6) / 1e9, 1),
                   kernels_us={k_glu: round(glu_us, 3), k_down: round(down_us, 3)},
-                  roofline=roofline(("axpy_mfma_kernel" if batch > 1 else "axpy_b1_kernel")
-                                    + " + splitk_reduce_kernel (the union's down rows read once, "
-                                    "per-token masks, one call)", down_b, down_us,
+                  roofline=roofline(("axpy_mfma_kernel + splitk_reduce_kernel (the union's down "
+                                     "rows read once, per-token masks, one call)" if batch > 1
+                                     else "axpy_keyed_kernel + splitk_reduce_kernel (the token's "
+                                     "down rows, formed from its keys, one call)"),
+                                    down_b, down_us,
                                     measured_traffic(f"union_down_b{batch}",
                                                      AXPY_MFMA_SOURCES if batch > 1
                                                      else AXPY_B1_SOURCES)),

@@ -136,7 +136,7 @@ const char* sffn_last_error(void);
 /* ABI revision of this header (bumped on any change of a signature or of what
    a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 15
+#define SFFN_ABI_VERSION 16
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -231,6 +231,26 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
                               void* stream);
 
 /*
+ * sparse_ffn_select_threshold -- the top-k rank range [0, k) of each row as
+ * a threshold instead of a list ([SelectInfer] §5: per token, the k neurons
+ * with the largest activation magnitudes).  The n entries of keys + r*ld
+ * (row r < rows) are ordered by (key descending, index ascending), as
+ * sparse_ffn_select orders them, and thr_out[2r], thr_out[2r+1] receive
+ * (T, I): entry j is among the first k iff key_j > T, or key_j == T and
+ * j <= I (I read as int32).  k = 0 gives (0xFFFFFFFF, -1), nothing; k >= n
+ * gives (0, 0x7FFFFFFF), everything.  The set is that of sparse_ffn_select
+ * with r_lo = 0, r_hi = k and no masks, entry for entry; no index list,
+ * count or mask is written -- a consumer such as sparse_ffn_gemv_keyed
+ * applies the test to the keys itself.
+ *  keys    : [rows][ld] in key_type's representation (ld >= n), 4-byte
+ *            aligned.
+ *  thr_out : uint32 [rows][2], 8-byte aligned.
+ * Limits: 1 <= n <= 32768 (EUNSUPPORTED outside), k >= 0, rows >= 0.
+ */
+sffn_status sparse_ffn_select_threshold(const void* keys, int key_type, int rows, int n, int ld,
+                                        int k, uint32_t* thr_out, void* stream);
+
+/*
  * sparse_ffn_gemv -- activations and gathered products over weight rows.
  * Rows processed: all n_rows rows when idx is NULL; otherwise, for
  * i < min(*count, k_max) and g < group, row idx[i]*group + g (a cluster of
@@ -305,6 +325,38 @@ sffn_status sparse_ffn_gemv(int op,
                             const float* alpha,
                             float* out, uint32_t* key_out, int ld_out, int accumulate,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_gemv_keyed -- the batch-1 gathered product over the rows a
+ * threshold selects ([SelectInfer] §5: only the selected neurons are read;
+ * [LeanStream] "Permutation-Invariant Execution": the sum over neurons may
+ * be taken in any grouping):
+ *   out[o] = (accumulate ? out[o] : 0) + alpha * sum over n < n_rows with
+ *            key_n > T or (key_n == T and n <= I) of in[n] * W[n][o],
+ * where (T, I) = (thr[0], (int32) thr[1]) -- the output of
+ * sparse_ffn_select_threshold -- and key_n is keys[n] read as key_type (the
+ * keys that selection ranked).  W = W_down^T, bf16 [n_rows][ld_w] with rows
+ * of length d; in fp32 [n_rows]; out fp32 [d].  Rows outside the selection
+ * are never read.  The neurons are split over workgroups and waves by
+ * index range; each wave forms its rows from the keys (no index list), and
+ * the partial sums are added in a fixed order
+ * (a second kernel): reproducible run to run, and the sum of
+ * sparse_ffn_gemv over the selection's index list up to the order of fp32
+ * additions.
+ *  k_max     : an upper bound of the number of selected rows; it sizes the
+ *              launch only (the threshold decides what is read).
+ *  alpha     : nullable device fp32 scale.
+ *  workspace : sparse_ffn_workspace_size(1, k_max, d) bytes, 256-byte
+ *              aligned; needs no initialisation.
+ * Limits: n_rows >= 1, d % 8 == 0, d >= 8, ld_w >= d, ld_w % 8 == 0,
+ * 0 <= k_max <= n_rows; W / in / out 16-byte aligned, keys 4-byte, thr
+ * 8-byte; n_rows up to 262,144 (EUNSUPPORTED above).
+ */
+sffn_status sparse_ffn_gemv_keyed(const uint16_t* W, int n_rows, int d, int ld_w,
+                                  const float* in, const void* keys, int key_type,
+                                  const uint32_t* thr, int k_max, const float* alpha,
+                                  float* out, int accumulate,
+                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * sparse_ffn_gemv_noalloc -- sparse_ffn_gemv without a workspace argument, for

@@ -213,6 +213,30 @@ void single_thread_cases() {
   expect("masked mask", masked(4, nullptr, nullptr, 0), SFFN_EINVAL, "row_mask");
   expect("masked idx", masked(4, I(), MK, 64), SFFN_EINVAL, "idx must be NULL");
   expect("masked ld", masked(4, nullptr, MK, 72), SFFN_EINVAL, "ld_mask");
+
+  // the top-k range as a threshold pair, and the product keyed by it
+  uint32_t* const THR = static_cast<uint32_t*>(reinterpret_cast<void*>(0x1008));
+  expect("thr keys", sparse_ffn_select_threshold(nullptr, 1, 1, 8, 8, 4, THR, nullptr), SFFN_EINVAL,
+         "keys");
+  expect("thr n", sparse_ffn_select_threshold(FAKE, 1, 1, 40000, 40000, 4, THR, nullptr),
+         SFFN_EUNSUPPORTED, "32768");
+  expect("thr k", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, -1, THR, nullptr), SFFN_EINVAL,
+         "k=");
+  expect("thr align", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, 4, static_cast<uint32_t*>(MIS4),
+                                                  nullptr),
+         SFFN_EINVAL, "8-byte");
+  auto keyed = [](const uint16_t* Wk, int n_rows, int d, int k_max, const uint32_t* thr, void* ws,
+                  size_t ws_bytes) {
+    return sparse_ffn_gemv_keyed(Wk, n_rows, d, d, F(), FAKE, 1, thr, k_max, nullptr, Fo(), 0, ws,
+                                 ws_bytes, nullptr);
+  };
+  void* const WS = reinterpret_cast<void*>(0x100000);
+  expect("keyed W", keyed(nullptr, 64, 256, 32, THR, WS, 1 << 30), SFFN_EINVAL, "W must");
+  expect("keyed thr", keyed(W(), 64, 256, 32, static_cast<uint32_t*>(MIS4), WS, 1 << 30),
+         SFFN_EINVAL, "thr");
+  expect("keyed k_max", keyed(W(), 64, 256, 65, THR, WS, 1 << 30), SFFN_EINVAL, "k_max");
+  expect("keyed rows", keyed(W(), 270000, 256, 10, THR, WS, 1 << 30), SFFN_EUNSUPPORTED, "chunks");
+  expect("keyed workspace", keyed(W(), 64, 256, 32, THR, nullptr, 0), SFFN_EWORKSPACE, "workspace");
 }
 
 // Several threads provoke different errors at once; each must read back the

@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 15
+    assert L.sffn_abi_version() == 16
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -457,6 +457,79 @@ def test_gather_validation(L):
     rc, msg = status_and_msg(L, g(FAKE, 10, FAKE, ctypes.c_void_p(0x1002), 4, FAKE, NULL))
     assert rc == 1 and "aligned" in msg
     assert g(FAKE, 10, NULL, NULL, 0, FAKE, NULL) == 0     # nothing to gather: no launch
+
+
+def test_select_threshold_validation(L):
+    t = L.sparse_ffn_select_threshold
+    ok_thr = ctypes.c_void_p(0x1008)
+
+    def call(keys=FAKE, key_type=1, rows=1, n=8, ld=8, k=4, thr=ok_thr):
+        return status_and_msg(L, t(keys, key_type, rows, n, ld, k, thr, NULL))
+
+    rc, msg = call(keys=NULL)
+    assert rc == 1 and "keys" in msg
+    rc, msg = call(key_type=3)
+    assert rc == 1 and "key type" in msg
+    rc, msg = call(rows=-1)
+    assert rc == 1 and "rows" in msg
+    rc, msg = call(n=40000, ld=40000)
+    assert rc == 2 and "32768" in msg
+    rc, msg = call(ld=4)
+    assert rc == 1 and "ld" in msg
+    rc, msg = call(k=-1)
+    assert rc == 1 and "k=" in msg
+    rc, msg = call(keys=ctypes.c_void_p(0x1002))
+    assert rc == 1 and "4-byte" in msg
+    rc, msg = call(thr=NULL)
+    assert rc == 1 and "thr_out" in msg
+    rc, msg = call(thr=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "8-byte" in msg
+    assert call(rows=0)[0] == 0                            # nothing to select: no launch
+
+
+def test_gemv_keyed_validation(L):
+    g = L.sparse_ffn_gemv_keyed
+    ws_ok = ctypes.c_void_p(0x100000)
+    big = 1 << 30
+
+    def call(W=FAKE, n_rows=64, d=256, ld_w=256, inp=FAKE, keys=FAKE, key_type=1,
+             thr=ctypes.c_void_p(0x1008), k_max=32, alpha=NULL, out=FAKE, acc=0, ws=ws_ok,
+             ws_bytes=big):
+        return status_and_msg(L, g(W, n_rows, d, ld_w, inp, keys, key_type, thr, k_max, alpha,
+                                   out, acc, ws, ws_bytes, NULL))
+
+    rc, msg = call(W=NULL)
+    assert rc == 1 and "W must" in msg
+    rc, msg = call(W=ctypes.c_void_p(0x1008))
+    assert rc == 1 and "W must" in msg
+    rc, msg = call(inp=NULL)
+    assert rc == 1 and "in must" in msg
+    rc, msg = call(out=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "out must" in msg
+    rc, msg = call(keys=NULL)
+    assert rc == 1 and "keys" in msg
+    rc, msg = call(key_type=5)
+    assert rc == 1 and "key type" in msg
+    rc, msg = call(thr=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "thr" in msg
+    rc, msg = call(n_rows=0)
+    assert rc == 1 and "n_rows" in msg
+    rc, msg = call(d=100, ld_w=104)
+    assert rc == 1 and "d=100" in msg
+    rc, msg = call(ld_w=200)
+    assert rc == 1 and "ld_w" in msg
+    rc, msg = call(k_max=65)
+    assert rc == 1 and "k_max" in msg
+    rc, msg = call(alpha=ctypes.c_void_p(0x1002))
+    assert rc == 1 and "alpha" in msg
+    rc, msg = call(n_rows=270000, k_max=10)
+    assert rc == 2 and "chunks" in msg
+    rc, msg = call(ws=NULL)
+    assert rc == 3 and "workspace" in msg
+    rc, msg = call(ws_bytes=100)
+    assert rc == 3 and "workspace" in msg
+    rc, msg = call(ws=ctypes.c_void_p(0x100010))
+    assert rc == 1 and "256-byte" in msg
 
 
 def test_no_fallback_when_library_missing(monkeypatch):

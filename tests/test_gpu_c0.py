@@ -25,20 +25,20 @@ def make(N, d, seed=0):
     return Wg, Wu, WdT, x
 
 
+@pytest.mark.parametrize("keyed", [True, False])
 @pytest.mark.parametrize("N,d,pct", CASES)
-def test_layer_stagewise(N, d, pct):
-    banner(f"c0 N={N} d={d} keep={pct}%")
+def test_layer_stagewise(N, d, pct, keyed):
+    banner(f"c0 N={N} d={d} keep={pct}% keyed={keyed}")
     Wg, Wu, WdT, x = make(N, d)
     keep = pct_count(pct, N)
-    layer = SwigluSparseLayer(dev(Wg), dev(Wu), dev(WdT), keep)
+    layer = SwigluSparseLayer(dev(Wg), dev(Wu), dev(WdT), keep, keyed=keyed)
     y = torch.zeros(d, dtype=torch.float32, device="cuda")
     layer(dev(x), y)
     torch.cuda.synchronize()
     a = host(layer.a)
     assert_close(a, oracle.swiglu_acts(Wg, Wu, x), what="activations")
     assert np.array_equal(host_u32(layer.key), oracle.key_abs(a))
-    cnt = int(host(layer.count)[0])
-    idx = host(layer.idx)[:cnt]
+    idx = layer.selected()   # from the threshold pair (keyed) or the index list
     assert np.array_equal(idx, oracle.rank_range(oracle.key_abs(a), 0, keep))
     y_ref = oracle.down_gather(WdT, idx, a[idx])
     e = assert_close(host(y), y_ref, what="gathered product")
@@ -59,8 +59,12 @@ def test_layer_stagewise(N, d, pct):
     skipped = np.setdiff1d(np.arange(N), idx)
     poisoned[skipped] = 0x7FC0
     y3 = torch.zeros_like(y)
-    B.sparse_ffn_gemv(B.OP_AXPY, dev(poisoned), None, layer.a, y3, idx=layer.idx,
-                      count=layer.count, k_max=keep, workspace=layer.ws)
+    if keyed:
+        B.sparse_ffn_gemv_keyed(dev(poisoned), layer.a, layer.key, B.KEY_U32, layer.thr, keep, y3,
+                                workspace=layer.ws)
+    else:
+        B.sparse_ffn_gemv(B.OP_AXPY, dev(poisoned), None, layer.a, y3, idx=layer.idx,
+                          count=layer.count, k_max=keep, workspace=layer.ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(y).view(np.uint32), host(y3).view(np.uint32))
 
@@ -74,7 +78,7 @@ def test_full_keep_equals_dense_and_empty_selection():
     layer(dev(x), y)
     torch.cuda.synchronize()
     a64 = oracle.swiglu_acts(Wg, Wu, x)
-    assert host(layer.count)[0] == N
+    assert layer.selected().size == N
     assert_close(host(y), oracle.widen_bf16(WdT).T @ a64, what="dense")
     # keep = 0: nothing is read, y = 0; with accumulate, y is unchanged
     empty = SwigluSparseLayer(dev(Wg), dev(Wu), dev(WdT), 0)

@@ -8,7 +8,7 @@ import torch
 import oracle
 from activation_sparse_decode_amd import binding as B
 from activation_sparse_decode_amd import synth
-from activation_sparse_decode_amd.pipelines import BatchedUnionLayer, pct_count
+from activation_sparse_decode_amd.pipelines import BatchedUnionLayer, pct_count, threshold_members
 from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
 
 pytestmark = [gpu, needs_gpu]
@@ -25,10 +25,15 @@ def make(N, d, batch, seed=0):
 def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None, union_list=False):
     Wg, Wu, WdT, X = make(N, d, batch, seed)
     keep = pct_count(pct, N)
-    layer = BatchedUnionLayer(dev(Wg), dev(Wu), dev(WdT), keep, batch, union_list=union_list)
-    # the union as an index list exists at batch 1 and with union_list; the
-    # masked product forms it from the token masks without listing it
-    listed = batch == 1 or union_list
+    # at batch 1 union_list picks the listed path (index list + listed
+    # product) over the keyed one (threshold + keyed product)
+    layer = BatchedUnionLayer(dev(Wg), dev(Wu), dev(WdT), keep, batch, union_list=union_list,
+                              keyed=not union_list)
+    keyed = layer.keyed
+    # the union as an index list exists on the listed batch-1 path and with
+    # union_list; the keyed product reads a threshold, the masked product
+    # forms the union from the token masks, neither lists it
+    listed = (batch == 1 and not keyed) or union_list
     Y = torch.zeros(batch, d, dtype=torch.float32, device="cuda")
     layer(dev(X), Y)
     torch.cuda.synchronize()
@@ -36,8 +41,12 @@ def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None, union_list=False
     K = host_u32(layer.K)
     M = host(layer.M)
     F = host_u32(layer.F)
-    cnt = int(host(layer.cnt)[0]) if listed else int(M.any(axis=0).sum())
-    U = host(layer.U)[:cnt] if listed else np.flatnonzero(M.any(axis=0))
+    if keyed:
+        U = threshold_members(K[0], host(layer.thr))
+        cnt = U.size
+    else:
+        cnt = int(host(layer.cnt)[0]) if listed else int(M.any(axis=0).sum())
+        U = host(layer.U)[:cnt] if listed else np.flatnonzero(M.any(axis=0))
     toks = range(batch) if sample_tokens is None else sample_tokens
     for b in toks:
         assert_close(A[b], oracle.swiglu_acts(Wg, Wu, X[b]), what=f"activations b={b}")
@@ -45,9 +54,10 @@ def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None, union_list=False
     for b in range(batch):
         assert np.array_equal(K[b], oracle.key_abs(A[b]))
         s = oracle.rank_range(oracle.key_abs(A[b]), 0, keep)
-        m = np.zeros(N, np.uint8)
-        m[s] = 1
-        assert np.array_equal(M[b], m), b
+        if not keyed:   # (the keyed path writes no masks)
+            m = np.zeros(N, np.uint8)
+            m[s] = 1
+            assert np.array_equal(M[b], m), b
         S.append(s)
     U_ref = oracle.union(*S)
     assert np.array_equal(U, U_ref)
@@ -63,7 +73,10 @@ def run_and_check(N, d, batch, pct, seed=0, sample_tokens=None, union_list=False
     torch.cuda.synchronize()
     A2 = host(layer.A)
     S2 = [oracle.rank_range(oracle.key_abs(A2[b]), 0, keep) for b in range(batch)]
-    if listed:
+    if keyed:
+        assert np.array_equal(threshold_members(host_u32(layer.K)[0], host(layer.thr)),
+                              oracle.union(*S2))
+    elif listed:
         cnt2 = int(host(layer.cnt)[0])
         assert np.array_equal(host(layer.U)[:cnt2], oracle.union(*S2))
     else:

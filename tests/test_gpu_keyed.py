@@ -1,0 +1,229 @@
+"""The top-k selection as a threshold pair and the product that reads the rows
+a threshold selects (sparse_ffn_select_threshold, sparse_ffn_gemv_keyed).
+
+Index sets: the set a pair stands for (key > T, or key == T and index <= I)
+must equal, entry for entry, sparse_ffn_select's list for the rank range
+[0, k) on the same keys and the oracle's rank_range -- for every key type,
+with ties, NaN / Inf bits, zeros, k = 0, k >= n and several rows.  Products:
+against the oracle over that set, within the output tolerance; rows outside
+the set NaN-poisoned (never read, bitwise the same output); run to run
+bitwise; alpha and accumulate; up to the largest row count;
+replayed from a HIP graph."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_decode_amd import binding as B
+from activation_sparse_decode_amd import synth
+from activation_sparse_decode_amd.pipelines import threshold_members
+from gpu_common import assert_close, banner, dev, gpu, host, host_u32, needs_gpu
+
+pytestmark = [gpu, needs_gpu]
+
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+def host_keys(raw_u32: np.ndarray, key_type: int) -> np.ndarray:
+    """The uint32 ordering key of each raw word, as the select reads it."""
+    if key_type == B.KEY_ABS_F32:
+        return oracle.key_abs(raw_u32.view(np.float32))
+    if key_type == B.KEY_U32:
+        return raw_u32.astype(np.uint32)
+    return oracle.key_signed(raw_u32.view(np.float32))
+
+
+def raw_row(rng, n, kind):
+    if kind == "normal":
+        return rng.standard_normal(n).astype(np.float32).view(np.uint32)
+    if kind == "ties":       # few distinct magnitudes: long runs of equal keys
+        return rng.integers(0, 5, n).astype(np.float32).view(np.uint32)
+    if kind == "equal":
+        return np.full(n, np.float32(0.75)).view(np.uint32)
+    if kind == "specials":   # NaN / +-Inf / +-0 among normals
+        v = rng.standard_normal(n).astype(np.float32)
+        pick = rng.choice(n, size=min(n, 12), replace=False)
+        spec = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, np.nan], np.float32)
+        v[pick] = spec[np.arange(pick.size) % spec.size]
+        return v.view(np.uint32)
+    return rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)   # any bits
+
+
+def check_threshold(raw: np.ndarray, key_type: int, k: int):
+    rows, n = raw.shape
+    keys = dev(raw.view(np.int32))
+    thr = torch.full((rows, 2), 7, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select_threshold(keys, key_type, k, thr)
+    idx = torch.zeros(rows, max(1, min(k, n)), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select(keys, key_type, 0, k, idx_out=idx, count_out=cnt)
+    torch.cuda.synchronize()
+    T = host(thr)
+    for r in range(rows):
+        kk = host_keys(raw[r], key_type)
+        got = threshold_members(kk, T[r])
+        ref = oracle.rank_range(kk, 0, k)
+        assert np.array_equal(got, ref), (r, n, k, T[r])
+        c = int(host(cnt)[r])
+        assert np.array_equal(host(idx)[r][:c], ref)
+    if k == 0:
+        assert np.all(T[:, 0].view(np.uint32) == 0xFFFFFFFF) and np.all(T[:, 1] == -1)
+    if k >= n:
+        assert np.all(T[:, 0] == 0) and np.all(T[:, 1] == 0x7FFFFFFF)
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 1000, 1024, 4097, 8192, 17408, 32768])
+def test_threshold_equals_rank_range(n):
+    banner(f"select_threshold n={n}")
+    rng = np.random.default_rng(n)
+    for kind in ("normal", "ties", "specials"):
+        raw = np.ascontiguousarray(raw_row(rng, n, kind).reshape(1, n)).copy()
+        for k in sorted({0, 1, n // 3, n // 2, max(0, n - 1), n, n + 5}):
+            check_threshold(raw, B.KEY_ABS_F32, k)
+
+
+@pytest.mark.parametrize("key_type", [B.KEY_ABS_F32, B.KEY_U32, B.KEY_F32])
+def test_threshold_key_types_rows_ties(key_type):
+    banner(f"select_threshold key_type={key_type}")
+    rng = np.random.default_rng(40 + key_type)
+    for n in (300, 5000):
+        for kind in ("normal", "ties", "equal", "bits", "specials"):
+            if kind == "bits" and key_type != B.KEY_U32:
+                continue
+            raw = np.stack([raw_row(rng, n, kind) for _ in range(3)])
+            for k in (0, 1, 17, n // 2, n - 1, n):
+                check_threshold(raw, key_type, k)
+
+
+def keyed_case(N, d, k, seed, k_max=None, alpha=None, accumulate=False):
+    """Keys and activations of a SwiGLU-like layer, the threshold, and the
+    keyed product against the oracle over the set it stands for."""
+    WdT = synth.weight_bf16(seed, synth.W_C0, 7, 0, synth.T_DOWN, N, d)
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal(N) * rng.lognormal(0.0, 1.0, N)).astype(np.float32)
+    key = oracle.key_abs(a)
+    W = dev(WdT)
+    keys = dev(key.view(np.int32))
+    if N <= 32768:   # the select's row limit
+        thr = torch.zeros(2, dtype=torch.int32, device="cuda")
+        B.sparse_ffn_select_threshold(keys, B.KEY_U32, k, thr)
+    else:            # past it, the pair of the k-th entry in (key desc, index asc) order
+        e = int(oracle.rank_order(key)[k - 1]) if k > 0 else -1
+        pair = [int(key[e]), e] if k > 0 else [0xFFFFFFFF, -1]
+        thr = dev(np.array(pair, dtype=np.int64).astype(np.uint32))
+    ws = B.new_workspace(1, max(k_max if k_max is not None else k, 1), d)
+    y0 = rng.standard_normal(d).astype(np.float32)
+    y = dev(y0) if accumulate else torch.zeros(d, dtype=torch.float32, device="cuda")
+    al = torch.tensor([alpha], dtype=torch.float32, device="cuda") if alpha is not None else None
+    km = k_max if k_max is not None else min(k, N)
+    B.sparse_ffn_gemv_keyed(W, dev(a), keys, B.KEY_U32, thr, km, y, alpha=al,
+                            accumulate=accumulate, workspace=ws)
+    torch.cuda.synchronize()
+    S = oracle.rank_range(key, 0, k)
+    assert np.array_equal(threshold_members(key, host(thr)), S)
+    ref = oracle.down_gather(WdT, S, a[S]) * (alpha if alpha is not None else 1.0)
+    if accumulate:
+        ref = ref + y0
+    if S.size or accumulate:
+        assert_close(host(y), ref, what=f"keyed N={N} d={d} k={k}")
+    else:
+        assert np.all(host(y) == 0.0)
+    return WdT, a, key, S, W, keys, thr, ws, y, km
+
+
+@pytest.mark.parametrize("N,d,k", [
+    (1000, 264, 500),        # ragged width, one chunk per lane
+    (1000, 2048, 37),
+    (8192, 2048, 4096),      # the single-layer shape, top 50%
+    (17408, 5120, 6963),     # the batched layer at one token, top 40%
+    (100000, 256, 5000),     # many chunks, wide per-lane groups
+    (262144, 64, 20000),     # the largest row count (1024 neurons per chunk)
+])
+def test_keyed_product(N, d, k):
+    banner(f"gemv_keyed N={N} d={d} k={k}")
+    WdT, a, key, S, W, keys, thr, ws, y, km = keyed_case(N, d, k, seed=N + d)
+    # rows outside the set are never read: NaN-poison them
+    P = np.full_like(WdT, NAN_BF16)
+    P[S] = WdT[S]
+    y2 = torch.zeros_like(y)
+    B.sparse_ffn_gemv_keyed(dev(P), dev(a), keys, B.KEY_U32, thr, km, y2, workspace=ws)
+    # run to run: the same bits
+    y3 = torch.zeros_like(y)
+    B.sparse_ffn_gemv_keyed(W, dev(a), keys, B.KEY_U32, thr, km, y3, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(host(y2))), "a row outside the selection (NaN) was read"
+    assert np.array_equal(host(y2).view(np.uint32), host(y).view(np.uint32))
+    assert np.array_equal(host(y3).view(np.uint32), host(y).view(np.uint32))
+
+
+def test_keyed_edges():
+    banner("gemv_keyed edges")
+    keyed_case(5000, 512, 0, seed=1)                              # nothing selected: y = 0
+    keyed_case(5000, 512, 0, seed=2, accumulate=True)             # nothing: y unchanged
+    keyed_case(5000, 512, 5000, seed=3)                           # everything
+    keyed_case(5000, 512, 1, seed=4, alpha=-0.5, accumulate=True)
+    keyed_case(3000, 1024, 999, seed=5, k_max=3000)               # a loose bound
+    keyed_case(3000, 1024, 1500, seed=6, k_max=10)                # a bound below the set
+    keyed_case(1, 8, 1, seed=7)                                   # one row, one chunk
+
+
+def test_keyed_abs_keys_on_the_activations():
+    """key_type ABS_F32 reads the fp32 activations themselves as keys."""
+    banner("gemv_keyed abs keys")
+    N, d, k = 4100, 520, 1234
+    WdT = synth.weight_bf16(3, synth.W_C0, 8, 0, synth.T_DOWN, N, d)
+    a = np.random.default_rng(5).standard_normal(N).astype(np.float32)
+    thr = torch.zeros(2, dtype=torch.int32, device="cuda")
+    ad = dev(a)
+    B.sparse_ffn_select_threshold(ad, B.KEY_ABS_F32, k, thr)
+    y = torch.zeros(d, dtype=torch.float32, device="cuda")
+    B.sparse_ffn_gemv_keyed(dev(WdT), ad, ad, B.KEY_ABS_F32, thr, k, y,
+                            workspace=B.new_workspace(1, k, d))
+    torch.cuda.synchronize()
+    S = oracle.rank_range(oracle.key_abs(a), 0, k)
+    assert_close(host(y), oracle.down_gather(WdT, S, a[S]), what="abs keys")
+
+
+def test_keyed_graph_replay():
+    """Threshold and keyed product captured in a HIP graph: every replay
+    gives the eager bits (new activations copied in between replays)."""
+    banner("keyed graph replay")
+    N, d, k = 8192, 2048, 4096
+    WdT = synth.weight_bf16(9, synth.W_C0, 9, 0, synth.T_DOWN, N, d)
+    rng = np.random.default_rng(9)
+    acts = [rng.standard_normal(N).astype(np.float32) for _ in range(3)]
+    W = dev(WdT)
+    a = torch.zeros(N, dtype=torch.float32, device="cuda")
+    thr = torch.zeros(2, dtype=torch.int32, device="cuda")
+    ws = B.new_workspace(1, k, d)
+    y = torch.zeros(d, dtype=torch.float32, device="cuda")
+
+    def body():
+        B.sparse_ffn_select_threshold(a, B.KEY_ABS_F32, k, thr)
+        B.sparse_ffn_gemv_keyed(W, a, a, B.KEY_ABS_F32, thr, k, y, workspace=ws)
+
+    eager = []
+    for v in acts:
+        a.copy_(torch.from_numpy(v).cuda())
+        body()
+        torch.cuda.synchronize()
+        eager.append(host(y).copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for v, ref in zip(acts, eager):
+            a.copy_(torch.from_numpy(v).cuda())
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(y).view(np.uint32), ref.view(np.uint32)), rep
+    S = oracle.rank_range(oracle.key_abs(acts[-1]), 0, k)
+    assert_close(eager[-1], oracle.down_gather(WdT, S, acts[-1][S]), what="graph case")
