@@ -91,11 +91,14 @@ def lib() -> ctypes.CDLL:
         L.sparse_ffn_pack_weights.restype = _i
         L.sparse_ffn_pack_weights.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp]
         L.sparse_ffn_select_threshold.restype = _i
-        L.sparse_ffn_select_threshold.argtypes = [_vp, _i, _i, _i, _i, _i, _vp, _vp]
+        L.sparse_ffn_select_threshold.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
         L.sparse_ffn_gemv_keyed.restype = _i
         L.sparse_ffn_gemv_keyed.argtypes = [_vp, _i, _i, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _i,
                                             _vp, _sz, _vp]
-        if L.sffn_abi_version() != 16:
+        L.sparse_ffn_tiered_gemv_keyed.restype = _i
+        L.sparse_ffn_tiered_gemv_keyed.argtypes = [_vp, _i, _vp, _i, _vp, _i, _i, _i, _vp, _vp, _i,
+                                                   _vp, _vp, _i, _i, _vp, _i, _vp, _sz, _vp]
+        if L.sffn_abi_version() != 17:
             raise RuntimeError("libsparse_ffn.so ABI version mismatch; rebuild it")
         _lib = L
     return _lib
@@ -188,12 +191,14 @@ def sparse_ffn_select(keys: torch.Tensor, key_type: int, r_lo: int, r_hi: int, *
 
 
 def sparse_ffn_select_threshold(keys: torch.Tensor, key_type: int, k: int, thr_out: torch.Tensor,
-                                stream=None) -> None:
+                                stream=None, *, k_top: int = 0,
+                                thr_top_out: torch.Tensor | None = None) -> None:
     """Per row of keys ([n] or [rows][n]): the top-k range [0, k) as a
-    threshold pair (T, I) in thr_out (int32/uint32 [rows][2] or [2])."""
+    threshold pair (T, I) in thr_out (int32/uint32 [rows][2] or [2]), and
+    with thr_top_out the pair of [0, k_top) there."""
     rows, n = (keys.shape[0], keys.shape[1]) if keys.dim() == 2 else (1, keys.shape[0])
-    _check(lib().sparse_ffn_select_threshold(_p(keys), key_type, rows, n, _ld(keys, n), k,
-                                             _p(thr_out), _stream(stream)))
+    _check(lib().sparse_ffn_select_threshold(_p(keys), key_type, rows, n, _ld(keys, n), k_top, k,
+                                             _p(thr_top_out), _p(thr_out), _stream(stream)))
 
 
 def sparse_ffn_gemv_keyed(W: torch.Tensor, inp: torch.Tensor, keys: torch.Tensor, key_type: int,
@@ -362,3 +367,17 @@ def sparse_ffn_tiered_gemv(Wt: torch.Tensor, mid_rec: torch.Tensor, seg_rows, x:
         _p(Wt), Wt.stride(0), _p(mid_rec), mid_rec.stride(0), arr, n_seg, Wt.shape[0],
         Wt.shape[1], _p(x), _p(idx_top), _p(cnt_top), k_top_max, _p(idx_mid), _p(cnt_mid),
         k_mid_max, _p(y), int(accumulate), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_ffn_tiered_gemv_keyed(Wt: torch.Tensor, mid_rec: torch.Tensor, seg_rows,
+                                 x: torch.Tensor, keys: torch.Tensor, key_type: int,
+                                 thr_top: torch.Tensor, thr: torch.Tensor, k_top_max: int,
+                                 k_mid_max: int, y: torch.Tensor, *, accumulate: bool = False,
+                                 workspace: torch.Tensor | None = None, stream=None) -> None:
+    """The three-tier read with the tiers given as threshold pairs over keys."""
+    arr, n_seg = _seg_array(seg_rows)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().sparse_ffn_tiered_gemv_keyed(
+        _p(Wt), Wt.stride(0), _p(mid_rec), mid_rec.stride(0), arr, n_seg, Wt.shape[0],
+        Wt.shape[1], _p(x), _p(keys), key_type, _p(thr_top), _p(thr), k_top_max, k_mid_max,
+        _p(y), int(accumulate), _p(workspace), ws_bytes, _stream(stream)))

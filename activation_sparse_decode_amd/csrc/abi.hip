@@ -238,7 +238,8 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
 }
 
 sffn_status sparse_ffn_select_threshold(const void* keys, int key_type, int rows, int n, int ld,
-                                        int k, uint32_t* thr_out, void* stream) {
+                                        int k_top, int k, uint32_t* thr_top_out, uint32_t* thr_out,
+                                        void* stream) {
   REQUIRE(keys != nullptr, SFFN_EINVAL, "select_threshold: keys must be non-null");
   REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "select_threshold: unknown key type %d",
           key_type);
@@ -246,13 +247,19 @@ sffn_status sparse_ffn_select_threshold(const void* keys, int key_type, int rows
   REQUIRE(n >= 1 && n <= 32768, SFFN_EUNSUPPORTED, "select_threshold: n=%d outside [1, 32768]", n);
   REQUIRE(ld >= n, SFFN_EINVAL, "select_threshold: ld=%d < n=%d", ld, n);
   REQUIRE(k >= 0, SFFN_EINVAL, "select_threshold: k=%d must be >= 0", k);
+  REQUIRE(k_top >= 0 && k_top <= k, SFFN_EINVAL, "select_threshold: k_top=%d outside [0, k=%d]",
+          k_top, k);
   REQUIRE(aligned(keys, 4), SFFN_EINVAL, "select_threshold: keys must be 4-byte aligned");
   REQUIRE(thr_out != nullptr && aligned(thr_out, 8), SFFN_EINVAL,
           "select_threshold: thr_out must be non-null and 8-byte aligned");
+  REQUIRE(thr_top_out == nullptr || aligned(thr_top_out, 8), SFFN_EINVAL,
+          "select_threshold: thr_top_out must be 8-byte aligned");
+  REQUIRE(k_top == 0 || thr_top_out != nullptr, SFFN_EINVAL,
+          "select_threshold: k_top=%d > 0 needs thr_top_out", k_top);
   if (rows == 0) return ok();
-  sffn::SelectArgs a{keys, key_type, nullptr, rows, n, ld, 1, 0, k, 0,
+  sffn::SelectArgs a{keys, key_type, nullptr, rows, n, ld, 1, k_top, k, 0,
                      nullptr, nullptr, nullptr, 0, nullptr, 0, nullptr,
-                     nullptr, 0, nullptr, nullptr, 0, thr_out};
+                     nullptr, 0, nullptr, nullptr, 0, thr_out, thr_top_out};
   return from_hip(sffn::launch_select(a, (hipStream_t)stream), "select_threshold launch");
 }
 
@@ -698,6 +705,50 @@ sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w, const uint8_t* 
   if (k_mid_max > 0)
     DEBUG_CHECK_LIST("tiered (mid)", 1, idx_mid, cnt_mid, k_mid_max, n_in, true, (hipStream_t)stream);
   return from_hip(sffn::launch_tiered(a, (hipStream_t)stream), "tiered launch");
+}
+
+sffn_status sparse_ffn_tiered_gemv_keyed(const uint16_t* Wt, int ld_w, const uint8_t* mid_rec,
+                                         int rec_bytes, const int32_t* seg_rows, int n_seg,
+                                         int n_in, int d_out, const float* x, const void* keys,
+                                         int key_type, const uint32_t* thr_top, const uint32_t* thr,
+                                         int k_top_max, int k_mid_max, float* y, int accumulate,
+                                         void* workspace, size_t ws_bytes, void* stream) {
+  REQUIRE(Wt && mid_rec && x && y, SFFN_EINVAL,
+          "tiered_keyed: Wt, mid_rec, x and y must be non-null");
+  REQUIRE(n_in >= 1 && d_out >= 64 && d_out % 64 == 0, SFFN_EINVAL,
+          "tiered_keyed: need n_in >= 1 and d_out a positive multiple of 64 (d_out=%d)", d_out);
+  REQUIRE(n_in <= 4096 * (sffn::kMaxSplit / 2), SFFN_EUNSUPPORTED,
+          "tiered_keyed: n_in=%d above %d", n_in, 4096 * (sffn::kMaxSplit / 2));
+  REQUIRE(ld_w >= d_out && ld_w % 8 == 0, SFFN_EINVAL,
+          "tiered_keyed: ld_w=%d must be >= d_out, %% 8", ld_w);
+  sffn_status st = check_segments("tiered_keyed", seg_rows, n_seg, d_out);
+  if (st != SFFN_OK) return st;
+  REQUIRE(rec_bytes % 16 == 0 && (size_t)rec_bytes >= sparse_ffn_tier_record_bytes(d_out, n_seg),
+          SFFN_EINVAL, "tiered_keyed: rec_bytes=%d must be a multiple of 16 and >= %zu", rec_bytes,
+          sparse_ffn_tier_record_bytes(d_out, n_seg));
+  REQUIRE(keys != nullptr && aligned(keys, 4), SFFN_EINVAL,
+          "tiered_keyed: keys must be non-null and 4-byte aligned");
+  REQUIRE(key_type >= 0 && key_type <= 2, SFFN_EINVAL, "tiered_keyed: unknown key type %d",
+          key_type);
+  REQUIRE(thr_top && thr && aligned(thr_top, 8) && aligned(thr, 8), SFFN_EINVAL,
+          "tiered_keyed: thr_top and thr must be non-null and 8-byte aligned");
+  REQUIRE(k_top_max >= 0 && k_top_max <= n_in && k_mid_max >= 0 && k_mid_max <= n_in, SFFN_EINVAL,
+          "tiered_keyed: k_top_max=%d / k_mid_max=%d outside [0, n_in=%d]", k_top_max, k_mid_max,
+          n_in);
+  REQUIRE(aligned(Wt, 16) && aligned(mid_rec, 16) && aligned(y, 16) && aligned(x, 4), SFFN_EINVAL,
+          "tiered_keyed: Wt/mid_rec/y must be 16-byte aligned, x 4-byte aligned");
+  const size_t need = sffn::workspace_bytes(1, k_top_max + k_mid_max, d_out);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, SFFN_EWORKSPACE,
+          "tiered_keyed: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : 0);
+  REQUIRE(aligned(workspace, 256), SFFN_EINVAL, "tiered_keyed: workspace must be 256-byte aligned");
+  sffn::TierArgs a{};
+  a.Wt = Wt; a.ld_w = ld_w; a.rec = mid_rec; a.rec_bytes = rec_bytes;
+  for (int i = 0; i <= n_seg; ++i) a.seg_bounds[i] = seg_rows[i];
+  a.n_seg = n_seg; a.n_in = n_in; a.d_out = d_out; a.x = x;
+  a.k_top_max = k_top_max; a.k_mid_max = k_mid_max;
+  a.y = y; a.accumulate = accumulate ? 1 : 0; a.ws = workspace; a.ws_bytes = ws_bytes;
+  a.keys = keys; a.key_type = key_type; a.thr_top = thr_top; a.thr = thr;
+  return from_hip(sffn::launch_tiered(a, (hipStream_t)stream), "tiered_keyed launch");
 }
 
 sffn_status sparse_ffn_gemv_keyed(const uint16_t* W, int n_rows, int d, int ld_w, const float* in,

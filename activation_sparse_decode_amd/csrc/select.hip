@@ -350,37 +350,48 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 
   if (a.thr_out) {
-    // Threshold mode (the range [0, r_hi), every entry eligible, no lists):
-    // T and the index I of the last entry equal to T inside; entry j is in
-    // iff key_j > T, or key_j == T and j <= I.  Without a split tie every
-    // entry whose key reaches the decided prefix is in (I = INT_MAX).
-    uint32_t* thr = a.thr_out + 2 * (size_t)row;
-    const bool split = need_hi && tie_hi > rem_hi;
-    if (!split) {
-      if (t == 0) {
-        thr[0] = rhi > 0 ? (all_hi ? 0u : pre_hi) : 0xFFFFFFFFu;
-        thr[1] = rhi > 0 ? 0x7FFFFFFFu : 0xFFFFFFFFu;
+    // Threshold mode (every entry eligible, no lists): for the range [0, r_hi)
+    // the key T and the index I of the last entry equal to T inside -- entry j
+    // is in iff key_j > T, or key_j == T and j <= I -- and, with thr_top_out,
+    // the same pair for [0, r_lo).  Without a split tie every entry whose key
+    // reaches the decided prefix is in (I = INT_MAX).
+    uint32_t* th = a.thr_out + 2 * (size_t)row;
+    uint32_t* tl = a.thr_top_out ? a.thr_top_out + 2 * (size_t)row : nullptr;
+    const bool split_h = need_hi && tie_hi > rem_hi;
+    const bool split_l = LO && need_lo && tie_lo > rem_lo;
+    if (t == 0) {
+      th[0] = rhi > 0 ? (all_hi ? 0u : pre_hi) : 0xFFFFFFFFu;
+      if (!split_h) th[1] = rhi > 0 ? 0x7FFFFFFFu : 0xFFFFFFFFu;
+      if (tl) {
+        tl[0] = rlo > 0 ? (all_lo ? 0u : pre_lo) : 0xFFFFFFFFu;
+        if (!split_l) tl[1] = rlo > 0 ? 0x7FFFFFFFu : 0xFFFFFFFFu;
       }
-      return;
     }
-    // the entries equal to T in index order: the rem_hi-th is the last inside
-    uint32_t eq = 0;
+    if (!(split_h || split_l)) return;
+    // the entries equal to a split T in index order (hi: high half, lo: low
+    // half of the packed counts): the rem-th is the last one inside
+    uint32_t eq_h = 0, eq_l = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) eq |= (key[j] == pre_hi ? 1u : 0u) << j;
-    eq &= elig;
-    const uint32_t wc = wave_incl<false>((uint32_t)__popc(eq));
+    for (int j = 0; j < KPT; ++j) {
+      eq_h |= (split_h && key[j] == pre_hi ? 1u : 0u) << j;
+      eq_l |= (split_l && key[j] == pre_lo ? 1u : 0u) << j;
+    }
+    eq_h &= elig;
+    eq_l &= elig;
+    const uint32_t wc = wave_incl<false>(((uint32_t)__popc(eq_h) << 16) + (uint32_t)__popc(eq_l));
     if (lane == 63) WT[1][w] = wc;
     __syncthreads();
     uint32_t dummy;
     uint32_t eq_run = waves_before<NW>(WT[1], dummy);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint64_t b = __ballot((eq >> j) & 1u);
-      const uint32_t pos = eq_run + lanes_below(b);
-      eq_run += (uint32_t)__popcll(b);
-      if (((eq >> j) & 1u) && pos + 1u == rem_hi) thr[1] = (uint32_t)(ebase + 64 * j);
+      const uint64_t bh = __ballot((eq_h >> j) & 1u);
+      const uint64_t bl = __ballot((eq_l >> j) & 1u);
+      const uint32_t ph = (eq_run >> 16) + lanes_below(bh), pl = (eq_run & 0xFFFFu) + lanes_below(bl);
+      eq_run += ((uint32_t)__popcll(bh) << 16) + (uint32_t)__popcll(bl);
+      if (((eq_h >> j) & 1u) && ph + 1u == rem_hi) th[1] = (uint32_t)(ebase + 64 * j);
+      if (((eq_l >> j) & 1u) && pl + 1u == rem_lo && tl) tl[1] = (uint32_t)(ebase + 64 * j);
     }
-    if (t == 0) thr[0] = pre_hi;
     return;
   }
 

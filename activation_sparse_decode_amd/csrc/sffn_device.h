@@ -166,7 +166,8 @@ struct SelectArgs {
   int32_t* count_top_out;
   uint32_t* freq;
   int clear_keys;
-  uint32_t* thr_out;   // threshold mode (one bound from rank 0, no lists): (T, I) per row
+  uint32_t* thr_out;       // threshold mode (no lists): (T, I) of the range [0, r_hi) per row
+  uint32_t* thr_top_out;   // and, if set, (T, I) of [0, r_lo)
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
@@ -186,8 +187,13 @@ struct TierArgs {
   const int32_t* idx_mid; const int32_t* cnt_mid; int k_mid_max;
   float* y; int accumulate;
   void* ws; size_t ws_bytes;
+  // keyed tiers (thr set, idx_* unused): the top tier is the set of thr_top,
+  // the middle tier the set of thr less the top tier; keys read as key_type
+  const void* keys; int key_type;
+  const uint32_t* thr_top; const uint32_t* thr;
 };
 hipError_t launch_tiered(const TierArgs& a, hipStream_t s);
+int tiered_keyed_min_chunks(int n_in);
 hipError_t launch_encode_tiers(const uint16_t* Wt, int ld_w, int n_in, int d_out,
                                const int* seg_bounds, int n_seg, uint8_t* rec,
                                int rec_bytes, hipStream_t s);

@@ -61,9 +61,73 @@ __device__ __forceinline__ void tier_rows(const int32_t* idx, const float* x, in
   }
 }
 
+// Keyed tiers: the workgroup forms its chunk's row list in LDS from the
+// keys.  A tier's chunk m covers the inputs [m c, (m + 1) c), c <= 4096, in
+// passes of 1024 (wave w tests the w-th 64 of a pass, one input per lane);
+// input j is in the top tier iff it is in the set of thr_top, in the middle
+// tier iff it is in the set of thr and not in the top tier (a pair (T, I)
+// holds j iff key_j > T, or key_j == T and j <= I).  The members go to
+// list[] in index order, and the waves then take its items round-robin as
+// from a global list, so the rows are spread evenly over the waves.
+// Returns the chunk's row count; every thread of the workgroup calls it.
+constexpr int kKeyedPass = kWaves * 64;
+constexpr int kKeyedPasses = 4;
+constexpr int kKeyedChunk = kKeyedPass * kKeyedPasses;
+
+__device__ __forceinline__ bool in_pair(uint32_t k, int j, uint32_t T, int I) {
+  return k > T || (k == T && j <= I);
+}
+
+__device__ __forceinline__ uint32_t tier_key(const void* keys, int key_type, int j) {
+  const uint32_t b = reinterpret_cast<const uint32_t*>(keys)[j];
+  if (key_type == 0) return b & 0x7FFFFFFFu;
+  if (key_type == 1) return b;
+  return key_signed(__uint_as_float(b));
+}
+
+__device__ __forceinline__ int keyed_tier_list(const TierArgs& a, bool top, int m, int KS_t,
+                                               int32_t* list, int* wcnt) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int c = (a.n_in + KS_t - 1) / KS_t;
+  const int n0 = m * c, n1 = min(a.n_in, n0 + c);
+  // every pass's keys requested up front (clamped reads past the chunk)
+  uint32_t kv[kKeyedPasses];
+#pragma unroll
+  for (int p = 0; p < kKeyedPasses; ++p)
+    kv[p] = tier_key(a.keys, a.key_type, min(n0 + p * kKeyedPass + w * 64 + lane, a.n_in - 1));
+  const uint32_t Tt = a.thr_top[0], T = a.thr[0];
+  const int It = (int)a.thr_top[1], I = (int)a.thr[1];
+  int tot = 0;
+#pragma unroll
+  for (int p = 0; p < kKeyedPasses; ++p) {
+    if (n0 + p * kKeyedPass >= n1) break;   // uniform
+    const int j = n0 + p * kKeyedPass + w * 64 + lane;
+    const bool it = in_pair(kv[p], j, Tt, It);
+    const bool in = j < n1 && (top ? it : (in_pair(kv[p], j, T, I) && !it));
+    const uint64_t mm = __ballot(in);
+    if (lane == 0) wcnt[w] = (int)__popcll(mm);
+    __syncthreads();
+    int off = tot, pt = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const int cv = wcnt[v];
+      off += v < w ? cv : 0;
+      pt += cv;
+    }
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+    if (in) list[off + rank] = j;
+    tot += pt;
+    __syncthreads();   // the list is complete, and wcnt free for the next pass
+  }
+  return tot;
+}
+
 __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid,
                                                       int xcd_order, float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
+  __shared__ int32_t klist[kKeyedChunk];   // keyed tiers: the chunk's rows
+  __shared__ int kcnt[kWaves];
   const int lane = threadIdx.x & 63, w = wave_id();
   int tile = blockIdx.x, ks = blockIdx.y;
   if (xcd_order) {
@@ -90,35 +154,34 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
   if (ks < KS_top) {
-    int n = a.cnt_top ? *a.cnt_top : 0;
-    n = n < a.k_top_max ? n : a.k_top_max;
-    n = n > 0 ? n : 0;
-    const int chunk = (n + KS_top - 1) / KS_top;
-    const int k0 = ks * chunk, k1 = min(n, k0 + chunk);
-    const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
     constexpr int U = 4;
     uint4 wv[U];
-    tier_rows<U>(
-        a.idx_top, a.x, k0, nu,
-        [&](int u, auto row_at) {
+    auto issue = [&](int u, auto row_at) {
 #pragma unroll
-          for (int uu = 0; uu < U; ++uu)
-            wv[uu] = load_stream16(a.Wt + (size_t)row_at(u + uu) * a.ld_w + colc);
-        },
-        [&](int uu, float xu) {
-          float f[8];
-          unpack8(wv[uu], f);
+      for (int uu = 0; uu < U; ++uu)
+        wv[uu] = load_stream16(a.Wt + (size_t)row_at(u + uu) * a.ld_w + colc);
+    };
+    auto accum = [&](int uu, float xu) {
+      float f[8];
+      unpack8(wv[uu], f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = fmaf(xu, f[e], acc[e]);
-        });
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(xu, f[e], acc[e]);
+    };
+    if (a.thr) {
+      const int n = keyed_tier_list(a, true, ks, KS_top, klist, kcnt);
+      const int nu = n > w ? (n - w + kWaves - 1) / kWaves : 0;
+      tier_rows<U>(klist, a.x, 0, nu, issue, accum);
+    } else {
+      int n = a.cnt_top ? *a.cnt_top : 0;
+      n = n < a.k_top_max ? n : a.k_top_max;
+      n = n > 0 ? n : 0;
+      const int chunk = (n + KS_top - 1) / KS_top;
+      const int k0 = ks * chunk, k1 = min(n, k0 + chunk);
+      const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
+      tier_rows<U>(a.idx_top, a.x, k0, nu, issue, accum);
+    }
   } else {
     const int m = ks - KS_top;
-    int n = a.cnt_mid ? *a.cnt_mid : 0;
-    n = n < a.k_mid_max ? n : a.k_mid_max;
-    n = n > 0 ? n : 0;
-    const int chunk = (n + KS_mid - 1) / KS_mid;
-    const int k0 = m * chunk, k1 = min(n, k0 + chunk);
-    const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
     int seg = 0;
 #pragma unroll
     for (int s = 1; s < 4; ++s)
@@ -128,29 +191,40 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
     float zacc = 0.f;
     constexpr int U = 8;
     uint32_t hdr[U], codes[U];
-    tier_rows<U>(
-        a.idx_mid, a.x, k0, nu,
-        [&](int u, auto row_at) {
+    auto issue = [&](int u, auto row_at) {
 #pragma unroll
-          for (int uu = 0; uu < U; ++uu) {
-            const uint8_t* rec = a.rec + (size_t)row_at(u + uu) * a.rec_bytes;
-            hdr[uu] = *reinterpret_cast<const uint32_t*>(rec + hdr_off);
-            codes[uu] = load_stream4(rec + code_off);
-          }
-        },
-        [&](int uu, float xu) {
-          const float sc = half_bits_to_float(hdr[uu] & 0xFFFFu);
-          const float z = half_bits_to_float(hdr[uu] >> 16);
-          const float sx = xu * sc;
-          zacc = fmaf(xu, z, zacc);
-          const uint32_t lo = codes[uu] & 0x0F0F0F0Fu;
-          const uint32_t hi = (codes[uu] >> 4) & 0x0F0F0F0Fu;
+      for (int uu = 0; uu < U; ++uu) {
+        const uint8_t* rec = a.rec + (size_t)row_at(u + uu) * a.rec_bytes;
+        hdr[uu] = *reinterpret_cast<const uint32_t*>(rec + hdr_off);
+        codes[uu] = load_stream4(rec + code_off);
+      }
+    };
+    auto accum = [&](int uu, float xu) {
+      const float sc = half_bits_to_float(hdr[uu] & 0xFFFFu);
+      const float z = half_bits_to_float(hdr[uu] >> 16);
+      const float sx = xu * sc;
+      zacc = fmaf(xu, z, zacc);
+      const uint32_t lo = codes[uu] & 0x0F0F0F0Fu;
+      const uint32_t hi = (codes[uu] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            acc[2 * b] = fmaf(sx, (float)((lo >> (8 * b)) & 0xFFu), acc[2 * b]);
-            acc[2 * b + 1] = fmaf(sx, (float)((hi >> (8 * b)) & 0xFFu), acc[2 * b + 1]);
-          }
-        });
+      for (int b = 0; b < 4; ++b) {
+        acc[2 * b] = fmaf(sx, (float)((lo >> (8 * b)) & 0xFFu), acc[2 * b]);
+        acc[2 * b + 1] = fmaf(sx, (float)((hi >> (8 * b)) & 0xFFu), acc[2 * b + 1]);
+      }
+    };
+    if (a.thr) {
+      const int n = keyed_tier_list(a, false, m, KS_mid, klist, kcnt);
+      const int nu = n > w ? (n - w + kWaves - 1) / kWaves : 0;
+      tier_rows<U>(klist, a.x, 0, nu, issue, accum);
+    } else {
+      int n = a.cnt_mid ? *a.cnt_mid : 0;
+      n = n < a.k_mid_max ? n : a.k_mid_max;
+      n = n > 0 ? n : 0;
+      const int chunk = (n + KS_mid - 1) / KS_mid;
+      const int k0 = m * chunk, k1 = min(n, k0 + chunk);
+      const int nu = k1 - k0 > w ? (k1 - k0 - w + kWaves - 1) / kWaves : 0;
+      tier_rows<U>(a.idx_mid, a.x, k0, nu, issue, accum);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += zacc;
   }
@@ -159,6 +233,8 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
   const int c = tile * kTileCols + (int)threadIdx.x;
   if (threadIdx.x < kTileCols && c < a.d_out) partials[(size_t)ks * a.d_out + c] = part;
 }
+
+int tiered_keyed_min_chunks(int n_in) { return (n_in + kKeyedChunk - 1) / kKeyedChunk; }
 
 hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   const int col_tiles = (a.d_out + kTileCols - 1) / kTileCols;
@@ -178,6 +254,16 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
     ks_mid = km > 0 ? std::max(1L, slots - ks_top) : 0;
     ks_top = std::min(ks_top, (kt + kWaves - 1) / kWaves);
     ks_mid = std::min(ks_mid, (km + kWaves - 1) / kWaves);
+  }
+  if (a.thr) {
+    // keyed tiers: the sizes are hints only (the pairs decide the tiers), so
+    // each tier's chunks cover all inputs, at most 4096 per chunk
+    // (raised, one tier is then given back slots from the other where it can)
+    const long need = tiered_keyed_min_chunks(a.n_in);
+    ks_top = std::max(ks_top, need);
+    ks_mid = std::max(ks_mid, need);
+    if (ks_top + ks_mid > slots) ks_top = std::max(need, std::min(ks_top, slots - ks_mid));
+    if (ks_top + ks_mid > slots) ks_mid = std::max(need, slots - ks_top);
   }
   ks_top = std::min<long>(ks_top, kMaxSplit / 2);
   ks_mid = std::min<long>(ks_mid, kMaxSplit / 2);

@@ -454,12 +454,16 @@ class TieredProjection:
 
     With ``weight_aware`` the columns are ranked by the WiSparse saliency
     |x_j| * ||W[:, j]||_2 instead, the norms computed once here.
-    ``buffers_from``: a projection of the same shape whose tier lists, counts
-    and workspace this one reuses (projections run one after another)."""
+    ``keyed`` (|x| ranking only): the selection leaves the two tiers as
+    threshold pairs and the product forms its columns from |x| itself, with
+    no index lists.  ``buffers_from``: a projection of the same shape whose
+    tier lists, counts and workspace this one reuses (projections run one
+    after another)."""
 
     def __init__(self, Wt: torch.Tensor, seg_rows, k_top: int, k_mid: int,
-                 weight_aware: bool = False, buffers_from=None):
+                 weight_aware: bool = False, buffers_from=None, keyed: bool = True):
         self.Wt, self.seg_rows, self.k_top, self.k_mid = Wt, list(seg_rows), k_top, k_mid
+        self.keyed = keyed and not weight_aware
         n_in, n_out = Wt.shape
         dev = Wt.device
         self.norms = None
@@ -469,14 +473,34 @@ class TieredProjection:
         rb = B.tier_record_bytes(n_out, len(seg_rows) - 1)
         self.rec = torch.zeros(n_in, rb, dtype=U8, device=dev)
         B.sparse_ffn_encode_tiers(Wt, self.seg_rows, self.rec)
-        if _reuse(self, buffers_from, ("idx_top", "idx_mid", "cnt", "ws")):
+        if _reuse(self, buffers_from, ("idx_top", "idx_mid", "cnt", "thr", "ws")):
             return
         self.idx_top = torch.zeros(max(k_top, 1), dtype=I32, device=dev)
         self.idx_mid = torch.zeros(max(k_mid, 1), dtype=I32, device=dev)
         self.cnt = torch.zeros(2, dtype=I32, device=dev)
+        self.thr = torch.zeros(2, 2, dtype=I32, device=dev)    # (T, I) of the top tier, of both
         self.ws = B.new_workspace(1, k_top + k_mid, n_out, device=dev)
 
+    def tiers(self, x: torch.Tensor):
+        """Host index lists (top, mid) of the last call's tiers (tests)."""
+        if not self.keyed:
+            c = self.cnt.cpu().numpy()
+            return (self.idx_top[:c[0]].cpu().numpy(), self.idx_mid[:c[1]].cpu().numpy())
+        key = x.detach().cpu().numpy().view(np.uint32) & np.uint32(0x7FFFFFFF)
+        t = self.thr.cpu().numpy()
+        top = threshold_members(key, t[0])
+        both = threshold_members(key, t[1])
+        return top, np.setdiff1d(both, top, assume_unique=True)
+
     def __call__(self, x: torch.Tensor, y: torch.Tensor) -> None:
+        if self.keyed:
+            # one selection yields both tiers as pairs: ranks [0, k_top) and [0, k_top + k_mid)
+            B.sparse_ffn_select_threshold(x, B.KEY_ABS_F32, self.k_top + self.k_mid, self.thr[1],
+                                          k_top=self.k_top, thr_top_out=self.thr[0])
+            B.sparse_ffn_tiered_gemv_keyed(self.Wt, self.rec, self.seg_rows, x, x, B.KEY_ABS_F32,
+                                           self.thr[0], self.thr[1], self.k_top, self.k_mid, y,
+                                           workspace=self.ws)
+            return
         # one selection yields both tiers: ranks [0, k_top) and [k_top, k_top + k_mid)
         B.sparse_ffn_select(x, B.KEY_ABS_F32, self.k_top, self.k_top + self.k_mid,
                             idx_out=self.idx_mid, count_out=self.cnt[1:2],

@@ -605,28 +605,39 @@ def run_c2(args, torch, B, synth, P, T):
     us_tok = total_ms * 1e3 / (args.steps * copies)
     dist = T.step_stats(gs, args.steps, before=before, per_step=copies)
 
+    keyed = projs[0][0].keyed
+
+    def product(p, x, y):
+        # the tiered product alone, on the tiers the last step selected
+        if keyed:
+            B.sparse_ffn_tiered_gemv_keyed(p.Wt, p.rec, p.seg_rows, x, x, B.KEY_ABS_F32, p.thr[0],
+                                           p.thr[1], p.k_top, p.k_mid, y, workspace=p.ws)
+        else:
+            B.sparse_ffn_tiered_gemv(p.Wt, p.rec, p.seg_rows, x, p.idx_top, p.cnt[0:1], p.k_top,
+                                     p.idx_mid, p.cnt[1:2], p.k_mid, y, workspace=p.ws)
+
     def down_only():
         for c in range(copies):
-            p = projs[c][1]
-            B.sparse_ffn_tiered_gemv(p.Wt, p.rec, p.seg_rows, xd[c], p.idx_top, p.cnt[0:1],
-                                     p.k_top, p.idx_mid, p.cnt[1:2], p.k_mid, yd[c],
-                                     workspace=p.ws)
+            product(projs[c][1], xd[c], yd[c])
 
     down_us = T.replay_ms(T.capture(down_only), args.steps) * 1e3 / (args.steps * copies)
 
     def qkv_only():
         for c in range(copies):
-            p = projs[c][0]
-            B.sparse_ffn_tiered_gemv(p.Wt, p.rec, p.seg_rows, xq[c], p.idx_top, p.cnt[0:1],
-                                     p.k_top, p.idx_mid, p.cnt[1:2], p.k_mid, yq[c],
-                                     workspace=p.ws)
+            product(projs[c][0], xq[c], yq[c])
 
     qkv_us = T.replay_ms(T.capture(qkv_only), args.steps) * 1e3 / (args.steps * copies)
     rec_q, rec_d = projs[0][0].rec.shape[1], projs[0][1].rec.shape[1]
-    qkv_b = kq_t * n_qkv * 2 + kq_m * rec_q + 8 * (kq_t + kq_m) + 4 * n_qkv
-    down_b = kd_t * d * 2 + kd_m * rec_d + 8 * (kd_t + kd_m) + 4 * d
-    # selection reads x (and the column norms when weight-aware), the product x again
-    step_b = qkv_b + down_b + (3 if args.weight_aware else 2) * (4 * d + 4 * dff)
+    if keyed:
+        # selected bf16 rows and records, x once (it is also the key), the two pairs, y
+        qkv_b = kq_t * n_qkv * 2 + kq_m * rec_q + 4 * d + 16 + 4 * n_qkv
+        down_b = kd_t * d * 2 + kd_m * rec_d + 4 * dff + 16 + 4 * d
+        step_b = qkv_b + down_b + (4 * d + 4 * dff)    # the selections read x
+    else:
+        qkv_b = kq_t * n_qkv * 2 + kq_m * rec_q + 8 * (kq_t + kq_m) + 4 * n_qkv
+        down_b = kd_t * d * 2 + kd_m * rec_d + 8 * (kd_t + kd_m) + 4 * d
+        # selection reads x (and the column norms when weight-aware), the product x again
+        step_b = qkv_b + down_b + (3 if args.weight_aware else 2) * (4 * d + 4 * dff)
     log(f"c2: {us_tok:.2f} us/token; tiered down {down_us:.2f} us, tiered QKV {qkv_us:.2f} us")
 
     cpu = None
@@ -656,7 +667,8 @@ def run_c2(args, torch, B, synth, P, T):
                           "down 14336->4096; 15% bf16 / 35% 4-bit / 50% skipped by "
                           + ("|x_j| * ||W[:, j]||_2 (WiSparse weight-aware)" if args.weight_aware
                              else "|x|")
-                          + "; batch 1 (8 rotating weight copies)",
+                          + "; batch 1 (8 rotating weight copies)"
+                          + ("; tiers as threshold pairs read by the product" if keyed else ""),
               "batch": 1, "tiers_qkv": [kq_t, kq_m], "tiers_down": [kd_t, kd_m]}
     return result(us_tok, "us/token", args.steps * copies, 2, total_ms / args.steps, config,
                   step_bytes=step_b, step_GBps=round(step_b / (us_tok * 1e-6) / 1e9, 1),

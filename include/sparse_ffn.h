@@ -136,7 +136,7 @@ const char* sffn_last_error(void);
 /* ABI revision of this header (bumped on any change of a signature or of what
    a call computes, e.g. a new op or option). */
 int sffn_abi_version(void);
-#define SFFN_ABI_VERSION 16
+#define SFFN_ABI_VERSION 17
 
 /* Bytes of workspace sparse_ffn_gemv / sparse_ffn_tiered_gemv need for a
  * product with `batch` tokens, up to `n_rows` gathered rows (after cluster
@@ -241,14 +241,22 @@ sffn_status sparse_ffn_select(const void* keys, int key_type, const float* key_s
  * gives (0, 0x7FFFFFFF), everything.  The set is that of sparse_ffn_select
  * with r_lo = 0, r_hi = k and no masks, entry for entry; no index list,
  * count or mask is written -- a consumer such as sparse_ffn_gemv_keyed
- * applies the test to the keys itself.
- *  keys    : [rows][ld] in key_type's representation (ld >= n), 4-byte
- *            aligned.
- *  thr_out : uint32 [rows][2], 8-byte aligned.
- * Limits: 1 <= n <= 32768 (EUNSUPPORTED outside), k >= 0, rows >= 0.
+ * applies the test to the keys itself.  With k_top > 0, thr_top_out[2r],
+ * thr_top_out[2r+1] receive the pair of [0, k_top) as well, from the same
+ * pass (the SpAx top tier; the middle tier [k_top, k) is the set of thr_out
+ * less that of thr_top_out).  With k_top = 0 a non-null thr_top_out
+ * receives the empty pair.
+ *  keys        : [rows][ld] in key_type's representation (ld >= n), 4-byte
+ *                aligned.
+ *  thr_out     : uint32 [rows][2], 8-byte aligned.
+ *  thr_top_out : nullable uint32 [rows][2], 8-byte aligned; required when
+ *                k_top > 0.
+ * Limits: 1 <= n <= 32768 (EUNSUPPORTED outside), 0 <= k_top <= k,
+ * rows >= 0.
  */
 sffn_status sparse_ffn_select_threshold(const void* keys, int key_type, int rows, int n, int ld,
-                                        int k, uint32_t* thr_out, void* stream);
+                                        int k_top, int k, uint32_t* thr_top_out,
+                                        uint32_t* thr_out, void* stream);
 
 /*
  * sparse_ffn_gemv -- activations and gathered products over weight rows.
@@ -609,6 +617,35 @@ sffn_status sparse_ffn_tiered_gemv(const uint16_t* Wt, int ld_w,
                                    const int32_t* idx_mid, const int32_t* cnt_mid, int k_mid_max,
                                    float* y, int accumulate,
                                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sparse_ffn_tiered_gemv_keyed -- sparse_ffn_tiered_gemv with the two tiers
+ * given as threshold pairs (the output of sparse_ffn_select_threshold with
+ * k_top and k) instead of column lists:
+ *   top = { j : key_j > T_top, or key_j == T_top and j <= I_top },
+ *   mid = { j : key_j > T, or key_j == T and j <= I } less top,
+ * with (T_top, I_top) = thr_top[0..1], (T, I) = thr[0..1] (I read as int32)
+ * and key_j = keys[j] read as key_type (the keys that selection ranked, e.g.
+ * x itself with SFFN_KEY_ABS_F32).  y is that of sparse_ffn_tiered_gemv over
+ * the two tiers' index lists up to the order of fp32 additions, and the same
+ * bits run to run.  Each wave forms its columns from the keys; columns in
+ * neither tier are never read.
+ *  k_top_max, k_mid_max : upper bounds of the tier sizes; they size the
+ *                         launch only.
+ *  workspace            : sparse_ffn_workspace_size(1, k_top_max +
+ *                         k_mid_max, d_out) bytes, 256-byte aligned.
+ * Limits: those of sparse_ffn_tiered_gemv, n_in up to 524,288
+ * (EUNSUPPORTED above); keys 4-byte aligned, thr_top / thr 8-byte aligned.
+ */
+sffn_status sparse_ffn_tiered_gemv_keyed(const uint16_t* Wt, int ld_w,
+                                         const uint8_t* mid_rec, int rec_bytes,
+                                         const int32_t* seg_rows, int n_seg,
+                                         int n_in, int d_out, const float* x,
+                                         const void* keys, int key_type,
+                                         const uint32_t* thr_top, const uint32_t* thr,
+                                         int k_top_max, int k_mid_max,
+                                         float* y, int accumulate,
+                                         void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -216,15 +216,19 @@ void single_thread_cases() {
 
   // the top-k range as a threshold pair, and the product keyed by it
   uint32_t* const THR = static_cast<uint32_t*>(reinterpret_cast<void*>(0x1008));
-  expect("thr keys", sparse_ffn_select_threshold(nullptr, 1, 1, 8, 8, 4, THR, nullptr), SFFN_EINVAL,
+  expect("thr keys", sparse_ffn_select_threshold(nullptr, 1, 1, 8, 8, 0, 4, nullptr, THR, nullptr), SFFN_EINVAL,
          "keys");
-  expect("thr n", sparse_ffn_select_threshold(FAKE, 1, 1, 40000, 40000, 4, THR, nullptr),
+  expect("thr n", sparse_ffn_select_threshold(FAKE, 1, 1, 40000, 40000, 0, 4, nullptr, THR, nullptr),
          SFFN_EUNSUPPORTED, "32768");
-  expect("thr k", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, -1, THR, nullptr), SFFN_EINVAL,
+  expect("thr k", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, 0, -1, nullptr, THR, nullptr), SFFN_EINVAL,
          "k=");
-  expect("thr align", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, 4, static_cast<uint32_t*>(MIS4),
-                                                  nullptr),
+  expect("thr align", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, 0, 4, nullptr,
+                                                  static_cast<uint32_t*>(MIS4), nullptr),
          SFFN_EINVAL, "8-byte");
+  expect("thr k_top", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, 5, 4, THR, THR, nullptr),
+         SFFN_EINVAL, "k_top=5");
+  expect("thr top", sparse_ffn_select_threshold(FAKE, 1, 1, 8, 8, 2, 4, nullptr, THR, nullptr),
+         SFFN_EINVAL, "needs thr_top_out");
   auto keyed = [](const uint16_t* Wk, int n_rows, int d, int k_max, const uint32_t* thr, void* ws,
                   size_t ws_bytes) {
     return sparse_ffn_gemv_keyed(Wk, n_rows, d, d, F(), FAKE, 1, thr, k_max, nullptr, Fo(), 0, ws,
@@ -237,6 +241,15 @@ void single_thread_cases() {
   expect("keyed k_max", keyed(W(), 64, 256, 65, THR, WS, 1 << 30), SFFN_EINVAL, "k_max");
   expect("keyed rows", keyed(W(), 270000, 256, 10, THR, WS, 1 << 30), SFFN_EUNSUPPORTED, "chunks");
   expect("keyed workspace", keyed(W(), 64, 256, 32, THR, nullptr, 0), SFFN_EWORKSPACE, "workspace");
+  const int32_t seg_k[4] = {0, 4096, 5120, 6144};
+  auto tk = [&](int n_in, const uint32_t* thr_top, size_t ws_bytes) {
+    return sparse_ffn_tiered_gemv_keyed(W(), 6144, static_cast<const uint8_t*>(FAKE), 3088, seg_k,
+                                        3, n_in, 6144, F(), FAKE, 0, thr_top, THR, 10, 10, Fo(), 0, WS,
+                                        ws_bytes, nullptr);
+  };
+  expect("tiered keyed n_in", tk(600000, THR, 1 << 30), SFFN_EUNSUPPORTED, "524288");
+  expect("tiered keyed thr", tk(4096, nullptr, 1 << 30), SFFN_EINVAL, "thr_top");
+  expect("tiered keyed workspace", tk(4096, THR, 64), SFFN_EWORKSPACE, "workspace");
 }
 
 // Several threads provoke different errors at once; each must read back the

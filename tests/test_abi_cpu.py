@@ -29,7 +29,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(L, name), f"{name} declared in sparse_ffn.h but not exported"
 
@@ -43,7 +43,7 @@ def test_sizes(L):
     assert B.tier_record_bytes(4096, 5) == 0
     assert B.workspace_size(1, 4096, 2048) >= 256 * 2048 * 4
     assert B.workspace_size(16, 17408, 5120) > B.workspace_size(1, 17408, 5120)
-    assert L.sffn_abi_version() == 16
+    assert L.sffn_abi_version() == 17
 
 
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -385,6 +385,33 @@ def test_tier_validation(L):
     rc, msg = status_and_msg(L, tg(FAKE, 6144, FAKE, 3088, seg, 3, 4096, 6144, FAKE, FAKE, FAKE, 614,
                                    FAKE, FAKE, 1433, FAKE, 0, FAKE, 64, NULL))
     assert rc == 3 and "workspace" in msg
+    tk = L.sparse_ffn_tiered_gemv_keyed
+    thr = ctypes.c_void_p(0x1008)
+
+    def keyed(n_in=4096, keys=FAKE, key_type=0, thr_top=thr, thr=thr, k_top=614, k_mid=1433,
+              x=FAKE, ws_bytes=1 << 30, seg_=seg, n_seg=3):
+        return status_and_msg(L, tk(FAKE, 6144, FAKE, 3088, seg_, n_seg, n_in, 6144, x, keys,
+                                    key_type, thr_top, thr, k_top, k_mid, FAKE, 0, FAKE, ws_bytes,
+                                    NULL))
+
+    rc, msg = keyed(x=NULL)
+    assert rc == 1 and "non-null" in msg
+    rc, msg = keyed(n_in=600000, k_top=10, k_mid=10)
+    assert rc == 2 and "524288" in msg
+    rc, msg = keyed(keys=NULL)
+    assert rc == 1 and "keys" in msg
+    rc, msg = keyed(key_type=3)
+    assert rc == 1 and "key type" in msg
+    rc, msg = keyed(thr_top=NULL)
+    assert rc == 1 and "thr_top" in msg
+    rc, msg = keyed(thr=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "8-byte" in msg
+    rc, msg = keyed(k_mid=5000)
+    assert rc == 1 and "k_mid_max" in msg
+    rc, msg = keyed(n_seg=5)
+    assert rc == 2
+    rc, msg = keyed(ws_bytes=64)
+    assert rc == 3 and "workspace" in msg
 
 
 def test_compact_validation(L):
@@ -463,8 +490,8 @@ def test_select_threshold_validation(L):
     t = L.sparse_ffn_select_threshold
     ok_thr = ctypes.c_void_p(0x1008)
 
-    def call(keys=FAKE, key_type=1, rows=1, n=8, ld=8, k=4, thr=ok_thr):
-        return status_and_msg(L, t(keys, key_type, rows, n, ld, k, thr, NULL))
+    def call(keys=FAKE, key_type=1, rows=1, n=8, ld=8, k=4, thr=ok_thr, k_top=0, thr_top=NULL):
+        return status_and_msg(L, t(keys, key_type, rows, n, ld, k_top, k, thr_top, thr, NULL))
 
     rc, msg = call(keys=NULL)
     assert rc == 1 and "keys" in msg
@@ -484,6 +511,14 @@ def test_select_threshold_validation(L):
     assert rc == 1 and "thr_out" in msg
     rc, msg = call(thr=ctypes.c_void_p(0x1004))
     assert rc == 1 and "8-byte" in msg
+    rc, msg = call(k_top=5, thr_top=ok_thr)
+    assert rc == 1 and "k_top=5" in msg
+    rc, msg = call(k_top=-1, thr_top=ok_thr)
+    assert rc == 1 and "k_top=-1" in msg
+    rc, msg = call(k_top=2)
+    assert rc == 1 and "needs thr_top_out" in msg
+    rc, msg = call(k_top=2, thr_top=ctypes.c_void_p(0x1004))
+    assert rc == 1 and "thr_top_out" in msg and "8-byte" in msg
     assert call(rows=0)[0] == 0                            # nothing to select: no launch
 
 

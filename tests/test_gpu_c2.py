@@ -1,6 +1,7 @@
 """SpAx three-tier read (Llama3.1-8B QKV and down at full size): the 4-bit
 encoder is bit-exact with the oracle's, the tiers are bit-exact rank
-ranges of |x|, and the product is within tolerance of the oracle's."""
+ranges of |x| (as index lists, or as threshold pairs the product reads the
+keys with), and the product is within tolerance of the oracle's."""
 import numpy as np
 import pytest
 import torch
@@ -8,7 +9,7 @@ import torch
 import oracle
 from activation_sparse_decode_amd import binding as B
 from activation_sparse_decode_amd import synth
-from activation_sparse_decode_amd.pipelines import TieredProjection, pct_count
+from activation_sparse_decode_amd.pipelines import TieredProjection, pct_count, threshold_members
 from gpu_common import assert_close, banner, dev, gpu, host, needs_gpu
 
 pytestmark = [gpu, needs_gpu]
@@ -39,23 +40,24 @@ def unpack_records(rec: np.ndarray, n_out: int, n_seg: int):
     return scale, zero, q
 
 
+@pytest.mark.parametrize("keyed", [True, False])
 @pytest.mark.parametrize("name", ["small", "qkv", "down"])
-def test_tiered_stagewise(name):
-    banner(f"c2 {name}")
+def test_tiered_stagewise(name, keyed):
+    banner(f"c2 {name} keyed={keyed}")
     Wt, x, seg = make(name)
     n_in, n_out = Wt.shape
     k_top, k_mid = pct_count(15, n_in), pct_count(35, n_in)
-    proj = TieredProjection(dev(Wt), seg, k_top, k_mid)
+    proj = TieredProjection(dev(Wt), seg, k_top, k_mid, keyed=keyed)
     y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
-    proj(dev(x), y)
+    xd = dev(x)
+    proj(xd, y)
     torch.cuda.synchronize()
     scale, zero, q = unpack_records(host(proj.rec), n_out, len(seg) - 1)
     o_scale, o_zero, o_q = oracle.encode_4bit(Wt, seg)
     assert np.array_equal(scale.view(np.uint16), o_scale.view(np.uint16))
     assert np.array_equal(zero.view(np.uint16), o_zero.view(np.uint16))
     assert np.array_equal(q, o_q)
-    cnt = host(proj.cnt)
-    top, mid = host(proj.idx_top)[:cnt[0]], host(proj.idx_mid)[:cnt[1]]
+    top, mid = proj.tiers(xd)
     o_top, o_mid = oracle.tier_sets(x, k_top, k_mid)
     assert np.array_equal(top, o_top) and np.array_equal(mid, o_mid)
     y_ref = oracle.tiered_gemv(Wt, o_scale, o_zero, o_q, seg, x, top, mid)
@@ -73,10 +75,79 @@ def test_tiered_stagewise(name):
     rec[skipped, :16] = np.frombuffer(np.array([0x7E00] * 8, np.uint16).tobytes(), np.uint8)
     rec[top] = 0xFF
     y2 = torch.zeros_like(y)
-    B.sparse_ffn_tiered_gemv(dev(Wp), dev(rec), seg, dev(x), proj.idx_top, proj.cnt[0:1], k_top,
-                             proj.idx_mid, proj.cnt[1:2], k_mid, y2, workspace=proj.ws)
+    if keyed:
+        B.sparse_ffn_tiered_gemv_keyed(dev(Wp), dev(rec), seg, xd, xd, B.KEY_ABS_F32, proj.thr[0],
+                                       proj.thr[1], k_top, k_mid, y2, workspace=proj.ws)
+    else:
+        B.sparse_ffn_tiered_gemv(dev(Wp), dev(rec), seg, xd, proj.idx_top, proj.cnt[0:1], k_top,
+                                 proj.idx_mid, proj.cnt[1:2], k_mid, y2, workspace=proj.ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+
+
+def test_keyed_tiers_with_ties():
+    """Both tier bounds inside runs of equal |x| (index order decides), and
+    the product over those tiers; several (k_top, k_mid) splits, including an
+    empty top or middle tier and everything selected."""
+    banner("c2 keyed ties")
+    n_in, n_out, seg = CASES["qkv"]
+    Wt = synth.weight_bf16(11, synth.W_C2, 0, 0, synth.T_QKV, n_in, n_out)
+    rng = np.random.default_rng(11)
+    x = (rng.integers(0, 6, n_in) * rng.choice([-1, 1], n_in)).astype(np.float32) * 0.25
+    xd = dev(x)
+    o_scale, o_zero, o_q = oracle.encode_4bit(Wt, seg)
+    y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+    proj = TieredProjection(dev(Wt), seg, 1, 1)
+    for k_top, k_mid in [(700, 1300), (0, 2000), (1500, 0), (1, n_in - 1), (n_in, 0)]:
+        thr = torch.zeros(2, 2, dtype=torch.int32, device="cuda")
+        B.sparse_ffn_select_threshold(xd, B.KEY_ABS_F32, k_top + k_mid, thr[1], k_top=k_top,
+                                      thr_top_out=thr[0])
+        ws = B.new_workspace(1, k_top + k_mid, n_out)
+        B.sparse_ffn_tiered_gemv_keyed(proj.Wt, proj.rec, seg, xd, xd, B.KEY_ABS_F32, thr[0],
+                                       thr[1], k_top, k_mid, y, workspace=ws)
+        torch.cuda.synchronize()
+        key = x.view(np.uint32) & np.uint32(0x7FFFFFFF)
+        T = host(thr)
+        top = threshold_members(key, T[0])
+        mid = np.setdiff1d(threshold_members(key, T[1]), top)
+        o_top, o_mid = oracle.tier_sets(x, k_top, k_mid)
+        assert np.array_equal(top, o_top) and np.array_equal(mid, o_mid), (k_top, k_mid)
+        y_ref = oracle.tiered_gemv(Wt, o_scale, o_zero, o_q, seg, x, o_top, o_mid)
+        if o_top.size + o_mid.size:
+            assert_close(host(y), y_ref, what=f"keyed ties {k_top}/{k_mid}")
+
+
+@pytest.mark.parametrize("n_in", [40000, 131072, 524288])
+def test_keyed_tiers_many_chunks(n_in):
+    """Inputs past the select's row limit (pairs built on the host from the
+    oracle's order): tier chunks of one to four passes of 1024 inputs, up to
+    the largest input count."""
+    banner(f"c2 keyed n_in={n_in}")
+    n_out, seg = (128, [0, 64, 128]) if n_in < 500000 else (64, [0, 64])
+    Wt = synth.weight_bf16(12, synth.W_C2, 0, 0, synth.T_DOWN, n_in, n_out)
+    x = synth.tokens(12, synth.W_C2, 9, 1, n_in)[0]
+    k_top, k_mid = pct_count(10, n_in), pct_count(30, n_in)
+    proj = TieredProjection(dev(Wt), seg, k_top, k_mid)
+    key = x.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    order = oracle.rank_order(key)
+
+    def pair(k):
+        if k == 0:
+            return [0xFFFFFFFF, 0xFFFFFFFF]
+        e = int(order[k - 1])
+        return [int(key[e]), e]
+
+    thr = dev(np.array([pair(k_top), pair(k_top + k_mid)], dtype=np.int64).astype(np.uint32))
+    y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+    xd = dev(x)
+    B.sparse_ffn_tiered_gemv_keyed(proj.Wt, proj.rec, seg, xd, xd, B.KEY_ABS_F32, thr[0], thr[1],
+                                   k_top, k_mid, y, workspace=proj.ws)
+    torch.cuda.synchronize()
+    o_top, o_mid = oracle.tier_sets(x, k_top, k_mid)
+    assert np.array_equal(threshold_members(key, host(thr)[0]), o_top)
+    o_scale, o_zero, o_q = oracle.encode_4bit(Wt, seg)
+    y_ref = oracle.tiered_gemv(Wt, o_scale, o_zero, o_q, seg, x, o_top, o_mid)
+    assert_close(host(y), y_ref, what=f"keyed n_in={n_in}")
 
 
 def test_tier_special_cases():

@@ -95,6 +95,35 @@ def test_threshold_key_types_rows_ties(key_type):
                 check_threshold(raw, key_type, k)
 
 
+@pytest.mark.parametrize("key_type", [B.KEY_ABS_F32, B.KEY_U32, B.KEY_F32])
+def test_threshold_pair_of_two_ranges(key_type):
+    """k_top > 0: the same pass writes the pair of [0, k_top) as well; both
+    sets equal the oracle's rank ranges (ties split at either bound), and
+    k_top = 0 with a second output gives the empty pair there."""
+    banner(f"select_threshold two ranges key_type={key_type}")
+    rng = np.random.default_rng(70 + key_type)
+    for n in (300, 5000, 32768):
+        for kind in ("normal", "ties", "specials"):
+            raw = np.stack([raw_row(rng, n, kind) for _ in range(3)])
+            keys = dev(raw.view(np.int32))
+            for k_top, k in ((0, n // 2), (1, 2), (n // 7, n // 2), (n // 2, n // 2), (n // 3, n),
+                             (n, n), (0, 0)):
+                thr = torch.full((3, 2), 7, dtype=torch.int32, device="cuda")
+                top = torch.full((3, 2), 7, dtype=torch.int32, device="cuda")
+                B.sparse_ffn_select_threshold(keys, key_type, k, thr, k_top=k_top,
+                                              thr_top_out=top)
+                torch.cuda.synchronize()
+                T, Tt = host(thr), host(top)
+                for r in range(3):
+                    kk = host_keys(raw[r], key_type)
+                    assert np.array_equal(threshold_members(kk, T[r]),
+                                          oracle.rank_range(kk, 0, k)), (n, kind, k_top, k, r)
+                    assert np.array_equal(threshold_members(kk, Tt[r]),
+                                          oracle.rank_range(kk, 0, k_top)), (n, kind, k_top, k, r)
+                if k_top == 0:
+                    assert np.all(Tt[:, 0].view(np.uint32) == 0xFFFFFFFF) and np.all(Tt[:, 1] == -1)
+
+
 def keyed_case(N, d, k, seed, k_max=None, alpha=None, accumulate=False):
     """Keys and activations of a SwiGLU-like layer, the threshold, and the
     keyed product against the oracle over the set it stands for."""
