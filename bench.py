@@ -1037,7 +1037,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     out["env"] = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
                   "compute_units": props.multi_processor_count,
-                  "hip": torch.version.hip, "torch": torch.__version__, **clock_info()}
+                  "hip": torch.version.hip, "torch": torch.__version__, **clock_info(torch)}
 
     # A plain device copy of known size: the reference that scales the HBM
     # counters (FETCH_SIZE / WRITE_SIZE) of profiled kernels to bytes.
@@ -1047,18 +1047,26 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def clock_info() -> dict:
-    """The GPU's current clocks as rocm-smi reports them and the amdgpu driver
-    version, best effort (either is left out when the tool or file is absent)."""
-    import subprocess
+def clock_info(torch=None) -> dict:
+    """The GPU's current core and memory clock levels (the amdgpu sysfs
+    files of device 0's PCI function, the entry marked current) and the
+    driver version, best effort: a missing file only drops its field.  Plain
+    file reads: no tool is started, so a profiler's preload in this process
+    is never carried into another program."""
     info = {}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        cards = json.loads(r.stdout)
-        card = cards[sorted(cards)[0]]
-        info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower() or "clk" in k.lower()}
-    except Exception:   # noqa: BLE001 -- a missing tool or odd output only drops the field
+        prop = torch.cuda.get_device_properties(0)
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (prop.pci_domain_id, prop.pci_bus_id,
+                                                         prop.pci_device_id)
+        clocks = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            with open(f"{dev}/{name}") as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            if cur:
+                clocks[name[-4:]] = cur[0].rstrip("* ").split(":", 1)[-1].strip()
+        if clocks:
+            info["clocks"] = clocks
+    except Exception:   # noqa: BLE001 -- absent files or properties only drop the field
         pass
     try:
         with open("/sys/module/amdgpu/version") as f:
