@@ -117,6 +117,59 @@ def test_keyed_tiers_with_ties():
             assert_close(host(y), y_ref, what=f"keyed ties {k_top}/{k_mid}")
 
 
+def test_keyed_tiers_accumulate_graph_replay():
+    """The threshold select (both pairs) and the keyed tiered product with
+    accumulate, captured in a HIP graph: every replay on new inputs gives
+    the eager bits, and the eager result is y0 plus the oracle's product."""
+    banner("c2 keyed accumulate + graph replay")
+    n_in, n_out, seg = CASES["qkv"]
+    Wt = synth.weight_bf16(13, synth.W_C2, 0, 0, synth.T_QKV, n_in, n_out)
+    xs = [synth.tokens(13, synth.W_C2, 20 + i, 1, n_in)[0] for i in range(3)]
+    y0 = np.random.default_rng(13).standard_normal(n_out).astype(np.float32)
+    k_top, k_mid = pct_count(15, n_in), pct_count(35, n_in)
+    proj = TieredProjection(dev(Wt), seg, k_top, k_mid)
+    x = torch.zeros(n_in, dtype=torch.float32, device="cuda")
+    y = torch.zeros(n_out, dtype=torch.float32, device="cuda")
+    y0d = dev(y0)
+
+    def body():
+        B.sparse_ffn_select_threshold(x, B.KEY_ABS_F32, k_top + k_mid, proj.thr[1], k_top=k_top,
+                                      thr_top_out=proj.thr[0])
+        B.sparse_ffn_tiered_gemv_keyed(proj.Wt, proj.rec, seg, x, x, B.KEY_ABS_F32, proj.thr[0],
+                                       proj.thr[1], k_top, k_mid, y, accumulate=True,
+                                       workspace=proj.ws)
+
+    o_scale, o_zero, o_q = oracle.encode_4bit(Wt, seg)
+    eager = []
+    for v in xs:
+        x.copy_(torch.from_numpy(v).cuda())
+        y.copy_(y0d)
+        body()
+        torch.cuda.synchronize()
+        eager.append(host(y).copy())
+        top, mid = oracle.tier_sets(v, k_top, k_mid)
+        ref = y0.astype(np.float64) + oracle.tiered_gemv(Wt, o_scale, o_zero, o_q, seg, v, top, mid)
+        assert_close(eager[-1], ref, what="keyed tiers, accumulate")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for v, ref in zip(xs, eager):
+            x.copy_(torch.from_numpy(v).cuda())
+            y.copy_(y0d)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(y).view(np.uint32), ref.view(np.uint32)), rep
+
+
 @pytest.mark.parametrize("n_in", [40000, 131072, 524288])
 def test_keyed_tiers_many_chunks(n_in):
     """Inputs past the select's row limit (pairs built on the host from the
