@@ -123,6 +123,11 @@ __device__ __forceinline__ int keyed_tier_list(const TierArgs& a, bool top, int 
   return tot;
 }
 
+// UM: middle-tier rows in flight per lane (8 for index lists; 9 for keyed
+// tiers, whose per-chunk row counts vary by about +-10% around the mean: at
+// the 14336-input down projection nine keep the fullest chunks at two
+// batches per wave).
+template <int UM>
 __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, int KS_mid,
                                                       int xcd_order, float* partials) {
   __shared__ float4 red[kWaves][kTileCols / 4];
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(1024) void tiered_kernel(TierArgs a, int KS_top, in
     const int hdr_off = 4 * seg;
     const int code_off = 16 + (colc >> 1);
     float zacc = 0.f;
-    constexpr int U = 8;
+    constexpr int U = UM;
     uint32_t hdr[U], codes[U];
     auto issue = [&](int u, auto row_at) {
 #pragma unroll
@@ -240,15 +245,15 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   const int col_tiles = (a.d_out + kTileCols - 1) / kTileCols;
   // One round of workgroups, one per CU (a second partial round costs more
   // than it adds).  The chunk slots are split between the tiers by row
-  // count, top rows weighted 1.3: measured on MI355X, a middle-tier row
-  // (4-bit codes decoded in registers) takes about as long as a top-tier row
-  // although it is a quarter of the bytes.  A chunk keeps at least one row
-  // per wave.
+  // count, top rows weighted 1.3 (1.45 for keyed tiers, with nine middle
+  // rows in flight): measured on MI355X, a middle-tier row (4-bit codes
+  // decoded in registers) takes about as long as a top-tier row although it
+  // is a quarter of the bytes.  A chunk keeps at least one row per wave.
   const long slots = std::max(1, 256 / col_tiles);
   const long kt = std::max(0, a.k_top_max), km = std::max(0, a.k_mid_max);
   long ks_top = 0, ks_mid = 0;
   if (kt + km > 0) {
-    const double wt = 1.3 * (double)kt, wm = (double)km;
+    const double wt = (a.thr ? 1.45 : 1.3) * (double)kt, wm = (double)km;
     ks_top = kt > 0 ? std::max(1L, (long)(slots * wt / (wt + wm) + 0.5)) : 0;
     if (km > 0 && ks_top >= slots) ks_top = std::max(1L, slots - 1);
     ks_mid = km > 0 ? std::max(1L, slots - ks_top) : 0;
@@ -273,8 +278,12 @@ hipError_t launch_tiered(const TierArgs& a, hipStream_t s) {
   // 21 chunks the plain order is kept)
   const int xcd_order = (ks_top + ks_mid) % 8 == 0 ? 1 : 2;
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + kWsHeaderBytes);
-  hipLaunchKernelGGL(tiered_kernel, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0, s,
-                     a, (int)ks_top, (int)ks_mid, xcd_order, partials);
+  if (a.thr)
+    hipLaunchKernelGGL(tiered_kernel<9>, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0,
+                       s, a, (int)ks_top, (int)ks_mid, xcd_order, partials);
+  else
+    hipLaunchKernelGGL(tiered_kernel<8>, dim3(col_tiles, (unsigned)(ks_top + ks_mid)), dim3(1024), 0,
+                       s, a, (int)ks_top, (int)ks_mid, xcd_order, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_reduce(partials, (int)(ks_top + ks_mid), 1, 1, a.d_out, nullptr, a.y,
