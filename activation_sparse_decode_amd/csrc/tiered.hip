@@ -11,10 +11,14 @@
 // The grid is (512-column tiles) x (KS_top + KS_mid chunks): a workgroup
 // streams either top rows (16-byte bf16 loads, 8 outputs per lane, four rows
 // in flight) or middle rows (4-byte code loads, 8 outputs per lane, so both
-// tiers share the lane -> output mapping; eight rows in flight).  The middle tier is decoded in registers:
+// tiers share the lane -> output mapping; eight rows in flight, nine for
+// keyed tiers).  The middle tier is decoded in registers:
 // x_j * What[j][o] = (x_j scale_js) q_jo + x_j zero_js, where the second term
 // is the same for all outputs of the segment and is summed once per lane.
-// Partials are summed in chunk order by the shared split-K reduction.
+// The tiers come as index lists (a chunk is a range of list items) or as two
+// threshold pairs over the keys (a chunk is a range of inputs; the workgroup
+// lists its tier's members in LDS first).  Partials are summed in chunk
+// order by the shared split-K reduction.
 #include <algorithm>
 
 #include <hip/hip_fp16.h>
