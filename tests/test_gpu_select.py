@@ -76,10 +76,49 @@ def test_special_values_and_zero_runs():
 
 
 def test_all_equal_keys():
+    """Rows whose eligible keys are all equal (every key on one histogram bin
+    in every pass): index order alone decides, for every row length class,
+    for all-zero float rows, with zeros left out by nonzero_only, with an
+    exclusion mask and with the two-list split."""
     banner("select all-equal keys")
     keys = np.full((3, 5000), 7, dtype=np.uint32)
     check(keys, B.KEY_U32, 0, 2500)
     check(keys, B.KEY_U32, 1234, 4321)
+    for n in (1, 300, 4096, 14336, 28000, 32768):
+        z = np.zeros((2, n), dtype=np.float32)
+        z[1] = -0.0
+        for lo, hi in ((0, max(1, n // 3)), (n // 5, n // 2 + 1), (0, n)):
+            check(z, B.KEY_ABS_F32, lo, hi)
+        v = np.full((1, n), np.float32(-2.5))
+        check(v, B.KEY_F32, 0, max(1, n // 4))
+    rng = np.random.default_rng(8)
+    n = 6000
+    sparse = np.where(rng.random((2, n)) < 0.3, 9, 0).astype(np.uint32)   # equal nonzero keys
+    check(sparse, B.KEY_U32, 0, 700, nonzero_only=True)
+    check(sparse, B.KEY_U32, 100, 5000, nonzero_only=True)
+    # excluded entries hold other keys; the eligible ones are all equal
+    keys = np.full(n, 5, dtype=np.uint32)
+    ex = rng.random(n) < 0.4
+    keys[ex] = rng.integers(0, 50, int(ex.sum()))
+    md = dev(ex.astype(np.uint8))
+    idx = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select(dev(keys), B.KEY_U32, 0, 1000, exclude_mask=md, idx_out=idx, count_out=cnt)
+    torch.cuda.synchronize()
+    elig = np.flatnonzero(~ex)
+    c = int(host(cnt)[0])
+    assert c == 1000 and np.array_equal(host(idx)[:c], elig[:1000])
+    # the two-list split on an all-equal row
+    eq = dev(np.full((1, n), np.float32(0.25)))
+    mid = torch.full((1, 3000), -1, dtype=torch.int32, device="cuda")
+    top = torch.full((1, 1000), -1, dtype=torch.int32, device="cuda")
+    cm = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ct = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.sparse_ffn_select(eq, B.KEY_ABS_F32, 1000, 4000, idx_out=mid, count_out=cm, idx_top_out=top,
+                        count_top_out=ct)
+    torch.cuda.synchronize()
+    assert int(host(ct)[0]) == 1000 and np.array_equal(host(top)[0], np.arange(1000))
+    assert int(host(cm)[0]) == 3000 and np.array_equal(host(mid)[0], np.arange(1000, 4000))
 
 
 def test_counts_with_heavy_ties_union_and_freq():
